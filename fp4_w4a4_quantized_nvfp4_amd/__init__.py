@@ -1,0 +1,323 @@
+"""Python binding of libq4rac (NVFP4 W4A4 GEMM with Residual Activation Compensation).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libq4rac.so``; PyTorch supplies device memory and the current stream.  The
+library must have been built (``python -m fp4_w4a4_quantized_nvfp4_amd.build``);
+importing the functions without it raises instead of falling back to anything.
+
+Function names and argument meaning follow ``include/q4rac.h``.  bf16 tensors
+may be passed as ``torch.bfloat16`` or as ``int16``/``uint16`` bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+__all__ = [
+    "Q4Error", "library_path", "lib",
+    "nvfp4_quantize", "mxfp4_quantize", "q4_select_channels", "q4_residual_gather",
+    "w4a4_gemm", "rac_gemm", "q4_moe_route", "q4_moe_sort", "q4_transpose_bf16",
+    "q4_moe_pack_w13", "moe_w4a4_grouped_gemm", "moe_workspace_layout", "prepare_weight",
+    "prepare_moe_weights", "NVFP4", "MXFP4", "OUT_F32", "OUT_BF16",
+]
+
+NVFP4, MXFP4 = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
+MOE_WS_FIELDS = 16
+MAX_TOPK = 1024
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libq4rac.so")
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"q4rac status {status}: {msg}")
+        self.status = status
+
+
+_LIB = None
+_P = C.c_void_p
+_I64, _I32, _SZ = C.c_int64, C.c_int32, C.c_size_t
+
+_SIGS = {
+    "q4_last_error": (C.c_char_p, []),
+    "q4_version": (_I32, []),
+    "q4_quantize_workspace_size": (_SZ, [_I64, _I64, _I32]),
+    "nvfp4_quantize": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "mxfp4_quantize": (_I32, [_P, _I64, _I64, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "q4_select_workspace_size": (_SZ, [_I64]),
+    "q4_select_channels": (_I32, [_P, _I64, _I32, _P, _P, _SZ, _P]),
+    "q4_residual_gather": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I64, _P]),
+    "w4a4_gemm": (_I32, [_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
+    "rac_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
+    "rac_gemm": (_I32, [_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
+                        _I32, _P, _SZ, _P]),
+    "q4_moe_route": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P]),
+    "q4_moe_sort_workspace_size": (_SZ, [_I64, _I32, _I32]),
+    "q4_moe_sort": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "q4_transpose_bf16": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
+    "q4_moe_pack_w13": (_I32, [_P, _I32, _I32, _I32, _P, _P]),
+    "moe_workspace_size": (_SZ, [_I32, _I64, _I32, _I32, _I32, _I32, _I32]),
+    "moe_workspace_layout": (_I32, [_I32, _I64, _I32, _I32, _I32, _I32, _I32, _P]),
+    "moe_w4a4_grouped_gemm": (_I32, [_I32, _P, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P,
+                                     _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _SZ, _P]),
+}
+
+
+def lib():
+    """The loaded library (ctypes).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m fp4_w4a4_quantized_nvfp4_amd.build`")
+        L = C.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int):
+    if status != 0:
+        raise Q4Error(status, lib().q4_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("q4rac takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("q4rac takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _bf16(t):
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError("expected a bf16 tensor (torch.bfloat16 or 16-bit bit patterns)")
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+# ------------------------------------------------------------------ quantizer
+def _quantize(fmt, x, tensor_scale_in=None, topk=0, want_scores=True, stream=None):
+    x = _bf16(x)
+    rows, cols = x.shape
+    dev = x.device
+    L = lib()
+    blk = 16 if fmt == NVFP4 else 32
+    codes = _empty((rows, cols // 2), torch.uint8, dev)
+    scales = _empty((rows, max(cols // blk, 0)), torch.uint8, dev)
+    ts = _empty((1,), torch.float32, dev) if fmt == NVFP4 else None
+    score = _empty((cols,), torch.float64, dev) if want_scores else None
+    idx = _empty((topk,), torch.int32, dev) if topk > 0 else None
+    wsb = L.q4_quantize_workspace_size(rows, cols, fmt)
+    ws = _empty((max(wsb, 1),), torch.uint8, dev)
+    if fmt == NVFP4:
+        st = L.nvfp4_quantize(_ptr(x), rows, cols, _ptr(tensor_scale_in), _ptr(codes), _ptr(scales),
+                              _ptr(ts), _ptr(score), topk, _ptr(idx), _ptr(ws), wsb, _stream(stream))
+    else:
+        st = L.mxfp4_quantize(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _ptr(score), topk,
+                              _ptr(idx), _ptr(ws), wsb, _stream(stream))
+    _check(st)
+    return {"fmt": fmt, "codes": codes, "scales": scales, "tensor_scale": ts,
+            "chan_score": score, "chan_idx": idx}
+
+
+def nvfp4_quantize(x, tensor_scale_in=None, topk=0, want_scores=True, stream=None):
+    """NVFP4 quantization of bf16 x [rows, cols] -> dict of device tensors."""
+    return _quantize(NVFP4, x, tensor_scale_in, topk, want_scores, stream)
+
+
+def mxfp4_quantize(x, topk=0, want_scores=True, stream=None):
+    return _quantize(MXFP4, x, None, topk, want_scores, stream)
+
+
+def q4_select_channels(chan_score, topk, stream=None):
+    cols = chan_score.shape[0]
+    idx = _empty((topk,), torch.int32, chan_score.device)
+    _check(lib().q4_select_channels(_ptr(chan_score), cols, topk, _ptr(idx) if topk else None,
+                                    None, 0, _stream(stream)))
+    return idx
+
+
+def q4_residual_gather(x, q, chan_idx, ld_r=None, stream=None):
+    x = _bf16(x)
+    rows, cols = x.shape
+    k = 0 if chan_idx is None else int(chan_idx.shape[0])
+    ld_r = max(k, 1) if ld_r is None else ld_r
+    R = _empty((rows, ld_r), torch.int16, x.device)
+    _check(lib().q4_residual_gather(q["fmt"], _ptr(x), rows, cols, _ptr(q["codes"]),
+                                    _ptr(q["scales"]), _ptr(q["tensor_scale"]),
+                                    _ptr(chan_idx) if k else None, k, _ptr(R), ld_r,
+                                    _stream(stream)))
+    return R
+
+
+# ------------------------------------------------------------------ GEMM
+def w4a4_gemm(A, W, out_dtype=OUT_F32, stream=None):
+    """Y = W4A4(A, W) for quantized dicts A [M, K] and W [N, K]."""
+    M = A["codes"].shape[0]
+    N = W["codes"].shape[0]
+    K = A["codes"].shape[1] * 2
+    Y = _empty((M, N), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
+               A["codes"].device)
+    _check(lib().w4a4_gemm(A["fmt"], M, N, K, _ptr(A["codes"]), _ptr(A["scales"]),
+                           _ptr(A["tensor_scale"]), _ptr(W["codes"]), _ptr(W["scales"]),
+                           _ptr(W["tensor_scale"]), _ptr(Y), out_dtype, _stream(stream)))
+    return Y
+
+
+def rac_gemm(x, A, W, w_hi_t, chan_set, out_dtype=OUT_F32, stream=None, Y=None, workspace=None):
+    """Y = W4A4(A, W) + residual(x on chan_set) @ W_hi[:, chan_set]^T."""
+    x = _bf16(x)
+    M, K = x.shape
+    N = W["codes"].shape[0]
+    k = 0 if chan_set is None else int(chan_set.shape[0])
+    L = lib()
+    if Y is None:
+        Y = _empty((M, N), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, x.device)
+    wsb = L.rac_gemm_workspace_size(M, N, K, k)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = _empty((max(wsb, 1),), torch.uint8, x.device)
+    _check(L.rac_gemm(A["fmt"], M, N, K, _ptr(x), _ptr(A["codes"]), _ptr(A["scales"]),
+                      _ptr(A["tensor_scale"]), _ptr(W["codes"]), _ptr(W["scales"]),
+                      _ptr(W["tensor_scale"]), _ptr(w_hi_t) if k else None,
+                      _ptr(chan_set) if k else None, k, _ptr(Y), out_dtype, _ptr(workspace),
+                      wsb, _stream(stream)))
+    return Y
+
+
+def q4_transpose_bf16(x, stream=None):
+    """[batch,] rows x cols -> [batch,] cols x rows."""
+    x = _bf16(x)
+    batch = x.shape[0] if x.dim() == 3 else 1
+    rows, cols = x.shape[-2], x.shape[-1]
+    out = _empty(x.shape[:-2] + (cols, rows), x.dtype, x.device)
+    _check(lib().q4_transpose_bf16(_ptr(x), batch, rows, cols, _ptr(out), _stream(stream)))
+    return out
+
+
+def prepare_weight(w, fmt=NVFP4, stream=None):
+    """Offline weight preparation: quantize W [N, K] and build W_hi^T [K, N]."""
+    q = _quantize(fmt, w, None, 0, False, stream)
+    q["w_hi_t"] = q4_transpose_bf16(w, stream)
+    return q
+
+
+# ------------------------------------------------------------------ MoE
+def q4_moe_route(logits, topk, stream=None):
+    T, E = logits.shape
+    idx = _empty((T, topk), torch.int32, logits.device)
+    w = _empty((T, topk), torch.float32, logits.device)
+    _check(lib().q4_moe_route(_ptr(logits), T, E, topk, _ptr(idx), _ptr(w), _stream(stream)))
+    return idx, w
+
+
+def q4_moe_sort(topk_idx, E, stream=None):
+    T, k = topk_idx.shape
+    L = lib()
+    perm = _empty((T * k,), torch.int32, topk_idx.device)
+    offsets = _empty((E + 1,), torch.int32, topk_idx.device)
+    wsb = L.q4_moe_sort_workspace_size(T, E, k)
+    ws = _empty((max(wsb, 1),), torch.uint8, topk_idx.device)
+    _check(L.q4_moe_sort(_ptr(topk_idx), T, E, k, _ptr(perm), _ptr(offsets), _ptr(ws), wsb,
+                         _stream(stream)))
+    return perm, offsets
+
+
+def q4_moe_pack_w13(w13, stream=None):
+    """[E, 2F, H] logical (gate rows, then up rows) -> packed 32-row groups."""
+    w13 = _bf16(w13)
+    E, F2, H = w13.shape
+    out = torch.empty_like(w13)
+    _check(lib().q4_moe_pack_w13(_ptr(w13), E, F2 // 2, H, _ptr(out), _stream(stream)))
+    return out
+
+
+def _quantize_stacked(fmt, w, stream=None):
+    """Quantize each expert [E, R, C] with its own tensor scale; stacked outputs."""
+    E, R, Cc = w.shape
+    blk = 16 if fmt == NVFP4 else 32
+    dev = w.device
+    codes = _empty((E, R, Cc // 2), torch.uint8, dev)
+    scales = _empty((E, R, Cc // blk), torch.uint8, dev)
+    ts = _empty((E,), torch.float32, dev) if fmt == NVFP4 else None
+    L = lib()
+    wsb = L.q4_quantize_workspace_size(R, Cc, fmt)
+    ws = _empty((max(wsb, 1),), torch.uint8, dev)
+    s = _stream(stream)
+    for e in range(E):
+        if fmt == NVFP4:
+            st = L.nvfp4_quantize(_ptr(w[e]), R, Cc, None, _ptr(codes[e]), _ptr(scales[e]),
+                                  ts[e:e + 1].data_ptr(), None, 0, None, _ptr(ws), wsb, s)
+        else:
+            st = L.mxfp4_quantize(_ptr(w[e]), R, Cc, _ptr(codes[e]), _ptr(scales[e]), None, 0,
+                                  None, _ptr(ws), wsb, s)
+        _check(st)
+    return {"fmt": fmt, "codes": codes, "scales": scales, "tensor_scale": ts}
+
+
+def prepare_moe_weights(w13, w2, fmt=NVFP4, with_hi=True, stream=None):
+    """Offline expert preparation from logical bf16 w13 [E, 2F, H] and w2 [E, H, F]."""
+    w13p = q4_moe_pack_w13(w13, stream)
+    out = {"fmt": fmt, "w13": _quantize_stacked(fmt, w13p, stream),
+           "w2": _quantize_stacked(fmt, _bf16(w2), stream),
+           "E": w13.shape[0], "F": w13.shape[1] // 2, "H": w13.shape[2]}
+    if with_hi:
+        out["w13_hi_t"] = q4_transpose_bf16(w13p, stream)
+        out["w2_hi_t"] = q4_transpose_bf16(_bf16(w2), stream)
+    return out
+
+
+def moe_workspace_layout(fmt, T, E, H, F, topk, rac_k):
+    L = lib()
+    offs = (C.c_size_t * MOE_WS_FIELDS)()
+    _check(L.moe_workspace_layout(fmt, T, E, H, F, topk, rac_k, offs))
+    return list(offs), L.moe_workspace_size(fmt, T, E, H, F, topk, rac_k)
+
+
+def moe_w4a4_grouped_gemm(tokens, topk_idx, topk_w, experts, rac_k, out_dtype=OUT_BF16,
+                          workspace=None, stream=None, Y=None):
+    """Token-sorted grouped W4A4+RAC SwiGLU expert layer; returns (Y, workspace)."""
+    tokens = _bf16(tokens)
+    T, H = tokens.shape
+    topk = topk_idx.shape[1]
+    fmt = experts["fmt"]
+    E, F = experts["E"], experts["F"]
+    L = lib()
+    wsb = L.moe_workspace_size(fmt, T, E, H, F, topk, rac_k)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = _empty((max(wsb, 1),), torch.uint8, tokens.device)
+    if Y is None:
+        Y = _empty((T, H), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
+                   tokens.device)
+    w13, w2 = experts["w13"], experts["w2"]
+    _check(L.moe_w4a4_grouped_gemm(
+        fmt, _ptr(tokens), T, H, _ptr(topk_idx), _ptr(topk_w), topk, E, F,
+        _ptr(w13["codes"]), _ptr(w13["scales"]), _ptr(w13["tensor_scale"]),
+        _ptr(w2["codes"]), _ptr(w2["scales"]), _ptr(w2["tensor_scale"]),
+        _ptr(experts.get("w13_hi_t")) if rac_k else None,
+        _ptr(experts.get("w2_hi_t")) if rac_k else None,
+        rac_k, _ptr(Y), out_dtype, _ptr(workspace), wsb, _stream(stream)))
+    return Y, workspace

@@ -1,0 +1,571 @@
+// C ABI of the q4rac library: argument validation, workspace sizing and launch
+// sequencing.  Declarations and the meaning of every argument are in
+// include/q4rac.h.  Every check runs on the host before the first launch.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/q4rac.h"
+#include "q4_internal.h"
+
+using namespace q4;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+q4_status_t fail(q4_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+q4_status_t hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return Q4_OK;
+  return fail(Q4_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+#define Q4_REQUIRE_PTR(p)                                                         \
+  do {                                                                            \
+    if (!(p)) return fail(Q4_EINVAL, "%s: '%s' is null", __func__, #p);            \
+    if (!aligned16(p)) return fail(Q4_EALIGN, "%s: '%s' is not 16-byte aligned", __func__, #p); \
+  } while (0)
+// scalar-accessed buffers (tensor scales, index lists, scores) need only their
+// element alignment
+#define Q4_REQUIRE_SCALAR(p, a)                                                   \
+  do {                                                                            \
+    if (!(p)) return fail(Q4_EINVAL, "%s: '%s' is null", __func__, #p);            \
+    if (!aligned(p, a)) return fail(Q4_EALIGN, "%s: '%s' is not %d-byte aligned", __func__, #p, (int)(a)); \
+  } while (0)
+#define Q4_OPT_PTR(p)                                                             \
+  do {                                                                            \
+    if ((p) && !aligned16(p))                                                     \
+      return fail(Q4_EALIGN, "%s: '%s' is not 16-byte aligned", __func__, #p);     \
+  } while (0)
+
+hipStream_t S(void* s) { return (hipStream_t)s; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+int32_t round_up32(int32_t k) { return (k + 31) & ~31; }
+
+}  // namespace
+
+extern "C" {
+
+const char* q4_last_error(void) { return g_err; }
+int32_t q4_version(void) { return 100; }
+
+// ======================================================================== quantize
+size_t q4_quantize_workspace_size(int64_t rows, int64_t cols, int32_t fmt) {
+  (void)fmt;
+  if (rows < 0 || cols <= 0) return 0;
+  return quantize_workspace_bytes(rows, cols);
+}
+
+static q4_status_t quantize_common(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
+                                   const float* ts_in, uint8_t* codes, uint8_t* scales,
+                                   float* ts_out, double* chan_score, int32_t topk,
+                                   int32_t* chan_idx, void* ws, size_t ws_bytes, void* stream,
+                                   const char* fn) {
+  const int blk = mx ? 32 : 16;
+  if (rows < 0 || cols <= 0 || cols % blk != 0 || rows >= kMaxDim || cols >= kMaxDim)
+    return fail(Q4_ESHAPE, "%s: need rows >= 0 and cols > 0 with cols %% %d == 0 (got %lld x %lld)",
+                fn, blk, (long long)rows, (long long)cols);
+  if (topk < 0 || topk > cols || topk > Q4_MAX_TOPK)
+    return fail(Q4_EINVAL, "%s: topk %d outside [0, min(cols, %d)]", fn, topk, Q4_MAX_TOPK);
+  if (rows > 0) {
+    if (!x) return fail(Q4_EINVAL, "%s: 'x' is null", fn);
+    if (!aligned16(x)) return fail(Q4_EALIGN, "%s: 'x' is not 16-byte aligned", fn);
+    if (!codes || !scales) return fail(Q4_EINVAL, "%s: 'codes'/'scales' is null", fn);
+    if (!aligned16(codes) || !aligned16(scales))
+      return fail(Q4_EALIGN, "%s: 'codes'/'scales' not 16-byte aligned", fn);
+  }
+  if (!mx && !ts_out) return fail(Q4_EINVAL, "%s: 'tensor_scale_out' is null", fn);
+  if (ts_in && !aligned(ts_in, 4)) return fail(Q4_EALIGN, "%s: 'tensor_scale_in' not aligned", fn);
+  if (ts_out && !aligned(ts_out, 4)) return fail(Q4_EALIGN, "%s: 'tensor_scale_out' not aligned", fn);
+  if (chan_score && !aligned(chan_score, 8)) return fail(Q4_EALIGN, "%s: 'chan_score' not aligned", fn);
+  if (topk > 0 && !chan_idx) return fail(Q4_EINVAL, "%s: 'chan_idx' is null with topk > 0", fn);
+  if (topk == 0 && chan_idx) return fail(Q4_EINVAL, "%s: 'chan_idx' given with topk == 0", fn);
+  if (chan_idx && !aligned(chan_idx, 4)) return fail(Q4_EALIGN, "%s: 'chan_idx' not aligned", fn);
+  const size_t need = quantize_workspace_bytes(rows, cols);
+  if (!ws || ws_bytes < need)
+    return fail(Q4_EWORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws_bytes);
+  if (!aligned16(ws)) return fail(Q4_EALIGN, "%s: 'workspace' not aligned", fn);
+  return hip_status(launch_quantize(mx, x, rows, cols, ts_in, codes, scales, ts_out, chan_score,
+                                    topk, chan_idx, ws, S(stream)),
+                    fn);
+}
+
+q4_status_t nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
+                           const float* tensor_scale_in, uint8_t* codes, uint8_t* scales,
+                           float* tensor_scale_out, double* chan_score, int32_t topk,
+                           int32_t* chan_idx, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return quantize_common(false, x, rows, cols, tensor_scale_in, codes, scales, tensor_scale_out,
+                         chan_score, topk, chan_idx, workspace, workspace_bytes, stream,
+                         "nvfp4_quantize");
+}
+
+q4_status_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, double* chan_score, int32_t topk, int32_t* chan_idx,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return quantize_common(true, x, rows, cols, nullptr, codes, scales, nullptr, chan_score, topk,
+                         chan_idx, workspace, workspace_bytes, stream, "mxfp4_quantize");
+}
+
+size_t q4_select_workspace_size(int64_t cols) {
+  (void)cols;
+  return 0;
+}
+
+q4_status_t q4_select_channels(const double* chan_score, int64_t cols, int32_t topk,
+                               int32_t* chan_idx, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (cols <= 0 || cols >= kMaxDim) return fail(Q4_ESHAPE, "q4_select_channels: cols %lld", (long long)cols);
+  if (topk < 0 || topk > cols || topk > Q4_MAX_TOPK)
+    return fail(Q4_EINVAL, "q4_select_channels: topk %d outside [0, min(cols, %d)]", topk, Q4_MAX_TOPK);
+  Q4_REQUIRE_SCALAR(chan_score, 8);
+  if (topk > 0) Q4_REQUIRE_SCALAR(chan_idx, 4);
+  return hip_status(launch_select(chan_score, cols, topk, chan_idx, S(stream)),
+                    "q4_select_channels");
+}
+
+q4_status_t q4_residual_gather(int32_t fmt, const uint16_t* x, int64_t rows, int64_t cols,
+                               const uint8_t* codes, const uint8_t* scales,
+                               const float* tensor_scale, const int32_t* chan_idx, int32_t k,
+                               uint16_t* R, int64_t ld_r, void* stream) {
+  if (fmt != Q4_NVFP4 && fmt != Q4_MXFP4) return fail(Q4_EINVAL, "q4_residual_gather: bad format %d", fmt);
+  const bool mx = fmt == Q4_MXFP4;
+  const int blk = mx ? 32 : 16;
+  if (rows < 0 || cols <= 0 || cols % blk || rows >= kMaxDim || cols >= kMaxDim)
+    return fail(Q4_ESHAPE, "q4_residual_gather: bad shape %lld x %lld", (long long)rows, (long long)cols);
+  if (k < 0 || k > cols || k > Q4_MAX_TOPK || ld_r < k || ld_r <= 0)
+    return fail(Q4_EINVAL, "q4_residual_gather: need 0 <= k <= min(cols, %d) and ld_r >= max(k, 1)", Q4_MAX_TOPK);
+  if (mx && tensor_scale) return fail(Q4_EINVAL, "q4_residual_gather: MXFP4 takes no tensor scale");
+  if (!mx) Q4_REQUIRE_SCALAR(tensor_scale, 4);
+  if (rows > 0) {
+    Q4_REQUIRE_PTR(x);
+    Q4_REQUIRE_PTR(codes);
+    Q4_REQUIRE_PTR(scales);
+    Q4_REQUIRE_PTR(R);
+    if (k > 0) Q4_REQUIRE_SCALAR(chan_idx, 4);
+  }
+  return hip_status(launch_residual_gather(mx, x, rows, cols, codes, scales, tensor_scale,
+                                           chan_idx, k, R, ld_r, S(stream)),
+                    "q4_residual_gather");
+}
+
+// ======================================================================== GEMM
+static q4_status_t check_gemm(const char* fn, int32_t fmt, int64_t M, int64_t N, int64_t K,
+                              const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                              const uint8_t* w_codes, const uint8_t* w_scales, const float* w_ts,
+                              void* Y, int32_t y_dtype) {
+  if (fmt != Q4_NVFP4 && fmt != Q4_MXFP4) return fail(Q4_EINVAL, "%s: bad format %d", fn, fmt);
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return fail(Q4_ESHAPE, "%s: need M, N >= 0 and K > 0 with K %% 32 == 0 (got %lld, %lld, %lld)",
+                fn, (long long)M, (long long)N, (long long)K);
+  if (y_dtype != Q4_OUT_F32 && y_dtype != Q4_OUT_BF16) return fail(Q4_EINVAL, "%s: bad y_dtype", fn);
+  if (M > 0 && N > 0) {
+    Q4_REQUIRE_PTR(a_codes);
+    Q4_REQUIRE_PTR(a_scales);
+    Q4_REQUIRE_PTR(w_codes);
+    Q4_REQUIRE_PTR(w_scales);
+    Q4_REQUIRE_PTR(Y);
+  }
+  if (fmt == Q4_NVFP4) {
+    Q4_REQUIRE_SCALAR(a_ts, 4);
+    Q4_REQUIRE_SCALAR(w_ts, 4);
+  } else if (a_ts || w_ts) {
+    return fail(Q4_EINVAL, "%s: MXFP4 operands take no tensor scale", fn);
+  }
+  return Q4_OK;
+}
+
+q4_status_t w4a4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                      const uint8_t* a_scales, const float* a_tensor_scale,
+                      const uint8_t* w_codes, const uint8_t* w_scales,
+                      const float* w_tensor_scale, void* Y, int32_t y_dtype, void* stream) {
+  q4_status_t st = check_gemm("w4a4_gemm", fmt, M, N, K, a_codes, a_scales, a_tensor_scale,
+                              w_codes, w_scales, w_tensor_scale, Y, y_dtype);
+  if (st != Q4_OK) return st;
+  if (M == 0 || N == 0) return Q4_OK;
+  GemmArgs g{};
+  g.M = M;
+  g.N = N;
+  g.K = (int32_t)K;
+  g.mx = fmt == Q4_MXFP4;
+  g.a_codes = a_codes;
+  g.a_scales = a_scales;
+  g.a_ts = a_tensor_scale;
+  g.w_codes = w_codes;
+  g.w_scales = w_scales;
+  g.w_ts = w_tensor_scale;
+  g.Y = Y;
+  g.ldy = N;
+  g.y_bf16 = y_dtype == Q4_OUT_BF16;
+  g.epilogue = kEpiStore;
+  return hip_status(launch_w4a4_gemm(g, 0, S(stream)), "w4a4_gemm");
+}
+
+size_t rac_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k) {
+  (void)K;
+  if (M < 0 || N < 0 || k < 0) return 0;
+  const int64_t kp = round_up32(k);
+  return align256((size_t)M * kp * 2) + align256((size_t)N * kp * 2);
+}
+
+q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                     const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+                     const uint8_t* w_codes, const uint8_t* w_scales, const float* w_tensor_scale,
+                     const uint16_t* w_hi_t, const int32_t* chan_set, int32_t k, void* Y,
+                     int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  q4_status_t st = check_gemm("rac_gemm", fmt, M, N, K, a_codes, a_scales, a_tensor_scale,
+                              w_codes, w_scales, w_tensor_scale, Y, y_dtype);
+  if (st != Q4_OK) return st;
+  if (k < 0 || k > K || k > Q4_MAX_TOPK)
+    return fail(Q4_EINVAL, "rac_gemm: k %d outside [0, min(K, %d)]", k, Q4_MAX_TOPK);
+  if (k > 0) {
+    Q4_REQUIRE_PTR(x);
+    Q4_REQUIRE_PTR(w_hi_t);
+    Q4_REQUIRE_SCALAR(chan_set, 4);
+    const size_t need = rac_gemm_workspace_size(M, N, K, k);
+    if (!workspace || workspace_bytes < need)
+      return fail(Q4_EWORKSPACE, "rac_gemm: workspace of %zu bytes needed (got %zu)", need,
+                  workspace_bytes);
+    Q4_REQUIRE_PTR(workspace);
+  }
+  if (M == 0 || N == 0) return Q4_OK;
+  const bool mx = fmt == Q4_MXFP4;
+  GemmArgs g{};
+  g.M = M;
+  g.N = N;
+  g.K = (int32_t)K;
+  g.mx = mx;
+  g.a_codes = a_codes;
+  g.a_scales = a_scales;
+  g.a_ts = a_tensor_scale;
+  g.w_codes = w_codes;
+  g.w_scales = w_scales;
+  g.w_ts = w_tensor_scale;
+  g.Y = Y;
+  g.ldy = N;
+  g.y_bf16 = y_dtype == Q4_OUT_BF16;
+  g.epilogue = kEpiStore;
+  if (k > 0) {
+    const int32_t kp = round_up32(k);
+    uint16_t* R = (uint16_t*)workspace;
+    uint16_t* W_S = (uint16_t*)((uint8_t*)workspace + align256((size_t)M * kp * 2));
+    hipError_t e = launch_residual_gather(mx, x, M, K, a_codes, a_scales, a_tensor_scale,
+                                          chan_set, k, R, kp, S(stream));
+    if (e != hipSuccess) return hip_status(e, "rac_gemm (residual gather)");
+    e = launch_wsel_gather(w_hi_t, 1, K, N, chan_set, k, kp, W_S, S(stream));
+    if (e != hipSuccess) return hip_status(e, "rac_gemm (weight gather)");
+    g.r_res = R;
+    g.ld_r = kp;
+    g.w_sel = W_S;
+    g.kp = kp;
+  }
+  return hip_status(launch_w4a4_gemm(g, 0, S(stream)), "rac_gemm");
+}
+
+// ======================================================================== MoE
+q4_status_t q4_moe_route(const float* logits, int64_t T, int32_t E, int32_t topk,
+                         int32_t* topk_idx, float* topk_w, void* stream) {
+  if (T < 0 || T >= kMaxDim) return fail(Q4_ESHAPE, "q4_moe_route: bad T");
+  if (E < 1 || E > 1024) return fail(Q4_ESHAPE, "q4_moe_route: need 1 <= E <= 1024");
+  if (topk < 1 || topk > E || topk > 16) return fail(Q4_EINVAL, "q4_moe_route: need 1 <= topk <= min(E, 16)");
+  if (T > 0) {
+    Q4_REQUIRE_SCALAR(logits, 4);
+    Q4_REQUIRE_SCALAR(topk_idx, 4);
+    Q4_REQUIRE_SCALAR(topk_w, 4);
+  }
+  return hip_status(launch_moe_route(logits, T, E, topk, topk_idx, topk_w, S(stream)),
+                    "q4_moe_route");
+}
+
+static int64_t moe_max_tiles(int64_t T, int32_t E, int32_t topk) {
+  return (T * topk + kGemmBM - 1) / kGemmBM + E;
+}
+
+size_t q4_moe_sort_workspace_size(int64_t T, int32_t E, int32_t topk) {
+  if (T < 0 || E < 1 || topk < 1) return 0;
+  return align256((size_t)E * 4) + align256((size_t)T * topk * 4) +
+         align256((size_t)moe_max_tiles(T, E, topk) * 16) + 256;
+}
+
+q4_status_t q4_moe_sort(const int32_t* topk_idx, int64_t T, int32_t E, int32_t topk,
+                        int32_t* perm, int32_t* offsets, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (T < 0 || T * 16 >= kMaxDim) return fail(Q4_ESHAPE, "q4_moe_sort: bad T");
+  if (E < 1 || E > 1024) return fail(Q4_ESHAPE, "q4_moe_sort: need 1 <= E <= 1024");
+  if (topk < 1 || topk > E || topk > 16) return fail(Q4_EINVAL, "q4_moe_sort: need 1 <= topk <= min(E, 16)");
+  Q4_REQUIRE_SCALAR(offsets, 4);
+  if (T > 0) {
+    Q4_REQUIRE_SCALAR(topk_idx, 4);
+    Q4_REQUIRE_SCALAR(perm, 4);
+  }
+  const size_t need = q4_moe_sort_workspace_size(T, E, topk);
+  if (!workspace || workspace_bytes < need)
+    return fail(Q4_EWORKSPACE, "q4_moe_sort: workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  Q4_REQUIRE_PTR(workspace);
+  uint8_t* w = (uint8_t*)workspace;
+  int32_t* counts = (int32_t*)w;
+  w += align256((size_t)E * 4);
+  int32_t* inv = (int32_t*)w;
+  w += align256((size_t)T * topk * 4);
+  int32_t* tiles = (int32_t*)w;
+  w += align256((size_t)moe_max_tiles(T, E, topk) * 16);
+  int32_t* ntiles = (int32_t*)w;
+  return hip_status(launch_moe_sort(topk_idx, T, E, topk, perm, offsets, inv, tiles, ntiles,
+                                    counts, S(stream)),
+                    "q4_moe_sort");
+}
+
+q4_status_t q4_transpose_bf16(const uint16_t* in, int64_t batch, int64_t rows, int64_t cols,
+                              uint16_t* out, void* stream) {
+  if (batch < 0 || rows < 0 || cols < 0 || batch >= 65536 || rows >= kMaxDim || cols >= kMaxDim)
+    return fail(Q4_ESHAPE, "q4_transpose_bf16: bad shape");
+  if (batch * rows * cols > 0) {
+    Q4_REQUIRE_PTR(in);
+    Q4_REQUIRE_PTR(out);
+  }
+  return hip_status(launch_transpose_bf16(in, batch, rows, cols, out, S(stream)), "q4_transpose_bf16");
+}
+
+q4_status_t q4_moe_pack_w13(const uint16_t* w13, int32_t E, int32_t F, int32_t H, uint16_t* out,
+                            void* stream) {
+  if (E < 0 || E >= 65536 || F <= 0 || F % 32 || H <= 0 || 2 * F >= 65536)
+    return fail(Q4_ESHAPE, "q4_moe_pack_w13: need F %% 32 == 0, F > 0, H > 0, 2F < 65536, E < 65536");
+  if (E > 0) {
+    Q4_REQUIRE_PTR(w13);
+    Q4_REQUIRE_PTR(out);
+  }
+  return hip_status(launch_moe_pack_w13(w13, E, F, H, out, S(stream)), "q4_moe_pack_w13");
+}
+
+// workspace fields of the grouped expert layer
+namespace {
+struct MoeLayout {
+  size_t off[Q4_MOE_WS_FIELDS];
+  size_t inv_perm, tiles, ntiles, counts, a_rows, w13_sel, w2_sel, qws, total;
+};
+
+MoeLayout moe_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F, int32_t topk,
+                     int32_t rac_k) {
+  MoeLayout L{};
+  const bool mx = fmt == Q4_MXFP4;
+  const int64_t R = T * topk;
+  const int64_t kp = round_up32(rac_k);
+  const int sdiv = mx ? 32 : 16;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  L.off[0] = take((size_t)R * 4);              // perm
+  L.off[1] = take((size_t)(E + 1) * 4);        // offsets
+  L.off[2] = take((size_t)T * H / 2);          // x codes
+  L.off[3] = take((size_t)T * H / sdiv);       // x scales
+  L.off[4] = take(4);                          // x tensor scale
+  L.off[5] = take((size_t)(rac_k > 0 ? rac_k : 1) * 4);
+  L.off[6] = take((size_t)T * (kp ? kp : 1) * 2);
+  L.off[7] = take((size_t)R * F * 2);          // h
+  L.off[8] = take((size_t)R * F / 2);          // h codes
+  L.off[9] = take((size_t)R * F / sdiv);       // h scales
+  L.off[10] = take(4);
+  L.off[11] = take((size_t)(rac_k > 0 ? rac_k : 1) * 4);
+  L.off[12] = take((size_t)R * (kp ? kp : 1) * 2);
+  L.off[13] = take((size_t)R * H * 4);         // out fp32
+  L.off[14] = take((size_t)H * 8);             // x scores
+  L.off[15] = take((size_t)F * 8);             // h scores
+  L.inv_perm = take((size_t)R * 4);
+  L.tiles = take((size_t)moe_max_tiles(T, E, topk) * 16);
+  L.ntiles = take(4);
+  L.counts = take((size_t)E * 4);
+  L.a_rows = take((size_t)R * 4);
+  L.w13_sel = take((size_t)E * 2 * F * (kp ? kp : 1) * 2);
+  L.w2_sel = take((size_t)E * H * (kp ? kp : 1) * 2);
+  const size_t qa = quantize_workspace_bytes(T, H), qb = quantize_workspace_bytes(R, F);
+  L.qws = take(qa > qb ? qa : qb);
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+size_t moe_workspace_size(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F, int32_t topk,
+                          int32_t rac_k) {
+  if (T < 0 || E < 1 || H <= 0 || F <= 0 || topk < 1 || rac_k < 0) return 0;
+  return moe_layout(fmt, T, E, H, F, topk, rac_k).total;
+}
+
+q4_status_t moe_workspace_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F,
+                                 int32_t topk, int32_t rac_k, size_t* offsets) {
+  if (!offsets) return fail(Q4_EINVAL, "moe_workspace_layout: 'offsets' is null");
+  if (T < 0 || E < 1 || H <= 0 || F <= 0 || topk < 1 || rac_k < 0)
+    return fail(Q4_ESHAPE, "moe_workspace_layout: bad shape");
+  MoeLayout L = moe_layout(fmt, T, E, H, F, topk, rac_k);
+  memcpy(offsets, L.off, sizeof(L.off));
+  return Q4_OK;
+}
+
+q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T, int32_t H,
+                                  const int32_t* topk_idx, const float* topk_w, int32_t topk,
+                                  int32_t E, int32_t F, const uint8_t* w13_codes,
+                                  const uint8_t* w13_scales, const float* w13_tensor_scales,
+                                  const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                  const float* w2_tensor_scales, const uint16_t* w13_hi_t,
+                                  const uint16_t* w2_hi_t, int32_t rac_k, void* Y,
+                                  int32_t y_dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  const char* fn = "moe_w4a4_grouped_gemm";
+  if (fmt != Q4_NVFP4 && fmt != Q4_MXFP4) return fail(Q4_EINVAL, "%s: bad format %d", fn, fmt);
+  const bool mx = fmt == Q4_MXFP4;
+  if (T < 0 || T * 16 >= kMaxDim) return fail(Q4_ESHAPE, "%s: bad T", fn);
+  if (E < 1 || E > 1024) return fail(Q4_ESHAPE, "%s: need 1 <= E <= 1024", fn);
+  if (topk < 1 || topk > E || topk > 16) return fail(Q4_EINVAL, "%s: need 1 <= topk <= min(E, 16)", fn);
+  if (H <= 0 || H % 32 || F <= 0 || F % 32)
+    return fail(Q4_ESHAPE, "%s: need H %% 32 == 0 and F %% 32 == 0 (got H %d, F %d)", fn, H, F);
+  if ((int64_t)E * 2 * F >= kMaxDim || (int64_t)E * H >= kMaxDim) return fail(Q4_ESHAPE, "%s: too many weight rows", fn);
+  if (rac_k < 0 || rac_k > F || rac_k > H || rac_k > Q4_MAX_TOPK)
+    return fail(Q4_EINVAL, "%s: rac_k %d outside [0, min(H, F, %d)]", fn, rac_k, Q4_MAX_TOPK);
+  if (y_dtype != Q4_OUT_F32 && y_dtype != Q4_OUT_BF16) return fail(Q4_EINVAL, "%s: bad y_dtype", fn);
+  Q4_REQUIRE_PTR(w13_codes);
+  Q4_REQUIRE_PTR(w13_scales);
+  Q4_REQUIRE_PTR(w2_codes);
+  Q4_REQUIRE_PTR(w2_scales);
+  if (!mx) {
+    Q4_REQUIRE_SCALAR(w13_tensor_scales, 4);
+    Q4_REQUIRE_SCALAR(w2_tensor_scales, 4);
+  } else if (w13_tensor_scales || w2_tensor_scales) {
+    return fail(Q4_EINVAL, "%s: MXFP4 weights take no tensor scales", fn);
+  }
+  if (rac_k > 0) {
+    Q4_REQUIRE_PTR(w13_hi_t);
+    Q4_REQUIRE_PTR(w2_hi_t);
+  }
+  if (T > 0) {
+    Q4_REQUIRE_PTR(tokens);
+    Q4_REQUIRE_SCALAR(topk_idx, 4);
+    Q4_REQUIRE_SCALAR(topk_w, 4);
+    Q4_REQUIRE_PTR(Y);
+  }
+  const MoeLayout L = moe_layout(fmt, T, E, H, F, topk, rac_k);
+  if (!workspace || workspace_bytes < L.total)
+    return fail(Q4_EWORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, L.total, workspace_bytes);
+  Q4_REQUIRE_PTR(workspace);
+  if (T == 0) return Q4_OK;
+
+  uint8_t* w = (uint8_t*)workspace;
+  auto P = [&](size_t off) { return (void*)(w + off); };
+  const int64_t R = T * topk;
+  const int32_t kp = rac_k > 0 ? round_up32(rac_k) : 0;
+  hipStream_t s = S(stream);
+  int32_t* perm = (int32_t*)P(L.off[0]);
+  int32_t* offsets = (int32_t*)P(L.off[1]);
+  int32_t* inv = (int32_t*)P(L.inv_perm);
+  int32_t* tiles = (int32_t*)P(L.tiles);
+  int32_t* ntiles = (int32_t*)P(L.ntiles);
+  int32_t* a_rows = (int32_t*)P(L.a_rows);
+  hipError_t e;
+#define Q4_TRY(call, what)                 \
+  do {                                     \
+    e = (call);                            \
+    if (e != hipSuccess) return hip_status(e, what); \
+  } while (0)
+  Q4_TRY(launch_moe_sort(topk_idx, T, E, topk, perm, offsets, inv, tiles, ntiles,
+                         (int32_t*)P(L.counts), s), "moe sort");
+  Q4_TRY(launch_gather_rows_index(perm, R, topk, a_rows, s), "moe row index");
+  // ---- activation site 1: tokens
+  uint8_t* xc = (uint8_t*)P(L.off[2]);
+  uint8_t* xs = (uint8_t*)P(L.off[3]);
+  float* xts = mx ? nullptr : (float*)P(L.off[4]);
+  int32_t* xS = (int32_t*)P(L.off[5]);
+  uint16_t* xR = (uint16_t*)P(L.off[6]);
+  Q4_TRY(launch_quantize(mx, tokens, T, H, nullptr, xc, xs, xts, (double*)P(L.off[14]), rac_k,
+                         rac_k ? xS : nullptr, P(L.qws), s), "moe quantize tokens");
+  if (kp) {
+    Q4_TRY(launch_residual_gather(mx, tokens, T, H, xc, xs, xts, xS, rac_k, xR, kp, s),
+           "moe residual tokens");
+    Q4_TRY(launch_wsel_gather(w13_hi_t, E, H, 2 * (int64_t)F, xS, rac_k, kp,
+                              (uint16_t*)P(L.w13_sel), s), "moe w13 gather");
+  }
+  uint16_t* hbuf = (uint16_t*)P(L.off[7]);
+  GemmArgs g{};
+  g.M = R;
+  g.N = 2 * (int64_t)F;
+  g.K = H;
+  g.mx = mx;
+  g.a_codes = xc;
+  g.a_scales = xs;
+  g.a_ts = xts;
+  g.w_codes = w13_codes;
+  g.w_scales = w13_scales;
+  g.w_ts = w13_tensor_scales;
+  g.r_res = kp ? xR : nullptr;
+  g.ld_r = kp;
+  g.w_sel = kp ? (const uint16_t*)P(L.w13_sel) : nullptr;
+  g.kp = kp;
+  g.Y = hbuf;
+  g.ldy = F;
+  g.y_bf16 = 1;
+  g.epilogue = kEpiSwiGLU;
+  g.tiles = tiles;
+  g.ntiles_dev = ntiles;
+  g.a_rows = a_rows;
+  const int64_t maxt = moe_max_tiles(T, E, topk);
+  Q4_TRY(launch_w4a4_gemm(g, maxt, s), "moe w13 gemm");
+  // ---- activation site 2: h (sorted rows)
+  uint8_t* hc = (uint8_t*)P(L.off[8]);
+  uint8_t* hs = (uint8_t*)P(L.off[9]);
+  float* hts = mx ? nullptr : (float*)P(L.off[10]);
+  int32_t* hS = (int32_t*)P(L.off[11]);
+  uint16_t* hR = (uint16_t*)P(L.off[12]);
+  Q4_TRY(launch_quantize(mx, hbuf, R, F, nullptr, hc, hs, hts, (double*)P(L.off[15]), rac_k,
+                         rac_k ? hS : nullptr, P(L.qws), s), "moe quantize h");
+  if (kp) {
+    Q4_TRY(launch_residual_gather(mx, hbuf, R, F, hc, hs, hts, hS, rac_k, hR, kp, s),
+           "moe residual h");
+    Q4_TRY(launch_wsel_gather(w2_hi_t, E, F, H, hS, rac_k, kp, (uint16_t*)P(L.w2_sel), s),
+           "moe w2 gather");
+  }
+  GemmArgs g2{};
+  g2.M = R;
+  g2.N = H;
+  g2.K = F;
+  g2.mx = mx;
+  g2.a_codes = hc;
+  g2.a_scales = hs;
+  g2.a_ts = hts;
+  g2.w_codes = w2_codes;
+  g2.w_scales = w2_scales;
+  g2.w_ts = w2_tensor_scales;
+  g2.r_res = kp ? hR : nullptr;
+  g2.ld_r = kp;
+  g2.w_sel = kp ? (const uint16_t*)P(L.w2_sel) : nullptr;
+  g2.kp = kp;
+  g2.Y = P(L.off[13]);
+  g2.ldy = H;
+  g2.y_bf16 = 0;
+  g2.epilogue = kEpiStore;
+  g2.tiles = tiles;
+  g2.ntiles_dev = ntiles;
+  g2.a_rows = nullptr;
+  Q4_TRY(launch_w4a4_gemm(g2, maxt, s), "moe w2 gemm");
+  Q4_TRY(launch_moe_combine((const float*)P(L.off[13]), inv, topk_w, T, topk, H, Y,
+                            y_dtype == Q4_OUT_BF16, s), "moe combine");
+#undef Q4_TRY
+  return Q4_OK;
+}
+
+}  // extern "C"

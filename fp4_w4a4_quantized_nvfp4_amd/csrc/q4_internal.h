@@ -1,0 +1,83 @@
+// Internal declarations of the q4rac library (host launchers and shared types).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "q4_device.h"
+
+namespace q4 {
+
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+__global__ void tensor_scale_kernel(const float* ts_in, float* ts_out);
+
+// ---------------------------------------------------------------- quantizer
+size_t quantize_workspace_bytes(int64_t rows, int64_t cols);
+hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
+                           const float* ts_in, uint8_t* codes, uint8_t* scales, float* ts_out,
+                           double* chan_score, int32_t topk, int32_t* chan_idx, void* ws,
+                           hipStream_t stream);
+hipError_t launch_select(const double* scores, int64_t cols, int32_t topk, int32_t* idx,
+                         hipStream_t stream);
+hipError_t launch_residual_gather(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
+                                  const uint8_t* codes, const uint8_t* scales, const float* ts,
+                                  const int32_t* idx, int32_t k, uint16_t* R, int64_t ld_r,
+                                  hipStream_t stream);
+hipError_t launch_wsel_gather(const uint16_t* w_hi_t, int64_t batch, int64_t K, int64_t N,
+                              const int32_t* idx, int32_t k, int32_t kp, uint16_t* ws,
+                              hipStream_t stream);
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t batch, int64_t rows, int64_t cols,
+                                 uint16_t* out, hipStream_t stream);
+hipError_t launch_moe_pack_w13(const uint16_t* w13, int32_t E, int32_t F, int32_t H,
+                               uint16_t* out, hipStream_t stream);
+
+// ---------------------------------------------------------------- GEMM
+enum GemmEpilogue : int32_t { kEpiStore = 0, kEpiSwiGLU = 1 };
+
+// One W4A4 (+ residual) GEMM, dense or grouped by expert.
+struct GemmArgs {
+  int64_t M;                 // dense: rows of A / Y.  grouped: total sorted rows
+  int64_t N;                 // output columns per expert (packed W13: 2F)
+  int32_t K;
+  int32_t mx;                // 0 NVFP4, 1 MXFP4
+  const uint8_t* a_codes;    // [A rows][K/2]
+  const uint8_t* a_scales;   // [A rows][K/16 | K/32]
+  const float* a_ts;         // [1] or null
+  const uint8_t* w_codes;    // [E][N][K/2]
+  const uint8_t* w_scales;   // [E][N][K/16 | K/32]
+  const float* w_ts;         // [E] or null
+  const uint16_t* r_res;     // bf16 [A rows][ld_r] residual (null: no compensation)
+  int32_t ld_r;
+  const uint16_t* w_sel;     // bf16 [E][N][kp] selected weight columns
+  int32_t kp;                // compensated channels, a multiple of 32 (0: none)
+  void* Y;                   // store: [rows][ldy] fp32|bf16.  SwiGLU: bf16 [rows][N/2]
+  int64_t ldy;
+  int32_t y_bf16;
+  int32_t epilogue;
+  // grouped
+  const int32_t* tiles;      // int4 {expert, row_begin, row_end, 0} per M tile (null: dense)
+  const int32_t* ntiles_dev; // number of valid M tiles (device)
+  const int32_t* a_rows;     // A row of each output row (null: identity)
+};
+
+hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream);
+
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 128;
+
+// ---------------------------------------------------------------- MoE
+hipError_t launch_moe_route(const float* logits, int64_t T, int32_t E, int32_t topk,
+                            int32_t* idx, float* w, hipStream_t stream);
+size_t moe_sort_workspace_bytes(int64_t T, int32_t E, int32_t topk);
+hipError_t launch_moe_sort(const int32_t* idx, int64_t T, int32_t E, int32_t topk, int32_t* perm,
+                           int32_t* offsets, int32_t* inv_perm, int32_t* tiles,
+                           int32_t* ntiles, int32_t* counts, hipStream_t stream);
+hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const float* topk_w,
+                              int64_t T, int32_t topk, int32_t H, void* Y, int32_t y_bf16,
+                              hipStream_t stream);
+hipError_t launch_gather_rows_index(const int32_t* perm, int64_t n, int32_t topk, int32_t* a_rows,
+                                   hipStream_t stream);
+
+}  // namespace q4

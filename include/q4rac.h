@@ -1,0 +1,232 @@
+/*
+ * q4rac -- NVFP4 W4A4 GEMM with Residual Activation Compensation on MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is a DEVICE pointer unless marked (host); every
+ * call enqueues its work asynchronously on `stream` (a hipStream_t passed as
+ * void*, NULL = the default stream) and returns after launching.  The caller
+ * owns all memory: the library never allocates or frees device memory; calls
+ * that need scratch memory take a caller-provided `workspace` whose minimum size
+ * the matching *_workspace_size() function returns.  Every argument check runs
+ * on the host before any launch, so a call that returns an error has enqueued
+ * nothing and written nothing.  Errors are returned as q4_status_t codes;
+ * q4_last_error() returns a thread-local message for the last failure in the
+ * calling thread.  Device-side faults surface at the caller's next
+ * synchronisation.  Calls are stateless and thread-safe when they use distinct
+ * workspaces and outputs.
+ *
+ * Alignment: tensor scales, logits, routing weights and index arrays need 4-byte
+ * alignment, channel scores 8-byte; every other device pointer (activations,
+ * codes, scales, outputs, workspaces) must be 16-byte aligned.  Inputs must be
+ * finite (bf16 activations and weights, fp32 logits); this is documented, not
+ * checked.
+ *
+ * Method: QUADS (arXiv 2607.15810), section 2.2 paragraph "FP4" for the NVFP4
+ * format, section 3.3 Eq. 20-24 for the residual compensation.  Layouts:
+ *
+ *   x        bf16 [rows][cols] row-major; cols is the channel (reduction) axis.
+ *   codes    uint8 [rows][cols/2]: element 2i in the low nibble, 2i+1 in the
+ *            high nibble; nibble = E2M1 magnitude code (0..7 for
+ *            0,0.5,1,1.5,2,3,4,6) | 8 * sign bit of x.
+ *   scales   NVFP4: uint8 [rows][cols/16], E4M3 (bias 7, no infinities, 0x7F
+ *            unused) block scale of sixteen consecutive elements of a row.
+ *            MXFP4: uint8 [rows][cols/32], E8M0 exponent byte e + 127.
+ *   tensor   NVFP4: fp32 per-tensor scale s_t; value = code * block * s_t.
+ *
+ * Quantization rule (the plain reading of the page; each "nearest" is decided
+ * on the exact real quotient):
+ *   s_t = RN32(amax / 2688) (6 * 448: largest E2M1 magnitude times the largest
+ *         E4M3 value), 1 for an all-zero tensor, or the caller's value;
+ *   sb  = E4M3 nearest to amax_block / (6 s_t), ties to the even code,
+ *         saturating at 448;
+ *   c   = E2M1 magnitude nearest to |x| / (sb s_t), ties to the even code,
+ *         saturating at 6, zero when sb == 0;
+ *   MXFP4: block of 32, scale 2^e, e = floor(log2 amax_block) - 2 clamped to
+ *         [-127, 127] (byte 0 for an all-zero block), c nearest to |x| / 2^e.
+ *   residual r = RN32(x - dequant(x)) (the negated Eq. 20 error);
+ *   channel score_j = sum_i r_ij^2 in fp64 (Eq. 23 squared), summed over rows
+ *         ascending inside tiles of 64 rows, then over tiles ascending;
+ *   channel set S = the topk channels of largest score, ties to the smaller
+ *         channel, listed in ascending channel order (Eq. 24, absolute k).
+ */
+#ifndef Q4RAC_H
+#define Q4RAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  Q4_OK = 0,
+  Q4_EINVAL = 1,        /* null pointer, bad enum, bad k                         */
+  Q4_ESHAPE = 2,        /* dimension not supported (see each call)               */
+  Q4_EALIGN = 3,        /* pointer not 16-byte aligned                            */
+  Q4_EWORKSPACE = 4,    /* workspace smaller than *_workspace_size()             */
+  Q4_EUNSUPPORTED = 5,  /* format / option combination not provided              */
+  Q4_EHIP = 6           /* a HIP launch or runtime call failed                   */
+} q4_status_t;
+
+typedef enum { Q4_NVFP4 = 0, Q4_MXFP4 = 1 } q4_format_t;
+typedef enum { Q4_OUT_F32 = 0, Q4_OUT_BF16 = 1 } q4_dtype_t;
+
+#define Q4_SCORE_TILE_ROWS 64
+#define Q4_MAX_TOPK 1024
+
+/* (host) message for the last non-OK status returned in this thread. */
+const char *q4_last_error(void);
+/* (host) library ABI version (major * 100 + minor). */
+int32_t q4_version(void);
+
+/* ---------------------------------------------------------------- quantizer
+ * Workspace bytes needed by nvfp4_quantize / mxfp4_quantize for this shape
+ * (fp64 partial channel sums, the amax word and the top-k scratch). */
+size_t q4_quantize_workspace_size(int64_t rows, int64_t cols, int32_t fmt);
+
+/* Online NVFP4 activation quantization with per-channel residual statistics
+ * (QUADS section 2.2 "FP4"; section 3.3 Eq. 20, 23, 24).
+ *   x               bf16 [rows][cols]; rows >= 0, cols > 0, cols % 16 == 0.
+ *   tensor_scale_in fp32 [1] or NULL.  NULL: s_t is computed from the tensor's
+ *                   amax inside the call.  Otherwise its value (positive,
+ *                   finite, normal) is used as s_t.
+ *   codes           uint8 [rows][cols/2] (out).   scales uint8 [rows][cols/16] (out).
+ *   tensor_scale_out fp32 [1] (out): the s_t used.
+ *   chan_score      fp64 [cols] (out) or NULL: sum of squared residuals.
+ *   topk            0 <= topk <= min(cols, Q4_MAX_TOPK); 0 skips the selection.
+ *   chan_idx        int32 [topk] (out), ascending channel indices; NULL iff topk == 0.
+ * rows == 0 is valid: s_t = 1 (or the supplied value), scores are 0 and the
+ * selection is channels 0..topk-1. */
+q4_status_t nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols,
+                           const float *tensor_scale_in, uint8_t *codes, uint8_t *scales,
+                           float *tensor_scale_out, double *chan_score, int32_t topk,
+                           int32_t *chan_idx, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* MXFP4 variant: cols % 32 == 0; scales uint8 [rows][cols/32] E8M0; no tensor
+ * scale.  Residual statistics and selection as nvfp4_quantize. */
+q4_status_t mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
+                           uint8_t *scales, double *chan_score, int32_t topk, int32_t *chan_idx,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Channel selection alone (section 3.3 Eq. 24) from fp64 scores [cols]:
+ * the topk largest, ties to the smaller index, written ascending to chan_idx. */
+size_t q4_select_workspace_size(int64_t cols);
+q4_status_t q4_select_channels(const double *chan_score, int64_t cols, int32_t topk,
+                               int32_t *chan_idx, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/* Residual gather (section 3.3 Eq. 21 on the selected channels):
+ * R[i][t] = bf16_RNE(r[i][S_t]) for t < k, and 0 for k <= t < ld_r, where r is
+ * the fp32 residual of x against its quantized form (codes/scales/tensor scale;
+ * tensor_scale must be NULL for MXFP4).  R is bf16 [rows][ld_r], ld_r >= k.
+ * Out-of-range channel indices are clamped into [0, cols). */
+q4_status_t q4_residual_gather(int32_t fmt, const uint16_t *x, int64_t rows, int64_t cols,
+                               const uint8_t *codes, const uint8_t *scales,
+                               const float *tensor_scale, const int32_t *chan_idx, int32_t k,
+                               uint16_t *R, int64_t ld_r, void *stream);
+
+/* ---------------------------------------------------------------- GEMM
+ * W4A4 GEMM (QUADS section 3.3, the native W4A4 product that Eq. 22's remark
+ * keeps on the FP4 path):
+ *   Y[i][j] = s_A s_W sum_k (c sb)_A[i][k] (c sb)_W[j][k]
+ * A is M x K (activations), W is N x K (weights, "out x in"); both in `fmt`
+ * with the layouts above.  a_tensor_scale / w_tensor_scale: fp32 [1] for
+ * NVFP4, NULL for MXFP4.  Y is [M][N] fp32 or bf16 (round to nearest even).
+ * Shapes: M >= 0, N >= 0, K > 0 with K % 32 == 0. */
+q4_status_t w4a4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_t *a_codes,
+                      const uint8_t *a_scales, const float *a_tensor_scale,
+                      const uint8_t *w_codes, const uint8_t *w_scales,
+                      const float *w_tensor_scale, void *Y, int32_t y_dtype, void *stream);
+
+/* W4A4 GEMM with Residual Activation Compensation (section 3.3 Eq. 21-22):
+ *   Y = W4A4(A, W) + sum_{t<k} R[i][t] W_hi[j][S_t]
+ * with R the bf16 residual of x on the channel set S (q4_residual_gather) and
+ * W_hi the bf16 weight.  Both extra operands are accumulated into the same
+ * fp32 tile as the W4A4 product, after its tensor scaling.
+ *   x       bf16 [M][K], the activation that produced A.
+ *   w_hi_t  bf16 [K][N]: the transposed bf16 weight (channel-major), so the
+ *           selected rows S_t are contiguous.
+ *   chan_set int32 [k] ascending unique channels in [0, K) (out-of-range
+ *           entries are clamped); 0 <= k <= min(K, Q4_MAX_TOPK).
+ * k == 0 gives exactly w4a4_gemm. */
+size_t rac_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);
+q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_t *x,
+                     const uint8_t *a_codes, const uint8_t *a_scales,
+                     const float *a_tensor_scale, const uint8_t *w_codes,
+                     const uint8_t *w_scales, const float *w_tensor_scale,
+                     const uint16_t *w_hi_t, const int32_t *chan_set, int32_t k, void *Y,
+                     int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------- MoE
+ * Router (top-k MoE of section 3.3's W13 site): for each token the topk experts
+ * of largest logit (ties to the smaller expert), highest first, and their
+ * weights softmax(selected logits).  logits fp32 [T][E]; 1 <= topk <= min(E, 16);
+ * E <= 1024.  topk_idx int32 [T][topk], topk_w fp32 [T][topk]. */
+q4_status_t q4_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk,
+                         int32_t *topk_idx, float *topk_w, void *stream);
+
+/* Token sort: routed rows (t, s) ordered by (expert, t, s).
+ * perm int32 [T*topk]: perm[r] = t*topk + s of sorted row r; offsets int32
+ * [E+1] (offsets[e] = first sorted row of expert e).  workspace: q4_moe_sort_workspace_size. */
+size_t q4_moe_sort_workspace_size(int64_t T, int32_t E, int32_t topk);
+q4_status_t q4_moe_sort(const int32_t *topk_idx, int64_t T, int32_t E, int32_t topk,
+                        int32_t *perm, int32_t *offsets, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Weight preparation (offline).
+ * q4_transpose_bf16: out[c][r] = in[r][c] for a [rows][cols] bf16 matrix,
+ *   repeated over `batch` stacked matrices.  Used to build W_hi^T.
+ * q4_moe_pack_w13: the logical W13 of each expert, [2F][H] with gate rows
+ *   0..F-1 and up rows F..2F-1, is re-ordered into groups of 32 rows
+ *   [gate 32g..32g+31, up 32g..32g+31] for g = 0..F/32-1 (F % 32 == 0); the
+ *   grouped GEMM's SwiGLU epilogue then finds a gate column and its up column
+ *   in the same tile.  Row order commutes with quantization (blocks run along H). */
+q4_status_t q4_transpose_bf16(const uint16_t *in, int64_t batch, int64_t rows, int64_t cols,
+                              uint16_t *out, void *stream);
+q4_status_t q4_moe_pack_w13(const uint16_t *w13, int32_t E, int32_t F, int32_t H,
+                            uint16_t *out, void *stream);
+
+/* Token-sorted grouped W4A4 + RAC SwiGLU expert layer (configs: top-k MoE).
+ *   tokens     bf16 [T][H]; H % 32 == 0 (MXFP4: % 32; NVFP4 GEMM: % 32).
+ *   topk_idx, topk_w: routing as produced by q4_moe_route.
+ *   w13_*      stacked packed W13 of all experts: rows E*2F (q4_moe_pack_w13
+ *              order), cols H; w13_tensor_scales fp32 [E] (NVFP4) or NULL.
+ *   w2_*       stacked W2: rows E*H, cols F; w2_tensor_scales fp32 [E] or NULL.
+ *   w13_hi_t   bf16 [E][H][2F]: per-expert transpose of the packed bf16 W13.
+ *   w2_hi_t    bf16 [E][F][H]:  per-expert transpose of the bf16 W2.
+ *              Both may be NULL when rac_k == 0.
+ *   rac_k      channels compensated at each of the two activation sites.
+ *   Y          [T][H] fp32 or bf16: y_t = sum_s p_ts out_(t,s), slots in order.
+ * Steps: sort; quantize tokens (one s_t, one selection over T rows); W13 RAC
+ * GEMM over sorted rows with the SwiGLU epilogue h = bf16(silu(g) * u); quantize
+ * h over all T*topk sorted rows (one s_t, one selection); W2 RAC GEMM; combine.
+ * F % 32 == 0, H % 32 == 0.  The workspace holds every intermediate at the
+ * offsets reported by moe_workspace_layout. */
+size_t moe_workspace_size(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F,
+                          int32_t topk, int32_t rac_k);
+/* (host) offsets[0..Q4_MOE_WS_FIELDS-1] in bytes from the workspace base:
+ *   0 perm int32 [T*topk]      1 offsets int32 [E+1]      2 x codes
+ *   3 x scales                 4 x tensor scale fp32      5 x channel set int32 [rac_k]
+ *   6 x residual R bf16 [T][kp] 7 h bf16 [T*topk][F]       8 h codes
+ *   9 h scales                10 h tensor scale fp32     11 h channel set
+ *  12 h residual R bf16 [T*topk][kp]                     13 out fp32 [T*topk][H]
+ *  14 x channel scores fp64 [H]                          15 h channel scores fp64 [F]
+ * kp = rac_k rounded up to a multiple of 32. */
+#define Q4_MOE_WS_FIELDS 16
+q4_status_t moe_workspace_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F,
+                                 int32_t topk, int32_t rac_k, size_t *offsets);
+q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t *tokens, int64_t T, int32_t H,
+                                  const int32_t *topk_idx, const float *topk_w, int32_t topk,
+                                  int32_t E, int32_t F, const uint8_t *w13_codes,
+                                  const uint8_t *w13_scales, const float *w13_tensor_scales,
+                                  const uint8_t *w2_codes, const uint8_t *w2_scales,
+                                  const float *w2_tensor_scales, const uint16_t *w13_hi_t,
+                                  const uint16_t *w2_hi_t, int32_t rac_k, void *Y,
+                                  int32_t y_dtype, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* Q4RAC_H */

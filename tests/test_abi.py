@@ -1,0 +1,82 @@
+"""The C-ABI library loads, exports every entry point of include/q4rac.h and
+rejects bad arguments on the host before any launch (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "q4rac.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import fp4_w4a4_quantized_nvfp4_amd as m
+    return m.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 19
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_header():
+    import fp4_w4a4_quantized_nvfp4_amd as m
+    assert set(_declared()) <= set(m._SIGS)
+
+
+def _err(L):
+    return L.q4_last_error().decode()
+
+
+def test_shape_and_pointer_errors(L):
+    fake = C.c_void_p(0x100000)          # aligned, never dereferenced on error paths
+    odd = C.c_void_p(0x100004)
+    # cols not a multiple of 16
+    assert L.nvfp4_quantize(fake, 4, 24, None, fake, fake, fake, None, 0, None, fake, 1 << 30, None) == 2
+    assert "cols % 16" in _err(L)
+    # topk beyond cols
+    assert L.nvfp4_quantize(fake, 4, 32, None, fake, fake, fake, None, 33, fake, fake, 1 << 30, None) == 1
+    # misaligned input
+    assert L.nvfp4_quantize(odd, 4, 32, None, fake, fake, fake, None, 0, None, fake, 1 << 30, None) == 3
+    # workspace too small
+    assert L.nvfp4_quantize(fake, 4, 32, None, fake, fake, fake, None, 0, None, fake, 8, None) == 4
+    # MXFP4 needs cols % 32
+    assert L.mxfp4_quantize(fake, 4, 48, fake, fake, None, 0, None, fake, 1 << 30, None) == 2
+    # GEMM: K % 32, bad format, missing tensor scale, MXFP4 with tensor scale
+    assert L.w4a4_gemm(0, 8, 8, 48, fake, fake, fake, fake, fake, fake, fake, 0, None) == 2
+    assert L.w4a4_gemm(7, 8, 8, 64, fake, fake, fake, fake, fake, fake, fake, 0, None) == 1
+    assert L.w4a4_gemm(0, 8, 8, 64, fake, fake, None, fake, fake, fake, fake, 0, None) == 1
+    assert L.w4a4_gemm(1, 8, 8, 64, fake, fake, fake, fake, fake, None, fake, 0, None) == 1
+    assert L.w4a4_gemm(0, 8, 8, 64, fake, fake, fake, fake, fake, fake, fake, 5, None) == 1
+    # RAC: k > K, missing workspace
+    assert L.rac_gemm(0, 8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, fake, 65,
+                      fake, 0, fake, 1 << 30, None) == 1
+    assert L.rac_gemm(0, 8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, fake, 16,
+                      fake, 0, None, 0, None) == 4
+    # MoE: bad E, F % 32, topk > E
+    assert L.q4_moe_route(fake, 4, 0, 1, fake, fake, None) == 2
+    assert L.q4_moe_route(fake, 4, 8, 9, fake, fake, None) == 1
+    assert L.moe_w4a4_grouped_gemm(0, fake, 4, 64, fake, fake, 2, 4, 48, fake, fake, fake, fake,
+                                   fake, fake, fake, fake, 0, fake, 1, fake, 1 << 30, None) == 2
+    assert L.q4_moe_pack_w13(fake, 2, 40, 64, fake, None) == 2
+
+
+def test_workspace_sizes(L):
+    assert L.q4_quantize_workspace_size(16384, 7168, 0) >= 256 * 7168 * 8
+    assert L.rac_gemm_workspace_size(8192, 14336, 4096, 128) >= (8192 + 14336) * 128 * 2
+    offs = (C.c_size_t * 16)()
+    assert L.moe_workspace_layout(0, 8192, 128, 2048, 768, 8, 64, offs) == 0
+    vals = list(offs)
+    assert vals == sorted(vals) and len(set(vals)) == 16
+    assert L.moe_workspace_size(0, 8192, 128, 2048, 768, 8, 64) > vals[-1]

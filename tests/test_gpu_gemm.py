@@ -1,0 +1,136 @@
+"""GPU parity of the W4A4 GEMM and the residual-compensated GEMM against the
+fp64 CPU oracle on the same quantized operands."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import bf16_bits_from_f32, make_inputs
+from tests.gpu_util import GEMM_TOL, check_bf16_output, dev, gemm_rel_err, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def q4():
+    import fp4_w4a4_quantized_nvfp4_amd as m
+    return m
+
+
+def _bits(a):
+    return bf16_bits_from_f32(np.asarray(a, dtype=np.float32))
+
+
+PAGE_GRID = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def _exact_operand(rng, rows, cols, scales=(0.5, 1.0, 2.0)):
+    sb = rng.choice(scales, size=(rows, cols // 16))
+    mag = rng.integers(0, 8, size=(rows, cols))
+    mag[:, ::16] = 7
+    sign = rng.random((rows, cols)) < 0.5
+    val = np.array(PAGE_GRID)[mag] * np.repeat(sb, 16, axis=1) * np.where(sign, -1, 1)
+    return _bits(val.astype(np.float32))
+
+
+def _quant_pair(m, xb, wb, fmt="nv", ts=None):
+    x, w = dev(xb), dev(wb)
+    if fmt == "mx":
+        return x, m.mxfp4_quantize(x), m.mxfp4_quantize(w), oracle.mxfp4_quantize(xb), oracle.mxfp4_quantize(wb)
+    tin = None if ts is None else torch.tensor([ts], dtype=torch.float32, device="cuda")
+    A = m.nvfp4_quantize(x, tensor_scale_in=tin)
+    W = m.nvfp4_quantize(w, tensor_scale_in=tin)
+    return x, A, W, oracle.nvfp4_quantize(xb, tensor_scale=ts), oracle.nvfp4_quantize(wb, tensor_scale=ts)
+
+
+def test_exact_special_case_bit_identical():
+    say("gemm exact special case")
+    m = q4()
+    rng = np.random.default_rng(11)
+    xb = _exact_operand(rng, 300, 512)
+    wb = _exact_operand(rng, 200, 512)
+    x, A, W, Ao, Wo = _quant_pair(m, xb, wb, ts=1.0)
+    Y = host(m.w4a4_gemm(A, W))
+    ref = oracle.w4a4_gemm(Ao, Wo)
+    assert np.array_equal(Y.astype(np.float64), ref)
+
+
+def _check_rac(xb, wb, k, out_dtype, fmt="nv"):
+    say(f"rac parity x={xb.shape} w={wb.shape} k={k} out={out_dtype} fmt={fmt}")
+    m = q4()
+    x, A, W, Ao, Wo = _quant_pair(m, xb, wb, fmt)
+    w_hi_t = m.q4_transpose_bf16(dev(wb))
+    if k:
+        qs = m.mxfp4_quantize(x, topk=k) if fmt == "mx" else m.nvfp4_quantize(x, topk=k)
+        S = qs["chan_idx"]
+        So = oracle.select_topk(oracle.channel_scores(Ao.resid), k)
+        assert np.array_equal(host(S), So)
+    else:
+        S, So = None, np.zeros(0, dtype=np.int32)
+    Y = m.rac_gemm(x, A, W, w_hi_t, S, out_dtype=out_dtype)
+    Ro = oracle.residual_gather(Ao.resid, So)
+    ref = oracle.rac_gemm(Ao, Wo, Ro, wb, So)
+    if out_dtype == m.OUT_F32:
+        err = gemm_rel_err(host(Y), ref)
+        say(f"  max rel err {err:.3e}")
+        assert err <= GEMM_TOL
+    else:
+        check_bf16_output(host(Y), ref)
+    return Y
+
+
+def test_small_dense_workload_rac():
+    d = make_inputs("dense_64x512")
+    _check_rac(d["x"], d["w"], 16, 0)
+
+
+def test_k0_equals_w4a4():
+    m = q4()
+    d = make_inputs("dense_64x512")
+    x, A, W, _, _ = _quant_pair(m, d["x"], d["w"])
+    Y0 = m.w4a4_gemm(A, W)
+    Y1 = m.rac_gemm(x, A, W, None, None)
+    torch.cuda.synchronize()
+    assert torch.equal(Y0, Y1)
+
+
+@pytest.mark.parametrize("M,N,K,k", [(300, 200, 96, 20), (1, 1, 32, 1), (257, 129, 160, 32),
+                                     (513, 384, 1024, 100)])
+def test_ragged_shapes(M, N, K, k):
+    rng = np.random.default_rng(M + N + K)
+    xb = _bits(rng.standard_t(3, size=(M, K)).astype(np.float32))
+    wb = _bits((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+    _check_rac(xb, wb, k, 0)
+    _check_rac(xb, wb, k, 1)
+
+
+def test_dense_prefill_workload_sampled():
+    """8192 x 14336 x 4096, k = 128, bf16 output: quantization bit-exact on the
+    full x, W sampled rows; GEMM checked on 96 sampled output rows."""
+    m = q4()
+    d = make_inputs("dense_8192x14336x4096")
+    xb, wb = d["x"], d["w"]
+    say("prefill workload: quantize on GPU")
+    x, w = dev(xb), dev(wb)
+    A = m.nvfp4_quantize(x, topk=128)
+    W = m.prepare_weight(w)
+    Y = m.rac_gemm(x, A, W, W["w_hi_t"], A["chan_idx"], out_dtype=m.OUT_BF16)
+    torch.cuda.synchronize()
+    Ao = oracle.nvfp4_quantize(xb)
+    assert np.array_equal(host(A["codes"]), Ao.codes)
+    assert np.array_equal(host(A["scales"]), Ao.scales)
+    So = oracle.select_topk(oracle.channel_scores(Ao.resid), 128)
+    assert np.array_equal(host(A["chan_idx"]), So)
+    rng = np.random.default_rng(3)
+    wrows = np.sort(rng.choice(wb.shape[0], 512, replace=False))
+    Wo_s = oracle.nvfp4_quantize(wb[wrows], tensor_scale=float(host(W["tensor_scale"])[0]))
+    assert np.array_equal(host(W["codes"])[wrows], Wo_s.codes)
+    assert np.array_equal(host(W["scales"])[wrows], Wo_s.scales)
+    Wo = oracle.nvfp4_quantize(wb)
+    assert np.float32(Wo.tensor_scale) == host(W["tensor_scale"])[0]
+    rows = np.sort(rng.choice(xb.shape[0], 96, replace=False))
+    Ro = oracle.residual_gather(Ao.resid, So)
+    sub = oracle.QuantResult("nvfp4", Ao.codes[rows], Ao.scales[rows], Ao.tensor_scale,
+                             Ao.resid[rows], Ao.mag[rows], Ao.sign[rows])
+    ref = oracle.rac_gemm(sub, Wo, Ro[rows], wb, So)
+    check_bf16_output(host(Y)[rows], ref)
+    say("prefill workload sampled parity ok")
