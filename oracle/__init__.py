@@ -25,7 +25,8 @@ Learning for MoE via QUantization-error Alignment across Dual Sides"):
 Every rounding decision is taken by comparing exact fp64 products (all
 operands have few significant bits), never by a rounded quotient.  Sums of
 squares follow a fixed order that is part of the definition (rows ascending
-inside tiles of 64 rows, tiles ascending).
+inside tiles of 32 rows, tiles ascending inside groups of 8 tiles, groups
+ascending).
 """
 from .formats import (  # noqa: F401
     E2M1_MAGNITUDES,
@@ -39,6 +40,7 @@ from .formats import (  # noqa: F401
     f64_to_f32,
 )
 from .quant import (  # noqa: F401
+    SCORE_GROUP_TILES,
     SCORE_TILE_ROWS,
     QuantResult,
     block_values,

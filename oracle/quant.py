@@ -26,9 +26,11 @@ Definitions (QUADS page, arXiv 2607.15810):
   residual r = x - dequant(quant(x)) = -(Eq. 20) rounded once to fp32.
 * Section 3.3, Eq. 23: s_j = ||r[:, j]||_2 over the current token batch.  The
   squared norm is accumulated in fp64 (each r^2 is exact in fp64) in a fixed
-  order: rows ascending inside tiles of SCORE_TILE_ROWS rows, then the tile
-  sums ascending.  The order is part of the definition so that the scores, and
-  the selection that depends on them, have one exact value.
+  three-level order: rows ascending inside tiles of SCORE_TILE_ROWS rows; tile
+  sums ascending inside groups of SCORE_GROUP_TILES tiles; group sums
+  ascending.  Every level starts from zero.  The order is part of the
+  definition so that the scores, and the selection that depends on them, have
+  one exact value.
 * Section 3.3, Eq. 24: the selected set S is the k channels with the largest
   score (ties -> smaller channel index), listed in ascending channel order.
   k is an absolute count.
@@ -47,7 +49,8 @@ import numpy as np
 
 from .formats import E2M1_MAGNITUDES, E4M3_VALUES, bf16_bits_to_f64, f32_to_bf16_bits
 
-SCORE_TILE_ROWS = 64
+SCORE_TILE_ROWS = 32
+SCORE_GROUP_TILES = 8
 
 _E2M1 = np.array(E2M1_MAGNITUDES, dtype=np.float64)
 # midpoints between consecutive E2M1 magnitudes and whether a tie goes up
@@ -218,16 +221,21 @@ def dequantize(q: QuantResult) -> np.ndarray:
     return block_values(q.codes, q.scales, q.fmt) * float(q.tensor_scale)
 
 
-def channel_scores(resid: np.ndarray, tile_rows: int = SCORE_TILE_ROWS) -> np.ndarray:
-    """Sum over tokens of r^2 per channel, fp64, in the fixed two-level order."""
+def channel_scores(resid: np.ndarray, tile_rows: int = SCORE_TILE_ROWS,
+                   group_tiles: int = SCORE_GROUP_TILES) -> np.ndarray:
+    """Sum over tokens of r^2 per channel, fp64, in the fixed three-level order."""
     r2 = resid.astype(np.float64) ** 2                  # exact: 24-bit mantissa squared
     M, K = r2.shape
     total = np.zeros(K, dtype=np.float64)
-    for t0 in range(0, M, tile_rows):
-        part = np.zeros(K, dtype=np.float64)
-        for i in range(t0, min(M, t0 + tile_rows)):
-            part += r2[i]                               # rows ascending
-        total += part                                   # tiles ascending
+    group_rows = tile_rows * group_tiles
+    for g0 in range(0, M, group_rows):
+        group = np.zeros(K, dtype=np.float64)
+        for t0 in range(g0, min(M, g0 + group_rows), tile_rows):
+            tile = np.zeros(K, dtype=np.float64)
+            for i in range(t0, min(M, t0 + tile_rows)):
+                tile += r2[i]                           # rows ascending
+            group += tile                               # tiles ascending
+        total += group                                  # groups ascending
     return total
 
 

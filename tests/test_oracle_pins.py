@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from oracle.quant import SCORE_TILE_ROWS
+from oracle.quant import SCORE_GROUP_TILES, SCORE_TILE_ROWS
 from workloads import bf16_bits_from_f32, f32_from_bf16_bits, make_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -257,10 +257,26 @@ def test_scores_exact_and_topk_brute_force():
         assert oracle.select_topk(s, k).tolist() == brute
     # ties -> smaller index
     assert oracle.select_topk(np.array([1.0, 2.0, 2.0, 0.0, 2.0]), 2).tolist() == [1, 2]
-    # the summation order is tiles of SCORE_TILE_ROWS rows, then tiles
-    r = np.zeros((2 * SCORE_TILE_ROWS, 1), dtype=np.float32)
-    r[0, 0], r[1, 0], r[SCORE_TILE_ROWS, 0] = 1.0, 2.0 ** -27, 2.0 ** -27
-    # tile 0 sum = 1 + 2^-54 -> 1 (rounded); + tile 1 (2^-54) -> 1
+    # the summation order: rows inside 32-row tiles, tiles inside 8-tile
+    # groups, then groups.  (2^-27)^2 = 2^-54 is lost when added alone onto 1,
+    # but three of them summed first give 1.5 * 2^-53, which survives.
+    T, G = SCORE_TILE_ROWS, SCORE_TILE_ROWS * SCORE_GROUP_TILES
+    e = np.float32(2.0 ** -27)
+    r = np.zeros((2 * G, 1), dtype=np.float32)
+    r[0, 0] = 1.0
+    r[1:4, 0] = e                      # same tile as the 1: each lost in turn
+    assert oracle.channel_scores(r)[0] == 1.0
+    r = np.zeros((2 * G, 1), dtype=np.float32)
+    r[0, 0] = 1.0
+    r[T:T + 3, 0] = e                  # tile 1 sums them before meeting the 1
+    assert oracle.channel_scores(r)[0] == 1.0 + 2.0 ** -52
+    r = np.zeros((2 * G, 1), dtype=np.float32)
+    r[0, 0] = 1.0
+    r[[G, G + T, G + 2 * T], 0] = e    # one per tile of group 1: the group sums first
+    assert oracle.channel_scores(r)[0] == 1.0 + 2.0 ** -52
+    r = np.zeros((G, 1), dtype=np.float32)
+    r[0, 0] = 1.0
+    r[[T, 2 * T, 3 * T], 0] = e        # one per tile of group 0: each tile meets the 1
     assert oracle.channel_scores(r)[0] == 1.0
 
 
