@@ -344,6 +344,241 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dense kernel with 256 x 256 tiles: four waves of 128 x 128 (4 x 4 MFMA
+// tiles, accumulators in AGPRs, one wave per SIMD).  Every decoded fragment
+// feeds four MFMAs, so decode costs four VALU instructions per MFMA.
+namespace big {
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int CB = BK / 2;
+constexpr int B_CODE_OFF = BM * CB;                 // 16384
+constexpr int A_SC_OFF = B_CODE_OFF + BN * CB;      // 32768
+constexpr int B_SC_OFF = A_SC_OFF + BM * 16;        // 36864 (fp16 scales, 8 per row)
+constexpr int STAGE = B_SC_OFF + BN * 16;           // 40960
+
+__device__ __forceinline__ int swzb(int row, int piece) {
+  return row * CB + ((piece ^ ((row >> 2) & 3)) << 4);
+}
+
+// four E4M3 bytes -> two dwords of fp16 pairs (exact)
+__device__ __forceinline__ uint2 e4m3x4_to_f16(uint32_t w) {
+  const uint32_t t = w & 0x78787878u;
+  const bool any_sub = ((t - 0x01010101u) & ~t & 0x80808080u) != 0u;   // some exponent field 0
+  uint2 r;
+  if (!any_sub) {
+    const uint32_t lo2 = __builtin_amdgcn_perm(0u, w, 0x0c010c00u);     // b0 | b1 << 16
+    const uint32_t hi2 = __builtin_amdgcn_perm(0u, w, 0x0c030c02u);     // b2 | b3 << 16
+    r.x = (lo2 << 7) + 0x20002000u;
+    r.y = (hi2 << 7) + 0x20002000u;
+  } else {
+    r.x = e4m3_to_f16_bits(w & 255u) | (e4m3_to_f16_bits((w >> 8) & 255u) << 16);
+    r.y = e4m3_to_f16_bits((w >> 16) & 255u) | (e4m3_to_f16_bits(w >> 24) << 16);
+  }
+  return r;
+}
+
+template <bool FULLK>
+__global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int K = g.K;
+  const int64_t N = g.N;
+
+  const int nbm = (int)((g.M + BM - 1) / BM), nbn = (int)((N + BN - 1) / BN);
+  const int nb = nbm * nbn;
+  int b = blockIdx.x;
+  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);   // contiguous tile range per XCD
+  const int GM = 4;
+  const int group = b / (GM * nbn);
+  const int first = group * GM;
+  const int gsz = min(nbm - first, GM);
+  const int in = b - group * GM * nbn;
+  const int64_t m0 = (int64_t)(first + in % gsz) * BM;
+  const int64_t n0 = (int64_t)(in / gsz) * BN;
+  const int64_t m_end = g.M;
+
+  const uint32_t cstride = (uint32_t)(K / 2), sstride = (uint32_t)(K / 16);
+  // 32-bit offsets from the (uniform) operand bases keep the staging state small
+  const uint8_t* const a_base = g.a_codes + (size_t)m0 * cstride;
+  const uint8_t* const b_base = g.w_codes + (size_t)n0 * cstride;
+  uint32_t a_off[4], b_off[4];
+  uint32_t ab_ok = 0;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int q = it * 256 + tid;
+    const int r = q >> 2;
+    const bool aok = m0 + r < m_end, bok = n0 + r < N;
+    ab_ok |= (aok ? 1u : 0u) << it;
+    ab_ok |= (bok ? 1u : 0u) << (4 + it);
+    a_off[it] = (aok ? (uint32_t)r : 0u) * cstride + (uint32_t)(q & 3) * 16u;
+    b_off[it] = (bok ? (uint32_t)r : 0u) * cstride + (uint32_t)(q & 3) * 16u;
+  }
+  const bool as_ok = m0 + tid < m_end, bs_ok = n0 + tid < N;
+  const uint8_t* const as_base = g.a_scales + (size_t)m0 * sstride;
+  const uint8_t* const bs_base = g.w_scales + (size_t)n0 * sstride;
+  const uint32_t as_off = (as_ok ? (uint32_t)tid : 0u) * sstride;
+  const uint32_t bs_off = (bs_ok ? (uint32_t)tid : 0u) * sstride;
+
+  uint4 pa[4], pb[4];
+  uint2 psa, psb;
+  auto load = [&](int kc) {
+    const int k0 = kc * BK;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int kel = k0 + 32 * ((it * 256 + tid) & 3);
+      pa[it] = (((ab_ok >> it) & 1u) && (FULLK || kel < K))
+                   ? *(const uint4*)(a_base + a_off[it] + k0 / 2) : make_uint4(0, 0, 0, 0);
+      pb[it] = (((ab_ok >> (4 + it)) & 1u) && (FULLK || kel < K))
+                   ? *(const uint4*)(b_base + b_off[it] + k0 / 2) : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (FULLK) {
+      psa = as_ok ? *(const uint2*)(as_base + as_off + k0 / 16) : make_uint2(0, 0);
+      psb = bs_ok ? *(const uint2*)(bs_base + bs_off + k0 / 16) : make_uint2(0, 0);
+    } else {
+      uint32_t sa4[4] = {0, 0, 0, 0}, sb4[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (k0 + 32 * q < K) {
+          if (as_ok) sa4[q] = *(const uint16_t*)(as_base + as_off + k0 / 16 + 2 * q);
+          if (bs_ok) sb4[q] = *(const uint16_t*)(bs_base + bs_off + k0 / 16 + 2 * q);
+        }
+      }
+      psa = make_uint2(sa4[0] | (sa4[1] << 16), sa4[2] | (sa4[3] << 16));
+      psb = make_uint2(sb4[0] | (sb4[1] << 16), sb4[2] | (sb4[3] << 16));
+    }
+  };
+  auto store = [&](int stg) {
+    uint8_t* base = smem + stg * STAGE;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int q = it * 256 + tid;
+      *(uint4*)(base + swzb(q >> 2, q & 3)) = pa[it];
+      *(uint4*)(base + B_CODE_OFF + swzb(q >> 2, q & 3)) = pb[it];
+    }
+    const uint2 a0 = e4m3x4_to_f16(psa.x), a1 = e4m3x4_to_f16(psa.y);
+    const uint2 b0 = e4m3x4_to_f16(psb.x), b1 = e4m3x4_to_f16(psb.y);
+    *(uint4*)(base + A_SC_OFF + tid * 16) = make_uint4(a0.x, a0.y, a1.x, a1.y);
+    *(uint4*)(base + B_SC_OFF + tid * 16) = make_uint4(b0.x, b0.y, b1.x, b1.y);
+  };
+
+  f32x16v acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  auto compute = [&](int stg) {
+    const uint8_t* base = smem + stg * STAGE;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int p = 2 * h + s2;
+      uint4 ra[4], rb[4];
+      uint32_t sa[4], sb[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const int row = wm * 128 + mi * 32 + l32;
+        ra[mi] = *(const uint4*)(base + swzb(row, p));
+        sa[mi] = *(const uint32_t*)(base + A_SC_OFF + row * 16 + h * 8 + s2 * 4);
+      }
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int row = wn * 128 + ni * 32 + l32;
+        rb[ni] = *(const uint4*)(base + B_CODE_OFF + swzb(row, p));
+        sb[ni] = *(const uint32_t*)(base + B_SC_OFF + row * 16 + h * 8 + s2 * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        half8v af[4], bf[4];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          af[mi] = decode8(word(ra[mi], j), j < 2 ? dup_lo(sa[mi]) : dup_hi(sa[mi]));
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          bf[ni] = decode8(word(rb[ni], j), j < 2 ? dup_lo(sb[ni]) : dup_hi(sb[ni]));
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni] =
+                __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+      }
+    }
+  };
+
+  const int nk = (K + BK - 1) / BK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kc = 0; kc < nk; ++kc) {
+    if (kc + 1 < nk) load(kc + 1);
+    compute(kc & 1);
+    if (kc + 1 < nk) store((kc + 1) & 1);
+    __syncthreads();
+  }
+
+  const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[0] : 1.0f;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= alpha;
+
+  if (g.kp > 0 && g.r_res) {
+    const uint16_t* rrow[4];
+    const uint16_t* wrow[4];
+    bool rok[4], wok[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t rr = m0 + wm * 128 + q * 32 + l32;
+      rok[q] = rr < m_end;
+      rrow[q] = g.r_res + (rok[q] ? rr : 0) * g.ld_r + 8 * h;
+      const int64_t cc = n0 + wn * 128 + q * 32 + l32;
+      wok[q] = cc < N;
+      wrow[q] = g.w_sel + (wok[q] ? cc : 0) * g.kp + 8 * h;
+    }
+    for (int kt = 0; kt < g.kp; kt += 16) {
+      bf16x8v af[4], bf[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        af[q] = __builtin_bit_cast(bf16x8v, rok[q] ? *(const uint4*)(rrow[q] + kt) : make_uint4(0, 0, 0, 0));
+        bf[q] = __builtin_bit_cast(bf16x8v, wok[q] ? *(const uint4*)(wrow[q] + kt) : make_uint4(0, 0, 0, 0));
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (row >= m_end) continue;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int64_t col = n0 + wn * 128 + ni * 32 + l32;
+        if (col >= N) continue;
+        const float v = acc[mi][ni][r];
+        if (g.y_bf16)
+          ((uint16_t*)g.Y)[row * g.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
+        else
+          ((float*)g.Y)[row * g.ldy + col] = v;
+      }
+    }
+  }
+}
+}  // namespace big
+
 template <bool FULLK, bool GROUPED>
 hipError_t launch_t(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
   const int64_t nbn = (g.N + BN - 1) / BN;
@@ -367,6 +602,14 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
   if (g.mx) return launch_mx_gemm(g, max_mtiles, stream);
   const bool fullk = (g.K % BK) == 0;
   const bool grouped = g.tiles != nullptr;
+  if (!grouped && g.epilogue == kEpiStore && g.M >= 512 && g.N >= 512) {
+    const int64_t nb = ((g.M + big::BM - 1) / big::BM) * ((g.N + big::BN - 1) / big::BN);
+    if (fullk)
+      hipLaunchKernelGGL(big::gemm_nvfp4_big_kernel<true>, dim3((unsigned)nb), dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL(big::gemm_nvfp4_big_kernel<false>, dim3((unsigned)nb), dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
   if (fullk)
     return grouped ? launch_t<true, true>(g, max_mtiles, stream)
                    : launch_t<true, false>(g, max_mtiles, stream);

@@ -17,7 +17,8 @@ typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef float f32x16v __attribute__((ext_vector_type(16)));
 typedef int i32x8v __attribute__((ext_vector_type(8)));
 
-constexpr int kScoreTileRows = 64;   // rows summed in order before tile sums combine
+constexpr int kScoreTileRows = 32;   // rows summed in order into one tile sum
+constexpr int kScoreGroupTiles = 8;  // tile sums added in order into one group sum
 
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

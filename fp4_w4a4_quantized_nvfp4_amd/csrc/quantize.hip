@@ -22,20 +22,24 @@ __device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t w) {
   return lo > hi ? lo : hi;
 }
 
-// max |x| as a bf16 bit pattern (non-negative bf16 order is integer order);
-// order-independent, so the atomic combine is deterministic.
+// Per-workgroup max |x| as a bf16 bit pattern (non-negative bf16 order is
+// integer order).  Each workgroup writes its own slot; the quantize kernel
+// reduces the slots, so no atomics are involved and the result is exact.
+constexpr int kAmaxBlocks = 1024;
+
 __global__ __launch_bounds__(256) void amax_kernel(const uint4* __restrict__ x, int64_t n16,
                                                    uint32_t* __restrict__ out) {
   uint32_t m = 0;
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    uint4 v0 = x[i], v1 = x[i + stride], v2 = x[i + 2 * stride], v3 = x[i + 3 * stride];
-    uint32_t a = max(max(absmax_bf16x2(v0.x), absmax_bf16x2(v0.y)), max(absmax_bf16x2(v0.z), absmax_bf16x2(v0.w)));
-    uint32_t b = max(max(absmax_bf16x2(v1.x), absmax_bf16x2(v1.y)), max(absmax_bf16x2(v1.z), absmax_bf16x2(v1.w)));
-    uint32_t c = max(max(absmax_bf16x2(v2.x), absmax_bf16x2(v2.y)), max(absmax_bf16x2(v2.z), absmax_bf16x2(v2.w)));
-    uint32_t d = max(max(absmax_bf16x2(v3.x), absmax_bf16x2(v3.y)), max(absmax_bf16x2(v3.z), absmax_bf16x2(v3.w)));
-    m = max(m, max(max(a, b), max(c, d)));
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = x[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      m = max(m, max(max(absmax_bf16x2(v[u].x), absmax_bf16x2(v[u].y)),
+                     max(absmax_bf16x2(v[u].z), absmax_bf16x2(v[u].w))));
   }
   for (; i < n16; i += stride) {
     uint4 v = x[i];
@@ -45,10 +49,7 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint4* __restrict__ x, 
   __shared__ uint32_t red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    m = max(max(red[0], red[1]), max(red[2], red[3]));
-    if (m) atomicMax(out, m);
-  }
+  if (threadIdx.x == 0) out[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
 }
 
 // ====================================================================== quantize
@@ -57,46 +58,98 @@ struct QuantKArgs {
   int64_t rows;
   int32_t cols;
   int32_t nstrips;      // ceil(cols / 512)
-  int64_t ntiles;       // ceil(rows / 64)
+  int64_t ngroups;      // ceil(rows / 256)
   const float* ts_in;   // NVFP4 supplied tensor scale or null
-  const uint32_t* amax; // NVFP4 amax (bf16 bits) when ts_in is null
+  const uint32_t* amax; // NVFP4 per-workgroup amax slots (bf16 bits) when ts_in is null
+  int32_t namax;        // number of slots
   uint8_t* codes;
   uint8_t* scales;
   float* ts_out;
-  double* partial;      // [ntiles][cols]
-  int32_t reverse;      // process tiles last-to-first (reuse of the last-level cache)
+  double* partial;      // [ngroups][cols]
+  int32_t reverse;      // process groups last-to-first (reuse of the last-level cache)
 };
 
-__device__ __forceinline__ float nvfp4_tensor_scale_dev(const QuantKArgs& a) {
+// tensor scale of the launch; every thread of the workgroup must call it
+__device__ float nvfp4_tensor_scale_dev(const QuantKArgs& a, uint32_t* red) {
   if (a.ts_in) return a.ts_in[0];
-  float am = __uint_as_float(a.amax[0] << 16);
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < a.namax; i += blockDim.x) m = max(m, a.amax[i]);
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) m = max(m, red[w]);
+  float am = __uint_as_float(m << 16);
   // RN32(amax / 2688): the fp64 quotient is never an fp32 midpoint
   // (2688 = 21 * 2^7, amax has 8 significant bits), so one more rounding to
   // fp32 gives the correctly rounded quotient.
   return am == 0.0f ? 1.0f : (float)((double)am / 2688.0);
 }
 
-// One wave per (64-row tile, 512-channel strip); lane l owns channels
-// strip*512 + 8l .. +7 and walks the tile's rows in order, so its fp64 sums of
-// squared residuals follow the fixed row order of the definition.
+// lane l <- lane l^1 / l^2 inside a quad (DPP quad permutes)
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+
+// E4M3 rounding of u = a / D for a block amax a = (1 + ma/128) 2^ea (a normal
+// bf16) and D = 6 s_t = Dp 2^eDp, Dp in [1, 2): the mantissa decision depends
+// on ma alone, so one exact table per launch covers every normal case.
+// Entry = E4M3 mantissa m (3 bits) | (exponent adjust + 1) << 3.
+// The comparisons num vs Dp * (17 + 2j) / 16 are exact in fp64 (<= 31 bits).
+__device__ uint32_t e4m3_mantissa_entry(int ma, double Dp) {
+  const double A = 1.0 + ma / 128.0;
+  int adj = 0;
+  double num = A;
+  if (A < Dp) {
+    adj = -1;
+    num = 2.0 * A;
+  }
+  int m = 0;
+  for (int j = 0; j < 8; ++j) {
+    const double t = Dp * (1.0 + (2 * j + 1) / 16.0);
+    if (num > t || (num == t && ((j + 1) & 1) == 0)) m = j + 1;   // ties to even mantissa
+  }
+  if (m == 8) {
+    m = 0;
+    adj += 1;
+  }
+  return (uint32_t)(m | ((adj + 1) << 3));
+}
+
+// One workgroup = 8 waves = one 256-row group of one 512-channel strip; wave w
+// owns the 32-row tile w of the group, lane l owns channels strip*512 + 8l..+7.
+// Every lane sums its squared residuals over its tile's rows in order; the
+// eight tile sums are then added in tile order through LDS, giving one fp64
+// partial per (group, channel).
 template <bool MX>
-__global__ __launch_bounds__(256) void quantize_kernel(QuantKArgs a) {
-  const int lane = threadIdx.x & 63;
-  int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t nunits = a.ntiles * a.nstrips;
-  if (unit >= nunits) return;
-  if (a.reverse) unit = nunits - 1 - unit;
-  const int64_t tile = unit / a.nstrips;
-  const int strip = (int)(unit % a.nstrips);
+__global__ __launch_bounds__(512) void quantize_kernel(QuantKArgs a) {
+  __shared__ uint8_t tab[128];
+  __shared__ uint32_t red[16];
+  __shared__ double part[kScoreGroupTiles][64][8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t wg = blockIdx.x;
+  const int64_t nwg = a.ngroups * a.nstrips;
+  if (a.reverse) wg = nwg - 1 - wg;
+  const int64_t group = wg / a.nstrips;
+  const int strip = (int)(wg % a.nstrips);
   const int cols = a.cols;
   const int col0 = strip * 512 + lane * 8;
   const bool active = col0 < cols;
 
   float st = 1.0f;
+  int eDp = 0;
   if constexpr (!MX) {
-    st = nvfp4_tensor_scale_dev(a);
+    st = nvfp4_tensor_scale_dev(a, red);
     if (blockIdx.x == 0 && threadIdx.x == 0 && a.ts_out) a.ts_out[0] = st;
+    int eD;
+    const double Dm = frexp(6.0 * (double)st, &eD);   // 6 s_t = Dm 2^eD, Dm in [0.5, 1)
+    eDp = eD - 1;
+    if (threadIdx.x < 128) tab[threadIdx.x] = (uint8_t)e4m3_mantissa_entry(threadIdx.x, 2.0 * Dm);
   }
+  __syncthreads();
   const float inv6st = 1.0f / (6.0f * st);
   const double st6 = 6.0 * (double)st;
 
@@ -104,49 +157,61 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantKArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0;
 
-  const int64_t r0 = tile * kScoreTileRows;
-  const int nr = (int)min((int64_t)kScoreTileRows, a.rows - r0);
-  const uint16_t* xp = a.x + r0 * cols + (active ? col0 : 0);
+  const int64_t r0 = group * (kScoreTileRows * kScoreGroupTiles) + wave * kScoreTileRows;
+  const int nr = (int)max((int64_t)0, min((int64_t)kScoreTileRows, a.rows - r0));
+  const uint16_t* xp = a.x + (nr > 0 ? r0 : 0) * cols + (active ? col0 : 0);
   const int64_t cstride = cols / 2, sstride = MX ? cols / 32 : cols / 16;
-  constexpr int U = 8;
+  constexpr int U = 4;
+
+  uint4 cur[U], nxt[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    cur[u] = (active && u < nr) ? *(const uint4*)(xp + (int64_t)u * cols) : make_uint4(0, 0, 0, 0);
 
   for (int rr = 0; rr < nr; rr += U) {
-    uint4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (active && rr + u < nr)
-        v[u] = *(const uint4*)(xp + (int64_t)(rr + u) * cols);
-      else
-        v[u] = make_uint4(0, 0, 0, 0);
-    }
+    for (int u = 0; u < U; ++u)
+      nxt[u] = (active && rr + U + u < nr) ? *(const uint4*)(xp + (int64_t)(rr + U + u) * cols)
+                                           : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (rr + u >= nr) break;
       const int64_t row = r0 + rr + u;
       float xf[8];
-      xf[0] = bf16_lo(v[u].x); xf[1] = bf16_hi(v[u].x);
-      xf[2] = bf16_lo(v[u].y); xf[3] = bf16_hi(v[u].y);
-      xf[4] = bf16_lo(v[u].z); xf[5] = bf16_hi(v[u].z);
-      xf[6] = bf16_lo(v[u].w); xf[7] = bf16_hi(v[u].w);
-      float m = fmaxf(fmaxf(fmaxf(fabsf(xf[0]), fabsf(xf[1])), fmaxf(fabsf(xf[2]), fabsf(xf[3]))),
-                      fmaxf(fmaxf(fabsf(xf[4]), fabsf(xf[5])), fmaxf(fabsf(xf[6]), fabsf(xf[7]))));
-      m = wave_xor_max(m, 1);                  // 16-element block = lane pair
+      xf[0] = bf16_lo(cur[u].x); xf[1] = bf16_hi(cur[u].x);
+      xf[2] = bf16_lo(cur[u].y); xf[3] = bf16_hi(cur[u].y);
+      xf[4] = bf16_lo(cur[u].z); xf[5] = bf16_hi(cur[u].z);
+      xf[6] = bf16_lo(cur[u].w); xf[7] = bf16_hi(cur[u].w);
+      float m = fmaxf(fmaxf(fabsf(xf[0]), fabsf(xf[1])), fabsf(xf[2]));
+      m = fmaxf(fmaxf(m, fabsf(xf[3])), fabsf(xf[4]));
+      m = fmaxf(fmaxf(m, fabsf(xf[5])), fabsf(xf[6]));
+      m = fmaxf(m, fabsf(xf[7]));
+      m = fmaxf(m, dpp_quad_xor1(m));          // 16-element block = lane pair
       uint32_t sc;
       float s;
+      bool ok;
       if constexpr (MX) {
-        m = wave_xor_max(m, 2);                // 32-element block = lane quad
+        m = fmaxf(m, dpp_quad_xor2(m));        // 32-element block = lane quad
         // floor(log2 m) - 2 clamped to [-127, 127]: exponent field - 129
-        int ef = (int)((__float_as_uint(m) >> 23) & 255u);
-        int e = max(ef - 129, -127);
+        const int ef = (int)(__float_as_uint(m) >> 23);
+        const int e = max(ef - 129, -127);
         sc = (uint32_t)(e + 127);
         s = e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : 0x1p-127f;
+        ok = true;
       } else {
-        sc = e4m3_scale_code(m, inv6st, st6);
-        s = e4m3_to_f32(sc);
+        const uint32_t ab = __float_as_uint(m);
+        const int ea = (int)(ab >> 23);
+        const uint32_t ent = tab[(ab >> 16) & 127u];
+        const int e = ea - 127 - eDp + (int)(ent >> 3) - 1;
+        const int ci = ((e + 7) << 3) | (int)(ent & 7u);
+        sc = (uint32_t)min(ci, 126);
+        ok = (ea != 0 && e >= -6) || ab == 0;
+        sc = ab == 0 ? 0u : sc;
+        s = sc >= 8u ? __uint_as_float((((sc >> 3) + 120u) << 23) | ((sc & 7u) << 20)) : 0.0f;
       }
       const float S = s * st;
-      const bool fast = S >= 0x1p-100f;
-      const float rinv = fast ? __builtin_amdgcn_rcpf(S) : 0.0f;
+      ok = ok && (S >= 0x1p-60f || S == 0.0f);
+      const float rinv = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
       const float rlo = rinv * (1.0f - 0x1p-20f), rhi = rinv * (1.0f + 0x1p-20f);
       uint32_t lo = 0, hi = 0;
       lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xf[0] * rlo, xf[1] * rlo, 1.0f, 0);
@@ -158,27 +223,47 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantKArgs a) {
       hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xf[4] * rhi, xf[5] * rhi, 1.0f, 2);
       hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xf[6] * rhi, xf[7] * rhi, 1.0f, 3);
       uint32_t code = lo;
-      if (!fast || lo != hi) {
-        // a value within 2^-20 of a rounding boundary (or an extreme scale):
-        // decide every element exactly
+      if (__builtin_expect(!ok, 0)) {
+        // a block scale outside the table's range or an extreme scale:
+        // decide the scale and every code exactly
+        if constexpr (!MX) {
+          sc = m == 0.0f ? 0u : e4m3_scale_code(m, inv6st, st6);
+          s = e4m3_to_f32(sc);
+        }
         code = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) code |= e2m1_nibble_exact(xf[i], s, st) << (4 * i);
+      } else if (__builtin_expect(__any(lo != hi), 0)) {
+        // values within 2^-20 of a rounding boundary: the two bracket codes are
+        // neighbours; compare |x| with their midpoint * s * st, exact in fp64
+        const uint32_t diff = lo ^ hi;
+        const double S64 = (double)s * (double)st;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (__any((diff >> (4 * i)) & 15u)) {
+            const uint32_t ml = (lo >> (4 * i)) & 7u, mh = (hi >> (4 * i)) & 7u;
+            if (ml != mh) {
+              const uint32_t mlow = ml < mh ? ml : mh;     // thresholds between mlow and mlow+1
+              const double mid = 0.5 * ((double)e2m1_mag(mlow) + (double)e2m1_mag(mlow + 1u));
+              const double ax = (double)fabsf(xf[i]);
+              const double t = mid * S64;
+              const bool up = ax > t || (ax == t && ((mlow + 1u) & 1u) == 0u);
+              const uint32_t mag = up ? mlow + 1u : mlow;
+              code = (code & ~(7u << (4 * i))) | (mag << (4 * i));
+            }
+          }
+        }
       }
       // residual r = RN32(x - c s st): c*s is exact, one fused rounding
-      float cv[8];
-      {
-        f32x2v c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
-        f32x2v c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 1);
-        f32x2v c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 2);
-        f32x2v c3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 3);
-        cv[0] = c0.x; cv[1] = c0.y; cv[2] = c1.x; cv[3] = c1.y;
-        cv[4] = c2.x; cv[5] = c2.y; cv[6] = c3.x; cv[7] = c3.y;
-      }
+      const f32x2v c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
+      const f32x2v c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 1);
+      const f32x2v c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 2);
+      const f32x2v c3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 3);
+      const float cv[8] = {c0.x, c0.y, c1.x, c1.y, c2.x, c2.y, c3.x, c3.y};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float r = fmaf(-(cv[i] * s), st, xf[i]);
-        double rd = (double)r;
+        const float r = fmaf(-(cv[i] * s), st, xf[i]);
+        const double rd = (double)r;
         acc[i] = fma(rd, rd, acc[i]);
       }
       if (active) {
@@ -190,39 +275,49 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantKArgs a) {
         }
       }
     }
-  }
-  if (active) {
-    double* pp = a.partial + tile * cols + col0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pp[i] = acc[i];
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+  }
+  // tile sums -> group sum, tiles in order
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[wave][lane][i] = acc[i];
+  __syncthreads();
+  {
+    const int c = threadIdx.x;   // channel strip*512 + c
+    double gsum = 0.0;
+#pragma unroll
+    for (int w = 0; w < kScoreGroupTiles; ++w) gsum += part[w][c >> 3][c & 7];
+    const int col = strip * 512 + c;
+    if (col < cols) a.partial[group * cols + col] = gsum;
   }
 }
 
 // ====================================================================== scores
-// score_j = sum over tiles ascending of the tile partial sums (fp64)
+// score_j = sum over groups ascending of the group partial sums (fp64)
 __global__ __launch_bounds__(256) void score_reduce_kernel(const double* __restrict__ partial,
-                                                           int64_t ntiles, int32_t cols,
+                                                           int64_t ngroups, int32_t cols,
                                                            double* __restrict__ scores) {
-  int j = blockIdx.x * 256 + threadIdx.x;
+  const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= cols) return;
   double s = 0.0;
   int64_t t = 0;
-  for (; t + 8 <= ntiles; t += 8) {
-    double p[8];
+  for (; t + 16 <= ngroups; t += 16) {
+    double p[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) p[u] = partial[(t + u) * cols + j];
+    for (int u = 0; u < 16; ++u) p[u] = partial[(t + u) * cols + j];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) s += p[u];
+    for (int u = 0; u < 16; ++u) s += p[u];
   }
-  for (; t < ntiles; ++t) s += partial[t * cols + j];
+  for (; t < ngroups; ++t) s += partial[t * cols + j];
   scores[j] = s;
 }
 
 // ====================================================================== top-k
-// One workgroup.  Radix select (8 bits per pass, most significant first) finds
-// the k-th largest key (non-negative fp64 bit patterns order as integers),
-// then an ordered scan emits every key above it and the first equal keys by
-// channel index, in ascending channel order.
+// One workgroup of 1024 threads.  Radix select over the fp64 bit patterns
+// (non-negative doubles order as unsigned integers), eight 8-bit digits from
+// the top: a wave-aggregated histogram, then one wave finds the digit that
+// holds the k-th largest key.  The emit pass takes every key above it and the
+// lowest-index copies of it, in ascending channel order.
 __device__ __forceinline__ int block_excl_scan_bits(bool flag, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   uint64_t b = __ballot(flag);
@@ -247,31 +342,51 @@ __global__ __launch_bounds__(1024) void topk_kernel(const double* __restrict__ s
   __shared__ int s_kleft;
   __shared__ int wsum[16];
   const uint64_t* keys = (const uint64_t*)scores;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint64_t prefix = 0, mask = 0;
   int kleft = k;
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 56 - 8 * pass;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int j = tid; j < cols; j += 1024) {
-      uint64_t key = keys[j];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    for (int j0 = 0; j0 < cols; j0 += 1024) {
+      const int j = j0 + tid;
+      const uint64_t key = j < cols ? keys[j] : 0ull;
+      const bool valid = j < cols && (key & mask) == prefix;
+      const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+      uint64_t pending = __ballot(valid);
+      while (pending) {
+        const int leader = __ffsll((unsigned long long)pending) - 1;
+        const uint32_t d0 = (uint32_t)__shfl((int)digit, leader, 64);
+        const uint64_t same = __ballot(valid && digit == d0) & pending;
+        if (lane == leader) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+        pending &= ~same;
+      }
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0;
-      for (int d = 255; d >= 0; --d) {
-        int h = (int)hist[d];
-        if (cum + h >= kleft) {
-          prefix |= (uint64_t)d << shift;
-          kleft -= cum;
-          break;
-        }
-        cum += h;
+    if (wave == 0) {
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      uint32_t c[4];
+      uint32_t sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[q] = hist[255 - 4 * lane - q];
+        sum += c[q];
       }
-      s_prefix = prefix;
-      s_kleft = kleft;
+      uint32_t incl = sum;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_up((int)incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      uint32_t cum = incl - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (cum < (uint32_t)kleft && cum + c[q] >= (uint32_t)kleft) {
+          s_prefix = prefix | ((uint64_t)(255 - 4 * lane - q) << shift);
+          s_kleft = kleft - (int)cum;
+        }
+        cum += c[q];
+      }
     }
     __syncthreads();
     prefix = s_prefix;
@@ -296,35 +411,53 @@ __global__ __launch_bounds__(1024) void topk_kernel(const double* __restrict__ s
 }
 
 // ====================================================================== gathers
-// R[i][t] = bf16(RN32(x[i][S_t] - dequant)) for t < k, 0 for k <= t < ld_r
+// R[i][t] = bf16(RN32(x[i][S_t] - dequant)) for t < k, 0 for k <= t < ld_r.
+// One thread per (row, 8 consecutive t): all loads of the eight are issued
+// before any is used.
 template <bool MX>
 __global__ __launch_bounds__(256) void residual_gather_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int32_t cols, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ ts,
     const int32_t* __restrict__ idx, int32_t k, uint16_t* __restrict__ R, int64_t ld_r) {
-  const int64_t total = rows * ld_r;
+  const int64_t n8 = (ld_r + 7) / 8;
+  const int64_t total = rows * n8;
   const float st = MX ? 1.0f : ts[0];
   for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total;
        g += (int64_t)gridDim.x * 256) {
-    const int64_t i = g / ld_r;
-    const int t = (int)(g - i * ld_r);
-    uint32_t out = 0;
-    if (t < k) {
-      int j = idx[t];
-      j = j < 0 ? 0 : (j >= cols ? cols - 1 : j);
-      const float xv = bf16_to_f32(x[i * cols + j]);
-      const uint32_t nib = (codes[i * (cols / 2) + (j >> 1)] >> ((j & 1) * 4)) & 15u;
-      float s;
-      if constexpr (MX) {
-        const int e = (int)scales[i * (cols / 32) + (j >> 5)] - 127;
-        s = e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : 0x1p-127f;
-      } else {
-        s = e4m3_to_f32(scales[i * (cols / 16) + (j >> 4)]);
-      }
-      const float r = fmaf(-(e2m1_value(nib) * s), st, xv);
-      out = f32_to_bf16_rne(r);
+    const int64_t i = g / n8;
+    const int t0 = (int)(g - i * n8) * 8;
+    int j[8];
+    uint16_t xv[8];
+    uint8_t cb[8], sb[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      int c = t0 + q < k ? idx[t0 + q] : 0;
+      j[q] = c < 0 ? 0 : (c >= cols ? cols - 1 : c);
     }
-    R[g] = (uint16_t)out;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      xv[q] = x[i * cols + j[q]];
+      cb[q] = codes[i * (cols / 2) + (j[q] >> 1)];
+      sb[q] = MX ? scales[i * (cols / 32) + (j[q] >> 5)] : scales[i * (cols / 16) + (j[q] >> 4)];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int t = t0 + q;
+      if (t >= ld_r) break;
+      uint32_t out = 0;
+      if (t < k) {
+        const uint32_t nib = (cb[q] >> ((j[q] & 1) * 4)) & 15u;
+        float s;
+        if constexpr (MX) {
+          const int e = (int)sb[q] - 127;
+          s = e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : 0x1p-127f;
+        } else {
+          s = e4m3_to_f32(sb[q]);
+        }
+        out = f32_to_bf16_rne(fmaf(-(e2m1_value(nib) * s), st, bf16_to_f32(xv[q])));
+      }
+      R[i * ld_r + t] = (uint16_t)out;
+    }
   }
 }
 
@@ -341,23 +474,28 @@ __global__ __launch_bounds__(256) void wsel_gather_kernel(const uint16_t* __rest
   const int t0 = blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const uint16_t* src = w_hi_t + b * K * N;
-  for (int r = ty; r < 64; r += 4) {
-    const int t = t0 + r;
-    const int64_t j = j0 + tx;
-    uint16_t v = 0;
-    if (t < k && j < N) {
-      int c = idx[t];
-      c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
-      v = src[(int64_t)c * N + j];
-    }
-    tile[r][tx] = v;
+  int64_t rowoff[16];
+  bool ok[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int t = t0 + ty + 4 * q;
+    int c = t < k ? idx[t] : 0;
+    c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
+    rowoff[q] = (int64_t)c * N;
+    ok[q] = t < k && j0 + tx < N;
   }
+  uint16_t v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v[q] = ok[q] ? src[rowoff[q] + j0 + tx] : (uint16_t)0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) tile[ty + 4 * q][tx] = v[q];
   __syncthreads();
   uint16_t* dst = ws + b * N * kp;
-  for (int r = ty; r < 64; r += 4) {
-    const int64_t j = j0 + r;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int64_t j = j0 + ty + 4 * q;
     const int t = t0 + tx;
-    if (j < N && t < kp) dst[j * kp + t] = tile[tx][r];
+    if (j < N && t < kp) dst[j * kp + t] = tile[tx][ty + 4 * q];
   }
 }
 
@@ -397,9 +535,18 @@ __global__ __launch_bounds__(256) void moe_pack_w13_kernel(const uint16_t* __res
 }
 
 // ====================================================================== launchers
+__global__ void tensor_scale_kernel(const float* ts_in, float* ts_out) {
+  if (threadIdx.x == 0) ts_out[0] = ts_in ? ts_in[0] : 1.0f;
+}
+
+static int64_t score_groups(int64_t rows) {
+  const int64_t g = kScoreTileRows * kScoreGroupTiles;
+  return (rows + g - 1) / g;
+}
+
 size_t quantize_workspace_bytes(int64_t rows, int64_t cols) {
-  const int64_t ntiles = (rows + kScoreTileRows - 1) / kScoreTileRows;
-  return 256 + align256((size_t)ntiles * (size_t)cols * 8) + align256((size_t)cols * 8);
+  return align256(kAmaxBlocks * 4) + align256((size_t)score_groups(rows) * (size_t)cols * 8) +
+         align256((size_t)cols * 8);
 }
 
 hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
@@ -408,17 +555,19 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
                            hipStream_t stream) {
   uint8_t* base = (uint8_t*)ws;
   uint32_t* amax = (uint32_t*)base;
-  const int64_t ntiles = (rows + kScoreTileRows - 1) / kScoreTileRows;
-  double* partial = (double*)(base + 256);
+  const int64_t ngroups = score_groups(rows);
+  const size_t amax_bytes = align256(kAmaxBlocks * 4);
+  double* partial = (double*)(base + amax_bytes);
   double* scores = chan_score ? chan_score
-                              : (double*)(base + 256 + align256((size_t)ntiles * cols * 8));
+                              : (double*)(base + amax_bytes + align256((size_t)ngroups * cols * 8));
   const bool need_amax = !mx && ts_in == nullptr;
+  int32_t namax = 0;
   if (need_amax) {
-    hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(256), 0, stream, amax, (int64_t)1, 0u);
     const int64_t n16 = rows * cols / 8;
     if (n16 > 0) {
       int64_t grid = (n16 + 256 * 8 - 1) / (256 * 8);
-      grid = grid < 1 ? 1 : (grid > 4096 ? 4096 : grid);
+      grid = grid < 1 ? 1 : (grid > kAmaxBlocks ? kAmaxBlocks : grid);
+      namax = (int32_t)grid;
       hipLaunchKernelGGL(amax_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                          (const uint4*)x, n16, amax);
     }
@@ -428,35 +577,32 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
   a.rows = rows;
   a.cols = (int32_t)cols;
   a.nstrips = (int32_t)((cols + 511) / 512);
-  a.ntiles = ntiles;
+  a.ngroups = ngroups;
   a.ts_in = ts_in;
   a.amax = amax;
+  a.namax = namax;
   a.codes = codes;
   a.scales = scales;
   a.ts_out = ts_out;
   a.partial = partial;
   a.reverse = need_amax ? 1 : 0;
-  const int64_t units = ntiles * a.nstrips;
+  const int64_t units = ngroups * a.nstrips;
   if (units > 0) {
-    const unsigned grid = (unsigned)((units + 3) / 4);
+    const unsigned grid = (unsigned)units;
     if (mx)
-      hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(512), 0, stream, a);
     else
-      hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(512), 0, stream, a);
   } else if (!mx && ts_out) {
     // no rows: still report s_t (1, or the supplied value)
     hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(64), 0, stream, ts_in, ts_out);
   }
   hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0,
-                     stream, (const double*)partial, ntiles, (int32_t)cols, scores);
+                     stream, (const double*)partial, ngroups, (int32_t)cols, scores);
   if (topk > 0)
     hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(1024), 0, stream, (const double*)scores,
                        (int32_t)cols, topk, chan_idx);
   return hipGetLastError();
-}
-
-__global__ void tensor_scale_kernel(const float* ts_in, float* ts_out) {
-  if (threadIdx.x == 0) ts_out[0] = ts_in ? ts_in[0] : 1.0f;
 }
 
 hipError_t launch_select(const double* scores, int64_t cols, int32_t topk, int32_t* idx,
@@ -471,7 +617,7 @@ hipError_t launch_residual_gather(bool mx, const uint16_t* x, int64_t rows, int6
                                   const uint8_t* codes, const uint8_t* scales, const float* ts,
                                   const int32_t* idx, int32_t k, uint16_t* R, int64_t ld_r,
                                   hipStream_t stream) {
-  const int64_t total = rows * ld_r;
+  const int64_t total = rows * ((ld_r + 7) / 8);
   if (total == 0) return hipSuccess;
   int64_t grid = (total + 255) / 256;
   grid = grid > 65536 ? 65536 : grid;

@@ -44,7 +44,8 @@
  *         [-127, 127] (byte 0 for an all-zero block), c nearest to |x| / 2^e.
  *   residual r = RN32(x - dequant(x)) (the negated Eq. 20 error);
  *   channel score_j = sum_i r_ij^2 in fp64 (Eq. 23 squared), summed over rows
- *         ascending inside tiles of 64 rows, then over tiles ascending;
+ *         ascending inside tiles of 32 rows, tile sums ascending inside groups
+ *         of 8 tiles, then group sums ascending (each level starts at zero);
  *   channel set S = the topk channels of largest score, ties to the smaller
  *         channel, listed in ascending channel order (Eq. 24, absolute k).
  */
@@ -71,7 +72,8 @@ typedef enum {
 typedef enum { Q4_NVFP4 = 0, Q4_MXFP4 = 1 } q4_format_t;
 typedef enum { Q4_OUT_F32 = 0, Q4_OUT_BF16 = 1 } q4_dtype_t;
 
-#define Q4_SCORE_TILE_ROWS 64
+#define Q4_SCORE_TILE_ROWS 32
+#define Q4_SCORE_GROUP_TILES 8
 #define Q4_MAX_TOPK 1024
 
 /* (host) message for the last non-OK status returned in this thread. */
