@@ -1,0 +1,183 @@
+"""GPU parity of the top-k MoE expert layer (route, token sort, grouped W4A4+RAC
+GEMMs with the SwiGLU epilogue, second activation site, combine) against the
+oracle, stage by stage.
+
+The silu in the W13 epilogue uses the device exp, so h cannot be bit-matched
+to the fp64 oracle; h is compared within the GEMM tolerance and every later
+stage is checked on the GPU's own h (the oracle quantizes it bit-exactly and
+recomputes the W2 GEMM and the combine from it)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.quant import QuantResult
+from workloads import WORKLOADS, bf16_bits_from_f32, make_activations, make_logits, make_moe_weights
+from tests.gpu_util import GEMM_TOL, bf16_to_f64, check_bf16_output, dev, gemm_rel_err, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+def q4():
+    import fp4_w4a4_quantized_nvfp4_amd as m
+    return m
+
+
+def _bits(a):
+    return bf16_bits_from_f32(np.asarray(a, dtype=np.float32))
+
+
+def _rows(q, rows):
+    return QuantResult(q.fmt, q.codes[rows], q.scales[rows], q.tensor_scale, q.resid[rows],
+                       q.mag[rows], q.sign[rows])
+
+
+def _swiglu64(y13, F):
+    g, u = y13[:, :F], y13[:, F:]
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def _ws_field(ws, offs, i, nbytes, dtype):
+    return host(ws[offs[i]:offs[i] + nbytes].view(dtype))
+
+
+def test_route_and_sort():
+    m = q4()
+    rng = np.random.default_rng(5)
+    logits = rng.standard_normal((300, 128)).astype(np.float32)
+    logits[7, 10] = logits[7, 99] = logits[7].max() + 1.0           # tie at the top
+    idx, w = m.q4_moe_route(dev(logits), 8)
+    idx, w = host(idx), host(w)
+    oi, op = oracle.moe_route(logits, 8)
+    assert np.array_equal(idx, oi)
+    np.testing.assert_allclose(w, op, rtol=2e-6, atol=1e-7)
+    perm, off = m.q4_moe_sort(dev(idx), 128)
+    pe, oe = oracle.moe_sort(idx, 128)
+    assert np.array_equal(host(perm), pe) and np.array_equal(host(off), oe)
+
+
+def _run_layer(m, xb, logits, w13, w2, topk, rac_k, fmt=0, out_dtype=1):
+    T, H = xb.shape
+    E, F2, _ = w13.shape
+    F = F2 // 2
+    x = dev(xb)
+    idx, p = m.q4_moe_route(dev(logits), topk)
+    experts = m.prepare_moe_weights(dev(w13), dev(w2), fmt=fmt)
+    Y, ws = m.moe_w4a4_grouped_gemm(x, idx, p, experts, rac_k, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    offs, _ = m.moe_workspace_layout(fmt, T, E, H, F, topk, rac_k)
+    R = T * topk
+    sdiv = 16 if fmt == 0 else 32
+    got = {
+        "idx": host(idx), "p": host(p), "Y": host(Y),
+        "perm": _ws_field(ws, offs, 0, R * 4, torch.int32),
+        "offsets": _ws_field(ws, offs, 1, (E + 1) * 4, torch.int32),
+        "x_codes": _ws_field(ws, offs, 2, T * H // 2, torch.uint8),
+        "x_scales": _ws_field(ws, offs, 3, T * H // sdiv, torch.uint8),
+        "x_ts": _ws_field(ws, offs, 4, 4, torch.float32),
+        "x_S": _ws_field(ws, offs, 5, rac_k * 4, torch.int32),
+        "h": _ws_field(ws, offs, 7, R * F * 2, torch.int16).reshape(R, F),
+        "h_codes": _ws_field(ws, offs, 8, R * F // 2, torch.uint8),
+        "h_scales": _ws_field(ws, offs, 9, R * F // sdiv, torch.uint8),
+        "h_ts": _ws_field(ws, offs, 10, 4, torch.float32),
+        "h_S": _ws_field(ws, offs, 11, rac_k * 4, torch.int32),
+        "out": _ws_field(ws, offs, 13, R * H * 4, torch.float32).reshape(R, H),
+    }
+    return got, experts
+
+
+def _check_site(fmt, xb, got, prefix, rac_k):
+    q = oracle.nvfp4_quantize(xb) if fmt == 0 else oracle.mxfp4_quantize(xb)
+    assert np.array_equal(got[prefix + "_codes"].reshape(q.codes.shape), q.codes)
+    assert np.array_equal(got[prefix + "_scales"].reshape(q.scales.shape), q.scales)
+    if fmt == 0:
+        assert got[prefix + "_ts"][0] == np.float32(q.tensor_scale)
+    S = oracle.select_topk(oracle.channel_scores(q.resid), rac_k)
+    assert np.array_equal(got[prefix + "_S"], S)
+    return q, S
+
+
+@pytest.mark.parametrize("fmt", [0])
+@pytest.mark.parametrize("T,H,E,F,topk,k", [(64, 256, 8, 128, 2, 16), (37, 512, 16, 64, 4, 32),
+                                            (300, 256, 4, 96, 1, 8)])
+def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
+    say(f"moe small fmt={fmt} T={T} H={H} E={E} F={F} topk={topk} k={k}")
+    m = q4()
+    rng = np.random.default_rng(T + H + E)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[:, rng.choice(H, 3, replace=False)] *= 40
+    xb = _bits(x)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    w13 = _bits((rng.standard_normal((E, 2 * F, H)) * 0.05).astype(np.float32))
+    w2 = _bits((rng.standard_normal((E, H, F)) * 0.05).astype(np.float32))
+    got, _ = _run_layer(m, xb, logits, w13, w2, topk, k, fmt)
+    oi, op = oracle.moe_route(logits, topk)
+    assert np.array_equal(got["idx"], oi)
+    ref = oracle.moe_layer(xb, got["idx"], got["p"].astype(np.float64), w13, w2, k,
+                           h_override=got["h"])
+    assert np.array_equal(got["perm"], ref["perm"]) and np.array_equal(got["offsets"], ref["offsets"])
+    _check_site(fmt, xb, got, "x", k)
+    # h (bf16) against the unrounded SwiGLU of the oracle's fp64 W13 product:
+    # the GEMM tolerance plus one bf16 ulp
+    check_bf16_output(got["h"], _swiglu64(ref["y13"], F), tol=2 * GEMM_TOL)
+    # second site on the GPU's h, bit-exact
+    _check_site(fmt, got["h"], got, "h", k)
+    err_o = gemm_rel_err(got["out"], ref["out"])
+    say(f"  W2 out rel err {err_o:.2e}")
+    assert err_o <= GEMM_TOL
+    check_bf16_output(got["Y"], ref["y"], tol=2 * GEMM_TOL)
+
+
+def _sampled_full(name, n_experts_checked=3):
+    m = q4()
+    wl = WORKLOADS[name]
+    T, H, E, F, topk, k = wl.rows, wl.cols, wl.experts, wl.ffn, wl.route_topk, wl.topk_channels
+    say(f"moe {name}: generating inputs")
+    xb = make_activations(wl)
+    logits = make_logits(wl)
+    w13, w2 = make_moe_weights(wl)
+    say(f"moe {name}: GPU layer")
+    got, experts = _run_layer(m, xb, logits, w13, w2, topk, k)
+    oi, op = oracle.moe_route(logits[:256], topk)
+    assert np.array_equal(got["idx"][:256], oi)
+    np.testing.assert_allclose(got["p"][:256], op, rtol=2e-6, atol=1e-7)
+    perm, offsets = oracle.moe_sort(got["idx"], E)
+    assert np.array_equal(got["perm"], perm) and np.array_equal(got["offsets"], offsets)
+    say(f"moe {name}: site 1")
+    qx, Sx = _check_site(0, xb, got, "x", k)
+    Rx = oracle.residual_gather(qx.resid, Sx)
+    say(f"moe {name}: site 2")
+    qh, Sh = _check_site(0, got["h"], got, "h", k)
+    Rh = oracle.residual_gather(qh.resid, Sh)
+    counts = np.diff(offsets)
+    rng = np.random.default_rng(1)
+    nonempty = np.where(counts > 0)[0]
+    check = sorted(set(rng.choice(nonempty, size=min(n_experts_checked, len(nonempty)), replace=False).tolist()))
+    tok = perm // topk
+    for e in check:
+        r0, r1 = offsets[e], offsets[e + 1]
+        say(f"moe {name}: expert {e} rows {r1 - r0}")
+        wq13 = oracle.nvfp4_quantize(w13[e])
+        y13 = oracle.rac_gemm(_rows(qx, tok[r0:r1]), wq13, Rx[tok[r0:r1]], w13[e], Sx)
+        check_bf16_output(got["h"][r0:r1], _swiglu64(y13, F), tol=2 * GEMM_TOL)
+        wq2 = oracle.nvfp4_quantize(w2[e])
+        rows = np.arange(r0, r1)
+        out_ref = oracle.rac_gemm(_rows(qh, rows), wq2, Rh[rows], w2[e], Sh)
+        err = gemm_rel_err(got["out"][r0:r1], out_ref)
+        say(f"  W2 out rel err {err:.2e}")
+        assert err <= GEMM_TOL
+    # combine on the GPU's out and routing weights
+    pos = np.empty(T * topk, dtype=np.int64)
+    pos[perm] = np.arange(T * topk)
+    y = np.zeros((T, H))
+    for s in range(topk):
+        y += got["p"][:, s:s + 1].astype(np.float64) * got["out"][pos[np.arange(T) * topk + s]]
+    check_bf16_output(got["Y"], y)
+
+
+def test_moe_decode_workload_sampled():
+    _sampled_full("moe_decode_256")
+
+
+def test_moe_prefill_workload_sampled():
+    _sampled_full("moe_prefill_8192", n_experts_checked=2)
