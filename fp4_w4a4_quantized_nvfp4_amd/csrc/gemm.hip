@@ -65,7 +65,7 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int j) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
-template <bool FULLK, bool GROUPED, int EPI>
+template <bool FULLK, bool GROUPED, int EPI, bool MX>
 __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
   const int tid = threadIdx.x;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
     n0 = (int64_t)bn * BN;
   }
 
-  const int64_t cstride = K / 2, sstride = K / 16;
+  const int64_t cstride = K / 2, sstride = MX ? K / 32 : K / 16;
   const uint8_t* wc = g.w_codes + (int64_t)e * N * cstride;
   const uint8_t* ws = g.w_scales + (int64_t)e * N * sstride;
 
@@ -157,7 +157,25 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
       pb[it] = (b_ok[it] && (FULLK || kel < K)) ? *(const uint4*)(b_ptr[it] + k0 / 2)
                                                 : make_uint4(0, 0, 0, 0);
     }
-    if constexpr (FULLK) {
+    if constexpr (MX) {
+      // E8M0 scales: one byte per 32 elements, four per row per chunk
+      if constexpr (FULLK) {
+        psa.x = as_ok ? *(const uint32_t*)(as_ptr + k0 / 32) : 0u;
+        psb.x = bs_ok ? *(const uint32_t*)(bs_ptr + k0 / 32) : 0u;
+      } else {
+        uint32_t s = 0, t = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (k0 + 32 * q < K) {
+            if (as_ok) s |= (uint32_t)as_ptr[k0 / 32 + q] << (8 * q);
+            if (bs_ok) t |= (uint32_t)bs_ptr[k0 / 32 + q] << (8 * q);
+          }
+        }
+        psa.x = s;
+        psb.x = t;
+      }
+      psa.y = psb.y = 0u;
+    } else if constexpr (FULLK) {
       psa = as_ok ? *(const uint2*)(as_ptr + k0 / 16) : make_uint2(0, 0);
       psb = bs_ok ? *(const uint2*)(bs_ptr + k0 / 16) : make_uint2(0, 0);
     } else {
@@ -187,23 +205,28 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
       const int q = it * 256 + tid;
       *(uint4*)(base + B_CODE_OFF + swz(q >> 2, q & 3)) = pb[it];
     }
-    {
-      const uint32_t w0 = psa.x, w1 = psa.y;
-      uint4 f;
-      f.x = e4m3_to_f16_bits(w0 & 255u) | (e4m3_to_f16_bits((w0 >> 8) & 255u) << 16);
-      f.y = e4m3_to_f16_bits((w0 >> 16) & 255u) | (e4m3_to_f16_bits(w0 >> 24) << 16);
-      f.z = e4m3_to_f16_bits(w1 & 255u) | (e4m3_to_f16_bits((w1 >> 8) & 255u) << 16);
-      f.w = e4m3_to_f16_bits((w1 >> 16) & 255u) | (e4m3_to_f16_bits(w1 >> 24) << 16);
-      *(uint4*)(base + A_SC_OFF + tid * 16) = f;
-    }
-    if (tid < BN) {
-      const uint32_t w0 = psb.x, w1 = psb.y;
-      uint4 f;
-      f.x = e4m3_to_f16_bits(w0 & 255u) | (e4m3_to_f16_bits((w0 >> 8) & 255u) << 16);
-      f.y = e4m3_to_f16_bits((w0 >> 16) & 255u) | (e4m3_to_f16_bits(w0 >> 24) << 16);
-      f.z = e4m3_to_f16_bits(w1 & 255u) | (e4m3_to_f16_bits((w1 >> 8) & 255u) << 16);
-      f.w = e4m3_to_f16_bits((w1 >> 16) & 255u) | (e4m3_to_f16_bits(w1 >> 24) << 16);
-      *(uint4*)(base + B_SC_OFF + tid * 16) = f;
+    if constexpr (MX) {
+      *(uint32_t*)(base + A_SC_OFF + tid * 4) = psa.x;
+      if (tid < BN) *(uint32_t*)(base + B_SC_OFF + tid * 4) = psb.x;
+    } else {
+      {
+        const uint32_t w0 = psa.x, w1 = psa.y;
+        uint4 f;
+        f.x = e4m3_to_f16_bits(w0 & 255u) | (e4m3_to_f16_bits((w0 >> 8) & 255u) << 16);
+        f.y = e4m3_to_f16_bits((w0 >> 16) & 255u) | (e4m3_to_f16_bits(w0 >> 24) << 16);
+        f.z = e4m3_to_f16_bits(w1 & 255u) | (e4m3_to_f16_bits((w1 >> 8) & 255u) << 16);
+        f.w = e4m3_to_f16_bits((w1 >> 16) & 255u) | (e4m3_to_f16_bits(w1 >> 24) << 16);
+        *(uint4*)(base + A_SC_OFF + tid * 16) = f;
+      }
+      if (tid < BN) {
+        const uint32_t w0 = psb.x, w1 = psb.y;
+        uint4 f;
+        f.x = e4m3_to_f16_bits(w0 & 255u) | (e4m3_to_f16_bits((w0 >> 8) & 255u) << 16);
+        f.y = e4m3_to_f16_bits((w0 >> 16) & 255u) | (e4m3_to_f16_bits(w0 >> 24) << 16);
+        f.z = e4m3_to_f16_bits(w1 & 255u) | (e4m3_to_f16_bits((w1 >> 8) & 255u) << 16);
+        f.w = e4m3_to_f16_bits((w1 >> 16) & 255u) | (e4m3_to_f16_bits(w1 >> 24) << 16);
+        *(uint4*)(base + B_SC_OFF + tid * 16) = f;
+      }
     }
   };
 
@@ -217,6 +240,40 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
 
   auto compute = [&](int stg) {
     const uint8_t* base = smem + stg * STAGE;
+    if constexpr (MX) {
+      // the scaled FP4 instruction consumes codes and E8M0 scales directly:
+      // lane half h supplies the 32-element block 2j + h of the chunk
+      uint32_t sa[4], sb[2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        sa[mi] = *(const uint32_t*)(base + A_SC_OFF + (wm * 128 + mi * 32 + l32) * 4);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        sb[ni] = *(const uint32_t*)(base + B_SC_OFF + (wn * 64 + ni * 32 + l32) * 4);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int p = 2 * j + h;
+        i32x8v af[4], bf[2];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const uint4 v = *(const uint4*)(base + swz(wm * 128 + mi * 32 + l32, p));
+          af[mi] = (i32x8v){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const uint4 v = *(const uint4*)(base + B_CODE_OFF + swz(wn * 64 + ni * 32 + l32, p));
+          bf[ni] = (i32x8v){(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[mi], bf[ni], acc[mi][ni], 4, 4, 0, (int)(sa[mi] >> (8 * p)), 0,
+                (int)(sb[ni] >> (8 * p)));
+      }
+      return;
+    }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const int p = 2 * h + s2;
@@ -579,29 +636,33 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
 }
 }  // namespace big
 
-template <bool FULLK, bool GROUPED>
+template <bool FULLK, bool GROUPED, bool MX>
 hipError_t launch_t(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
   const int64_t nbn = (g.N + BN - 1) / BN;
   const int64_t nbm = GROUPED ? max_mtiles : (g.M + BM - 1) / BM;
   const int64_t nb = nbm * nbn;
   if (nb == 0) return hipSuccess;
   if (g.epilogue == kEpiSwiGLU)
-    hipLaunchKernelGGL((gemm_nvfp4_kernel<FULLK, GROUPED, kEpiSwiGLU>), dim3((unsigned)nb),
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<FULLK, GROUPED, kEpiSwiGLU, MX>), dim3((unsigned)nb),
                        dim3(256), 0, stream, g);
   else
-    hipLaunchKernelGGL((gemm_nvfp4_kernel<FULLK, GROUPED, kEpiStore>), dim3((unsigned)nb),
+    hipLaunchKernelGGL((gemm_nvfp4_kernel<FULLK, GROUPED, kEpiStore, MX>), dim3((unsigned)nb),
                        dim3(256), 0, stream, g);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_mx_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream);
-
 hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
-  if (g.mx) return launch_mx_gemm(g, max_mtiles, stream);
   const bool fullk = (g.K % BK) == 0;
   const bool grouped = g.tiles != nullptr;
+  if (g.mx) {
+    if (fullk)
+      return grouped ? launch_t<true, true, true>(g, max_mtiles, stream)
+                     : launch_t<true, false, true>(g, max_mtiles, stream);
+    return grouped ? launch_t<false, true, true>(g, max_mtiles, stream)
+                   : launch_t<false, false, true>(g, max_mtiles, stream);
+  }
   if (!grouped && g.epilogue == kEpiStore && g.M >= 512 && g.N >= 512) {
     const int64_t nb = ((g.M + big::BM - 1) / big::BM) * ((g.N + big::BN - 1) / big::BN);
     if (fullk)
@@ -611,10 +672,10 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
     return hipGetLastError();
   }
   if (fullk)
-    return grouped ? launch_t<true, true>(g, max_mtiles, stream)
-                   : launch_t<true, false>(g, max_mtiles, stream);
-  return grouped ? launch_t<false, true>(g, max_mtiles, stream)
-                 : launch_t<false, false>(g, max_mtiles, stream);
+    return grouped ? launch_t<true, true, false>(g, max_mtiles, stream)
+                   : launch_t<true, false, false>(g, max_mtiles, stream);
+  return grouped ? launch_t<false, true, false>(g, max_mtiles, stream)
+                 : launch_t<false, false, false>(g, max_mtiles, stream);
 }
 
 }  // namespace q4

@@ -24,7 +24,8 @@ import numpy as np
 
 from .formats import bf16_bits_to_f64, f64_to_bf16_bits
 from .gemm import rac_gemm
-from .quant import QuantResult, channel_scores, nvfp4_quantize, residual_gather, select_topk
+from .quant import (QuantResult, channel_scores, mxfp4_quantize, nvfp4_quantize, residual_gather,
+                    select_topk)
 
 
 def moe_route(logits: np.ndarray, topk: int):
@@ -66,29 +67,31 @@ def _rows(q: QuantResult, rows: np.ndarray) -> QuantResult:
 
 
 def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
-              wq13=None, wq2=None):
+              wq13=None, wq2=None, fmt: str = "nvfp4"):
     """Whole expert layer; returns a dict of every intermediate (fp64 unless noted).
 
     x_bits [T, H] bf16 bits; idx/p from ``moe_route``; w13_bits [E, 2F, H] and
     w2_bits [E, H, F] bf16 bits (logical layout).  ``h_override`` replaces the
     oracle's own h (bf16 bits [T*topk, F], sorted order) before the second
     quantization, for stage-wise comparison.  ``wq13``/``wq2`` are optional
-    pre-quantized expert weights (lists of QuantResult).
+    pre-quantized expert weights (lists of QuantResult).  ``fmt`` selects the
+    activation and weight format ("nvfp4" or "mxfp4").
     """
+    quant = nvfp4_quantize if fmt == "nvfp4" else mxfp4_quantize
     T, H = x_bits.shape
     E, F2, _ = w13_bits.shape
     F = F2 // 2
     k = idx.shape[1]
     perm, offsets = moe_sort(idx, E)
     tok = perm // k
-    qx = nvfp4_quantize(x_bits)
+    qx = quant(x_bits)
     sx = channel_scores(qx.resid)
     Sx = select_topk(sx, rac_k)
     Rx = residual_gather(qx.resid, Sx)
     if wq13 is None:
-        wq13 = [nvfp4_quantize(w13_bits[e]) for e in range(E)]
+        wq13 = [quant(w13_bits[e]) for e in range(E)]
     if wq2 is None:
-        wq2 = [nvfp4_quantize(w2_bits[e]) for e in range(E)]
+        wq2 = [quant(w2_bits[e]) for e in range(E)]
     y13 = np.zeros((T * k, F2), dtype=np.float64)
     for e in range(E):
         r0, r1 = offsets[e], offsets[e + 1]
@@ -98,7 +101,7 @@ def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
         y13[r0:r1] = rac_gemm(_rows(qx, rows), wq13[e], Rx[rows], w13_bits[e], Sx)
     h = swiglu_bf16(y13[:, :F], y13[:, F:])
     h_used = h if h_override is None else np.asarray(h_override, dtype=np.uint16)
-    qh = nvfp4_quantize(h_used)
+    qh = quant(h_used)
     sh = channel_scores(qh.resid)
     Sh = select_topk(sh, rac_k)
     Rh = residual_gather(qh.resid, Sh)

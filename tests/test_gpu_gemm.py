@@ -135,3 +135,35 @@ def test_dense_prefill_workload_sampled():
     ref = oracle.rac_gemm(sub, Wo, Ro[rows], wb, So)
     check_bf16_output(host(Y)[rows], ref)
     say("prefill workload sampled parity ok")
+
+
+@pytest.mark.parametrize("M,N,K,k", [(64, 512, 512, 16), (300, 200, 96, 20), (513, 640, 1024, 64),
+                                     (1000, 1300, 512, 64)])
+def test_mxfp4_rac_gemm(M, N, K, k):
+    """MXFP4 operands on the scaled FP4 matrix instruction, RAC on bf16."""
+    rng = np.random.default_rng(M * 7 + K)
+    x = rng.standard_t(3, size=(M, K)).astype(np.float32)
+    x[:, rng.choice(K, 3, replace=False)] *= 50
+    xb = _bits(x)
+    wb = _bits((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+    _check_rac(xb, wb, k, 0, fmt="mx")
+    _check_rac(xb, wb, k, 1, fmt="mx")
+
+
+def test_mxfp4_exact_special_case():
+    """Power-of-two scales and E2M1 values: every partial sum is exact, so the
+    scaled-MFMA product must equal the integer result bit for bit."""
+    m = q4()
+    rng = np.random.default_rng(17)
+    M, N, K = 96, 160, 256
+    def operand(rows):
+        e = rng.integers(-2, 3, size=(rows, K // 32))
+        mag = rng.integers(0, 8, size=(rows, K))
+        mag[:, ::32] = 7
+        val = np.array(PAGE_GRID)[mag] * np.repeat(2.0 ** e, 32, axis=1) * 0.25
+        val *= np.where(rng.random((rows, K)) < 0.5, -1, 1)
+        return _bits(val.astype(np.float32))
+    xb, wb = operand(M), operand(N)
+    x, A, W, Ao, Wo = _quant_pair(m, xb, wb, "mx")
+    Y = host(m.w4a4_gemm(A, W))
+    assert np.array_equal(Y.astype(np.float64), oracle.w4a4_gemm(Ao, Wo))

@@ -97,7 +97,7 @@ def _check_site(fmt, xb, got, prefix, rac_k):
     return q, S
 
 
-@pytest.mark.parametrize("fmt", [0])
+@pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("T,H,E,F,topk,k", [(64, 256, 8, 128, 2, 16), (37, 512, 16, 64, 4, 32),
                                             (300, 256, 4, 96, 1, 8)])
 def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
@@ -114,7 +114,7 @@ def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
     oi, op = oracle.moe_route(logits, topk)
     assert np.array_equal(got["idx"], oi)
     ref = oracle.moe_layer(xb, got["idx"], got["p"].astype(np.float64), w13, w2, k,
-                           h_override=got["h"])
+                           h_override=got["h"], fmt="nvfp4" if fmt == 0 else "mxfp4")
     assert np.array_equal(got["perm"], ref["perm"]) and np.array_equal(got["offsets"], ref["offsets"])
     _check_site(fmt, xb, got, "x", k)
     # h (bf16) against the unrounded SwiGLU of the oracle's fp64 W13 product:
@@ -128,7 +128,11 @@ def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
     check_bf16_output(got["Y"], ref["y"], tol=2 * GEMM_TOL)
 
 
-def _sampled_full(name, n_experts_checked=3):
+def _quant(fmt):
+    return oracle.nvfp4_quantize if fmt == 0 else oracle.mxfp4_quantize
+
+
+def _sampled_full(name, n_experts_checked=3, fmt=0):
     m = q4()
     wl = WORKLOADS[name]
     T, H, E, F, topk, k = wl.rows, wl.cols, wl.experts, wl.ffn, wl.route_topk, wl.topk_channels
@@ -137,17 +141,17 @@ def _sampled_full(name, n_experts_checked=3):
     logits = make_logits(wl)
     w13, w2 = make_moe_weights(wl)
     say(f"moe {name}: GPU layer")
-    got, experts = _run_layer(m, xb, logits, w13, w2, topk, k)
+    got, experts = _run_layer(m, xb, logits, w13, w2, topk, k, fmt)
     oi, op = oracle.moe_route(logits[:256], topk)
     assert np.array_equal(got["idx"][:256], oi)
     np.testing.assert_allclose(got["p"][:256], op, rtol=2e-6, atol=1e-7)
     perm, offsets = oracle.moe_sort(got["idx"], E)
     assert np.array_equal(got["perm"], perm) and np.array_equal(got["offsets"], offsets)
     say(f"moe {name}: site 1")
-    qx, Sx = _check_site(0, xb, got, "x", k)
+    qx, Sx = _check_site(fmt, xb, got, "x", k)
     Rx = oracle.residual_gather(qx.resid, Sx)
     say(f"moe {name}: site 2")
-    qh, Sh = _check_site(0, got["h"], got, "h", k)
+    qh, Sh = _check_site(fmt, got["h"], got, "h", k)
     Rh = oracle.residual_gather(qh.resid, Sh)
     counts = np.diff(offsets)
     rng = np.random.default_rng(1)
@@ -157,10 +161,10 @@ def _sampled_full(name, n_experts_checked=3):
     for e in check:
         r0, r1 = offsets[e], offsets[e + 1]
         say(f"moe {name}: expert {e} rows {r1 - r0}")
-        wq13 = oracle.nvfp4_quantize(w13[e])
+        wq13 = _quant(fmt)(w13[e])
         y13 = oracle.rac_gemm(_rows(qx, tok[r0:r1]), wq13, Rx[tok[r0:r1]], w13[e], Sx)
         check_bf16_output(got["h"][r0:r1], _swiglu64(y13, F), tol=2 * GEMM_TOL)
-        wq2 = oracle.nvfp4_quantize(w2[e])
+        wq2 = _quant(fmt)(w2[e])
         rows = np.arange(r0, r1)
         out_ref = oracle.rac_gemm(_rows(qh, rows), wq2, Rh[rows], w2[e], Sh)
         err = gemm_rel_err(got["out"][r0:r1], out_ref)
@@ -175,8 +179,11 @@ def _sampled_full(name, n_experts_checked=3):
     check_bf16_output(got["Y"], y)
 
 
-def test_moe_decode_workload_sampled():
-    _sampled_full("moe_decode_256")
+@pytest.mark.parametrize("fmt", [0, 1], ids=["nvfp4", "mxfp4"])
+def test_moe_decode_workload_sampled(fmt):
+    """256 tokens, 128 experts of 4096 -> 2 x 1536 -> 4096, top-8: run as NVFP4
+    and again as MXFP4 (E8M0 per 32, native scaled FP4 MFMA)."""
+    _sampled_full("moe_decode_256", fmt=fmt)
 
 
 def test_moe_prefill_workload_sampled():
