@@ -29,10 +29,28 @@ constexpr int A_SC_OFF = B_CODE_OFF + BN * CB;        // 24576
 constexpr int B_SC_OFF = A_SC_OFF + BM * NBLK * 2;    // 28672 (fp16 scales)
 constexpr int STAGE = B_SC_OFF + BN * NBLK * 2;       // 30720
 
-// 16-byte piece p of row r, xor-swizzled so that 16 consecutive rows reading
-// the same piece hit distinct bank groups
+// 16-byte piece p of row r (rows of 64 bytes), xor-swizzled so that 8 (or 16)
+// consecutive rows reading the same piece hit distinct 16-byte bank groups
+// whether the LDS serves 128 or 256 bytes per cycle
 __device__ __forceinline__ int swz(int row, int piece) {
-  return row * CB + ((piece ^ ((row >> 2) & 3)) << 4);
+  return row * CB + ((piece ^ ((row >> 1) ^ (row >> 2)) & 3) << 4);
+}
+
+// dword d of a 16-byte per-row scale record, xor-swizzled so that 32
+// consecutive rows reading the same dword hit distinct banks
+__device__ __forceinline__ int swz_sc(int row, int d) {
+  return row * 16 + ((d ^ ((row >> 3) & 3)) << 2);
+}
+
+// the four dwords of a 16-byte scale record in swizzled order for row `row`
+__device__ __forceinline__ uint4 swz_sc_rec(uint4 v, int row) {
+  const int q = (row >> 3) & 3;
+  uint4 r;
+  r.x = q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+  r.y = q == 0 ? v.y : (q == 1 ? v.x : (q == 2 ? v.w : v.z));
+  r.z = q == 0 ? v.z : (q == 1 ? v.w : (q == 2 ? v.x : v.y));
+  r.w = q == 0 ? v.w : (q == 1 ? v.z : (q == 2 ? v.y : v.x));
+  return r;
 }
 
 // E4M3 code -> fp16 bits (exact: 4 significant bits, 2^-9 .. 448)
@@ -216,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
         f.y = e4m3_to_f16_bits((w0 >> 16) & 255u) | (e4m3_to_f16_bits(w0 >> 24) << 16);
         f.z = e4m3_to_f16_bits(w1 & 255u) | (e4m3_to_f16_bits((w1 >> 8) & 255u) << 16);
         f.w = e4m3_to_f16_bits((w1 >> 16) & 255u) | (e4m3_to_f16_bits(w1 >> 24) << 16);
-        *(uint4*)(base + A_SC_OFF + tid * 16) = f;
+        *(uint4*)(base + A_SC_OFF + tid * 16) = swz_sc_rec(f, tid);
       }
       if (tid < BN) {
         const uint32_t w0 = psb.x, w1 = psb.y;
@@ -225,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
         f.y = e4m3_to_f16_bits((w0 >> 16) & 255u) | (e4m3_to_f16_bits(w0 >> 24) << 16);
         f.z = e4m3_to_f16_bits(w1 & 255u) | (e4m3_to_f16_bits((w1 >> 8) & 255u) << 16);
         f.w = e4m3_to_f16_bits((w1 >> 16) & 255u) | (e4m3_to_f16_bits(w1 >> 24) << 16);
-        *(uint4*)(base + B_SC_OFF + tid * 16) = f;
+        *(uint4*)(base + B_SC_OFF + tid * 16) = swz_sc_rec(f, tid);
       }
     }
   };
@@ -283,13 +301,13 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
       for (int mi = 0; mi < 4; ++mi) {
         const int row = wm * 128 + mi * 32 + l32;
         ra[mi] = *(const uint4*)(base + swz(row, p));
-        sa[mi] = *(const uint32_t*)(base + A_SC_OFF + row * 16 + h * 8 + s2 * 4);
+        sa[mi] = *(const uint32_t*)(base + A_SC_OFF + swz_sc(row, 2 * h + s2));
       }
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
         const int row = wn * 64 + ni * 32 + l32;
         rb[ni] = *(const uint4*)(base + B_CODE_OFF + swz(row, p));
-        sb[ni] = *(const uint32_t*)(base + B_SC_OFF + row * 16 + h * 8 + s2 * 4);
+        sb[ni] = *(const uint32_t*)(base + B_SC_OFF + swz_sc(row, 2 * h + s2));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -402,47 +420,70 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// Dense kernel with 256 x 256 tiles: four waves of 128 x 128 (4 x 4 MFMA
-// tiles, accumulators in AGPRs, one wave per SIMD).  Every decoded fragment
-// feeds four MFMAs, so decode costs four VALU instructions per MFMA.
+// Dense kernel with 256 x 256 tiles for K % 128 == 0: four waves of 128 x 128
+// (4 x 4 MFMA tiles, accumulators in AGPRs, one wave per SIMD).  Every decoded
+// fragment feeds four MFMAs, so decode costs about four VALU instructions per
+// MFMA.
+//
+// Pipeline: three LDS stages filled straight from global memory
+// (global_load_lds, no registers), three chunks ahead: FP4 codes as 16-byte
+// pieces, raw E4M3 scales as dwords.  Each wave widens its own scales to fp16
+// when it reads a fragment.  Each chunk is consumed in two halves (s2): while
+// the MFMAs of one half run, the fragments of the next half are read from
+// LDS, and the decode of step j + 1 overlaps the MFMAs of step j.  One
+// workgroup barrier per chunk sits between the two halves.
 namespace big {
 constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int CB = BK / 2;
+constexpr int NST = 3;
 constexpr int B_CODE_OFF = BM * CB;                 // 16384
-constexpr int A_SC_OFF = B_CODE_OFF + BN * CB;      // 32768
-constexpr int B_SC_OFF = A_SC_OFF + BM * 16;        // 36864 (fp16 scales, 8 per row)
-constexpr int STAGE = B_SC_OFF + BN * 16;           // 40960
+constexpr int A_SC_OFF = B_CODE_OFF + BN * CB;      // 32768 (E4M3, 8 bytes per row)
+constexpr int B_SC_OFF = A_SC_OFF + BM * 8;         // 34816
+constexpr int STAGE = B_SC_OFF + BN * 8;            // 36864
+constexpr int DMA_PER_CHUNK = 12;                   // per wave: 8 code + 4 scale loads
 
-__device__ __forceinline__ int swzb(int row, int piece) {
-  return row * CB + ((piece ^ ((row >> 2) & 3)) << 4);
+typedef const void __attribute__((address_space(1)))* gptr_t;
+typedef void __attribute__((address_space(3)))* lptr_t;
+
+// s_waitcnt immediate that waits for at most n outstanding vector-memory
+// operations and leaves the other counters alone
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// four E4M3 bytes -> two dwords of fp16 pairs (exact)
-__device__ __forceinline__ uint2 e4m3x4_to_f16(uint32_t w) {
-  const uint32_t t = w & 0x78787878u;
-  const bool any_sub = ((t - 0x01010101u) & ~t & 0x80808080u) != 0u;   // some exponent field 0
-  uint2 r;
-  if (!any_sub) {
-    const uint32_t lo2 = __builtin_amdgcn_perm(0u, w, 0x0c010c00u);     // b0 | b1 << 16
-    const uint32_t hi2 = __builtin_amdgcn_perm(0u, w, 0x0c030c02u);     // b2 | b3 << 16
-    r.x = (lo2 << 7) + 0x20002000u;
-    r.y = (hi2 << 7) + 0x20002000u;
-  } else {
-    r.x = e4m3_to_f16_bits(w & 255u) | (e4m3_to_f16_bits((w >> 8) & 255u) << 16);
-    r.y = e4m3_to_f16_bits((w >> 16) & 255u) | (e4m3_to_f16_bits(w >> 24) << 16);
-  }
-  return r;
+// byte `which` of an E4M3 pair -> that scale as fp16 in both halves (exact,
+// subnormal scales included): the byte shifted left by 7 is an fp16 whose
+// value is the E4M3 value times 2^-8, normal and subnormal alike, and the
+// multiply by 256 is exact
+__device__ __forceinline__ uint32_t e4m3_dup_f16(uint32_t pair, int which) {
+  const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
+  const uint32_t d = __builtin_amdgcn_perm(0u, pair, which ? 0x0c010c01u : 0x0c000c00u) << 7;
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d) * k256);
 }
 
-template <bool FULLK>
+struct Frag {
+  uint4 a[4], b[4];
+  uint32_t sa[4], sb[4];   // two raw E4M3 scales (blocks 2p, 2p + 1) per row
+};
+
 __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  // one LDS object per stage, addressed with compile-time stage indices, so
+  // the compiler can tell that reads of one stage do not wait for the
+  // global -> LDS loads still filling another
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t stage2[STAGE];
+  uint8_t* const stages[NST] = {stage0, stage1, stage2};
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, h = lane >> 5;
   const int K = g.K;
   const int64_t N = g.N;
+  const int nk = K / BK;
 
   const int nbm = (int)((g.M + BM - 1) / BM), nbn = (int)((N + BN - 1) / BN);
   const int nb = nbm * nbn;
@@ -456,69 +497,93 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   const int64_t m0 = (int64_t)(first + in % gsz) * BM;
   const int64_t n0 = (int64_t)(in / gsz) * BN;
   const int64_t m_end = g.M;
+  // rows past the end of A or W read the last row again: their products land
+  // only in output rows / columns that are never stored
+  const int a_last = (int)min<int64_t>(BM - 1, g.M - 1 - m0);
+  const int b_last = (int)min<int64_t>(BN - 1, N - 1 - n0);
 
   const uint32_t cstride = (uint32_t)(K / 2), sstride = (uint32_t)(K / 16);
-  // 32-bit offsets from the (uniform) operand bases keep the staging state small
   const uint8_t* const a_base = g.a_codes + (size_t)m0 * cstride;
   const uint8_t* const b_base = g.w_codes + (size_t)n0 * cstride;
-  uint32_t a_off[4], b_off[4];
-  uint32_t ab_ok = 0;
+  // direct loads: instruction `it` of this wave fills the 1 KiB of LDS that
+  // holds tile rows 16 * (4 * it + wave) .. + 15; lane l writes 16 bytes at
+  // l * 16, i.e. row 16 * c + l / 4, swizzled slot l % 4, which holds the
+  // logical 16-byte piece slot ^ f(row)
+  uint32_t a_goff[4], b_goff[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int q = it * 256 + tid;
-    const int r = q >> 2;
-    const bool aok = m0 + r < m_end, bok = n0 + r < N;
-    ab_ok |= (aok ? 1u : 0u) << it;
-    ab_ok |= (bok ? 1u : 0u) << (4 + it);
-    a_off[it] = (aok ? (uint32_t)r : 0u) * cstride + (uint32_t)(q & 3) * 16u;
-    b_off[it] = (bok ? (uint32_t)r : 0u) * cstride + (uint32_t)(q & 3) * 16u;
+    const int row = 16 * (4 * it + wave) + (lane >> 2);
+    const int piece = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
+    a_goff[it] = (uint32_t)min(row, a_last) * cstride + (uint32_t)piece * 16u;
+    b_goff[it] = (uint32_t)min(row, b_last) * cstride + (uint32_t)piece * 16u;
   }
-  const bool as_ok = m0 + tid < m_end, bs_ok = n0 + tid < N;
+  // scale loads: instruction `it` of this wave fills 256 bytes of LDS (rows
+  // 32 * (4 * it + wave) .. + 31, 8 bytes each); lane l loads dword l % 2 of
+  // row 32 * c + l / 2
   const uint8_t* const as_base = g.a_scales + (size_t)m0 * sstride;
   const uint8_t* const bs_base = g.w_scales + (size_t)n0 * sstride;
-  const uint32_t as_off = (as_ok ? (uint32_t)tid : 0u) * sstride;
-  const uint32_t bs_off = (bs_ok ? (uint32_t)tid : 0u) * sstride;
+  uint32_t as_goff[2], bs_goff[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int row = 32 * (4 * it + wave) + (lane >> 1);
+    as_goff[it] = (uint32_t)min(row, a_last) * sstride + (uint32_t)(lane & 1) * 4u;
+    bs_goff[it] = (uint32_t)min(row, b_last) * sstride + (uint32_t)(lane & 1) * 4u;
+  }
 
-  uint4 pa[4], pb[4];
-  uint2 psa, psb;
-  auto load = [&](int kc) {
-    const int k0 = kc * BK;
+  // LDS read offsets within a stage for half s2 = 0 (s2 = 1: code ^ 16,
+  // scale + 2); piece p = 2 h + s2 holds scale blocks 2p and 2p + 1
+  uint32_t ca_off[4], cb_off[4], sa_off[4], sb_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int ra = wm * 128 + q * 32 + l32, rb = wn * 128 + q * 32 + l32;
+    ca_off[q] = (uint32_t)swz(ra, 2 * h);
+    cb_off[q] = (uint32_t)(B_CODE_OFF + swz(rb, 2 * h));
+    sa_off[q] = (uint32_t)(A_SC_OFF + ra * 8 + 4 * h);
+    sb_off[q] = (uint32_t)(B_SC_OFF + rb * 8 + 4 * h);
+  }
+
+  // all global -> LDS traffic of chunk kc (clamped: chunks past the end
+  // reload the last one into a stage nobody reads again)
+  auto issue_chunk = [&](int kc, uint8_t* const sbase) {
+    const uint32_t kb = (uint32_t)min(kc, nk - 1) * (BK / 2);
+    const uint32_t ks = (uint32_t)min(kc, nk - 1) * (BK / 16);
+    uint8_t* const dst = sbase + wave * 1024;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int kel = k0 + 32 * ((it * 256 + tid) & 3);
-      pa[it] = (((ab_ok >> it) & 1u) && (FULLK || kel < K))
-                   ? *(const uint4*)(a_base + a_off[it] + k0 / 2) : make_uint4(0, 0, 0, 0);
-      pb[it] = (((ab_ok >> (4 + it)) & 1u) && (FULLK || kel < K))
-                   ? *(const uint4*)(b_base + b_off[it] + k0 / 2) : make_uint4(0, 0, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)(a_base + kb + a_goff[it]),
+                                       (lptr_t)(dst + it * 4096), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)(b_base + kb + b_goff[it]),
+                                       (lptr_t)(dst + B_CODE_OFF + it * 4096), 16, 0, 0);
     }
-    if constexpr (FULLK) {
-      psa = as_ok ? *(const uint2*)(as_base + as_off + k0 / 16) : make_uint2(0, 0);
-      psb = bs_ok ? *(const uint2*)(bs_base + bs_off + k0 / 16) : make_uint2(0, 0);
-    } else {
-      uint32_t sa4[4] = {0, 0, 0, 0}, sb4[4] = {0, 0, 0, 0};
+    uint8_t* const sdst = sbase + wave * 256;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (k0 + 32 * q < K) {
-          if (as_ok) sa4[q] = *(const uint16_t*)(as_base + as_off + k0 / 16 + 2 * q);
-          if (bs_ok) sb4[q] = *(const uint16_t*)(bs_base + bs_off + k0 / 16 + 2 * q);
-        }
-      }
-      psa = make_uint2(sa4[0] | (sa4[1] << 16), sa4[2] | (sa4[3] << 16));
-      psb = make_uint2(sb4[0] | (sb4[1] << 16), sb4[2] | (sb4[3] << 16));
+    for (int it = 0; it < 2; ++it) {
+      __builtin_amdgcn_global_load_lds((gptr_t)(as_base + ks + as_goff[it]),
+                                       (lptr_t)(sdst + A_SC_OFF + it * 1024), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((gptr_t)(bs_base + ks + bs_goff[it]),
+                                       (lptr_t)(sdst + B_SC_OFF + it * 1024), 4, 0, 0);
     }
   };
-  auto store = [&](int stg) {
-    uint8_t* base = smem + stg * STAGE;
+  auto read_frag = [&](Frag& f, const uint8_t* const base, int s2) {
+    const uint32_t cx = s2 ? 16u : 0u, sx = s2 ? 2u : 0u;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int q = it * 256 + tid;
-      *(uint4*)(base + swzb(q >> 2, q & 3)) = pa[it];
-      *(uint4*)(base + B_CODE_OFF + swzb(q >> 2, q & 3)) = pb[it];
+    for (int q = 0; q < 4; ++q) {
+      f.a[q] = *(const uint4*)(base + (ca_off[q] ^ cx));
+      f.sa[q] = *(const uint16_t*)(base + sa_off[q] + sx);
     }
-    const uint2 a0 = e4m3x4_to_f16(psa.x), a1 = e4m3x4_to_f16(psa.y);
-    const uint2 b0 = e4m3x4_to_f16(psb.x), b1 = e4m3x4_to_f16(psb.y);
-    *(uint4*)(base + A_SC_OFF + tid * 16) = make_uint4(a0.x, a0.y, a1.x, a1.y);
-    *(uint4*)(base + B_SC_OFF + tid * 16) = make_uint4(b0.x, b0.y, b1.x, b1.y);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f.b[q] = *(const uint4*)(base + (cb_off[q] ^ cx));
+      f.sb[q] = *(const uint16_t*)(base + sb_off[q] + sx);
+    }
+  };
+  auto decode = [&](const Frag& f, int j, half8v* da, half8v* db) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      da[q] = decode8(word(f.a[q], j), e4m3_dup_f16(f.sa[q], j >= 2));
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      db[q] = decode8(word(f.b[q], j), e4m3_dup_f16(f.sb[q], j >= 2));
   };
 
   f32x16v acc[4][4];
@@ -529,54 +594,75 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  auto compute = [&](int stg) {
-    const uint8_t* base = smem + stg * STAGE;
+  auto mfma16 = [&](const half8v* da, const half8v* db) {
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int p = 2 * h + s2;
-      uint4 ra[4], rb[4];
-      uint32_t sa[4], sb[4];
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const int row = wm * 128 + mi * 32 + l32;
-        ra[mi] = *(const uint4*)(base + swzb(row, p));
-        sa[mi] = *(const uint32_t*)(base + A_SC_OFF + row * 16 + h * 8 + s2 * 4);
+      for (int ni = 0; ni < 4; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[mi], db[ni], acc[mi][ni], 0, 0, 0);
+  };
+
+  // one half-chunk: MFMAs of steps j = 0..3 on `cur`, decoding step j + 1
+  // (or step 0 of `next` after the last) into the other register set
+  // The instruction order is pinned step by step: each MFMA is followed by
+  // about five independent VALU instructions (the matrix core runs them in
+  // its shadow); in the first step of a half the sixteen LDS reads of the
+  // next half, and the `vmem` global -> LDS loads, go out behind the MFMAs.
+  half8v da[2][4], db[2][4];
+  auto half_chunk = [&](const Frag& cur, const Frag& next, int vmem) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (j < 3)
+        decode(cur, j + 1, da[(j + 1) & 1], db[(j + 1) & 1]);
+      else
+        decode(next, 0, da[0], db[0]);
+      mfma16(da[j & 1], db[j & 1]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
+        if (j == 0) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
+          if (i < vmem) __builtin_amdgcn_sched_group_barrier(0x060, 1, 0);   // VMEM
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);      // VALU
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);      // VALU
+        }
       }
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int row = wn * 128 + ni * 32 + l32;
-        rb[ni] = *(const uint4*)(base + B_CODE_OFF + swzb(row, p));
-        sb[ni] = *(const uint32_t*)(base + B_SC_OFF + row * 16 + h * 8 + s2 * 4);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        half8v af[4], bf[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-          af[mi] = decode8(word(ra[mi], j), j < 2 ? dup_lo(sa[mi]) : dup_hi(sa[mi]));
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          bf[ni] = decode8(word(rb[ni], j), j < 2 ? dup_lo(sb[ni]) : dup_hi(sb[ni]));
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-            acc[mi][ni] =
-                __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  const int nk = (K + BK - 1) / BK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kc = 0; kc < nk; ++kc) {
-    if (kc + 1 < nk) load(kc + 1);
-    compute(kc & 1);
-    if (kc + 1 < nk) store((kc + 1) & 1);
-    __syncthreads();
+  // prologue: chunks 0..2 in flight
+  issue_chunk(0, stages[0]);
+  issue_chunk(1, stages[1]);
+  issue_chunk(2, stages[2]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));   // chunk 0 has landed
+  lds_barrier();
+  Frag f0, f1;
+  read_frag(f0, stages[0], 0);
+  decode(f0, 0, da[0], db[0]);
+
+  // chunk kc lives in stage kc % 3
+  auto chunk = [&](int kc, uint8_t* const cur, uint8_t* const nxt) {
+    read_frag(f1, cur, 1);
+    half_chunk(f0, f1, 0);
+    // chunk kc + 1 has landed (chunk kc + 2 may still be in flight); after
+    // the barrier every wave is done with stage `cur`
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA_PER_CHUNK));
+    lds_barrier();
+    read_frag(f0, nxt, 0);
+    issue_chunk(kc + 3, cur);
+    half_chunk(f1, f0, DMA_PER_CHUNK);
+  };
+  int kc = 0;
+  for (; kc + 3 <= nk; kc += 3) {
+    chunk(kc, stages[0], stages[1]);
+    chunk(kc + 1, stages[1], stages[2]);
+    chunk(kc + 2, stages[2], stages[0]);
   }
+  if (kc < nk) chunk(kc, stages[0], stages[1]);
+  if (kc + 1 < nk) chunk(kc + 1, stages[1], stages[2]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[0] : 1.0f;
 #pragma unroll
@@ -663,12 +749,9 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
     return grouped ? launch_t<false, true, true>(g, max_mtiles, stream)
                    : launch_t<false, false, true>(g, max_mtiles, stream);
   }
-  if (!grouped && g.epilogue == kEpiStore && g.M >= 512 && g.N >= 512) {
+  if (!grouped && fullk && g.epilogue == kEpiStore && g.M >= 512 && g.N >= 512) {
     const int64_t nb = ((g.M + big::BM - 1) / big::BM) * ((g.N + big::BN - 1) / big::BN);
-    if (fullk)
-      hipLaunchKernelGGL(big::gemm_nvfp4_big_kernel<true>, dim3((unsigned)nb), dim3(256), 0, stream, g);
-    else
-      hipLaunchKernelGGL(big::gemm_nvfp4_big_kernel<false>, dim3((unsigned)nb), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL(big::gemm_nvfp4_big_kernel, dim3((unsigned)nb), dim3(256), 0, stream, g);
     return hipGetLastError();
   }
   if (fullk)
