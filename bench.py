@@ -30,7 +30,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "NVFP4 W4A4+RAC GEMM TFLOP/s & quantizer GB/s, % of MI355X roofline"
 PEAK_FP16_TFLOPS = 2516.6          # MI355X dense fp16/bf16 MFMA
+PEAK_FP4_TFLOPS = 10100.0          # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+
+# HBM bytes per launch of the dense GEMM kernel from rocprofv3 --pmc FETCH_SIZE /
+# WRITE_SIZE (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives
+# (fetch x 2.00, write x 1.00); valid only for the kernel source it was taken on
+TRAFFIC = {"gemm_src_sha256": "9030ac17cfece613c12bc89bcdcc166042fbdd7b83a3d562f80db87b00953209",
+           "fetch_kib": 226080.0, "fetch_scale": 2.0, "write_kib": 286720.0, "write_scale": 1.0}
 
 
 def _args():
@@ -40,13 +47,45 @@ def _args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--quant-iters", type=int, default=50)
+    p.add_argument("--no-mx", action="store_true", help="skip the MXFP4 comparison leg")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return p.parse_args()
 
 
+def _traffic():
+    import hashlib
+    src = os.path.join(ROOT, "fp4_w4a4_quantized_nvfp4_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC["gemm_src_sha256"]:
+            return None
+    return round((TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"]
+                  + TRAFFIC["write_kib"] * TRAFFIC["write_scale"]) * 1024.0)
+
+
+def _say(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _copy_probe():
+    """A plain device-to-device copy of known size: the reference point that
+    scales the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of a profile."""
+    import torch
+    n = 1 << 30
+    src = torch.empty((n,), dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}),
+          flush=True)
+
+
 def _cpu_baseline():
-    """The oracle as it stands, on a bounded sample of the same step:
-    the first 2048 of the 8192 activation rows (quantize, score, select,
-    residual gather, fp64 W4A4+RAC GEMM against all 14336 weight rows)."""
+    """The oracle as it stands on the same step: all 8192 activation rows
+    (quantize, score, select, residual gather, fp64 W4A4+RAC GEMM against all
+    14336 weight rows); about ten seconds on the host cores."""
     import oracle
     from workloads import WORKLOADS, make_activations, make_weight
     try:
@@ -55,7 +94,7 @@ def _cpu_baseline():
     except Exception:
         threads = 1
     wl = WORKLOADS["dense_8192x14336x4096"]
-    rows = 2048
+    rows = wl.rows
     xb = make_activations(wl)[:rows]
     wb = make_weight(wl)
     Wq = oracle.nvfp4_quantize(wb)          # offline weight preparation, not timed
@@ -74,6 +113,9 @@ def _cpu_baseline():
 
 def main():
     a = _args()
+    if a.copy_probe:
+        _copy_probe()
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (this build runs "
               "the hot path on a single MI355X, no collectives)", file=sys.stderr)
@@ -90,6 +132,7 @@ def main():
     def todev(b):
         return torch.from_numpy(b.view(np.int16)).to(dev)
 
+    _say("generating the dense workload")
     xb = make_activations(wl)
     x = [todev(xb)]
     # a second copy with the rows rotated, so consecutive steps do not hit the
@@ -130,6 +173,7 @@ def main():
         if events:
             events[2].record(stream)
 
+    _say("dense step: warmup + timed steps")
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -148,6 +192,7 @@ def main():
     achieved = step_flops / (t_gemm * 1e-3) / 1e12
 
     # ---------------------------------------------------------------- quantizer line
+    _say("quantizer workload")
     wq = WORKLOADS["quant_16384x7168"]
     qb = make_activations(wq)
     Mq, Kq, kq = wq.rows, wq.cols, wq.topk_channels
@@ -186,6 +231,48 @@ def main():
     q_gbs = q_bytes / (tq_ms * 1e-3) / 1e9
     q1_gbs = q_bytes / (tq1_ms * 1e-3) / 1e9
 
+    # ---------------------------------------------------------------- MXFP4 leg
+    # the same dense shape with MXFP4 operands on the scaled FP4 matrix
+    # instruction (E8M0 per 32, no tensor scale), RAC k = 128 on bf16: the
+    # comparison the two GEMM designs are judged by
+    mx = None
+    if not a.no_mx:
+        _say("MXFP4 leg")
+        Wm = q4.prepare_weight(todev(make_weight(wl)), fmt=q4.MXFP4)
+        cm = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        smx = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+        scm = torch.empty((K,), dtype=torch.float64, device=dev)
+        im = torch.empty((k,), dtype=torch.int32, device=dev)
+        mws_b = L.q4_quantize_workspace_size(M, K, 1)
+        mws = torch.empty((mws_b,), dtype=torch.uint8, device=dev)
+
+        def mstep(i):
+            q4._check(L.mxfp4_quantize(x[i % 2].data_ptr(), M, K, cm.data_ptr(), smx.data_ptr(),
+                                       scm.data_ptr(), k, im.data_ptr(), mws.data_ptr(), mws_b, sp))
+            q4._check(L.rac_gemm(1, M, N, K, x[i % 2].data_ptr(), cm.data_ptr(), smx.data_ptr(),
+                                 None, Wm["codes"].data_ptr(), Wm["scales"].data_ptr(), None,
+                                 Wm["w_hi_t"].data_ptr(), im.data_ptr(), k, Y.data_ptr(), 1,
+                                 rws.data_ptr(), rws_b, sp))
+        for i in range(3):
+            mstep(i)
+        mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+        for i in range(5):
+            q4._check(L.mxfp4_quantize(x[i % 2].data_ptr(), M, K, cm.data_ptr(), smx.data_ptr(),
+                                       scm.data_ptr(), k, im.data_ptr(), mws.data_ptr(), mws_b, sp))
+            mev[i][0].record(stream)
+            q4._check(L.rac_gemm(1, M, N, K, x[i % 2].data_ptr(), cm.data_ptr(), smx.data_ptr(),
+                                 None, Wm["codes"].data_ptr(), Wm["scales"].data_ptr(), None,
+                                 Wm["w_hi_t"].data_ptr(), im.data_ptr(), k, Y.data_ptr(), 1,
+                                 rws.data_ptr(), rws_b, sp))
+            mev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_mx = float(np.mean([e[0].elapsed_time(e[1]) for e in mev]))
+        mx_tf = step_flops / (t_mx * 1e-3) / 1e12
+        mx = {"workload": "dense_8192x14336x4096 as MXFP4 (scaled FP4 MFMA), RAC k=128, bf16 out",
+              "rac_gemm_ms": round(t_mx, 4), "tflops": round(mx_tf, 2),
+              "frac_fp4_peak": round(mx_tf / PEAK_FP4_TFLOPS, 4)}
+        del Wm
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -204,8 +291,8 @@ def main():
                    "M": M, "N": N, "K": K, "rac_k": k, "format": "nvfp4", "out": "bf16"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-                     "traffic": None, "kernel": "rac_gemm call (residual + weight gathers, "
-                                                "fused W4A4+RAC GEMM)",
+                     "traffic": _traffic(), "kernel": "rac_gemm call (residual + weight "
+                                                      "gathers, fused W4A4+RAC GEMM)",
                      "ms": round(float(t_gemm), 4)},
         "breakdown_ms": {"nvfp4_quantize": round(float(t_quant), 4), "rac_gemm": round(float(t_gemm), 4)},
         "quantizer": {"workload": "quant_16384x7168 (Student-t(3), 1% outlier channels, top-64)",
@@ -217,7 +304,10 @@ def main():
         "context": "pages: ~16% end-to-end rollout gain over FP8 and FP4 ~2x FP8 peak, both on "
                    "NVIDIA Blackwell (not targets)",
     }
+    if mx is not None:
+        out["mxfp4"] = mx
     if not a.no_cpu:
+        _say("oracle CPU baseline")
         out["cpu_baseline"] = _cpu_baseline()
     print(json.dumps(out), flush=True)
 

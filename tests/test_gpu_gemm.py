@@ -42,13 +42,29 @@ def _quant_pair(m, xb, wb, fmt="nv", ts=None):
     return x, A, W, oracle.nvfp4_quantize(xb, tensor_scale=ts), oracle.nvfp4_quantize(wb, tensor_scale=ts)
 
 
-def test_exact_special_case_bit_identical():
-    say("gemm exact special case")
+# E4M3 subnormal block scales m * 2^-9, m = 1..7
+SUBNORMAL_SCALES = tuple(m * 2.0 ** -9 for m in range(1, 8))
+
+
+@pytest.mark.parametrize("M,N,K,scales", [(300, 200, 512, (0.5, 1.0, 2.0)),
+                                          (512, 768, 512, (0.5, 1.0, 2.0)),
+                                          (512, 768, 512, SUBNORMAL_SCALES),
+                                          (300, 200, 512, SUBNORMAL_SCALES)],
+                         ids=["small", "large_tile", "large_tile_subnormal", "small_subnormal"])
+def test_exact_special_case_bit_identical(M, N, K, scales):
+    """E2M1 values times exact E4M3 scales with a supplied tensor scale of 1:
+    every product and partial sum is exact in fp32, so any correct GEMM gives
+    the oracle's result bit for bit (the subnormal case checks that E4M3
+    subnormal block scales are widened exactly)."""
+    say(f"gemm exact special case {M}x{N}x{K}")
     m = q4()
-    rng = np.random.default_rng(11)
-    xb = _exact_operand(rng, 300, 512)
-    wb = _exact_operand(rng, 200, 512)
+    rng = np.random.default_rng(11 + M + len(scales))
+    xb = _exact_operand(rng, M, K, scales)
+    wb = _exact_operand(rng, N, K, scales)
     x, A, W, Ao, Wo = _quant_pair(m, xb, wb, ts=1.0)
+    assert np.array_equal(host(A["scales"]), Ao.scales)
+    if scales is SUBNORMAL_SCALES:
+        assert Ao.scales.max() < 8          # exponent field 0: subnormal E4M3
     Y = host(m.w4a4_gemm(A, W))
     ref = oracle.w4a4_gemm(Ao, Wo)
     assert np.array_equal(Y.astype(np.float64), ref)
