@@ -301,12 +301,12 @@ __global__ __launch_bounds__(256) void score_reduce_kernel(const double* __restr
   if (j >= cols) return;
   double s = 0.0;
   int64_t t = 0;
-  for (; t + 16 <= ngroups; t += 16) {
-    double p[16];
+  for (; t + 32 <= ngroups; t += 32) {
+    double p[32];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) p[u] = partial[(t + u) * cols + j];
+    for (int u = 0; u < 32; ++u) p[u] = partial[(t + u) * cols + j];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) s += p[u];
+    for (int u = 0; u < 32; ++u) s += p[u];
   }
   for (; t < ngroups; ++t) s += partial[t * cols + j];
   scores[j] = s;
@@ -408,6 +408,122 @@ __global__ __launch_bounds__(1024) void topk_kernel(const double* __restrict__ s
     base_eq += tot_eq;
     base_sel += tot_sel;
   }
+}
+
+// Register-resident variant for cols <= 1024 * KPT: thread t holds the keys
+// of channels t*KPT .. t*KPT + KPT - 1 (loaded once), the radix passes stop as
+// soon as the bin that holds the k-th largest key is taken whole, and the
+// emit pass needs two block scans (ties by channel index, then positions).
+__device__ __forceinline__ int block_excl_scan_int(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int s = wsum[i];
+    before += (i < w) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict__ scores,
+                                                        int32_t cols, int32_t k,
+                                                        int32_t* __restrict__ out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_kleft, s_done;
+  __shared__ int wsum[16];
+  const uint64_t* keys = (const uint64_t*)scores;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = tid * KPT;
+  uint64_t kv[KPT];
+#pragma unroll
+  for (int q = 0; q < KPT; ++q) kv[q] = j0 + q < cols ? keys[j0 + q] : 0ull;
+  uint64_t prefix = 0, mask = 0;
+  int kleft = k;
+  bool done = false;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const bool valid = j0 + q < cols && (kv[q] & mask) == prefix;
+      const uint32_t digit = (uint32_t)(kv[q] >> shift) & 255u;
+      uint64_t pending = __ballot(valid);
+      while (pending) {
+        const int leader = __ffsll((unsigned long long)pending) - 1;
+        const uint32_t d0 = (uint32_t)__shfl((int)digit, leader, 64);
+        const uint64_t same = __ballot(valid && digit == d0) & pending;
+        if (lane == leader) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+        pending &= ~same;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      uint32_t c[4];
+      uint32_t sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[q] = hist[255 - 4 * lane - q];
+        sum += c[q];
+      }
+      uint32_t incl = sum;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_up((int)incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      uint32_t cum = incl - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (cum < (uint32_t)kleft && cum + c[q] >= (uint32_t)kleft) {
+          s_prefix = prefix | ((uint64_t)(255 - 4 * lane - q) << shift);
+          s_kleft = kleft - (int)cum;
+          s_done = (cum + c[q] == (uint32_t)kleft) ? 1 : 0;   // the whole bin is taken
+        }
+        cum += c[q];
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    kleft = s_kleft;
+    mask |= 0xffull << shift;
+    done = s_done != 0;
+    if (done) break;
+  }
+  // keys whose top bits exceed the boundary prefix are all taken; keys on it
+  // are all taken (done) or the first kleft of them by channel index
+  int neq = 0;
+#pragma unroll
+  for (int q = 0; q < KPT; ++q) neq += (j0 + q < cols && (kv[q] & mask) == prefix) ? 1 : 0;
+  int tot;
+  int eq_rank = block_excl_scan_int(neq, wsum, &tot);
+  bool sel[KPT];
+  int nsel = 0;
+#pragma unroll
+  for (int q = 0; q < KPT; ++q) {
+    const bool valid = j0 + q < cols;
+    const uint64_t mk = kv[q] & mask;
+    const bool eq = valid && mk == prefix;
+    sel[q] = valid && (mk > prefix || (eq && (done || eq_rank < kleft)));
+    eq_rank += eq ? 1 : 0;
+    nsel += sel[q] ? 1 : 0;
+  }
+  int pos = block_excl_scan_int(nsel, wsum, &tot);
+#pragma unroll
+  for (int q = 0; q < KPT; ++q)
+    if (sel[q]) out[pos++] = j0 + q;
 }
 
 // ====================================================================== gathers
@@ -599,17 +715,26 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
   }
   hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0,
                      stream, (const double*)partial, ngroups, (int32_t)cols, scores);
-  if (topk > 0)
-    hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(1024), 0, stream, (const double*)scores,
-                       (int32_t)cols, topk, chan_idx);
+  if (topk > 0) return launch_select(scores, cols, topk, chan_idx, stream);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const double* scores, int64_t cols, int32_t topk, int32_t* idx,
                          hipStream_t stream) {
-  if (topk > 0)
-    hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(1024), 0, stream, scores, (int32_t)cols, topk,
-                       idx);
+  if (topk <= 0) return hipSuccess;
+  const int c = (int)cols;
+  if (cols <= 1024)
+    hipLaunchKernelGGL(topk_reg_kernel<1>, dim3(1), dim3(1024), 0, stream, scores, c, topk, idx);
+  else if (cols <= 2048)
+    hipLaunchKernelGGL(topk_reg_kernel<2>, dim3(1), dim3(1024), 0, stream, scores, c, topk, idx);
+  else if (cols <= 4096)
+    hipLaunchKernelGGL(topk_reg_kernel<4>, dim3(1), dim3(1024), 0, stream, scores, c, topk, idx);
+  else if (cols <= 8192)
+    hipLaunchKernelGGL(topk_reg_kernel<8>, dim3(1), dim3(1024), 0, stream, scores, c, topk, idx);
+  else if (cols <= 16384)
+    hipLaunchKernelGGL(topk_reg_kernel<16>, dim3(1), dim3(1024), 0, stream, scores, c, topk, idx);
+  else
+    hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(1024), 0, stream, scores, c, topk, idx);
   return hipGetLastError();
 }
 

@@ -157,3 +157,20 @@ def test_quantizer_workload_full_size():
     d = make_inputs("quant_16384x7168")
     g, o = _compare_nvfp4(d["x"], 64)
     say("full-size quantizer parity ok; s_t", float(o.tensor_scale))
+
+
+@pytest.mark.parametrize("cols", [1, 100, 1024, 1500, 4096, 7168, 8192, 10000, 16384, 20000])
+def test_select_channels_ties(cols):
+    """Top-k over crafted fp64 scores: long runs of equal values, zeros, values
+    that share their top bytes, k at the edges and inside a tie run; every
+    register-resident size class and the general kernel."""
+    m = q4()
+    rng = np.random.default_rng(cols)
+    base = rng.choice([0.0, 1.0, 2.5, 1e-300, 3.0e5], size=cols)
+    base = base * (1.0 + rng.integers(0, 3, size=cols) * 2.0 ** -50)   # ties in the low bits only
+    base[rng.random(cols) < 0.3] = 7.0                                   # a long run of ties
+    for k in sorted({1, min(cols, 2), min(cols, 64), min(cols, 1000), min(cols // 2 or 1, 1024),
+                     min(cols, 1024)}):
+        got = m.q4_select_channels(dev(base), k)
+        ref = oracle.select_topk(base, k)
+        assert np.array_equal(host(got), ref), (cols, k)
