@@ -119,16 +119,46 @@ __device__ uint32_t e4m3_mantissa_entry(int ma, double Dp) {
   return (uint32_t)(m | ((adj + 1) << 3));
 }
 
-// One workgroup = 8 waves = one 256-row group of one 512-channel strip; wave w
-// owns the 32-row tile w of the group, lane l owns channels strip*512 + 8l..+7.
+// One workgroup = 8 waves = one 256-row group of one strip of 64 * CPL
+// channels; wave w owns the 32-row tile w of the group, lane l owns channels
+// strip * 64 * CPL + CPL * l .. + CPL - 1 (CPL = 8 or 16 channels per lane).
 // Every lane sums its squared residuals over its tile's rows in order; the
 // eight tile sums are then added in tile order through LDS, giving one fp64
 // partial per (group, channel).
-template <bool MX>
-__global__ __launch_bounds__(512) void quantize_kernel(QuantKArgs a) {
+//
+// Codes: the FP4 conversion instruction on v * (1 - 2^-20) and v * (1 + 2^-20),
+// v = x / (s s_t) (approximate reciprocal, relative error < 2^-22).  Where the
+// two brackets agree the code is exact.  Where they differ, x lies within
+// 2^-20 of a rounding midpoint (frequent: s_t is a rounded simple rational, so
+// many x / (s s_t) fall within 2^-24 of a midpoint); each such element is
+// settled by comparing |x| with midpoint * s * s_t, exact in fp64, one element
+// per lane per round, all lanes of the wave at once.
+template <int CPL>
+__device__ __forceinline__ float lane_x(const uint4* v, int pos) {
+  const int d = pos >> 1;
+  uint4 a = v[0];
+  if constexpr (CPL == 16) {
+    if (d & 4) a = v[1];
+  }
+  const uint32_t lo2 = (d & 2) ? a.z : a.x, hi2 = (d & 2) ? a.w : a.y;
+  const uint32_t w = (d & 1) ? hi2 : lo2;
+  return (pos & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+// 4 * (E2M1 midpoint above magnitude m), m = 0..6: 1 3 5 7 10 14 20
+__device__ __forceinline__ float e2m1_mid_above(uint32_t m) {
+  const uint32_t q = __builtin_amdgcn_perm(0x00140e0au, 0x07050301u, m);
+  return (float)(q & 255u) * 0.25f;
+}
+
+template <bool MX, int CPL>
+__global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
+  constexpr int NW = CPL / 8;              // code words (8 nibbles) per lane per row
+  constexpr int U = 32 / CPL;              // rows loaded ahead
+  constexpr int STRIP = 64 * CPL;
   __shared__ uint8_t tab[128];
   __shared__ uint32_t red[16];
-  __shared__ double part[kScoreGroupTiles][64][8];
+  __shared__ double part[kScoreGroupTiles][64][CPL + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int64_t wg = blockIdx.x;
   const int64_t nwg = a.ngroups * a.nstrips;
@@ -136,7 +166,7 @@ __global__ __launch_bounds__(512) void quantize_kernel(QuantKArgs a) {
   const int64_t group = wg / a.nstrips;
   const int strip = (int)(wg % a.nstrips);
   const int cols = a.cols;
-  const int col0 = strip * 512 + lane * 8;
+  const int col0 = strip * STRIP + lane * CPL;
   const bool active = col0 < cols;
 
   float st = 1.0f;
@@ -152,46 +182,57 @@ __global__ __launch_bounds__(512) void quantize_kernel(QuantKArgs a) {
   __syncthreads();
   const float inv6st = 1.0f / (6.0f * st);
   const double st6 = 6.0 * (double)st;
+  const double st64 = (double)st;
 
-  double acc[8];
+  double acc[CPL];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0;
+  for (int i = 0; i < CPL; ++i) acc[i] = 0.0;
 
   const int64_t r0 = group * (kScoreTileRows * kScoreGroupTiles) + wave * kScoreTileRows;
   const int nr = (int)max((int64_t)0, min((int64_t)kScoreTileRows, a.rows - r0));
   const uint16_t* xp = a.x + (nr > 0 ? r0 : 0) * cols + (active ? col0 : 0);
   const int64_t cstride = cols / 2, sstride = MX ? cols / 32 : cols / 16;
-  constexpr int U = 4;
 
-  uint4 cur[U], nxt[U];
+  uint4 cur[U][NW], nxt[U][NW];
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    cur[u] = (active && u < nr) ? *(const uint4*)(xp + (int64_t)u * cols) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < NW; ++q)
+      cur[u][q] = (active && u < nr) ? *(const uint4*)(xp + (int64_t)u * cols + 8 * q)
+                                     : make_uint4(0, 0, 0, 0);
 
   for (int rr = 0; rr < nr; rr += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      nxt[u] = (active && rr + U + u < nr) ? *(const uint4*)(xp + (int64_t)(rr + U + u) * cols)
-                                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < NW; ++q)
+        nxt[u][q] = (active && rr + U + u < nr)
+                        ? *(const uint4*)(xp + (int64_t)(rr + U + u) * cols + 8 * q)
+                        : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (rr + u >= nr) break;
       const int64_t row = r0 + rr + u;
-      float xf[8];
-      xf[0] = bf16_lo(cur[u].x); xf[1] = bf16_hi(cur[u].x);
-      xf[2] = bf16_lo(cur[u].y); xf[3] = bf16_hi(cur[u].y);
-      xf[4] = bf16_lo(cur[u].z); xf[5] = bf16_hi(cur[u].z);
-      xf[6] = bf16_lo(cur[u].w); xf[7] = bf16_hi(cur[u].w);
-      float m = fmaxf(fmaxf(fabsf(xf[0]), fabsf(xf[1])), fabsf(xf[2]));
-      m = fmaxf(fmaxf(m, fabsf(xf[3])), fabsf(xf[4]));
-      m = fmaxf(fmaxf(m, fabsf(xf[5])), fabsf(xf[6]));
-      m = fmaxf(m, fabsf(xf[7]));
-      m = fmaxf(m, dpp_quad_xor1(m));          // 16-element block = lane pair
+      float xf[CPL];
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        xf[8 * q + 0] = bf16_lo(cur[u][q].x); xf[8 * q + 1] = bf16_hi(cur[u][q].x);
+        xf[8 * q + 2] = bf16_lo(cur[u][q].y); xf[8 * q + 3] = bf16_hi(cur[u][q].y);
+        xf[8 * q + 4] = bf16_lo(cur[u][q].z); xf[8 * q + 5] = bf16_hi(cur[u][q].z);
+        xf[8 * q + 6] = bf16_lo(cur[u][q].w); xf[8 * q + 7] = bf16_hi(cur[u][q].w);
+      }
+      float m = 0.0f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) m = fmaxf(m, fabsf(xf[i]));
+      if constexpr (!MX && CPL == 8) m = fmaxf(m, dpp_quad_xor1(m));   // 16-block = lane pair
+      if constexpr (MX) {
+        m = fmaxf(m, dpp_quad_xor1(m));                                // 32-block
+        if constexpr (CPL == 8) m = fmaxf(m, dpp_quad_xor2(m));
+      }
       uint32_t sc;
       float s;
       bool ok;
       if constexpr (MX) {
-        m = fmaxf(m, dpp_quad_xor2(m));        // 32-element block = lane quad
         // floor(log2 m) - 2 clamped to [-127, 127]: exponent field - 129
         const int ef = (int)(__float_as_uint(m) >> 23);
         const int e = max(ef - 129, -127);
@@ -213,16 +254,22 @@ __global__ __launch_bounds__(512) void quantize_kernel(QuantKArgs a) {
       ok = ok && (S >= 0x1p-60f || S == 0.0f);
       const float rinv = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
       const float rlo = rinv * (1.0f - 0x1p-20f), rhi = rinv * (1.0f + 0x1p-20f);
-      uint32_t lo = 0, hi = 0;
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xf[0] * rlo, xf[1] * rlo, 1.0f, 0);
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xf[2] * rlo, xf[3] * rlo, 1.0f, 1);
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xf[4] * rlo, xf[5] * rlo, 1.0f, 2);
-      lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xf[6] * rlo, xf[7] * rlo, 1.0f, 3);
-      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xf[0] * rhi, xf[1] * rhi, 1.0f, 0);
-      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xf[2] * rhi, xf[3] * rhi, 1.0f, 1);
-      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xf[4] * rhi, xf[5] * rhi, 1.0f, 2);
-      hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xf[6] * rhi, xf[7] * rhi, 1.0f, 3);
-      uint32_t code = lo;
+      uint32_t code[NW], diff[NW];
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        uint32_t lo = 0, hi = 0;
+        const float* xq = xf + 8 * q;
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xq[0] * rlo, xq[1] * rlo, 1.0f, 0);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xq[2] * rlo, xq[3] * rlo, 1.0f, 1);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xq[4] * rlo, xq[5] * rlo, 1.0f, 2);
+        lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xq[6] * rlo, xq[7] * rlo, 1.0f, 3);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xq[0] * rhi, xq[1] * rhi, 1.0f, 0);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xq[2] * rhi, xq[3] * rhi, 1.0f, 1);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xq[4] * rhi, xq[5] * rhi, 1.0f, 2);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xq[6] * rhi, xq[7] * rhi, 1.0f, 3);
+        code[q] = lo;
+        diff[q] = lo ^ hi;
+      }
       if (__builtin_expect(!ok, 0)) {
         // a block scale outside the table's range or an extreme scale:
         // decide the scale and every code exactly
@@ -230,64 +277,92 @@ __global__ __launch_bounds__(512) void quantize_kernel(QuantKArgs a) {
           sc = m == 0.0f ? 0u : e4m3_scale_code(m, inv6st, st6);
           s = e4m3_to_f32(sc);
         }
-        code = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) code |= e2m1_nibble_exact(xf[i], s, st) << (4 * i);
-      } else if (__builtin_expect(__any(lo != hi), 0)) {
-        // values within 2^-20 of a rounding boundary: the two bracket codes are
-        // neighbours; compare |x| with their midpoint * s * st, exact in fp64
-        const uint32_t diff = lo ^ hi;
-        const double S64 = (double)s * (double)st;
+        for (int q = 0; q < NW; ++q) {
+          uint32_t c = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (__any((diff >> (4 * i)) & 15u)) {
-            const uint32_t ml = (lo >> (4 * i)) & 7u, mh = (hi >> (4 * i)) & 7u;
-            if (ml != mh) {
-              const uint32_t mlow = ml < mh ? ml : mh;     // thresholds between mlow and mlow+1
-              const double mid = 0.5 * ((double)e2m1_mag(mlow) + (double)e2m1_mag(mlow + 1u));
-              const double ax = (double)fabsf(xf[i]);
-              const double t = mid * S64;
-              const bool up = ax > t || (ax == t && ((mlow + 1u) & 1u) == 0u);
-              const uint32_t mag = up ? mlow + 1u : mlow;
-              code = (code & ~(7u << (4 * i))) | (mag << (4 * i));
-            }
+          for (int i = 0; i < 8; ++i) c |= e2m1_nibble_exact(xf[8 * q + i], s, st) << (4 * i);
+          code[q] = c;
+          diff[q] = 0;
+        }
+      }
+      // near-ties: one element per lane per round
+      uint32_t dany = diff[0];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) dany |= diff[q];
+      while (__builtin_expect(__any(dany != 0u), 0)) {
+        if (dany != 0u) {
+          int q = 0;
+          if constexpr (NW == 2) q = diff[0] != 0u ? 0 : 1;
+          const uint32_t dq = NW == 2 ? (q ? diff[1] : diff[0]) : diff[0];
+          const uint32_t wq = NW == 2 ? (q ? code[1] : code[0]) : code[0];
+          const int nib = (int)(__builtin_ctz(dq) >> 2);
+          const uint32_t sh = 4u * (uint32_t)nib;
+          const uint32_t ml = (wq >> sh) & 7u, mh = ((wq ^ dq) >> sh) & 7u;
+          const uint32_t mlow = ml < mh ? ml : mh;
+          const double ax = (double)fabsf(lane_x<CPL>(cur[u], 8 * q + nib));
+          const double t = (double)(e2m1_mid_above(mlow) * s) * st64;
+          const bool up = ax > t || (ax == t && ((mlow + 1u) & 1u) == 0u);
+          const uint32_t nw = (wq & ~(7u << sh)) | ((up ? mlow + 1u : mlow) << sh);
+          const uint32_t nd = dq & ~(15u << sh);
+          if constexpr (NW == 2) {
+            if (q) { code[1] = nw; diff[1] = nd; } else { code[0] = nw; diff[0] = nd; }
+          } else {
+            code[0] = nw;
+            diff[0] = nd;
           }
+          dany = diff[0];
+#pragma unroll
+          for (int q2 = 1; q2 < NW; ++q2) dany |= diff[q2];
         }
       }
       // residual r = RN32(x - c s st): c*s is exact, one fused rounding
-      const f32x2v c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
-      const f32x2v c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 1);
-      const f32x2v c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 2);
-      const f32x2v c3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 3);
-      const float cv[8] = {c0.x, c0.y, c1.x, c1.y, c2.x, c2.y, c3.x, c3.y};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float r = fmaf(-(cv[i] * s), st, xf[i]);
-        const double rd = (double)r;
-        acc[i] = fma(rd, rd, acc[i]);
+      for (int q = 0; q < NW; ++q) {
+        f32x2v c2[4];
+        c2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 0);
+        c2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 1);
+        c2[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 2);
+        c2[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 3);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i0 = 8 * q + 2 * b;
+          const float r0v = fmaf(-(c2[b].x * s), st, xf[i0]);
+          const float r1v = fmaf(-(c2[b].y * s), st, xf[i0 + 1]);
+          const double d0 = (double)r0v, d1 = (double)r1v;
+          acc[i0] = fma(d0, d0, acc[i0]);
+          acc[i0 + 1] = fma(d1, d1, acc[i0 + 1]);
+        }
       }
       if (active) {
-        *(uint32_t*)(a.codes + row * cstride + (col0 >> 1)) = code;
+        uint8_t* cp = a.codes + row * cstride + (col0 >> 1);
+        if constexpr (NW == 2)
+          *(uint2*)cp = make_uint2(code[0], code[1]);
+        else
+          *(uint32_t*)cp = code[0];
         if constexpr (MX) {
-          if ((lane & 3) == 0) a.scales[row * sstride + (col0 >> 5)] = (uint8_t)sc;
+          if ((lane & (32 / CPL - 1)) == 0) a.scales[row * sstride + (col0 >> 5)] = (uint8_t)sc;
         } else {
-          if ((lane & 1) == 0) a.scales[row * sstride + (col0 >> 4)] = (uint8_t)sc;
+          if (CPL == 16 || (lane & 1) == 0) a.scales[row * sstride + (col0 >> 4)] = (uint8_t)sc;
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int q = 0; q < NW; ++q) cur[u][q] = nxt[u][q];
   }
   // tile sums -> group sum, tiles in order
 #pragma unroll
-  for (int i = 0; i < 8; ++i) part[wave][lane][i] = acc[i];
+  for (int i = 0; i < CPL; ++i) part[wave][lane][i] = acc[i];
   __syncthreads();
-  {
-    const int c = threadIdx.x;   // channel strip*512 + c
+#pragma unroll
+  for (int h = 0; h < NW; ++h) {
+    const int c = threadIdx.x + 512 * h;   // channel strip * STRIP + c
     double gsum = 0.0;
 #pragma unroll
-    for (int w = 0; w < kScoreGroupTiles; ++w) gsum += part[w][c >> 3][c & 7];
-    const int col = strip * 512 + c;
+    for (int w = 0; w < kScoreGroupTiles; ++w) gsum += part[w][c / CPL][c % CPL];
+    const int col = strip * STRIP + c;
     if (col < cols) a.partial[group * cols + col] = gsum;
   }
 }
@@ -692,7 +767,10 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
   a.x = x;
   a.rows = rows;
   a.cols = (int32_t)cols;
-  a.nstrips = (int32_t)((cols + 511) / 512);
+  // 16 channels per lane halves the per-block work; 8 per lane when that
+  // would leave fewer than 256 workgroups (one per CU)
+  const bool wide = ngroups * ((cols + 1023) / 1024) >= 256;
+  a.nstrips = (int32_t)(wide ? (cols + 1023) / 1024 : (cols + 511) / 512);
   a.ngroups = ngroups;
   a.ts_in = ts_in;
   a.amax = amax;
@@ -705,10 +783,14 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
   const int64_t units = ngroups * a.nstrips;
   if (units > 0) {
     const unsigned grid = (unsigned)units;
-    if (mx)
-      hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(512), 0, stream, a);
+    if (mx && wide)
+      hipLaunchKernelGGL((quantize_kernel<true, 16>), dim3(grid), dim3(512), 0, stream, a);
+    else if (mx)
+      hipLaunchKernelGGL((quantize_kernel<true, 8>), dim3(grid), dim3(512), 0, stream, a);
+    else if (wide)
+      hipLaunchKernelGGL((quantize_kernel<false, 16>), dim3(grid), dim3(512), 0, stream, a);
     else
-      hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(512), 0, stream, a);
+      hipLaunchKernelGGL((quantize_kernel<false, 8>), dim3(grid), dim3(512), 0, stream, a);
   } else if (!mx && ts_out) {
     // no rows: still report s_t (1, or the supplied value)
     hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(64), 0, stream, ts_in, ts_out);
