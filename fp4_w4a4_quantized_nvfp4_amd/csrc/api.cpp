@@ -217,11 +217,17 @@ q4_status_t w4a4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_
   return hip_status(launch_w4a4_gemm(g, 0, S(stream)), "w4a4_gemm");
 }
 
+// tiled fp16 scale records of A and W for the dense 256 x 256 kernel
+static size_t scale_tiles_bytes(int64_t M, int64_t N, int64_t K) {
+  if (K <= 0 || K % 128 != 0) return 0;
+  return align256((size_t)tile_rows_pad(M) * (size_t)(K / 128) * 16) +
+         align256((size_t)tile_rows_pad(N) * (size_t)(K / 128) * 16);
+}
+
 size_t rac_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k) {
-  (void)K;
   if (M < 0 || N < 0 || k < 0) return 0;
   const int64_t kp = round_up32(k);
-  return align256((size_t)M * kp * 2) + align256((size_t)N * kp * 2);
+  return align256((size_t)M * kp * 2) + align256((size_t)N * kp * 2) + scale_tiles_bytes(M, N, K);
 }
 
 q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_t* x,
@@ -261,8 +267,25 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
   g.ldy = N;
   g.y_bf16 = y_dtype == Q4_OUT_BF16;
   g.epilogue = kEpiStore;
+  const int32_t kp = round_up32(k);
+  const size_t rac_bytes = align256((size_t)M * kp * 2) + align256((size_t)N * kp * 2);
+  // the dense 256 x 256 kernel reads block scales as tiled fp16 records when
+  // the workspace has room for them
+  if (!mx && K % 128 == 0 && M >= 512 && N >= 512 && workspace &&
+      ((uintptr_t)workspace & 15u) == 0 &&
+      workspace_bytes >= rac_bytes + scale_tiles_bytes(M, N, K)) {
+    uint8_t* ta = (uint8_t*)workspace + rac_bytes;
+    uint8_t* tw = ta + align256((size_t)tile_rows_pad(M) * (size_t)(K / 128) * 16);
+    hipError_t e = launch_scale_tile(a_scales, M, (int32_t)K, tile_rows_pad(M), ta, S(stream));
+    if (e == hipSuccess)
+      e = launch_scale_tile(w_scales, N, (int32_t)K, tile_rows_pad(N), tw, S(stream));
+    if (e != hipSuccess) return hip_status(e, "rac_gemm (scale records)");
+    g.a_scales_t = ta;
+    g.w_scales_t = tw;
+    g.a_rows_pad = tile_rows_pad(M);
+    g.w_rows_pad = tile_rows_pad(N);
+  }
   if (k > 0) {
-    const int32_t kp = round_up32(k);
     uint16_t* R = (uint16_t*)workspace;
     uint16_t* W_S = (uint16_t*)((uint8_t*)workspace + align256((size_t)M * kp * 2));
     hipError_t e = launch_residual_gather(mx, x, M, K, a_codes, a_scales, a_tensor_scale,

@@ -16,6 +16,8 @@
 //
 // Tiles: 256 x 128 per workgroup of four waves (2 x 2), 128 x 64 per wave
 // (4 x 2 MFMA 32x32 tiles), K chunks of 128 double-buffered in LDS.
+#include <type_traits>
+
 #include "q4_internal.h"
 
 namespace q4 {
@@ -437,10 +439,14 @@ constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int CB = BK / 2;
 constexpr int NST = 3;
 constexpr int B_CODE_OFF = BM * CB;                 // 16384
-constexpr int A_SC_OFF = B_CODE_OFF + BN * CB;      // 32768 (E4M3, 8 bytes per row)
-constexpr int B_SC_OFF = A_SC_OFF + BM * 8;         // 34816
-constexpr int STAGE = B_SC_OFF + BN * 8;            // 36864
-constexpr int DMA_PER_CHUNK = 12;                   // per wave: 8 code + 4 scale loads
+constexpr int A_SC_OFF = B_CODE_OFF + BN * CB;      // 32768
+// scale bytes per row per chunk: 8 raw E4M3, or 16 as tiled fp16 records
+template <bool TILED> constexpr int SC_ROW = TILED ? 16 : 8;
+template <bool TILED> constexpr int B_SC_OFF = A_SC_OFF + BM * SC_ROW<TILED>;
+template <bool TILED> constexpr int STAGE = B_SC_OFF<TILED> + BN * SC_ROW<TILED>;
+// global -> LDS loads per wave per chunk: 8 code pieces + 4 raw scale dwords,
+// or + one 16-byte tiled scale record per operand
+template <bool TILED> constexpr int DMA_PER_CHUNK = TILED ? 10 : 12;
 
 typedef const void __attribute__((address_space(1)))* gptr_t;
 typedef void __attribute__((address_space(3)))* lptr_t;
@@ -468,14 +474,16 @@ struct Frag {
   uint32_t sa[4], sb[4];   // two raw E4M3 scales (blocks 2p, 2p + 1) per row
 };
 
+template <bool TILED>
 __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
+  constexpr int STAGE = big::STAGE<TILED>, B_SC_OFF = big::B_SC_OFF<TILED>;
+  constexpr int DMA_PER_CHUNK = big::DMA_PER_CHUNK<TILED>;
   // one LDS object per stage, addressed with compile-time stage indices, so
   // the compiler can tell that reads of one stage do not wait for the
   // global -> LDS loads still filling another
   __shared__ __attribute__((aligned(16))) uint8_t stage0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t stage2[STAGE];
-  uint8_t* const stages[NST] = {stage0, stage1, stage2};
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -538,15 +546,18 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     const int ra = wm * 128 + q * 32 + l32, rb = wn * 128 + q * 32 + l32;
     ca_off[q] = (uint32_t)swz(ra, 2 * h);
     cb_off[q] = (uint32_t)(B_CODE_OFF + swz(rb, 2 * h));
-    sa_off[q] = (uint32_t)(A_SC_OFF + ra * 8 + 4 * h);
-    sb_off[q] = (uint32_t)(B_SC_OFF + rb * 8 + 4 * h);
+    if constexpr (TILED) {
+      sa_off[q] = (uint32_t)(A_SC_OFF + swz_sc(ra, 2 * h));
+      sb_off[q] = (uint32_t)(B_SC_OFF + swz_sc(rb, 2 * h));
+    } else {
+      sa_off[q] = (uint32_t)(A_SC_OFF + ra * 8 + 4 * h);
+      sb_off[q] = (uint32_t)(B_SC_OFF + rb * 8 + 4 * h);
+    }
   }
 
-  // all global -> LDS traffic of chunk kc (clamped: chunks past the end
-  // reload the last one into a stage nobody reads again)
-  auto issue_chunk = [&](int kc, uint8_t* const sbase) {
-    const uint32_t kb = (uint32_t)min(kc, nk - 1) * (BK / 2);
-    const uint32_t ks = (uint32_t)min(kc, nk - 1) * (BK / 16);
+  // global -> LDS traffic of FP4 chunk kc (kc < nk): codes, then scales
+  auto issue_codes = [&](int kc, uint8_t* const sbase) {
+    const uint32_t kb = (uint32_t)kc * (BK / 2);
     uint8_t* const dst = sbase + wave * 1024;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -555,35 +566,100 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
       __builtin_amdgcn_global_load_lds((gptr_t)(b_base + kb + b_goff[it]),
                                        (lptr_t)(dst + B_CODE_OFF + it * 4096), 16, 0, 0);
     }
-    uint8_t* const sdst = sbase + wave * 256;
+  };
+  auto issue_scales = [&](int kc, uint8_t* const sbase) {
+    const uint32_t ks = (uint32_t)kc * (BK / 16);
+    if constexpr (TILED) {
+      // record of tile row 64 * wave + lane in chunk kc: [chunk][padded row][16 B]
+      const size_t kt = (size_t)kc;
+      __builtin_amdgcn_global_load_lds(
+          (gptr_t)(g.a_scales_t + ((kt * g.a_rows_pad + m0 + 64 * wave + lane) << 4)),
+          (lptr_t)(sbase + A_SC_OFF + wave * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (gptr_t)(g.w_scales_t + ((kt * g.w_rows_pad + n0 + 64 * wave + lane) << 4)),
+          (lptr_t)(sbase + B_SC_OFF + wave * 1024), 16, 0, 0);
+    } else {
+      uint8_t* const sdst = sbase + wave * 256;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      __builtin_amdgcn_global_load_lds((gptr_t)(as_base + ks + as_goff[it]),
-                                       (lptr_t)(sdst + A_SC_OFF + it * 1024), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((gptr_t)(bs_base + ks + bs_goff[it]),
-                                       (lptr_t)(sdst + B_SC_OFF + it * 1024), 4, 0, 0);
+      for (int it = 0; it < 2; ++it) {
+        __builtin_amdgcn_global_load_lds((gptr_t)(as_base + ks + as_goff[it]),
+                                         (lptr_t)(sdst + A_SC_OFF + it * 1024), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr_t)(bs_base + ks + bs_goff[it]),
+                                         (lptr_t)(sdst + B_SC_OFF + it * 1024), 4, 0, 0);
+      }
+    }
+  };
+  // every chunk issue is DMA_PER_CHUNK loads per wave, whatever it carries
+  auto issue_chunk = [&](int kc, uint8_t* const sbase) {   // FP4 chunk kc < nk
+    issue_codes(kc, sbase);
+    issue_scales(kc, sbase);
+  };
+
+  // Residual compensation chunks: R [M][ld_r] and W_S [N][kp] (bf16,
+  // kp % 32 == 0) follow the FP4 chunks through the same stages, 32 channels
+  // per chunk (64 bytes per row, the code chunks' layout), straight into bf16
+  // MFMAs.  Chunk nk + j is RAC chunk j.
+  const int nrac = (g.kp > 0 && g.r_res) ? g.kp / 32 : 0;
+  const uint8_t* const r_base = (const uint8_t*)(g.r_res + (size_t)m0 * g.ld_r);
+  const uint8_t* const w_base = (const uint8_t*)(g.w_sel + (size_t)n0 * g.kp);
+  const uint32_t r_stride = (uint32_t)g.ld_r * 2u, w_stride = (uint32_t)g.kp * 2u;
+  auto issue_rac = [&](int j, uint8_t* const sbase) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = 16 * (4 * it + wave) + (lane >> 2);
+      const uint32_t piece = (uint32_t)((lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3));
+      const uint32_t off = 64u * (uint32_t)j + piece * 16u;
+      __builtin_amdgcn_global_load_lds(
+          (gptr_t)(r_base + (uint32_t)min(row, a_last) * r_stride + off),
+          (lptr_t)(sbase + wave * 1024 + it * 4096), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (gptr_t)(w_base + (uint32_t)min(row, b_last) * w_stride + off),
+          (lptr_t)(sbase + B_CODE_OFF + wave * 1024 + it * 4096), 16, 0, 0);
+    }
+  };
+  // chunk c of the whole schedule: FP4, RAC, or (past the end) a repeat of
+  // the last FP4 chunk into a stage nobody reads again
+  auto issue_any = [&](int c, uint8_t* const sbase) {
+    if (c < nk) {
+      issue_chunk(c, sbase);
+    } else if (c - nk < nrac) {
+      issue_rac(c - nk, sbase);
+      issue_scales(nk - 1, sbase);   // keeps the count; the scale area is unused
+    } else {
+      issue_chunk(nk - 1, sbase);
     }
   };
   auto read_frag = [&](Frag& f, const uint8_t* const base, int s2) {
-    const uint32_t cx = s2 ? 16u : 0u, sx = s2 ? 2u : 0u;
+    const uint32_t cx = s2 ? 16u : 0u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       f.a[q] = *(const uint4*)(base + (ca_off[q] ^ cx));
-      f.sa[q] = *(const uint16_t*)(base + sa_off[q] + sx);
+      if constexpr (TILED)
+        f.sa[q] = *(const uint32_t*)(base + (sa_off[q] ^ (s2 ? 4u : 0u)));
+      else
+        f.sa[q] = *(const uint16_t*)(base + sa_off[q] + (s2 ? 2u : 0u));
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       f.b[q] = *(const uint4*)(base + (cb_off[q] ^ cx));
-      f.sb[q] = *(const uint16_t*)(base + sb_off[q] + sx);
+      if constexpr (TILED)
+        f.sb[q] = *(const uint32_t*)(base + (sb_off[q] ^ (s2 ? 4u : 0u)));
+      else
+        f.sb[q] = *(const uint16_t*)(base + sb_off[q] + (s2 ? 2u : 0u));
     }
   };
   auto decode = [&](const Frag& f, int j, half8v* da, half8v* db) {
+    // the scale of each block in both fp16 halves
+    auto dup = [&](uint32_t v) {
+      if constexpr (TILED)   // fp16 pair (block 2p, block 2p + 1)
+        return __builtin_amdgcn_perm(v, v, j >= 2 ? 0x03020302u : 0x01000100u);
+      else                   // raw E4M3 pair
+        return e4m3_dup_f16(v, j >= 2);
+    };
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      da[q] = decode8(word(f.a[q], j), e4m3_dup_f16(f.sa[q], j >= 2));
+    for (int q = 0; q < 4; ++q) da[q] = decode8(word(f.a[q], j), dup(f.sa[q]));
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      db[q] = decode8(word(f.b[q], j), e4m3_dup_f16(f.sb[q], j >= 2));
+    for (int q = 0; q < 4; ++q) db[q] = decode8(word(f.b[q], j), dup(f.sb[q]));
   };
 
   f32x16v acc[4][4];
@@ -632,18 +708,31 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     }
   };
 
+  // FP4 chunk kc lives in stage (kc + off) % 3, so that chunk nk (the first
+  // RAC chunk) lands in stage 0: every loop below addresses its stages
+  // statically
+  const int off = (3 - nk % 3) % 3;
   // prologue: chunks 0..2 in flight
-  issue_chunk(0, stages[0]);
-  issue_chunk(1, stages[1]);
-  issue_chunk(2, stages[2]);
+  if (off == 0) {
+    issue_any(0, stage0); issue_any(1, stage1); issue_any(2, stage2);
+  } else if (off == 1) {
+    issue_any(0, stage1); issue_any(1, stage2); issue_any(2, stage0);
+  } else {
+    issue_any(0, stage2); issue_any(1, stage0); issue_any(2, stage1);
+  }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));   // chunk 0 has landed
   lds_barrier();
   Frag f0, f1;
-  read_frag(f0, stages[0], 0);
+  if (off == 0)
+    read_frag(f0, stage0, 0);
+  else if (off == 1)
+    read_frag(f0, stage1, 0);
+  else
+    read_frag(f0, stage2, 0);
   decode(f0, 0, da[0], db[0]);
 
-  // chunk kc lives in stage kc % 3
-  auto chunk = [&](int kc, uint8_t* const cur, uint8_t* const nxt) {
+  // one FP4 chunk; ANY: the chunk issued three ahead may be a RAC chunk
+  auto chunk = [&](int kc, uint8_t* const cur, uint8_t* const nxt, auto any) {
     read_frag(f1, cur, 1);
     half_chunk(f0, f1, 0);
     // chunk kc + 1 has landed (chunk kc + 2 may still be in flight); after
@@ -651,18 +740,33 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA_PER_CHUNK));
     lds_barrier();
     read_frag(f0, nxt, 0);
-    issue_chunk(kc + 3, cur);
-    half_chunk(f1, f0, DMA_PER_CHUNK);
+    if constexpr (decltype(any)::value)
+      issue_any(kc + 3, cur);
+    else
+      issue_chunk(kc + 3, cur);
+    half_chunk(f1, f0, decltype(any)::value ? 0 : DMA_PER_CHUNK);
   };
+  using fp4_only = std::false_type;
+  using with_rac = std::true_type;
   int kc = 0;
-  for (; kc + 3 <= nk; kc += 3) {
-    chunk(kc, stages[0], stages[1]);
-    chunk(kc + 1, stages[1], stages[2]);
-    chunk(kc + 2, stages[2], stages[0]);
+  if (off == 1) {
+    chunk(0, stage1, stage2, with_rac{});
+    if (nk > 1) chunk(1, stage2, stage0, with_rac{});
+    kc = 2;
+  } else if (off == 2) {
+    chunk(0, stage2, stage0, with_rac{});
+    kc = 1;
   }
-  if (kc < nk) chunk(kc, stages[0], stages[1]);
-  if (kc + 1 < nk) chunk(kc + 1, stages[1], stages[2]);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  for (; kc + 6 <= nk; kc += 3) {
+    chunk(kc, stage0, stage1, fp4_only{});
+    chunk(kc + 1, stage1, stage2, fp4_only{});
+    chunk(kc + 2, stage2, stage0, fp4_only{});
+  }
+  if (kc + 3 <= nk) {
+    chunk(kc, stage0, stage1, with_rac{});
+    chunk(kc + 1, stage1, stage2, with_rac{});
+    chunk(kc + 2, stage2, stage0, with_rac{});
+  }
 
   const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[0] : 1.0f;
 #pragma unroll
@@ -672,35 +776,103 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= alpha;
 
-  if (g.kp > 0 && g.r_res) {
-    const uint16_t* rrow[4];
-    const uint16_t* wrow[4];
-    bool rok[4], wok[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t rr = m0 + wm * 128 + q * 32 + l32;
-      rok[q] = rr < m_end;
-      rrow[q] = g.r_res + (rok[q] ? rr : 0) * g.ld_r + 8 * h;
-      const int64_t cc = n0 + wn * 128 + q * 32 + l32;
-      wok[q] = cc < N;
-      wrow[q] = g.w_sel + (wok[q] ? cc : 0) * g.kp + 8 * h;
+  // RAC chunk jr in stage jr % 3; chunk 0 has landed and is visible, and two
+  // chunk issues are always in flight behind the one being read
+  auto rac_chunk = [&](int jr, uint8_t* const sb) {
+    if (jr > 0) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));
+      lds_barrier();
     }
-    for (int kt = 0; kt < g.kp; kt += 16) {
-      bf16x8v af[4], bf[4];
+    uint4 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        af[q] = __builtin_bit_cast(bf16x8v, rok[q] ? *(const uint4*)(rrow[q] + kt) : make_uint4(0, 0, 0, 0));
-        bf[q] = __builtin_bit_cast(bf16x8v, wok[q] ? *(const uint4*)(wrow[q] + kt) : make_uint4(0, 0, 0, 0));
+        fa[s2][q] = *(const uint4*)(sb + swz(wm * 128 + q * 32 + l32, 2 * s2 + h));
+        fb[s2][q] = *(const uint4*)(sb + B_CODE_OFF + swz(wn * 128 + q * 32 + l32, 2 * s2 + h));
       }
+    lds_barrier();   // every wave is done with this stage
+    issue_any(nk + jr + 3, sb);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-    }
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8v, fa[s2][mi]), __builtin_bit_cast(bf16x8v, fb[s2][ni]),
+              acc[mi][ni], 0, 0, 0);
+  };
+  int jr = 0;
+  for (; jr + 3 <= nrac; jr += 3) {
+    rac_chunk(jr, stage0);
+    rac_chunk(jr + 1, stage1);
+    rac_chunk(jr + 2, stage2);
   }
+  if (jr < nrac) rac_chunk(jr, stage0);
+  if (jr + 1 < nrac) rac_chunk(jr + 1, stage1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
+  // Epilogue through LDS so that every global store writes 16 contiguous
+  // bytes: per pass, a wave's 16 rows x 128 columns (rows 16 * half .. + 15 of
+  // MFMA tile row mi) go to its own LDS region and come back as row chunks.
+  // Accumulator element r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
+  // column l % 32 of its 32 x 32 tile.
+  const int vec = g.y_bf16 ? 8 : 4;
+  const bool staged = (N % vec) == 0 && (g.ldy % vec) == 0 && (((uintptr_t)g.Y) & 15u) == 0;
+  if (staged) {
+    __syncthreads();   // every wave is done with the stages
+    constexpr int PB = 272, PF = 544;   // row pitches (bytes) of the bf16 / fp32 staging tiles
+    uint8_t* const ep = stage0 + wave * (16 * PF);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int64_t rbase = m0 + wm * 128 + mi * 32 + 16 * half;
+        if (g.y_bf16) {
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+            for (int rr = 0; rr < 8; rr += 2) {
+              const int r = 8 * half + rr;
+              const int lr = 8 * ((r >> 2) - 2 * half) + 4 * h + (r & 3);
+              typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+              const bf16x2 pr = {(__bf16)acc[mi][ni][r], (__bf16)acc[mi][ni][r + 1]};
+              const uint32_t w = __builtin_bit_cast(uint32_t, pr);
+              uint8_t* const p = ep + lr * PB + (ni * 32 + l32) * 2;
+              *(uint16_t*)p = (uint16_t)w;
+              *(uint16_t*)(p + PB) = (uint16_t)(w >> 16);
+            }
+          }
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const int cid = it * 64 + lane, lr = cid >> 4, cc = (cid & 15) * 8;
+            const uint4 v = *(const uint4*)(ep + lr * PB + cc * 2);
+            const int64_t row = rbase + lr, col = n0 + wn * 128 + cc;
+            if (row < m_end && col < N) *(uint4*)((uint16_t*)g.Y + row * g.ldy + col) = v;
+          }
+        } else {
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+              const int r = 8 * half + rr;
+              const int lr = 8 * ((r >> 2) - 2 * half) + 4 * h + (r & 3);
+              *(float*)(ep + lr * PF + (ni * 32 + l32) * 4) = acc[mi][ni][r];
+            }
+          }
+#pragma unroll
+          for (int it = 0; it < 8; ++it) {
+            const int cid = it * 64 + lane, lr = cid >> 5, cc = (cid & 31) * 4;
+            const uint4 v = *(const uint4*)(ep + lr * PF + cc * 4);
+            const int64_t row = rbase + lr, col = n0 + wn * 128 + cc;
+            if (row < m_end && col < N) *(uint4*)((float*)g.Y + row * g.ldy + col) = v;
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -751,7 +923,12 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
   }
   if (!grouped && fullk && g.epilogue == kEpiStore && g.M >= 512 && g.N >= 512) {
     const int64_t nb = ((g.M + big::BM - 1) / big::BM) * ((g.N + big::BN - 1) / big::BN);
-    hipLaunchKernelGGL(big::gemm_nvfp4_big_kernel, dim3((unsigned)nb), dim3(256), 0, stream, g);
+    if (g.a_scales_t && g.w_scales_t)
+      hipLaunchKernelGGL(big::gemm_nvfp4_big_kernel<true>, dim3((unsigned)nb), dim3(256), 0,
+                         stream, g);
+    else
+      hipLaunchKernelGGL(big::gemm_nvfp4_big_kernel<false>, dim3((unsigned)nb), dim3(256), 0,
+                         stream, g);
     return hipGetLastError();
   }
   if (fullk)
@@ -759,6 +936,42 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
                    : launch_t<true, false, false>(g, max_mtiles, stream);
   return grouped ? launch_t<false, true, false>(g, max_mtiles, stream)
                  : launch_t<false, false, false>(g, max_mtiles, stream);
+}
+
+// Tiled scale records for the 256 x 256 kernel: record (c, r) = the eight
+// block scales of row r in K-chunk c (128 channels) as fp16 (exact, E4M3
+// subnormals included), dwords placed so that dword d sits at d ^ ((r / 8) % 4);
+// layout [K / 128][rows_pad][16 B], rows past `rows` zero.
+__global__ __launch_bounds__(256) void scale_tile_kernel(const uint8_t* __restrict__ sc,
+                                                         int64_t rows, int32_t K,
+                                                         int64_t rows_pad,
+                                                         uint4* __restrict__ out) {
+  const int64_t total = (int64_t)(K / 128) * rows_pad;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t c = i / rows_pad, r = i - c * rows_pad;
+    uint2 raw = make_uint2(0, 0);
+    if (r < rows) raw = *(const uint2*)(sc + r * (K / 16) + 8 * c);
+    const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
+    auto cvt2 = [&](uint32_t w, uint32_t sel) {
+      const uint32_t d = __builtin_amdgcn_perm(0u, w, sel) << 7;
+      return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d) * k256);
+    };
+    const uint4 rec = make_uint4(cvt2(raw.x, 0x0c010c00u), cvt2(raw.x, 0x0c030c02u),
+                                 cvt2(raw.y, 0x0c010c00u), cvt2(raw.y, 0x0c030c02u));
+    out[i] = swz_sc_rec(rec, (int)(r & 255));
+  }
+}
+
+hipError_t launch_scale_tile(const uint8_t* scales, int64_t rows, int32_t K, int64_t rows_pad,
+                             uint8_t* out, hipStream_t stream) {
+  const int64_t total = (int64_t)(K / 128) * rows_pad;
+  if (total == 0) return hipSuccess;
+  int64_t grid = (total + 255) / 256;
+  grid = grid > 8192 ? 8192 : grid;
+  hipLaunchKernelGGL(scale_tile_kernel, dim3((unsigned)grid), dim3(256), 0, stream, scales, rows,
+                     K, rows_pad, (uint4*)out);
+  return hipGetLastError();
 }
 
 }  // namespace q4

@@ -60,9 +60,18 @@ struct GemmArgs {
   const int32_t* tiles;      // int4 {expert, row_begin, row_end, 0} per M tile (null: dense)
   const int32_t* ntiles_dev; // number of valid M tiles (device)
   const int32_t* a_rows;     // A row of each output row (null: identity)
+  // optional tiled fp16 scale records (dense NVFP4, K % 128 == 0): see launch_scale_tile
+  const uint8_t* a_scales_t;
+  const uint8_t* w_scales_t;
+  int64_t a_rows_pad;        // rows of the tiled records (a multiple of 256)
+  int64_t w_rows_pad;
 };
 
 hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream);
+// scale records [K/128][rows_pad][16 B] of an NVFP4 operand for the dense kernel
+hipError_t launch_scale_tile(const uint8_t* scales, int64_t rows, int32_t K, int64_t rows_pad,
+                             uint8_t* out, hipStream_t stream);
+inline int64_t tile_rows_pad(int64_t rows) { return (rows + 255) / 256 * 256; }
 
 constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 128;

@@ -151,7 +151,12 @@ q4_status_t w4a4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_
  *           selected rows S_t are contiguous.
  *   chan_set int32 [k] ascending unique channels in [0, K) (out-of-range
  *           entries are clamped); 0 <= k <= min(K, Q4_MAX_TOPK).
- * k == 0 gives exactly w4a4_gemm. */
+ * k == 0 gives exactly w4a4_gemm.
+ * Workspace: R and the selected weight columns (when k > 0) and, for NVFP4
+ * with K % 128 == 0, re-laid-out fp16 copies of both operands' block scales
+ * that the large-tile kernel reads; with k == 0 the workspace is optional (a
+ * null or smaller one selects the kernel that reads the scales in place).
+ * Results are identical either way. */
 size_t rac_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);
 q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_t *x,
                      const uint8_t *a_codes, const uint8_t *a_scales,

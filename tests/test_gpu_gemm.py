@@ -183,3 +183,27 @@ def test_mxfp4_exact_special_case():
     x, A, W, Ao, Wo = _quant_pair(m, xb, wb, "mx")
     Y = host(m.w4a4_gemm(A, W))
     assert np.array_equal(Y.astype(np.float64), oracle.w4a4_gemm(Ao, Wo))
+
+
+@pytest.mark.parametrize("M,N,K,sub", [(512, 768, 512, False), (512, 768, 512, True),
+                                       (1000, 1300, 1024, False), (777, 640, 384, True)])
+def test_tiled_scale_records_match_in_place_scales(M, N, K, sub):
+    """rac_gemm with k = 0 (workspace given: the large-tile kernel reads the
+    re-laid-out fp16 scale records) equals w4a4_gemm (no workspace: it reads
+    the E4M3 scales in place) bit for bit, subnormal E4M3 scales included."""
+    m = q4()
+    rng = np.random.default_rng(M + N + K)
+    if sub:
+        xb = _exact_operand(rng, M, K, SUBNORMAL_SCALES)
+        wb = _exact_operand(rng, N, K, SUBNORMAL_SCALES)
+        ts = 1.0
+    else:
+        xb = _bits(rng.standard_t(3, size=(M, K)).astype(np.float32))
+        wb = _bits((rng.standard_normal((N, K)) * 0.05).astype(np.float32))
+        ts = None
+    x, A, W, _, _ = _quant_pair(m, xb, wb, ts=ts)
+    for out in (m.OUT_F32, m.OUT_BF16):
+        Y0 = m.w4a4_gemm(A, W, out_dtype=out)
+        Y1 = m.rac_gemm(x, A, W, None, None, out_dtype=out)
+        torch.cuda.synchronize()
+        assert torch.equal(Y0, Y1), (M, N, K, sub, out)
