@@ -48,6 +48,7 @@ def _args():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--quant-iters", type=int, default=50)
     p.add_argument("--no-mx", action="store_true", help="skip the MXFP4 comparison leg")
+    p.add_argument("--no-moe", action="store_true", help="skip the MoE expert-layer legs")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return p.parse_args()
@@ -61,6 +62,68 @@ def _traffic():
             return None
     return round((TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"]
                   + TRAFFIC["write_kib"] * TRAFFIC["write_scale"]) * 1024.0)
+
+
+def _moe_legs(q4, L, dev, stream, sp, iters=10):
+    """Top-k MoE expert layer (route + token-sorted grouped W4A4+RAC SwiGLU
+    layer) on the 8192-token prefill and the 256-token decode shapes.  Tokens
+    and router logits come from the seeded workload generators; the expert
+    weights, N(0, 0.02) like theirs, are drawn on the GPU with a seeded torch
+    generator (the layer's timing does not depend on their values)."""
+    import torch
+    from workloads import WORKLOADS, make_activations, make_logits
+    res = {}
+    for name, fmts in (("moe_prefill_8192", (q4.NVFP4,)), ("moe_decode_256", (q4.NVFP4, q4.MXFP4))):
+        wl = WORKLOADS[name]
+        T, H, E, F, topk, k = wl.rows, wl.cols, wl.experts, wl.ffn, wl.route_topk, wl.topk_channels
+        _say(f"{name}: expert weights")
+        g = torch.Generator(device=dev).manual_seed(20261202 + wl.index)
+        w13 = (torch.randn((E, 2 * F, H), generator=g, device=dev) * wl.weight_std).to(torch.bfloat16)
+        w2 = (torch.randn((E, H, F), generator=g, device=dev) * wl.weight_std).to(torch.bfloat16)
+        tokens = torch.from_numpy(make_activations(wl).view(np.int16)).to(dev)
+        logits = torch.from_numpy(make_logits(wl)).to(dev)
+        idx = torch.empty((T, topk), dtype=torch.int32, device=dev)
+        pw = torch.empty((T, topk), dtype=torch.float32, device=dev)
+        Y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        kp = (k + 31) // 32 * 32
+        flops = 2.0 * T * topk * (2 * F * H + H * F) + 2.0 * T * topk * (2 * F * kp + H * kp)
+        for fmt in fmts:
+            experts = q4.prepare_moe_weights(w13, w2, fmt=fmt)
+            torch.cuda.synchronize()
+            wsb = L.moe_workspace_size(fmt, T, E, H, F, topk, k)
+            ws = torch.empty((wsb,), dtype=torch.uint8, device=dev)
+
+            def layer():
+                q4._check(L.q4_moe_route(logits.data_ptr(), T, E, topk, idx.data_ptr(),
+                                         pw.data_ptr(), sp))
+                q4.moe_w4a4_grouped_gemm(tokens, idx, pw, experts, k, out_dtype=q4.OUT_BF16,
+                                         workspace=ws, Y=Y)
+            for _ in range(3):
+                layer()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(iters):
+                layer()
+            e1.record(stream)
+            e1.synchronize()
+            ms = e0.elapsed_time(e1) / iters
+            w_bytes = sum(t.numel() * t.element_size() for t in
+                          (experts["w13"]["codes"], experts["w13"]["scales"],
+                           experts["w2"]["codes"], experts["w2"]["scales"]))
+            sel_bytes = E * (2 * F + H) * kp * 2      # selected bf16 weight columns
+            leg = {"fmt": "nvfp4" if fmt == q4.NVFP4 else "mxfp4", "ms": round(ms, 4),
+                   "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                   "frac_fp16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
+                   "weight_gbps": round((w_bytes + sel_bytes) / (ms * 1e-3) / 1e9, 1),
+                   "frac_hbm_weights": round((w_bytes + sel_bytes) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            res.setdefault(name, {})[leg["fmt"]] = leg
+            del experts, ws
+        res[name]["shape"] = {"T": T, "H": H, "E": E, "F": F, "topk": topk, "rac_k": k,
+                              "flops_per_layer": flops}
+        del w13, w2
+        torch.cuda.empty_cache()
+    return res
 
 
 def _say(msg):
@@ -273,6 +336,9 @@ def main():
               "frac_fp4_peak": round(mx_tf / PEAK_FP4_TFLOPS, 4)}
         del Wm
 
+    # ---------------------------------------------------------------- MoE legs
+    moe = None if a.no_moe else _moe_legs(q4, L, dev, stream, sp)
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -306,6 +372,8 @@ def main():
     }
     if mx is not None:
         out["mxfp4"] = mx
+    if moe is not None:
+        out["moe"] = moe
     if not a.no_cpu:
         _say("oracle CPU baseline")
         out["cpu_baseline"] = _cpu_baseline()

@@ -322,7 +322,7 @@ static int64_t moe_max_tiles(int64_t T, int32_t E, int32_t topk) {
 
 size_t q4_moe_sort_workspace_size(int64_t T, int32_t E, int32_t topk) {
   if (T < 0 || E < 1 || topk < 1) return 0;
-  return align256((size_t)E * 4) + align256((size_t)T * topk * 4) +
+  return moe_sort_workspace_bytes(T, E, topk) + align256((size_t)T * topk * 4) +
          align256((size_t)moe_max_tiles(T, E, topk) * 16) + 256;
 }
 
@@ -343,7 +343,7 @@ q4_status_t q4_moe_sort(const int32_t* topk_idx, int64_t T, int32_t E, int32_t t
   Q4_REQUIRE_PTR(workspace);
   uint8_t* w = (uint8_t*)workspace;
   int32_t* counts = (int32_t*)w;
-  w += align256((size_t)E * 4);
+  w += moe_sort_workspace_bytes(T, E, topk);
   int32_t* inv = (int32_t*)w;
   w += align256((size_t)T * topk * 4);
   int32_t* tiles = (int32_t*)w;
@@ -415,7 +415,7 @@ MoeLayout moe_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F, in
   L.inv_perm = take((size_t)R * 4);
   L.tiles = take((size_t)moe_max_tiles(T, E, topk) * 16);
   L.ntiles = take(4);
-  L.counts = take((size_t)E * 4);
+  L.counts = take(moe_sort_workspace_bytes(T, E, topk));
   L.a_rows = take((size_t)R * 4);
   L.w13_sel = take((size_t)E * 2 * F * (kp ? kp : 1) * 2);
   L.w2_sel = take((size_t)E * H * (kp ? kp : 1) * 2);

@@ -72,54 +72,60 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
 }
 
 // ====================================================================== sort
-// block-wide exclusive scan of 0/1 flags (ballot + per-wave counts)
-__device__ __forceinline__ int block_scan_flag(bool flag, int* wsum, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const uint64_t b = __ballot(flag);
-  const int in_wave = __popcll(b & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-  if (lane == 0) wsum[wv] = __popcll(b);
+// The token sort is a stable counting sort over blocks of 1024 routed rows:
+// per-block expert histograms, per-expert bases (one thread per expert walks
+// the blocks in order), then a scatter in which each row's rank inside its
+// block comes from wave ballots and per-wave counts.
+
+// bt[b][e] = rows of block b routed to expert e
+__global__ __launch_bounds__(1024) void moe_block_hist_kernel(const int32_t* __restrict__ idx,
+                                                              int64_t n, int32_t E,
+                                                              int32_t* __restrict__ bt) {
+  __shared__ int hist[1024];
+  const int lane = threadIdx.x & 63;
+  for (int e = threadIdx.x; e < E; e += 1024) hist[e] = 0;
   __syncthreads();
-  int before = 0, tot = 0;
-  for (int i = 0; i < nw; ++i) {
-    const int c = wsum[i];
-    before += (i < wv) ? c : 0;
-    tot += c;
+  const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  const bool valid = i < n;
+  const int e = valid ? idx[i] : -1;
+  uint64_t pending = __ballot(valid);
+  while (pending) {
+    const int leader = __ffsll((unsigned long long)pending) - 1;
+    const int d0 = __shfl(e, leader, 64);
+    const uint64_t same = __ballot(valid && e == d0) & pending;
+    if (lane == leader) atomicAdd(&hist[d0], __popcll(same));
+    pending &= ~same;
   }
   __syncthreads();
-  *total = tot;
-  return before + in_wave;
+  for (int q = threadIdx.x; q < E; q += 1024) bt[(int64_t)blockIdx.x * E + q] = hist[q];
 }
 
-// counts[e] = number of routed rows (t, s) with idx == e
-__global__ __launch_bounds__(1024) void moe_count_kernel(const int32_t* __restrict__ idx, int64_t n,
-                                                         int32_t* __restrict__ counts) {
-  __shared__ int wsum[16];
-  const int e = blockIdx.x;
-  int c = 0;
-  for (int64_t b0 = 0; b0 < n; b0 += 1024) {
-    const int64_t i = b0 + threadIdx.x;
-    int tot;
-    block_scan_flag(i < n && idx[i] == e, wsum, &tot);
-    c += tot;
-  }
-  if (threadIdx.x == 0) counts[e] = c;
-}
-
-// offsets = exclusive scan of counts; one M tile entry {e, begin, end, 0} per
-// kGemmBM rows of each expert
-__global__ __launch_bounds__(1024) void moe_offsets_kernel(const int32_t* __restrict__ counts,
+// counts and offsets per expert, bt[b][e] -> rows of expert e in blocks
+// before b, and one M tile entry {e, begin, end, 0} per kGemmBM rows
+__global__ __launch_bounds__(1024) void moe_offsets_kernel(int32_t* __restrict__ bt, int64_t nb,
                                                            int32_t E, int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ tiles,
                                                            int32_t* __restrict__ ntiles) {
+  __shared__ int s_cnt[1024];
   __shared__ int s_off[1025];
   __shared__ int s_tile[1025];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c = 0;
+    for (int64_t b = 0; b < nb; ++b) {
+      const int v = bt[b * E + e];
+      bt[b * E + e] = c;
+      c += v;
+    }
+    s_cnt[e] = c;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     int o = 0, tcount = 0;
     for (int e = 0; e < E; ++e) {
       s_off[e] = o;
       s_tile[e] = tcount;
-      o += counts[e];
-      tcount += (counts[e] + kGemmBM - 1) / kGemmBM;
+      o += s_cnt[e];
+      tcount += (s_cnt[e] + kGemmBM - 1) / kGemmBM;
     }
     s_off[E] = o;
     s_tile[E] = tcount;
@@ -141,23 +147,36 @@ __global__ __launch_bounds__(1024) void moe_offsets_kernel(const int32_t* __rest
 }
 
 // stable scatter: rows of expert e in flat (t, s) order
-__global__ __launch_bounds__(1024) void moe_scatter_kernel(const int32_t* __restrict__ idx, int64_t n,
+__global__ __launch_bounds__(1024) void moe_scatter_kernel(const int32_t* __restrict__ idx,
+                                                           int64_t n, int32_t E,
+                                                           const int32_t* __restrict__ bt,
                                                            const int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ inv_perm) {
-  __shared__ int wsum[16];
-  const int e = blockIdx.x;
-  int base = offsets[e];
-  for (int64_t b0 = 0; b0 < n; b0 += 1024) {
-    const int64_t i = b0 + threadIdx.x;
-    const bool f = i < n && idx[i] == e;
-    int tot;
-    const int r = block_scan_flag(f, wsum, &tot);
-    if (f) {
-      perm[base + r] = (int32_t)i;
-      inv_perm[i] = base + r;
-    }
-    base += tot;
+  __shared__ int wcnt[16][1024];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int q = threadIdx.x; q < 16 * E; q += 1024) wcnt[q / E][q % E] = 0;
+  __syncthreads();
+  const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  const bool valid = i < n;
+  const int e = valid ? idx[i] : -1;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int rank = 0;
+  uint64_t pending = __ballot(valid);
+  while (pending) {
+    const int leader = __ffsll((unsigned long long)pending) - 1;
+    const int d0 = __shfl(e, leader, 64);
+    const uint64_t same = __ballot(valid && e == d0) & pending;
+    if (valid && e == d0) rank = __popcll(same & below);
+    if (lane == leader) wcnt[wv][d0] = __popcll(same);
+    pending &= ~same;
+  }
+  __syncthreads();
+  if (valid) {
+    for (int w = 0; w < wv; ++w) rank += wcnt[w][e];
+    const int pos = offsets[e] + bt[(int64_t)blockIdx.x * E + e] + rank;
+    perm[pos] = (int32_t)i;
+    inv_perm[i] = pos;
   }
 }
 
@@ -208,20 +227,23 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int32_t E, int32_t t
 }
 
 size_t moe_sort_workspace_bytes(int64_t T, int32_t E, int32_t topk) {
-  (void)T;
-  (void)topk;
-  return align256((size_t)E * 4);
+  const int64_t nb = (T * topk + 1023) / 1024;
+  return align256((size_t)(nb > 0 ? nb : 1) * E * 4);
 }
 
 hipError_t launch_moe_sort(const int32_t* idx, int64_t T, int32_t E, int32_t topk, int32_t* perm,
                            int32_t* offsets, int32_t* inv_perm, int32_t* tiles, int32_t* ntiles,
                            int32_t* counts, hipStream_t stream) {
   const int64_t n = T * topk;
-  hipLaunchKernelGGL(moe_count_kernel, dim3((unsigned)E), dim3(1024), 0, stream, idx, n, counts);
-  hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, stream, (const int32_t*)counts,
-                     E, offsets, tiles, ntiles);
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3((unsigned)E), dim3(1024), 0, stream, idx, n,
-                     (const int32_t*)offsets, perm, inv_perm);
+  const int64_t nb = (n + 1023) / 1024;
+  if (nb > 0)
+    hipLaunchKernelGGL(moe_block_hist_kernel, dim3((unsigned)nb), dim3(1024), 0, stream, idx, n,
+                       E, counts);
+  hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, stream, counts, nb, E, offsets,
+                     tiles, ntiles);
+  if (nb > 0)
+    hipLaunchKernelGGL(moe_scatter_kernel, dim3((unsigned)nb), dim3(1024), 0, stream, idx, n, E,
+                       (const int32_t*)counts, (const int32_t*)offsets, perm, inv_perm);
   return hipGetLastError();
 }
 
