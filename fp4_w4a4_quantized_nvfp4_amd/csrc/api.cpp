@@ -319,6 +319,12 @@ q4_status_t q4_moe_route(const float* logits, int64_t T, int32_t E, int32_t topk
 static int64_t moe_max_tiles(int64_t T, int32_t E, int32_t topk) {
   return (T * topk + kGemmBM - 1) / kGemmBM + E;
 }
+static int64_t moe_max_tiles_skinny(int64_t T, int32_t E, int32_t topk) {
+  return (T * topk + kSkinnyBM - 1) / kSkinnyBM + E;
+}
+// few rows per expert (decode-shaped): the grouped GEMMs stream the weights
+// with 32-row tiles instead of 256-row tiles
+static bool moe_skinny(int64_t T, int32_t E, int32_t topk) { return T * topk <= 64 * (int64_t)E; }
 
 size_t q4_moe_sort_workspace_size(int64_t T, int32_t E, int32_t topk) {
   if (T < 0 || E < 1 || topk < 1) return 0;
@@ -380,7 +386,7 @@ q4_status_t q4_moe_pack_w13(const uint16_t* w13, int32_t E, int32_t F, int32_t H
 namespace {
 struct MoeLayout {
   size_t off[Q4_MOE_WS_FIELDS];
-  size_t inv_perm, tiles, ntiles, counts, a_rows, w13_sel, w2_sel, qws, total;
+  size_t inv_perm, tiles, ntiles, tiles_s, ntiles_s, counts, a_rows, w13_sel, w2_sel, qws, total;
 };
 
 MoeLayout moe_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F, int32_t topk,
@@ -415,6 +421,8 @@ MoeLayout moe_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F, in
   L.inv_perm = take((size_t)R * 4);
   L.tiles = take((size_t)moe_max_tiles(T, E, topk) * 16);
   L.ntiles = take(4);
+  L.tiles_s = take((size_t)moe_max_tiles_skinny(T, E, topk) * 16);
+  L.ntiles_s = take(4);
   L.counts = take(moe_sort_workspace_bytes(T, E, topk));
   L.a_rows = take((size_t)R * 4);
   L.w13_sel = take((size_t)E * 2 * F * (kp ? kp : 1) * 2);
@@ -509,6 +517,18 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   Q4_TRY(launch_moe_sort(topk_idx, T, E, topk, perm, offsets, inv, tiles, ntiles,
                          (int32_t*)P(L.counts), s), "moe sort");
   Q4_TRY(launch_gather_rows_index(perm, R, topk, a_rows, s), "moe row index");
+  const bool skinny = moe_skinny(T, E, topk);
+  if (skinny)
+    Q4_TRY(launch_moe_tiles(offsets, E, kSkinnyBM, (int32_t*)P(L.tiles_s), (int32_t*)P(L.ntiles_s),
+                            s), "moe tiles");
+  auto grouped_gemm = [&](GemmArgs& gg) {
+    if (skinny) {
+      gg.tiles = (const int32_t*)P(L.tiles_s);
+      gg.ntiles_dev = (const int32_t*)P(L.ntiles_s);
+      return launch_skinny_gemm(gg, moe_max_tiles_skinny(T, E, topk), s);
+    }
+    return launch_w4a4_gemm(gg, moe_max_tiles(T, E, topk), s);
+  };
   // ---- activation site 1: tokens
   uint8_t* xc = (uint8_t*)P(L.off[2]);
   uint8_t* xs = (uint8_t*)P(L.off[3]);
@@ -546,8 +566,7 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   g.tiles = tiles;
   g.ntiles_dev = ntiles;
   g.a_rows = a_rows;
-  const int64_t maxt = moe_max_tiles(T, E, topk);
-  Q4_TRY(launch_w4a4_gemm(g, maxt, s), "moe w13 gemm");
+  Q4_TRY(grouped_gemm(g), "moe w13 gemm");
   // ---- activation site 2: h (sorted rows)
   uint8_t* hc = (uint8_t*)P(L.off[8]);
   uint8_t* hs = (uint8_t*)P(L.off[9]);
@@ -584,7 +603,7 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   g2.tiles = tiles;
   g2.ntiles_dev = ntiles;
   g2.a_rows = nullptr;
-  Q4_TRY(launch_w4a4_gemm(g2, maxt, s), "moe w2 gemm");
+  Q4_TRY(grouped_gemm(g2), "moe w2 gemm");
   Q4_TRY(launch_moe_combine((const float*)P(L.off[13]), inv, topk_w, T, topk, H, Y,
                             y_dtype == Q4_OUT_BF16, s), "moe combine");
 #undef Q4_TRY

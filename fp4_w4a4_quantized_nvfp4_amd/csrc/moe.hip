@@ -217,6 +217,36 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   }
 }
 
+// tile table {e, begin, end, 0} with at most bm rows per tile, from offsets
+__global__ __launch_bounds__(1024) void moe_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                         int32_t E, int32_t bm,
+                                                         int32_t* __restrict__ tiles,
+                                                         int32_t* __restrict__ ntiles) {
+  __shared__ int s_tile[1025];
+  if (threadIdx.x == 0) {
+    int tcount = 0;
+    for (int e = 0; e < E; ++e) {
+      s_tile[e] = tcount;
+      tcount += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+    }
+    s_tile[E] = tcount;
+    ntiles[0] = tcount;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int b0 = offsets[e], b1 = offsets[e + 1];
+    const int nt = s_tile[e + 1] - s_tile[e];
+    for (int q = 0; q < nt; ++q) {
+      int4 v;
+      v.x = e;
+      v.y = b0 + q * bm;
+      v.z = min(b0 + (q + 1) * bm, b1);
+      v.w = 0;
+      ((int4*)tiles)[s_tile[e] + q] = v;
+    }
+  }
+}
+
 // ====================================================================== launchers
 hipError_t launch_moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* idx,
                             float* w, hipStream_t stream) {
@@ -262,6 +292,13 @@ hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const f
   const int64_t nch = (H + 1023) / 1024;
   hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)(T * nch)), dim3(256), 0, stream, out,
                      inv_perm, topk_w, T, topk, H, Y, y_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_tiles(const int32_t* offsets, int32_t E, int32_t bm, int32_t* tiles,
+                            int32_t* ntiles, hipStream_t stream) {
+  hipLaunchKernelGGL(moe_tiles_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, bm, tiles,
+                     ntiles);
   return hipGetLastError();
 }
 

@@ -1,0 +1,257 @@
+// Grouped W4A4 (+ residual compensation) GEMM for expert groups of few rows:
+// the decode-shaped MoE layer, where each expert sees a handful of tokens and
+// the layer is bound by streaming the expert weights from HBM.
+//
+// QUADS (arXiv 2607.15810) section 3.3: the W4A4 product on FP4 operands with
+// the residual of the selected channels (Eq. 21) accumulated on top; the
+// expert layer is the top-k MoE block the page profiles (W13 site, Figure 4b).
+//
+// A tile is at most 32 rows of one expert (the 32-row tile table) by 256
+// output columns; each wave owns 64 of the columns (two 32 x 32 MFMA tiles)
+// and streams its own weight rows straight from global memory into registers,
+// one K-chunk ahead, with no LDS and no barriers.  The few activation rows are
+// read by every wave (they stay in the caches).  NVFP4 fragments are decoded
+// exactly to fp16 (c * sb has at most six significant bits) for
+// v_mfma_f32_32x32x16_f16; MXFP4 fragments go to the scaled FP4 instruction
+// with their E8M0 block scales.  Lane (row l % 32, half h) supplies, for
+// K-step (s2, j), word j of the 16-byte piece 2 h + s2 of its row's 64-byte
+// chunk, the same K order for both operands.
+#include "q4_internal.h"
+
+namespace q4 {
+namespace {
+
+constexpr int SM = 32;    // rows per tile
+constexpr int SN = 256;   // output columns per workgroup
+constexpr int CK = 128;   // K per chunk
+
+__device__ __forceinline__ uint32_t e4m3_dup_f16_s(uint32_t pair, int which) {
+  const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
+  const uint32_t d = __builtin_amdgcn_perm(0u, pair, which ? 0x0c010c01u : 0x0c000c00u) << 7;
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d) * k256);
+}
+
+__device__ __forceinline__ half8v decode8_s(uint32_t w, uint32_t pair) {
+  const half2v s = __builtin_bit_cast(half2v, pair);
+  const half2v h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+  const half2v h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+  const half2v h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+  const half2v h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+  half8v r;
+  r[0] = h0.x; r[1] = h0.y; r[2] = h1.x; r[3] = h1.y;
+  r[4] = h2.x; r[5] = h2.y; r[6] = h3.x; r[7] = h3.y;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t word_s(const uint4& v, int j) {
+  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+// one K-chunk of one lane: codes of the lane's A row and of its two W rows
+// (pieces 2h and 2h + 1), and the E4M3 bytes of blocks 4h .. 4h + 3 (NVFP4)
+// or the E8M0 bytes of blocks 2 s + h (MXFP4, two 64-element steps)
+struct SkinnyChunk {
+  uint4 a[2], b[2][2];
+  uint32_t sa, sb[2];
+};
+
+template <bool MX, int EPI>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t N = g.N;
+  const int K = g.K;
+  const int nbn = (int)((N + SN - 1) / SN);
+  const int mt = blockIdx.x / nbn, nt = blockIdx.x % nbn;
+  if (mt >= g.ntiles_dev[0]) return;
+  const int4 t = ((const int4*)g.tiles)[mt];
+  const int e = t.x;
+  const int64_t m0 = t.y, m_end = t.z;
+  const int64_t c0 = (int64_t)nt * SN + wave * 64;   // first output column of this wave
+  if (c0 >= N) return;                                // no barriers below: waves are independent
+
+  const int64_t cstride = K / 2, sstride = MX ? K / 32 : K / 16;
+  const int64_t r = m0 + l32;
+  const bool rok = r < m_end;
+  const int64_t arow = rok ? (g.a_rows ? (int64_t)g.a_rows[r] : r) : 0;
+  const uint8_t* const ac = g.a_codes + arow * cstride;
+  const uint8_t* const as = g.a_scales + arow * sstride;
+  const uint8_t* bc[2];
+  const uint8_t* bs[2];
+  bool cok[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) {
+    const int64_t col = c0 + ni * 32 + l32;
+    cok[ni] = col < N;
+    bc[ni] = g.w_codes + ((int64_t)e * N + (cok[ni] ? col : 0)) * cstride;
+    bs[ni] = g.w_scales + ((int64_t)e * N + (cok[ni] ? col : 0)) * sstride;
+  }
+
+  // NVFP4 scale bytes 4h .. 4h + 3 of a chunk as two 16-bit loads (rows are
+  // only 2-byte aligned when K % 64 != 0); blocks past K read as zero
+  auto scales4 = [&](const uint8_t* sp, int k0) -> uint32_t {
+    const int left = K - (k0 + 64 * h);   // channels of this lane's half still inside K
+    const uint32_t lo = left >= 32 ? *(const uint16_t*)(sp + k0 / 16 + 4 * h) : 0u;
+    const uint32_t hi = left >= 64 ? *(const uint16_t*)(sp + k0 / 16 + 4 * h + 2) : 0u;
+    return lo | (hi << 16);
+  };
+  auto load = [&](SkinnyChunk& c, int k0) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // NVFP4: piece 2h + s (channels k0 + 32 (2h + s) ..).  MXFP4: step s,
+      // block h (channels k0 + 64 s + 32 h ..): piece 2s + h
+      const int piece = MX ? 2 * s + h : 2 * h + s;
+      const bool kin = k0 + 32 * piece < K;
+      c.a[s] = (rok && kin) ? *(const uint4*)(ac + k0 / 2 + 16 * piece) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        c.b[ni][s] = (cok[ni] && kin) ? *(const uint4*)(bc[ni] + k0 / 2 + 16 * piece)
+                                      : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (MX) {
+      // E8M0 bytes of blocks (k0 / 32) + h and + 2 + h, byte s of the word
+      uint32_t sa = 0, sb0 = 0, sb1 = 0;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int blk = k0 / 32 + 2 * s + h;
+        if (blk * 32 < K) {
+          if (rok) sa |= (uint32_t)as[blk] << (8 * s);
+          if (cok[0]) sb0 |= (uint32_t)bs[0][blk] << (8 * s);
+          if (cok[1]) sb1 |= (uint32_t)bs[1][blk] << (8 * s);
+        }
+      }
+      c.sa = sa;
+      c.sb[0] = sb0;
+      c.sb[1] = sb1;
+    } else {
+      c.sa = rok ? scales4(as, k0) : 0u;
+      c.sb[0] = cok[0] ? scales4(bs[0], k0) : 0u;
+      c.sb[1] = cok[1] ? scales4(bs[1], k0) : 0u;
+    }
+  };
+
+  f32x16v acc[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[ni][q] = 0.0f;
+
+  auto compute = [&](const SkinnyChunk& c) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const i32x8v af = {(int)c.a[s].x, (int)c.a[s].y, (int)c.a[s].z, (int)c.a[s].w, 0, 0, 0, 0};
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const i32x8v bf = {(int)c.b[ni][s].x, (int)c.b[ni][s].y, (int)c.b[ni][s].z,
+                             (int)c.b[ni][s].w, 0, 0, 0, 0};
+          acc[ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af, bf, acc[ni], 4, 4, 0, (int)((c.sa >> (8 * s)) & 255u), 0,
+              (int)((c.sb[ni] >> (8 * s)) & 255u));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        // piece 2h + s holds blocks 4h + 2s and 4h + 2s + 1: bytes 2s, 2s + 1
+        const uint32_t pa = c.sa >> (16 * s), pb0 = c.sb[0] >> (16 * s), pb1 = c.sb[1] >> (16 * s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const half8v af = decode8_s(word_s(c.a[s], j), e4m3_dup_f16_s(pa, j >= 2));
+          const half8v b0 = decode8_s(word_s(c.b[0][s], j), e4m3_dup_f16_s(pb0, j >= 2));
+          const half8v b1 = decode8_s(word_s(c.b[1][s], j), e4m3_dup_f16_s(pb1, j >= 2));
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b0, acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b1, acc[1], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // the next chunk loads while the current one is computed (two register
+  // sets); occupancy hides the rest of the memory latency
+  SkinnyChunk cA, cB;
+  load(cA, 0);
+  for (int k0 = 0;;) {
+    if (k0 + CK < K) load(cB, k0 + CK);
+    compute(cA);
+    k0 += CK;
+    if (k0 >= K) break;
+    if (k0 + CK < K) load(cA, k0 + CK);
+    compute(cB);
+    k0 += CK;
+    if (k0 >= K) break;
+  }
+
+  const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[e] : 1.0f;
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[ni][q] *= alpha;
+
+  // residual compensation: bf16 R rows of the tile x bf16 selected W columns
+  if (g.kp > 0 && g.r_res) {
+    const uint16_t* rrow = g.r_res + arow * g.ld_r + 8 * h;
+    const uint16_t* wrow[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int64_t col = c0 + ni * 32 + l32;
+      wrow[ni] = g.w_sel + ((int64_t)e * N + (cok[ni] ? col : 0)) * g.kp + 8 * h;
+    }
+    for (int kt = 0; kt < g.kp; kt += 16) {
+      const bf16x8v af =
+          __builtin_bit_cast(bf16x8v, rok ? *(const uint4*)(rrow + kt) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const bf16x8v bf = __builtin_bit_cast(
+            bf16x8v, cok[ni] ? *(const uint4*)(wrow[ni] + kt) : make_uint4(0, 0, 0, 0));
+        acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[ni], 0, 0, 0);
+      }
+    }
+  }
+
+  // accumulator element q of lane l: row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int64_t row = m0 + 8 * (q >> 2) + 4 * h + (q & 3);
+    if (row >= m_end) continue;
+    if constexpr (EPI == kEpiSwiGLU) {
+      // packed W13: columns c0 .. c0 + 31 gate, c0 + 32 .. c0 + 63 up
+      const float gv = acc[0][q], uv = acc[1][q];
+      const float hv = gv / (1.0f + __expf(-gv)) * uv;
+      ((uint16_t*)g.Y)[row * g.ldy + c0 / 2 + l32] = (uint16_t)f32_to_bf16_rne(hv);
+    } else {
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int64_t col = c0 + ni * 32 + l32;
+        if (col >= N) continue;
+        if (g.y_bf16)
+          ((uint16_t*)g.Y)[row * g.ldy + col] = (uint16_t)f32_to_bf16_rne(acc[ni][q]);
+        else
+          ((float*)g.Y)[row * g.ldy + col] = acc[ni][q];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t stream) {
+  const int64_t nbn = (g.N + SN - 1) / SN;
+  const int64_t nb = max_tiles * nbn;
+  if (nb == 0) return hipSuccess;
+  const dim3 grid((unsigned)nb), block(256);
+  if (g.mx) {
+    if (g.epilogue == kEpiSwiGLU)
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, kEpiSwiGLU>), grid, block, 0, stream, g);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<true, kEpiStore>), grid, block, 0, stream, g);
+  } else {
+    if (g.epilogue == kEpiSwiGLU)
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, kEpiSwiGLU>), grid, block, 0, stream, g);
+    else
+      hipLaunchKernelGGL((gemm_skinny_kernel<false, kEpiStore>), grid, block, 0, stream, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace q4
