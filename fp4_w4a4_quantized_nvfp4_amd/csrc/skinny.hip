@@ -233,6 +233,288 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same tiles with the operands staged through LDS: each wave fills its
+// own four-stage LDS ring straight from global memory (global_load_lds, four
+// lanes per 64-byte row chunk, so every load is fully coalesced) three chunks
+// ahead, and reads its MFMA fragments back from LDS.  No barriers: a wave
+// only reads what it loaded itself.  Needs K % 64 == 0 (NVFP4) or
+// K % 128 == 0 (MXFP4: 4-byte scale rows per chunk).
+typedef const void __attribute__((address_space(1)))* sk_gptr_t;
+typedef void __attribute__((address_space(3)))* sk_lptr_t;
+
+constexpr int SW_CODE = 0;        // 64 W rows x 64 B
+constexpr int SA_CODE = 4096;     // 32 A rows x 64 B
+constexpr int SW_SC = 6144;       // W scales: 64 x 8 B (NVFP4) or 64 x 4 B (MXFP4)
+constexpr int SA_SC = 6656;       // A scales: 32 x 8 B (NVFP4) or 32 x 4 B (+ copies)
+constexpr int SREGION = 6912;     // bytes per wave per stage
+constexpr int SSTAGE = 4 * SREGION;
+
+__device__ __forceinline__ int sk_swz(int row, int piece) {
+  return row * 64 + ((piece ^ ((row >> 1) ^ (row >> 2)) & 3) << 4);
+}
+
+constexpr int sk_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <bool MX, int EPI>
+__global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
+  constexpr int DMA = MX ? 8 : 9;   // global -> LDS loads per wave per chunk
+  __shared__ __attribute__((aligned(16))) uint8_t st0[SSTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[SSTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[SSTAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[SSTAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t N = g.N;
+  const int K = g.K;
+  const int nk = (K + CK - 1) / CK;
+  const int nbn = (int)((N + SN - 1) / SN);
+  const int mt = blockIdx.x / nbn, nt = blockIdx.x % nbn;
+  if (mt >= g.ntiles_dev[0]) return;
+  const int4 t = ((const int4*)g.tiles)[mt];
+  const int e = t.x;
+  const int64_t m0 = t.y, m_end = t.z;
+  const int64_t c0 = (int64_t)nt * SN + wave * 64;
+  if (c0 >= N) return;                      // no barriers: waves are independent
+  const int reg = wave * SREGION;
+
+  const int64_t cstride = K / 2, sstride = MX ? K / 32 : K / 16;
+  const uint8_t* const wcb = g.w_codes + (int64_t)e * N * cstride;
+  const uint8_t* const wsb = g.w_scales + (int64_t)e * N * sstride;
+  // rows past the tile read a valid row again (their results are never stored)
+  auto wrow = [&](int r) -> int64_t { return min(c0 + r, N - 1); };
+  auto arow_of = [&](int r) -> int64_t {
+    const int64_t rr = min(m0 + r, m_end - 1);
+    return g.a_rows ? (int64_t)g.a_rows[rr] : rr;
+  };
+  // per-lane global offsets of this wave's loads (row and swizzled piece)
+  uint32_t wco[4], aco[2];
+  int wpiece[4], apiece[2];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int row = 16 * it + (lane >> 2);
+    wpiece[it] = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
+    wco[it] = (uint32_t)(wrow(row) * cstride);
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int row = 16 * it + (lane >> 2);
+    apiece[it] = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
+    aco[it] = (uint32_t)0;
+  }
+  const uint8_t* abase[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) abase[it] = g.a_codes + arow_of(16 * it + (lane >> 2)) * cstride;
+  // scale loads
+  const uint8_t* wsrc[2];
+  const uint8_t* asrc;
+  if constexpr (MX) {
+    wsrc[0] = wsb + wrow(lane) * sstride;
+    wsrc[1] = wsrc[0];
+    asrc = g.a_scales + arow_of(lane & 31) * sstride;
+  } else {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) wsrc[it] = wsb + wrow(32 * it + (lane >> 1)) * sstride + 4 * (lane & 1);
+    asrc = g.a_scales + arow_of(lane >> 1) * sstride + 4 * (lane & 1);
+  }
+  (void)aco;
+
+  // chunk c (clamped: past the end, the last chunk again into a stage nobody reads)
+  auto issue = [&](int c, uint8_t* const sb) {
+    const int cc = min(c, nk - 1);
+    const int k0 = cc * CK;
+    uint8_t* const base = sb + reg;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      // pieces past K (K % 128 == 64) read the chunk's first half again
+      const int pc = (k0 + 32 * wpiece[it] < K) ? wpiece[it] : (wpiece[it] & 1);
+      __builtin_amdgcn_global_load_lds((sk_gptr_t)(wcb + wco[it] + k0 / 2 + 16 * pc),
+                                       (sk_lptr_t)(base + SW_CODE + it * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int pc = (k0 + 32 * apiece[it] < K) ? apiece[it] : (apiece[it] & 1);
+      __builtin_amdgcn_global_load_lds((sk_gptr_t)(abase[it] + k0 / 2 + 16 * pc),
+                                       (sk_lptr_t)(base + SA_CODE + it * 1024), 16, 0, 0);
+    }
+    if constexpr (MX) {
+      __builtin_amdgcn_global_load_lds((sk_gptr_t)(wsrc[0] + k0 / 32),
+                                       (sk_lptr_t)(base + SW_SC), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((sk_gptr_t)(asrc + k0 / 32),
+                                       (sk_lptr_t)(base + SA_SC), 4, 0, 0);
+    } else {
+      // second dword (blocks 4..7) past K reads the first again
+      const int dw = (k0 + 64 < K) ? 1 : 0;
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+        __builtin_amdgcn_global_load_lds(
+            (sk_gptr_t)(wsrc[it] + k0 / 16 - 4 * (lane & 1) + 4 * ((lane & 1) & dw)),
+            (sk_lptr_t)(base + SW_SC + it * 256), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (sk_gptr_t)(asrc + k0 / 16 - 4 * (lane & 1) + 4 * ((lane & 1) & dw)),
+          (sk_lptr_t)(base + SA_SC), 4, 0, 0);
+    }
+  };
+
+  f32x16v acc[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[ni][q] = 0.0f;
+
+  auto compute = [&](const SkinnyChunk& c) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const i32x8v af = {(int)c.a[s].x, (int)c.a[s].y, (int)c.a[s].z, (int)c.a[s].w, 0, 0, 0, 0};
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const i32x8v bf = {(int)c.b[ni][s].x, (int)c.b[ni][s].y, (int)c.b[ni][s].z,
+                             (int)c.b[ni][s].w, 0, 0, 0, 0};
+          acc[ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af, bf, acc[ni], 4, 4, 0, (int)((c.sa >> (8 * s)) & 255u), 0,
+              (int)((c.sb[ni] >> (8 * s)) & 255u));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        // piece 2h + s holds blocks 4h + 2s and 4h + 2s + 1: bytes 2s, 2s + 1
+        const uint32_t pa = c.sa >> (16 * s), pb0 = c.sb[0] >> (16 * s), pb1 = c.sb[1] >> (16 * s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const half8v af = decode8_s(word_s(c.a[s], j), e4m3_dup_f16_s(pa, j >= 2));
+          const half8v b0 = decode8_s(word_s(c.b[0][s], j), e4m3_dup_f16_s(pb0, j >= 2));
+          const half8v b1 = decode8_s(word_s(c.b[1][s], j), e4m3_dup_f16_s(pb1, j >= 2));
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b0, acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b1, acc[1], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // one chunk from stage sb: fragments, then the loads of chunk c + 3 into
+  // stage nx (read in the previous chunk), then the MFMAs
+  auto step = [&](int c, const uint8_t* const sb, uint8_t* const nx) {
+    const uint8_t* const base = sb + reg;
+    const int k0 = c * CK;
+    SkinnyChunk f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int piece = MX ? 2 * s + h : 2 * h + s;
+      const bool kin = k0 + 32 * piece < K;
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      const uint4 a = *(const uint4*)(base + SA_CODE + sk_swz(l32, piece));
+      const uint4 b0 = *(const uint4*)(base + SW_CODE + sk_swz(l32, piece));
+      const uint4 b1 = *(const uint4*)(base + SW_CODE + sk_swz(32 + l32, piece));
+      f.a[s] = kin ? a : z;
+      f.b[0][s] = kin ? b0 : z;
+      f.b[1][s] = kin ? b1 : z;
+    }
+    if constexpr (MX) {
+      // E8M0 of blocks 2s + h: bytes of the row's 4-byte record; 127 (= 1.0)
+      // where the block is past K
+      const uint32_t ra = *(const uint32_t*)(base + SA_SC + l32 * 4);
+      const uint32_t rb0 = *(const uint32_t*)(base + SW_SC + l32 * 4);
+      const uint32_t rb1 = *(const uint32_t*)(base + SW_SC + (32 + l32) * 4);
+      uint32_t sa = 0, sb0 = 0, sb1 = 0;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int bi = 2 * s + h;
+        const bool kin = k0 + 32 * bi < K;
+        sa |= (kin ? (ra >> (8 * bi)) & 255u : 127u) << (8 * s);
+        sb0 |= (kin ? (rb0 >> (8 * bi)) & 255u : 127u) << (8 * s);
+        sb1 |= (kin ? (rb1 >> (8 * bi)) & 255u : 127u) << (8 * s);
+      }
+      f.sa = sa;
+      f.sb[0] = sb0;
+      f.sb[1] = sb1;
+    } else {
+      f.sa = *(const uint32_t*)(base + SA_SC + l32 * 8 + 4 * h);
+      f.sb[0] = *(const uint32_t*)(base + SW_SC + l32 * 8 + 4 * h);
+      f.sb[1] = *(const uint32_t*)(base + SW_SC + (32 + l32) * 8 + 4 * h);
+    }
+    issue(c + 3, nx);
+    compute(f);
+  };
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+  int kc = 0;
+  for (; kc < nk; kc += 4) {
+    __builtin_amdgcn_s_waitcnt(sk_vmcnt(2 * DMA));
+    step(kc, st0, st3);
+    if (kc + 1 >= nk) break;
+    __builtin_amdgcn_s_waitcnt(sk_vmcnt(2 * DMA));
+    step(kc + 1, st1, st0);
+    if (kc + 2 >= nk) break;
+    __builtin_amdgcn_s_waitcnt(sk_vmcnt(2 * DMA));
+    step(kc + 2, st2, st1);
+    if (kc + 3 >= nk) break;
+    __builtin_amdgcn_s_waitcnt(sk_vmcnt(2 * DMA));
+    step(kc + 3, st3, st2);
+  }
+  __builtin_amdgcn_s_waitcnt(sk_vmcnt(0));
+
+  const int64_t r = m0 + l32;
+  const bool rok = r < m_end;
+  const int64_t arow = rok ? (g.a_rows ? (int64_t)g.a_rows[r] : r) : 0;
+  bool cok[2];
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) cok[ni] = c0 + ni * 32 + l32 < N;
+
+  const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[e] : 1.0f;
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[ni][q] *= alpha;
+
+  // residual compensation: bf16 R rows of the tile x bf16 selected W columns
+  if (g.kp > 0 && g.r_res) {
+    const uint16_t* rrow = g.r_res + arow * g.ld_r + 8 * h;
+    const uint16_t* wrow[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int64_t col = c0 + ni * 32 + l32;
+      wrow[ni] = g.w_sel + ((int64_t)e * N + (cok[ni] ? col : 0)) * g.kp + 8 * h;
+    }
+    for (int kt = 0; kt < g.kp; kt += 16) {
+      const bf16x8v af =
+          __builtin_bit_cast(bf16x8v, rok ? *(const uint4*)(rrow + kt) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const bf16x8v bf = __builtin_bit_cast(
+            bf16x8v, cok[ni] ? *(const uint4*)(wrow[ni] + kt) : make_uint4(0, 0, 0, 0));
+        acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[ni], 0, 0, 0);
+      }
+    }
+  }
+
+  // accumulator element q of lane l: row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int64_t row = m0 + 8 * (q >> 2) + 4 * h + (q & 3);
+    if (row >= m_end) continue;
+    if constexpr (EPI == kEpiSwiGLU) {
+      // packed W13: columns c0 .. c0 + 31 gate, c0 + 32 .. c0 + 63 up
+      const float gv = acc[0][q], uv = acc[1][q];
+      const float hv = gv / (1.0f + __expf(-gv)) * uv;
+      ((uint16_t*)g.Y)[row * g.ldy + c0 / 2 + l32] = (uint16_t)f32_to_bf16_rne(hv);
+    } else {
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const int64_t col = c0 + ni * 32 + l32;
+        if (col >= N) continue;
+        if (g.y_bf16)
+          ((uint16_t*)g.Y)[row * g.ldy + col] = (uint16_t)f32_to_bf16_rne(acc[ni][q]);
+        else
+          ((float*)g.Y)[row * g.ldy + col] = acc[ni][q];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t stream) {
@@ -240,6 +522,20 @@ hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t 
   const int64_t nb = max_tiles * nbn;
   if (nb == 0) return hipSuccess;
   const dim3 grid((unsigned)nb), block(256);
+  if (g.mx ? g.K % 128 == 0 : g.K % 64 == 0) {
+    if (g.mx) {
+      if (g.epilogue == kEpiSwiGLU)
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<true, kEpiSwiGLU>), grid, block, 0, stream, g);
+      else
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<true, kEpiStore>), grid, block, 0, stream, g);
+    } else {
+      if (g.epilogue == kEpiSwiGLU)
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<false, kEpiSwiGLU>), grid, block, 0, stream, g);
+      else
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<false, kEpiStore>), grid, block, 0, stream, g);
+    }
+    return hipGetLastError();
+  }
   if (g.mx) {
     if (g.epilogue == kEpiSwiGLU)
       hipLaunchKernelGGL((gemm_skinny_kernel<true, kEpiSwiGLU>), grid, block, 0, stream, g);
