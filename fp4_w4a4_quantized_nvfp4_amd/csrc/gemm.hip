@@ -505,55 +505,73 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   const int64_t m0 = (int64_t)(first + in % gsz) * BM;
   const int64_t n0 = (int64_t)(in / gsz) * BN;
   const int64_t m_end = g.M;
-  // rows past the end of A or W read the last row again: their products land
-  // only in output rows / columns that are never stored
-  const int a_last = (int)min<int64_t>(BM - 1, g.M - 1 - m0);
-  const int b_last = (int)min<int64_t>(BN - 1, N - 1 - n0);
 
+  // Global -> LDS loads go through buffer resources based at the tile's
+  // first row, with the operand's extent from there as the range: rows past
+  // the end of A or W read as zeros (their products land only in output rows
+  // and columns that are never stored).  Every per-lane offset is the same
+  // for all chunks and all load instructions of one operand; the chunk and
+  // the instruction's row block go into the scalar offset.
   const uint32_t cstride = (uint32_t)(K / 2), sstride = (uint32_t)(K / 16);
-  const uint8_t* const a_base = g.a_codes + (size_t)m0 * cstride;
-  const uint8_t* const b_base = g.w_codes + (size_t)n0 * cstride;
-  // direct loads: instruction `it` of this wave fills the 1 KiB of LDS that
+  auto rsrc = [](const void* base, int64_t bytes) {
+    // every input is uniform; readfirstlane says so, so that the resource
+    // stays in scalar registers
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    const uint32_t n = bytes <= 0 ? 0u : (bytes >= 0xffffffffLL ? 0xffffffffu : (uint32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0,
+                                             __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
+  };
+  const __amdgpu_buffer_rsrc_t a_rs = rsrc(g.a_codes + (size_t)m0 * cstride, (g.M - m0) * cstride);
+  const __amdgpu_buffer_rsrc_t b_rs = rsrc(g.w_codes + (size_t)n0 * cstride, (N - n0) * cstride);
+  // code loads: instruction `it` of this wave fills the 1 KiB of LDS that
   // holds tile rows 16 * (4 * it + wave) .. + 15; lane l writes 16 bytes at
   // l * 16, i.e. row 16 * c + l / 4, swizzled slot l % 4, which holds the
-  // logical 16-byte piece slot ^ f(row)
-  uint32_t a_goff[4], b_goff[4];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int row = 16 * (4 * it + wave) + (lane >> 2);
-    const int piece = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-    a_goff[it] = (uint32_t)min(row, a_last) * cstride + (uint32_t)piece * 16u;
-    b_goff[it] = (uint32_t)min(row, b_last) * cstride + (uint32_t)piece * 16u;
-  }
-  // scale loads: instruction `it` of this wave fills 256 bytes of LDS (rows
-  // 32 * (4 * it + wave) .. + 31, 8 bytes each); lane l loads dword l % 2 of
-  // row 32 * c + l / 2
-  const uint8_t* const as_base = g.a_scales + (size_t)m0 * sstride;
-  const uint8_t* const bs_base = g.w_scales + (size_t)n0 * sstride;
-  uint32_t as_goff[2], bs_goff[2];
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int row = 32 * (4 * it + wave) + (lane >> 1);
-    as_goff[it] = (uint32_t)min(row, a_last) * sstride + (uint32_t)(lane & 1) * 4u;
-    bs_goff[it] = (uint32_t)min(row, b_last) * sstride + (uint32_t)(lane & 1) * 4u;
-  }
+  // logical 16-byte piece slot ^ f(row) (f sees row bits 1..3 only, which
+  // `it` does not change)
+  const int c_row = 16 * wave + (lane >> 2);
+  const uint32_t c_voff = (uint32_t)c_row * cstride +
+                          (uint32_t)(((lane & 3) ^ (((c_row >> 1) ^ (c_row >> 2)) & 3)) * 16);
+  // raw scale loads: instruction `it` of this wave fills 256 bytes of LDS
+  // (rows 32 * (4 * it + wave) .. + 31, 8 bytes each); lane l loads dword
+  // l % 2 of row 32 * c + l / 2
+  const __amdgpu_buffer_rsrc_t as_rs = rsrc(g.a_scales + (size_t)m0 * sstride, (g.M - m0) * sstride);
+  const __amdgpu_buffer_rsrc_t bs_rs = rsrc(g.w_scales + (size_t)n0 * sstride, (N - n0) * sstride);
+  const uint32_t s_voff = (uint32_t)(32 * wave + (lane >> 1)) * sstride + (uint32_t)(lane & 1) * 4u;
+  // tiled scale records [chunk][padded row][16 B]: lane l of the wave loads
+  // the record of tile row 64 * wave + l
+  const __amdgpu_buffer_rsrc_t ast_rs =
+      rsrc(g.a_scales_t + ((size_t)m0 << 4), ((int64_t)nk * g.a_rows_pad - m0) << 4);
+  const __amdgpu_buffer_rsrc_t bst_rs =
+      rsrc(g.w_scales_t + ((size_t)n0 << 4), ((int64_t)nk * g.w_rows_pad - n0) << 4);
+  const uint32_t t_voff = (uint32_t)(64 * wave + lane) << 4;
 
-  // LDS read offsets within a stage for half s2 = 0 (s2 = 1: code ^ 16,
-  // scale + 2); piece p = 2 h + s2 holds scale blocks 2p and 2p + 1
-  uint32_t ca_off[4], cb_off[4], sa_off[4], sb_off[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int ra = wm * 128 + q * 32 + l32, rb = wn * 128 + q * 32 + l32;
-    ca_off[q] = (uint32_t)swz(ra, 2 * h);
-    cb_off[q] = (uint32_t)(B_CODE_OFF + swz(rb, 2 * h));
+  // LDS read offsets within a stage of fragment q = 0 for half s2 (piece
+  // p = 2 h + s2 holds scale blocks 2p and 2p + 1).  Both swizzles depend on
+  // row bits 1..4 only, so fragment q sits at a fixed distance (q * 32 rows)
+  // from fragment 0: one address register per operand and half, the rest
+  // goes into the instruction's immediate offset.
+  uint32_t ca_off[2], cb_off[2], sa_off[2], sb_off[2];
+  {
+    const int ra = wm * 128 + l32, rb = wn * 128 + l32;
+    ca_off[0] = (uint32_t)swz(ra, 2 * h);
+    cb_off[0] = (uint32_t)(B_CODE_OFF + swz(rb, 2 * h));
+    ca_off[1] = ca_off[0] ^ 16u;
+    cb_off[1] = cb_off[0] ^ 16u;
     if constexpr (TILED) {
-      sa_off[q] = (uint32_t)(A_SC_OFF + swz_sc(ra, 2 * h));
-      sb_off[q] = (uint32_t)(B_SC_OFF + swz_sc(rb, 2 * h));
+      sa_off[0] = (uint32_t)(A_SC_OFF + swz_sc(ra, 2 * h));
+      sb_off[0] = (uint32_t)(B_SC_OFF + swz_sc(rb, 2 * h));
+      sa_off[1] = sa_off[0] ^ 4u;
+      sb_off[1] = sb_off[0] ^ 4u;
     } else {
-      sa_off[q] = (uint32_t)(A_SC_OFF + ra * 8 + 4 * h);
-      sb_off[q] = (uint32_t)(B_SC_OFF + rb * 8 + 4 * h);
+      sa_off[0] = (uint32_t)(A_SC_OFF + ra * 8 + 4 * h);
+      sb_off[0] = (uint32_t)(B_SC_OFF + rb * 8 + 4 * h);
+      sa_off[1] = sa_off[0] + 2u;
+      sb_off[1] = sb_off[0] + 2u;
     }
   }
+  constexpr uint32_t Q_CODE = 32 * CB, Q_SC = 32 * SC_ROW<TILED>;
 
   // global -> LDS traffic of FP4 chunk kc (kc < nk): codes, then scales
   auto issue_codes = [&](int kc, uint8_t* const sbase) {
@@ -561,31 +579,28 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     uint8_t* const dst = sbase + wave * 1024;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      __builtin_amdgcn_global_load_lds((gptr_t)(a_base + kb + a_goff[it]),
-                                       (lptr_t)(dst + it * 4096), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gptr_t)(b_base + kb + b_goff[it]),
-                                       (lptr_t)(dst + B_CODE_OFF + it * 4096), 16, 0, 0);
+      const uint32_t so = kb + (uint32_t)(64 * it) * cstride;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lptr_t)(dst + it * 4096), 16, c_voff, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lptr_t)(dst + B_CODE_OFF + it * 4096), 16,
+                                               c_voff, so, 0, 0);
     }
   };
   auto issue_scales = [&](int kc, uint8_t* const sbase) {
-    const uint32_t ks = (uint32_t)kc * (BK / 16);
     if constexpr (TILED) {
-      // record of tile row 64 * wave + lane in chunk kc: [chunk][padded row][16 B]
-      const size_t kt = (size_t)kc;
-      __builtin_amdgcn_global_load_lds(
-          (gptr_t)(g.a_scales_t + ((kt * g.a_rows_pad + m0 + 64 * wave + lane) << 4)),
-          (lptr_t)(sbase + A_SC_OFF + wave * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (gptr_t)(g.w_scales_t + ((kt * g.w_rows_pad + n0 + 64 * wave + lane) << 4)),
-          (lptr_t)(sbase + B_SC_OFF + wave * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ast_rs, (lptr_t)(sbase + A_SC_OFF + wave * 1024), 16,
+                                               t_voff, (uint32_t)(kc * g.a_rows_pad) << 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bst_rs, (lptr_t)(sbase + B_SC_OFF + wave * 1024), 16,
+                                               t_voff, (uint32_t)(kc * g.w_rows_pad) << 4, 0, 0);
     } else {
+      const uint32_t ks = (uint32_t)kc * (BK / 16);
       uint8_t* const sdst = sbase + wave * 256;
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
-        __builtin_amdgcn_global_load_lds((gptr_t)(as_base + ks + as_goff[it]),
-                                         (lptr_t)(sdst + A_SC_OFF + it * 1024), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((gptr_t)(bs_base + ks + bs_goff[it]),
-                                         (lptr_t)(sdst + B_SC_OFF + it * 1024), 4, 0, 0);
+        const uint32_t so = ks + (uint32_t)(128 * it) * sstride;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rs, (lptr_t)(sdst + A_SC_OFF + it * 1024), 4,
+                                                 s_voff, so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rs, (lptr_t)(sdst + B_SC_OFF + it * 1024), 4,
+                                                 s_voff, so, 0, 0);
       }
     }
   };
@@ -596,56 +611,57 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   };
 
   // Residual compensation chunks: R [M][ld_r] and W_S [N][kp] (bf16,
-  // kp % 32 == 0) follow the FP4 chunks through the same stages, 32 channels
-  // per chunk (64 bytes per row, the code chunks' layout), straight into bf16
-  // MFMAs.  Chunk nk + j is RAC chunk j.
+  // kp % 32 == 0) go through the same stages ahead of the FP4 chunks, 32
+  // channels per chunk (64 bytes per row, the code chunks' layout), straight
+  // into bf16 MFMAs.  Chunk j < nrac is RAC chunk j, chunk nrac + kc is FP4
+  // chunk kc.
   const int nrac = (g.kp > 0 && g.r_res) ? g.kp / 32 : 0;
-  const uint8_t* const r_base = (const uint8_t*)(g.r_res + (size_t)m0 * g.ld_r);
-  const uint8_t* const w_base = (const uint8_t*)(g.w_sel + (size_t)n0 * g.kp);
   const uint32_t r_stride = (uint32_t)g.ld_r * 2u, w_stride = (uint32_t)g.kp * 2u;
+  const __amdgpu_buffer_rsrc_t r_rs =
+      rsrc(g.r_res + (size_t)m0 * g.ld_r, nrac ? (g.M - m0) * (int64_t)r_stride : 0);
+  const __amdgpu_buffer_rsrc_t w_rs =
+      rsrc(g.w_sel + (size_t)n0 * g.kp, nrac ? (N - n0) * (int64_t)w_stride : 0);
+  // same row / piece layout as the code loads, with the operands' own strides
+  const uint32_t c_piece = (uint32_t)(((lane & 3) ^ (((c_row >> 1) ^ (c_row >> 2)) & 3)) * 16);
+  const uint32_t r_voff = (uint32_t)c_row * r_stride + c_piece;
+  const uint32_t w_voff = (uint32_t)c_row * w_stride + c_piece;
   auto issue_rac = [&](int j, uint8_t* const sbase) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int row = 16 * (4 * it + wave) + (lane >> 2);
-      const uint32_t piece = (uint32_t)((lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3));
-      const uint32_t off = 64u * (uint32_t)j + piece * 16u;
-      __builtin_amdgcn_global_load_lds(
-          (gptr_t)(r_base + (uint32_t)min(row, a_last) * r_stride + off),
-          (lptr_t)(sbase + wave * 1024 + it * 4096), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (gptr_t)(w_base + (uint32_t)min(row, b_last) * w_stride + off),
-          (lptr_t)(sbase + B_CODE_OFF + wave * 1024 + it * 4096), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_rs, (lptr_t)(sbase + wave * 1024 + it * 4096), 16,
+                                               r_voff, 64u * (uint32_t)j + (uint32_t)(64 * it) * r_stride,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_rs, (lptr_t)(sbase + B_CODE_OFF + wave * 1024 + it * 4096), 16, w_voff,
+          64u * (uint32_t)j + (uint32_t)(64 * it) * w_stride, 0, 0);
     }
   };
-  // chunk c of the whole schedule: FP4, RAC, or (past the end) a repeat of
+  // chunk c of the whole schedule: RAC, FP4, or (past the end) a repeat of
   // the last FP4 chunk into a stage nobody reads again
   auto issue_any = [&](int c, uint8_t* const sbase) {
-    if (c < nk) {
-      issue_chunk(c, sbase);
-    } else if (c - nk < nrac) {
-      issue_rac(c - nk, sbase);
-      issue_scales(nk - 1, sbase);   // keeps the count; the scale area is unused
+    if (c < nrac) {
+      issue_rac(c, sbase);
+      issue_scales(0, sbase);   // keeps the count; the scale area is unused
     } else {
-      issue_chunk(nk - 1, sbase);
+      issue_chunk(min(c - nrac, nk - 1), sbase);
     }
   };
   auto read_frag = [&](Frag& f, const uint8_t* const base, int s2) {
-    const uint32_t cx = s2 ? 16u : 0u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      f.a[q] = *(const uint4*)(base + (ca_off[q] ^ cx));
+      f.a[q] = *(const uint4*)(base + ca_off[s2] + q * Q_CODE);
       if constexpr (TILED)
-        f.sa[q] = *(const uint32_t*)(base + (sa_off[q] ^ (s2 ? 4u : 0u)));
+        f.sa[q] = *(const uint32_t*)(base + sa_off[s2] + q * Q_SC);
       else
-        f.sa[q] = *(const uint16_t*)(base + sa_off[q] + (s2 ? 2u : 0u));
+        f.sa[q] = *(const uint16_t*)(base + sa_off[s2] + q * Q_SC);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      f.b[q] = *(const uint4*)(base + (cb_off[q] ^ cx));
+      f.b[q] = *(const uint4*)(base + cb_off[s2] + q * Q_CODE);
       if constexpr (TILED)
-        f.sb[q] = *(const uint32_t*)(base + (sb_off[q] ^ (s2 ? 4u : 0u)));
+        f.sb[q] = *(const uint32_t*)(base + sb_off[s2] + q * Q_SC);
       else
-        f.sb[q] = *(const uint16_t*)(base + sb_off[q] + (s2 ? 2u : 0u));
+        f.sb[q] = *(const uint16_t*)(base + sb_off[s2] + q * Q_SC);
     }
   };
   auto decode = [&](const Frag& f, int j, half8v* da, half8v* db) {
@@ -708,109 +724,129 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     }
   };
 
-  // FP4 chunk kc lives in stage (kc + off) % 3, so that chunk nk (the first
-  // RAC chunk) lands in stage 0: every loop below addresses its stages
-  // statically
-  const int off = (3 - nk % 3) % 3;
-  // prologue: chunks 0..2 in flight
-  if (off == 0) {
+  // Schedule chunk c lives in stage (c + roff) % 3, with roff chosen so that
+  // FP4 chunk 0 (schedule chunk nrac) lands in stage 0: the FP4 loop then
+  // needs no head, and only the cheap RAC part has one.  Prologue: chunks
+  // 0..2 in flight.
+  const int roff = (3 - nrac % 3) % 3;
+  if (roff == 0) {
     issue_any(0, stage0); issue_any(1, stage1); issue_any(2, stage2);
-  } else if (off == 1) {
+  } else if (roff == 1) {
     issue_any(0, stage1); issue_any(1, stage2); issue_any(2, stage0);
   } else {
     issue_any(0, stage2); issue_any(1, stage0); issue_any(2, stage1);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));   // chunk 0 has landed
   lds_barrier();
-  Frag f0, f1;
-  if (off == 0)
-    read_frag(f0, stage0, 0);
-  else if (off == 1)
-    read_frag(f0, stage1, 0);
-  else
-    read_frag(f0, stage2, 0);
-  decode(f0, 0, da[0], db[0]);
 
-  // one FP4 chunk; ANY: the chunk issued three ahead may be a RAC chunk
-  auto chunk = [&](int kc, uint8_t* const cur, uint8_t* const nxt, auto any) {
-    read_frag(f1, cur, 1);
-    half_chunk(f0, f1, 0);
-    // chunk kc + 1 has landed (chunk kc + 2 may still be in flight); after
-    // the barrier every wave is done with stage `cur`
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA_PER_CHUNK));
-    lds_barrier();
-    read_frag(f0, nxt, 0);
-    if constexpr (decltype(any)::value)
-      issue_any(kc + 3, cur);
-    else
-      issue_chunk(kc + 3, cur);
-    half_chunk(f1, f0, decltype(any)::value ? 0 : DMA_PER_CHUNK);
-  };
-  using fp4_only = std::false_type;
-  using with_rac = std::true_type;
-  int kc = 0;
-  if (off == 1) {
-    chunk(0, stage1, stage2, with_rac{});
-    if (nk > 1) chunk(1, stage2, stage0, with_rac{});
-    kc = 2;
-  } else if (off == 2) {
-    chunk(0, stage2, stage0, with_rac{});
-    kc = 1;
-  }
-  for (; kc + 6 <= nk; kc += 3) {
-    chunk(kc, stage0, stage1, fp4_only{});
-    chunk(kc + 1, stage1, stage2, fp4_only{});
-    chunk(kc + 2, stage2, stage0, fp4_only{});
-  }
-  if (kc + 3 <= nk) {
-    chunk(kc, stage0, stage1, with_rac{});
-    chunk(kc + 1, stage1, stage2, with_rac{});
-    chunk(kc + 2, stage2, stage0, with_rac{});
+  // RAC first, into the zeroed accumulators: RAC chunk jr in stage
+  // (jr + roff) % 3; each one waits for its own chunk (two more are in
+  // flight behind it).
+  // Piece 2 s2 + h of a row: half s2 = 1 is half 0 with offset bit 5 flipped.
+  {
+    uint32_t ra_off[2], rb_off[2];
+    ra_off[0] = (uint32_t)swz(wm * 128 + l32, h);
+    rb_off[0] = (uint32_t)(B_CODE_OFF + swz(wn * 128 + l32, h));
+    ra_off[1] = ra_off[0] ^ 32u;
+    rb_off[1] = rb_off[0] ^ 32u;
+    auto rac_chunk = [&](int jr, uint8_t* const sb) {
+      if (jr > 0) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));
+        lds_barrier();
+      }
+      uint4 fa[2][4], fb[2][4];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          fa[s2][q] = *(const uint4*)(sb + ra_off[s2] + q * Q_CODE);
+          fb[s2][q] = *(const uint4*)(sb + rb_off[s2] + q * Q_CODE);
+        }
+      lds_barrier();   // every wave is done with this stage
+      issue_any(jr + 3, sb);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8v, fa[s2][mi]), __builtin_bit_cast(bf16x8v, fb[s2][ni]),
+                acc[mi][ni], 0, 0, 0);
+    };
+    int jr = 0;
+    if (roff == 1) {   // nrac % 3 == 2
+      rac_chunk(0, stage1);
+      rac_chunk(1, stage2);
+      jr = 2;
+    } else if (roff == 2) {   // nrac % 3 == 1
+      rac_chunk(0, stage2);
+      jr = 1;
+    }
+    for (; jr < nrac; jr += 3) {
+      rac_chunk(jr, stage0);
+      rac_chunk(jr + 1, stage1);
+      rac_chunk(jr + 2, stage2);
+    }
   }
 
+  // Y = alpha * (W4A4 sum) + RAC is accumulated as alpha * (RAC / alpha +
+  // W4A4 sum): the RAC part is divided by alpha = m * 2^e (m in [0.5, 1))
+  // as a multiply by 1 / m and an exact power-of-two scaling, and alpha is
+  // applied once in the epilogue.  No range problem while |RAC| / alpha <
+  // 2^127 (with tensor scales taken from the operands' own amax it is below
+  // kp * 2688^2).  alpha == 0 leaves Y = RAC and skips the W4A4 chunks.
   const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[0] : 1.0f;
+  if (nrac > 0 && alpha != 0.0f) {
+    int e;
+    const float m = frexpf(alpha, &e);
+    const float inv_m = 1.0f / m;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= alpha;
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = ldexpf(acc[mi][ni][r] * inv_m, -e);
+  }
+  const float y_scale = alpha != 0.0f ? alpha : 1.0f;
 
-  // RAC chunk jr in stage jr % 3; chunk 0 has landed and is visible, and two
-  // chunk issues are always in flight behind the one being read
-  auto rac_chunk = [&](int jr, uint8_t* const sb) {
-    if (jr > 0) {
+  if (alpha != 0.0f) {
+    // FP4 chunk kc is schedule chunk nrac + kc, in stage kc % 3
+    if (nrac > 0) {   // FP4 chunk 0 has landed
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));
       lds_barrier();
     }
-    uint4 fa[2][4], fb[2][4];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        fa[s2][q] = *(const uint4*)(sb + swz(wm * 128 + q * 32 + l32, 2 * s2 + h));
-        fb[s2][q] = *(const uint4*)(sb + B_CODE_OFF + swz(wn * 128 + q * 32 + l32, 2 * s2 + h));
-      }
-    lds_barrier();   // every wave is done with this stage
-    issue_any(nk + jr + 3, sb);
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8v, fa[s2][mi]), __builtin_bit_cast(bf16x8v, fb[s2][ni]),
-              acc[mi][ni], 0, 0, 0);
-  };
-  int jr = 0;
-  for (; jr + 3 <= nrac; jr += 3) {
-    rac_chunk(jr, stage0);
-    rac_chunk(jr + 1, stage1);
-    rac_chunk(jr + 2, stage2);
+    Frag f0, f1;
+    read_frag(f0, stage0, 0);
+    decode(f0, 0, da[0], db[0]);
+
+    // one FP4 chunk; the chunk issued three ahead is FP4 chunk kc + 3, or a
+    // repeat of the last one past the end.  In the main loop its loads are
+    // interleaved with the MFMAs (LOOP); the tail copies issue them in one
+    // block, which also keeps the compiler from merging those copies with
+    // the loop body (that would make the stage addresses dynamic).
+    auto chunk = [&](int kc, uint8_t* const cur, uint8_t* const nxt, auto loop) {
+      read_frag(f1, cur, 1);
+      half_chunk(f0, f1, 0);
+      // chunk kc + 1 has landed (chunk kc + 2 may still be in flight); after
+      // the barrier every wave is done with stage `cur`
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA_PER_CHUNK));
+      lds_barrier();
+      read_frag(f0, nxt, 0);
+      issue_chunk(min(kc + 3, nk - 1), cur);
+      half_chunk(f1, f0, decltype(loop)::value ? DMA_PER_CHUNK : 0);
+    };
+    using in_loop = std::true_type;
+    using edge = std::false_type;
+    int kc = 0;
+    for (; kc + 3 <= nk; kc += 3) {
+      chunk(kc, stage0, stage1, in_loop{});
+      chunk(kc + 1, stage1, stage2, in_loop{});
+      chunk(kc + 2, stage2, stage0, in_loop{});
+    }
+    if (kc < nk) chunk(kc, stage0, stage1, edge{});
+    if (kc + 1 < nk) chunk(kc + 1, stage1, stage2, edge{});
   }
-  if (jr < nrac) rac_chunk(jr, stage0);
-  if (jr + 1 < nrac) rac_chunk(jr + 1, stage1);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // Epilogue through LDS so that every global store writes 16 contiguous
@@ -837,7 +873,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
               const int r = 8 * half + rr;
               const int lr = 8 * ((r >> 2) - 2 * half) + 4 * h + (r & 3);
               typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-              const bf16x2 pr = {(__bf16)acc[mi][ni][r], (__bf16)acc[mi][ni][r + 1]};
+              const bf16x2 pr = {(__bf16)(acc[mi][ni][r] * y_scale), (__bf16)(acc[mi][ni][r + 1] * y_scale)};
               const uint32_t w = __builtin_bit_cast(uint32_t, pr);
               uint8_t* const p = ep + lr * PB + (ni * 32 + l32) * 2;
               *(uint16_t*)p = (uint16_t)w;
@@ -858,7 +894,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
             for (int rr = 0; rr < 8; ++rr) {
               const int r = 8 * half + rr;
               const int lr = 8 * ((r >> 2) - 2 * half) + 4 * h + (r & 3);
-              *(float*)(ep + lr * PF + (ni * 32 + l32) * 4) = acc[mi][ni][r];
+              *(float*)(ep + lr * PF + (ni * 32 + l32) * 4) = acc[mi][ni][r] * y_scale;
             }
           }
 #pragma unroll
@@ -883,7 +919,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
       for (int ni = 0; ni < 4; ++ni) {
         const int64_t col = n0 + wn * 128 + ni * 32 + l32;
         if (col >= N) continue;
-        const float v = acc[mi][ni][r];
+        const float v = acc[mi][ni][r] * y_scale;
         if (g.y_bf16)
           ((uint16_t*)g.Y)[row * g.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
         else
