@@ -566,6 +566,7 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   g.tiles = tiles;
   g.ntiles_dev = ntiles;
   g.a_rows = a_rows;
+  g.a_src_rows = T;
   Q4_TRY(grouped_gemm(g), "moe w13 gemm");
   // ---- activation site 2: h (sorted rows)
   uint8_t* hc = (uint8_t*)P(L.off[8]);

@@ -474,8 +474,10 @@ struct Frag {
   uint32_t sa[4], sb[4];   // two raw E4M3 scales (blocks 2p, 2p + 1) per row
 };
 
-template <bool TILED>
+template <bool TILED, bool GROUPED, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
+  static_assert(!(TILED && GROUPED), "grouped tiles take raw scales");
+  static_assert(GROUPED || EPI == kEpiStore, "SwiGLU is a grouped epilogue");
   constexpr int STAGE = big::STAGE<TILED>, B_SC_OFF = big::B_SC_OFF<TILED>;
   constexpr int DMA_PER_CHUNK = big::DMA_PER_CHUNK<TILED>;
   // one LDS object per stage, addressed with compile-time stage indices, so
@@ -493,18 +495,39 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   const int64_t N = g.N;
   const int nk = K / BK;
 
-  const int nbm = (int)((g.M + BM - 1) / BM), nbn = (int)((N + BN - 1) / BN);
-  const int nb = nbm * nbn;
-  int b = blockIdx.x;
-  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);   // contiguous tile range per XCD
-  const int GM = 4;
-  const int group = b / (GM * nbn);
-  const int first = group * GM;
-  const int gsz = min(nbm - first, GM);
-  const int in = b - group * GM * nbn;
-  const int64_t m0 = (int64_t)(first + in % gsz) * BM;
-  const int64_t n0 = (int64_t)(in / gsz) * BN;
-  const int64_t m_end = g.M;
+  int64_t m0, n0, m_end;
+  int ex = 0;   // expert (grouped)
+  if constexpr (GROUPED) {
+    // tiles of the table ({expert, first row, end row} per M tile), M tile
+    // major; each XCD (workgroup index mod 8; the grid is a multiple of 8)
+    // takes a contiguous range of the tiles that exist, so it works through
+    // whole experts and their weights stay in its L2
+    const int nbn = (int)((N + BN - 1) / BN);
+    const int total = g.ntiles_dev[0] * nbn;
+    const int per = (total + 7) >> 3;
+    const int l = (int)(blockIdx.x >> 3), t = (int)(blockIdx.x & 7) * per + l;
+    if (l >= per || t >= total) return;
+    const int mt = t / nbn;
+    const int4 tt = ((const int4*)g.tiles)[mt];
+    ex = tt.x;
+    m0 = tt.y;
+    m_end = tt.z;
+    n0 = (int64_t)(t - mt * nbn) * BN;
+  } else {
+    const int nbm = (int)((g.M + BM - 1) / BM), nbn = (int)((N + BN - 1) / BN);
+    const int nb = nbm * nbn;
+    int b = blockIdx.x;
+    if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);   // contiguous tile range per XCD
+    const int GM = 4;
+    const int group = b / (GM * nbn);
+    const int first = group * GM;
+    const int gsz = min(nbm - first, GM);
+    const int in = b - group * GM * nbn;
+    m0 = (int64_t)(first + in % gsz) * BM;
+    n0 = (int64_t)(in / gsz) * BN;
+    m_end = g.M;
+  }
+  const int64_t wrow0 = (int64_t)ex * N + n0;   // first W row of the tile
 
   // Global -> LDS loads go through buffer resources based at the tile's
   // first row, with the operand's extent from there as the range: rows past
@@ -523,22 +546,46 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0,
                                              __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
   };
-  const __amdgpu_buffer_rsrc_t a_rs = rsrc(g.a_codes + (size_t)m0 * cstride, (g.M - m0) * cstride);
-  const __amdgpu_buffer_rsrc_t b_rs = rsrc(g.w_codes + (size_t)n0 * cstride, (N - n0) * cstride);
+  // Grouped: A rows are addressed absolutely (gathered through a_rows when
+  // given; rows past the tile's end repeat its last row, whose products
+  // land only in rows that are never stored), from the whole A operand.
+  const int64_t a_src_rows = g.a_src_rows > 0 ? g.a_src_rows : g.M;
+  const __amdgpu_buffer_rsrc_t a_rs =
+      GROUPED ? rsrc(g.a_codes, a_src_rows * cstride)
+              : rsrc(g.a_codes + (size_t)m0 * cstride, (g.M - m0) * cstride);
+  const __amdgpu_buffer_rsrc_t b_rs = rsrc(g.w_codes + (size_t)wrow0 * cstride, (N - n0) * cstride);
+  auto a_src = [&](int r) {   // A row of tile row r
+    const int64_t row = m0 + r < m_end ? m0 + r : m_end - 1;
+    return g.a_rows ? (int64_t)g.a_rows[row] : row;
+  };
   // code loads: instruction `it` of this wave fills the 1 KiB of LDS that
   // holds tile rows 16 * (4 * it + wave) .. + 15; lane l writes 16 bytes at
   // l * 16, i.e. row 16 * c + l / 4, swizzled slot l % 4, which holds the
   // logical 16-byte piece slot ^ f(row) (f sees row bits 1..3 only, which
   // `it` does not change)
   const int c_row = 16 * wave + (lane >> 2);
-  const uint32_t c_voff = (uint32_t)c_row * cstride +
-                          (uint32_t)(((lane & 3) ^ (((c_row >> 1) ^ (c_row >> 2)) & 3)) * 16);
+  const uint32_t c_piece = (uint32_t)(((lane & 3) ^ (((c_row >> 1) ^ (c_row >> 2)) & 3)) * 16);
+  const uint32_t c_voff = (uint32_t)c_row * cstride + c_piece;
+  uint32_t ga_voff[4] = {0, 0, 0, 0};   // grouped: A code offset of load `it`
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      ga_voff[it] = (uint32_t)a_src(16 * (4 * it + wave) + (lane >> 2)) * cstride + c_piece;
+  }
   // raw scale loads: instruction `it` of this wave fills 256 bytes of LDS
   // (rows 32 * (4 * it + wave) .. + 31, 8 bytes each); lane l loads dword
   // l % 2 of row 32 * c + l / 2
-  const __amdgpu_buffer_rsrc_t as_rs = rsrc(g.a_scales + (size_t)m0 * sstride, (g.M - m0) * sstride);
-  const __amdgpu_buffer_rsrc_t bs_rs = rsrc(g.w_scales + (size_t)n0 * sstride, (N - n0) * sstride);
+  const __amdgpu_buffer_rsrc_t as_rs =
+      GROUPED ? rsrc(g.a_scales, a_src_rows * sstride)
+              : rsrc(g.a_scales + (size_t)m0 * sstride, (g.M - m0) * sstride);
+  const __amdgpu_buffer_rsrc_t bs_rs = rsrc(g.w_scales + (size_t)wrow0 * sstride, (N - n0) * sstride);
   const uint32_t s_voff = (uint32_t)(32 * wave + (lane >> 1)) * sstride + (uint32_t)(lane & 1) * 4u;
+  uint32_t gs_voff[2] = {0, 0};   // grouped: A scale offset of load `it`
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+      gs_voff[it] = (uint32_t)a_src(32 * (4 * it + wave) + (lane >> 1)) * sstride + (uint32_t)(lane & 1) * 4u;
+  }
   // tiled scale records [chunk][padded row][16 B]: lane l of the wave loads
   // the record of tile row 64 * wave + l
   const __amdgpu_buffer_rsrc_t ast_rs =
@@ -580,7 +627,11 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const uint32_t so = kb + (uint32_t)(64 * it) * cstride;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lptr_t)(dst + it * 4096), 16, c_voff, so, 0, 0);
+      if constexpr (GROUPED)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lptr_t)(dst + it * 4096), 16, ga_voff[it], kb,
+                                                 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lptr_t)(dst + it * 4096), 16, c_voff, so, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lptr_t)(dst + B_CODE_OFF + it * 4096), 16,
                                                c_voff, so, 0, 0);
     }
@@ -597,8 +648,12 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         const uint32_t so = ks + (uint32_t)(128 * it) * sstride;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rs, (lptr_t)(sdst + A_SC_OFF + it * 1024), 4,
-                                                 s_voff, so, 0, 0);
+        if constexpr (GROUPED)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rs, (lptr_t)(sdst + A_SC_OFF + it * 1024), 4,
+                                                   gs_voff[it], ks, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rs, (lptr_t)(sdst + A_SC_OFF + it * 1024), 4,
+                                                   s_voff, so, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rs, (lptr_t)(sdst + B_SC_OFF + it * 1024), 4,
                                                  s_voff, so, 0, 0);
       }
@@ -617,20 +672,33 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   // chunk kc.
   const int nrac = (g.kp > 0 && g.r_res) ? g.kp / 32 : 0;
   const uint32_t r_stride = (uint32_t)g.ld_r * 2u, w_stride = (uint32_t)g.kp * 2u;
+  // (grouped: R rows of the A source rows, W_S rows of the expert's)
   const __amdgpu_buffer_rsrc_t r_rs =
-      rsrc(g.r_res + (size_t)m0 * g.ld_r, nrac ? (g.M - m0) * (int64_t)r_stride : 0);
+      GROUPED ? rsrc(g.r_res, nrac ? a_src_rows * (int64_t)r_stride : 0)
+              : rsrc(g.r_res + (size_t)m0 * g.ld_r, nrac ? (g.M - m0) * (int64_t)r_stride : 0);
   const __amdgpu_buffer_rsrc_t w_rs =
-      rsrc(g.w_sel + (size_t)n0 * g.kp, nrac ? (N - n0) * (int64_t)w_stride : 0);
+      rsrc(g.w_sel + (size_t)wrow0 * g.kp, nrac ? (N - n0) * (int64_t)w_stride : 0);
   // same row / piece layout as the code loads, with the operands' own strides
-  const uint32_t c_piece = (uint32_t)(((lane & 3) ^ (((c_row >> 1) ^ (c_row >> 2)) & 3)) * 16);
   const uint32_t r_voff = (uint32_t)c_row * r_stride + c_piece;
   const uint32_t w_voff = (uint32_t)c_row * w_stride + c_piece;
+  uint32_t gr_voff[4] = {0, 0, 0, 0};   // grouped: R offset of load `it`
+  if constexpr (GROUPED) {
+    if (nrac > 0) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+        gr_voff[it] = (uint32_t)a_src(16 * (4 * it + wave) + (lane >> 2)) * r_stride + c_piece;
+    }
+  }
   auto issue_rac = [&](int j, uint8_t* const sbase) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_rs, (lptr_t)(sbase + wave * 1024 + it * 4096), 16,
-                                               r_voff, 64u * (uint32_t)j + (uint32_t)(64 * it) * r_stride,
-                                               0, 0);
+      if constexpr (GROUPED)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_rs, (lptr_t)(sbase + wave * 1024 + it * 4096), 16,
+                                                 gr_voff[it], 64u * (uint32_t)j, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_rs, (lptr_t)(sbase + wave * 1024 + it * 4096), 16,
+                                                 r_voff, 64u * (uint32_t)j + (uint32_t)(64 * it) * r_stride,
+                                                 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           w_rs, (lptr_t)(sbase + B_CODE_OFF + wave * 1024 + it * 4096), 16, w_voff,
           64u * (uint32_t)j + (uint32_t)(64 * it) * w_stride, 0, 0);
@@ -796,7 +864,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   // applied once in the epilogue.  No range problem while |RAC| / alpha <
   // 2^127 (with tensor scales taken from the operands' own amax it is below
   // kp * 2688^2).  alpha == 0 leaves Y = RAC and skips the W4A4 chunks.
-  const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[0] : 1.0f;
+  const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[ex] : 1.0f;
   if (nrac > 0 && alpha != 0.0f) {
     int e;
     const float m = frexpf(alpha, &e);
@@ -849,11 +917,73 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
+  // Accumulator element r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
+  // column l % 32 of its 32 x 32 tile.
+  if constexpr (EPI == kEpiSwiGLU) {
+    // W13 with gate and up rows interleaved in blocks of 32: MFMA column
+    // tile ni = 2p is the gate and 2p + 1 the up of h columns
+    // (n0 + 128 wn) / 2 + 32 p + l % 32; h = silu(gate) * up as bf16 into
+    // Y [rows][ldy], ldy >= N / 2.  Staged through LDS per pass (a wave's 16
+    // rows x 64 h columns) so that every store writes 16 contiguous bytes.
+    const int64_t fcols = N / 2, f0 = (n0 + wn * 128) / 2;
+    const bool staged = (fcols % 8) == 0 && (g.ldy % 8) == 0 && (((uintptr_t)g.Y) & 15u) == 0;
+    auto hval = [&](int mi, int p, int r) {
+      return silu(acc[mi][2 * p][r] * y_scale) * (acc[mi][2 * p + 1][r] * y_scale);
+    };
+    if (staged) {
+      __syncthreads();   // every wave is done with the stages
+      constexpr int PS = 144;   // row pitch (bytes): 64 bf16 and 16 bytes of pad
+      uint8_t* const ep = stage0 + wave * (16 * PS);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int64_t rbase = m0 + wm * 128 + mi * 32 + 16 * half;
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+#pragma unroll
+            for (int rr = 0; rr < 8; rr += 2) {
+              const int r = 8 * half + rr;
+              const int lr = 8 * (rr >> 2) + 4 * h + (rr & 3);
+              typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+              const bf16x2 pr = {(__bf16)hval(mi, pp, r), (__bf16)hval(mi, pp, r + 1)};
+              const uint32_t w = __builtin_bit_cast(uint32_t, pr);
+              uint8_t* const q = ep + lr * PS + (pp * 32 + l32) * 2;
+              *(uint16_t*)q = (uint16_t)w;
+              *(uint16_t*)(q + PS) = (uint16_t)(w >> 16);
+            }
+          }
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const int cid = it * 64 + lane, lr = cid >> 3, cc = (cid & 7) * 8;
+            const uint4 v = *(const uint4*)(ep + lr * PS + cc * 2);
+            const int64_t row = rbase + lr, col = f0 + cc;
+            if (row < m_end && col < fcols) *(uint4*)((uint16_t*)g.Y + row * g.ldy + col) = v;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row >= m_end) continue;
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const int64_t col = f0 + pp * 32 + l32;
+            if (col < fcols)
+              ((uint16_t*)g.Y)[row * g.ldy + col] = (uint16_t)f32_to_bf16_rne(hval(mi, pp, r));
+          }
+        }
+      }
+    }
+    return;
+  }
+
   // Epilogue through LDS so that every global store writes 16 contiguous
   // bytes: per pass, a wave's 16 rows x 128 columns (rows 16 * half .. + 15 of
   // MFMA tile row mi) go to its own LDS region and come back as row chunks.
-  // Accumulator element r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
-  // column l % 32 of its 32 x 32 tile.
   const int vec = g.y_bf16 ? 8 : 4;
   const bool staged = (N % vec) == 0 && (g.ldy % vec) == 0 && (((uintptr_t)g.Y) & 15u) == 0;
   if (staged) {
@@ -960,11 +1090,26 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
   if (!grouped && fullk && g.epilogue == kEpiStore && g.M >= 512 && g.N >= 512) {
     const int64_t nb = ((g.M + big::BM - 1) / big::BM) * ((g.N + big::BN - 1) / big::BN);
     if (g.a_scales_t && g.w_scales_t)
-      hipLaunchKernelGGL(big::gemm_nvfp4_big_kernel<true>, dim3((unsigned)nb), dim3(256), 0,
-                         stream, g);
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<true, false, kEpiStore>), dim3((unsigned)nb),
+                         dim3(256), 0, stream, g);
     else
-      hipLaunchKernelGGL(big::gemm_nvfp4_big_kernel<false>, dim3((unsigned)nb), dim3(256), 0,
-                         stream, g);
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<false, false, kEpiStore>), dim3((unsigned)nb),
+                         dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
+  if (grouped && fullk && g.N % big::BN == 0 && g.K >= 1024) {
+    // (with fewer than 8 chunks per tile the fixed cost of a 256 x 256 tile
+    // outweighs its better decode reuse; the 256 x 128 kernel does those)
+    // The grid covers every possible tile, rounded up to whole XCD rounds;
+    // workgroups past the tiles that exist return at once.
+    const int64_t nb = (max_mtiles * (g.N / big::BN) + 7) / 8 * 8;
+    if (nb == 0) return hipSuccess;
+    if (g.epilogue == kEpiSwiGLU)
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<false, true, kEpiSwiGLU>), dim3((unsigned)nb),
+                         dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<false, true, kEpiStore>), dim3((unsigned)nb),
+                         dim3(256), 0, stream, g);
     return hipGetLastError();
   }
   if (fullk)

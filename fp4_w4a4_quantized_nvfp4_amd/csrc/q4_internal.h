@@ -60,6 +60,7 @@ struct GemmArgs {
   const int32_t* tiles;      // int4 {expert, row_begin, row_end, 0} per M tile (null: dense)
   const int32_t* ntiles_dev; // number of valid M tiles (device)
   const int32_t* a_rows;     // A row of each output row (null: identity)
+  int64_t a_src_rows;        // rows of the A operand that a_rows indexes (0: M)
   // optional tiled fp16 scale records (dense NVFP4, K % 128 == 0): see launch_scale_tile
   const uint8_t* a_scales_t;
   const uint8_t* w_scales_t;

@@ -99,7 +99,11 @@ def _check_site(fmt, xb, got, prefix, rac_k):
 
 @pytest.mark.parametrize("fmt", [0, 1])
 @pytest.mark.parametrize("T,H,E,F,topk,k", [(64, 256, 8, 128, 2, 16), (37, 512, 16, 64, 4, 32),
-                                            (300, 256, 4, 96, 1, 8)])
+                                            (300, 256, 4, 96, 1, 8),
+                                            # grouped tiles (256 x 256 for W13 when
+                                            # K >= 1024): partial M tiles, gathered rows
+                                            (300, 256, 2, 128, 2, 16),
+                                            (520, 1024, 4, 256, 2, 32)])
 def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
     say(f"moe small fmt={fmt} T={T} H={H} E={E} F={F} topk={topk} k={k}")
     m = q4()
