@@ -515,7 +515,8 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
                                                         int32_t cols, int32_t k,
                                                         int32_t* __restrict__ out) {
   __shared__ uint32_t hist[256];
-  __shared__ uint64_t s_prefix;
+  __shared__ uint64_t s_prefix, s_ref;
+  __shared__ uint64_t s_or[16];
   __shared__ int s_kleft, s_done;
   __shared__ int wsum[16];
   const uint64_t* keys = (const uint64_t*)scores;
@@ -524,25 +525,36 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
   uint64_t kv[KPT];
 #pragma unroll
   for (int q = 0; q < KPT; ++q) kv[q] = j0 + q < cols ? keys[j0 + q] : 0ull;
-  uint64_t prefix = 0, mask = 0;
+  // Bits that every key shares need no pass: the radix passes start at the
+  // highest bit where two keys differ (OR of key ^ key 0 over all keys).
+  if (tid == 0) s_ref = keys[0];
+  __syncthreads();
+  const uint64_t ref = s_ref;
+  uint64_t dx = 0;
+#pragma unroll
+  for (int q = 0; q < KPT; ++q)
+    if (j0 + q < cols) dx |= kv[q] ^ ref;
+  for (int o = 32; o >= 1; o >>= 1) dx |= (uint64_t)__shfl_xor((long long)dx, o, 64);
+  if (lane == 0) s_or[wave] = dx;
+  __syncthreads();
+  uint64_t dall = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) dall |= s_or[w];
+  const int lead = dall ? __clzll((long long)dall) : 64;   // bits all keys share
+  uint64_t mask = lead == 0 ? 0ull : (lead == 64 ? ~0ull : ~0ull << (64 - lead));
+  uint64_t prefix = ref & mask;
   int kleft = k;
   bool done = false;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
+  // 8-bit digits from the first differing bit down; the last pass may
+  // overlap bits already fixed by the prefix (equal on every key it counts)
+  for (int shift = 64 - lead - 8; lead < 64; shift -= 8) {
+    const int sh = shift < 0 ? 0 : shift;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
       const bool valid = j0 + q < cols && (kv[q] & mask) == prefix;
-      const uint32_t digit = (uint32_t)(kv[q] >> shift) & 255u;
-      uint64_t pending = __ballot(valid);
-      while (pending) {
-        const int leader = __ffsll((unsigned long long)pending) - 1;
-        const uint32_t d0 = (uint32_t)__shfl((int)digit, leader, 64);
-        const uint64_t same = __ballot(valid && digit == d0) & pending;
-        if (lane == leader) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
-        pending &= ~same;
-      }
+      if (valid) atomicAdd(&hist[(uint32_t)(kv[q] >> sh) & 255u], 1u);
     }
     __syncthreads();
     if (wave == 0) {
@@ -563,7 +575,7 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (cum < (uint32_t)kleft && cum + c[q] >= (uint32_t)kleft) {
-          s_prefix = prefix | ((uint64_t)(255 - 4 * lane - q) << shift);
+          s_prefix = prefix | ((uint64_t)(255 - 4 * lane - q) << sh);
           s_kleft = kleft - (int)cum;
           s_done = (cum + c[q] == (uint32_t)kleft) ? 1 : 0;   // the whole bin is taken
         }
@@ -573,9 +585,9 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
     __syncthreads();
     prefix = s_prefix;
     kleft = s_kleft;
-    mask |= 0xffull << shift;
+    mask |= 0xffull << sh;
     done = s_done != 0;
-    if (done) break;
+    if (done || sh == 0) break;
   }
   // keys whose top bits exceed the boundary prefix are all taken; keys on it
   // are all taken (done) or the first kleft of them by channel index
