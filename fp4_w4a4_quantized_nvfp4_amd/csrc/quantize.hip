@@ -182,7 +182,6 @@ __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
   __syncthreads();
   const float inv6st = 1.0f / (6.0f * st);
   const double st6 = 6.0 * (double)st;
-  const double st64 = (double)st;
 
   double acc[CPL];
 #pragma unroll
@@ -300,9 +299,15 @@ __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
           const uint32_t sh = 4u * (uint32_t)nib;
           const uint32_t ml = (wq >> sh) & 7u, mh = ((wq ^ dq) >> sh) & 7u;
           const uint32_t mlow = ml < mh ? ml : mh;
-          const double ax = (double)fabsf(lane_x<CPL>(cur[u], 8 * q + nib));
-          const double t = (double)(e2m1_mid_above(mlow) * s) * st64;
-          const bool up = ax > t || (ax == t && ((mlow + 1u) & 1u) == 0u);
+          // |x| against the midpoint t = (mid s) s_t, exactly in fp32: t = p + e
+          // with p = RN(ms s_t) and e = its rounding error (exact: ms has at
+          // most 9 significant bits and no product here is subnormal), and
+          // |x| - p is exact (|x| lies within a factor 1 +- 2^-19 of t)
+          const float ax = fabsf(lane_x<CPL>(cur[u], 8 * q + nib));
+          const float ms = e2m1_mid_above(mlow) * s;
+          const float pt = ms * st, et = fmaf(ms, st, -pt);
+          const float dt = ax - pt;
+          const bool up = dt > et || (dt == et && ((mlow + 1u) & 1u) == 0u);
           const uint32_t nw = (wq & ~(7u << sh)) | ((up ? mlow + 1u : mlow) << sh);
           const uint32_t nd = dq & ~(15u << sh);
           if constexpr (NW == 2) {
