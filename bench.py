@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 # HBM bytes per launch of the dense GEMM kernel from rocprofv3 --pmc FETCH_SIZE /
 # WRITE_SIZE (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives
 # (fetch x 2.00, write x 1.00); valid only for the kernel source it was taken on
-TRAFFIC = {"gemm_src_sha256": "df1566cba88669cdb1562253075e7e96a35223c4a5c3122990ff7ef7f1d79be9",
-           "fetch_kib": 242227.4, "fetch_scale": 2.0, "write_kib": 265216.0, "write_scale": 1.0}
+TRAFFIC = {"gemm_src_sha256": "7a4ec20202c18badcbdca739a3fe0b17e9db517a1014a2a6fe6bcc3eff7362a3",
+           "fetch_kib": 242165.1, "fetch_scale": 2.0, "write_kib": 265216.0, "write_scale": 1.0}
 
 
 def _args():

@@ -271,33 +271,32 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
   const size_t rac_bytes = align256((size_t)M * kp * 2) + align256((size_t)N * kp * 2);
   // the dense 256 x 256 kernel reads block scales as tiled fp16 records when
   // the workspace has room for them
+  uint8_t* ta = nullptr;
+  uint8_t* tw = nullptr;
   if (!mx && K % 128 == 0 && M >= 512 && N >= 512 && workspace &&
       ((uintptr_t)workspace & 15u) == 0 &&
       workspace_bytes >= rac_bytes + scale_tiles_bytes(M, N, K)) {
-    uint8_t* ta = (uint8_t*)workspace + rac_bytes;
-    uint8_t* tw = ta + align256((size_t)tile_rows_pad(M) * (size_t)(K / 128) * 16);
-    hipError_t e = launch_scale_tile(a_scales, M, (int32_t)K, tile_rows_pad(M), ta, S(stream));
-    if (e == hipSuccess)
-      e = launch_scale_tile(w_scales, N, (int32_t)K, tile_rows_pad(N), tw, S(stream));
-    if (e != hipSuccess) return hip_status(e, "rac_gemm (scale records)");
+    ta = (uint8_t*)workspace + rac_bytes;
+    tw = ta + align256((size_t)tile_rows_pad(M) * (size_t)(K / 128) * 16);
     g.a_scales_t = ta;
     g.w_scales_t = tw;
     g.a_rows_pad = tile_rows_pad(M);
     g.w_rows_pad = tile_rows_pad(N);
   }
+  uint16_t* R = nullptr;
+  uint16_t* W_S = nullptr;
   if (k > 0) {
-    uint16_t* R = (uint16_t*)workspace;
-    uint16_t* W_S = (uint16_t*)((uint8_t*)workspace + align256((size_t)M * kp * 2));
-    hipError_t e = launch_residual_gather(mx, x, M, K, a_codes, a_scales, a_tensor_scale,
-                                          chan_set, k, R, kp, S(stream));
-    if (e != hipSuccess) return hip_status(e, "rac_gemm (residual gather)");
-    e = launch_wsel_gather(w_hi_t, 1, K, N, chan_set, k, kp, W_S, S(stream));
-    if (e != hipSuccess) return hip_status(e, "rac_gemm (weight gather)");
+    R = (uint16_t*)workspace;
+    W_S = (uint16_t*)((uint8_t*)workspace + align256((size_t)M * kp * 2));
     g.r_res = R;
     g.ld_r = kp;
     g.w_sel = W_S;
     g.kp = kp;
   }
+  hipError_t e = launch_rac_prep(mx, x, M, N, (int32_t)K, a_codes, a_scales, a_tensor_scale,
+                                 w_scales, w_hi_t, chan_set, k, kp, R, W_S, ta, tw,
+                                 tile_rows_pad(M), tile_rows_pad(N), S(stream));
+  if (e != hipSuccess) return hip_status(e, "rac_gemm (operand preparation)");
   return hip_status(launch_w4a4_gemm(g, 0, S(stream)), "rac_gemm");
 }
 

@@ -19,6 +19,7 @@
 #include <type_traits>
 
 #include "q4_internal.h"
+#include "q4_prep.h"
 
 namespace q4 {
 namespace {
@@ -42,17 +43,6 @@ __device__ __forceinline__ int swz(int row, int piece) {
 // consecutive rows reading the same dword hit distinct banks
 __device__ __forceinline__ int swz_sc(int row, int d) {
   return row * 16 + ((d ^ ((row >> 3) & 3)) << 2);
-}
-
-// the four dwords of a 16-byte scale record in swizzled order for row `row`
-__device__ __forceinline__ uint4 swz_sc_rec(uint4 v, int row) {
-  const int q = (row >> 3) & 3;
-  uint4 r;
-  r.x = q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
-  r.y = q == 0 ? v.y : (q == 1 ? v.x : (q == 2 ? v.w : v.z));
-  r.z = q == 0 ? v.z : (q == 1 ? v.w : (q == 2 ? v.x : v.y));
-  r.w = q == 0 ? v.w : (q == 1 ? v.z : (q == 2 ? v.y : v.x));
-  return r;
 }
 
 // E4M3 code -> fp16 bits (exact: 4 significant bits, 2^-9 .. 448)
@@ -1119,29 +1109,12 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
                  : launch_t<false, false, false>(g, max_mtiles, stream);
 }
 
-// Tiled scale records for the 256 x 256 kernel: record (c, r) = the eight
-// block scales of row r in K-chunk c (128 channels) as fp16 (exact, E4M3
-// subnormals included), dwords placed so that dword d sits at d ^ ((r / 8) % 4);
-// layout [K / 128][rows_pad][16 B], rows past `rows` zero.
+// tiled fp16 scale records for the 256 x 256 kernel (body in q4_prep.h)
 __global__ __launch_bounds__(256) void scale_tile_kernel(const uint8_t* __restrict__ sc,
                                                          int64_t rows, int32_t K,
                                                          int64_t rows_pad,
                                                          uint4* __restrict__ out) {
-  const int64_t total = (int64_t)(K / 128) * rows_pad;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * 256) {
-    const int64_t c = i / rows_pad, r = i - c * rows_pad;
-    uint2 raw = make_uint2(0, 0);
-    if (r < rows) raw = *(const uint2*)(sc + r * (K / 16) + 8 * c);
-    const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
-    auto cvt2 = [&](uint32_t w, uint32_t sel) {
-      const uint32_t d = __builtin_amdgcn_perm(0u, w, sel) << 7;
-      return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d) * k256);
-    };
-    const uint4 rec = make_uint4(cvt2(raw.x, 0x0c010c00u), cvt2(raw.x, 0x0c030c02u),
-                                 cvt2(raw.y, 0x0c010c00u), cvt2(raw.y, 0x0c030c02u));
-    out[i] = swz_sc_rec(rec, (int)(r & 255));
-  }
+  scale_tile_part(sc, rows, K, rows_pad, out, blockIdx.x, gridDim.x);
 }
 
 hipError_t launch_scale_tile(const uint8_t* scales, int64_t rows, int32_t K, int64_t rows_pad,

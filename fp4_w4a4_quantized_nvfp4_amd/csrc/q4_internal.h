@@ -73,6 +73,14 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
 hipError_t launch_scale_tile(const uint8_t* scales, int64_t rows, int32_t K, int64_t rows_pad,
                              uint8_t* out, hipStream_t stream);
 inline int64_t tile_rows_pad(int64_t rows) { return (rows + 255) / 256 * 256; }
+// R and W_S of a dense RAC GEMM (when k > 0 and R, W_S are given) and the
+// scale records of both operands (NVFP4, when a_tiles and w_tiles are given)
+// in one launch
+hipError_t launch_rac_prep(bool mx, const uint16_t* x, int64_t M, int64_t N, int32_t K,
+                           const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                           const uint8_t* w_scales, const uint16_t* w_hi_t, const int32_t* idx,
+                           int32_t k, int32_t kp, uint16_t* R, uint16_t* W_S, uint8_t* a_tiles,
+                           uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream);
 
 constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 128;

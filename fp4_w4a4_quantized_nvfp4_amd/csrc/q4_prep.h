@@ -1,0 +1,144 @@
+// Operand preparation for the W4A4 + RAC GEMM (gfx950): the residual gather
+// R, the selected weight columns W_S and the tiled fp16 scale records, as
+// device bodies that take their block index, so that the stand-alone kernels
+// and the one-launch preparation of a dense GEMM share them.
+//
+// QUADS (arXiv 2607.15810) section 3.3: Eq. 21 (residual of the selected
+// channels, multiplied by the matching high-precision weight columns),
+// Eq. 24 (the selected channel set S).
+#pragma once
+
+#include "q4_device.h"
+
+namespace q4 {
+
+// the four dwords of a 16-byte scale record in swizzled order for row `row`:
+// dword d sits at d ^ ((row / 8) % 4), so that 32 consecutive rows reading the
+// same dword hit distinct LDS banks
+__device__ __forceinline__ uint4 swz_sc_rec(uint4 v, int row) {
+  const int q = (row >> 3) & 3;
+  uint4 r;
+  r.x = q == 0 ? v.x : (q == 1 ? v.y : (q == 2 ? v.z : v.w));
+  r.y = q == 0 ? v.y : (q == 1 ? v.x : (q == 2 ? v.w : v.z));
+  r.z = q == 0 ? v.z : (q == 1 ? v.w : (q == 2 ? v.x : v.y));
+  r.w = q == 0 ? v.w : (q == 1 ? v.z : (q == 2 ? v.y : v.x));
+  return r;
+}
+
+// R[i][t] = bf16(RN32(x[i][S_t] - dequant)) for t < k, 0 for k <= t < ld_r.
+// One thread per (row, 8 consecutive t): all loads of the eight are issued
+// before any is used.  Block `blk` of `nblk` (grid-stride).
+template <bool MX>
+__device__ __forceinline__ void residual_gather_part(
+    const uint16_t* __restrict__ x, int64_t rows, int32_t cols, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ ts,
+    const int32_t* __restrict__ idx, int32_t k, uint16_t* __restrict__ R, int64_t ld_r,
+    int64_t blk, int64_t nblk) {
+  const int64_t n8 = (ld_r + 7) / 8;
+  const int64_t total = rows * n8;
+  const float st = MX ? 1.0f : ts[0];
+  for (int64_t g = blk * 256 + threadIdx.x; g < total; g += nblk * 256) {
+    const int64_t i = g / n8;
+    const int t0 = (int)(g - i * n8) * 8;
+    int j[8];
+    uint16_t xv[8];
+    uint8_t cb[8], sb[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      int c = t0 + q < k ? idx[t0 + q] : 0;
+      j[q] = c < 0 ? 0 : (c >= cols ? cols - 1 : c);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      xv[q] = x[i * cols + j[q]];
+      cb[q] = codes[i * (cols / 2) + (j[q] >> 1)];
+      sb[q] = MX ? scales[i * (cols / 32) + (j[q] >> 5)] : scales[i * (cols / 16) + (j[q] >> 4)];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int t = t0 + q;
+      if (t >= ld_r) break;
+      uint32_t out = 0;
+      if (t < k) {
+        const uint32_t nib = (cb[q] >> ((j[q] & 1) * 4)) & 15u;
+        float s;
+        if constexpr (MX) {
+          const int e = (int)sb[q] - 127;
+          s = e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : 0x1p-127f;
+        } else {
+          s = e4m3_to_f32(sb[q]);
+        }
+        out = f32_to_bf16_rne(fmaf(-(e2m1_value(nib) * s), st, bf16_to_f32(xv[q])));
+      }
+      R[i * ld_r + t] = (uint16_t)out;
+    }
+  }
+}
+
+// W_S[b][j][t] = w_hi_t[b][S_t][j] for t < k, 0 for k <= t < kp: a transposing
+// gather through a 64 x 64 LDS tile (the selected rows are contiguous in j).
+// Tile (bx, by) of matrix b covers j in [64 bx, 64 bx + 64), t in [64 by, 64 by + 64).
+__device__ __forceinline__ void wsel_gather_part(const uint16_t* __restrict__ w_hi_t, int64_t K,
+                                                 int64_t N, const int32_t* __restrict__ idx,
+                                                 int32_t k, int32_t kp, uint16_t* __restrict__ ws,
+                                                 int64_t b, int64_t bx, int by,
+                                                 uint16_t (*tile)[66]) {
+  const int64_t j0 = bx * 64;
+  const int t0 = by * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const uint16_t* src = w_hi_t + b * K * N;
+  int64_t rowoff[16];
+  bool ok[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int t = t0 + ty + 4 * q;
+    int c = t < k ? idx[t] : 0;
+    c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
+    rowoff[q] = (int64_t)c * N;
+    ok[q] = t < k && j0 + tx < N;
+  }
+  uint16_t v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v[q] = ok[q] ? src[rowoff[q] + j0 + tx] : (uint16_t)0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) tile[ty + 4 * q][tx] = v[q];
+  __syncthreads();
+  uint16_t* dst = ws + b * N * kp;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int64_t j = j0 + ty + 4 * q;
+    const int t = t0 + tx;
+    if (j < N && t < kp) dst[j * kp + t] = tile[tx][ty + 4 * q];
+  }
+}
+
+// Tiled fp16 scale records of an NVFP4 operand: record (c, r) holds the eight
+// E4M3 block scales of row r over K columns [128 c, 128 c + 128) as fp16
+// (exact, subnormal scales included), in swz_sc_rec order for r % 256;
+// layout [K / 128][rows_pad][16 B], rows past `rows` zero.  Block `blk` of
+// `nblk` (grid-stride).
+__device__ __forceinline__ void scale_tile_part(const uint8_t* __restrict__ sc, int64_t rows,
+                                                int32_t K, int64_t rows_pad,
+                                                uint4* __restrict__ out, int64_t blk,
+                                                int64_t nblk) {
+  const int64_t total = (int64_t)(K / 128) * rows_pad;
+  for (int64_t i = blk * 256 + threadIdx.x; i < total; i += nblk * 256) {
+    const int64_t c = i / rows_pad, r = i - c * rows_pad;
+    uint2 raw = make_uint2(0, 0);
+    if (r < rows) raw = *(const uint2*)(sc + r * (K / 16) + 8 * c);
+    const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
+    // the E4M3 byte shifted left by 7 is an fp16 of value 2^-8 times the
+    // scale; the multiply by 256 is exact
+    const uint32_t d0 = __builtin_amdgcn_perm(0u, raw.x, 0x0c010c00u) << 7;
+    const uint32_t d1 = __builtin_amdgcn_perm(0u, raw.x, 0x0c030c02u) << 7;
+    const uint32_t d2 = __builtin_amdgcn_perm(0u, raw.y, 0x0c010c00u) << 7;
+    const uint32_t d3 = __builtin_amdgcn_perm(0u, raw.y, 0x0c030c02u) << 7;
+    const uint4 rec = make_uint4(__builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d0) * k256),
+                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d1) * k256),
+                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d2) * k256),
+                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d3) * k256));
+    out[i] = swz_sc_rec(rec, (int)(r & 255));
+  }
+}
+
+}  // namespace q4

@@ -8,6 +8,7 @@
 // kernel; here one pass over x emits codes, block scales and fp64 per-channel
 // partial sums of squared residuals.
 #include "q4_internal.h"
+#include "q4_prep.h"
 
 namespace q4 {
 
@@ -619,92 +620,24 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
 }
 
 // ====================================================================== gathers
-// R[i][t] = bf16(RN32(x[i][S_t] - dequant)) for t < k, 0 for k <= t < ld_r.
-// One thread per (row, 8 consecutive t): all loads of the eight are issued
-// before any is used.
+// residual gather (body in q4_prep.h)
 template <bool MX>
 __global__ __launch_bounds__(256) void residual_gather_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int32_t cols, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ ts,
     const int32_t* __restrict__ idx, int32_t k, uint16_t* __restrict__ R, int64_t ld_r) {
-  const int64_t n8 = (ld_r + 7) / 8;
-  const int64_t total = rows * n8;
-  const float st = MX ? 1.0f : ts[0];
-  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < total;
-       g += (int64_t)gridDim.x * 256) {
-    const int64_t i = g / n8;
-    const int t0 = (int)(g - i * n8) * 8;
-    int j[8];
-    uint16_t xv[8];
-    uint8_t cb[8], sb[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      int c = t0 + q < k ? idx[t0 + q] : 0;
-      j[q] = c < 0 ? 0 : (c >= cols ? cols - 1 : c);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      xv[q] = x[i * cols + j[q]];
-      cb[q] = codes[i * (cols / 2) + (j[q] >> 1)];
-      sb[q] = MX ? scales[i * (cols / 32) + (j[q] >> 5)] : scales[i * (cols / 16) + (j[q] >> 4)];
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int t = t0 + q;
-      if (t >= ld_r) break;
-      uint32_t out = 0;
-      if (t < k) {
-        const uint32_t nib = (cb[q] >> ((j[q] & 1) * 4)) & 15u;
-        float s;
-        if constexpr (MX) {
-          const int e = (int)sb[q] - 127;
-          s = e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : 0x1p-127f;
-        } else {
-          s = e4m3_to_f32(sb[q]);
-        }
-        out = f32_to_bf16_rne(fmaf(-(e2m1_value(nib) * s), st, bf16_to_f32(xv[q])));
-      }
-      R[i * ld_r + t] = (uint16_t)out;
-    }
-  }
+  residual_gather_part<MX>(x, rows, cols, codes, scales, ts, idx, k, R, ld_r, blockIdx.x,
+                           gridDim.x);
 }
 
-// W_S[b][j][t] = w_hi_t[b][S_t][j] for t < k, 0 for k <= t < kp (a transposing
-// gather through a 64 x 64 LDS tile; the selected rows are contiguous in j).
+// selected weight columns, one 64 x 64 tile per workgroup (body in q4_prep.h)
 __global__ __launch_bounds__(256) void wsel_gather_kernel(const uint16_t* __restrict__ w_hi_t,
                                                           int64_t K, int64_t N,
                                                           const int32_t* __restrict__ idx,
                                                           int32_t k, int32_t kp,
                                                           uint16_t* __restrict__ ws) {
   __shared__ uint16_t tile[64][66];
-  const int64_t b = blockIdx.z;
-  const int64_t j0 = (int64_t)blockIdx.x * 64;
-  const int t0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const uint16_t* src = w_hi_t + b * K * N;
-  int64_t rowoff[16];
-  bool ok[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int t = t0 + ty + 4 * q;
-    int c = t < k ? idx[t] : 0;
-    c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
-    rowoff[q] = (int64_t)c * N;
-    ok[q] = t < k && j0 + tx < N;
-  }
-  uint16_t v[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) v[q] = ok[q] ? src[rowoff[q] + j0 + tx] : (uint16_t)0;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) tile[ty + 4 * q][tx] = v[q];
-  __syncthreads();
-  uint16_t* dst = ws + b * N * kp;
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int64_t j = j0 + ty + 4 * q;
-    const int t = t0 + tx;
-    if (j < N && t < kp) dst[j * kp + t] = tile[tx][ty + 4 * q];
-  }
+  wsel_gather_part(w_hi_t, K, N, idx, k, kp, ws, blockIdx.z, blockIdx.x, blockIdx.y, tile);
 }
 
 // out[b][c][r] = in[b][r][c]
