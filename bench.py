@@ -269,7 +269,7 @@ def main():
     iq = torch.empty((kq,), dtype=torch.int32, device=dev)
     wsq_b = L.q4_quantize_workspace_size(Mq, Kq, 0)
     wsq = torch.empty((wsq_b,), dtype=torch.uint8, device=dev)
-    tin = torch.tensor([0.05], dtype=torch.float32, device=dev)
+    tin = torch.empty((1,), dtype=torch.float32, device=dev)
 
     def qstep(i, supplied=False):
         q4._check(L.nvfp4_quantize(xq[i % 2].data_ptr(), Mq, Kq, tin.data_ptr() if supplied else None,
@@ -289,6 +289,9 @@ def main():
         return e0.elapsed_time(e1) / a.quant_iters
 
     tq_ms = time_q(False)
+    # supplied s_t: the value the in-call pass computed for this tensor (a
+    # scale kept from an earlier step, as delayed scaling supplies it)
+    tin.copy_(tq)
     tq1_ms = time_q(True)
     q_bytes = Mq * Kq * (2 + 0.5 + 1.0 / 16)        # read x, write codes + scales
     q_gbs = q_bytes / (tq_ms * 1e-3) / 1e9

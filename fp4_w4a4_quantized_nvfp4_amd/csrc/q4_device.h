@@ -16,6 +16,7 @@ typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef float f32x16v __attribute__((ext_vector_type(16)));
 typedef int i32x8v __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
 constexpr int kScoreTileRows = 32;   // rows summed in order into one tile sum
 constexpr int kScoreGroupTiles = 8;  // tile sums added in order into one group sum

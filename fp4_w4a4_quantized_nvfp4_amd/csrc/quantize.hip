@@ -26,25 +26,29 @@ __device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t w) {
 // Per-workgroup max |x| as a bf16 bit pattern (non-negative bf16 order is
 // integer order).  Each workgroup writes its own slot; the quantize kernel
 // reduces the slots, so no atomics are involved and the result is exact.
+// The tensor is walked front to back in segments of 32 KB (eight 16-byte
+// loads per thread in flight), workgroup b taking segments b, b + grid, ...:
+// each workgroup reads contiguous memory, and the data read last (the end of
+// the tensor) is what the quantize pass, walking groups in reverse, reads
+// first while it is still in the last-level cache.
 constexpr int kAmaxBlocks = 1024;
+constexpr int kAmaxUnroll = 8;
+constexpr int64_t kAmaxSeg = 256 * kAmaxUnroll;   // uint4 per segment
 
 __global__ __launch_bounds__(256) void amax_kernel(const uint4* __restrict__ x, int64_t n16,
                                                    uint32_t* __restrict__ out) {
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 7 * stride < n16; i += 8 * stride) {
-    uint4 v[8];
+  const int64_t nseg = (n16 + kAmaxSeg - 1) / kAmaxSeg;
+  for (int64_t sg = blockIdx.x; sg < nseg; sg += gridDim.x) {
+    const int64_t base = sg * kAmaxSeg + threadIdx.x;
+    uint4 v[kAmaxUnroll];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = x[i + u * stride];
+    for (int u = 0; u < kAmaxUnroll; ++u)
+      v[u] = base + u * 256 < n16 ? x[base + u * 256] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < kAmaxUnroll; ++u)
       m = max(m, max(max(absmax_bf16x2(v[u].x), absmax_bf16x2(v[u].y)),
                      max(absmax_bf16x2(v[u].z), absmax_bf16x2(v[u].w))));
-  }
-  for (; i < n16; i += stride) {
-    uint4 v = x[i];
-    m = max(m, max(max(absmax_bf16x2(v.x), absmax_bf16x2(v.y)), max(absmax_bf16x2(v.z), absmax_bf16x2(v.w))));
   }
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
   __shared__ uint32_t red[4];
@@ -70,9 +74,42 @@ struct QuantKArgs {
   int32_t reverse;      // process groups last-to-first (reuse of the last-level cache)
 };
 
-// tensor scale of the launch; every thread of the workgroup must call it
-__device__ float nvfp4_tensor_scale_dev(const QuantKArgs& a, uint32_t* red) {
-  if (a.ts_in) return a.ts_in[0];
+// How the codes of elements whose x / (s s_t) lies within 2^-20 of an E2M1
+// rounding midpoint are decided (uniform per launch).
+//
+// With s_t = RN32(a / 2688) taken from the tensor's bf16 amax a, every such
+// element is an exact tie of rationals, x * 2688 = mid * a * s: x (8
+// significant bits) * 21 and mid * a * s (3 + 8 + 4 bits) differ by at least
+// one part in 2^15 otherwise, far outside the 2^-20 window.  For an exact tie
+// |x| - mid * s * s_t has the sign of a / 2688 - s_t, the same for every
+// element of the launch: the tie rounds up in magnitude when s_t was rounded
+// down, down when it was rounded up, and to the even code when the quotient
+// was exact.  MXFP4 (s a power of two, no s_t) only has exact ties: even.
+// A supplied s_t of the same form, RN32(a / 2688) for some bf16 a (a scale
+// kept from an earlier amax), has the same structure; any other supplied s_t
+// has none, and each element near a midpoint is then settled exactly.
+enum TieMode : int { kTieUp = 0, kTieDown = 1, kTieEven = 2, kTieExact = 3 };
+
+// tie mode of s_t against the bf16 amax a it is the rounded quotient of
+__device__ __forceinline__ int tie_mode_of(float st, float a) {
+  const double back = (double)st * 2688.0;   // exact: 24 + 5 significant bits
+  return back < (double)a ? kTieUp : (back > (double)a ? kTieDown : kTieEven);
+}
+
+// tensor scale of the launch and its tie mode; every thread of the
+// workgroup must call it
+__device__ float nvfp4_tensor_scale_dev(const QuantKArgs& a, uint32_t* red, int* tie_mode) {
+  if (a.ts_in) {
+    const float st = a.ts_in[0];
+    *tie_mode = kTieExact;
+    if (st > 0.0f && st <= 0x1p100f && st >= 0x1p-100f) {
+      // the bf16 nearest to s_t * 2688 is the only amax s_t can come from
+      const uint32_t pb = __float_as_uint((float)((double)st * 2688.0));
+      const float ac = __uint_as_float((pb + 0x7fffu + ((pb >> 16) & 1u)) & 0xffff0000u);
+      if ((float)((double)ac / 2688.0) == st) *tie_mode = tie_mode_of(st, ac);
+    }
+    return st;
+  }
   uint32_t m = 0;
   for (int i = threadIdx.x; i < a.namax; i += blockDim.x) m = max(m, a.amax[i]);
   for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
@@ -84,7 +121,9 @@ __device__ float nvfp4_tensor_scale_dev(const QuantKArgs& a, uint32_t* red) {
   // RN32(amax / 2688): the fp64 quotient is never an fp32 midpoint
   // (2688 = 21 * 2^7, amax has 8 significant bits), so one more rounding to
   // fp32 gives the correctly rounded quotient.
-  return am == 0.0f ? 1.0f : (float)((double)am / 2688.0);
+  const float st = am == 0.0f ? 1.0f : (float)((double)am / 2688.0);
+  *tie_mode = am == 0.0f ? kTieEven : tie_mode_of(st, am);
+  return st;
 }
 
 // lane l <- lane l^1 / l^2 inside a quad (DPP quad permutes)
@@ -134,16 +173,17 @@ __device__ uint32_t e4m3_mantissa_entry(int ma, double Dp) {
 // many x / (s s_t) fall within 2^-24 of a midpoint); each such element is
 // settled by comparing |x| with midpoint * s * s_t, exact in fp64, one element
 // per lane per round, all lanes of the wave at once.
+// element pos of a lane's row, from its raw words v0 (channels 0-7) and v1
+// (channels 8-15; ignored when CPL = 8), by selects only
 template <int CPL>
-__device__ __forceinline__ float lane_x(const uint4* v, int pos) {
+__device__ __forceinline__ float lane_x(uint4 v0, uint4 v1, int pos) {
   const int d = pos >> 1;
-  uint4 a = v[0];
-  if constexpr (CPL == 16) {
-    if (d & 4) a = v[1];
-  }
-  const uint32_t lo2 = (d & 2) ? a.z : a.x, hi2 = (d & 2) ? a.w : a.y;
-  const uint32_t w = (d & 1) ? hi2 : lo2;
-  return (pos & 1) ? bf16_hi(w) : bf16_lo(w);
+  const bool hi4 = CPL == 16 && (d & 4);
+  const uint32_t x = hi4 ? v1.x : v0.x, y = hi4 ? v1.y : v0.y;
+  const uint32_t z = hi4 ? v1.z : v0.z, w = hi4 ? v1.w : v0.w;
+  const uint32_t lo2 = (d & 2) ? z : x, hi2 = (d & 2) ? w : y;
+  const uint32_t wd = (d & 1) ? hi2 : lo2;
+  return (pos & 1) ? bf16_hi(wd) : bf16_lo(wd);
 }
 
 // 4 * (E2M1 midpoint above magnitude m), m = 0..6: 1 3 5 7 10 14 20
@@ -155,12 +195,14 @@ __device__ __forceinline__ float e2m1_mid_above(uint32_t m) {
 template <bool MX, int CPL>
 __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
   constexpr int NW = CPL / 8;              // code words (8 nibbles) per lane per row
-  constexpr int U = 32 / CPL;              // rows loaded ahead
+  constexpr int U = 64 / CPL;              // rows in flight per lane
   constexpr int STRIP = 64 * CPL;
   __shared__ uint8_t tab[128];
   __shared__ uint32_t red[16];
   __shared__ double part[kScoreGroupTiles][64][CPL + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform per wave: keep it (and the row range derived from
+  // it) in scalar registers, so the row loop is a scalar loop
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t wg = blockIdx.x;
   const int64_t nwg = a.ngroups * a.nstrips;
   if (a.reverse) wg = nwg - 1 - wg;
@@ -172,8 +214,9 @@ __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
 
   float st = 1.0f;
   int eDp = 0;
+  int tie_mode = kTieEven;
   if constexpr (!MX) {
-    st = nvfp4_tensor_scale_dev(a, red);
+    st = nvfp4_tensor_scale_dev(a, red, &tie_mode);
     if (blockIdx.x == 0 && threadIdx.x == 0 && a.ts_out) a.ts_out[0] = st;
     int eD;
     const double Dm = frexp(6.0 * (double)st, &eD);   // 6 s_t = Dm 2^eD, Dm in [0.5, 1)
@@ -190,103 +233,152 @@ __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
 
   const int64_t r0 = group * (kScoreTileRows * kScoreGroupTiles) + wave * kScoreTileRows;
   const int nr = (int)max((int64_t)0, min((int64_t)kScoreTileRows, a.rows - r0));
-  const uint16_t* xp = a.x + (nr > 0 ? r0 : 0) * cols + (active ? col0 : 0);
   const int64_t cstride = cols / 2, sstride = MX ? cols / 32 : cols / 16;
 
-  uint4 cur[U][NW], nxt[U][NW];
+  // x, codes and scales of this wave's tile through buffer resources based at
+  // the tile's first row, sized to its nr rows: the row goes into the scalar
+  // offset, the lane's channels into one per-lane offset.  Anything outside
+  // the range (rows past the tile, lanes past the last channel) loads zeros
+  // and stores nothing, so no access needs a branch.
+  auto rsrc = [](const void* base, int64_t bytes) __attribute__((always_inline)) {
+    const uint64_t p = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+    const uint32_t n = bytes <= 0 ? 0u : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0,
+                                             __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
+  };
+  const int64_t rb = nr > 0 ? r0 : 0;
+  const __amdgpu_buffer_rsrc_t x_rs = rsrc(a.x + rb * cols, (int64_t)nr * cols * 2);
+  const __amdgpu_buffer_rsrc_t c_rs = rsrc(a.codes + rb * cstride, (int64_t)nr * cstride);
+  const __amdgpu_buffer_rsrc_t s_rs = rsrc(a.scales + rb * sstride, (int64_t)nr * sstride);
+  constexpr uint32_t kOut = 0x80000000u;   // a per-lane offset past every range
+  const uint32_t x_voff = active ? (uint32_t)col0 * 2u : kOut;
+  const uint32_t c_voff = active ? (uint32_t)(col0 >> 1) : kOut;
+  bool writes_scale;
+  if constexpr (MX) writes_scale = (lane & (32 / CPL - 1)) == 0;
+  else writes_scale = CPL == 16 || (lane & 1) == 0;
+  const uint32_t s_voff = (active && writes_scale) ? (uint32_t)(col0 >> (MX ? 5 : 4)) : kOut;
+  const int x_rowb = cols * 2;
+
+  // ring of U rows in flight per lane: slot u holds row rr + u and is
+  // refilled with row rr + u + U once that row is done, so the loop carries no
+  // register copies
+  uint4 buf[U][NW];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u) {
+    const int soff = u * x_rowb;
 #pragma unroll
     for (int q = 0; q < NW; ++q)
-      cur[u][q] = (active && u < nr) ? *(const uint4*)(xp + (int64_t)u * cols + 8 * q)
-                                     : make_uint4(0, 0, 0, 0);
+      buf[u][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, x_voff + 16 * q, soff, 0));
+    // keep the slots' issue order (slot 0 oldest), the order the loop refills
+    // them in, so the wait before each row covers that row's loads only
+    __builtin_amdgcn_sched_barrier(0);
+  }
 
-  for (int rr = 0; rr < nr; rr += U) {
+  // one row: codes, block scale, residual statistics (w: the row's raw words)
+  auto do_row = [&](const uint4* w, int64_t row) __attribute__((always_inline)) {
+    float xf[CPL];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int q = 0; q < NW; ++q) {
+      xf[8 * q + 0] = bf16_lo(w[q].x); xf[8 * q + 1] = bf16_hi(w[q].x);
+      xf[8 * q + 2] = bf16_lo(w[q].y); xf[8 * q + 3] = bf16_hi(w[q].y);
+      xf[8 * q + 4] = bf16_lo(w[q].z); xf[8 * q + 5] = bf16_hi(w[q].z);
+      xf[8 * q + 6] = bf16_lo(w[q].w); xf[8 * q + 7] = bf16_hi(w[q].w);
+    }
+    float m = 0.0f;
 #pragma unroll
-      for (int q = 0; q < NW; ++q)
-        nxt[u][q] = (active && rr + U + u < nr)
-                        ? *(const uint4*)(xp + (int64_t)(rr + U + u) * cols + 8 * q)
-                        : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < CPL; ++i) m = fmaxf(m, fabsf(xf[i]));
+    if constexpr (!MX && CPL == 8) m = fmaxf(m, dpp_quad_xor1(m));   // 16-block = lane pair
+    if constexpr (MX) {
+      m = fmaxf(m, dpp_quad_xor1(m));                                // 32-block
+      if constexpr (CPL == 8) m = fmaxf(m, dpp_quad_xor2(m));
+    }
+    uint32_t sc;
+    float s;
+    bool ok;
+    if constexpr (MX) {
+      // floor(log2 m) - 2 clamped to [-127, 127]: exponent field - 129
+      const int ef = (int)(__float_as_uint(m) >> 23);
+      const int e = max(ef - 129, -127);
+      sc = (uint32_t)(e + 127);
+      s = e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : 0x1p-127f;
+      ok = true;
+    } else {
+      const uint32_t ab = __float_as_uint(m);
+      const int ea = (int)(ab >> 23);
+      const uint32_t ent = tab[(ab >> 16) & 127u];
+      const int e = ea - 127 - eDp + (int)(ent >> 3) - 1;
+      const int ci = ((e + 7) << 3) | (int)(ent & 7u);
+      sc = (uint32_t)min(ci, 126);
+      ok = (ea != 0 && e >= -6) || ab == 0;
+      sc = ab == 0 ? 0u : sc;
+      s = sc >= 8u ? __uint_as_float((((sc >> 3) + 120u) << 23) | ((sc & 7u) << 20)) : 0.0f;
+    }
+    const float S = s * st;
+    ok = ok && (S >= 0x1p-60f || S == 0.0f);
+    const float rinv = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
+    const float rlo = rinv * (1.0f - 0x1p-20f), rhi = rinv * (1.0f + 0x1p-20f);
+    // codes of x * rhi; where the tie mode needs them, also of x * rlo (the
+    // two differ only at elements within 2^-20 of a midpoint)
+    const float r1 = tie_mode == kTieDown ? rlo : rhi;
+    uint32_t code[NW], diff[NW];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (rr + u >= nr) break;
-      const int64_t row = r0 + rr + u;
-      float xf[CPL];
+    for (int q = 0; q < NW; ++q) {
+      uint32_t c = 0;
+      const float* xq = xf + 8 * q;
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, xq[0] * r1, xq[1] * r1, 1.0f, 0);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, xq[2] * r1, xq[3] * r1, 1.0f, 1);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, xq[4] * r1, xq[5] * r1, 1.0f, 2);
+      c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, xq[6] * r1, xq[7] * r1, 1.0f, 3);
+      code[q] = c;
+      diff[q] = 0;
+    }
+    if (tie_mode >= kTieEven) {
 #pragma unroll
       for (int q = 0; q < NW; ++q) {
-        xf[8 * q + 0] = bf16_lo(cur[u][q].x); xf[8 * q + 1] = bf16_hi(cur[u][q].x);
-        xf[8 * q + 2] = bf16_lo(cur[u][q].y); xf[8 * q + 3] = bf16_hi(cur[u][q].y);
-        xf[8 * q + 4] = bf16_lo(cur[u][q].z); xf[8 * q + 5] = bf16_hi(cur[u][q].z);
-        xf[8 * q + 6] = bf16_lo(cur[u][q].w); xf[8 * q + 7] = bf16_hi(cur[u][q].w);
-      }
-      float m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) m = fmaxf(m, fabsf(xf[i]));
-      if constexpr (!MX && CPL == 8) m = fmaxf(m, dpp_quad_xor1(m));   // 16-block = lane pair
-      if constexpr (MX) {
-        m = fmaxf(m, dpp_quad_xor1(m));                                // 32-block
-        if constexpr (CPL == 8) m = fmaxf(m, dpp_quad_xor2(m));
-      }
-      uint32_t sc;
-      float s;
-      bool ok;
-      if constexpr (MX) {
-        // floor(log2 m) - 2 clamped to [-127, 127]: exponent field - 129
-        const int ef = (int)(__float_as_uint(m) >> 23);
-        const int e = max(ef - 129, -127);
-        sc = (uint32_t)(e + 127);
-        s = e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : 0x1p-127f;
-        ok = true;
-      } else {
-        const uint32_t ab = __float_as_uint(m);
-        const int ea = (int)(ab >> 23);
-        const uint32_t ent = tab[(ab >> 16) & 127u];
-        const int e = ea - 127 - eDp + (int)(ent >> 3) - 1;
-        const int ci = ((e + 7) << 3) | (int)(ent & 7u);
-        sc = (uint32_t)min(ci, 126);
-        ok = (ea != 0 && e >= -6) || ab == 0;
-        sc = ab == 0 ? 0u : sc;
-        s = sc >= 8u ? __uint_as_float((((sc >> 3) + 120u) << 23) | ((sc & 7u) << 20)) : 0.0f;
-      }
-      const float S = s * st;
-      ok = ok && (S >= 0x1p-60f || S == 0.0f);
-      const float rinv = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
-      const float rlo = rinv * (1.0f - 0x1p-20f), rhi = rinv * (1.0f + 0x1p-20f);
-      uint32_t code[NW], diff[NW];
-#pragma unroll
-      for (int q = 0; q < NW; ++q) {
-        uint32_t lo = 0, hi = 0;
+        uint32_t lo = 0;
         const float* xq = xf + 8 * q;
         lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xq[0] * rlo, xq[1] * rlo, 1.0f, 0);
         lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xq[2] * rlo, xq[3] * rlo, 1.0f, 1);
         lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xq[4] * rlo, xq[5] * rlo, 1.0f, 2);
         lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, xq[6] * rlo, xq[7] * rlo, 1.0f, 3);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xq[0] * rhi, xq[1] * rhi, 1.0f, 0);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xq[2] * rhi, xq[3] * rhi, 1.0f, 1);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xq[4] * rhi, xq[5] * rhi, 1.0f, 2);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, xq[6] * rhi, xq[7] * rhi, 1.0f, 3);
-        code[q] = lo;
-        diff[q] = lo ^ hi;
-      }
-      if (__builtin_expect(!ok, 0)) {
-        // a block scale outside the table's range or an extreme scale:
-        // decide the scale and every code exactly
-        if constexpr (!MX) {
-          sc = m == 0.0f ? 0u : e4m3_scale_code(m, inv6st, st6);
-          s = e4m3_to_f32(sc);
-        }
-#pragma unroll
-        for (int q = 0; q < NW; ++q) {
-          uint32_t c = 0;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) c |= e2m1_nibble_exact(xf[8 * q + i], s, st) << (4 * i);
-          code[q] = c;
-          diff[q] = 0;
+        if (tie_mode == kTieEven) {
+          // the two candidates of a tie are neighbouring magnitudes: keep the
+          // nibble whose magnitude is even (lo where lo's low bit is clear)
+          const uint32_t keep_lo = ((~lo) & 0x11111111u) * 15u;
+          code[q] = (lo & keep_lo) | (code[q] & ~keep_lo);
+        } else {
+          diff[q] = lo ^ code[q];
+          code[q] = lo;
         }
       }
-      // near-ties: one element per lane per round
+    }
+    if (__builtin_expect(!ok, 0)) {
+      // a block scale outside the table's range or an extreme scale:
+      // decide the scale and every code exactly
+      if constexpr (!MX) {
+        sc = m == 0.0f ? 0u : e4m3_scale_code(m, inv6st, st6);
+        s = e4m3_to_f32(sc);
+      }
+      // (rare: one element at a time from the raw words, to keep this path's
+      // registers out of the common path's budget)
+      uint32_t c[2] = {0u, 0u};
+#pragma unroll 1
+      for (int i = 0; i < CPL; ++i) {
+        const uint32_t nib = e2m1_nibble_exact(lane_x<CPL>(w[0], w[NW - 1], i), s, st);
+        const uint32_t sh = 4u * (uint32_t)(i & 7);
+        if (i < 8) c[0] |= nib << sh;
+        else c[1] |= nib << sh;
+      }
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        code[q] = c[q];
+        diff[q] = 0;
+      }
+    }
+    // near-ties under a supplied s_t: one element per lane per round
+    if (tie_mode == kTieExact) {
       uint32_t dany = diff[0];
 #pragma unroll
       for (int q = 1; q < NW; ++q) dany |= diff[q];
@@ -304,7 +396,7 @@ __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
           // with p = RN(ms s_t) and e = its rounding error (exact: ms has at
           // most 9 significant bits and no product here is subnormal), and
           // |x| - p is exact (|x| lies within a factor 1 +- 2^-19 of t)
-          const float ax = fabsf(lane_x<CPL>(cur[u], 8 * q + nib));
+          const float ax = fabsf(lane_x<CPL>(w[0], w[NW - 1], 8 * q + nib));
           const float ms = e2m1_mid_above(mlow) * s;
           const float pt = ms * st, et = fmaf(ms, st, -pt);
           const float dt = ax - pt;
@@ -322,41 +414,63 @@ __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
           for (int q2 = 1; q2 < NW; ++q2) dany |= diff[q2];
         }
       }
-      // residual r = RN32(x - c s st): c*s is exact, one fused rounding
+    }
+    // residual r = RN32(x - c s st): c*s is exact, one fused rounding
 #pragma unroll
-      for (int q = 0; q < NW; ++q) {
-        f32x2v c2[4];
-        c2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 0);
-        c2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 1);
-        c2[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 2);
-        c2[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 3);
+    for (int q = 0; q < NW; ++q) {
+      f32x2v c2[4];
+      c2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 0);
+      c2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 1);
+      c2[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 2);
+      c2[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code[q], 1.0f, 3);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int i0 = 8 * q + 2 * b;
-          const float r0v = fmaf(-(c2[b].x * s), st, xf[i0]);
-          const float r1v = fmaf(-(c2[b].y * s), st, xf[i0 + 1]);
-          const double d0 = (double)r0v, d1 = (double)r1v;
-          acc[i0] = fma(d0, d0, acc[i0]);
-          acc[i0 + 1] = fma(d1, d1, acc[i0 + 1]);
-        }
-      }
-      if (active) {
-        uint8_t* cp = a.codes + row * cstride + (col0 >> 1);
-        if constexpr (NW == 2)
-          *(uint2*)cp = make_uint2(code[0], code[1]);
-        else
-          *(uint32_t*)cp = code[0];
-        if constexpr (MX) {
-          if ((lane & (32 / CPL - 1)) == 0) a.scales[row * sstride + (col0 >> 5)] = (uint8_t)sc;
-        } else {
-          if (CPL == 16 || (lane & 1) == 0) a.scales[row * sstride + (col0 >> 4)] = (uint8_t)sc;
-        }
+      for (int b = 0; b < 4; ++b) {
+        const int i0 = 8 * q + 2 * b;
+        const float r0v = fmaf(-(c2[b].x * s), st, xf[i0]);
+        const float r1v = fmaf(-(c2[b].y * s), st, xf[i0 + 1]);
+        const double d0 = (double)r0v, d1 = (double)r1v;
+        acc[i0] = fma(d0, d0, acc[i0]);
+        acc[i0 + 1] = fma(d1, d1, acc[i0 + 1]);
       }
     }
+    // add this row into the sums here: left to itself the compiler sinks
+    // every row's accumulation to the end of the unrolled rows, keeping all
+    // their residuals live at once
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int i = 0; i < CPL; ++i) asm volatile("" : "+v"(acc[i]));
+    {
+      const int rl = (int)(row - rb);
+      if constexpr (NW == 2) {
+        const u32x2v cw = {code[0], code[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(cw, c_rs, c_voff, rl * (int)cstride, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(code[0], c_rs, c_voff, rl * (int)cstride, 0);
+      }
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sc, s_rs, s_voff, rl * (int)sstride, 0);
+    }
+  };
+
+  // full groups of U rows through the ring; the (rare) ragged rows of a
+  // tile's end one at a time
+  const int nfull = nr & ~(U - 1);
+  for (int rr = 0; rr < nfull; rr += U) {
 #pragma unroll
-      for (int q = 0; q < NW; ++q) cur[u][q] = nxt[u][q];
+    for (int u = 0; u < U; ++u) {
+      do_row(buf[u], r0 + rr + u);
+      const int soff = (rr + u + U) * x_rowb;
+#pragma unroll
+      for (int q = 0; q < NW; ++q)
+        buf[u][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, x_voff + 16 * q, soff, 0));
+      // rows one after another: interleaving them only raises register use
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  for (int r = nfull; r < nr; ++r) {
+    uint4 w[NW];
+#pragma unroll
+    for (int q = 0; q < NW; ++q)
+      w[q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, x_voff + 16 * q, r * x_rowb, 0));
+    do_row(w, r0 + r);
   }
   // tile sums -> group sum, tiles in order
 #pragma unroll
@@ -520,11 +634,17 @@ template <int KPT>
 __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict__ scores,
                                                         int32_t cols, int32_t k,
                                                         int32_t* __restrict__ out) {
+  // once the bin holding the k-th key has at most kCand keys, those are
+  // ranked directly instead of by further radix passes
+  constexpr int kCand = 256;
   __shared__ uint32_t hist[256];
   __shared__ uint64_t s_prefix, s_ref;
   __shared__ uint64_t s_or[16];
-  __shared__ int s_kleft, s_done;
+  __shared__ int s_kleft, s_done, s_cnt;
   __shared__ int wsum[16];
+  __shared__ uint64_t c_key[kCand];
+  __shared__ int c_idx[kCand];
+  __shared__ uint8_t c_sel[kCand];
   const uint64_t* keys = (const uint64_t*)scores;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j0 = tid * KPT;
@@ -551,6 +671,7 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
   uint64_t prefix = ref & mask;
   int kleft = k;
   bool done = false;
+  int cnt = 0x7fffffff;
   // 8-bit digits from the first differing bit down; the last pass may
   // overlap bits already fixed by the prefix (equal on every key it counts)
   for (int shift = 64 - lead - 8; lead < 64; shift -= 8) {
@@ -584,6 +705,7 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
           s_prefix = prefix | ((uint64_t)(255 - 4 * lane - q) << sh);
           s_kleft = kleft - (int)cum;
           s_done = (cum + c[q] == (uint32_t)kleft) ? 1 : 0;   // the whole bin is taken
+          s_cnt = (int)c[q];
         }
         cum += c[q];
       }
@@ -593,7 +715,37 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
     kleft = s_kleft;
     mask |= 0xffull << sh;
     done = s_done != 0;
-    if (done || sh == 0) break;
+    cnt = s_cnt;
+    if (done || sh == 0 || cnt <= kCand) break;
+  }
+  // a small boundary bin that is not fully decided: rank its keys (by key
+  // descending, then channel ascending) and keep the first kleft
+  const bool ranked = !done && cnt <= kCand && lead < 64;
+  if (ranked) {
+    int nc = 0;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) nc += (j0 + q < cols && (kv[q] & mask) == prefix) ? 1 : 0;
+    int ctot;
+    int cp = block_excl_scan_int(nc, wsum, &ctot);
+#pragma unroll
+    for (int q = 0; q < KPT; ++q)
+      if (j0 + q < cols && (kv[q] & mask) == prefix) {
+        c_key[cp] = kv[q];
+        c_idx[cp] = j0 + q;
+        ++cp;
+      }
+    __syncthreads();
+    if (tid < ctot) {
+      const uint64_t key = c_key[tid];
+      const int id = c_idx[tid];
+      int r = 0;
+      for (int i = 0; i < ctot; ++i) {
+        const uint64_t k2 = c_key[i];
+        r += (k2 > key || (k2 == key && c_idx[i] < id)) ? 1 : 0;
+      }
+      c_sel[tid] = r < kleft ? 1 : 0;
+    }
+    __syncthreads();
   }
   // keys whose top bits exceed the boundary prefix are all taken; keys on it
   // are all taken (done) or the first kleft of them by channel index
@@ -609,7 +761,7 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
     const bool valid = j0 + q < cols;
     const uint64_t mk = kv[q] & mask;
     const bool eq = valid && mk == prefix;
-    sel[q] = valid && (mk > prefix || (eq && (done || eq_rank < kleft)));
+    sel[q] = valid && (mk > prefix || (eq && (done || (ranked ? c_sel[eq_rank] != 0 : eq_rank < kleft))));
     eq_rank += eq ? 1 : 0;
     nsel += sel[q] ? 1 : 0;
   }
@@ -706,8 +858,9 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
   if (need_amax) {
     const int64_t n16 = rows * cols / 8;
     if (n16 > 0) {
-      int64_t grid = (n16 + 256 * 8 - 1) / (256 * 8);
-      grid = grid < 1 ? 1 : (grid > kAmaxBlocks ? kAmaxBlocks : grid);
+      // one workgroup per CU streams fastest (measured: 7.2 TB/s over 235 MB)
+      int64_t grid = (n16 + kAmaxSeg - 1) / kAmaxSeg;
+      grid = grid < 1 ? 1 : (grid > 256 ? 256 : grid);
       namax = (int32_t)grid;
       hipLaunchKernelGGL(amax_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                          (const uint4*)x, n16, amax);

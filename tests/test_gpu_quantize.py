@@ -102,6 +102,49 @@ def test_exact_ties_and_signed_zeros():
     _compare_nvfp4(_bits(y), 4, ts=1.0)
 
 
+def _tie_direction_amax():
+    """bf16 amax mantissas whose s_t = RN32(a / 2688) is rounded down, up and
+    exact (the three in-call tie rules of the kernel)."""
+    from fractions import Fraction
+    from tests.test_tie_rule import _rn32
+    picks = {}
+    for am in range(128):
+        a = 1 + Fraction(am, 128)
+        st = _rn32(a / 2688)
+        d = "up" if st < a / 2688 else ("down" if st > a / 2688 else "even")
+        picks.setdefault(d, am)
+    return picks
+
+
+@pytest.mark.parametrize("direction", ["up", "down", "even"])
+def test_in_call_tie_directions(direction):
+    # Student-t data whose amax is a chosen bf16 value, so that s_t = RN32(amax
+    # / 2688) is rounded down, rounded up or exact; structural ties occur at
+    # every such amax
+    am = _tie_direction_amax()[direction]
+    target = np.float32((1 + am / 128) * 64.0)
+    rng = np.random.default_rng(40 + am)
+    x = rng.standard_t(3, size=(256, 1024)).astype(np.float32)
+    x *= 0.9 * target / np.abs(x).max()
+    x[7, 100] = -target
+    xb = _bits(x)
+    assert np.float32(oracle.nvfp4_quantize(xb).tensor_scale) == np.float32(float(target) / 2688.0)
+    _compare_nvfp4(xb, 32)
+
+
+@pytest.mark.parametrize("direction", ["up", "down", "even"])
+def test_supplied_derived_scale_tie_directions(direction):
+    # a supplied s_t = RN32(a / 2688) for a bf16 a other than this tensor's
+    # amax (a scale kept from an earlier step): the same tie structure
+    am = _tie_direction_amax()[direction]
+    a2 = np.float32((1 + am / 128) * 128.0)
+    st = float(np.float32(float(a2) / 2688.0))
+    rng = np.random.default_rng(60 + am)
+    x = rng.standard_t(3, size=(256, 1024)).astype(np.float32)
+    x *= 100.0 / np.abs(x).max()
+    _compare_nvfp4(_bits(x), 32, ts=st)
+
+
 def test_zero_tiny_and_huge():
     z = np.zeros((70, 64), dtype=np.uint16)
     z[3, 5] = 0x8000                     # -0.0
