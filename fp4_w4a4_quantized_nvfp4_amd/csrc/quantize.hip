@@ -488,22 +488,24 @@ __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
 }
 
 // ====================================================================== scores
-// score_j = sum over groups ascending of the group partial sums (fp64)
-__global__ __launch_bounds__(256) void score_reduce_kernel(const double* __restrict__ partial,
-                                                           int64_t ngroups, int32_t cols,
-                                                           double* __restrict__ scores) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
+// score_j = sum over groups ascending of the group partial sums (fp64).  One
+// wave per 64 channels, so that the loads spread over as many CUs as possible
+__global__ __launch_bounds__(64) void score_reduce_kernel(const double* __restrict__ partial,
+                                                          int64_t ngroups, int32_t cols,
+                                                          double* __restrict__ scores) {
+  const int j = blockIdx.x * 64 + threadIdx.x;
   if (j >= cols) return;
   double s = 0.0;
   int64_t t = 0;
-  for (; t + 32 <= ngroups; t += 32) {
-    double p[32];
+  // up to 64 loads in flight; slots past the last group read as +0.0, which
+  // leaves the (non-negative) running sum unchanged
+  for (; t < ngroups; t += 64) {
+    double p[64];
 #pragma unroll
-    for (int u = 0; u < 32; ++u) p[u] = partial[(t + u) * cols + j];
+    for (int u = 0; u < 64; ++u) p[u] = t + u < ngroups ? partial[(t + u) * cols + j] : 0.0;
 #pragma unroll
-    for (int u = 0; u < 32; ++u) s += p[u];
+    for (int u = 0; u < 64; ++u) s += p[u];
   }
-  for (; t < ngroups; ++t) s += partial[t * cols + j];
   scores[j] = s;
 }
 
@@ -630,32 +632,41 @@ __device__ __forceinline__ int block_excl_scan_int(int v, int* wsum, int* total)
   return before + incl - v;
 }
 
+// Register-resident top-k (cols <= 1024 * KPT), one workgroup of 1024
+// threads holding KPT keys each (fp64 bit patterns: non-negative doubles
+// order as unsigned integers).  Radix select with 11-bit digits from the
+// first bit where two keys differ (two histogram buffers, so one pass costs
+// two barriers).  Once the bin holding the k-th key has at most 64 keys and
+// is not taken whole, those are ranked directly (key descending, channel
+// ascending).  The emit pass takes every key above the boundary and the
+// chosen keys on it, in ascending channel order.
 template <int KPT>
 __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict__ scores,
                                                         int32_t cols, int32_t k,
                                                         int32_t* __restrict__ out) {
-  // once the bin holding the k-th key has at most kCand keys, those are
-  // ranked directly instead of by further radix passes
-  constexpr int kCand = 256;
-  __shared__ uint32_t hist[256];
-  __shared__ uint64_t s_prefix, s_ref;
+  constexpr int DB = 11, NB = 1 << DB;   // digit bits, bins
+  constexpr int BPL = NB / 64;           // bins per lane in the boundary search
+  constexpr int kCand = 64;
+  __shared__ uint32_t hist[2][NB];
+  __shared__ uint64_t s_prefix;
   __shared__ uint64_t s_or[16];
-  __shared__ int s_kleft, s_done, s_cnt;
+  __shared__ int s_kleft, s_done, s_cnt, s_nc;
   __shared__ int wsum[16];
   __shared__ uint64_t c_key[kCand];
   __shared__ int c_idx[kCand];
-  __shared__ uint8_t c_sel[kCand];
+  __shared__ int c_rank[kCand];
   const uint64_t* keys = (const uint64_t*)scores;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j0 = tid * KPT;
   uint64_t kv[KPT];
 #pragma unroll
   for (int q = 0; q < KPT; ++q) kv[q] = j0 + q < cols ? keys[j0 + q] : 0ull;
+  const uint64_t ref = keys[0];
+  for (int i = tid; i < NB; i += 1024) hist[0][i] = 0;
+  if (tid == 0) s_nc = 0;
+  if (tid < kCand) c_rank[tid] = 0;
   // Bits that every key shares need no pass: the radix passes start at the
   // highest bit where two keys differ (OR of key ^ key 0 over all keys).
-  if (tid == 0) s_ref = keys[0];
-  __syncthreads();
-  const uint64_t ref = s_ref;
   uint64_t dx = 0;
 #pragma unroll
   for (int q = 0; q < KPT; ++q)
@@ -672,88 +683,104 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
   int kleft = k;
   bool done = false;
   int cnt = 0x7fffffff;
-  // 8-bit digits from the first differing bit down; the last pass may
+  // DB-bit digits from the first differing bit down; the last pass may
   // overlap bits already fixed by the prefix (equal on every key it counts)
-  for (int shift = 64 - lead - 8; lead < 64; shift -= 8) {
+  int pb = 0;
+  for (int shift = 64 - lead - DB; lead < 64; shift -= DB, pb ^= 1) {
     const int sh = shift < 0 ? 0 : shift;
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+    uint32_t* h = hist[pb];
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
       const bool valid = j0 + q < cols && (kv[q] & mask) == prefix;
-      if (valid) atomicAdd(&hist[(uint32_t)(kv[q] >> sh) & 255u], 1u);
+      if (valid) atomicAdd(&h[(uint32_t)(kv[q] >> sh) & (NB - 1)], 1u);
     }
+    for (int i = tid; i < NB; i += 1024) hist[pb ^ 1][i] = 0;   // for the next pass
     __syncthreads();
     if (wave == 0) {
-      // lane l owns digits 255-4l .. 252-4l (descending)
-      uint32_t c[4];
+      // lane l owns digits NB-1-BPL*l .. NB-BPL-BPL*l (descending); its sum is
+      // read in a lane-rotated order (bank-conflict free), then the one lane
+      // range holding the k-th key is scanned bin by bin across the wave
       uint32_t sum = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        c[q] = hist[255 - 4 * lane - q];
-        sum += c[q];
-      }
+      for (int q = 0; q < BPL; ++q) sum += h[NB - 1 - BPL * lane - ((q + lane) & (BPL - 1))];
       uint32_t incl = sum;
       for (int o = 1; o < 64; o <<= 1) {
         const uint32_t v = (uint32_t)__shfl_up((int)incl, o, 64);
         if (lane >= o) incl += v;
       }
-      uint32_t cum = incl - sum;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (cum < (uint32_t)kleft && cum + c[q] >= (uint32_t)kleft) {
-          s_prefix = prefix | ((uint64_t)(255 - 4 * lane - q) << sh);
-          s_kleft = kleft - (int)cum;
-          s_done = (cum + c[q] == (uint32_t)kleft) ? 1 : 0;   // the whole bin is taken
-          s_cnt = (int)c[q];
-        }
-        cum += c[q];
+      const uint32_t before = incl - sum;
+      const uint64_t hit = __ballot(before < (uint32_t)kleft && incl >= (uint32_t)kleft);
+      const int L = hit ? (int)__builtin_ctzll(hit) : 63;   // exactly one lane holds it
+      const uint32_t base = (uint32_t)__shfl((int)before, L, 64);
+      const int dig = NB - 1 - BPL * L - lane;                  // lanes < BPL: descending digits
+      const uint32_t cb = lane < BPL ? h[dig] : 0u;
+      uint32_t inc2 = cb;
+      for (int o = 1; o < BPL; o <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_up((int)inc2, o, 64);
+        if (lane >= o) inc2 += v;
+      }
+      const uint32_t cum = base + inc2 - cb;
+      if (lane < BPL && cum < (uint32_t)kleft && cum + cb >= (uint32_t)kleft) {
+        s_prefix = prefix | ((uint64_t)dig << sh);
+        s_kleft = kleft - (int)cum;
+        s_done = (cum + cb == (uint32_t)kleft) ? 1 : 0;   // the whole bin is taken
+        s_cnt = (int)cb;
       }
     }
     __syncthreads();
     prefix = s_prefix;
     kleft = s_kleft;
-    mask |= 0xffull << sh;
+    mask |= (uint64_t)(NB - 1) << sh;
     done = s_done != 0;
     cnt = s_cnt;
     if (done || sh == 0 || cnt <= kCand) break;
   }
-  // a small boundary bin that is not fully decided: rank its keys (by key
-  // descending, then channel ascending) and keep the first kleft
+  // the boundary bin: taken whole (done), ranked (at most kCand keys), or
+  // keys all equal (every bit decided), taken by channel order
   const bool ranked = !done && cnt <= kCand && lead < 64;
+  int slot[KPT];
+  int eq_rank = 0;
   if (ranked) {
-    int nc = 0;
+    // candidate slots: a ballot per key position, one atomic per wave
 #pragma unroll
-    for (int q = 0; q < KPT; ++q) nc += (j0 + q < cols && (kv[q] & mask) == prefix) ? 1 : 0;
-    int ctot;
-    int cp = block_excl_scan_int(nc, wsum, &ctot);
-#pragma unroll
-    for (int q = 0; q < KPT; ++q)
-      if (j0 + q < cols && (kv[q] & mask) == prefix) {
-        c_key[cp] = kv[q];
-        c_idx[cp] = j0 + q;
-        ++cp;
+    for (int q = 0; q < KPT; ++q) {
+      const bool c = j0 + q < cols && (kv[q] & mask) == prefix;
+      const uint64_t b = __ballot(c);
+      int base = 0;
+      if (b != 0ull) {
+        if (lane == 0) base = atomicAdd(&s_nc, (int)__popcll(b));
+        base = __shfl(base, 0, 64);
       }
+      slot[q] = -1;
+      if (c) {
+        const int sl = base + (int)__popcll(b & ((1ull << lane) - 1ull));
+        c_key[sl] = kv[q];
+        c_idx[sl] = j0 + q;
+        slot[q] = sl;
+      }
+    }
     __syncthreads();
-    if (tid < ctot) {
-      const uint64_t key = c_key[tid];
-      const int id = c_idx[tid];
+    // rank of candidate l = number of candidates before it (key descending,
+    // channel ascending); the sixteen waves each compare against every
+    // sixteenth candidate and add their counts
+    if (lane < cnt) {
+      const uint64_t key = c_key[lane];
+      const int id = c_idx[lane];
       int r = 0;
-      for (int i = 0; i < ctot; ++i) {
+      for (int i = wave; i < cnt; i += 16) {
         const uint64_t k2 = c_key[i];
         r += (k2 > key || (k2 == key && c_idx[i] < id)) ? 1 : 0;
       }
-      c_sel[tid] = r < kleft ? 1 : 0;
+      if (r) atomicAdd(&c_rank[lane], r);
     }
     __syncthreads();
-  }
-  // keys whose top bits exceed the boundary prefix are all taken; keys on it
-  // are all taken (done) or the first kleft of them by channel index
-  int neq = 0;
+  } else if (!done) {
+    int neq = 0;
 #pragma unroll
-  for (int q = 0; q < KPT; ++q) neq += (j0 + q < cols && (kv[q] & mask) == prefix) ? 1 : 0;
-  int tot;
-  int eq_rank = block_excl_scan_int(neq, wsum, &tot);
+    for (int q = 0; q < KPT; ++q) neq += (j0 + q < cols && (kv[q] & mask) == prefix) ? 1 : 0;
+    int etot;
+    eq_rank = block_excl_scan_int(neq, wsum, &etot);
+  }
   bool sel[KPT];
   int nsel = 0;
 #pragma unroll
@@ -761,10 +788,14 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
     const bool valid = j0 + q < cols;
     const uint64_t mk = kv[q] & mask;
     const bool eq = valid && mk == prefix;
-    sel[q] = valid && (mk > prefix || (eq && (done || (ranked ? c_sel[eq_rank] != 0 : eq_rank < kleft))));
+    bool take_eq = done;
+    if (ranked) take_eq = eq && c_rank[slot[q]] < kleft;
+    else if (!done) take_eq = eq_rank < kleft;
+    sel[q] = valid && (mk > prefix || (eq && take_eq));
     eq_rank += eq ? 1 : 0;
     nsel += sel[q] ? 1 : 0;
   }
+  int tot;
   int pos = block_excl_scan_int(nsel, wsum, &tot);
 #pragma unroll
   for (int q = 0; q < KPT; ++q)
@@ -898,7 +929,7 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
     // no rows: still report s_t (1, or the supplied value)
     hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(64), 0, stream, ts_in, ts_out);
   }
-  hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((cols + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(64), 0,
                      stream, (const double*)partial, ngroups, (int32_t)cols, scores);
   if (topk > 0) return launch_select(scores, cols, topk, chan_idx, stream);
   return hipGetLastError();
