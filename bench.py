@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 # HBM bytes per launch of the dense GEMM kernel from rocprofv3 --pmc FETCH_SIZE /
 # WRITE_SIZE (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives
 # (fetch x 2.00, write x 1.00); valid only for the kernel source it was taken on
-TRAFFIC = {"gemm_src_sha256": "7a4ec20202c18badcbdca739a3fe0b17e9db517a1014a2a6fe6bcc3eff7362a3",
-           "fetch_kib": 242165.1, "fetch_scale": 2.0, "write_kib": 265216.0, "write_scale": 1.0}
+TRAFFIC = {"gemm_src_sha256": "924a3903cb0b910a67928abbb6ff1aea67d8283c81f7ec0bec936b625365e94a",
+           "fetch_kib": 242328.6, "fetch_scale": 2.0, "write_kib": 265216.0, "write_scale": 1.0}
 
 
 def _args():
@@ -49,6 +49,7 @@ def _args():
     p.add_argument("--quant-iters", type=int, default=50)
     p.add_argument("--no-mx", action="store_true", help="skip the MXFP4 comparison leg")
     p.add_argument("--no-moe", action="store_true", help="skip the MoE expert-layer legs")
+    p.add_argument("--no-eq21", action="store_true", help="skip the Eq. 21 compensation leg")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return p.parse_args()
@@ -339,6 +340,40 @@ def main():
               "frac_fp4_peak": round(mx_tf / PEAK_FP4_TFLOPS, 4)}
         del Wm
 
+    # ---------------------------------------------------------------- Eq. 21 leg
+    # the page-literal compensation on the same dense step: the quantization
+    # error re-quantized to NVFP4 (own tensor scale, one extra pass over x for
+    # its amax), masked to the same top-128 channels, times the NVFP4 weight
+    eq21 = None
+    if not a.no_eq21:
+        _say("Eq. 21 leg")
+        ews_b = L.rac_gemm_eq21_workspace_size(M, N, K, k)
+        ews = torch.empty((ews_b,), dtype=torch.uint8, device=dev)
+
+        def estep(i):
+            q4._check(L.rac_gemm_eq21(M, N, K, x[i % 2].data_ptr(), codes.data_ptr(),
+                                      scales.data_ptr(), ts.data_ptr(), W["codes"].data_ptr(),
+                                      W["scales"].data_ptr(), W["tensor_scale"].data_ptr(),
+                                      idx.data_ptr(), k, Y.data_ptr(), 1, None, ews.data_ptr(),
+                                      ews_b, sp))
+        for i in range(3):
+            step(i)
+            estep(i)
+        eev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+        for i in range(5):
+            step(i)
+            eev[i][0].record(stream)
+            estep(i)
+            eev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_eq = float(np.mean([e[0].elapsed_time(e[1]) for e in eev]))
+        eq_tf = step_flops / (t_eq * 1e-3) / 1e12
+        eq21 = {"workload": "dense_8192x14336x4096, Eq. 21 compensation (NVFP4 residual x NVFP4 "
+                            "weight on the top-128 channels), bf16 out",
+                "rac_gemm_eq21_ms": round(t_eq, 4), "tflops": round(eq_tf, 2),
+                "frac_fp16_peak": round(eq_tf / PEAK_FP16_TFLOPS, 4)}
+        del ews
+
     # ---------------------------------------------------------------- MoE legs
     moe = None if a.no_moe else _moe_legs(q4, L, dev, stream, sp)
 
@@ -375,6 +410,8 @@ def main():
     }
     if mx is not None:
         out["mxfp4"] = mx
+    if eq21 is not None:
+        out["eq21"] = eq21
     if moe is not None:
         out["moe"] = moe
     if not a.no_cpu:

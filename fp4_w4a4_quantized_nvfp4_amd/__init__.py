@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "Q4Error", "library_path", "lib",
     "nvfp4_quantize", "mxfp4_quantize", "q4_select_channels", "q4_residual_gather",
-    "w4a4_gemm", "rac_gemm", "q4_moe_route", "q4_moe_sort", "q4_transpose_bf16",
+    "w4a4_gemm", "rac_gemm", "rac_gemm_eq21", "q4_moe_route", "q4_moe_sort", "q4_transpose_bf16",
     "q4_moe_pack_w13", "moe_w4a4_grouped_gemm", "moe_workspace_layout", "prepare_weight",
     "prepare_moe_weights", "NVFP4", "MXFP4", "OUT_F32", "OUT_BF16",
 ]
@@ -58,6 +58,9 @@ _SIGS = {
     "rac_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "rac_gemm": (_I32, [_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
                         _I32, _P, _SZ, _P]),
+    "rac_gemm_eq21_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
+    "rac_gemm_eq21": (_I32, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32,
+                             _P, _P, _SZ, _P]),
     "q4_moe_route": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "q4_moe_sort_workspace_size": (_SZ, [_I64, _I32, _I32]),
     "q4_moe_sort": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
@@ -205,6 +208,29 @@ def rac_gemm(x, A, W, w_hi_t, chan_set, out_dtype=OUT_F32, stream=None, Y=None, 
                       _ptr(W["tensor_scale"]), _ptr(w_hi_t) if k else None,
                       _ptr(chan_set) if k else None, k, _ptr(Y), out_dtype, _ptr(workspace),
                       wsb, _stream(stream)))
+    return Y
+
+
+def rac_gemm_eq21(x, A, W, chan_set, out_dtype=OUT_F32, stream=None, Y=None, workspace=None,
+                  resid_tensor_scale=None):
+    """Page-literal compensation: Y = (Q(x) - M_S * Q(Q(x) - x)) @ Q(W)^T for NVFP4
+    operands A (of x) and W; resid_tensor_scale (fp32 [1], optional) receives the
+    residual's tensor scale."""
+    x = _bf16(x)
+    M, K = x.shape
+    N = W["codes"].shape[0]
+    k = 0 if chan_set is None else int(chan_set.shape[0])
+    L = lib()
+    if Y is None:
+        Y = _empty((M, N), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, x.device)
+    wsb = L.rac_gemm_eq21_workspace_size(M, N, K, k)
+    if workspace is None or workspace.numel() < wsb:
+        workspace = _empty((max(wsb, 1),), torch.uint8, x.device)
+    _check(L.rac_gemm_eq21(M, N, K, _ptr(x), _ptr(A["codes"]), _ptr(A["scales"]),
+                           _ptr(A["tensor_scale"]), _ptr(W["codes"]), _ptr(W["scales"]),
+                           _ptr(W["tensor_scale"]), _ptr(chan_set) if k else None, k, _ptr(Y),
+                           out_dtype, _ptr(resid_tensor_scale) if resid_tensor_scale is not None
+                           else None, _ptr(workspace), wsb, _stream(stream)))
     return Y
 
 

@@ -61,7 +61,7 @@ int32_t round_up32(int32_t k) { return (k + 31) & ~31; }
 extern "C" {
 
 const char* q4_last_error(void) { return g_err; }
-int32_t q4_version(void) { return 100; }
+int32_t q4_version(void) { return 101; }
 
 // ======================================================================== quantize
 size_t q4_quantize_workspace_size(int64_t rows, int64_t cols, int32_t fmt) {
@@ -301,6 +301,92 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
 }
 
 // ======================================================================== MoE
+// Page-literal compensation (Eq. 21): workspace = R' [M][kp] bf16, W' [N][kp]
+// bf16, the residual-amax slots, s_R, then the scale records as in rac_gemm.
+constexpr int32_t kEq21MaxSlots = 1024;
+static int32_t eq21_slots(int64_t M, int64_t K) {
+  const int64_t blocks = M * (K / 16);
+  const int64_t g = (blocks + 255) / 256;
+  return (int32_t)(g < 1 ? 1 : (g > kEq21MaxSlots ? kEq21MaxSlots : g));
+}
+
+size_t rac_gemm_eq21_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k) {
+  if (M < 0 || N < 0 || k < 0) return 0;
+  const int64_t kp = round_up32(k);
+  return align256((size_t)M * kp * 2) + align256((size_t)N * kp * 2) +
+         align256((size_t)kEq21MaxSlots * 4) + 256 + scale_tiles_bytes(M, N, K);
+}
+
+q4_status_t rac_gemm_eq21(int64_t M, int64_t N, int64_t K, const uint16_t* x,
+                          const uint8_t* a_codes, const uint8_t* a_scales,
+                          const float* a_tensor_scale, const uint8_t* w_codes,
+                          const uint8_t* w_scales, const float* w_tensor_scale,
+                          const int32_t* chan_set, int32_t k, void* Y, int32_t y_dtype,
+                          float* resid_tensor_scale_out, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  q4_status_t st = check_gemm("rac_gemm_eq21", Q4_NVFP4, M, N, K, a_codes, a_scales,
+                              a_tensor_scale, w_codes, w_scales, w_tensor_scale, Y, y_dtype);
+  if (st != Q4_OK) return st;
+  if (k < 0 || k > K || k > Q4_MAX_TOPK)
+    return fail(Q4_EINVAL, "rac_gemm_eq21: k %d outside [0, min(K, %d)]", k, Q4_MAX_TOPK);
+  if (resid_tensor_scale_out) Q4_REQUIRE_SCALAR(resid_tensor_scale_out, 4);
+  if (k > 0) {
+    Q4_REQUIRE_PTR(x);
+    Q4_REQUIRE_SCALAR(chan_set, 4);
+    const size_t need = rac_gemm_eq21_workspace_size(M, N, K, k);
+    if (!workspace || workspace_bytes < need)
+      return fail(Q4_EWORKSPACE, "rac_gemm_eq21: workspace of %zu bytes needed (got %zu)", need,
+                  workspace_bytes);
+    Q4_REQUIRE_PTR(workspace);
+  }
+  if (M == 0 || N == 0) return Q4_OK;
+  if (k == 0)
+    return w4a4_gemm(Q4_NVFP4, M, N, K, a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
+                     w_tensor_scale, Y, y_dtype, stream);
+  GemmArgs g{};
+  g.M = M;
+  g.N = N;
+  g.K = (int32_t)K;
+  g.mx = 0;
+  g.a_codes = a_codes;
+  g.a_scales = a_scales;
+  g.a_ts = a_tensor_scale;
+  g.w_codes = w_codes;
+  g.w_scales = w_scales;
+  g.w_ts = w_tensor_scale;
+  g.Y = Y;
+  g.ldy = N;
+  g.y_bf16 = y_dtype == Q4_OUT_BF16;
+  g.epilogue = kEpiStore;
+  const int32_t kp = round_up32(k);
+  uint8_t* base = (uint8_t*)workspace;
+  uint16_t* R = (uint16_t*)base;
+  uint16_t* W_S = (uint16_t*)(base + align256((size_t)M * kp * 2));
+  uint32_t* slots = (uint32_t*)((uint8_t*)W_S + align256((size_t)N * kp * 2));
+  float* r_ts = (float*)((uint8_t*)slots + align256((size_t)kEq21MaxSlots * 4));
+  uint8_t* ta = nullptr;
+  uint8_t* tw = nullptr;
+  if (K % 128 == 0 && M >= 512 && N >= 512) {
+    ta = (uint8_t*)r_ts + 256;
+    tw = ta + align256((size_t)tile_rows_pad(M) * (size_t)(K / 128) * 16);
+    g.a_scales_t = ta;
+    g.w_scales_t = tw;
+    g.a_rows_pad = tile_rows_pad(M);
+    g.w_rows_pad = tile_rows_pad(N);
+  }
+  g.r_res = R;
+  g.ld_r = kp;
+  g.w_sel = W_S;
+  g.kp = kp;
+  g.r_ts = r_ts;
+  hipError_t e = launch_eq21_prep(x, M, N, (int32_t)K, a_codes, a_scales, a_tensor_scale,
+                                  w_codes, w_scales, chan_set, k, kp, R, W_S, slots,
+                                  eq21_slots(M, K), r_ts, resid_tensor_scale_out, ta, tw,
+                                  tile_rows_pad(M), tile_rows_pad(N), S(stream));
+  if (e != hipSuccess) return hip_status(e, "rac_gemm_eq21 (operand preparation)");
+  return hip_status(launch_w4a4_gemm(g, 0, S(stream)), "rac_gemm_eq21");
+}
+
 q4_status_t q4_moe_route(const float* logits, int64_t T, int32_t E, int32_t topk,
                          int32_t* topk_idx, float* topk_w, void* stream) {
   if (T < 0 || T >= kMaxDim) return fail(Q4_ESHAPE, "q4_moe_route: bad T");

@@ -332,13 +332,18 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
   }
 
   // ------------------------------------------------------------ tensor scales
+  // With a scaled compensation term (beta = -s_R s_W) the W4A4 sum is taken
+  // to alpha / beta = -s_A / s_R, the term added, and the sum scaled by beta.
+  const bool rscaled = g.kp > 0 && g.r_res && g.r_ts && g.a_ts;
   const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[e] : 1.0f;
+  const float beta = rscaled ? -(g.r_ts[0] * g.w_ts[e]) : 1.0f;
+  const float pre = rscaled ? -(g.a_ts[0] / g.r_ts[0]) : alpha;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= alpha;
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= pre;
 
   // ------------------------------------------------------------ residual tail
   if (g.kp > 0 && g.r_res) {
@@ -378,6 +383,14 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
         for (int ni = 0; ni < 2; ++ni)
           acc[mi][ni] =
               __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+    }
+    if (rscaled) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= beta;
     }
   }
 
@@ -464,7 +477,9 @@ struct Frag {
   uint32_t sa[4], sb[4];   // two raw E4M3 scales (blocks 2p, 2p + 1) per row
 };
 
-template <bool TILED, bool GROUPED, int EPI>
+// RSC: the compensation term carries its own scale (g.r_ts); a separate
+// instantiation so the plain kernels keep their register allocation
+template <bool TILED, bool GROUPED, int EPI, bool RSC = false>
 __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   static_assert(!(TILED && GROUPED), "grouped tiles take raw scales");
   static_assert(GROUPED || EPI == kEpiStore, "SwiGLU is a grouped epilogue");
@@ -854,11 +869,19 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   // applied once in the epilogue.  No range problem while |RAC| / alpha <
   // 2^127 (with tensor scales taken from the operands' own amax it is below
   // kp * 2688^2).  alpha == 0 leaves Y = RAC and skips the W4A4 chunks.
+  // A scaled compensation term (g.r_ts, beta = -s_R s_W) takes the factor
+  // beta / alpha = -s_R / s_A instead (one fp32 division), or beta itself
+  // when alpha == 0.
   const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[ex] : 1.0f;
-  if (nrac > 0 && alpha != 0.0f) {
-    int e;
-    const float m = frexpf(alpha, &e);
-    const float inv_m = 1.0f / m;
+  if (nrac > 0 && (alpha != 0.0f || RSC)) {
+    int e = 0;
+    float inv_m;
+    if constexpr (RSC) {
+      inv_m = alpha != 0.0f ? -(g.r_ts[0] / g.a_ts[0]) : -(g.r_ts[0] * g.w_ts[ex]);
+    } else {
+      const float m = frexpf(alpha, &e);
+      inv_m = 1.0f / m;
+    }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -1079,7 +1102,13 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
   }
   if (!grouped && fullk && g.epilogue == kEpiStore && g.M >= 512 && g.N >= 512) {
     const int64_t nb = ((g.M + big::BM - 1) / big::BM) * ((g.N + big::BN - 1) / big::BN);
-    if (g.a_scales_t && g.w_scales_t)
+    if (g.r_ts && g.a_ts && g.a_scales_t && g.w_scales_t)
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<true, false, kEpiStore, true>),
+                         dim3((unsigned)nb), dim3(256), 0, stream, g);
+    else if (g.r_ts && g.a_ts)
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<false, false, kEpiStore, true>),
+                         dim3((unsigned)nb), dim3(256), 0, stream, g);
+    else if (g.a_scales_t && g.w_scales_t)
       hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<true, false, kEpiStore>), dim3((unsigned)nb),
                          dim3(256), 0, stream, g);
     else

@@ -52,6 +52,10 @@ struct GemmArgs {
   int32_t ld_r;
   const uint16_t* w_sel;     // bf16 [E][N][kp] selected weight columns
   int32_t kp;                // compensated channels, a multiple of 32 (0: none)
+  // null: the compensation term R W_S^T is added as it is.  Set: it is
+  // multiplied by -(r_ts[0] * w_ts[e]) (the residual's own tensor scale and
+  // the weight's, subtracted: the FP4-quantized residual form of Eq. 21)
+  const float* r_ts;
   void* Y;                   // store: [rows][ldy] fp32|bf16.  SwiGLU: bf16 [rows][N/2]
   int64_t ldy;
   int32_t y_bf16;
@@ -76,6 +80,16 @@ inline int64_t tile_rows_pad(int64_t rows) { return (rows + 255) / 256 * 256; }
 // R and W_S of a dense RAC GEMM (when k > 0 and R, W_S are given) and the
 // scale records of both operands (NVFP4, when a_tiles and w_tiles are given)
 // in one launch
+// Page-literal (Eq. 21) compensation operands of a dense NVFP4 GEMM: the
+// residual's tensor amax (per-workgroup maxima in `slots`, nslots of them),
+// then in one launch s_R (to r_ts and, if given, r_ts_out), R' [M][kp], W'
+// [N][kp] and, when a_tiles and w_tiles are given, both operands' scale records
+hipError_t launch_eq21_prep(const uint16_t* x, int64_t M, int64_t N, int32_t K,
+                            const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
+                            const uint8_t* w_codes, const uint8_t* w_scales, const int32_t* idx,
+                            int32_t k, int32_t kp, uint16_t* R, uint16_t* W_S, uint32_t* slots,
+                            int32_t nslots, float* r_ts, float* r_ts_out, uint8_t* a_tiles,
+                            uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream);
 hipError_t launch_rac_prep(bool mx, const uint16_t* x, int64_t M, int64_t N, int32_t K,
                            const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                            const uint8_t* w_scales, const uint16_t* w_hi_t, const int32_t* idx,

@@ -26,41 +26,45 @@ __device__ __forceinline__ uint4 swz_sc_rec(uint4 v, int row) {
 }
 
 // R[i][t] = bf16(RN32(x[i][S_t] - dequant)) for t < k, 0 for k <= t < ld_r.
-// One thread per (row, 8 consecutive t): all loads of the eight are issued
-// before any is used.  Block `blk` of `nblk` (grid-stride).
+// One thread per (4 consecutive rows, t), t fastest across lanes: S is
+// ascending and its channels cluster in a few blocks (the outlier blocks), so
+// one load instruction of a wave touches few cache lines, and each row's
+// stores are contiguous.  The twelve loads of a thread are issued before any
+// is used.  Items: residual_gather_items(rows, ld_r); block `blk` of `nblk`
+// (grid-stride).
+__host__ __device__ inline int64_t residual_gather_items(int64_t rows, int64_t ld_r) {
+  return (rows + 3) / 4 * ld_r;
+}
+
 template <bool MX>
 __device__ __forceinline__ void residual_gather_part(
     const uint16_t* __restrict__ x, int64_t rows, int32_t cols, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ ts,
     const int32_t* __restrict__ idx, int32_t k, uint16_t* __restrict__ R, int64_t ld_r,
     int64_t blk, int64_t nblk) {
-  const int64_t n8 = (ld_r + 7) / 8;
-  const int64_t total = rows * n8;
+  const int64_t total = residual_gather_items(rows, ld_r);
   const float st = MX ? 1.0f : ts[0];
+  const int64_t cst = cols / 2, sst = MX ? cols / 32 : cols / 16;
   for (int64_t g = blk * 256 + threadIdx.x; g < total; g += nblk * 256) {
-    const int64_t i = g / n8;
-    const int t0 = (int)(g - i * n8) * 8;
-    int j[8];
-    uint16_t xv[8];
-    uint8_t cb[8], sb[8];
+    const int64_t i0 = g / ld_r * 4;
+    const int t = (int)(g - g / ld_r * ld_r);
+    int c = t < k ? idx[t] : 0;
+    c = c < 0 ? 0 : (c >= cols ? cols - 1 : c);
+    uint16_t xv[4];
+    uint8_t cb[4], sb[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      int c = t0 + q < k ? idx[t0 + q] : 0;
-      j[q] = c < 0 ? 0 : (c >= cols ? cols - 1 : c);
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + q < rows ? i0 + q : rows - 1;
+      xv[q] = x[i * cols + c];
+      cb[q] = codes[i * cst + (c >> 1)];
+      sb[q] = scales[i * sst + (c >> (MX ? 5 : 4))];
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      xv[q] = x[i * cols + j[q]];
-      cb[q] = codes[i * (cols / 2) + (j[q] >> 1)];
-      sb[q] = MX ? scales[i * (cols / 32) + (j[q] >> 5)] : scales[i * (cols / 16) + (j[q] >> 4)];
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int t = t0 + q;
-      if (t >= ld_r) break;
+    for (int q = 0; q < 4; ++q) {
+      if (i0 + q >= rows) break;
       uint32_t out = 0;
       if (t < k) {
-        const uint32_t nib = (cb[q] >> ((j[q] & 1) * 4)) & 15u;
+        const uint32_t nib = (cb[q] >> ((c & 1) * 4)) & 15u;
         float s;
         if constexpr (MX) {
           const int e = (int)sb[q] - 127;
@@ -70,7 +74,7 @@ __device__ __forceinline__ void residual_gather_part(
         }
         out = f32_to_bf16_rne(fmaf(-(e2m1_value(nib) * s), st, bf16_to_f32(xv[q])));
       }
-      R[i * ld_r + t] = (uint16_t)out;
+      R[(i0 + q) * ld_r + t] = (uint16_t)out;
     }
   }
 }

@@ -958,7 +958,7 @@ hipError_t launch_residual_gather(bool mx, const uint16_t* x, int64_t rows, int6
                                   const uint8_t* codes, const uint8_t* scales, const float* ts,
                                   const int32_t* idx, int32_t k, uint16_t* R, int64_t ld_r,
                                   hipStream_t stream) {
-  const int64_t total = rows * ((ld_r + 7) / 8);
+  const int64_t total = residual_gather_items(rows, ld_r);
   if (total == 0) return hipSuccess;
   int64_t grid = (total + 255) / 256;
   grid = grid > 65536 ? 65536 : grid;

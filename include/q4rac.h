@@ -165,6 +165,38 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
                      const uint16_t *w_hi_t, const int32_t *chan_set, int32_t k, void *Y,
                      int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Page-literal compensation (QUADS section 3.3, Eq. 20-21), NVFP4 only.  The
+ * quantization error dX = dequant(A) - x is quantized as an activation of its
+ * own: carried as bf16 (dX = bf16(RN32(dequant - x))), tensor scale
+ * s_R = RN32(amax|dX| / 2688) (1 if dX is all zero), E4M3 block scales and
+ * E2M1 codes by the quantization rule above.  It is masked to the channel set
+ * S after quantization, and the corrected activation multiplies the NVFP4
+ * weight (no bf16 weight is needed):
+ *   Y = ( dequant(A) - M_S * dequant(Q(dX)) ) W_dequant^T
+ *     = s_A s_W sum_K d_A d_W - s_R s_W sum_{t<k} (c sb)_dX[i][S_t] (c sb)_W[j][S_t].
+ * Both factors of the second sum are exact in bf16; it runs as extra bf16 MFMA
+ * steps into the same fp32 tile.
+ *   x, A, W, chan_set, k, Y, y_dtype as rac_gemm (A and W NVFP4).
+ *   resid_tensor_scale_out fp32 [1] (out) or NULL: s_R, written when M, N and
+ *           k are all > 0.
+ * k == 0 gives exactly w4a4_gemm.  Range (documented, not checked): the W4A4
+ * sum is carried scaled by s_A / s_R on one path and the compensation by
+ * s_R / s_A on the other, so s_R / s_A must lie in [2^-90, 2^90].  With s_A
+ * computed from the tensor's own amax it is at most 1/6 (or dX is all zero,
+ * which is harmless); it falls below 2^-90 only for a tensor whose largest
+ * quantization error is below about 2^-90 of its largest element.
+ * Workspace (rac_gemm_eq21_workspace_size): at offset 0 the bf16 matrix
+ * R' [M][kp] = (c sb) of Q(dX) on S (0 past k), kp = k rounded up to 32, then
+ * the weight factor [N][kp], the amax partials, s_R and the scale records. */
+size_t rac_gemm_eq21_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);
+q4_status_t rac_gemm_eq21(int64_t M, int64_t N, int64_t K, const uint16_t *x,
+                          const uint8_t *a_codes, const uint8_t *a_scales,
+                          const float *a_tensor_scale, const uint8_t *w_codes,
+                          const uint8_t *w_scales, const float *w_tensor_scale,
+                          const int32_t *chan_set, int32_t k, void *Y, int32_t y_dtype,
+                          float *resid_tensor_scale_out, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------- MoE
  * Router (top-k MoE of section 3.3's W13 site): for each token the topk experts
  * of largest logit (ties to the smaller expert), highest first, and their

@@ -52,5 +52,5 @@ from .quant import (  # noqa: F401
     residual_gather,
     select_topk,
 )
-from .gemm import rac_gemm, w4a4_gemm, rac_gemm_eq21  # noqa: F401
+from .gemm import rac_gemm, w4a4_gemm, rac_gemm_eq21, eq21_residual_quant  # noqa: F401
 from .moe import moe_route, moe_sort, moe_layer, swiglu_bf16  # noqa: F401

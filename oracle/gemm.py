@@ -48,16 +48,25 @@ def rac_gemm(A: QuantResult, W: QuantResult, R_bits: np.ndarray, w_hi_bits: np.n
     return y
 
 
-def rac_gemm_eq21(x_bits: np.ndarray, A: QuantResult, W: QuantResult, S: np.ndarray) -> np.ndarray:
-    """Page-literal Eq. 21: X~ = Q_A(X) - M_S * Q_A(Q_A(X) - X), times the NVFP4 W."""
+def eq21_residual_quant(A: QuantResult) -> QuantResult:
+    """Q_A(dX_q), dX_q = Q_A(X) - X = -resid (fp32, rounded once), carried as
+    bf16 like any activation entering Q_A: its own tensor scale and blocks."""
     from .formats import f32_to_bf16_bits
-    # dX_q = Q_A(X) - X = -resid (fp32 exact-once rounding of the difference);
-    # as activation it is carried as bf16 like any activation entering Q_A.
-    dxq_bits = f32_to_bf16_bits(-A.resid)
-    Q = nvfp4_quantize(dxq_bits)
-    qd = block_values(Q.codes, Q.scales, "nvfp4") * float(Q.tensor_scale)
+    return nvfp4_quantize(f32_to_bf16_bits(-A.resid))
+
+
+def rac_gemm_eq21(x_bits: np.ndarray, A: QuantResult, W: QuantResult, S: np.ndarray,
+                  rows=None, Q: QuantResult | None = None) -> np.ndarray:
+    """Page-literal Eq. 21: X~ = Q_A(X) - M_S * Q_A(Q_A(X) - X), times the NVFP4 W.
+
+    ``rows`` (optional index array) restricts the output to those rows; ``Q``
+    may pass a precomputed ``eq21_residual_quant(A)``."""
+    if Q is None:
+        Q = eq21_residual_quant(A)
+    sel = slice(None) if rows is None else np.asarray(rows, dtype=np.int64)
+    qd = block_values(Q.codes[sel], Q.scales[sel], "nvfp4") * float(Q.tensor_scale)
     mask = np.zeros(A.resid.shape[1], dtype=bool)
     mask[np.asarray(S, dtype=np.int64)] = True
-    xt = block_values(A.codes, A.scales, "nvfp4") * float(A.tensor_scale) - qd * mask[None, :]
+    xt = block_values(A.codes[sel], A.scales[sel], "nvfp4") * float(A.tensor_scale) - qd * mask[None, :]
     wd = block_values(W.codes, W.scales, "nvfp4") * float(W.tensor_scale)
     return xt @ wd.T

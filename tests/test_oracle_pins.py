@@ -355,6 +355,29 @@ def test_eq21_literal_reduces_error(c1):
     assert np.linalg.norm(y1 - ref) < np.linalg.norm(y0 - ref)
 
 
+def test_eq21_all_channels_error_bound(c1):
+    """Eq. 21 with S = every channel: X~ - x = dX - dequant(Q(dX)) up to the bf16
+    carrying of dX, so each element is within half an E2M1 grid step of dX's own
+    block scale (at most 1 * sb * s_R) plus 2^-8 |dX|, and the whole residual
+    shrinks well below the plain quantization error (a dropped or sign-flipped
+    correction leaves it at 1x or 2x)."""
+    d, A = c1
+    x = f32_from_bf16_bits(d["x"]).astype(np.float64)
+    deq = oracle.dequantize(A)
+    Q = oracle.eq21_residual_quant(A)
+    qd = oracle.dequantize(Q)
+    xt = deq - qd
+    dx = deq - x
+    sbq = np.repeat(oracle.E4M3_VALUES[Q.scales.astype(np.int64)], 16, axis=1) * float(Q.tensor_scale)
+    assert np.all(np.abs(xt - x) <= np.abs(dx) * 2.0 ** -8 + sbq)
+    assert np.linalg.norm(xt - x) <= 0.2 * np.linalg.norm(dx)
+    # and the GEMM form agrees with the corrected activation times dequant(W)
+    W = oracle.nvfp4_quantize(d["w"])
+    y = oracle.rac_gemm_eq21(d["x"], A, W, np.arange(x.shape[1]))
+    ref = xt @ oracle.dequantize(W).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
 # ---------------------------------------------------------------- MXFP4
 def test_mxfp4_brute_force():
     rng = np.random.default_rng(5)
