@@ -599,13 +599,13 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
     e = (call);                            \
     if (e != hipSuccess) return hip_status(e, what); \
   } while (0)
-  Q4_TRY(launch_moe_sort(topk_idx, T, E, topk, perm, offsets, inv, tiles, ntiles,
-                         (int32_t*)P(L.counts), s), "moe sort");
-  Q4_TRY(launch_gather_rows_index(perm, R, topk, a_rows, s), "moe row index");
+  // the sort also writes each sorted row's token and, for decode-shaped
+  // layers, the 32-row tile table of the skinny kernel
   const bool skinny = moe_skinny(T, E, topk);
-  if (skinny)
-    Q4_TRY(launch_moe_tiles(offsets, E, kSkinnyBM, (int32_t*)P(L.tiles_s), (int32_t*)P(L.ntiles_s),
-                            s), "moe tiles");
+  Q4_TRY(launch_moe_sort(topk_idx, T, E, topk, perm, offsets, inv, tiles, ntiles,
+                         (int32_t*)P(L.counts), s, a_rows, skinny ? kSkinnyBM : 0,
+                         skinny ? (int32_t*)P(L.tiles_s) : nullptr,
+                         skinny ? (int32_t*)P(L.ntiles_s) : nullptr), "moe sort");
   auto grouped_gemm = [&](GemmArgs& gg) {
     if (skinny) {
       gg.tiles = (const int32_t*)P(L.tiles_s);

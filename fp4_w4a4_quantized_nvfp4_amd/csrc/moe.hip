@@ -9,7 +9,9 @@ namespace q4 {
 
 // ====================================================================== route
 // one wave per token: repeated arg-max over the logits (ties -> smaller
-// expert), then softmax over the selected logits
+// expert), then softmax over the selected logits.  MAXPER logits per lane
+// (E <= 64 MAXPER).
+template <int MAXPER>
 __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int64_t T,
                                                         int32_t E, int32_t topk,
                                                         int32_t* __restrict__ idx,
@@ -18,7 +20,6 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* lg = logits + t * E;
-  constexpr int MAXPER = 16;   // E <= 1024
   float v[MAXPER];
   const int per = (E + 63) / 64;
 #pragma unroll
@@ -100,50 +101,72 @@ __global__ __launch_bounds__(1024) void moe_block_hist_kernel(const int32_t* __r
   for (int q = threadIdx.x; q < E; q += 1024) bt[(int64_t)blockIdx.x * E + q] = hist[q];
 }
 
-// counts and offsets per expert, bt[b][e] -> rows of expert e in blocks
-// before b, and one M tile entry {e, begin, end, 0} per kGemmBM rows
-__global__ __launch_bounds__(1024) void moe_offsets_kernel(int32_t* __restrict__ bt, int64_t nb,
-                                                           int32_t E, int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ tiles,
-                                                           int32_t* __restrict__ ntiles) {
-  __shared__ int s_cnt[1024];
-  __shared__ int s_off[1025];
-  __shared__ int s_tile[1025];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int64_t b = 0; b < nb; ++b) {
-      const int v = bt[b * E + e];
-      bt[b * E + e] = c;
-      c += v;
-    }
-    s_cnt[e] = c;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int o = 0, tcount = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = o;
-      s_tile[e] = tcount;
-      o += s_cnt[e];
-      tcount += (s_cnt[e] + kGemmBM - 1) / kGemmBM;
-    }
-    s_off[E] = o;
-    s_tile[E] = tcount;
-    ntiles[0] = tcount;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = s_off[e];
+// tile entries {e, begin, end, 0}, at most bm rows each, for every expert
+__device__ __forceinline__ void write_tiles(const int* s_off, const int* s_tile, int32_t E, int bm,
+                                            int32_t* __restrict__ tiles) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int nt = s_tile[e + 1] - s_tile[e];
     for (int q = 0; q < nt; ++q) {
       int4 v;
       v.x = e;
-      v.y = s_off[e] + q * kGemmBM;
-      v.z = min(s_off[e] + (q + 1) * kGemmBM, s_off[e + 1]);
+      v.y = s_off[e] + q * bm;
+      v.z = min(s_off[e] + (q + 1) * bm, s_off[e + 1]);
       v.w = 0;
       ((int4*)tiles)[s_tile[e] + q] = v;
     }
   }
+}
+
+// counts and offsets per expert, bt[b][e] -> rows of expert e in blocks
+// before b, one M tile entry {e, begin, end, 0} per kGemmBM rows and, when
+// tiles2 is given, a second table with bm2 rows per tile
+__global__ __launch_bounds__(1024) void moe_offsets_kernel(int32_t* __restrict__ bt, int64_t nb,
+                                                           int32_t E, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ tiles,
+                                                           int32_t* __restrict__ ntiles, int32_t bm2,
+                                                           int32_t* __restrict__ tiles2,
+                                                           int32_t* __restrict__ ntiles2) {
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1025];
+  __shared__ int s_tile[1025];
+  __shared__ int s_tile2[1025];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    // sixteen blocks' counts loaded before any is rewritten, so the walk
+    // waits for one load round trip per sixteen blocks
+    int c = 0;
+    for (int64_t b0 = 0; b0 < nb; b0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = b0 + u < nb ? bt[(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (b0 + u < nb) bt[(b0 + u) * E + e] = c;
+        c += v[u];
+      }
+    }
+    s_cnt[e] = c;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int o = 0, tcount = 0, tcount2 = 0;
+    for (int e = 0; e < E; ++e) {
+      s_off[e] = o;
+      s_tile[e] = tcount;
+      s_tile2[e] = tcount2;
+      o += s_cnt[e];
+      tcount += (s_cnt[e] + kGemmBM - 1) / kGemmBM;
+      if (tiles2) tcount2 += (s_cnt[e] + bm2 - 1) / bm2;
+    }
+    s_off[E] = o;
+    s_tile[E] = tcount;
+    s_tile2[E] = tcount2;
+    ntiles[0] = tcount;
+    if (tiles2) ntiles2[0] = tcount2;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = s_off[e];
+  write_tiles(s_off, s_tile, E, kGemmBM, tiles);
+  if (tiles2) write_tiles(s_off, s_tile2, E, bm2, tiles2);
 }
 
 // stable scatter: rows of expert e in flat (t, s) order
@@ -152,7 +175,9 @@ __global__ __launch_bounds__(1024) void moe_scatter_kernel(const int32_t* __rest
                                                            const int32_t* __restrict__ bt,
                                                            const int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm,
-                                                           int32_t* __restrict__ inv_perm) {
+                                                           int32_t* __restrict__ inv_perm,
+                                                           int32_t topk,
+                                                           int32_t* __restrict__ a_rows) {
   __shared__ int wcnt[16][1024];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   for (int q = threadIdx.x; q < 16 * E; q += 1024) wcnt[q / E][q % E] = 0;
@@ -177,13 +202,8 @@ __global__ __launch_bounds__(1024) void moe_scatter_kernel(const int32_t* __rest
     const int pos = offsets[e] + bt[(int64_t)blockIdx.x * E + e] + rank;
     perm[pos] = (int32_t)i;
     inv_perm[i] = pos;
+    if (a_rows) a_rows[pos] = (int32_t)(i / topk);
   }
-}
-
-__global__ __launch_bounds__(256) void moe_arows_kernel(const int32_t* __restrict__ perm, int64_t n,
-                                                        int32_t topk, int32_t* __restrict__ a_rows) {
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (r < n) a_rows[r] = perm[r] / topk;
 }
 
 // y[t][h] = sum over slots s = 0..topk-1 of w[t][s] * out[inv_perm[t*topk+s]][h]
@@ -217,42 +237,17 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   }
 }
 
-// tile table {e, begin, end, 0} with at most bm rows per tile, from offsets
-__global__ __launch_bounds__(1024) void moe_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                         int32_t E, int32_t bm,
-                                                         int32_t* __restrict__ tiles,
-                                                         int32_t* __restrict__ ntiles) {
-  __shared__ int s_tile[1025];
-  if (threadIdx.x == 0) {
-    int tcount = 0;
-    for (int e = 0; e < E; ++e) {
-      s_tile[e] = tcount;
-      tcount += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-    }
-    s_tile[E] = tcount;
-    ntiles[0] = tcount;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const int b0 = offsets[e], b1 = offsets[e + 1];
-    const int nt = s_tile[e + 1] - s_tile[e];
-    for (int q = 0; q < nt; ++q) {
-      int4 v;
-      v.x = e;
-      v.y = b0 + q * bm;
-      v.z = min(b0 + (q + 1) * bm, b1);
-      v.w = 0;
-      ((int4*)tiles)[s_tile[e] + q] = v;
-    }
-  }
-}
-
 // ====================================================================== launchers
 hipError_t launch_moe_route(const float* logits, int64_t T, int32_t E, int32_t topk, int32_t* idx,
                             float* w, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_route_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream,
-                     logits, T, E, topk, idx, w);
+  const dim3 grid((unsigned)((T + 3) / 4));
+  if (E <= 128)
+    hipLaunchKernelGGL(moe_route_kernel<2>, grid, dim3(256), 0, stream, logits, T, E, topk, idx, w);
+  else if (E <= 256)
+    hipLaunchKernelGGL(moe_route_kernel<4>, grid, dim3(256), 0, stream, logits, T, E, topk, idx, w);
+  else
+    hipLaunchKernelGGL(moe_route_kernel<16>, grid, dim3(256), 0, stream, logits, T, E, topk, idx, w);
   return hipGetLastError();
 }
 
@@ -263,25 +258,19 @@ size_t moe_sort_workspace_bytes(int64_t T, int32_t E, int32_t topk) {
 
 hipError_t launch_moe_sort(const int32_t* idx, int64_t T, int32_t E, int32_t topk, int32_t* perm,
                            int32_t* offsets, int32_t* inv_perm, int32_t* tiles, int32_t* ntiles,
-                           int32_t* counts, hipStream_t stream) {
+                           int32_t* counts, hipStream_t stream, int32_t* a_rows, int32_t bm2,
+                           int32_t* tiles2, int32_t* ntiles2) {
   const int64_t n = T * topk;
   const int64_t nb = (n + 1023) / 1024;
   if (nb > 0)
     hipLaunchKernelGGL(moe_block_hist_kernel, dim3((unsigned)nb), dim3(1024), 0, stream, idx, n,
                        E, counts);
   hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, stream, counts, nb, E, offsets,
-                     tiles, ntiles);
+                     tiles, ntiles, bm2, tiles2, ntiles2);
   if (nb > 0)
     hipLaunchKernelGGL(moe_scatter_kernel, dim3((unsigned)nb), dim3(1024), 0, stream, idx, n, E,
-                       (const int32_t*)counts, (const int32_t*)offsets, perm, inv_perm);
-  return hipGetLastError();
-}
-
-hipError_t launch_gather_rows_index(const int32_t* perm, int64_t n, int32_t topk, int32_t* a_rows,
-                                   hipStream_t stream) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_arows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
-                     perm, n, topk, a_rows);
+                       (const int32_t*)counts, (const int32_t*)offsets, perm, inv_perm, topk,
+                       a_rows);
   return hipGetLastError();
 }
 
@@ -292,13 +281,6 @@ hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const f
   const int64_t nch = (H + 1023) / 1024;
   hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)(T * nch)), dim3(256), 0, stream, out,
                      inv_perm, topk_w, T, topk, H, Y, y_bf16);
-  return hipGetLastError();
-}
-
-hipError_t launch_moe_tiles(const int32_t* offsets, int32_t E, int32_t bm, int32_t* tiles,
-                            int32_t* ntiles, hipStream_t stream) {
-  hipLaunchKernelGGL(moe_tiles_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, bm, tiles,
-                     ntiles);
   return hipGetLastError();
 }
 

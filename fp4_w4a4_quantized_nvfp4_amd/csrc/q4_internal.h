@@ -103,18 +103,18 @@ constexpr int kGemmBN = 128;
 hipError_t launch_moe_route(const float* logits, int64_t T, int32_t E, int32_t topk,
                             int32_t* idx, float* w, hipStream_t stream);
 size_t moe_sort_workspace_bytes(int64_t T, int32_t E, int32_t topk);
+// optional: a_rows[r] = token of sorted row r; a second tile table with bm2
+// rows per tile (tiles2, ntiles2)
 hipError_t launch_moe_sort(const int32_t* idx, int64_t T, int32_t E, int32_t topk, int32_t* perm,
                            int32_t* offsets, int32_t* inv_perm, int32_t* tiles,
-                           int32_t* ntiles, int32_t* counts, hipStream_t stream);
+                           int32_t* ntiles, int32_t* counts, hipStream_t stream,
+                           int32_t* a_rows = nullptr, int32_t bm2 = 0, int32_t* tiles2 = nullptr,
+                           int32_t* ntiles2 = nullptr);
 hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const float* topk_w,
                               int64_t T, int32_t topk, int32_t H, void* Y, int32_t y_bf16,
                               hipStream_t stream);
-hipError_t launch_moe_tiles(const int32_t* offsets, int32_t E, int32_t bm, int32_t* tiles,
-                            int32_t* ntiles, hipStream_t stream);
 // grouped GEMM over tiles of at most kSkinnyBM rows (few rows per expert)
 constexpr int kSkinnyBM = 32;
 hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t stream);
-hipError_t launch_gather_rows_index(const int32_t* perm, int64_t n, int32_t topk, int32_t* a_rows,
-                                   hipStream_t stream);
 
 }  // namespace q4
