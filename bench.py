@@ -50,6 +50,7 @@ def _args():
     p.add_argument("--no-mx", action="store_true", help="skip the MXFP4 comparison leg")
     p.add_argument("--no-moe", action="store_true", help="skip the MoE expert-layer legs")
     p.add_argument("--no-eq21", action="store_true", help="skip the Eq. 21 compensation leg")
+    p.add_argument("--no-w4a4", action="store_true", help="skip the k = 0 (W4A4 only) leg")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return p.parse_args()
@@ -340,6 +341,37 @@ def main():
               "frac_fp4_peak": round(mx_tf / PEAK_FP4_TFLOPS, 4)}
         del Wm
 
+    # ---------------------------------------------------------------- RAC cost
+    # the same call with k = 0 (the W4A4 product alone, same kernel and scale
+    # records), interleaved with the k = 128 call: what the compensation costs
+    wf = None
+    if not a.no_w4a4:
+        _say("W4A4-only leg")
+
+        def wstep(kk):
+            q4._check(L.rac_gemm(0, M, N, K, x[0].data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                                 ts.data_ptr(), W["codes"].data_ptr(), W["scales"].data_ptr(),
+                                 W["tensor_scale"].data_ptr(), W["w_hi_t"].data_ptr(),
+                                 idx.data_ptr() if kk else None, kk, Y.data_ptr(), 1,
+                                 rws.data_ptr(), rws_b, sp))
+        tw = {0: [], k: []}
+        for i in range(12):
+            for kk in (0, k):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                wstep(kk)
+                e1.record(stream)
+                e1.synchronize()
+                if i >= 2:
+                    tw[kk].append(e0.elapsed_time(e1))
+        t0w, tkw = float(np.median(tw[0])), float(np.median(tw[k]))
+        wf = {"workload": "dense_8192x14336x4096, rac_gemm with k = 0 (W4A4 product only) "
+                          "alternating with k = 128",
+              "k0_ms": round(t0w, 4), "k0_tflops": round(gemm_flops / (t0w * 1e-3) / 1e12, 2),
+              "k0_frac_fp16_peak": round(gemm_flops / (t0w * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
+              "k128_ms": round(tkw, 4), "rac_overhead_ms": round(tkw - t0w, 4)}
+
     # ---------------------------------------------------------------- Eq. 21 leg
     # the page-literal compensation on the same dense step: the quantization
     # error re-quantized to NVFP4 (own tensor scale, one extra pass over x for
@@ -412,6 +444,8 @@ def main():
         out["mxfp4"] = mx
     if eq21 is not None:
         out["eq21"] = eq21
+    if wf is not None:
+        out["w4a4_only"] = wf
     if moe is not None:
         out["moe"] = moe
     if not a.no_cpu:

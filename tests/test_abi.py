@@ -64,6 +64,19 @@ def test_shape_and_pointer_errors(L):
                       fake, 0, fake, 1 << 30, None) == 1
     assert L.rac_gemm(0, 8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, fake, 16,
                       fake, 0, None, 0, None) == 4
+    # Eq. 21 compensation: K % 32, k > K, missing workspace, misaligned scale output,
+    # missing tensor scale (NVFP4 only)
+    assert L.rac_gemm_eq21(8, 8, 48, fake, fake, fake, fake, fake, fake, fake, fake, 16, fake, 0,
+                           None, fake, 1 << 30, None) == 2
+    assert L.rac_gemm_eq21(8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, 65, fake, 0,
+                           None, fake, 1 << 30, None) == 1
+    assert L.rac_gemm_eq21(8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, 16, fake, 0,
+                           None, None, 0, None) == 4
+    assert L.rac_gemm_eq21(8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, 16, fake, 0,
+                           C.c_void_p(0x100002), fake, 1 << 30, None) == 3
+    assert L.rac_gemm_eq21(8, 8, 64, fake, fake, fake, None, fake, fake, fake, fake, 16, fake, 0,
+                           None, fake, 1 << 30, None) == 1
+    assert "a_ts" in _err(L)
     # MoE: bad E, F % 32, topk > E
     assert L.q4_moe_route(fake, 4, 0, 1, fake, fake, None) == 2
     assert L.q4_moe_route(fake, 4, 8, 9, fake, fake, None) == 1
@@ -75,6 +88,10 @@ def test_shape_and_pointer_errors(L):
 def test_workspace_sizes(L):
     assert L.q4_quantize_workspace_size(16384, 7168, 0) >= 64 * 7168 * 8
     assert L.rac_gemm_workspace_size(8192, 14336, 4096, 128) >= (8192 + 14336) * 128 * 2
+    # Eq. 21: R' and W' [rows][kp] bf16 first, then amax partials, s_R and the records
+    assert L.rac_gemm_eq21_workspace_size(8192, 14336, 4096, 128) >= \
+        L.rac_gemm_workspace_size(8192, 14336, 4096, 128) + 1024 * 4
+    assert L.rac_gemm_eq21_workspace_size(64, 512, 512, 20) >= (64 + 512) * 32 * 2
     offs = (C.c_size_t * 16)()
     assert L.moe_workspace_layout(0, 8192, 128, 2048, 768, 8, 64, offs) == 0
     vals = list(offs)
