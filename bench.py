@@ -409,6 +409,26 @@ def main():
     # ---------------------------------------------------------------- MoE legs
     moe = None if a.no_moe else _moe_legs(q4, L, dev, stream, sp)
 
+    # ---------------------------------------------------------------- HBM reference
+    # a plain 1 GiB device-to-device copy (torch), read + write bytes over its
+    # time: what a streaming kernel reaches on this device, next to the 8 TB/s
+    # nominal peak the fractions above use
+    _say("copy reference")
+    cbuf = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(cbuf)
+    cdst.copy_(cbuf)
+    cts = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cdst.copy_(cbuf)
+        e1.record(stream)
+        e1.synchronize()
+        cts.append(e0.elapsed_time(e1))
+    copy_gbs = 2.0 * (1 << 30) / (float(np.median(cts)) * 1e-3) / 1e9
+    del cbuf, cdst
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -439,6 +459,9 @@ def main():
                       "algorithmic_bytes": int(q_bytes)},
         "context": "pages: ~16% end-to-end rollout gain over FP8 and FP4 ~2x FP8 peak, both on "
                    "NVIDIA Blackwell (not targets)",
+        "hbm_copy_reference": {"gbps": round(copy_gbs, 1),
+                               "frac_hbm": round(copy_gbs / PEAK_HBM_GBS, 4),
+                               "what": "1 GiB torch device copy, read + write bytes"},
     }
     if mx is not None:
         out["mxfp4"] = mx
