@@ -51,6 +51,7 @@ def _args():
     p.add_argument("--no-moe", action="store_true", help="skip the MoE expert-layer legs")
     p.add_argument("--no-eq21", action="store_true", help="skip the Eq. 21 compensation leg")
     p.add_argument("--no-w4a4", action="store_true", help="skip the k = 0 (W4A4 only) leg")
+    p.add_argument("--no-sweep", action="store_true", help="skip the selection-ratio sweep")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
     return p.parse_args()
@@ -126,6 +127,85 @@ def _moe_legs(q4, L, dev, stream, sp, iters=10):
         del w13, w2
         torch.cuda.empty_cache()
     return res
+
+
+def _ratio_sweep(q4, L, dev, stream, sp, reps=7):
+    """Selection ratio k / K = 0, 12.5, 25, 50, 75 % on an 8192 x 4096 x 1024
+    projection: the output mismatch ||Y - x W^T|| / ||x W^T|| (Frobenius; the
+    reference in fp32 from the bf16 x and W) of the plain W4A4 product, of the
+    bf16-residual compensation and of the Eq. 21 compensation, and the time of
+    each call (`reps` calls back to back, median of three such runs, the
+    modes alternating)."""
+    import torch
+    from workloads import WORKLOADS, make_activations, make_weight
+    wl = WORKLOADS["sweep_8192x4096x1024"]
+    M, K, N = wl.rows, wl.cols, wl.n_out
+    _say("ratio sweep")
+    x = torch.from_numpy(make_activations(wl).view(np.int16)).to(dev)
+    wb = torch.from_numpy(make_weight(wl).view(np.int16)).to(dev)
+    W = q4.prepare_weight(wb)
+    xf = x.view(torch.bfloat16).float()
+    refs = {"bf16": xf @ wb.view(torch.bfloat16).float().t().contiguous(),
+            "qdqw": xf @ _nvfp4_weight_values(W).t().contiguous()}
+    rnorm = {r: float(torch.linalg.vector_norm(v)) for r, v in refs.items()}
+    Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    rows = []
+    for pct in (0.0, 12.5, 25.0, 50.0, 75.0):
+        k = int(round(K * pct / 100.0))
+        A = q4.nvfp4_quantize(x, topk=k)
+        S = A["chan_idx"] if k else None
+        ws_b = max(L.rac_gemm_workspace_size(M, N, K, k), L.rac_gemm_eq21_workspace_size(M, N, K, k))
+        ws = torch.empty((ws_b,), dtype=torch.uint8, device=dev)
+        modes = {"w4a4": lambda: q4.w4a4_gemm(A, W),
+                 "rac": lambda: q4.rac_gemm(x, A, W, W["w_hi_t"], S, Y=Y, workspace=ws),
+                 "eq21": lambda: q4.rac_gemm_eq21(x, A, W, S, Y=Y, workspace=ws)}
+        if not k:
+            modes = {"w4a4": modes["w4a4"]}
+        row = {"pct": pct, "k": k}
+        times = {m: [] for m in modes}
+        for it in range(3):
+            for m, f in modes.items():
+                out = f()
+                torch.cuda.synchronize()
+                if it == 0:
+                    for r, v in refs.items():
+                        row[f"err_{r}_{m}"] = round(float(torch.linalg.vector_norm(out - v)) / rnorm[r], 6)
+                # `reps` calls back to back between two events
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    f()
+                e1.record(stream)
+                e1.synchronize()
+                times[m].append(e0.elapsed_time(e1) / reps)
+        for m in modes:
+            row[f"ms_{m}"] = round(float(np.median(times[m])), 4)
+        rows.append(row)
+        del ws
+    return {"workload": "sweep_8192x4096x1024: x N(0,1) with 5 channels x50, W N(0, 0.02), "
+                        "fp32 out",
+            "errors": "err_bf16 = ||Y - x W^T|| / ||x W^T|| (W in bf16); err_qdqw = the same "
+                      "against x dequant(Q(W))^T, the unquantized activation times the "
+                      "quantized weight (a trainer that shares the weight quantization): the "
+                      "activation-side mismatch the compensation targets",
+            "rows": rows}
+
+
+def _nvfp4_weight_values(W):
+    """fp32 values c * sb * s_W of an NVFP4 weight (codes [N][K/2], E4M3 scales
+    [N][K/16], fp32 tensor scale): the reference weight of the sweep's
+    activation-side mismatch, decoded with torch integer ops."""
+    import torch
+    codes, scales, ts = W["codes"], W["scales"], W["tensor_scale"]
+    n = codes.shape[0]
+    nib = torch.stack([codes & 15, codes >> 4], dim=-1).reshape(n, -1).long()
+    grid = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device=codes.device)
+    c = grid[nib & 7] * torch.where((nib & 8) != 0, -1.0, 1.0)
+    e = ((scales.long() >> 3) & 15).float()
+    m = (scales.long() & 7).float()
+    sb = torch.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * torch.exp2(e - 7.0))
+    return c * sb.repeat_interleave(16, dim=1) * ts.float()
 
 
 def _say(msg):
@@ -406,6 +486,9 @@ def main():
                 "frac_fp16_peak": round(eq_tf / PEAK_FP16_TFLOPS, 4)}
         del ews
 
+    # ---------------------------------------------------------------- ratio sweep
+    sweep = None if a.no_sweep else _ratio_sweep(q4, L, dev, stream, sp)
+
     # ---------------------------------------------------------------- MoE legs
     moe = None if a.no_moe else _moe_legs(q4, L, dev, stream, sp)
 
@@ -469,6 +552,8 @@ def main():
         out["eq21"] = eq21
     if wf is not None:
         out["w4a4_only"] = wf
+    if sweep is not None:
+        out["ratio_sweep"] = sweep
     if moe is not None:
         out["moe"] = moe
     if not a.no_cpu:

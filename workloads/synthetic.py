@@ -62,6 +62,11 @@ WORKLOADS = {
     "moe_decode_256": Workload(4, "moe_decode_256", 256, 4096, "t3", 41, (20.0, 100.0),
                                topk_channels=64, out_dtype="bf16", experts=128, ffn=1536,
                                route_topk=8),
+    # selection-ratio sweep (k = 12.5 .. 75 % of the channels, the page's range):
+    # the dense prefill distribution on a 1024-channel projection
+    "sweep_8192x4096x1024": Workload(5, "sweep_8192x4096x1024", 8192, 1024, "normal", 5,
+                                     (50.0, 50.0), n_out=4096, topk_channels=128,
+                                     out_dtype="f32"),
 }
 
 
