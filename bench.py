@@ -379,6 +379,32 @@ def main():
     q_gbs = q_bytes / (tq_ms * 1e-3) / 1e9
     q1_gbs = q_bytes / (tq1_ms * 1e-3) / 1e9
 
+    # ---------------------------------------------------------------- weight QDQ
+    # trainer-side fake quantization of the 14336 x 4096 weight (in-call s_t,
+    # bf16 out): 2 B read + 2 B written per element
+    _say("weight QDQ leg")
+    wq_src = torch.from_numpy(make_weight(wl).view(np.int16)).to(dev)
+    wq_out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    wq_ws_b = L.nvfp4_qdq_workspace_size(N, K)
+    wq_ws = torch.empty((wq_ws_b,), dtype=torch.uint8, device=dev)
+
+    def qdq_call():
+        q4._check(L.nvfp4_qdq(wq_src.data_ptr(), N, K, None, wq_out.data_ptr(), 1, None,
+                              wq_ws.data_ptr(), wq_ws_b, sp))
+    for _ in range(3):
+        qdq_call()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        qdq_call()
+    e1.record(stream)
+    e1.synchronize()
+    t_qdq = e0.elapsed_time(e1) / 10
+    qdq = {"workload": "weight 14336x4096 bf16 -> NVFP4 QDQ -> bf16, in-call tensor scale",
+           "ms": round(t_qdq, 4), "gbps": round(4.0 * N * K / (t_qdq * 1e-3) / 1e9, 1)}
+    del wq_src, wq_out, wq_ws
+
     # ---------------------------------------------------------------- MXFP4 leg
     # the same dense shape with MXFP4 operands on the scaled FP4 matrix
     # instruction (E8M0 per 32, no tensor scale), RAC k = 128 on bf16: the
@@ -554,6 +580,7 @@ def main():
         out["w4a4_only"] = wf
     if sweep is not None:
         out["ratio_sweep"] = sweep
+    out["weight_qdq"] = qdq
     if moe is not None:
         out["moe"] = moe
     if not a.no_cpu:

@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "Q4Error", "library_path", "lib",
-    "nvfp4_quantize", "mxfp4_quantize", "q4_select_channels", "q4_residual_gather",
+    "nvfp4_quantize", "mxfp4_quantize", "nvfp4_qdq", "q4_select_channels", "q4_residual_gather",
     "w4a4_gemm", "rac_gemm", "rac_gemm_eq21", "q4_moe_route", "q4_moe_sort", "q4_transpose_bf16",
     "q4_moe_pack_w13", "moe_w4a4_grouped_gemm", "moe_workspace_layout", "prepare_weight",
     "prepare_moe_weights", "NVFP4", "MXFP4", "OUT_F32", "OUT_BF16",
@@ -51,6 +51,8 @@ _SIGS = {
     "q4_quantize_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "nvfp4_quantize": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "mxfp4_quantize": (_I32, [_P, _I64, _I64, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "nvfp4_qdq_workspace_size": (_SZ, [_I64, _I64]),
+    "nvfp4_qdq": (_I32, [_P, _I64, _I64, _P, _P, _I32, _P, _P, _SZ, _P]),
     "q4_select_workspace_size": (_SZ, [_I64]),
     "q4_select_channels": (_I32, [_P, _I64, _I32, _P, _P, _SZ, _P]),
     "q4_residual_gather": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I64, _P]),
@@ -154,6 +156,21 @@ def nvfp4_quantize(x, tensor_scale_in=None, topk=0, want_scores=True, stream=Non
 
 def mxfp4_quantize(x, topk=0, want_scores=True, stream=None):
     return _quantize(MXFP4, x, None, topk, want_scores, stream)
+
+
+def nvfp4_qdq(x, tensor_scale_in=None, out_dtype=OUT_F32, stream=None, want_scale=False):
+    """Weight fake quantization: the values c sb s_t of nvfp4_quantize(x), fp32 or
+    bf16; with want_scale also the tensor scale used."""
+    x = _bf16(x)
+    rows, cols = x.shape
+    L = lib()
+    y = _empty((rows, cols), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, x.device)
+    ts = _empty((1,), torch.float32, x.device)
+    wsb = L.nvfp4_qdq_workspace_size(rows, cols)
+    ws = _empty((max(wsb, 1),), torch.uint8, x.device)
+    _check(L.nvfp4_qdq(_ptr(x), rows, cols, _ptr(tensor_scale_in), _ptr(y), out_dtype, _ptr(ts),
+                       _ptr(ws), wsb, _stream(stream)))
+    return (y, ts) if want_scale else y
 
 
 def q4_select_channels(chan_score, topk, stream=None):

@@ -121,6 +121,45 @@ q4_status_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_
                          chan_idx, workspace, workspace_bytes, stream, "mxfp4_quantize");
 }
 
+// Trainer-side weight fake quantization (QDQ): quantize as nvfp4_quantize,
+// then the dequantized values.  Workspace: the quantizer's, then codes,
+// scales and s_t.
+size_t nvfp4_qdq_workspace_size(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0) return 0;
+  return quantize_workspace_bytes(rows, cols) + align256((size_t)rows * (size_t)cols / 2) +
+         align256((size_t)rows * (size_t)cols / 16) + 256;
+}
+
+q4_status_t nvfp4_qdq(const uint16_t* x, int64_t rows, int64_t cols, const float* tensor_scale_in,
+                      void* y, int32_t y_dtype, float* tensor_scale_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const char* fn = "nvfp4_qdq";
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows >= kMaxDim || cols >= kMaxDim)
+    return fail(Q4_ESHAPE, "%s: need rows >= 0 and cols > 0 with cols %% 16 == 0", fn);
+  if (y_dtype != Q4_OUT_F32 && y_dtype != Q4_OUT_BF16) return fail(Q4_EINVAL, "%s: bad y_dtype", fn);
+  if (rows > 0) {
+    Q4_REQUIRE_PTR(y);
+  }
+  if (tensor_scale_out) Q4_REQUIRE_SCALAR(tensor_scale_out, 4);
+  const size_t need = nvfp4_qdq_workspace_size(rows, cols);
+  if (!workspace || workspace_bytes < need)
+    return fail(Q4_EWORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need,
+                workspace_bytes);
+  Q4_REQUIRE_PTR(workspace);
+  uint8_t* base = (uint8_t*)workspace;
+  const size_t qb = quantize_workspace_bytes(rows, cols);
+  uint8_t* codes = base + qb;
+  uint8_t* scales = codes + align256((size_t)rows * (size_t)cols / 2);
+  float* ts = tensor_scale_out ? tensor_scale_out
+                               : (float*)(scales + align256((size_t)rows * (size_t)cols / 16));
+  q4_status_t st = quantize_common(false, x, rows, cols, tensor_scale_in, codes, scales, ts,
+                                   nullptr, 0, nullptr, base, qb, stream, fn);
+  if (st != Q4_OK) return st;
+  return hip_status(launch_dequant_nvfp4(codes, scales, ts, rows, cols, y_dtype == Q4_OUT_BF16, y,
+                                         S(stream)),
+                    fn);
+}
+
 size_t q4_select_workspace_size(int64_t cols) {
   (void)cols;
   return 0;

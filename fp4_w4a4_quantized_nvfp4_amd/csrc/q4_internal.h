@@ -15,6 +15,10 @@ __global__ void tensor_scale_kernel(const float* ts_in, float* ts_out);
 
 // ---------------------------------------------------------------- quantizer
 size_t quantize_workspace_bytes(int64_t rows, int64_t cols);
+// values c sb s_t of an NVFP4 tensor [rows][cols] as fp32 or bf16 (one rounding)
+hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, const float* ts,
+                                int64_t rows, int64_t cols, int32_t y_bf16, void* y,
+                                hipStream_t stream);
 hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
                            const float* ts_in, uint8_t* codes, uint8_t* scales, float* ts_out,
                            double* chan_score, int32_t topk, int32_t* chan_idx, void* ws,

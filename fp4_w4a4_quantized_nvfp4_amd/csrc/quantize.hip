@@ -954,6 +954,77 @@ hipError_t launch_select(const double* scores, int64_t cols, int32_t topk, int32
   return hipGetLastError();
 }
 
+// ====================================================================== QDQ
+// Trainer-side weight fake quantization (QUADS section 3.2, Eq. 12): the value
+// each code stands for, c sb s_t, from codes, E4M3 scales and the tensor
+// scale.  One thread per 16-element block.  fp32 output: (c sb) s_t with one
+// rounding (c sb is exact in fp32).  bf16 output: the exact value (c sb has at
+// most 6 significant bits, s_t 24: exact in fp64) rounded once to bf16, by
+// round-to-odd to fp32 (24 >= 8 + 2 bits, so the second rounding is exact)
+// and then to nearest even.
+__global__ __launch_bounds__(256) void dequant_nvfp4_kernel(const uint2* __restrict__ codes,
+                                                            const uint8_t* __restrict__ scales,
+                                                            const float* __restrict__ ts,
+                                                            int64_t nblocks, int32_t y_bf16,
+                                                            void* __restrict__ y) {
+  const float st = ts[0];
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblocks;
+       b += (int64_t)gridDim.x * 256) {
+    const uint2 cw = codes[b];
+    const float s = e4m3_to_f32(scales[b]);
+    float v[16];
+    const uint32_t cws[2] = {cw.x, cw.y};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      f32x2v c2[4];
+      c2[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cws[q], 1.0f, 0);
+      c2[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cws[q], 1.0f, 1);
+      c2[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cws[q], 1.0f, 2);
+      c2[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cws[q], 1.0f, 3);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * q + 2 * j] = c2[j].x * s;
+        v[8 * q + 2 * j + 1] = c2[j].y * s;
+      }
+    }
+    if (y_bf16) {
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t h[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const double ex = (double)v[2 * i + u] * (double)st;
+          float f = __double2float_rz(ex);
+          if ((double)f != ex) f = __uint_as_float(__float_as_uint(f) | 1u);
+          h[u] = f32_to_bf16_rne(f);
+        }
+        o[i] = h[0] | (h[1] << 16);
+      }
+      uint4* dst = (uint4*)((uint16_t*)y + b * 16);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    } else {
+      float4* dst = (float4*)((float*)y + b * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dst[i] = make_float4(v[4 * i] * st, v[4 * i + 1] * st, v[4 * i + 2] * st, v[4 * i + 3] * st);
+    }
+  }
+}
+
+hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, const float* ts,
+                                int64_t rows, int64_t cols, int32_t y_bf16, void* y,
+                                hipStream_t stream) {
+  const int64_t nblocks = rows * (cols / 16);
+  if (nblocks == 0) return hipSuccess;
+  int64_t grid = (nblocks + 255) / 256;
+  grid = grid > 8192 ? 8192 : grid;
+  hipLaunchKernelGGL(dequant_nvfp4_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const uint2*)codes, scales, ts, nblocks, y_bf16, y);
+  return hipGetLastError();
+}
+
 hipError_t launch_residual_gather(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
                                   const uint8_t* codes, const uint8_t* scales, const float* ts,
                                   const int32_t* idx, int32_t k, uint16_t* R, int64_t ld_r,

@@ -111,6 +111,21 @@ q4_status_t mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_
                            uint8_t *scales, double *chan_score, int32_t topk, int32_t *chan_idx,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* Trainer-side weight fake quantization (QUADS section 3.2, Eq. 12: the weight
+ * QDQ operator whose scale layout and rounding match the rollout quantizer, so
+ * that trainer and rollout see the same discretized weight, Eq. 16):
+ *   y = c * sb * s_t of nvfp4_quantize(x) (the same kernels, so the codes,
+ *       scales and s_t are those nvfp4_quantize gives), rounded once to fp32
+ *       or to bf16 (y_dtype).
+ *   x, rows, cols, tensor_scale_in as nvfp4_quantize; y [rows][cols];
+ *   tensor_scale_out fp32 [1] (out) or NULL.
+ * The backward of the page's straight-through estimator (Eq. 13) is the
+ * identity on the gradient and needs no kernel. */
+size_t nvfp4_qdq_workspace_size(int64_t rows, int64_t cols);
+q4_status_t nvfp4_qdq(const uint16_t *x, int64_t rows, int64_t cols, const float *tensor_scale_in,
+                      void *y, int32_t y_dtype, float *tensor_scale_out, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* Channel selection alone (section 3.3 Eq. 24) from fp64 scores [cols]:
  * the topk largest, ties to the smaller index, written ascending to chan_idx. */
 size_t q4_select_workspace_size(int64_t cols);

@@ -47,6 +47,7 @@ from .quant import (  # noqa: F401
     channel_scores,
     dequantize,
     mxfp4_quantize,
+    nvfp4_qdq,
     nvfp4_quantize,
     nvfp4_tensor_scale,
     residual_gather,

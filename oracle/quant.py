@@ -221,6 +221,15 @@ def dequantize(q: QuantResult) -> np.ndarray:
     return block_values(q.codes, q.scales, q.fmt) * float(q.tensor_scale)
 
 
+def nvfp4_qdq(x_bits: np.ndarray, tensor_scale=None) -> np.ndarray:
+    """Trainer-side weight fake quantization (QUADS section 3.2, Eq. 12): the
+    QDQ operator whose scale layout and rounding match the rollout quantizer,
+    i.e. the values c sb s_t of this module's NVFP4 quantization, exact in fp64
+    (at most 6 + 24 significant bits).  Eq. 13's straight-through backward is
+    the identity on the gradient."""
+    return dequantize(nvfp4_quantize(x_bits, tensor_scale=tensor_scale))
+
+
 def channel_scores(resid: np.ndarray, tile_rows: int = SCORE_TILE_ROWS,
                    group_tiles: int = SCORE_GROUP_TILES) -> np.ndarray:
     """Sum over tokens of r^2 per channel, fp64, in the fixed three-level order."""

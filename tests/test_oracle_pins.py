@@ -378,6 +378,32 @@ def test_eq21_all_channels_error_bound(c1):
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
 
 
+def test_qdq_identity_and_idempotence():
+    """Weight QDQ (Eq. 12): (a) a tensor that is already E2M1 values times
+    power-of-two block scales, each block holding a +-6, comes back unchanged at
+    s_t = 1; (b) with a supplied power-of-two s_t and every block scale an E4M3
+    normal, QDQ of the (bf16-exact) QDQ output is the QDQ output."""
+    rng = np.random.default_rng(12)
+    grid = np.array(PAGE_GRID)
+    mag = rng.integers(0, 8, size=(24, 256))
+    mag[:, ::16] = 7
+    sign = np.where(rng.random((24, 256)) < 0.5, -1.0, 1.0)
+    sc = 2.0 ** rng.integers(-4, 4, size=(24, 16)).repeat(16, axis=1)
+    xv = grid[mag] * sign * sc
+    xb = bf16_bits_from_f32(xv.astype(np.float32))
+    assert np.array_equal(oracle.nvfp4_qdq(xb, tensor_scale=1.0), xv)
+    w = rng.standard_normal((32, 512)) * 3.0
+    wb = bf16_bits_from_f32(w.astype(np.float32))
+    st = 2.0 ** -6
+    q1 = oracle.nvfp4_qdq(wb, tensor_scale=st)
+    assert np.all(oracle.nvfp4_quantize(wb, tensor_scale=st).scales >= 8)   # normal E4M3 scales
+    q1b = bf16_bits_from_f32(q1.astype(np.float32))
+    assert np.array_equal(f32_from_bf16_bits(q1b).astype(np.float64), q1)   # exact in bf16
+    assert np.array_equal(oracle.nvfp4_qdq(q1b, tensor_scale=st), q1)
+    # and it is the dequantized rollout quantization, element for element
+    assert np.array_equal(q1, oracle.dequantize(oracle.nvfp4_quantize(wb, tensor_scale=st)))
+
+
 # ---------------------------------------------------------------- MXFP4
 def test_mxfp4_brute_force():
     rng = np.random.default_rng(5)
