@@ -479,12 +479,17 @@ struct Frag {
 
 // RSC: the compensation term carries its own scale (g.r_ts); a separate
 // instantiation so the plain kernels keep their register allocation
-template <bool TILED, bool GROUPED, int EPI, bool RSC = false>
+// MX: MXFP4 operands (E8M0 scale per 32 elements, no tensor scale) fed
+// straight from LDS to the scaled FP4 instruction, no decode (dense only)
+template <bool TILED, bool GROUPED, int EPI, bool RSC = false, bool MX = false>
 __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   static_assert(!(TILED && GROUPED), "grouped tiles take raw scales");
   static_assert(GROUPED || EPI == kEpiStore, "SwiGLU is a grouped epilogue");
-  constexpr int STAGE = big::STAGE<TILED>, B_SC_OFF = big::B_SC_OFF<TILED>;
-  constexpr int DMA_PER_CHUNK = big::DMA_PER_CHUNK<TILED>;
+  static_assert(!MX || (!TILED && !GROUPED && !RSC), "MXFP4: dense, raw scales");
+  // MX scale area: 4 E8M0 bytes per row per chunk
+  constexpr int STAGE = big::STAGE<TILED>;
+  constexpr int B_SC_OFF = MX ? A_SC_OFF + BM * 4 : big::B_SC_OFF<TILED>;
+  constexpr int DMA_PER_CHUNK = MX ? 10 : big::DMA_PER_CHUNK<TILED>;
   // one LDS object per stage, addressed with compile-time stage indices, so
   // the compiler can tell that reads of one stage do not wait for the
   // global -> LDS loads still filling another
@@ -540,7 +545,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   // and columns that are never stored).  Every per-lane offset is the same
   // for all chunks and all load instructions of one operand; the chunk and
   // the instruction's row block go into the scalar offset.
-  const uint32_t cstride = (uint32_t)(K / 2), sstride = (uint32_t)(K / 16);
+  const uint32_t cstride = (uint32_t)(K / 2), sstride = (uint32_t)(MX ? K / 32 : K / 16);
   auto rsrc = [](const void* base, int64_t bytes) {
     // every input is uniform; readfirstlane says so, so that the resource
     // stays in scalar registers
@@ -641,8 +646,17 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
                                                c_voff, so, 0, 0);
     }
   };
+  // MX: lane l of the wave loads the chunk's four E8M0 bytes of tile row
+  // 64 * wave + l (one dword per operand)
+  const uint32_t mxs_voff = (uint32_t)(64 * wave + lane) * sstride;
   auto issue_scales = [&](int kc, uint8_t* const sbase) {
-    if constexpr (TILED) {
+    if constexpr (MX) {
+      const uint32_t ks = (uint32_t)kc * (BK / 32);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rs, (lptr_t)(sbase + A_SC_OFF + wave * 256), 4,
+                                               mxs_voff, ks, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rs, (lptr_t)(sbase + B_SC_OFF + wave * 256), 4,
+                                               mxs_voff, ks, 0, 0);
+    } else if constexpr (TILED) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ast_rs, (lptr_t)(sbase + A_SC_OFF + wave * 1024), 16,
                                                t_voff, (uint32_t)(kc * g.a_rows_pad) << 4, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(bst_rs, (lptr_t)(sbase + B_SC_OFF + wave * 1024), 16,
@@ -873,7 +887,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   // beta / alpha = -s_R / s_A instead (one fp32 division), or beta itself
   // when alpha == 0.
   const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[ex] : 1.0f;
-  if (nrac > 0 && (alpha != 0.0f || RSC)) {
+  if (!MX && nrac > 0 && (alpha != 0.0f || RSC)) {
     int e = 0;
     float inv_m;
     if constexpr (RSC) {
@@ -891,7 +905,64 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   }
   const float y_scale = alpha != 0.0f ? alpha : 1.0f;
 
-  if (alpha != 0.0f) {
+  if constexpr (MX) {
+    // FP4 chunk kc in stage kc % 3.  Per chunk: the chunk has landed, every
+    // wave reads its fragments (two 64-element steps: lane half h supplies
+    // 32-element block 2 j + h of its row), a barrier frees the stage for
+    // chunk kc + 3, then 32 scaled FP4 MFMAs.
+    const int ra = wm * 128 + l32, rb = wn * 128 + l32;
+    uint32_t xa[2], xb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      xa[j] = (uint32_t)swz(ra, 2 * j + h);
+      xb[j] = (uint32_t)(B_CODE_OFF + swz(rb, 2 * j + h));
+    }
+    const uint32_t xsa = (uint32_t)(A_SC_OFF + ra * 4), xsb = (uint32_t)(B_SC_OFF + rb * 4);
+    auto mx_chunk = [&](int kc, uint8_t* const cur) {
+      if (kc > 0 || nrac > 0) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));
+        lds_barrier();
+      }
+      uint4 fa[2][4], fb[2][4];
+      uint32_t sa[4], sb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sa[q] = *(const uint32_t*)(cur + xsa + q * 128);
+        sb[q] = *(const uint32_t*)(cur + xsb + q * 128);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          fa[j][q] = *(const uint4*)(cur + xa[j] + q * Q_CODE);
+          fb[j][q] = *(const uint4*)(cur + xb[j] + q * Q_CODE);
+        }
+      lds_barrier();   // every wave is done with this stage
+      issue_chunk(min(kc + 3, nk - 1), cur);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int p = 2 * j + h;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni) {
+            const uint4 va = fa[j][mi], vb = fb[j][ni];
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                (i32x8v){(int)va.x, (int)va.y, (int)va.z, (int)va.w, 0, 0, 0, 0},
+                (i32x8v){(int)vb.x, (int)vb.y, (int)vb.z, (int)vb.w, 0, 0, 0, 0}, acc[mi][ni], 4,
+                4, 0, (int)(sa[mi] >> (8 * p)), 0, (int)(sb[ni] >> (8 * p)));
+          }
+      }
+    };
+    int kc = 0;
+    for (; kc + 3 <= nk; kc += 3) {
+      mx_chunk(kc, stage0);
+      mx_chunk(kc + 1, stage1);
+      mx_chunk(kc + 2, stage2);
+    }
+    if (kc < nk) mx_chunk(kc, stage0);
+    if (kc + 1 < nk) mx_chunk(kc + 1, stage1);
+  } else if (alpha != 0.0f) {
     // FP4 chunk kc is schedule chunk nrac + kc, in stage kc % 3
     if (nrac > 0) {   // FP4 chunk 0 has landed
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));
@@ -1093,6 +1164,12 @@ hipError_t launch_t(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
 hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
   const bool fullk = (g.K % BK) == 0;
   const bool grouped = g.tiles != nullptr;
+  if (g.mx && !grouped && fullk && g.epilogue == kEpiStore && g.M >= 512 && g.N >= 512) {
+    const int64_t nb = ((g.M + big::BM - 1) / big::BM) * ((g.N + big::BN - 1) / big::BN);
+    hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<false, false, kEpiStore, false, true>),
+                       dim3((unsigned)nb), dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
   if (g.mx) {
     if (fullk)
       return grouped ? launch_t<true, true, true>(g, max_mtiles, stream)

@@ -166,12 +166,15 @@ def test_mxfp4_rac_gemm(M, N, K, k):
     _check_rac(xb, wb, k, 1, fmt="mx")
 
 
-def test_mxfp4_exact_special_case():
+@pytest.mark.parametrize("M,N,K", [(96, 160, 256), (512, 768, 512), (600, 520, 1024)],
+                         ids=["small_tile", "large_tile", "large_tile_ragged"])
+def test_mxfp4_exact_special_case(M, N, K):
     """Power-of-two scales and E2M1 values: every partial sum is exact, so the
-    scaled-MFMA product must equal the integer result bit for bit."""
+    scaled-MFMA product must equal the integer result bit for bit (both the
+    256 x 128 and the 256 x 256 kernels)."""
     m = q4()
-    rng = np.random.default_rng(17)
-    M, N, K = 96, 160, 256
+    say(f"mxfp4 exact special case {M}x{N}x{K}")
+    rng = np.random.default_rng(17 + M)
     def operand(rows):
         e = rng.integers(-2, 3, size=(rows, K // 32))
         mag = rng.integers(0, 8, size=(rows, K))
