@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 # (fetch x 2.00, write x 1.00); valid only for the kernel source it was taken on
 # (the recorded source's NVFP4 instantiations compile to the same instructions
 # as those the counters were taken on)
-TRAFFIC = {"gemm_src_sha256": "61a344d385865d3b95cefb9cbcd1ba3a5dc35ef527354a9dc2788a29b553f387",
+TRAFFIC = {"gemm_src_sha256": "e97b33b9b33f763481eb608fd1ac67552e5409c497f48216cca3d5ded87bd41c",
            "fetch_kib": 242328.6, "fetch_scale": 2.0, "write_kib": 265216.0, "write_scale": 1.0}
 
 

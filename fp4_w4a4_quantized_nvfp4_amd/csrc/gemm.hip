@@ -906,10 +906,16 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   const float y_scale = alpha != 0.0f ? alpha : 1.0f;
 
   if constexpr (MX) {
-    // FP4 chunk kc in stage kc % 3.  Per chunk: the chunk has landed, every
-    // wave reads its fragments (two 64-element steps: lane half h supplies
-    // 32-element block 2 j + h of its row), a barrier frees the stage for
-    // chunk kc + 3, then 32 scaled FP4 MFMAs.
+    // A fourth stage (the MXFP4 stage is smaller, and a chunk's 32 MFMAs are
+    // a quarter of an NVFP4 chunk's work, so more of the load latency needs
+    // cover): chunks 0..2 are in stages 0..2 (the RAC part or the prologue
+    // put them there), chunk 3 goes to stage 3 now, and FP4 chunk kc lives
+    // in stage kc % 4.  Per chunk: the chunk has landed, every wave reads
+    // its fragments (two 64-element steps: lane half h supplies 32-element
+    // block 2 j + h of its row), a barrier frees the stage for chunk kc + 4,
+    // then 32 scaled FP4 MFMAs.
+    __shared__ __attribute__((aligned(16))) uint8_t stage3[STAGE];
+    issue_chunk(min(3, nk - 1), stage3);
     const int ra = wm * 128 + l32, rb = wn * 128 + l32;
     uint32_t xa[2], xb[2];
 #pragma unroll
@@ -919,10 +925,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     }
     const uint32_t xsa = (uint32_t)(A_SC_OFF + ra * 4), xsb = (uint32_t)(B_SC_OFF + rb * 4);
     auto mx_chunk = [&](int kc, uint8_t* const cur) {
-      if (kc > 0 || nrac > 0) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));
-        lds_barrier();
-      }
+      // chunks kc .. kc + 3 in flight: wait until chunk kc has landed
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DMA_PER_CHUNK));
+      lds_barrier();
       uint4 fa[2][4], fb[2][4];
       uint32_t sa[4], sb[4];
 #pragma unroll
@@ -938,7 +943,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
           fb[j][q] = *(const uint4*)(cur + xb[j] + q * Q_CODE);
         }
       lds_barrier();   // every wave is done with this stage
-      issue_chunk(min(kc + 3, nk - 1), cur);
+      issue_chunk(min(kc + 4, nk - 1), cur);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int p = 2 * j + h;
@@ -955,13 +960,15 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
       }
     };
     int kc = 0;
-    for (; kc + 3 <= nk; kc += 3) {
+    for (; kc + 4 <= nk; kc += 4) {
       mx_chunk(kc, stage0);
       mx_chunk(kc + 1, stage1);
       mx_chunk(kc + 2, stage2);
+      mx_chunk(kc + 3, stage3);
     }
     if (kc < nk) mx_chunk(kc, stage0);
     if (kc + 1 < nk) mx_chunk(kc + 1, stage1);
+    if (kc + 2 < nk) mx_chunk(kc + 2, stage2);
   } else if (alpha != 0.0f) {
     // FP4 chunk kc is schedule chunk nrac + kc, in stage kc % 3
     if (nrac > 0) {   // FP4 chunk 0 has landed

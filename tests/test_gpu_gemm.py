@@ -154,7 +154,8 @@ def test_dense_prefill_workload_sampled():
 
 
 @pytest.mark.parametrize("M,N,K,k", [(64, 512, 512, 16), (300, 200, 96, 20), (513, 640, 1024, 64),
-                                     (1000, 1300, 512, 64)])
+                                     (1000, 1300, 512, 64), (512, 520, 640, 32),
+                                     (700, 512, 384, 100)])
 def test_mxfp4_rac_gemm(M, N, K, k):
     """MXFP4 operands on the scaled FP4 matrix instruction, RAC on bf16."""
     rng = np.random.default_rng(M * 7 + K)
@@ -166,8 +167,10 @@ def test_mxfp4_rac_gemm(M, N, K, k):
     _check_rac(xb, wb, k, 1, fmt="mx")
 
 
-@pytest.mark.parametrize("M,N,K", [(96, 160, 256), (512, 768, 512), (600, 520, 1024)],
-                         ids=["small_tile", "large_tile", "large_tile_ragged"])
+@pytest.mark.parametrize("M,N,K", [(96, 160, 256), (512, 768, 512), (600, 520, 1024),
+                                   (512, 512, 384), (520, 600, 640)],
+                         ids=["small_tile", "large_tile", "large_tile_ragged", "large_tile_3_chunks",
+                              "large_tile_5_chunks"])
 def test_mxfp4_exact_special_case(M, N, K):
     """Power-of-two scales and E2M1 values: every partial sum is exact, so the
     scaled-MFMA product must equal the integer result bit for bit (both the
