@@ -496,9 +496,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t stage0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t stage2[STAGE];
-  // dense NVFP4 with four compensation chunks (k = 97 .. 128): a fourth stage
-  // holds the fourth of them, so that all four are in flight at the start
-  constexpr bool RAC4 = TILED && !GROUPED && !MX;
+  // NVFP4 with one to four compensation chunks (k <= 128): a fourth stage
+  // lets all of them and the first FP4 chunks be in flight at the start
+  constexpr bool RAC4 = !MX;
   __shared__ __attribute__((aligned(16))) uint8_t stage3r[RAC4 ? STAGE : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -820,11 +820,21 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   // needs no head, and only the cheap RAC part has one.  Prologue: chunks
   // 0..2 in flight.
   const int roff = (3 - nrac % 3) % 3;
-  // four compensation chunks on four stages: RAC chunk j in stage j, FP4
-  // chunks 0..2 follow into stages 0..2 (as with roff == 0)
-  const bool rac4 = RAC4 && nrac == 4;
+  // one to four compensation chunks on four stages: schedule chunks 0..3
+  // are issued at once, RAC chunk j in stage (j + 4 - nrac) % 4 and FP4
+  // chunk f < 4 - nrac in stage f, so that FP4 chunk f always lands in stage
+  // f % 3 and the fourth stage holds the last RAC chunk
+  const bool rac4 = RAC4 && nrac >= 1 && nrac <= 4;
   if (rac4) {
-    issue_any(0, stage0); issue_any(1, stage1); issue_any(2, stage2); issue_any(3, stage3r);
+    if (nrac == 1) {
+      issue_any(0, stage3r); issue_any(1, stage0); issue_any(2, stage1); issue_any(3, stage2);
+    } else if (nrac == 2) {
+      issue_any(0, stage2); issue_any(1, stage3r); issue_any(2, stage0); issue_any(3, stage1);
+    } else if (nrac == 3) {
+      issue_any(0, stage1); issue_any(1, stage2); issue_any(2, stage3r); issue_any(3, stage0);
+    } else {
+      issue_any(0, stage0); issue_any(1, stage1); issue_any(2, stage2); issue_any(3, stage3r);
+    }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DMA_PER_CHUNK));   // chunk 0 has landed
   } else {
     if (roff == 0) {
@@ -874,8 +884,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
                 acc[mi][ni], 0, 0, 0);
     };
     // the four-stage form: each chunk waits with three behind it and refills
-    // its stage with FP4 chunk j (schedule chunk j + 4); the fourth stage is
-    // not refilled, which leaves FP4 chunks 0..2 in flight as below
+    // its stage with schedule chunk j + 4 (the FP4 chunk that belongs
+    // there); the fourth stage is not refilled, which leaves FP4 chunks 0..2
+    // in flight as below
     auto rac_chunk4 = [&](int jr, uint8_t* const sb, bool refill) {
       if (jr > 0) {
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DMA_PER_CHUNK));
@@ -902,10 +913,21 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
                 acc[mi][ni], 0, 0, 0);
     };
     if (rac4) {
-      rac_chunk4(0, stage0, true);
-      rac_chunk4(1, stage1, true);
-      rac_chunk4(2, stage2, true);
-      rac_chunk4(3, stage3r, false);
+      if (nrac == 1) {
+        rac_chunk4(0, stage3r, false);
+      } else if (nrac == 2) {
+        rac_chunk4(0, stage2, true);
+        rac_chunk4(1, stage3r, false);
+      } else if (nrac == 3) {
+        rac_chunk4(0, stage1, true);
+        rac_chunk4(1, stage2, true);
+        rac_chunk4(2, stage3r, false);
+      } else {
+        rac_chunk4(0, stage0, true);
+        rac_chunk4(1, stage1, true);
+        rac_chunk4(2, stage2, true);
+        rac_chunk4(3, stage3r, false);
+      }
     } else {
       int jr = 0;
       if (roff == 1) {   // nrac % 3 == 2

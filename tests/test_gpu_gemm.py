@@ -111,7 +111,9 @@ def test_k0_equals_w4a4():
 
 @pytest.mark.parametrize("M,N,K,k", [(300, 200, 96, 20), (1, 1, 32, 1), (257, 129, 160, 32),
                                      (513, 384, 1024, 100), (600, 520, 160, 24),
-                                     (1000, 1300, 512, 64), (512, 512, 4096, 128)])
+                                     (1000, 1300, 512, 64), (512, 512, 4096, 128),
+                                     (512, 768, 1024, 80), (520, 512, 512, 17),
+                                     (640, 520, 1024, 200)])
 def test_ragged_shapes(M, N, K, k):
     rng = np.random.default_rng(M + N + K)
     xb = _bits(rng.standard_t(3, size=(M, K)).astype(np.float32))
