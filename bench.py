@@ -36,8 +36,8 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 # HBM bytes per launch of the dense GEMM kernel from rocprofv3 --pmc FETCH_SIZE /
 # WRITE_SIZE (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives
 # (fetch x 2.00, write x 1.00); valid only for the kernel source it was taken on
-TRAFFIC = {"gemm_src_sha256": "7b446dd7aa3cc631a821a4fd9c6a45b5285ffa6422cf122ec3ef8429b0ed77b8",
-           "fetch_kib": 242303.0, "fetch_scale": 2.0, "write_kib": 263424.0, "write_scale": 1.0}
+TRAFFIC = {"gemm_src_sha256": "e97b33b9b33f763481eb608fd1ac67552e5409c497f48216cca3d5ded87bd41c",
+           "fetch_kib": 242328.6, "fetch_scale": 2.0, "write_kib": 265216.0, "write_scale": 1.0}
 
 
 def _args():

@@ -496,10 +496,6 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t stage0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t stage2[STAGE];
-  // NVFP4 with one to four compensation chunks (k <= 128): a fourth stage
-  // lets all of them and the first FP4 chunks be in flight at the start
-  constexpr bool RAC4 = !MX;
-  __shared__ __attribute__((aligned(16))) uint8_t stage3r[RAC4 ? STAGE : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -820,32 +816,14 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   // needs no head, and only the cheap RAC part has one.  Prologue: chunks
   // 0..2 in flight.
   const int roff = (3 - nrac % 3) % 3;
-  // one to four compensation chunks on four stages: schedule chunks 0..3
-  // are issued at once, RAC chunk j in stage (j + 4 - nrac) % 4 and FP4
-  // chunk f < 4 - nrac in stage f, so that FP4 chunk f always lands in stage
-  // f % 3 and the fourth stage holds the last RAC chunk
-  const bool rac4 = RAC4 && nrac >= 1 && nrac <= 4;
-  if (rac4) {
-    if (nrac == 1) {
-      issue_any(0, stage3r); issue_any(1, stage0); issue_any(2, stage1); issue_any(3, stage2);
-    } else if (nrac == 2) {
-      issue_any(0, stage2); issue_any(1, stage3r); issue_any(2, stage0); issue_any(3, stage1);
-    } else if (nrac == 3) {
-      issue_any(0, stage1); issue_any(1, stage2); issue_any(2, stage3r); issue_any(3, stage0);
-    } else {
-      issue_any(0, stage0); issue_any(1, stage1); issue_any(2, stage2); issue_any(3, stage3r);
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DMA_PER_CHUNK));   // chunk 0 has landed
+  if (roff == 0) {
+    issue_any(0, stage0); issue_any(1, stage1); issue_any(2, stage2);
+  } else if (roff == 1) {
+    issue_any(0, stage1); issue_any(1, stage2); issue_any(2, stage0);
   } else {
-    if (roff == 0) {
-      issue_any(0, stage0); issue_any(1, stage1); issue_any(2, stage2);
-    } else if (roff == 1) {
-      issue_any(0, stage1); issue_any(1, stage2); issue_any(2, stage0);
-    } else {
-      issue_any(0, stage2); issue_any(1, stage0); issue_any(2, stage1);
-    }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));   // chunk 0 has landed
+    issue_any(0, stage2); issue_any(1, stage0); issue_any(2, stage1);
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));   // chunk 0 has landed
   lds_barrier();
 
   // RAC first, into the zeroed accumulators: RAC chunk jr in stage
@@ -883,66 +861,19 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
                 __builtin_bit_cast(bf16x8v, fa[s2][mi]), __builtin_bit_cast(bf16x8v, fb[s2][ni]),
                 acc[mi][ni], 0, 0, 0);
     };
-    // the four-stage form: each chunk waits with three behind it and refills
-    // its stage with schedule chunk j + 4 (the FP4 chunk that belongs
-    // there); the fourth stage is not refilled, which leaves FP4 chunks 0..2
-    // in flight as below
-    auto rac_chunk4 = [&](int jr, uint8_t* const sb, bool refill) {
-      if (jr > 0) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DMA_PER_CHUNK));
-        lds_barrier();
-      }
-      uint4 fa[2][4], fb[2][4];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          fa[s2][q] = *(const uint4*)(sb + ra_off[s2] + q * Q_CODE);
-          fb[s2][q] = *(const uint4*)(sb + rb_off[s2] + q * Q_CODE);
-        }
-      lds_barrier();   // every wave is done with this stage
-      if (refill) issue_any(jr + 4, sb);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8v, fa[s2][mi]), __builtin_bit_cast(bf16x8v, fb[s2][ni]),
-                acc[mi][ni], 0, 0, 0);
-    };
-    if (rac4) {
-      if (nrac == 1) {
-        rac_chunk4(0, stage3r, false);
-      } else if (nrac == 2) {
-        rac_chunk4(0, stage2, true);
-        rac_chunk4(1, stage3r, false);
-      } else if (nrac == 3) {
-        rac_chunk4(0, stage1, true);
-        rac_chunk4(1, stage2, true);
-        rac_chunk4(2, stage3r, false);
-      } else {
-        rac_chunk4(0, stage0, true);
-        rac_chunk4(1, stage1, true);
-        rac_chunk4(2, stage2, true);
-        rac_chunk4(3, stage3r, false);
-      }
-    } else {
-      int jr = 0;
-      if (roff == 1) {   // nrac % 3 == 2
-        rac_chunk(0, stage1);
-        rac_chunk(1, stage2);
-        jr = 2;
-      } else if (roff == 2) {   // nrac % 3 == 1
-        rac_chunk(0, stage2);
-        jr = 1;
-      }
-      for (; jr < nrac; jr += 3) {
-        rac_chunk(jr, stage0);
-        rac_chunk(jr + 1, stage1);
-        rac_chunk(jr + 2, stage2);
-      }
+    int jr = 0;
+    if (roff == 1) {   // nrac % 3 == 2
+      rac_chunk(0, stage1);
+      rac_chunk(1, stage2);
+      jr = 2;
+    } else if (roff == 2) {   // nrac % 3 == 1
+      rac_chunk(0, stage2);
+      jr = 1;
+    }
+    for (; jr < nrac; jr += 3) {
+      rac_chunk(jr, stage0);
+      rac_chunk(jr + 1, stage1);
+      rac_chunk(jr + 2, stage2);
     }
   }
 
