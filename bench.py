@@ -76,7 +76,7 @@ def _moe_legs(q4, L, dev, stream, sp, iters=10):
     import torch
     from workloads import WORKLOADS, make_activations, make_logits
     res = {}
-    for name, fmts in (("moe_prefill_8192", (q4.NVFP4,)), ("moe_decode_256", (q4.NVFP4, q4.MXFP4))):
+    for name, fmts in (("moe_prefill_8192", (q4.NVFP4, q4.MXFP4)), ("moe_decode_256", (q4.NVFP4, q4.MXFP4))):
         wl = WORKLOADS[name]
         T, H, E, F, topk, k = wl.rows, wl.cols, wl.experts, wl.ffn, wl.route_topk, wl.topk_channels
         _say(f"{name}: expert weights")

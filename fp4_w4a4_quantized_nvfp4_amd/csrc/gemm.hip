@@ -485,7 +485,7 @@ template <bool TILED, bool GROUPED, int EPI, bool RSC = false, bool MX = false>
 __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   static_assert(!(TILED && GROUPED), "grouped tiles take raw scales");
   static_assert(GROUPED || EPI == kEpiStore, "SwiGLU is a grouped epilogue");
-  static_assert(!MX || (!TILED && !GROUPED && !RSC), "MXFP4: dense, raw scales");
+  static_assert(!MX || (!TILED && !RSC), "MXFP4: raw scales, no scaled compensation");
   // MX scale area: 4 E8M0 bytes per row per chunk
   constexpr int STAGE = big::STAGE<TILED>;
   constexpr int B_SC_OFF = MX ? A_SC_OFF + BM * 4 : big::B_SC_OFF<TILED>;
@@ -647,13 +647,15 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     }
   };
   // MX: lane l of the wave loads the chunk's four E8M0 bytes of tile row
-  // 64 * wave + l (one dword per operand)
+  // 64 * wave + l (one dword per operand); grouped A rows through a_src
   const uint32_t mxs_voff = (uint32_t)(64 * wave + lane) * sstride;
+  uint32_t mxa_voff = mxs_voff;
+  if constexpr (MX && GROUPED) mxa_voff = (uint32_t)a_src(64 * wave + lane) * sstride;
   auto issue_scales = [&](int kc, uint8_t* const sbase) {
     if constexpr (MX) {
       const uint32_t ks = (uint32_t)kc * (BK / 32);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rs, (lptr_t)(sbase + A_SC_OFF + wave * 256), 4,
-                                               mxs_voff, ks, 0, 0);
+                                               mxa_voff, ks, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rs, (lptr_t)(sbase + B_SC_OFF + wave * 256), 4,
                                                mxs_voff, ks, 0, 0);
     } else if constexpr (TILED) {
@@ -1171,6 +1173,17 @@ hipError_t launch_t(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
 hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
   const bool fullk = (g.K % BK) == 0;
   const bool grouped = g.tiles != nullptr;
+  if (g.mx && grouped && fullk && g.N % big::BN == 0 && g.K >= 1024) {
+    const int64_t nb = (max_mtiles * (g.N / big::BN) + 7) / 8 * 8;
+    if (nb == 0) return hipSuccess;
+    if (g.epilogue == kEpiSwiGLU)
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<false, true, kEpiSwiGLU, false, true>),
+                         dim3((unsigned)nb), dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<false, true, kEpiStore, false, true>),
+                         dim3((unsigned)nb), dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
   if (g.mx && !grouped && fullk && g.epilogue == kEpiStore && g.M >= 512 && g.N >= 512) {
     const int64_t nb = ((g.M + big::BM - 1) / big::BM) * ((g.N + big::BN - 1) / big::BN);
     hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<false, false, kEpiStore, false, true>),

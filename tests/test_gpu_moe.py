@@ -190,5 +190,8 @@ def test_moe_decode_workload_sampled(fmt):
     _sampled_full("moe_decode_256", fmt=fmt)
 
 
-def test_moe_prefill_workload_sampled():
-    _sampled_full("moe_prefill_8192", n_experts_checked=2)
+@pytest.mark.parametrize("fmt", [0, 1], ids=["nvfp4", "mxfp4"])
+def test_moe_prefill_workload_sampled(fmt):
+    """8192 tokens, 128 experts of 2048 -> 2 x 768 -> 2048, top-8, as NVFP4 and as
+    MXFP4 (W13 on the grouped 256 x 256 kernel in both formats)."""
+    _sampled_full("moe_prefill_8192", n_experts_checked=2, fmt=fmt)
