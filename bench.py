@@ -38,7 +38,7 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 # (fetch x 2.00, write x 1.00); valid only for the kernel source it was taken on
 # (recorded here for a source whose NVFP4 instantiations assemble to the same
 # instructions as the one the counters were taken on)
-TRAFFIC = {"gemm_src_sha256": "158e05612b58b6c4b2a50cbc7e14620879e50f290d5470a879b7bafb636233fb",
+TRAFFIC = {"gemm_src_sha256": "0595cd58d7ae3513a81a9c685ad0694f870698dda855420a486988df3f3f25c3",
            "fetch_kib": 242328.6, "fetch_scale": 2.0, "write_kib": 265216.0, "write_scale": 1.0}
 
 

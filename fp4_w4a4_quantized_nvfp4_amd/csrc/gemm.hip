@@ -1173,7 +1173,10 @@ hipError_t launch_t(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
 hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
   const bool fullk = (g.K % BK) == 0;
   const bool grouped = g.tiles != nullptr;
-  if (g.mx && grouped && fullk && g.N % big::BN == 0 && g.K >= 1024) {
+  // MXFP4 grouped: the 256 x 256 tiles win from K = 512 on (no decode, so a
+  // tile's fixed cost is smaller than on the NVFP4 path, which keeps its
+  // 256 x 128 tiles below K = 1024)
+  if (g.mx && grouped && fullk && g.N % big::BN == 0 && g.K >= 512) {
     const int64_t nb = (max_mtiles * (g.N / big::BN) + 7) / 8 * 8;
     if (nb == 0) return hipSuccess;
     if (g.epilogue == kEpiSwiGLU)
