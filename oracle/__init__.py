@@ -23,10 +23,9 @@ Learning for MoE via QUantization-error Alignment across Dual Sides"):
   (page thelatestinai.com/papers/2607.15810) with the OCP power-of-two scale.
 
 Every rounding decision is taken by comparing exact fp64 products (all
-operands have few significant bits), never by a rounded quotient.  Sums of
-squares follow a fixed order that is part of the definition (rows ascending
-inside tiles of 32 rows, tiles ascending inside groups of 8 tiles, groups
-ascending).
+operands have few significant bits), never by a rounded quotient.  Channel
+scores are exact sums of squares rounded once to fp64, so no summation order
+enters them.
 """
 from .formats import (  # noqa: F401
     E2M1_MAGNITUDES,
@@ -40,8 +39,6 @@ from .formats import (  # noqa: F401
     f64_to_f32,
 )
 from .quant import (  # noqa: F401
-    SCORE_GROUP_TILES,
-    SCORE_TILE_ROWS,
     QuantResult,
     block_values,
     channel_scores,

@@ -56,9 +56,13 @@ def moe_sort(idx: np.ndarray, E: int):
 
 
 def swiglu_bf16(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
+    """h = RN_bf16(silu(gate) * up), silu(g) = g / (1 + exp(-g)), computed in
+    fp64 and rounded once (the SwiGLU expert block; the page does not spell
+    the block out, this is its standard form)."""
     g = np.asarray(gate, dtype=np.float64)
     u = np.asarray(up, dtype=np.float64)
-    return f64_to_bf16_bits(g / (1.0 + np.exp(-g)) * u)
+    with np.errstate(over="ignore"):          # exp(-g) = inf gives silu = -0
+        return f64_to_bf16_bits(g / (1.0 + np.exp(-g)) * u)
 
 
 def _rows(q: QuantResult, rows: np.ndarray) -> QuantResult:
@@ -67,7 +71,7 @@ def _rows(q: QuantResult, rows: np.ndarray) -> QuantResult:
 
 
 def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
-              wq13=None, wq2=None, fmt: str = "nvfp4"):
+              wq13=None, wq2=None, fmt: str = "nvfp4", Sx_override=None, Sh_override=None):
     """Whole expert layer; returns a dict of every intermediate (fp64 unless noted).
 
     x_bits [T, H] bf16 bits; idx/p from ``moe_route``; w13_bits [E, 2F, H] and
@@ -75,7 +79,10 @@ def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
     oracle's own h (bf16 bits [T*topk, F], sorted order) before the second
     quantization, for stage-wise comparison.  ``wq13``/``wq2`` are optional
     pre-quantized expert weights (lists of QuantResult).  ``fmt`` selects the
-    activation and weight format ("nvfp4" or "mxfp4").
+    activation and weight format ("nvfp4" or "mxfp4").  ``Sx_override`` /
+    ``Sh_override`` replace the selected channel sets of the two sites (a set
+    already validated against this oracle's scores, where several sets are
+    correct at a near-tie).
     """
     quant = nvfp4_quantize if fmt == "nvfp4" else mxfp4_quantize
     T, H = x_bits.shape
@@ -86,7 +93,7 @@ def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
     tok = perm // k
     qx = quant(x_bits)
     sx = channel_scores(qx.resid)
-    Sx = select_topk(sx, rac_k)
+    Sx = select_topk(sx, rac_k) if Sx_override is None else np.asarray(Sx_override)
     Rx = residual_gather(qx.resid, Sx)
     if wq13 is None:
         wq13 = [quant(w13_bits[e]) for e in range(E)]
@@ -103,7 +110,7 @@ def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
     h_used = h if h_override is None else np.asarray(h_override, dtype=np.uint16)
     qh = quant(h_used)
     sh = channel_scores(qh.resid)
-    Sh = select_topk(sh, rac_k)
+    Sh = select_topk(sh, rac_k) if Sh_override is None else np.asarray(Sh_override)
     Rh = residual_gather(qh.resid, Sh)
     out = np.zeros((T * k, H), dtype=np.float64)
     for e in range(E):

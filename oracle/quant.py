@@ -25,12 +25,11 @@ Definitions (QUADS page, arXiv 2607.15810):
 * Section 3.3, Eq. 20: the quantization error.  This oracle keeps the
   residual r = x - dequant(quant(x)) = -(Eq. 20) rounded once to fp32.
 * Section 3.3, Eq. 23: s_j = ||r[:, j]||_2 over the current token batch.  The
-  squared norm is accumulated in fp64 (each r^2 is exact in fp64) in a fixed
-  three-level order: rows ascending inside tiles of SCORE_TILE_ROWS rows; tile
-  sums ascending inside groups of SCORE_GROUP_TILES tiles; group sums
-  ascending.  Every level starts from zero.  The order is part of the
-  definition so that the scores, and the selection that depends on them, have
-  one exact value.
+  oracle's score is s_j^2 = sum_i r_ij^2 as the fp64 value nearest to the
+  exact real sum (ties to even): each r_ij is an fp32 value m 2^e (integer m <
+  2^24), so the sum is accumulated exactly in integers and rounded once.  No
+  summation order enters the definition; any fp64 summation of the same terms
+  lies within (rows - 1) 2^-53 relative of it.
 * Section 3.3, Eq. 24: the selected set S is the k channels with the largest
   score (ties -> smaller channel index), listed in ascending channel order.
   k is an absolute count.
@@ -48,9 +47,6 @@ import dataclasses
 import numpy as np
 
 from .formats import E2M1_MAGNITUDES, E4M3_VALUES, bf16_bits_to_f64, f32_to_bf16_bits
-
-SCORE_TILE_ROWS = 32
-SCORE_GROUP_TILES = 8
 
 _E2M1 = np.array(E2M1_MAGNITUDES, dtype=np.float64)
 # midpoints between consecutive E2M1 magnitudes and whether a tie goes up
@@ -223,29 +219,57 @@ def dequantize(q: QuantResult) -> np.ndarray:
 
 def nvfp4_qdq(x_bits: np.ndarray, tensor_scale=None) -> np.ndarray:
     """Trainer-side weight fake quantization (QUADS section 3.2, Eq. 12): the
-    QDQ operator whose scale layout and rounding match the rollout quantizer,
-    i.e. the values c sb s_t of this module's NVFP4 quantization, exact in fp64
-    (at most 6 + 24 significant bits).  Eq. 13's straight-through backward is
-    the identity on the gradient."""
+    trainer quantizes and dequantizes its weight with the rollout quantizer's
+    own block layout and rounding, so the values are c sb s_t of this module's
+    NVFP4 quantization, exact in fp64 (at most 6 + 24 significant bits).
+    Eq. 13's straight-through backward is the identity on the gradient."""
     return dequantize(nvfp4_quantize(x_bits, tensor_scale=tensor_scale))
 
 
-def channel_scores(resid: np.ndarray, tile_rows: int = SCORE_TILE_ROWS,
-                   group_tiles: int = SCORE_GROUP_TILES) -> np.ndarray:
-    """Sum over tokens of r^2 per channel, fp64, in the fixed three-level order."""
-    r2 = resid.astype(np.float64) ** 2                  # exact: 24-bit mantissa squared
-    M, K = r2.shape
-    total = np.zeros(K, dtype=np.float64)
-    group_rows = tile_rows * group_tiles
-    for g0 in range(0, M, group_rows):
-        group = np.zeros(K, dtype=np.float64)
-        for t0 in range(g0, min(M, g0 + group_rows), tile_rows):
-            tile = np.zeros(K, dtype=np.float64)
-            for i in range(t0, min(M, t0 + tile_rows)):
-                tile += r2[i]                           # rows ascending
-            group += tile                               # tiles ascending
-        total += group                                  # groups ascending
-    return total
+def channel_scores(resid: np.ndarray) -> np.ndarray:
+    """s_j^2 = sum_i r_ij^2 per channel j (Eq. 23 squared): the fp64 value
+    nearest to the exact sum.
+
+    Every fp32 residual is m * 2^e with an integer 0 <= m < 2^24 and
+    e = max(E, 1) - 150 (E the biased exponent field), so r^2 = m^2 * 2^(2e)
+    with m^2 < 2^48.  The squares are binned by e per channel; within a bin
+    the integer m^2 values are summed exactly (split in two 24-bit halves so
+    each half's running sum stays an integer below 2^53 for fewer than 2^29
+    rows); the bins are then combined as one Python integer and converted to
+    fp64 with a single correctly rounded conversion.
+    """
+    r = np.ascontiguousarray(resid, dtype=np.float32)
+    M, K = r.shape
+    NE = 254                                   # e = -149 .. 104
+    hi = np.zeros(K * NE, dtype=np.float64)
+    lo = np.zeros(K * NE, dtype=np.float64)
+    col = np.arange(K, dtype=np.int64)[None, :] * NE
+    for i0 in range(0, M, 1024):
+        bits = r[i0:i0 + 1024].view(np.uint32)
+        ef = ((bits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int64)
+        mant = (bits & np.uint32(0x7FFFFF)).astype(np.int64)
+        m = np.where(ef > 0, mant | 0x800000, mant)
+        sq = m * m                             # < 2^48, exact in int64
+        b = (col + (np.maximum(ef, 1) - 1)).ravel()
+        hi += np.bincount(b, weights=(sq >> 24).ravel().astype(np.float64), minlength=K * NE)
+        lo += np.bincount(b, weights=(sq & 0xFFFFFF).ravel().astype(np.float64), minlength=K * NE)
+    hi = hi.reshape(K, NE)
+    lo = lo.reshape(K, NE)
+    out = np.zeros(K, dtype=np.float64)
+    for j in range(K):
+        nz = np.nonzero((hi[j] != 0) | (lo[j] != 0))[0]
+        if nz.size == 0:
+            continue
+        base = int(nz[0])
+        total = 0
+        for t in nz:                            # bin t holds multiples of 2^(2(t - 149))
+            c = (int(hi[j, t]) << 24) + int(lo[j, t])
+            total += c << (2 * (int(t) - base))
+        # one rounding: Python's int -> float conversion and int / int true
+        # division are both correctly rounded (nearest, ties to even)
+        sh = 2 * (base - 149)
+        out[j] = float(total << sh) if sh >= 0 else total / (1 << -sh)
+    return out
 
 
 def select_topk(scores: np.ndarray, k: int) -> np.ndarray:

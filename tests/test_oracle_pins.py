@@ -13,7 +13,6 @@ import pytest
 import torch
 
 import oracle
-from oracle.quant import SCORE_GROUP_TILES, SCORE_TILE_ROWS
 from workloads import bf16_bits_from_f32, f32_from_bf16_bits, make_inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -244,40 +243,57 @@ def test_round_trip_unit_tensor_scale(c1):
 
 # ---------------------------------------------------------------- scores / top-k
 def test_scores_exact_and_topk_brute_force():
+    """Eq. 23 squared: each channel's score is the fp64 value nearest to the
+    exact sum of squared residuals (float() of a Fraction rounds correctly),
+    so the oracle must equal it bit for bit; Eq. 24: top-k by brute force."""
     xb = _t3_bits(rows=130, cols=64)
     q = oracle.nvfp4_quantize(xb)
     s = oracle.channel_scores(q.resid)
-    M = q.resid.shape[0]
-    for j in range(0, 64, 7):
-        exact = sum(Fraction(float(v)) ** 2 for v in q.resid[:, j])
-        assert abs(Fraction(float(s[j])) - exact) <= exact * M * Fraction(1, 2 ** 52)
     ex = [sum(Fraction(float(v)) ** 2 for v in q.resid[:, j]) for j in range(64)]
+    assert [float(e) for e in ex] == s.tolist()
     for k in (0, 1, 5, 17, 64):
         brute = sorted(sorted(range(64), key=lambda j: (-ex[j], j))[:k])
         assert oracle.select_topk(s, k).tolist() == brute
     # ties -> smaller index
     assert oracle.select_topk(np.array([1.0, 2.0, 2.0, 0.0, 2.0]), 2).tolist() == [1, 2]
-    # the summation order: rows inside 32-row tiles, tiles inside 8-tile
-    # groups, then groups.  (2^-27)^2 = 2^-54 is lost when added alone onto 1,
-    # but three of them summed first give 1.5 * 2^-53, which survives.
-    T, G = SCORE_TILE_ROWS, SCORE_TILE_ROWS * SCORE_GROUP_TILES
+
+
+def test_scores_extreme_exponents_exact():
+    """Residuals spanning the whole fp32 range (subnormals to 1e38) in one
+    channel: still the correctly rounded exact sum."""
+    rng = np.random.default_rng(8)
+    r = (rng.standard_normal((300, 24)) * np.exp(rng.uniform(-85, 85, (300, 24)))).astype(np.float32)
+    r[0, 0], r[1, 0], r[2, 0] = 3.0e38, 1.0e-45, -2.0e-40
+    r[:, 5] = 0.0
+    s = oracle.channel_scores(r)
+    for j in range(24):
+        assert s[j] == float(sum(Fraction(float(v)) ** 2 for v in r[:, j])), j
+    assert s[5] == 0.0
+
+
+def test_scores_order_free_closed_form():
+    """The score has no summation order: 1 + three squares of 2^-27 is
+    1 + 1.5 * 2^-53 exactly, whose nearest fp64 is 1 + 2^-52, wherever the
+    four rows sit; a row permutation leaves every score bit-identical."""
     e = np.float32(2.0 ** -27)
-    r = np.zeros((2 * G, 1), dtype=np.float32)
-    r[0, 0] = 1.0
-    r[1:4, 0] = e                      # same tile as the 1: each lost in turn
-    assert oracle.channel_scores(r)[0] == 1.0
-    r = np.zeros((2 * G, 1), dtype=np.float32)
-    r[0, 0] = 1.0
-    r[T:T + 3, 0] = e                  # tile 1 sums them before meeting the 1
-    assert oracle.channel_scores(r)[0] == 1.0 + 2.0 ** -52
-    r = np.zeros((2 * G, 1), dtype=np.float32)
-    r[0, 0] = 1.0
-    r[[G, G + T, G + 2 * T], 0] = e    # one per tile of group 1: the group sums first
-    assert oracle.channel_scores(r)[0] == 1.0 + 2.0 ** -52
-    r = np.zeros((G, 1), dtype=np.float32)
-    r[0, 0] = 1.0
-    r[[T, 2 * T, 3 * T], 0] = e        # one per tile of group 0: each tile meets the 1
-    assert oracle.channel_scores(r)[0] == 1.0
+    for rows in ([1, 2, 3], [32, 64, 96], [256, 288, 511], [5, 300, 700]):
+        r = np.zeros((1024, 1), dtype=np.float32)
+        r[0, 0] = 1.0
+        r[rows, 0] = e
+        assert oracle.channel_scores(r)[0] == 1.0 + 2.0 ** -52
+        r2 = r[::-1].copy()
+        assert oracle.channel_scores(r2)[0] == 1.0 + 2.0 ** -52
+    # one square of 2^-27 is a quarter of an ulp of 1 (rounds down); two make
+    # exactly half an ulp, a tie that goes to the even neighbour 1.0
+    for n in (1, 2):
+        r = np.zeros((4, 1), dtype=np.float32)
+        r[0, 0] = 1.0
+        r[1:1 + n, 0] = e
+        assert oracle.channel_scores(r)[0] == 1.0
+    q = oracle.nvfp4_quantize(_t3_bits(seed=3, rows=300, cols=96))
+    perm = np.random.default_rng(1).permutation(300)
+    np.testing.assert_array_equal(oracle.channel_scores(q.resid[perm]).view(np.uint64),
+                                  oracle.channel_scores(q.resid).view(np.uint64))
 
 
 def test_selection_lands_in_outlier_blocks(c1):
@@ -353,6 +369,55 @@ def test_eq21_literal_reduces_error(c1):
     y0 = oracle.w4a4_gemm(A, W)
     y1 = oracle.rac_gemm_eq21(d["x"], A, W, S)
     assert np.linalg.norm(y1 - ref) < np.linalg.norm(y0 - ref)
+
+
+def test_golden_eq21_mask_after_quantize():
+    """Eq. 21's order (mask applied to the quantized residual), worked by hand
+    in tests/golden/eq21_mask_after_quantize.txt: a selected channel whose
+    16-block holds a larger unselected residual is quantized at that block's
+    scale (here to zero), which masking before quantizing would not do."""
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :3] = [5.25, 1.9140625, 0.87890625]
+    w = np.zeros((2, 32), dtype=np.float32)
+    w[0, 2] = 5.25
+    w[1, :3] = 5.25
+    xb, wb = _bits(x), _bits(w)
+    A = oracle.nvfp4_quantize(xb)
+    W = oracle.nvfp4_quantize(wb)
+    assert float(A.tensor_scale) == 2.0 ** -9 and float(W.tensor_scale) == 2.0 ** -9
+    Q = oracle.eq21_residual_quant(A)
+    assert float(Q.tensor_scale) == 2.0 ** -14 and Q.scales[0, 0] == 0x7E
+    assert Q.mag[0, 1] == 7 and Q.mag[0, 2] == 0
+    for S, y0, y1, before in _load("eq21_mask_after_quantize.txt"):
+        S = np.array([int(s) for s in S.split(",")], dtype=np.int64)
+        y = oracle.rac_gemm_eq21(xb, A, W, S)
+        assert y.tolist() == [[float(y0), float(y1)]]
+        if float(before) != float(y0):
+            assert abs(y[0, 0] - float(before)) > 0.01
+
+
+def test_swiglu_against_torch_silu():
+    """The SwiGLU product h = bf16(silu(gate) * up): silu against torch's
+    own silu in fp64 (a library routine), silu on the gate half only, and
+    one rounding to the nearest bf16."""
+    from oracle.moe import swiglu_bf16
+    rng = np.random.default_rng(17)
+    g = rng.standard_normal((64, 96)) * np.exp(rng.uniform(-4, 3, (64, 96)))
+    u = rng.standard_normal((64, 96)) * np.exp(rng.uniform(-4, 3, (64, 96)))
+    g[0, :6] = [0.0, -0.0, 40.0, -40.0, 1e-30, -750.0]
+    ref = (torch.nn.functional.silu(torch.from_numpy(g)) * torch.from_numpy(u)).numpy()
+    h = f32_from_bf16_bits(swiglu_bf16(g, u)).astype(np.float64)
+    # h is a neighbour of the library value and the nearer one (up to fp64
+    # rounding of the two computations): |h - ref| <= half a bf16 ulp of ref
+    ulp = np.where(ref == 0, 0.0, 2.0 ** (np.floor(np.log2(np.abs(np.where(ref == 0, 1, ref)))) - 7))
+    assert np.all(np.abs(h - ref) <= ulp / 2 * (1 + 1e-9) + 1e-300)
+    # swapping the halves changes the result (silu is applied to the gate)
+    h_sw = f32_from_bf16_bits(swiglu_bf16(u, g)).astype(np.float64)
+    assert np.mean(h_sw != h) > 0.9
+    # large positive gate: silu(g) -> g, so h -> bf16(g * u); large negative -> 0
+    assert h[0, 2] == f32_from_bf16_bits(_bits([40.0 * u[0, 2]]))[0] or \
+        abs(h[0, 2] - 40.0 * u[0, 2]) <= abs(40.0 * u[0, 2]) * 2.0 ** -8
+    assert h[0, 5] == 0.0
 
 
 def test_eq21_all_channels_error_bound(c1):
