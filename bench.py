@@ -229,22 +229,16 @@ def _copy_probe():
           flush=True)
 
 
-def _cpu_baseline():
-    """The oracle as it stands on the same step: all 8192 activation rows
-    (quantize, score, select, residual gather, fp64 W4A4+RAC GEMM against all
-    14336 weight rows); about ten seconds on the host cores."""
+def _oracle_step(rows):
+    """The oracle's dense step on the first `rows` activation rows: quantize,
+    score, select, residual gather, fp64 W4A4+RAC GEMM against the whole
+    14336 x 4096 weight (quantized beforehand, untimed); returns (s, flops)."""
     import oracle
     from workloads import WORKLOADS, make_activations, make_weight
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
     wl = WORKLOADS["dense_8192x14336x4096"]
-    rows = wl.rows
     xb = make_activations(wl)[:rows]
     wb = make_weight(wl)
-    Wq = oracle.nvfp4_quantize(wb)          # offline weight preparation, not timed
+    Wq = oracle.nvfp4_quantize(wb)
     t0 = time.perf_counter()
     A = oracle.nvfp4_quantize(xb)
     S = oracle.select_topk(oracle.channel_scores(A.resid), wl.topk_channels)
@@ -252,10 +246,25 @@ def _cpu_baseline():
     Y = oracle.rac_gemm(A, Wq, R, wb, S)
     oracle.f64_to_bf16_bits(Y)
     dt = time.perf_counter() - t0
-    flops = 2.0 * rows * wl.n_out * (wl.cols + wl.topk_channels)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle step on {rows} of {wl.rows} rows (quantize + select + gather + "
-                      f"fp64 RAC GEMM vs {wl.n_out}x{wl.cols} W), {dt:.1f} s"}
+    return dt, 2.0 * rows * wl.n_out * (wl.cols + wl.topk_channels)
+
+
+def _cpu_baseline():
+    """The oracle as it stands, timed on the host: with T = every core this
+    process may run on (BLAS limited to T threads; numpy's elementwise work is
+    one thread) on all 8192 rows, and with one thread on a 1024-row sample."""
+    from threadpoolctl import threadpool_limits
+    T = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=T):
+        dt, fl = _oracle_step(8192)
+    with threadpool_limits(limits=1):
+        dt1, fl1 = _oracle_step(1024)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": T, "kind": "oracle",
+            "sample": f"oracle dense step on all 8192 rows (quantize + exact scores + select + "
+                      f"gather + fp64 RAC GEMM vs the 14336x4096 weight), {dt:.1f} s with BLAS "
+                      f"on {T} threads",
+            "one_thread": {"value": fl1 / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                           "sample": f"the same step on the first 1024 rows, {dt1:.1f} s"}}
 
 
 def main():
@@ -281,10 +290,10 @@ def main():
 
     _say("generating the dense workload")
     xb = make_activations(wl)
-    x = [todev(xb)]
-    # a second copy with the rows rotated, so consecutive steps do not hit the
-    # same activation bytes in the last-level cache
-    x.append(todev(np.ascontiguousarray(np.roll(xb, 4096, axis=0))))
+    # NX copies of x (rows rotated) that together exceed the 256 MB last-level
+    # cache, used in turn, so no step finds its activation bytes in that cache
+    NX = 5
+    x = [todev(np.ascontiguousarray(np.roll(xb, (M // NX) * j, axis=0))) for j in range(NX)]
     W = q4.prepare_weight(todev(make_weight(wl)))
     L = q4.lib()
     stream = torch.cuda.current_stream()
@@ -305,7 +314,7 @@ def main():
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(a.steps)]
 
     def step(i, events=None):
-        xi = x[i % 2]
+        xi = x[i % NX]
         if events:
             events[0].record(stream)
         q4._check(L.nvfp4_quantize(xi.data_ptr(), M, K, None, codes.data_ptr(), scales.data_ptr(),
@@ -316,7 +325,7 @@ def main():
         q4._check(L.rac_gemm(0, M, N, K, xi.data_ptr(), codes.data_ptr(), scales.data_ptr(),
                              ts.data_ptr(), W["codes"].data_ptr(), W["scales"].data_ptr(),
                              W["tensor_scale"].data_ptr(), W["w_hi_t"].data_ptr(), idx.data_ptr(),
-                             k, Y.data_ptr(), 1, rws.data_ptr(), rws_b, sp))
+                             k, Y.data_ptr(), 1, rws.data_ptr(), rws_b, None, sp))
         if events:
             events[2].record(stream)
 
@@ -428,7 +437,7 @@ def main():
             q4._check(L.rac_gemm(1, M, N, K, x[i % 2].data_ptr(), cm.data_ptr(), smx.data_ptr(),
                                  None, Wm["codes"].data_ptr(), Wm["scales"].data_ptr(), None,
                                  Wm["w_hi_t"].data_ptr(), im.data_ptr(), k, Y.data_ptr(), 1,
-                                 rws.data_ptr(), rws_b, sp))
+                                 rws.data_ptr(), rws_b, None, sp))
         for i in range(3):
             mstep(i)
         mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
@@ -439,7 +448,7 @@ def main():
             q4._check(L.rac_gemm(1, M, N, K, x[i % 2].data_ptr(), cm.data_ptr(), smx.data_ptr(),
                                  None, Wm["codes"].data_ptr(), Wm["scales"].data_ptr(), None,
                                  Wm["w_hi_t"].data_ptr(), im.data_ptr(), k, Y.data_ptr(), 1,
-                                 rws.data_ptr(), rws_b, sp))
+                                 rws.data_ptr(), rws_b, None, sp))
             mev[i][1].record(stream)
         torch.cuda.synchronize()
         t_mx = float(np.mean([e[0].elapsed_time(e[1]) for e in mev]))
@@ -461,7 +470,7 @@ def main():
                                  ts.data_ptr(), W["codes"].data_ptr(), W["scales"].data_ptr(),
                                  W["tensor_scale"].data_ptr(), W["w_hi_t"].data_ptr(),
                                  idx.data_ptr() if kk else None, kk, Y.data_ptr(), 1,
-                                 rws.data_ptr(), rws_b, sp))
+                                 rws.data_ptr(), rws_b, None, sp))
         tw = {0: [], k: []}
         for i in range(12):
             for kk in (0, k):
@@ -495,7 +504,7 @@ def main():
                                       scales.data_ptr(), ts.data_ptr(), W["codes"].data_ptr(),
                                       W["scales"].data_ptr(), W["tensor_scale"].data_ptr(),
                                       idx.data_ptr(), k, Y.data_ptr(), 1, None, ews.data_ptr(),
-                                      ews_b, sp))
+                                      ews_b, None, sp))
         for i in range(3):
             step(i)
             estep(i)

@@ -55,23 +55,23 @@ _SIGS = {
     "nvfp4_qdq": (_I32, [_P, _I64, _I64, _P, _P, _I32, _P, _P, _SZ, _P]),
     "q4_select_workspace_size": (_SZ, [_I64]),
     "q4_select_channels": (_I32, [_P, _I64, _I32, _P, _P, _SZ, _P]),
-    "q4_residual_gather": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I64, _P]),
+    "q4_residual_gather": (_I32, [_I32, _P, _I64, _I64, _P, _P, _P, _P, _I32, _P, _I64, _P, _P]),
     "w4a4_gemm": (_I32, [_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _I32, _P]),
     "rac_gemm_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "rac_gemm": (_I32, [_I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
-                        _I32, _P, _SZ, _P]),
+                        _I32, _P, _SZ, _P, _P]),
     "rac_gemm_eq21_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "rac_gemm_eq21": (_I32, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32,
-                             _P, _P, _SZ, _P]),
+                             _P, _P, _SZ, _P, _P]),
     "q4_moe_route": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P]),
     "q4_moe_sort_workspace_size": (_SZ, [_I64, _I32, _I32]),
-    "q4_moe_sort": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "q4_moe_sort": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P, _P]),
     "q4_transpose_bf16": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
     "q4_moe_pack_w13": (_I32, [_P, _I32, _I32, _I32, _P, _P]),
     "moe_workspace_size": (_SZ, [_I32, _I64, _I32, _I32, _I32, _I32, _I32]),
     "moe_workspace_layout": (_I32, [_I32, _I64, _I32, _I32, _I32, _I32, _I32, _P]),
     "moe_w4a4_grouped_gemm": (_I32, [_I32, _P, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P,
-                                     _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _SZ, _P]),
+                                     _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _SZ, _P, _P]),
 }
 
 
@@ -97,14 +97,42 @@ def _check(status: int):
         raise Q4Error(status, lib().q4_last_error().decode())
 
 
-def _ptr(t):
+_BF16_TYPES = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor"):
+    """Device pointer of a contiguous tensor, after checking its dtype (a torch
+    dtype or a tuple of them) and shape (None entries are free)."""
     if t is None:
         return None
     if not t.is_cuda:
-        raise ValueError("q4rac takes device tensors")
+        raise ValueError(f"q4rac: '{name}' must be a device tensor")
     if not t.is_contiguous():
-        raise ValueError("q4rac takes contiguous tensors")
+        raise ValueError(f"q4rac: '{name}' must be contiguous")
+    if dtype is not None:
+        ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+        if not ok:
+            raise TypeError(f"q4rac: '{name}' has dtype {t.dtype}, expected {dtype}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(w is not None and int(d) != int(w)
+                                        for d, w in zip(t.shape, shape)):
+            raise ValueError(f"q4rac: '{name}' has shape {tuple(t.shape)}, expected "
+                             f"{tuple('*' if w is None else w for w in shape)}")
     return t.data_ptr()
+
+
+def _on(stream):
+    """Run the body with `stream` current, so temporaries allocated there are
+    stream-ordered with the kernels that use them (freed only after them)."""
+    return torch.cuda.stream(stream) if stream is not None else _NullCtx()
+
+
+class _NullCtx:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *a):
+        return False
 
 
 def _stream(stream=None):
@@ -112,22 +140,42 @@ def _stream(stream=None):
     return s.cuda_stream
 
 
-def _bf16(t):
-    if t.dtype == torch.bfloat16:
+def _bf16(t, name="x"):
+    if t.dtype in _BF16_TYPES:
         return t
-    if t.dtype in (torch.int16, torch.uint16):
-        return t
-    raise TypeError("expected a bf16 tensor (torch.bfloat16 or 16-bit bit patterns)")
+    raise TypeError(f"q4rac: '{name}' must be bf16 (torch.bfloat16 or 16-bit bit patterns), "
+                    f"got {t.dtype}")
 
 
 def _empty(shape, dtype, device):
     return torch.empty(shape, dtype=dtype, device=device)
 
 
+def _status(status):
+    return _ptr(status, torch.int32, (1,), "status")
+
+
+def _qshape(q, rows, K, name):
+    """Check a quantized operand dict against rows x K."""
+    blk = 16 if q["fmt"] == NVFP4 else 32
+    _ptr(q["codes"], torch.uint8, (rows, K // 2), name + " codes")
+    _ptr(q["scales"], torch.uint8, (rows, K // blk), name + " scales")
+    if q["fmt"] == NVFP4:
+        _ptr(q["tensor_scale"], torch.float32, (None,), name + " tensor_scale")
+
+
 # ------------------------------------------------------------------ quantizer
 def _quantize(fmt, x, tensor_scale_in=None, topk=0, want_scores=True, stream=None):
+    with _on(stream):
+        return _quantize_body(fmt, x, tensor_scale_in, topk, want_scores)
+
+
+def _quantize_body(fmt, x, tensor_scale_in, topk, want_scores, stream=None):
     x = _bf16(x)
+    if x.dim() != 2:
+        raise ValueError("q4rac: x must be 2-D [rows, cols]")
     rows, cols = x.shape
+    _ptr(tensor_scale_in, torch.float32, (1,), "tensor_scale_in")
     dev = x.device
     L = lib()
     blk = 16 if fmt == NVFP4 else 32
@@ -161,7 +209,13 @@ def mxfp4_quantize(x, topk=0, want_scores=True, stream=None):
 def nvfp4_qdq(x, tensor_scale_in=None, out_dtype=OUT_F32, stream=None, want_scale=False):
     """Weight fake quantization: the values c sb s_t of nvfp4_quantize(x), fp32 or
     bf16; with want_scale also the tensor scale used."""
+    with _on(stream):
+        return _nvfp4_qdq_body(x, tensor_scale_in, out_dtype, want_scale)
+
+
+def _nvfp4_qdq_body(x, tensor_scale_in, out_dtype, want_scale, stream=None):
     x = _bf16(x)
+    _ptr(tensor_scale_in, torch.float32, (1,), "tensor_scale_in")
     rows, cols = x.shape
     L = lib()
     y = _empty((rows, cols), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, x.device)
@@ -174,32 +228,45 @@ def nvfp4_qdq(x, tensor_scale_in=None, out_dtype=OUT_F32, stream=None, want_scal
 
 
 def q4_select_channels(chan_score, topk, stream=None):
-    cols = chan_score.shape[0]
-    idx = _empty((topk,), torch.int32, chan_score.device)
-    _check(lib().q4_select_channels(_ptr(chan_score), cols, topk, _ptr(idx) if topk else None,
-                                    None, 0, _stream(stream)))
-    return idx
+    with _on(stream):
+        cols = chan_score.shape[0]
+        _ptr(chan_score, torch.float64, (cols,), "chan_score")
+        idx = _empty((topk,), torch.int32, chan_score.device)
+        _check(lib().q4_select_channels(_ptr(chan_score), cols, topk, _ptr(idx) if topk else None,
+                                        None, 0, _stream(stream)))
+        return idx
 
 
-def q4_residual_gather(x, q, chan_idx, ld_r=None, stream=None):
-    x = _bf16(x)
-    rows, cols = x.shape
-    k = 0 if chan_idx is None else int(chan_idx.shape[0])
-    ld_r = max(k, 1) if ld_r is None else ld_r
-    R = _empty((rows, ld_r), torch.int16, x.device)
-    _check(lib().q4_residual_gather(q["fmt"], _ptr(x), rows, cols, _ptr(q["codes"]),
-                                    _ptr(q["scales"]), _ptr(q["tensor_scale"]),
-                                    _ptr(chan_idx) if k else None, k, _ptr(R), ld_r,
-                                    _stream(stream)))
-    return R
+def q4_residual_gather(x, q, chan_idx, ld_r=None, stream=None, status=None):
+    with _on(stream):
+        x = _bf16(x)
+        rows, cols = x.shape
+        _qshape(q, rows, cols, "q")
+        k = 0 if chan_idx is None else int(chan_idx.shape[0])
+        ld_r = max(k, 1) if ld_r is None else ld_r
+        R = _empty((rows, ld_r), torch.int16, x.device)
+        _check(lib().q4_residual_gather(q["fmt"], _ptr(x), rows, cols, _ptr(q["codes"]),
+                                        _ptr(q["scales"]), _ptr(q["tensor_scale"]),
+                                        _ptr(chan_idx, torch.int32, (k,), "chan_idx") if k else None,
+                                        k, _ptr(R), ld_r, _status(status), _stream(stream)))
+        return R
 
 
 # ------------------------------------------------------------------ GEMM
 def w4a4_gemm(A, W, out_dtype=OUT_F32, stream=None):
     """Y = W4A4(A, W) for quantized dicts A [M, K] and W [N, K]."""
+    with _on(stream):
+        return _w4a4_gemm_body(A, W, out_dtype, stream)
+
+
+def _w4a4_gemm_body(A, W, out_dtype, stream):
     M = A["codes"].shape[0]
     N = W["codes"].shape[0]
     K = A["codes"].shape[1] * 2
+    if A["fmt"] != W["fmt"]:
+        raise ValueError("q4rac: A and W must share a format")
+    _qshape(A, M, K, "A")
+    _qshape(W, N, K, "W")
     Y = _empty((M, N), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
                A["codes"].device)
     _check(lib().w4a4_gemm(A["fmt"], M, N, K, _ptr(A["codes"]), _ptr(A["scales"]),
@@ -208,47 +275,70 @@ def w4a4_gemm(A, W, out_dtype=OUT_F32, stream=None):
     return Y
 
 
-def rac_gemm(x, A, W, w_hi_t, chan_set, out_dtype=OUT_F32, stream=None, Y=None, workspace=None):
-    """Y = W4A4(A, W) + residual(x on chan_set) @ W_hi[:, chan_set]^T."""
-    x = _bf16(x)
-    M, K = x.shape
-    N = W["codes"].shape[0]
-    k = 0 if chan_set is None else int(chan_set.shape[0])
-    L = lib()
-    if Y is None:
-        Y = _empty((M, N), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, x.device)
-    wsb = L.rac_gemm_workspace_size(M, N, K, k)
-    if workspace is None or workspace.numel() < wsb:
-        workspace = _empty((max(wsb, 1),), torch.uint8, x.device)
-    _check(L.rac_gemm(A["fmt"], M, N, K, _ptr(x), _ptr(A["codes"]), _ptr(A["scales"]),
-                      _ptr(A["tensor_scale"]), _ptr(W["codes"]), _ptr(W["scales"]),
-                      _ptr(W["tensor_scale"]), _ptr(w_hi_t) if k else None,
-                      _ptr(chan_set) if k else None, k, _ptr(Y), out_dtype, _ptr(workspace),
-                      wsb, _stream(stream)))
-    return Y
+def _out_check(Y, M, N, out_dtype):
+    _ptr(Y, torch.float32 if out_dtype == OUT_F32 else _BF16_TYPES, (M, N), "Y")
+
+
+def rac_gemm(x, A, W, w_hi_t, chan_set, out_dtype=OUT_F32, stream=None, Y=None, workspace=None,
+             status=None):
+    """Y = W4A4(A, W) + residual(x on chan_set) @ W_hi[:, chan_set]^T.  ``status``
+    (optional int32 [1] device tensor) receives 0, or 1 for an invalid channel set."""
+    with _on(stream):
+        x = _bf16(x)
+        M, K = x.shape
+        N = W["codes"].shape[0]
+        if A["fmt"] != W["fmt"]:
+            raise ValueError("q4rac: A and W must share a format")
+        _qshape(A, M, K, "A")
+        _qshape(W, N, K, "W")
+        k = 0 if chan_set is None else int(chan_set.shape[0])
+        L = lib()
+        if Y is None:
+            Y = _empty((M, N), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, x.device)
+        _out_check(Y, M, N, out_dtype)
+        wsb = L.rac_gemm_workspace_size(M, N, K, k)
+        if workspace is None or workspace.numel() < wsb:
+            workspace = _empty((max(wsb, 1),), torch.uint8, x.device)
+        _check(L.rac_gemm(A["fmt"], M, N, K, _ptr(x), _ptr(A["codes"]), _ptr(A["scales"]),
+                          _ptr(A["tensor_scale"]), _ptr(W["codes"]), _ptr(W["scales"]),
+                          _ptr(W["tensor_scale"]),
+                          _ptr(_bf16(w_hi_t, "w_hi_t"), None, (K, N), "w_hi_t") if k else None,
+                          _ptr(chan_set, torch.int32, (k,), "chan_set") if k else None, k,
+                          _ptr(Y), out_dtype, _ptr(workspace, torch.uint8), wsb,
+                          _status(status), _stream(stream)))
+        return Y
 
 
 def rac_gemm_eq21(x, A, W, chan_set, out_dtype=OUT_F32, stream=None, Y=None, workspace=None,
-                  resid_tensor_scale=None):
+                  resid_tensor_scale=None, status=None):
     """Page-literal compensation: Y = (Q(x) - M_S * Q(Q(x) - x)) @ Q(W)^T for NVFP4
     operands A (of x) and W; resid_tensor_scale (fp32 [1], optional) receives the
-    residual's tensor scale."""
-    x = _bf16(x)
-    M, K = x.shape
-    N = W["codes"].shape[0]
-    k = 0 if chan_set is None else int(chan_set.shape[0])
-    L = lib()
-    if Y is None:
-        Y = _empty((M, N), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, x.device)
-    wsb = L.rac_gemm_eq21_workspace_size(M, N, K, k)
-    if workspace is None or workspace.numel() < wsb:
-        workspace = _empty((max(wsb, 1),), torch.uint8, x.device)
-    _check(L.rac_gemm_eq21(M, N, K, _ptr(x), _ptr(A["codes"]), _ptr(A["scales"]),
-                           _ptr(A["tensor_scale"]), _ptr(W["codes"]), _ptr(W["scales"]),
-                           _ptr(W["tensor_scale"]), _ptr(chan_set) if k else None, k, _ptr(Y),
-                           out_dtype, _ptr(resid_tensor_scale) if resid_tensor_scale is not None
-                           else None, _ptr(workspace), wsb, _stream(stream)))
-    return Y
+    residual's tensor scale, status (int32 [1], optional) 0 or 1 (invalid set)."""
+    with _on(stream):
+        x = _bf16(x)
+        M, K = x.shape
+        N = W["codes"].shape[0]
+        if A["fmt"] != NVFP4 or W["fmt"] != NVFP4:
+            raise ValueError("q4rac: rac_gemm_eq21 takes NVFP4 operands")
+        _qshape(A, M, K, "A")
+        _qshape(W, N, K, "W")
+        k = 0 if chan_set is None else int(chan_set.shape[0])
+        L = lib()
+        if Y is None:
+            Y = _empty((M, N), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16, x.device)
+        _out_check(Y, M, N, out_dtype)
+        wsb = L.rac_gemm_eq21_workspace_size(M, N, K, k)
+        if workspace is None or workspace.numel() < wsb:
+            workspace = _empty((max(wsb, 1),), torch.uint8, x.device)
+        _check(L.rac_gemm_eq21(M, N, K, _ptr(x), _ptr(A["codes"]), _ptr(A["scales"]),
+                               _ptr(A["tensor_scale"]), _ptr(W["codes"]), _ptr(W["scales"]),
+                               _ptr(W["tensor_scale"]),
+                               _ptr(chan_set, torch.int32, (k,), "chan_set") if k else None, k,
+                               _ptr(Y), out_dtype,
+                               _ptr(resid_tensor_scale, torch.float32, (1,), "resid_tensor_scale"),
+                               _ptr(workspace, torch.uint8), wsb, _status(status),
+                               _stream(stream)))
+        return Y
 
 
 def q4_transpose_bf16(x, stream=None):
@@ -270,23 +360,27 @@ def prepare_weight(w, fmt=NVFP4, stream=None):
 
 # ------------------------------------------------------------------ MoE
 def q4_moe_route(logits, topk, stream=None):
-    T, E = logits.shape
-    idx = _empty((T, topk), torch.int32, logits.device)
-    w = _empty((T, topk), torch.float32, logits.device)
-    _check(lib().q4_moe_route(_ptr(logits), T, E, topk, _ptr(idx), _ptr(w), _stream(stream)))
-    return idx, w
+    with _on(stream):
+        T, E = logits.shape
+        _ptr(logits, torch.float32, (T, E), "logits")
+        idx = _empty((T, topk), torch.int32, logits.device)
+        w = _empty((T, topk), torch.float32, logits.device)
+        _check(lib().q4_moe_route(_ptr(logits), T, E, topk, _ptr(idx), _ptr(w), _stream(stream)))
+        return idx, w
 
 
-def q4_moe_sort(topk_idx, E, stream=None):
-    T, k = topk_idx.shape
-    L = lib()
-    perm = _empty((T * k,), torch.int32, topk_idx.device)
-    offsets = _empty((E + 1,), torch.int32, topk_idx.device)
-    wsb = L.q4_moe_sort_workspace_size(T, E, k)
-    ws = _empty((max(wsb, 1),), torch.uint8, topk_idx.device)
-    _check(L.q4_moe_sort(_ptr(topk_idx), T, E, k, _ptr(perm), _ptr(offsets), _ptr(ws), wsb,
-                         _stream(stream)))
-    return perm, offsets
+def q4_moe_sort(topk_idx, E, stream=None, status=None):
+    with _on(stream):
+        T, k = topk_idx.shape
+        _ptr(topk_idx, torch.int32, (T, k), "topk_idx")
+        L = lib()
+        perm = _empty((T * k,), torch.int32, topk_idx.device)
+        offsets = _empty((E + 1,), torch.int32, topk_idx.device)
+        wsb = L.q4_moe_sort_workspace_size(T, E, k)
+        ws = _empty((max(wsb, 1),), torch.uint8, topk_idx.device)
+        _check(L.q4_moe_sort(_ptr(topk_idx), T, E, k, _ptr(perm), _ptr(offsets), _ptr(ws), wsb,
+                             _status(status), _stream(stream)))
+        return perm, offsets
 
 
 def q4_moe_pack_w13(w13, stream=None):
@@ -341,26 +435,43 @@ def moe_workspace_layout(fmt, T, E, H, F, topk, rac_k):
 
 
 def moe_w4a4_grouped_gemm(tokens, topk_idx, topk_w, experts, rac_k, out_dtype=OUT_BF16,
-                          workspace=None, stream=None, Y=None):
-    """Token-sorted grouped W4A4+RAC SwiGLU expert layer; returns (Y, workspace)."""
-    tokens = _bf16(tokens)
-    T, H = tokens.shape
-    topk = topk_idx.shape[1]
-    fmt = experts["fmt"]
-    E, F = experts["E"], experts["F"]
-    L = lib()
-    wsb = L.moe_workspace_size(fmt, T, E, H, F, topk, rac_k)
-    if workspace is None or workspace.numel() < wsb:
-        workspace = _empty((max(wsb, 1),), torch.uint8, tokens.device)
-    if Y is None:
-        Y = _empty((T, H), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
-                   tokens.device)
-    w13, w2 = experts["w13"], experts["w2"]
-    _check(L.moe_w4a4_grouped_gemm(
-        fmt, _ptr(tokens), T, H, _ptr(topk_idx), _ptr(topk_w), topk, E, F,
-        _ptr(w13["codes"]), _ptr(w13["scales"]), _ptr(w13["tensor_scale"]),
-        _ptr(w2["codes"]), _ptr(w2["scales"]), _ptr(w2["tensor_scale"]),
-        _ptr(experts.get("w13_hi_t")) if rac_k else None,
-        _ptr(experts.get("w2_hi_t")) if rac_k else None,
-        rac_k, _ptr(Y), out_dtype, _ptr(workspace), wsb, _stream(stream)))
-    return Y, workspace
+                          workspace=None, stream=None, Y=None, status=None):
+    """Token-sorted grouped W4A4+RAC SwiGLU expert layer; returns (Y, workspace).
+    ``status`` (optional int32 [1]) receives 0, or 1 for an expert index
+    outside [0, E)."""
+    with _on(stream):
+        tokens = _bf16(tokens, "tokens")
+        T, H = tokens.shape
+        topk = topk_idx.shape[1]
+        fmt = experts["fmt"]
+        E, F = experts["E"], experts["F"]
+        if experts["H"] != H:
+            raise ValueError(f"q4rac: tokens have {H} channels, the experts {experts['H']}")
+        _ptr(topk_idx, torch.int32, (T, topk), "topk_idx")
+        _ptr(topk_w, torch.float32, (T, topk), "topk_w")
+        w13, w2 = experts["w13"], experts["w2"]
+        blk = 16 if fmt == NVFP4 else 32
+        _ptr(w13["codes"], torch.uint8, (E, 2 * F, H // 2), "w13 codes")
+        _ptr(w13["scales"], torch.uint8, (E, 2 * F, H // blk), "w13 scales")
+        _ptr(w2["codes"], torch.uint8, (E, H, F // 2), "w2 codes")
+        _ptr(w2["scales"], torch.uint8, (E, H, F // blk), "w2 scales")
+        if fmt == NVFP4:
+            _ptr(w13["tensor_scale"], torch.float32, (E,), "w13 tensor_scale")
+            _ptr(w2["tensor_scale"], torch.float32, (E,), "w2 tensor_scale")
+        L = lib()
+        wsb = L.moe_workspace_size(fmt, T, E, H, F, topk, rac_k)
+        if workspace is None or workspace.numel() < wsb:
+            workspace = _empty((max(wsb, 1),), torch.uint8, tokens.device)
+        if Y is None:
+            Y = _empty((T, H), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
+                       tokens.device)
+        _out_check(Y, T, H, out_dtype)
+        _check(L.moe_w4a4_grouped_gemm(
+            fmt, _ptr(tokens), T, H, _ptr(topk_idx), _ptr(topk_w), topk, E, F,
+            _ptr(w13["codes"]), _ptr(w13["scales"]), _ptr(w13["tensor_scale"]),
+            _ptr(w2["codes"]), _ptr(w2["scales"]), _ptr(w2["tensor_scale"]),
+            _ptr(experts.get("w13_hi_t"), _BF16_TYPES, (E, H, 2 * F), "w13_hi_t") if rac_k else None,
+            _ptr(experts.get("w2_hi_t"), _BF16_TYPES, (E, F, H), "w2_hi_t") if rac_k else None,
+            rac_k, _ptr(Y), out_dtype, _ptr(workspace, torch.uint8), wsb, _status(status),
+            _stream(stream)))
+        return Y, workspace

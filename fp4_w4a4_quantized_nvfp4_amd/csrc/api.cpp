@@ -61,7 +61,7 @@ int32_t round_up32(int32_t k) { return (k + 31) & ~31; }
 extern "C" {
 
 const char* q4_last_error(void) { return g_err; }
-int32_t q4_version(void) { return 101; }
+int32_t q4_version(void) { return 102; }
 
 // ======================================================================== quantize
 size_t q4_quantize_workspace_size(int64_t rows, int64_t cols, int32_t fmt) {
@@ -182,7 +182,7 @@ q4_status_t q4_select_channels(const double* chan_score, int64_t cols, int32_t t
 q4_status_t q4_residual_gather(int32_t fmt, const uint16_t* x, int64_t rows, int64_t cols,
                                const uint8_t* codes, const uint8_t* scales,
                                const float* tensor_scale, const int32_t* chan_idx, int32_t k,
-                               uint16_t* R, int64_t ld_r, void* stream) {
+                               uint16_t* R, int64_t ld_r, int32_t* status, void* stream) {
   if (fmt != Q4_NVFP4 && fmt != Q4_MXFP4) return fail(Q4_EINVAL, "q4_residual_gather: bad format %d", fmt);
   const bool mx = fmt == Q4_MXFP4;
   const int blk = mx ? 32 : 16;
@@ -197,14 +197,29 @@ q4_status_t q4_residual_gather(int32_t fmt, const uint16_t* x, int64_t rows, int
     Q4_REQUIRE_PTR(codes);
     Q4_REQUIRE_PTR(scales);
     Q4_REQUIRE_PTR(R);
-    if (k > 0) Q4_REQUIRE_SCALAR(chan_idx, 4);
   }
+  if (k > 0) Q4_REQUIRE_SCALAR(chan_idx, 4);
+  if (status) Q4_REQUIRE_SCALAR(status, 4);
   return hip_status(launch_residual_gather(mx, x, rows, cols, codes, scales, tensor_scale,
-                                           chan_idx, k, R, ld_r, S(stream)),
+                                           chan_idx, k, R, ld_r, S(stream), status),
                     "q4_residual_gather");
 }
 
 // ======================================================================== GEMM
+// An empty product (M or N zero) still reports on its channel set: a gather
+// of zero rows validates the set and writes the status word.
+static q4_status_t empty_status(const char* fn, int32_t fmt, int64_t K, const float* a_ts,
+                                const int32_t* chan_set, int32_t k, int32_t* status, void* stream) {
+  if (!status) return Q4_OK;
+  hipError_t e;
+  if (k == 0)
+    e = launch_fill_u32((uint32_t*)status, 1, 0u, S(stream));
+  else
+    e = launch_residual_gather(fmt == Q4_MXFP4, nullptr, 0, K, nullptr, nullptr, a_ts, chan_set,
+                               k, nullptr, k, S(stream), status);
+  return hip_status(e, fn);
+}
+
 static q4_status_t check_gemm(const char* fn, int32_t fmt, int64_t M, int64_t N, int64_t K,
                               const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                               const uint8_t* w_codes, const uint8_t* w_scales, const float* w_ts,
@@ -273,15 +288,16 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
                      const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                      const uint8_t* w_codes, const uint8_t* w_scales, const float* w_tensor_scale,
                      const uint16_t* w_hi_t, const int32_t* chan_set, int32_t k, void* Y,
-                     int32_t y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+                     int32_t y_dtype, void* workspace, size_t workspace_bytes, int32_t* status,
+                     void* stream) {
   q4_status_t st = check_gemm("rac_gemm", fmt, M, N, K, a_codes, a_scales, a_tensor_scale,
                               w_codes, w_scales, w_tensor_scale, Y, y_dtype);
   if (st != Q4_OK) return st;
   if (k < 0 || k > K || k > Q4_MAX_TOPK)
     return fail(Q4_EINVAL, "rac_gemm: k %d outside [0, min(K, %d)]", k, Q4_MAX_TOPK);
   if (k > 0) {
-    Q4_REQUIRE_PTR(x);
-    Q4_REQUIRE_PTR(w_hi_t);
+    if (M > 0) Q4_REQUIRE_PTR(x);
+    if (N > 0) Q4_REQUIRE_PTR(w_hi_t);
     Q4_REQUIRE_SCALAR(chan_set, 4);
     const size_t need = rac_gemm_workspace_size(M, N, K, k);
     if (!workspace || workspace_bytes < need)
@@ -289,7 +305,8 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
                   workspace_bytes);
     Q4_REQUIRE_PTR(workspace);
   }
-  if (M == 0 || N == 0) return Q4_OK;
+  if (status) Q4_REQUIRE_SCALAR(status, 4);
+  if (M == 0 || N == 0) return empty_status("rac_gemm", fmt, K, a_tensor_scale, chan_set, k, status, stream);
   const bool mx = fmt == Q4_MXFP4;
   GemmArgs g{};
   g.M = M;
@@ -334,7 +351,7 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
   }
   hipError_t e = launch_rac_prep(mx, x, M, N, (int32_t)K, a_codes, a_scales, a_tensor_scale,
                                  w_scales, w_hi_t, chan_set, k, kp, R, W_S, ta, tw,
-                                 tile_rows_pad(M), tile_rows_pad(N), S(stream));
+                                 tile_rows_pad(M), tile_rows_pad(N), S(stream), status);
   if (e != hipSuccess) return hip_status(e, "rac_gemm (operand preparation)");
   return hip_status(launch_w4a4_gemm(g, 0, S(stream)), "rac_gemm");
 }
@@ -362,7 +379,7 @@ q4_status_t rac_gemm_eq21(int64_t M, int64_t N, int64_t K, const uint16_t* x,
                           const uint8_t* w_scales, const float* w_tensor_scale,
                           const int32_t* chan_set, int32_t k, void* Y, int32_t y_dtype,
                           float* resid_tensor_scale_out, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          int32_t* status, void* stream) {
   q4_status_t st = check_gemm("rac_gemm_eq21", Q4_NVFP4, M, N, K, a_codes, a_scales,
                               a_tensor_scale, w_codes, w_scales, w_tensor_scale, Y, y_dtype);
   if (st != Q4_OK) return st;
@@ -370,7 +387,7 @@ q4_status_t rac_gemm_eq21(int64_t M, int64_t N, int64_t K, const uint16_t* x,
     return fail(Q4_EINVAL, "rac_gemm_eq21: k %d outside [0, min(K, %d)]", k, Q4_MAX_TOPK);
   if (resid_tensor_scale_out) Q4_REQUIRE_SCALAR(resid_tensor_scale_out, 4);
   if (k > 0) {
-    Q4_REQUIRE_PTR(x);
+    if (M > 0) Q4_REQUIRE_PTR(x);
     Q4_REQUIRE_SCALAR(chan_set, 4);
     const size_t need = rac_gemm_eq21_workspace_size(M, N, K, k);
     if (!workspace || workspace_bytes < need)
@@ -378,10 +395,17 @@ q4_status_t rac_gemm_eq21(int64_t M, int64_t N, int64_t K, const uint16_t* x,
                   workspace_bytes);
     Q4_REQUIRE_PTR(workspace);
   }
-  if (M == 0 || N == 0) return Q4_OK;
-  if (k == 0)
+  if (status) Q4_REQUIRE_SCALAR(status, 4);
+  if (M == 0 || N == 0)
+    return empty_status("rac_gemm_eq21", Q4_NVFP4, K, a_tensor_scale, chan_set, k, status, stream);
+  if (k == 0) {
+    if (status) {
+      const hipError_t e = launch_fill_u32((uint32_t*)status, 1, 0u, S(stream));
+      if (e != hipSuccess) return hip_status(e, "rac_gemm_eq21 (status)");
+    }
     return w4a4_gemm(Q4_NVFP4, M, N, K, a_codes, a_scales, a_tensor_scale, w_codes, w_scales,
                      w_tensor_scale, Y, y_dtype, stream);
+  }
   GemmArgs g{};
   g.M = M;
   g.N = N;
@@ -421,7 +445,7 @@ q4_status_t rac_gemm_eq21(int64_t M, int64_t N, int64_t K, const uint16_t* x,
   hipError_t e = launch_eq21_prep(x, M, N, (int32_t)K, a_codes, a_scales, a_tensor_scale,
                                   w_codes, w_scales, chan_set, k, kp, R, W_S, slots,
                                   eq21_slots(M, K), r_ts, resid_tensor_scale_out, ta, tw,
-                                  tile_rows_pad(M), tile_rows_pad(N), S(stream));
+                                  tile_rows_pad(M), tile_rows_pad(N), S(stream), status);
   if (e != hipSuccess) return hip_status(e, "rac_gemm_eq21 (operand preparation)");
   return hip_status(launch_w4a4_gemm(g, 0, S(stream)), "rac_gemm_eq21");
 }
@@ -458,7 +482,7 @@ size_t q4_moe_sort_workspace_size(int64_t T, int32_t E, int32_t topk) {
 
 q4_status_t q4_moe_sort(const int32_t* topk_idx, int64_t T, int32_t E, int32_t topk,
                         int32_t* perm, int32_t* offsets, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        int32_t* status, void* stream) {
   if (T < 0 || T * 16 >= kMaxDim) return fail(Q4_ESHAPE, "q4_moe_sort: bad T");
   if (E < 1 || E > 1024) return fail(Q4_ESHAPE, "q4_moe_sort: need 1 <= E <= 1024");
   if (topk < 1 || topk > E || topk > 16) return fail(Q4_EINVAL, "q4_moe_sort: need 1 <= topk <= min(E, 16)");
@@ -471,6 +495,7 @@ q4_status_t q4_moe_sort(const int32_t* topk_idx, int64_t T, int32_t E, int32_t t
   if (!workspace || workspace_bytes < need)
     return fail(Q4_EWORKSPACE, "q4_moe_sort: workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   Q4_REQUIRE_PTR(workspace);
+  if (status) Q4_REQUIRE_SCALAR(status, 4);
   uint8_t* w = (uint8_t*)workspace;
   int32_t* counts = (int32_t*)w;
   w += moe_sort_workspace_bytes(T, E, topk);
@@ -480,7 +505,7 @@ q4_status_t q4_moe_sort(const int32_t* topk_idx, int64_t T, int32_t E, int32_t t
   w += align256((size_t)moe_max_tiles(T, E, topk) * 16);
   int32_t* ntiles = (int32_t*)w;
   return hip_status(launch_moe_sort(topk_idx, T, E, topk, perm, offsets, inv, tiles, ntiles,
-                                    counts, S(stream)),
+                                    counts, S(stream), nullptr, 0, nullptr, nullptr, status),
                     "q4_moe_sort");
 }
 
@@ -582,7 +607,7 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
                                   const float* w2_tensor_scales, const uint16_t* w13_hi_t,
                                   const uint16_t* w2_hi_t, int32_t rac_k, void* Y,
                                   int32_t y_dtype, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+                                  int32_t* status, void* stream) {
   const char* fn = "moe_w4a4_grouped_gemm";
   if (fmt != Q4_NVFP4 && fmt != Q4_MXFP4) return fail(Q4_EINVAL, "%s: bad format %d", fn, fmt);
   const bool mx = fmt == Q4_MXFP4;
@@ -619,7 +644,8 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   if (!workspace || workspace_bytes < L.total)
     return fail(Q4_EWORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, L.total, workspace_bytes);
   Q4_REQUIRE_PTR(workspace);
-  if (T == 0) return Q4_OK;
+  if (status) Q4_REQUIRE_SCALAR(status, 4);
+  if (T == 0) return status ? hip_status(launch_fill_u32((uint32_t*)status, 1, 0u, S(stream)), fn) : Q4_OK;
 
   uint8_t* w = (uint8_t*)workspace;
   auto P = [&](size_t off) { return (void*)(w + off); };
@@ -644,7 +670,7 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   Q4_TRY(launch_moe_sort(topk_idx, T, E, topk, perm, offsets, inv, tiles, ntiles,
                          (int32_t*)P(L.counts), s, a_rows, skinny ? kSkinnyBM : 0,
                          skinny ? (int32_t*)P(L.tiles_s) : nullptr,
-                         skinny ? (int32_t*)P(L.ntiles_s) : nullptr), "moe sort");
+                         skinny ? (int32_t*)P(L.ntiles_s) : nullptr, status), "moe sort");
   auto grouped_gemm = [&](GemmArgs& gg) {
     if (skinny) {
       gg.tiles = (const int32_t*)P(L.tiles_s);
@@ -729,7 +755,7 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   g2.ntiles_dev = ntiles;
   g2.a_rows = nullptr;
   Q4_TRY(grouped_gemm(g2), "moe w2 gemm");
-  Q4_TRY(launch_moe_combine((const float*)P(L.off[13]), inv, topk_w, T, topk, H, Y,
+  Q4_TRY(launch_moe_combine((const float*)P(L.off[13]), inv, topk_w, topk_idx, E, T, topk, H, Y,
                             y_dtype == Q4_OUT_BF16, s), "moe combine");
 #undef Q4_TRY
   return Q4_OK;

@@ -25,7 +25,10 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
 #pragma unroll
   for (int q = 0; q < MAXPER; ++q) {
     const int ex = q * 64 + lane;
-    v[q] = (q < per && ex < E) ? lg[ex] : -INFINITY;
+    // a NaN logit ranks below every number (as -inf; ties to the smaller
+    // expert), so every token gets topk distinct experts in [0, E)
+    const float l = (q < per && ex < E) ? lg[ex] : -INFINITY;
+    v[q] = l == l ? l : -INFINITY;
   }
   bool taken[MAXPER];
 #pragma unroll
@@ -62,7 +65,9 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
     float sum = 0.0f;
     float ex[16];
     for (int s = 0; s < topk; ++s) {
-      ex[s] = __expf(sel[s] - mx);
+      // equal to the largest: weight 1 before normalisation (also when every
+      // selected logit is -inf, which then gives uniform weights)
+      ex[s] = sel[s] == mx ? 1.0f : __expf(sel[s] - mx);
       sum += ex[s];
     }
     for (int s = 0; s < topk; ++s) {
@@ -78,17 +83,32 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
 // the blocks in order), then a scatter in which each row's rank inside its
 // block comes from wave ballots and per-wave counts.
 
-// bt[b][e] = rows of block b routed to expert e
+// An expert index outside [0, E) is invalid: it is counted as expert 0 (so
+// every index the sort writes stays in bounds), its slot gets weight 0 in the
+// combine, and the call's status word reports Q4_EINVAL.
+__device__ __forceinline__ int routed_expert(const int32_t* __restrict__ idx, int64_t i, bool valid,
+                                             int32_t E, bool& bad) {
+  const int e = valid ? idx[i] : -1;
+  bad = valid && (e < 0 || e >= E);
+  return bad ? 0 : e;
+}
+
+// bt[b][e] = rows of block b routed to expert e; flags[b] = block b holds an
+// invalid expert index
 __global__ __launch_bounds__(1024) void moe_block_hist_kernel(const int32_t* __restrict__ idx,
                                                               int64_t n, int32_t E,
-                                                              int32_t* __restrict__ bt) {
+                                                              int32_t* __restrict__ bt,
+                                                              int32_t* __restrict__ flags) {
   __shared__ int hist[1024];
   const int lane = threadIdx.x & 63;
   for (int e = threadIdx.x; e < E; e += 1024) hist[e] = 0;
   __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
   const bool valid = i < n;
-  const int e = valid ? idx[i] : -1;
+  bool bad;
+  const int e = routed_expert(idx, i, valid, E, bad);
+  const int any_bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) flags[blockIdx.x] = any_bad;
   uint64_t pending = __ballot(valid);
   while (pending) {
     const int leader = __ffsll((unsigned long long)pending) - 1;
@@ -125,11 +145,17 @@ __global__ __launch_bounds__(1024) void moe_offsets_kernel(int32_t* __restrict__
                                                            int32_t* __restrict__ tiles,
                                                            int32_t* __restrict__ ntiles, int32_t bm2,
                                                            int32_t* __restrict__ tiles2,
-                                                           int32_t* __restrict__ ntiles2) {
+                                                           int32_t* __restrict__ ntiles2,
+                                                           const int32_t* __restrict__ flags,
+                                                           int32_t* __restrict__ status) {
   __shared__ int s_cnt[1024];
   __shared__ int s_off[1025];
   __shared__ int s_tile[1025];
   __shared__ int s_tile2[1025];
+  int bad = 0;
+  for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) bad |= flags[b];
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0 && status) status[0] = bad ? 1 : 0;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     // sixteen blocks' counts loaded before any is rewritten, so the walk
     // waits for one load round trip per sixteen blocks
@@ -184,7 +210,8 @@ __global__ __launch_bounds__(1024) void moe_scatter_kernel(const int32_t* __rest
   __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
   const bool valid = i < n;
-  const int e = valid ? idx[i] : -1;
+  bool bad;
+  const int e = routed_expert(idx, i, valid, E, bad);
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   int rank = 0;
   uint64_t pending = __ballot(valid);
@@ -207,19 +234,22 @@ __global__ __launch_bounds__(1024) void moe_scatter_kernel(const int32_t* __rest
 }
 
 // y[t][h] = sum over slots s = 0..topk-1 of w[t][s] * out[inv_perm[t*topk+s]][h]
-// (fp32, slot order fixed).  One workgroup per (token, 1024 columns).
+// (fp32, slot order fixed; a slot with an invalid expert index contributes
+// nothing).  One workgroup per (token, 1024 columns).
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ out,
                                                           const int32_t* __restrict__ inv_perm,
-                                                          const float* __restrict__ w, int64_t T,
-                                                          int32_t topk, int32_t H, void* Y,
-                                                          int32_t y_bf16) {
+                                                          const float* __restrict__ w,
+                                                          const int32_t* __restrict__ idx,
+                                                          int32_t E, int64_t T, int32_t topk,
+                                                          int32_t H, void* Y, int32_t y_bf16) {
   const int nch = (H + 1023) / 1024;
   const int64_t t = blockIdx.x / nch;
   const int h0 = (int)(blockIdx.x % nch) * 1024 + threadIdx.x * 4;
   if (t >= T || h0 >= H) return;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
   for (int s = 0; s < topk; ++s) {
-    const float p = w[t * topk + s];
+    const int32_t ex = idx[t * topk + s];
+    const float p = (ex >= 0 && ex < E) ? w[t * topk + s] : 0.0f;
     const int64_t r = inv_perm[t * topk + s];
     const float4 v = *(const float4*)(out + r * H + h0);
     a0 = fmaf(p, v.x, a0);
@@ -251,22 +281,25 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int32_t E, int32_t t
   return hipGetLastError();
 }
 
+// block histograms [nb][E], then one invalid-index flag per block
 size_t moe_sort_workspace_bytes(int64_t T, int32_t E, int32_t topk) {
   const int64_t nb = (T * topk + 1023) / 1024;
-  return align256((size_t)(nb > 0 ? nb : 1) * E * 4);
+  const size_t b = (size_t)(nb > 0 ? nb : 1);
+  return align256(b * E * 4) + align256(b * 4);
 }
 
 hipError_t launch_moe_sort(const int32_t* idx, int64_t T, int32_t E, int32_t topk, int32_t* perm,
                            int32_t* offsets, int32_t* inv_perm, int32_t* tiles, int32_t* ntiles,
                            int32_t* counts, hipStream_t stream, int32_t* a_rows, int32_t bm2,
-                           int32_t* tiles2, int32_t* ntiles2) {
+                           int32_t* tiles2, int32_t* ntiles2, int32_t* status) {
   const int64_t n = T * topk;
   const int64_t nb = (n + 1023) / 1024;
+  int32_t* flags = counts + align256((size_t)(nb > 0 ? nb : 1) * E * 4) / 4;
   if (nb > 0)
     hipLaunchKernelGGL(moe_block_hist_kernel, dim3((unsigned)nb), dim3(1024), 0, stream, idx, n,
-                       E, counts);
+                       E, counts, flags);
   hipLaunchKernelGGL(moe_offsets_kernel, dim3(1), dim3(1024), 0, stream, counts, nb, E, offsets,
-                     tiles, ntiles, bm2, tiles2, ntiles2);
+                     tiles, ntiles, bm2, tiles2, ntiles2, (const int32_t*)flags, status);
   if (nb > 0)
     hipLaunchKernelGGL(moe_scatter_kernel, dim3((unsigned)nb), dim3(1024), 0, stream, idx, n, E,
                        (const int32_t*)counts, (const int32_t*)offsets, perm, inv_perm, topk,
@@ -275,12 +308,12 @@ hipError_t launch_moe_sort(const int32_t* idx, int64_t T, int32_t E, int32_t top
 }
 
 hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const float* topk_w,
-                              int64_t T, int32_t topk, int32_t H, void* Y, int32_t y_bf16,
-                              hipStream_t stream) {
+                              const int32_t* topk_idx, int32_t E, int64_t T, int32_t topk,
+                              int32_t H, void* Y, int32_t y_bf16, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int64_t nch = (H + 1023) / 1024;
   hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)(T * nch)), dim3(256), 0, stream, out,
-                     inv_perm, topk_w, T, topk, H, Y, y_bf16);
+                     inv_perm, topk_w, topk_idx, E, T, topk, H, Y, y_bf16);
   return hipGetLastError();
 }
 

@@ -34,24 +34,33 @@ struct PrepArgs {
   // workgroup ranges, in launch order: W_S tiles, R, A records, W records
   int64_t n_ws, n_r, n_ta, n_tw;
   int64_t ws_gx;  // W_S tiles along N
+  int32_t* status;  // optional: Q4_OK, or Q4_EINVAL for an invalid channel set
 };
 
 template <bool MX>
 __global__ __launch_bounds__(256) void rac_prep_kernel(PrepArgs p) {
   __shared__ uint16_t tile[64][66];
   int64_t b = blockIdx.x;
+  // every gathering workgroup checks the whole channel set (at most 1024
+  // entries, L2-resident); an invalid set gathers zeros, so the GEMM adds no
+  // compensation, and workgroup 0 reports it
+  const bool gathers = b < p.n_ws + p.n_r;
+  const bool ok = gathers ? chan_set_ok(p.idx, p.k, p.K) : true;
+  if (b == 0 && threadIdx.x == 0 && p.status) p.status[0] = ok ? 0 : 1;
+  const int32_t k = ok ? p.k : 0;
   if (b < p.n_ws) {
     const int64_t by = b / p.ws_gx;
-    wsel_gather_part(p.w_hi_t, p.K, p.N, p.idx, p.k, p.kp, p.W_S, 0, b - by * p.ws_gx, (int)by,
+    wsel_gather_part(p.w_hi_t, p.K, p.N, p.idx, k, p.kp, p.W_S, 0, b - by * p.ws_gx, (int)by,
                      tile);
     return;
   }
   b -= p.n_ws;
   if (b < p.n_r) {
-    residual_gather_part<MX>(p.x, p.M, p.K, p.a_codes, p.a_scales, p.a_ts, p.idx, p.k, p.R, p.kp,
+    residual_gather_part<MX>(p.x, p.M, p.K, p.a_codes, p.a_scales, p.a_ts, p.idx, k, p.R, p.kp,
                              b, p.n_r);
     return;
   }
+  if (b - p.n_r >= p.n_ta + p.n_tw) return;  // the status-only workgroup
   b -= p.n_r;
   if (b < p.n_ta) {
     scale_tile_part(p.a_scales, p.M, p.K, p.a_pad, p.a_tiles, b, p.n_ta);
@@ -72,8 +81,10 @@ hipError_t launch_rac_prep(bool mx, const uint16_t* x, int64_t M, int64_t N, int
                            const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                            const uint8_t* w_scales, const uint16_t* w_hi_t, const int32_t* idx,
                            int32_t k, int32_t kp, uint16_t* R, uint16_t* W_S, uint8_t* a_tiles,
-                           uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream) {
+                           uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream,
+                           int32_t* status) {
   PrepArgs p{};
+  p.status = status;
   p.x = x;
   p.a_codes = a_codes;
   p.a_scales = a_scales;
@@ -99,7 +110,8 @@ hipError_t launch_rac_prep(bool mx, const uint16_t* x, int64_t M, int64_t N, int
   p.n_r = rac ? grid_stride_blocks(residual_gather_items(M, kp)) : 0;
   p.n_ta = tiles ? grid_stride_blocks((int64_t)(K / 128) * a_pad) : 0;
   p.n_tw = tiles ? grid_stride_blocks((int64_t)(K / 128) * w_pad) : 0;
-  const int64_t grid = p.n_ws + p.n_r + p.n_ta + p.n_tw;
+  int64_t grid = p.n_ws + p.n_r + p.n_ta + p.n_tw;
+  if (grid == 0 && status) grid = 1;   // one workgroup writes the status word
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (mx)
@@ -229,6 +241,7 @@ struct Eq21PrepArgs {
   int32_t K, k, kp;
   // workgroup ranges, in launch order: W', R', A records, W records
   int64_t n_w, n_r, n_ta, n_tw;
+  int32_t* status;  // optional: Q4_OK, or Q4_EINVAL for an invalid channel set
 };
 
 __device__ __forceinline__ int clamp_chan(const int32_t* idx, int t, int k, int K) {
@@ -240,9 +253,15 @@ __global__ __launch_bounds__(256) void eq21_prep_kernel(Eq21PrepArgs p) {
   __shared__ uint32_t red[256];
   __shared__ int32_t sidx[Q4_MAX_TOPK];
   int64_t b = blockIdx.x;
-  if (b < p.n_w + p.n_r) {
+  // an invalid channel set (not ascending, unique and in [0, K)) gathers
+  // zeros, so the GEMM adds no compensation; workgroup 0 reports it
+  const bool gathers = b < p.n_w + p.n_r;
+  const bool ok = gathers ? chan_set_ok(p.idx, p.k, p.K) : true;
+  if (b == 0 && threadIdx.x == 0 && p.status) p.status[0] = ok ? 0 : 1;
+  const int32_t kk = ok ? p.k : 0;
+  if (gathers) {
     // the channel set, clamped into [0, K), staged once per workgroup
-    for (int t = threadIdx.x; t < p.kp; t += 256) sidx[t] = clamp_chan(p.idx, t, p.k, p.K);
+    for (int t = threadIdx.x; t < p.kp; t += 256) sidx[t] = clamp_chan(p.idx, t, kk, p.K);
     __syncthreads();
   }
   if (b < p.n_w) {
@@ -265,7 +284,7 @@ __global__ __launch_bounds__(256) void eq21_prep_kernel(Eq21PrepArgs p) {
       for (int q = 0; q < 8; ++q) {
         if (j0 + q >= p.N) break;
         const float val = e2m1_value((cb[q] >> ((c & 1) * 4)) & 15u) * e4m3_to_f32(sb[q]);
-        p.W_S[(j0 + q) * p.kp + t] = (uint16_t)(t < p.k ? f32_to_bf16_rne(val) : 0u);
+        p.W_S[(j0 + q) * p.kp + t] = (uint16_t)(t < kk ? f32_to_bf16_rne(val) : 0u);
       }
     }
     return;
@@ -332,7 +351,7 @@ __global__ __launch_bounds__(256) void eq21_prep_kernel(Eq21PrepArgs p) {
         const float sbv = e4m3_to_f32(sc);
         const uint32_t nib = e2m1_nibble_exact(dc, sbv, sr);
         p.R[(i0 + q) * p.kp + t] =
-            (uint16_t)(t < p.k ? f32_to_bf16_rne(e2m1_value(nib) * sbv) : 0u);
+            (uint16_t)(t < kk ? f32_to_bf16_rne(e2m1_value(nib) * sbv) : 0u);
       }
     }
     return;
@@ -353,7 +372,8 @@ hipError_t launch_eq21_prep(const uint16_t* x, int64_t M, int64_t N, int32_t K,
                             const uint8_t* w_codes, const uint8_t* w_scales, const int32_t* idx,
                             int32_t k, int32_t kp, uint16_t* R, uint16_t* W_S, uint32_t* slots,
                             int32_t nslots, float* r_ts, float* r_ts_out, uint8_t* a_tiles,
-                            uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream) {
+                            uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream,
+                            int32_t* status) {
   Eq21AmaxArgs a{};
   a.x = (const uint4*)x;
   a.codes = (const uint2*)a_codes;
@@ -387,6 +407,7 @@ hipError_t launch_eq21_prep(const uint16_t* x, int64_t M, int64_t N, int32_t K,
   p.K = K;
   p.k = k;
   p.kp = kp;
+  p.status = status;
   const bool tiles = a_tiles && w_tiles;
   p.n_w = grid_stride_blocks((N + 7) / 8 * kp);
   p.n_r = grid_stride_blocks((M + 3) / 4 * kp);

@@ -25,10 +25,12 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
                            hipStream_t stream);
 hipError_t launch_select(const double* scores, int64_t cols, int32_t topk, int32_t* idx,
                          hipStream_t stream);
+// p[0..n) = v (a kernel, not a memset, so the write may sit in a captured graph)
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_residual_gather(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
                                   const uint8_t* codes, const uint8_t* scales, const float* ts,
                                   const int32_t* idx, int32_t k, uint16_t* R, int64_t ld_r,
-                                  hipStream_t stream);
+                                  hipStream_t stream, int32_t* status = nullptr);
 hipError_t launch_wsel_gather(const uint16_t* w_hi_t, int64_t batch, int64_t K, int64_t N,
                               const int32_t* idx, int32_t k, int32_t kp, uint16_t* ws,
                               hipStream_t stream);
@@ -93,12 +95,14 @@ hipError_t launch_eq21_prep(const uint16_t* x, int64_t M, int64_t N, int32_t K,
                             const uint8_t* w_codes, const uint8_t* w_scales, const int32_t* idx,
                             int32_t k, int32_t kp, uint16_t* R, uint16_t* W_S, uint32_t* slots,
                             int32_t nslots, float* r_ts, float* r_ts_out, uint8_t* a_tiles,
-                            uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream);
+                            uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream,
+                            int32_t* status = nullptr);
 hipError_t launch_rac_prep(bool mx, const uint16_t* x, int64_t M, int64_t N, int32_t K,
                            const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
                            const uint8_t* w_scales, const uint16_t* w_hi_t, const int32_t* idx,
                            int32_t k, int32_t kp, uint16_t* R, uint16_t* W_S, uint8_t* a_tiles,
-                           uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream);
+                           uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream,
+                           int32_t* status = nullptr);
 
 constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 128;
@@ -113,10 +117,10 @@ hipError_t launch_moe_sort(const int32_t* idx, int64_t T, int32_t E, int32_t top
                            int32_t* offsets, int32_t* inv_perm, int32_t* tiles,
                            int32_t* ntiles, int32_t* counts, hipStream_t stream,
                            int32_t* a_rows = nullptr, int32_t bm2 = 0, int32_t* tiles2 = nullptr,
-                           int32_t* ntiles2 = nullptr);
+                           int32_t* ntiles2 = nullptr, int32_t* status = nullptr);
 hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const float* topk_w,
-                              int64_t T, int32_t topk, int32_t H, void* Y, int32_t y_bf16,
-                              hipStream_t stream);
+                              const int32_t* topk_idx, int32_t E, int64_t T, int32_t topk,
+                              int32_t H, void* Y, int32_t y_bf16, hipStream_t stream);
 // grouped GEMM over tiles of at most kSkinnyBM rows (few rows per expert)
 constexpr int kSkinnyBM = 32;
 hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t stream);

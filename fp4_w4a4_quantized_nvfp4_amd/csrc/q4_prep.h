@@ -25,6 +25,20 @@ __device__ __forceinline__ uint4 swz_sc_rec(uint4 v, int row) {
   return r;
 }
 
+// Whether the channel set holds k ascending, unique channels in [0, cols).
+// Every thread of the workgroup must call it (it ends in a workgroup-wide
+// reduction).  A kernel that finds the set invalid gathers nothing (k taken as
+// 0, so the compensation adds zero) and reports Q4_EINVAL in its status word.
+__device__ __forceinline__ bool chan_set_ok(const int32_t* __restrict__ idx, int32_t k,
+                                            int64_t cols) {
+  int bad = 0;
+  for (int t = threadIdx.x; t < k; t += blockDim.x) {
+    const int32_t c = idx[t];
+    bad |= (c < 0) | ((int64_t)c >= cols) | (t > 0 && idx[t - 1] >= c);
+  }
+  return __syncthreads_or(bad) == 0;
+}
+
 // R[i][t] = bf16(RN32(x[i][S_t] - dequant)) for t < k, 0 for k <= t < ld_r.
 // One thread per (4 consecutive rows, t), t fastest across lanes: S is
 // ascending and its channels cluster in a few blocks (the outlier blocks), so

@@ -18,6 +18,13 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t n, u
   if (i < n) p[i] = v;
 }
 
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p,
+                     n, v);
+  return hipGetLastError();
+}
+
 __device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t w) {
   uint32_t lo = w & 0x7fffu, hi = (w >> 16) & 0x7fffu;
   return lo > hi ? lo : hi;
@@ -808,8 +815,11 @@ template <bool MX>
 __global__ __launch_bounds__(256) void residual_gather_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int32_t cols, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ ts,
-    const int32_t* __restrict__ idx, int32_t k, uint16_t* __restrict__ R, int64_t ld_r) {
-  residual_gather_part<MX>(x, rows, cols, codes, scales, ts, idx, k, R, ld_r, blockIdx.x,
+    const int32_t* __restrict__ idx, int32_t k, uint16_t* __restrict__ R, int64_t ld_r,
+    int32_t* __restrict__ status) {
+  const bool ok = chan_set_ok(idx, k, cols);
+  if (status && blockIdx.x == 0 && threadIdx.x == 0) status[0] = ok ? 0 : 1;
+  residual_gather_part<MX>(x, rows, cols, codes, scales, ts, idx, ok ? k : 0, R, ld_r, blockIdx.x,
                            gridDim.x);
 }
 
@@ -820,7 +830,9 @@ __global__ __launch_bounds__(256) void wsel_gather_kernel(const uint16_t* __rest
                                                           int32_t k, int32_t kp,
                                                           uint16_t* __restrict__ ws) {
   __shared__ uint16_t tile[64][66];
-  wsel_gather_part(w_hi_t, K, N, idx, k, kp, ws, blockIdx.z, blockIdx.x, blockIdx.y, tile);
+  const bool ok = chan_set_ok(idx, k, K);
+  wsel_gather_part(w_hi_t, K, N, idx, ok ? k : 0, kp, ws, blockIdx.z, blockIdx.x, blockIdx.y,
+                   tile);
 }
 
 // out[b][c][r] = in[b][r][c]
@@ -1028,17 +1040,17 @@ hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, con
 hipError_t launch_residual_gather(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
                                   const uint8_t* codes, const uint8_t* scales, const float* ts,
                                   const int32_t* idx, int32_t k, uint16_t* R, int64_t ld_r,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, int32_t* status) {
   const int64_t total = residual_gather_items(rows, ld_r);
-  if (total == 0) return hipSuccess;
+  if (total == 0 && !status) return hipSuccess;
   int64_t grid = (total + 255) / 256;
-  grid = grid > 65536 ? 65536 : grid;
+  grid = grid > 65536 ? 65536 : (grid < 1 ? 1 : grid);
   if (mx)
     hipLaunchKernelGGL(residual_gather_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x,
-                       rows, (int32_t)cols, codes, scales, ts, idx, k, R, ld_r);
+                       rows, (int32_t)cols, codes, scales, ts, idx, k, R, ld_r, status);
   else
     hipLaunchKernelGGL(residual_gather_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       x, rows, (int32_t)cols, codes, scales, ts, idx, k, R, ld_r);
+                       x, rows, (int32_t)cols, codes, scales, ts, idx, k, R, ld_r, status);
   return hipGetLastError();
 }
 

@@ -43,11 +43,18 @@
  *   MXFP4: block of 32, scale 2^e, e = floor(log2 amax_block) - 2 clamped to
  *         [-127, 127] (byte 0 for an all-zero block), c nearest to |x| / 2^e.
  *   residual r = RN32(x - dequant(x)) (the negated Eq. 20 error);
- *   channel score_j = sum_i r_ij^2 in fp64 (Eq. 23 squared), summed over rows
- *         ascending inside tiles of 32 rows, tile sums ascending inside groups
- *         of 8 tiles, then group sums ascending (each level starts at zero);
+ *   channel score_j = sum_i r_ij^2 (Eq. 23 squared): the exact fp64 squares
+ *         summed in fp64 in a fixed order (so a call is deterministic), which
+ *         is within (rows - 1) * 2^-53 relative of the exact sum;
  *   channel set S = the topk channels of largest score, ties to the smaller
  *         channel, listed in ascending channel order (Eq. 24, absolute k).
+ *
+ * Status words: calls that take a device channel set or device expert indices
+ * also take `status`, an optional device int32 [1].  When given, the call
+ * writes Q4_OK there, or Q4_EINVAL if those device inputs break their
+ * contract (the call then takes the documented safe path instead of reading
+ * out of bounds or double counting).  It is written in stream order, like the
+ * outputs.
  */
 #ifndef Q4RAC_H
 #define Q4RAC_H
@@ -72,8 +79,6 @@ typedef enum {
 typedef enum { Q4_NVFP4 = 0, Q4_MXFP4 = 1 } q4_format_t;
 typedef enum { Q4_OUT_F32 = 0, Q4_OUT_BF16 = 1 } q4_dtype_t;
 
-#define Q4_SCORE_TILE_ROWS 32
-#define Q4_SCORE_GROUP_TILES 8
 #define Q4_MAX_TOPK 1024
 
 /* (host) message for the last non-OK status returned in this thread. */
@@ -105,15 +110,19 @@ q4_status_t nvfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols,
                            int32_t *chan_idx, void *workspace, size_t workspace_bytes,
                            void *stream);
 
-/* MXFP4 variant: cols % 32 == 0; scales uint8 [rows][cols/32] E8M0; no tensor
- * scale.  Residual statistics and selection as nvfp4_quantize. */
+/* MXFP4 variant (the open-standard MXFP4 with power-of-two block scales named
+ * by the Rollout-ResQ abstract on the listing page thelatestinai.com,
+ * papers/2607.15810; block rule of the OCP MX format): cols % 32 == 0; scales
+ * uint8 [rows][cols/32] E8M0; no tensor scale.  Residual statistics and
+ * selection as nvfp4_quantize (QUADS section 3.3, Eq. 20, 23, 24). */
 q4_status_t mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_t *codes,
                            uint8_t *scales, double *chan_score, int32_t topk, int32_t *chan_idx,
                            void *workspace, size_t workspace_bytes, void *stream);
 
-/* Trainer-side weight fake quantization (QUADS section 3.2, Eq. 12: the weight
- * QDQ operator whose scale layout and rounding match the rollout quantizer, so
- * that trainer and rollout see the same discretized weight, Eq. 16):
+/* Trainer-side weight fake quantization (QUADS section 3.2, Eq. 12, and the
+ * alignment of Eq. 16: the trainer's weight quantize-dequantize must use the
+ * same block layout and the same rounding as the rollout kernels, so both
+ * sides compute with one discretized weight):
  *   y = c * sb * s_t of nvfp4_quantize(x) (the same kernels, so the codes,
  *       scales and s_t are those nvfp4_quantize gives), rounded once to fp32
  *       or to bf16 (y_dtype).
@@ -137,11 +146,12 @@ q4_status_t q4_select_channels(const double *chan_score, int64_t cols, int32_t t
  * R[i][t] = bf16_RNE(r[i][S_t]) for t < k, and 0 for k <= t < ld_r, where r is
  * the fp32 residual of x against its quantized form (codes/scales/tensor scale;
  * tensor_scale must be NULL for MXFP4).  R is bf16 [rows][ld_r], ld_r >= k.
- * Out-of-range channel indices are clamped into [0, cols). */
+ * chan_idx must hold k ascending, unique channels in [0, cols); a set that
+ * does not gathers nothing (R all zero) and sets *status to Q4_EINVAL. */
 q4_status_t q4_residual_gather(int32_t fmt, const uint16_t *x, int64_t rows, int64_t cols,
                                const uint8_t *codes, const uint8_t *scales,
                                const float *tensor_scale, const int32_t *chan_idx, int32_t k,
-                               uint16_t *R, int64_t ld_r, void *stream);
+                               uint16_t *R, int64_t ld_r, int32_t *status, void *stream);
 
 /* ---------------------------------------------------------------- GEMM
  * W4A4 GEMM (QUADS section 3.3, the native W4A4 product that Eq. 22's remark
@@ -164,8 +174,11 @@ q4_status_t w4a4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_
  *   x       bf16 [M][K], the activation that produced A.
  *   w_hi_t  bf16 [K][N]: the transposed bf16 weight (channel-major), so the
  *           selected rows S_t are contiguous.
- *   chan_set int32 [k] ascending unique channels in [0, K) (out-of-range
- *           entries are clamped); 0 <= k <= min(K, Q4_MAX_TOPK).
+ *   chan_set int32 [k] ascending unique channels in [0, K);
+ *           0 <= k <= min(K, Q4_MAX_TOPK).  Checked on the device: a set
+ *           that is not ascending, unique and in range adds no compensation
+ *           (Y is then exactly w4a4_gemm) and sets *status to Q4_EINVAL.
+ *   status  int32 [1] (out, device) or NULL: Q4_OK / Q4_EINVAL as above.
  * k == 0 gives exactly w4a4_gemm.
  * Workspace: R and the selected weight columns (when k > 0) and, for NVFP4
  * with K % 128 == 0, re-laid-out fp16 copies of both operands' block scales
@@ -178,7 +191,8 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
                      const float *a_tensor_scale, const uint8_t *w_codes,
                      const uint8_t *w_scales, const float *w_tensor_scale,
                      const uint16_t *w_hi_t, const int32_t *chan_set, int32_t k, void *Y,
-                     int32_t y_dtype, void *workspace, size_t workspace_bytes, void *stream);
+                     int32_t y_dtype, void *workspace, size_t workspace_bytes, int32_t *status,
+                     void *stream);
 
 /* Page-literal compensation (QUADS section 3.3, Eq. 20-21), NVFP4 only.  The
  * quantization error dX = dequant(A) - x is quantized as an activation of its
@@ -191,7 +205,8 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
  *     = s_A s_W sum_K d_A d_W - s_R s_W sum_{t<k} (c sb)_dX[i][S_t] (c sb)_W[j][S_t].
  * Both factors of the second sum are exact in bf16; it runs as extra bf16 MFMA
  * steps into the same fp32 tile.
- *   x, A, W, chan_set, k, Y, y_dtype as rac_gemm (A and W NVFP4).
+ *   x, A, W, chan_set, k, Y, y_dtype, status as rac_gemm (A and W NVFP4; an
+ *           invalid channel set adds no compensation and reports Q4_EINVAL).
  *   resid_tensor_scale_out fp32 [1] (out) or NULL: s_R, written when M, N and
  *           k are all > 0.
  * k == 0 gives exactly w4a4_gemm.  Range (documented, not checked): the W4A4
@@ -210,23 +225,34 @@ q4_status_t rac_gemm_eq21(int64_t M, int64_t N, int64_t K, const uint16_t *x,
                           const uint8_t *w_scales, const float *w_tensor_scale,
                           const int32_t *chan_set, int32_t k, void *Y, int32_t y_dtype,
                           float *resid_tensor_scale_out, void *workspace,
-                          size_t workspace_bytes, void *stream);
+                          size_t workspace_bytes, int32_t *status, void *stream);
 
 /* ---------------------------------------------------------------- MoE
- * Router (top-k MoE of section 3.3's W13 site): for each token the topk experts
- * of largest logit (ties to the smaller expert), highest first, and their
- * weights softmax(selected logits).  logits fp32 [T][E]; 1 <= topk <= min(E, 16);
- * E <= 1024.  topk_idx int32 [T][topk], topk_w fp32 [T][topk]. */
+ * The QUADS page compensates the activations of MoE expert projections: its
+ * profiled site is the W13 (gate/up) input, section 3.3 "Online per-channel
+ * selection", and Figure 4b compares layer-wise MoE outputs.  It does not
+ * spell out the expert block; the calls below are the standard top-k SwiGLU
+ * expert layer.
+ *
+ * Router: for each token the topk experts of largest logit (ties to the
+ * smaller expert), highest first, and their weights softmax(selected logits).
+ * logits fp32 [T][E]; 1 <= topk <= min(E, 16); E <= 1024.  topk_idx int32
+ * [T][topk], topk_w fp32 [T][topk].  A NaN logit ranks below every number
+ * (every token still gets topk distinct experts in [0, E)). */
 q4_status_t q4_moe_route(const float *logits, int64_t T, int32_t E, int32_t topk,
                          int32_t *topk_idx, float *topk_w, void *stream);
 
-/* Token sort: routed rows (t, s) ordered by (expert, t, s).
+/* Token sort for the grouped GEMM of the W13 site (section 3.3): routed rows
+ * (t, s) ordered by (expert, t, s), a stable counting sort.
  * perm int32 [T*topk]: perm[r] = t*topk + s of sorted row r; offsets int32
- * [E+1] (offsets[e] = first sorted row of expert e).  workspace: q4_moe_sort_workspace_size. */
+ * [E+1] (offsets[e] = first sorted row of expert e).  workspace:
+ * q4_moe_sort_workspace_size.  An index outside [0, E) is invalid: it is
+ * sorted as expert 0 (nothing is written out of bounds) and *status (device
+ * int32 [1], optional) is set to Q4_EINVAL. */
 size_t q4_moe_sort_workspace_size(int64_t T, int32_t E, int32_t topk);
 q4_status_t q4_moe_sort(const int32_t *topk_idx, int64_t T, int32_t E, int32_t topk,
                         int32_t *perm, int32_t *offsets, void *workspace,
-                        size_t workspace_bytes, void *stream);
+                        size_t workspace_bytes, int32_t *status, void *stream);
 
 /* Weight preparation (offline).
  * q4_transpose_bf16: out[c][r] = in[r][c] for a [rows][cols] bf16 matrix,
@@ -241,7 +267,9 @@ q4_status_t q4_transpose_bf16(const uint16_t *in, int64_t batch, int64_t rows, i
 q4_status_t q4_moe_pack_w13(const uint16_t *w13, int32_t E, int32_t F, int32_t H,
                             uint16_t *out, void *stream);
 
-/* Token-sorted grouped W4A4 + RAC SwiGLU expert layer (configs: top-k MoE).
+/* Token-sorted grouped W4A4 + RAC SwiGLU expert layer: the compensation of
+ * QUADS section 3.3 (Eq. 21-24) at both activation sites of the expert block,
+ * the W13 input (the page's profiled site) and the W2 input.
  *   tokens     bf16 [T][H]; H % 32 == 0 (MXFP4: % 32; NVFP4 GEMM: % 32).
  *   topk_idx, topk_w: routing as produced by q4_moe_route.
  *   w13_*      stacked packed W13 of all experts: rows E*2F (q4_moe_pack_w13
@@ -256,7 +284,9 @@ q4_status_t q4_moe_pack_w13(const uint16_t *w13, int32_t E, int32_t F, int32_t H
  * GEMM over sorted rows with the SwiGLU epilogue h = bf16(silu(g) * u); quantize
  * h over all T*topk sorted rows (one s_t, one selection); W2 RAC GEMM; combine.
  * F % 32 == 0, H % 32 == 0.  The workspace holds every intermediate at the
- * offsets reported by moe_workspace_layout. */
+ * offsets reported by moe_workspace_layout.  An expert index outside [0, E)
+ * is invalid: its slot is computed as expert 0 but adds nothing to y, and
+ * *status (device int32 [1], optional) is set to Q4_EINVAL. */
 size_t moe_workspace_size(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F,
                           int32_t topk, int32_t rac_k);
 /* (host) offsets[0..Q4_MOE_WS_FIELDS-1] in bytes from the workspace base:
@@ -278,7 +308,7 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t *tokens, int64_t T
                                   const float *w2_tensor_scales, const uint16_t *w13_hi_t,
                                   const uint16_t *w2_hi_t, int32_t rac_k, void *Y,
                                   int32_t y_dtype, void *workspace, size_t workspace_bytes,
-                                  void *stream);
+                                  int32_t *status, void *stream);
 
 #ifdef __cplusplus
 }

@@ -48,6 +48,17 @@ def check_bf16_output(y_bits: np.ndarray, ref: np.ndarray, tol: float = GEMM_TOL
     assert ok.all(), f"bf16 output off at {np.argwhere(~ok)[:5].tolist()}"
 
 
+_CACHE = {}
+
+
+def cached(key, fn):
+    """fn() computed once per test process (large oracle results and inputs
+    that several tests share)."""
+    if key not in _CACHE:
+        _CACHE[key] = fn()
+    return _CACHE[key]
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()

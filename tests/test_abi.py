@@ -59,29 +59,38 @@ def test_shape_and_pointer_errors(L):
     assert L.w4a4_gemm(0, 8, 8, 64, fake, fake, None, fake, fake, fake, fake, 0, None) == 1
     assert L.w4a4_gemm(1, 8, 8, 64, fake, fake, fake, fake, fake, None, fake, 0, None) == 1
     assert L.w4a4_gemm(0, 8, 8, 64, fake, fake, fake, fake, fake, fake, fake, 5, None) == 1
-    # RAC: k > K, missing workspace
+    # RAC: k > K, missing workspace, misaligned status word
     assert L.rac_gemm(0, 8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, fake, 65,
-                      fake, 0, fake, 1 << 30, None) == 1
+                      fake, 0, fake, 1 << 30, None, None) == 1
     assert L.rac_gemm(0, 8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, fake, 16,
-                      fake, 0, None, 0, None) == 4
+                      fake, 0, None, 0, None, None) == 4
+    assert L.rac_gemm(0, 8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, fake, 16,
+                      fake, 0, fake, 1 << 30, C.c_void_p(0x100002), None) == 3
+    assert "status" in _err(L)
     # Eq. 21 compensation: K % 32, k > K, missing workspace, misaligned scale output,
     # missing tensor scale (NVFP4 only)
     assert L.rac_gemm_eq21(8, 8, 48, fake, fake, fake, fake, fake, fake, fake, fake, 16, fake, 0,
-                           None, fake, 1 << 30, None) == 2
+                           None, fake, 1 << 30, None, None) == 2
     assert L.rac_gemm_eq21(8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, 65, fake, 0,
-                           None, fake, 1 << 30, None) == 1
+                           None, fake, 1 << 30, None, None) == 1
     assert L.rac_gemm_eq21(8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, 16, fake, 0,
-                           None, None, 0, None) == 4
+                           None, None, 0, None, None) == 4
     assert L.rac_gemm_eq21(8, 8, 64, fake, fake, fake, fake, fake, fake, fake, fake, 16, fake, 0,
-                           C.c_void_p(0x100002), fake, 1 << 30, None) == 3
+                           C.c_void_p(0x100002), fake, 1 << 30, None, None) == 3
     assert L.rac_gemm_eq21(8, 8, 64, fake, fake, fake, None, fake, fake, fake, fake, 16, fake, 0,
-                           None, fake, 1 << 30, None) == 1
+                           None, fake, 1 << 30, None, None) == 1
     assert "a_ts" in _err(L)
+    # residual gather: ld_r < k
+    assert L.q4_residual_gather(0, fake, 4, 64, fake, fake, fake, fake, 8, fake, 4, None, None) == 1
     # MoE: bad E, F % 32, topk > E
     assert L.q4_moe_route(fake, 4, 0, 1, fake, fake, None) == 2
     assert L.q4_moe_route(fake, 4, 8, 9, fake, fake, None) == 1
     assert L.moe_w4a4_grouped_gemm(0, fake, 4, 64, fake, fake, 2, 4, 48, fake, fake, fake, fake,
-                                   fake, fake, fake, fake, 0, fake, 1, fake, 1 << 30, None) == 2
+                                   fake, fake, fake, fake, 0, fake, 1, fake, 1 << 30, None,
+                                   None) == 2
+    # sort: topk > 16, misaligned status
+    assert L.q4_moe_sort(fake, 4, 32, 17, fake, fake, fake, 1 << 20, None, None) == 1
+    assert L.q4_moe_sort(fake, 4, 32, 2, fake, fake, fake, 1 << 20, C.c_void_p(0x100002), None) == 3
     assert L.q4_moe_pack_w13(fake, 2, 40, 64, fake, None) == 2
 
 

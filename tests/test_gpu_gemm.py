@@ -6,7 +6,8 @@ import torch
 
 import oracle
 from workloads import bf16_bits_from_f32, make_inputs
-from tests.gpu_util import GEMM_TOL, check_bf16_output, dev, gemm_rel_err, host, say
+from tests.gpu_util import GEMM_TOL, cached, check_bf16_output, dev, gemm_rel_err, host, say
+from tests.parity import check_scores, check_selection
 
 pytestmark = pytest.mark.gpu
 
@@ -70,18 +71,25 @@ def test_exact_special_case_bit_identical(M, N, K, scales):
     assert np.array_equal(Y.astype(np.float64), ref)
 
 
+def _gpu_selection(m, x, Ao, k, fmt="nv"):
+    """GPU channel selection on x, validated against the oracle's exact scores;
+    returns (device S, host S) -- the host copy is the oracle's S downstream."""
+    if not k:
+        return None, np.zeros(0, dtype=np.int64)
+    qs = m.mxfp4_quantize(x, topk=k) if fmt == "mx" else m.nvfp4_quantize(x, topk=k)
+    ref = oracle.channel_scores(Ao.resid)
+    gsc = host(qs["chan_score"])
+    check_scores(gsc, ref, Ao.resid.shape[0])
+    So = check_selection(host(qs["chan_idx"]), ref, k, Ao.resid.shape[0], gpu_scores=gsc)
+    return qs["chan_idx"], So
+
+
 def _check_rac(xb, wb, k, out_dtype, fmt="nv"):
     say(f"rac parity x={xb.shape} w={wb.shape} k={k} out={out_dtype} fmt={fmt}")
     m = q4()
     x, A, W, Ao, Wo = _quant_pair(m, xb, wb, fmt)
     w_hi_t = m.q4_transpose_bf16(dev(wb))
-    if k:
-        qs = m.mxfp4_quantize(x, topk=k) if fmt == "mx" else m.nvfp4_quantize(x, topk=k)
-        S = qs["chan_idx"]
-        So = oracle.select_topk(oracle.channel_scores(Ao.resid), k)
-        assert np.array_equal(host(S), So)
-    else:
-        S, So = None, np.zeros(0, dtype=np.int32)
+    S, So = _gpu_selection(m, x, Ao, k, fmt)
     Y = m.rac_gemm(x, A, W, w_hi_t, S, out_dtype=out_dtype)
     Ro = oracle.residual_gather(Ao.resid, So)
     ref = oracle.rac_gemm(Ao, Wo, Ro, wb, So)
@@ -122,37 +130,73 @@ def test_ragged_shapes(M, N, K, k):
     _check_rac(xb, wb, k, 1)
 
 
-def test_dense_prefill_workload_sampled():
-    """8192 x 14336 x 4096, k = 128, bf16 output: quantization bit-exact on the
-    full x, W sampled rows; GEMM checked on 96 sampled output rows."""
+def test_dense_prefill_workload_full():
+    """8192 x 14336 x 4096, k = 128: x quantization bit-exact, scores within the
+    summation bound and the selection validated, W codes and scales bit-exact
+    on every row, and EVERY output element of rac_gemm against the fp64
+    oracle, in bf16 (the workload's output type) and in fp32."""
     m = q4()
-    d = make_inputs("dense_8192x14336x4096")
+    d = cached("dense_inputs", lambda: make_inputs("dense_8192x14336x4096"))
     xb, wb = d["x"], d["w"]
-    say("prefill workload: quantize on GPU")
+    say("prefill workload: GPU quantize + rac_gemm (bf16 and fp32 output)")
     x, w = dev(xb), dev(wb)
     A = m.nvfp4_quantize(x, topk=128)
     W = m.prepare_weight(w)
-    Y = m.rac_gemm(x, A, W, W["w_hi_t"], A["chan_idx"], out_dtype=m.OUT_BF16)
+    Yb = host(m.rac_gemm(x, A, W, W["w_hi_t"], A["chan_idx"], out_dtype=m.OUT_BF16))
+    Yf = host(m.rac_gemm(x, A, W, W["w_hi_t"], A["chan_idx"], out_dtype=m.OUT_F32))
     torch.cuda.synchronize()
-    Ao = oracle.nvfp4_quantize(xb)
+    say("prefill workload: oracle quantization of x and W")
+    Ao = cached("dense_Ao", lambda: oracle.nvfp4_quantize(xb))
     assert np.array_equal(host(A["codes"]), Ao.codes)
     assert np.array_equal(host(A["scales"]), Ao.scales)
-    So = oracle.select_topk(oracle.channel_scores(Ao.resid), 128)
-    assert np.array_equal(host(A["chan_idx"]), So)
-    rng = np.random.default_rng(3)
-    wrows = np.sort(rng.choice(wb.shape[0], 512, replace=False))
-    Wo_s = oracle.nvfp4_quantize(wb[wrows], tensor_scale=float(host(W["tensor_scale"])[0]))
-    assert np.array_equal(host(W["codes"])[wrows], Wo_s.codes)
-    assert np.array_equal(host(W["scales"])[wrows], Wo_s.scales)
-    Wo = oracle.nvfp4_quantize(wb)
+    ref_sc = oracle.channel_scores(Ao.resid)
+    gsc = host(A["chan_score"])
+    check_scores(gsc, ref_sc, 8192)
+    So = check_selection(host(A["chan_idx"]), ref_sc, 128, 8192, gpu_scores=gsc)
+    Wo = cached("dense_Wo", lambda: oracle.nvfp4_quantize(wb))
     assert np.float32(Wo.tensor_scale) == host(W["tensor_scale"])[0]
-    rows = np.sort(rng.choice(xb.shape[0], 96, replace=False))
-    Ro = oracle.residual_gather(Ao.resid, So)
-    sub = oracle.QuantResult("nvfp4", Ao.codes[rows], Ao.scales[rows], Ao.tensor_scale,
-                             Ao.resid[rows], Ao.mag[rows], Ao.sign[rows])
-    ref = oracle.rac_gemm(sub, Wo, Ro[rows], wb, So)
-    check_bf16_output(host(Y)[rows], ref)
-    say("prefill workload sampled parity ok")
+    assert np.array_equal(host(W["codes"]), Wo.codes)
+    assert np.array_equal(host(W["scales"]), Wo.scales)
+    del W
+    say("prefill workload: oracle fp64 GEMM (every row)")
+    ref = oracle.rac_gemm(Ao, Wo, oracle.residual_gather(Ao.resid, So), wb, So)
+    err = gemm_rel_err(Yf, ref)
+    say(f"  fp32 output max rel err {err:.3e}")
+    assert err <= GEMM_TOL
+    check_bf16_output(Yb, ref)
+    say("prefill workload full parity ok")
+
+
+@pytest.mark.parametrize("k", [128, 256, 512, 768])
+def test_selection_ratio_sweep_parity(k):
+    """The selection-ratio sweep's projection, 8192 x 4096 x 1024, at k = 12.5,
+    25, 50 and 75 % of the channels (4 to 24 compensation chunks per tile):
+    rac_gemm and rac_gemm_eq21 against the oracle on every output element."""
+    m = q4()
+    d = make_inputs("sweep_8192x4096x1024")
+    xb, wb = d["x"], d["w"]
+    say(f"sweep parity k={k}")
+    x, w = dev(xb), dev(wb)
+    A = m.nvfp4_quantize(x, topk=k)
+    W = m.prepare_weight(w)
+    Y = host(m.rac_gemm(x, A, W, W["w_hi_t"], A["chan_idx"], out_dtype=m.OUT_F32))
+    Y21 = host(m.rac_gemm_eq21(x, A, W, A["chan_idx"], out_dtype=m.OUT_F32))
+    torch.cuda.synchronize()
+    Ao = oracle.nvfp4_quantize(xb)
+    Wo = oracle.nvfp4_quantize(wb)
+    assert np.array_equal(host(A["codes"]), Ao.codes)
+    assert np.array_equal(host(W["codes"]), Wo.codes)
+    ref_sc = oracle.channel_scores(Ao.resid)
+    So = check_selection(host(A["chan_idx"]), ref_sc, k, xb.shape[0],
+                         gpu_scores=host(A["chan_score"]))
+    ref = oracle.rac_gemm(Ao, Wo, oracle.residual_gather(Ao.resid, So), wb, So)
+    err = gemm_rel_err(Y, ref)
+    say(f"  rac_gemm max rel err {err:.3e}")
+    assert err <= GEMM_TOL
+    ref21 = oracle.rac_gemm_eq21(xb, Ao, Wo, So)
+    err21 = gemm_rel_err(Y21, ref21)
+    say(f"  rac_gemm_eq21 max rel err {err21:.3e}")
+    assert err21 <= GEMM_TOL
 
 
 @pytest.mark.parametrize("M,N,K,k", [(64, 512, 512, 16), (300, 200, 96, 20), (513, 640, 1024, 64),

@@ -13,7 +13,8 @@ import torch
 import oracle
 from oracle.quant import QuantResult
 from workloads import WORKLOADS, bf16_bits_from_f32, make_activations, make_logits, make_moe_weights
-from tests.gpu_util import GEMM_TOL, bf16_to_f64, check_bf16_output, dev, gemm_rel_err, host, say
+from tests.gpu_util import GEMM_TOL, bf16_to_f64, cached, check_bf16_output, dev, gemm_rel_err, host, say
+from tests.parity import check_scores, check_selection
 
 pytestmark = pytest.mark.gpu
 
@@ -82,18 +83,25 @@ def _run_layer(m, xb, logits, w13, w2, topk, rac_k, fmt=0, out_dtype=1):
         "h_ts": _ws_field(ws, offs, 10, 4, torch.float32),
         "h_S": _ws_field(ws, offs, 11, rac_k * 4, torch.int32),
         "out": _ws_field(ws, offs, 13, R * H * 4, torch.float32).reshape(R, H),
+        "x_scores": _ws_field(ws, offs, 14, H * 8, torch.float64),
+        "h_scores": _ws_field(ws, offs, 15, F * 8, torch.float64),
     }
     return got, experts
 
 
 def _check_site(fmt, xb, got, prefix, rac_k):
+    """One activation site: codes, scales and tensor scale bit-exact, scores
+    within the summation bound, the channel set validated; returns the oracle
+    quantization and the (validated) GPU channel set."""
     q = oracle.nvfp4_quantize(xb) if fmt == 0 else oracle.mxfp4_quantize(xb)
     assert np.array_equal(got[prefix + "_codes"].reshape(q.codes.shape), q.codes)
     assert np.array_equal(got[prefix + "_scales"].reshape(q.scales.shape), q.scales)
     if fmt == 0:
         assert got[prefix + "_ts"][0] == np.float32(q.tensor_scale)
-    S = oracle.select_topk(oracle.channel_scores(q.resid), rac_k)
-    assert np.array_equal(got[prefix + "_S"], S)
+    ref = oracle.channel_scores(q.resid)
+    check_scores(got[prefix + "_scores"], ref, xb.shape[0])
+    S = check_selection(got[prefix + "_S"], ref, rac_k, xb.shape[0],
+                        gpu_scores=got[prefix + "_scores"])
     return q, S
 
 
@@ -117,15 +125,16 @@ def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
     got, _ = _run_layer(m, xb, logits, w13, w2, topk, k, fmt)
     oi, op = oracle.moe_route(logits, topk)
     assert np.array_equal(got["idx"], oi)
+    _, Sx = _check_site(fmt, xb, got, "x", k)
+    # second site on the GPU's h, bit-exact
+    _, Sh = _check_site(fmt, got["h"], got, "h", k)
     ref = oracle.moe_layer(xb, got["idx"], got["p"].astype(np.float64), w13, w2, k,
-                           h_override=got["h"], fmt="nvfp4" if fmt == 0 else "mxfp4")
+                           h_override=got["h"], fmt="nvfp4" if fmt == 0 else "mxfp4",
+                           Sx_override=Sx, Sh_override=Sh)
     assert np.array_equal(got["perm"], ref["perm"]) and np.array_equal(got["offsets"], ref["offsets"])
-    _check_site(fmt, xb, got, "x", k)
     # h (bf16) against the unrounded SwiGLU of the oracle's fp64 W13 product:
     # the GEMM tolerance plus one bf16 ulp
     check_bf16_output(got["h"], _swiglu64(ref["y13"], F), tol=2 * GEMM_TOL)
-    # second site on the GPU's h, bit-exact
-    _check_site(fmt, got["h"], got, "h", k)
     err_o = gemm_rel_err(got["out"], ref["out"])
     say(f"  W2 out rel err {err_o:.2e}")
     assert err_o <= GEMM_TOL
@@ -136,19 +145,59 @@ def _quant(fmt):
     return oracle.nvfp4_quantize if fmt == 0 else oracle.mxfp4_quantize
 
 
-def _sampled_full(name, n_experts_checked=3, fmt=0):
+def _w13_packed_order(F):
+    """Logical W13 row of each packed row: groups of 32 gate rows then the
+    matching 32 up rows (the documented q4_moe_pack_w13 layout)."""
+    p = np.arange(2 * F)
+    g, i = p // 64, p % 64
+    return np.where(i < 32, 32 * g + i, F + 32 * g + (i - 32))
+
+
+def _gpu_weights(experts, key, fmt, e, order=None):
+    """The GPU's quantization of expert e as an oracle QuantResult (codes and
+    scales in logical row order)."""
+    q = experts[key]
+    codes = host(q["codes"][e])
+    scales = host(q["scales"][e])
+    if order is not None:
+        inv = np.empty_like(order)
+        inv[order] = np.arange(order.size)
+        codes, scales = codes[inv], scales[inv]
+    ts = np.float32(host(q["tensor_scale"][e:e + 1])[0]) if fmt == 0 else np.float32(1.0)
+    return QuantResult("nvfp4" if fmt == 0 else "mxfp4", codes, scales, ts, None, None, None)
+
+
+def _check_weight_sample(fmt, wl_bits, Wq, rng, n=8):
+    """The GPU's expert weight quantization: tensor scale = RN32(amax / 2688)
+    (NVFP4) and n random rows bit-exact against the oracle."""
+    if fmt == 0:
+        amax = float(np.abs(bf16_to_f64(wl_bits)).max())
+        st = np.float32(amax / 2688.0) if amax else np.float32(1.0)
+        assert Wq.tensor_scale == st
+    rows = np.sort(rng.choice(wl_bits.shape[0], n, replace=False))
+    o = _quant(fmt)(wl_bits[rows], tensor_scale=float(Wq.tensor_scale)) if fmt == 0 else \
+        _quant(fmt)(wl_bits[rows])
+    assert np.array_equal(Wq.codes[rows], o.codes) and np.array_equal(Wq.scales[rows], o.scales)
+
+
+def _full_layer(name, fmt=0):
+    """The whole workload layer against the oracle: routing of every token,
+    the sort, both activation sites, the W13 product (through h) and the W2
+    product of EVERY expert, and the combine; the expert weight codes are the
+    GPU's, each expert's tensor scale and a row sample checked bit-exact."""
     m = q4()
     wl = WORKLOADS[name]
     T, H, E, F, topk, k = wl.rows, wl.cols, wl.experts, wl.ffn, wl.route_topk, wl.topk_channels
-    say(f"moe {name}: generating inputs")
-    xb = make_activations(wl)
-    logits = make_logits(wl)
-    w13, w2 = make_moe_weights(wl)
+    say(f"moe {name} fmt={fmt}: generating inputs")
+    xb = cached(name + "_x", lambda: make_activations(wl))
+    logits = cached(name + "_logits", lambda: make_logits(wl))
+    w13, w2 = cached(name + "_w", lambda: make_moe_weights(wl))
     say(f"moe {name}: GPU layer")
     got, experts = _run_layer(m, xb, logits, w13, w2, topk, k, fmt)
-    oi, op = oracle.moe_route(logits[:256], topk)
-    assert np.array_equal(got["idx"][:256], oi)
-    np.testing.assert_allclose(got["p"][:256], op, rtol=2e-6, atol=1e-7)
+    say(f"moe {name}: routing of all {T} tokens")
+    oi, op = cached(name + "_route", lambda: oracle.moe_route(logits, topk))
+    assert np.array_equal(got["idx"], oi)
+    np.testing.assert_allclose(got["p"], op, rtol=2e-6, atol=1e-7)
     perm, offsets = oracle.moe_sort(got["idx"], E)
     assert np.array_equal(got["perm"], perm) and np.array_equal(got["offsets"], offsets)
     say(f"moe {name}: site 1")
@@ -157,23 +206,29 @@ def _sampled_full(name, n_experts_checked=3, fmt=0):
     say(f"moe {name}: site 2")
     qh, Sh = _check_site(fmt, got["h"], got, "h", k)
     Rh = oracle.residual_gather(qh.resid, Sh)
-    counts = np.diff(offsets)
-    rng = np.random.default_rng(1)
-    nonempty = np.where(counts > 0)[0]
-    check = sorted(set(rng.choice(nonempty, size=min(n_experts_checked, len(nonempty)), replace=False).tolist()))
+    order = _w13_packed_order(F)
     tok = perm // topk
-    for e in check:
+    rng = np.random.default_rng(1)
+    worst13 = worst2 = 0.0
+    for e in range(E):
         r0, r1 = offsets[e], offsets[e + 1]
-        say(f"moe {name}: expert {e} rows {r1 - r0}")
-        wq13 = _quant(fmt)(w13[e])
+        wq13 = _gpu_weights(experts, "w13", fmt, e, order)
+        wq2 = _gpu_weights(experts, "w2", fmt, e)
+        _check_weight_sample(fmt, w13[e], wq13, rng)
+        _check_weight_sample(fmt, w2[e], wq2, rng)
+        if r1 == r0:
+            continue
         y13 = oracle.rac_gemm(_rows(qx, tok[r0:r1]), wq13, Rx[tok[r0:r1]], w13[e], Sx)
-        check_bf16_output(got["h"][r0:r1], _swiglu64(y13, F), tol=2 * GEMM_TOL)
-        wq2 = _quant(fmt)(w2[e])
+        hr = _swiglu64(y13, F)
+        check_bf16_output(got["h"][r0:r1], hr, tol=2 * GEMM_TOL)
         rows = np.arange(r0, r1)
         out_ref = oracle.rac_gemm(_rows(qh, rows), wq2, Rh[rows], w2[e], Sh)
         err = gemm_rel_err(got["out"][r0:r1], out_ref)
-        say(f"  W2 out rel err {err:.2e}")
-        assert err <= GEMM_TOL
+        assert err <= GEMM_TOL, (e, err)
+        worst2 = max(worst2, err)
+        worst13 = max(worst13, gemm_rel_err(bf16_to_f64(got["h"][r0:r1]), hr))
+    say(f"moe {name}: all {E} experts; h max rel err {worst13:.2e} (bf16 output), "
+        f"W2 out max rel err {worst2:.2e}")
     # combine on the GPU's out and routing weights
     pos = np.empty(T * topk, dtype=np.int64)
     pos[perm] = np.arange(T * topk)
@@ -184,14 +239,14 @@ def _sampled_full(name, n_experts_checked=3, fmt=0):
 
 
 @pytest.mark.parametrize("fmt", [0, 1], ids=["nvfp4", "mxfp4"])
-def test_moe_decode_workload_sampled(fmt):
+def test_moe_decode_workload_full(fmt):
     """256 tokens, 128 experts of 4096 -> 2 x 1536 -> 4096, top-8: run as NVFP4
-    and again as MXFP4 (E8M0 per 32, native scaled FP4 MFMA)."""
-    _sampled_full("moe_decode_256", fmt=fmt)
+    and again as MXFP4 (E8M0 per 32, native scaled FP4 MFMA); every expert."""
+    _full_layer("moe_decode_256", fmt=fmt)
 
 
 @pytest.mark.parametrize("fmt", [0, 1], ids=["nvfp4", "mxfp4"])
-def test_moe_prefill_workload_sampled(fmt):
+def test_moe_prefill_workload_full(fmt):
     """8192 tokens, 128 experts of 2048 -> 2 x 768 -> 2048, top-8, as NVFP4 and as
-    MXFP4 (W13 on the grouped 256 x 256 kernel in both formats)."""
-    _sampled_full("moe_prefill_8192", n_experts_checked=2, fmt=fmt)
+    MXFP4; every expert, every token."""
+    _full_layer("moe_prefill_8192", fmt=fmt)

@@ -7,6 +7,7 @@ import torch
 import oracle
 from workloads import bf16_bits_from_f32, make_inputs
 from tests.gpu_util import dev, host, say
+from tests.parity import check_scores, check_selection
 
 pytestmark = pytest.mark.gpu
 
@@ -46,13 +47,15 @@ def _compare_nvfp4(xb, topk, ts=None, mx=False):
     assert bad.size == 0, f"codes differ at {bad[:5].tolist()}: gpu {gc[tuple(bad[0])]:#x} oracle {o.codes[tuple(bad[0])]:#x}"
     bad = np.argwhere(gs != o.scales)
     assert bad.size == 0, f"scales differ at {bad[:5].tolist()}"
+    # scores: the oracle's exact sums, within the fp64 summation bound; the
+    # selection: exact top-k of the GPU's own scores, equal to the oracle's
+    # exact top-k outside a near-tie band
     sc = oracle.channel_scores(o.resid)
     gsc = host(g["chan_score"])
-    assert np.array_equal(gsc.view(np.uint64), sc.view(np.uint64)), \
-        f"scores differ at {np.argwhere(gsc != sc)[:5].ravel().tolist()}"
+    rel = check_scores(gsc, sc, xb.shape[0])
+    say(f"  scores: max rel diff {rel:.2e}")
     if topk:
-        S = oracle.select_topk(sc, topk)
-        assert np.array_equal(host(g["chan_idx"]), S)
+        S = check_selection(host(g["chan_idx"]), sc, topk, xb.shape[0], gpu_scores=gsc)
         R = host(m.q4_residual_gather(x, g, g["chan_idx"], ld_r=topk + 5))
         Ro = oracle.residual_gather(o.resid, S)
         assert np.array_equal(R[:, :topk], Ro)
