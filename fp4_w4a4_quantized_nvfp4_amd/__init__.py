@@ -51,6 +51,8 @@ _SIGS = {
     "q4_quantize_workspace_size": (_SZ, [_I64, _I64, _I32]),
     "nvfp4_quantize": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "mxfp4_quantize": (_I32, [_P, _I64, _I64, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "nvfp4_quantize_noalloc_max_scratch": (_SZ, []),
+    "nvfp4_quantize_noalloc": (_I32, [_P, _I64, _I64, _P, _P, _P, _P, _P, _I32, _P, _P]),
     "nvfp4_qdq_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_qdq": (_I32, [_P, _I64, _I64, _P, _P, _I32, _P, _P, _SZ, _P]),
     "q4_select_workspace_size": (_SZ, [_I64]),

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/q4rac.h"
 #include "q4_internal.h"
@@ -112,6 +113,67 @@ q4_status_t nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols,
   return quantize_common(false, x, rows, cols, tensor_scale_in, codes, scales, tensor_scale_out,
                          chan_score, topk, chan_idx, workspace, workspace_bytes, stream,
                          "nvfp4_quantize");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ no-allocation quantize
+// nvfp4_quantize_noalloc takes its scratch (amax slots, fp64 partial channel
+// sums, the score buffer) from this file-scope device array instead of a
+// caller workspace.  In host code the name `scratch` is only a host-side
+// stand-in: the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address reaches a kernel.
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)24 << 20;
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kNoAllocMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static q4_status_t scratch_for_current_device(void** out, const char* fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kNoAllocMaxDevices)
+    return fail(Q4_EUNSUPPORTED, "%s: device %d beyond the %d devices supported", fn, dev,
+                kNoAllocMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (!p) return fail(Q4_EHIP, "%s: no device address for the scratch array", fn);
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return Q4_OK;
+}
+
+extern "C" {
+
+size_t nvfp4_quantize_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
+
+q4_status_t nvfp4_quantize_noalloc(const uint16_t* x, int64_t rows, int64_t cols,
+                                   const float* tensor_scale_in, uint8_t* codes, uint8_t* scales,
+                                   float* tensor_scale_out, double* chan_score, int32_t topk,
+                                   int32_t* chan_idx, void* stream) {
+  const char* fn = "nvfp4_quantize_noalloc";
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows >= kMaxDim || cols >= kMaxDim)
+    return fail(Q4_ESHAPE, "%s: need rows >= 0 and cols > 0 with cols %% 16 == 0 (got %lld x %lld)",
+                fn, (long long)rows, (long long)cols);
+  const size_t need = quantize_workspace_bytes(rows, cols);
+  if (need > kNoAllocScratchBytes)
+    return fail(Q4_EWORKSPACE,
+                "%s: a %lld x %lld tensor needs %zu bytes of scratch, above the static %zu "
+                "(use nvfp4_quantize with a workspace)",
+                fn, (long long)rows, (long long)cols, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const q4_status_t st = scratch_for_current_device(&ws, fn);
+  if (st != Q4_OK) return st;
+  return quantize_common(false, x, rows, cols, tensor_scale_in, codes, scales, tensor_scale_out,
+                         chan_score, topk, chan_idx, ws, kNoAllocScratchBytes, stream, fn);
 }
 
 q4_status_t mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* codes,

@@ -119,6 +119,23 @@ q4_status_t mxfp4_quantize(const uint16_t *x, int64_t rows, int64_t cols, uint8_
                            uint8_t *scales, double *chan_score, int32_t topk, int32_t *chan_idx,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* nvfp4_quantize for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, kernels and results as
+ * nvfp4_quantize, minus the workspace: the scratch comes from a static device
+ * array of nvfp4_quantize_noalloc_max_scratch() bytes (24 MiB) that each GPU
+ * the library runs on holds until the process ends.  The call allocates
+ * nothing.  A shape whose scratch (q4_quantize_workspace_size) exceeds that
+ * maximum returns Q4_EWORKSPACE before any launch.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams
+ * or host threads without ordering between them) race, so serialize them.
+ * Nothing in the array needs to start at zero. */
+size_t nvfp4_quantize_noalloc_max_scratch(void);
+q4_status_t nvfp4_quantize_noalloc(const uint16_t *x, int64_t rows, int64_t cols,
+                                   const float *tensor_scale_in, uint8_t *codes,
+                                   uint8_t *scales, float *tensor_scale_out, double *chan_score,
+                                   int32_t topk, int32_t *chan_idx, void *stream);
+
 /* Trainer-side weight fake quantization (QUADS section 3.2, Eq. 12, and the
  * alignment of Eq. 16: the trainer's weight quantize-dequantize must use the
  * same block layout and the same rounding as the rollout kernels, so both
