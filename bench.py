@@ -56,6 +56,9 @@ def _args():
     p.add_argument("--no-sweep", action="store_true", help="skip the selection-ratio sweep")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration) and exit")
+    p.add_argument("--only-moe", action="store_true",
+                   help="only run the MoE expert-layer legs (for profiling them) and exit")
+    p.add_argument("--moe-iters", type=int, default=10)
     return p.parse_args()
 
 
@@ -282,6 +285,11 @@ def main():
 
     torch.cuda.init()
     dev = torch.device("cuda:0")
+    if a.only_moe:
+        stream = torch.cuda.current_stream()
+        moe = _moe_legs(q4, q4.lib(), dev, stream, stream.cuda_stream, iters=a.moe_iters)
+        print(json.dumps({"moe": moe}), flush=True)
+        return
     wl = WORKLOADS["dense_8192x14336x4096"]
     M, K, N, k = wl.rows, wl.cols, wl.n_out, wl.topk_channels
 
@@ -527,7 +535,7 @@ def main():
     sweep = None if a.no_sweep else _ratio_sweep(q4, L, dev, stream, sp)
 
     # ---------------------------------------------------------------- MoE legs
-    moe = None if a.no_moe else _moe_legs(q4, L, dev, stream, sp)
+    moe = None if a.no_moe else _moe_legs(q4, L, dev, stream, sp, iters=a.moe_iters)
 
     # ---------------------------------------------------------------- HBM reference
     # a plain 1 GiB device-to-device copy (torch), read + write bytes over its
