@@ -412,7 +412,7 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
     g.kp = kp;
   }
   hipError_t e = launch_rac_prep(mx, x, M, N, (int32_t)K, a_codes, a_scales, a_tensor_scale,
-                                 w_scales, w_hi_t, chan_set, k, kp, R, W_S, ta, tw,
+                                 w_scales, w_tensor_scale, w_hi_t, chan_set, k, kp, R, W_S, ta, tw,
                                  tile_rows_pad(M), tile_rows_pad(N), S(stream), status);
   if (e != hipSuccess) return hip_status(e, "rac_gemm (operand preparation)");
   return hip_status(launch_w4a4_gemm(g, 0, S(stream)), "rac_gemm");
@@ -750,10 +750,13 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   Q4_TRY(launch_quantize(mx, tokens, T, H, nullptr, xc, xs, xts, (double*)P(L.off[14]), rac_k,
                          rac_k ? xS : nullptr, P(L.qws), s), "moe quantize tokens");
   if (kp) {
-    Q4_TRY(launch_residual_gather(mx, tokens, T, H, xc, xs, xts, xS, rac_k, xR, kp, s),
-           "moe residual tokens");
+    // NVFP4: fp16 compensation operands in the W4A4 sum's units (R 2^-e_x,
+    // W_S / (s_W f_x) per expert)
+    Q4_TRY(launch_residual_gather(mx, tokens, T, H, xc, xs, xts, xS, rac_k, xR, kp, s, nullptr,
+                                  !mx), "moe residual tokens");
     Q4_TRY(launch_wsel_gather(w13_hi_t, E, H, 2 * (int64_t)F, xS, rac_k, kp,
-                              (uint16_t*)P(L.w13_sel), s), "moe w13 gather");
+                              (uint16_t*)P(L.w13_sel), s, mx ? nullptr : w13_tensor_scales, xts),
+           "moe w13 gather");
   }
   uint16_t* hbuf = (uint16_t*)P(L.off[7]);
   GemmArgs g{};
@@ -789,10 +792,10 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   Q4_TRY(launch_quantize(mx, hbuf, R, F, nullptr, hc, hs, hts, (double*)P(L.off[15]), rac_k,
                          rac_k ? hS : nullptr, P(L.qws), s), "moe quantize h");
   if (kp) {
-    Q4_TRY(launch_residual_gather(mx, hbuf, R, F, hc, hs, hts, hS, rac_k, hR, kp, s),
-           "moe residual h");
-    Q4_TRY(launch_wsel_gather(w2_hi_t, E, F, H, hS, rac_k, kp, (uint16_t*)P(L.w2_sel), s),
-           "moe w2 gather");
+    Q4_TRY(launch_residual_gather(mx, hbuf, R, F, hc, hs, hts, hS, rac_k, hR, kp, s, nullptr,
+                                  !mx), "moe residual h");
+    Q4_TRY(launch_wsel_gather(w2_hi_t, E, F, H, hS, rac_k, kp, (uint16_t*)P(L.w2_sel), s,
+                              mx ? nullptr : w2_tensor_scales, hts), "moe w2 gather");
   }
   GemmArgs g2{};
   g2.M = R;

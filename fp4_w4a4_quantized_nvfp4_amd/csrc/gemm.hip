@@ -334,16 +334,29 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
   // ------------------------------------------------------------ tensor scales
   // With a scaled compensation term (beta = -s_R s_W) the W4A4 sum is taken
   // to alpha / beta = -s_A / s_R, the term added, and the sum scaled by beta.
-  const bool rscaled = g.kp > 0 && g.r_res && g.r_ts && g.a_ts;
-  const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[e] : 1.0f;
-  const float beta = rscaled ? -(g.r_ts[0] * g.w_ts[e]) : 1.0f;
-  const float pre = rscaled ? -(g.a_ts[0] / g.r_ts[0]) : alpha;
+  // (s_A s_W is applied without underflow: out_scale).  NVFP4 compensation
+  // operands are fp16; without their own scale they come in the sum's units
+  // and add to the unscaled sum before that multiply.  MXFP4 (no tensor
+  // scale): bf16 operands.
+  const bool rac = g.kp > 0 && g.r_res;
+  const bool rscaled = rac && g.r_ts && g.a_ts;
+  const bool units = rac && !rscaled && !MX;
+  OutScale pre{1.0f, 0, false}, post{1.0f, 0, false};
+  if (rscaled) {
+    pre.mul = -(g.a_ts[0] / g.r_ts[0]);
+    post = out_scale(g.r_ts[0], g.w_ts[e]);
+    post.mul = -post.mul;
+  } else if (g.a_ts) {
+    (units ? post : pre) = out_scale(g.a_ts[0], g.w_ts[e]);
+  }
+  if (!units) {
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= pre;
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = apply_scale(pre, acc[mi][ni][r]);
+  }
 
   // ------------------------------------------------------------ residual tail
   if (g.kp > 0 && g.r_res) {
@@ -366,32 +379,35 @@ __global__ __launch_bounds__(256, 2) void gemm_nvfp4_kernel(GemmArgs g) {
       wrow[ni] = wsel + (wok[ni] ? cc : 0) * g.kp + 8 * h;
     }
     for (int kt = 0; kt < g.kp; kt += 16) {
-      bf16x8v af[4], bf[2];
+      uint4 av[4], bv[2];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const uint4 v = rok[mi] ? *(const uint4*)(rrow[mi] + kt) : make_uint4(0, 0, 0, 0);
-        af[mi] = __builtin_bit_cast(bf16x8v, v);
-      }
+      for (int mi = 0; mi < 4; ++mi)
+        av[mi] = rok[mi] ? *(const uint4*)(rrow[mi] + kt) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const uint4 v = wok[ni] ? *(const uint4*)(wrow[ni] + kt) : make_uint4(0, 0, 0, 0);
-        bf[ni] = __builtin_bit_cast(bf16x8v, v);
-      }
+      for (int ni = 0; ni < 2; ++ni)
+        bv[ni] = wok[ni] ? *(const uint4*)(wrow[ni] + kt) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
+        for (int ni = 0; ni < 2; ++ni) {
+          if constexpr (MX)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8v, av[mi]), __builtin_bit_cast(bf16x8v, bv[ni]),
+                acc[mi][ni], 0, 0, 0);
+          else
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(half8v, av[mi]), __builtin_bit_cast(half8v, bv[ni]),
+                acc[mi][ni], 0, 0, 0);
+        }
     }
-    if (rscaled) {
+  }
+  if (rscaled || units) {
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= beta;
-    }
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = apply_scale(post, acc[mi][ni][r]);
   }
 
   // ------------------------------------------------------------ epilogue
@@ -829,83 +845,94 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   lds_barrier();
 
   // RAC first, into the zeroed accumulators: RAC chunk jr in stage
-  // (jr + roff) % 3; each one waits for its own chunk (two more are in
-  // flight behind it).
+  // (jr + roff) % 3.  Each chunk is consumed in two halves of 16 bf16 MFMAs;
+  // a half's fragments are read from LDS under the previous half's MFMAs, and
+  // the wait for the next chunk (two more are in flight behind it) sits
+  // between the halves, so no LDS read is exposed after the first.
   // Piece 2 s2 + h of a row: half s2 = 1 is half 0 with offset bit 5 flipped.
-  {
+  if (nrac > 0) {
     uint32_t ra_off[2], rb_off[2];
     ra_off[0] = (uint32_t)swz(wm * 128 + l32, h);
     rb_off[0] = (uint32_t)(B_CODE_OFF + swz(wn * 128 + l32, h));
     ra_off[1] = ra_off[0] ^ 32u;
     rb_off[1] = rb_off[0] ^ 32u;
-    auto rac_chunk = [&](int jr, uint8_t* const sb) {
-      if (jr > 0) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));
-        lds_barrier();
+    uint4 A0[4], B0[4], A1[4], B1[4];
+    auto rd = [&](uint4* A, uint4* B, const uint8_t* const sb, int s2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        A[q] = *(const uint4*)(sb + ra_off[s2] + q * Q_CODE);
+        B[q] = *(const uint4*)(sb + rb_off[s2] + q * Q_CODE);
       }
-      uint4 fa[2][4], fb[2][4];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          fa[s2][q] = *(const uint4*)(sb + ra_off[s2] + q * Q_CODE);
-          fb[s2][q] = *(const uint4*)(sb + rb_off[s2] + q * Q_CODE);
-        }
-      lds_barrier();   // every wave is done with this stage
-      issue_any(jr + 3, sb);
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8v, fa[s2][mi]), __builtin_bit_cast(bf16x8v, fb[s2][ni]),
-                acc[mi][ni], 0, 0, 0);
     };
-    int jr = 0;
-    if (roff == 1) {   // nrac % 3 == 2
-      rac_chunk(0, stage1);
-      rac_chunk(1, stage2);
-      jr = 2;
-    } else if (roff == 2) {   // nrac % 3 == 1
-      rac_chunk(0, stage2);
-      jr = 1;
-    }
-    for (; jr < nrac; jr += 3) {
-      rac_chunk(jr, stage0);
-      rac_chunk(jr + 1, stage1);
-      rac_chunk(jr + 2, stage2);
-    }
+    // NVFP4: fp16 operands (in the units of the W4A4 sum, or the exact
+    // Eq. 21 values); MXFP4: bf16
+    auto mm = [&](const uint4* A, const uint4* B) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          if constexpr (MX)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8v, A[mi]), __builtin_bit_cast(bf16x8v, B[ni]),
+                acc[mi][ni], 0, 0, 0);
+          else
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                __builtin_bit_cast(half8v, A[mi]), __builtin_bit_cast(half8v, B[ni]),
+                acc[mi][ni], 0, 0, 0);
+        }
+    };
+    // RAC chunk jr in `cur`, the next chunk (RAC jr + 1, or FP4 chunk 0) in `nxt`
+    auto rstep = [&](int jr, uint8_t* const cur, uint8_t* const nxt) {
+      rd(A1, B1, cur, 1);
+      mm(A0, B0);
+      // chunk jr + 1 has landed; after the barrier every wave is done with `cur`
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA_PER_CHUNK));
+      lds_barrier();
+      issue_any(jr + 3, cur);
+      if (jr + 1 < nrac) rd(A0, B0, nxt, 0);
+      mm(A1, B1);
+    };
+    auto rrun = [&](uint8_t* const s0, uint8_t* const s1, uint8_t* const s2) {
+      rd(A0, B0, s0, 0);
+      int jr = 0;
+      for (; jr + 3 <= nrac; jr += 3) {
+        rstep(jr, s0, s1);
+        rstep(jr + 1, s1, s2);
+        rstep(jr + 2, s2, s0);
+      }
+      if (jr < nrac) rstep(jr, s0, s1);
+      if (jr + 1 < nrac) rstep(jr + 1, s1, s2);
+    };
+    // RAC chunk 0 sits in stage roff
+    if (roff == 0)
+      rrun(stage0, stage1, stage2);
+    else if (roff == 1)
+      rrun(stage1, stage2, stage0);
+    else
+      rrun(stage2, stage0, stage1);
   }
 
-  // Y = alpha * (W4A4 sum) + RAC is accumulated as alpha * (RAC / alpha +
-  // W4A4 sum): the RAC part is divided by alpha = m * 2^e (m in [0.5, 1))
-  // as a multiply by 1 / m and an exact power-of-two scaling, and alpha is
-  // applied once in the epilogue.  No range problem while |RAC| / alpha <
-  // 2^127 (with tensor scales taken from the operands' own amax it is below
-  // kp * 2688^2).  alpha == 0 leaves Y = RAC and skips the W4A4 chunks.
-  // A scaled compensation term (g.r_ts, beta = -s_R s_W) takes the factor
-  // beta / alpha = -s_R / s_A instead (one fp32 division), or beta itself
-  // when alpha == 0.
-  const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[ex] : 1.0f;
-  if (!MX && nrac > 0 && (alpha != 0.0f || RSC)) {
-    int e = 0;
-    float inv_m;
-    if constexpr (RSC) {
-      inv_m = alpha != 0.0f ? -(g.r_ts[0] / g.a_ts[0]) : -(g.r_ts[0] * g.w_ts[ex]);
-    } else {
-      const float m = frexpf(alpha, &e);
-      inv_m = 1.0f / m;
+  // Y = s_A s_W (W4A4 sum + RAC'), the NVFP4 compensation operands coming
+  // in fp16 in the sum's units (R 2^-e_A, W_S / (s_W f_A), s_A = f_A 2^e_A):
+  // no scaling between the compensation and the FP4 chunks, and the product
+  // of the tensor scales applied once in the epilogue without underflow
+  // (out_scale).  The Eq. 21 form (RSC) adds its exact fp16 compensation with
+  // the factor beta = -s_R s_W: the accumulators are taken to
+  // beta / (s_A s_W) = -s_R / s_A (one fp32 division) before the FP4 chunks.
+  // MXFP4: no tensor scale.
+  const OutScale os =
+      (!MX && g.a_ts) ? out_scale(g.a_ts[0], g.w_ts[ex]) : OutScale{1.0f, 0, false};
+  if constexpr (RSC) {
+    if (nrac > 0) {
+      const float to_alpha = -(g.r_ts[0] / g.a_ts[0]);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= to_alpha;
     }
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = ldexpf(acc[mi][ni][r] * inv_m, -e);
   }
-  const float y_scale = alpha != 0.0f ? alpha : 1.0f;
 
   if constexpr (MX) {
     // A fourth stage (the MXFP4 stage is smaller, and a chunk's 32 MFMAs are
@@ -971,12 +998,9 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     if (kc < nk) mx_chunk(kc, stage0);
     if (kc + 1 < nk) mx_chunk(kc + 1, stage1);
     if (kc + 2 < nk) mx_chunk(kc + 2, stage2);
-  } else if (alpha != 0.0f) {
-    // FP4 chunk kc is schedule chunk nrac + kc, in stage kc % 3
-    if (nrac > 0) {   // FP4 chunk 0 has landed
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_PER_CHUNK));
-      lds_barrier();
-    }
+  } else {
+    // FP4 chunk kc is schedule chunk nrac + kc, in stage kc % 3; FP4 chunk 0
+    // has landed behind a barrier (the prologue, or the last RAC step)
     Frag f0, f1;
     read_frag(f0, stage0, 0);
     decode(f0, 0, da[0], db[0]);
@@ -1009,147 +1033,161 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     if (kc + 1 < nk) chunk(kc + 1, stage1, stage2, edge{});
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-
-  // Accumulator element r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
-  // column l % 32 of its 32 x 32 tile.
-  if constexpr (EPI == kEpiSwiGLU) {
-    // W13 with gate and up rows interleaved in blocks of 32: MFMA column
-    // tile ni = 2p is the gate and 2p + 1 the up of h columns
-    // (n0 + 128 wn) / 2 + 32 p + l % 32; h = silu(gate) * up as bf16 into
-    // Y [rows][ldy], ldy >= N / 2.  Staged through LDS per pass (a wave's 16
-    // rows x 64 h columns) so that every store writes 16 contiguous bytes.
-    const int64_t fcols = N / 2, f0 = (n0 + wn * 128) / 2;
-    const bool staged = (fcols % 8) == 0 && (g.ldy % 8) == 0 && (((uintptr_t)g.Y) & 15u) == 0;
-    auto hval = [&](int mi, int p, int r) {
-      return silu(acc[mi][2 * p][r] * y_scale) * (acc[mi][2 * p + 1][r] * y_scale);
+  // The epilogue, once with the single multiply by s_A s_W and once (a
+  // product below fp32's normal range) with mantissa and exponent apart.
+  auto epilogue = [&](auto split) {
+    auto sc = [&](float v) {
+      if constexpr (decltype(split)::value)
+        return ldexpf(v * os.mul, os.e);
+      else
+        return v * os.mul;
     };
+    // Accumulator element r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
+    // column l % 32 of its 32 x 32 tile.
+    if constexpr (EPI == kEpiSwiGLU) {
+      // W13 with gate and up rows interleaved in blocks of 32: MFMA column
+      // tile ni = 2p is the gate and 2p + 1 the up of h columns
+      // (n0 + 128 wn) / 2 + 32 p + l % 32; h = silu(gate) * up as bf16 into
+      // Y [rows][ldy], ldy >= N / 2.  Staged through LDS per pass (a wave's 16
+      // rows x 64 h columns) so that every store writes 16 contiguous bytes.
+      const int64_t fcols = N / 2, f0 = (n0 + wn * 128) / 2;
+      const bool staged = (fcols % 8) == 0 && (g.ldy % 8) == 0 && (((uintptr_t)g.Y) & 15u) == 0;
+      auto hval = [&](int mi, int p, int r) {
+        return silu(sc(acc[mi][2 * p][r])) * (sc(acc[mi][2 * p + 1][r]));
+      };
+      if (staged) {
+        __syncthreads();   // every wave is done with the stages
+        constexpr int PS = 144;   // row pitch (bytes): 64 bf16 and 16 bytes of pad
+        uint8_t* const ep = stage0 + wave * (16 * PS);
+  #pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+  #pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int64_t rbase = m0 + wm * 128 + mi * 32 + 16 * half;
+  #pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+  #pragma unroll
+              for (int rr = 0; rr < 8; rr += 2) {
+                const int r = 8 * half + rr;
+                const int lr = 8 * (rr >> 2) + 4 * h + (rr & 3);
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                const bf16x2 pr = {(__bf16)hval(mi, pp, r), (__bf16)hval(mi, pp, r + 1)};
+                const uint32_t w = __builtin_bit_cast(uint32_t, pr);
+                uint8_t* const q = ep + lr * PS + (pp * 32 + l32) * 2;
+                *(uint16_t*)q = (uint16_t)w;
+                *(uint16_t*)(q + PS) = (uint16_t)(w >> 16);
+              }
+            }
+  #pragma unroll
+            for (int it = 0; it < 2; ++it) {
+              const int cid = it * 64 + lane, lr = cid >> 3, cc = (cid & 7) * 8;
+              const uint4 v = *(const uint4*)(ep + lr * PS + cc * 2);
+              const int64_t row = rbase + lr, col = f0 + cc;
+              if (row < m_end && col < fcols) *(uint4*)((uint16_t*)g.Y + row * g.ldy + col) = v;
+            }
+          }
+        }
+      } else {
+  #pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (row >= m_end) continue;
+  #pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              const int64_t col = f0 + pp * 32 + l32;
+              if (col < fcols)
+                ((uint16_t*)g.Y)[row * g.ldy + col] = (uint16_t)f32_to_bf16_rne(hval(mi, pp, r));
+            }
+          }
+        }
+      }
+      return;
+    }
+
+    // Epilogue through LDS so that every global store writes 16 contiguous
+    // bytes: per pass, a wave's 16 rows x 128 columns (rows 16 * half .. + 15 of
+    // MFMA tile row mi) go to its own LDS region and come back as row chunks.
+    const int vec = g.y_bf16 ? 8 : 4;
+    const bool staged = (N % vec) == 0 && (g.ldy % vec) == 0 && (((uintptr_t)g.Y) & 15u) == 0;
     if (staged) {
       __syncthreads();   // every wave is done with the stages
-      constexpr int PS = 144;   // row pitch (bytes): 64 bf16 and 16 bytes of pad
-      uint8_t* const ep = stage0 + wave * (16 * PS);
-#pragma unroll
+      constexpr int PB = 272, PF = 544;   // row pitches (bytes) of the bf16 / fp32 staging tiles
+      uint8_t* const ep = stage0 + wave * (16 * PF);
+  #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
+  #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int64_t rbase = m0 + wm * 128 + mi * 32 + 16 * half;
-#pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-#pragma unroll
-            for (int rr = 0; rr < 8; rr += 2) {
-              const int r = 8 * half + rr;
-              const int lr = 8 * (rr >> 2) + 4 * h + (rr & 3);
-              typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-              const bf16x2 pr = {(__bf16)hval(mi, pp, r), (__bf16)hval(mi, pp, r + 1)};
-              const uint32_t w = __builtin_bit_cast(uint32_t, pr);
-              uint8_t* const q = ep + lr * PS + (pp * 32 + l32) * 2;
-              *(uint16_t*)q = (uint16_t)w;
-              *(uint16_t*)(q + PS) = (uint16_t)(w >> 16);
+          if (g.y_bf16) {
+  #pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+  #pragma unroll
+              for (int rr = 0; rr < 8; rr += 2) {
+                const int r = 8 * half + rr;
+                const int lr = 8 * ((r >> 2) - 2 * half) + 4 * h + (r & 3);
+                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                const bf16x2 pr = {(__bf16)sc(acc[mi][ni][r]),
+                                   (__bf16)sc(acc[mi][ni][r + 1])};
+                const uint32_t w = __builtin_bit_cast(uint32_t, pr);
+                uint8_t* const p = ep + lr * PB + (ni * 32 + l32) * 2;
+                *(uint16_t*)p = (uint16_t)w;
+                *(uint16_t*)(p + PB) = (uint16_t)(w >> 16);
+              }
+            }
+  #pragma unroll
+            for (int it = 0; it < 4; ++it) {
+              const int cid = it * 64 + lane, lr = cid >> 4, cc = (cid & 15) * 8;
+              const uint4 v = *(const uint4*)(ep + lr * PB + cc * 2);
+              const int64_t row = rbase + lr, col = n0 + wn * 128 + cc;
+              if (row < m_end && col < N) *(uint4*)((uint16_t*)g.Y + row * g.ldy + col) = v;
+            }
+          } else {
+  #pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+  #pragma unroll
+              for (int rr = 0; rr < 8; ++rr) {
+                const int r = 8 * half + rr;
+                const int lr = 8 * ((r >> 2) - 2 * half) + 4 * h + (r & 3);
+                *(float*)(ep + lr * PF + (ni * 32 + l32) * 4) = sc(acc[mi][ni][r]);
+              }
+            }
+  #pragma unroll
+            for (int it = 0; it < 8; ++it) {
+              const int cid = it * 64 + lane, lr = cid >> 5, cc = (cid & 31) * 4;
+              const uint4 v = *(const uint4*)(ep + lr * PF + cc * 4);
+              const int64_t row = rbase + lr, col = n0 + wn * 128 + cc;
+              if (row < m_end && col < N) *(uint4*)((float*)g.Y + row * g.ldy + col) = v;
             }
           }
-#pragma unroll
-          for (int it = 0; it < 2; ++it) {
-            const int cid = it * 64 + lane, lr = cid >> 3, cc = (cid & 7) * 8;
-            const uint4 v = *(const uint4*)(ep + lr * PS + cc * 2);
-            const int64_t row = rbase + lr, col = f0 + cc;
-            if (row < m_end && col < fcols) *(uint4*)((uint16_t*)g.Y + row * g.ldy + col) = v;
-          }
         }
       }
-    } else {
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (row >= m_end) continue;
-#pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            const int64_t col = f0 + pp * 32 + l32;
-            if (col < fcols)
-              ((uint16_t*)g.Y)[row * g.ldy + col] = (uint16_t)f32_to_bf16_rne(hval(mi, pp, r));
-          }
-        }
-      }
+      return;
     }
-    return;
-  }
-
-  // Epilogue through LDS so that every global store writes 16 contiguous
-  // bytes: per pass, a wave's 16 rows x 128 columns (rows 16 * half .. + 15 of
-  // MFMA tile row mi) go to its own LDS region and come back as row chunks.
-  const int vec = g.y_bf16 ? 8 : 4;
-  const bool staged = (N % vec) == 0 && (g.ldy % vec) == 0 && (((uintptr_t)g.Y) & 15u) == 0;
-  if (staged) {
-    __syncthreads();   // every wave is done with the stages
-    constexpr int PB = 272, PF = 544;   // row pitches (bytes) of the bf16 / fp32 staging tiles
-    uint8_t* const ep = stage0 + wave * (16 * PF);
-#pragma unroll
+  #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int64_t rbase = m0 + wm * 128 + mi * 32 + 16 * half;
-        if (g.y_bf16) {
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) {
-#pragma unroll
-            for (int rr = 0; rr < 8; rr += 2) {
-              const int r = 8 * half + rr;
-              const int lr = 8 * ((r >> 2) - 2 * half) + 4 * h + (r & 3);
-              typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-              const bf16x2 pr = {(__bf16)(acc[mi][ni][r] * y_scale), (__bf16)(acc[mi][ni][r + 1] * y_scale)};
-              const uint32_t w = __builtin_bit_cast(uint32_t, pr);
-              uint8_t* const p = ep + lr * PB + (ni * 32 + l32) * 2;
-              *(uint16_t*)p = (uint16_t)w;
-              *(uint16_t*)(p + PB) = (uint16_t)(w >> 16);
-            }
-          }
-#pragma unroll
-          for (int it = 0; it < 4; ++it) {
-            const int cid = it * 64 + lane, lr = cid >> 4, cc = (cid & 15) * 8;
-            const uint4 v = *(const uint4*)(ep + lr * PB + cc * 2);
-            const int64_t row = rbase + lr, col = n0 + wn * 128 + cc;
-            if (row < m_end && col < N) *(uint4*)((uint16_t*)g.Y + row * g.ldy + col) = v;
-          }
-        } else {
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) {
-#pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
-              const int r = 8 * half + rr;
-              const int lr = 8 * ((r >> 2) - 2 * half) + 4 * h + (r & 3);
-              *(float*)(ep + lr * PF + (ni * 32 + l32) * 4) = acc[mi][ni][r] * y_scale;
-            }
-          }
-#pragma unroll
-          for (int it = 0; it < 8; ++it) {
-            const int cid = it * 64 + lane, lr = cid >> 5, cc = (cid & 31) * 4;
-            const uint4 v = *(const uint4*)(ep + lr * PF + cc * 4);
-            const int64_t row = rbase + lr, col = n0 + wn * 128 + cc;
-            if (row < m_end && col < N) *(uint4*)((float*)g.Y + row * g.ldy + col) = v;
-          }
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row >= m_end) continue;
+  #pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int64_t col = n0 + wn * 128 + ni * 32 + l32;
+          if (col >= N) continue;
+          const float v = sc(acc[mi][ni][r]);
+          if (g.y_bf16)
+            ((uint16_t*)g.Y)[row * g.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
+          else
+            ((float*)g.Y)[row * g.ldy + col] = v;
         }
       }
     }
-    return;
-  }
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-      if (row >= m_end) continue;
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int64_t col = n0 + wn * 128 + ni * 32 + l32;
-        if (col >= N) continue;
-        const float v = acc[mi][ni][r] * y_scale;
-        if (g.y_bf16)
-          ((uint16_t*)g.Y)[row * g.ldy + col] = (uint16_t)f32_to_bf16_rne(v);
-        else
-          ((float*)g.Y)[row * g.ldy + col] = v;
-      }
-    }
-  }
+  };
+  if (os.split)
+    epilogue(std::true_type{});
+  else
+    epilogue(std::false_type{});
 }
 }  // namespace big
 

@@ -1,8 +1,12 @@
 // One-launch operand preparation for a dense W4A4 + RAC GEMM (gfx950).
 //
 // QUADS (arXiv 2607.15810) section 3.3, Eq. 21: before the product, the
-// residual of the selected channels (R, bf16) and the matching weight columns
-// (W_S, bf16) are gathered; the dense 256 x 256 kernel also reads the NVFP4
+// residual of the selected channels (R) and the matching weight columns (W_S)
+// are gathered -- for NVFP4 as fp16 operands in the units of the W4A4 sum
+// (R = bf16(r) 2^-e_A exactly, W_S = w / (s_W f_A) rounded to fp16, with
+// s_A = f_A 2^e_A), so the GEMM adds them to its unscaled sum and applies
+// s_A s_W once; MXFP4 keeps bf16 (no tensor scale) -- and the dense 256 x 256
+// kernel also reads the NVFP4
 // block scales of both operands as tiled fp16 records.  The four jobs are
 // small and independent, so one grid runs them side by side: its workgroups
 // are split into consecutive ranges, one per job, instead of four launches
@@ -27,6 +31,7 @@ struct PrepArgs {
   const int32_t* idx;
   // scale records
   const uint8_t* w_scales;
+  const float* w_ts;   // NVFP4: R and W_S as fp16 operands in the W4A4 sum's units
   uint4* a_tiles;
   uint4* w_tiles;
   int64_t M, N, a_pad, w_pad;
@@ -51,13 +56,13 @@ __global__ __launch_bounds__(256) void rac_prep_kernel(PrepArgs p) {
   if (b < p.n_ws) {
     const int64_t by = b / p.ws_gx;
     wsel_gather_part(p.w_hi_t, p.K, p.N, p.idx, k, p.kp, p.W_S, 0, b - by * p.ws_gx, (int)by,
-                     tile);
+                     tile, MX ? nullptr : p.w_ts, p.a_ts);
     return;
   }
   b -= p.n_ws;
   if (b < p.n_r) {
-    residual_gather_part<MX>(p.x, p.M, p.K, p.a_codes, p.a_scales, p.a_ts, p.idx, k, p.R, p.kp,
-                             b, p.n_r);
+    residual_gather_part<MX, true>(p.x, p.M, p.K, p.a_codes, p.a_scales, p.a_ts, p.idx, k, p.R,
+                                   p.kp, b, p.n_r);
     return;
   }
   if (b - p.n_r >= p.n_ta + p.n_tw) return;  // the status-only workgroup
@@ -79,7 +84,8 @@ int64_t grid_stride_blocks(int64_t items) {
 
 hipError_t launch_rac_prep(bool mx, const uint16_t* x, int64_t M, int64_t N, int32_t K,
                            const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
-                           const uint8_t* w_scales, const uint16_t* w_hi_t, const int32_t* idx,
+                           const uint8_t* w_scales, const float* w_ts, const uint16_t* w_hi_t,
+                           const int32_t* idx,
                            int32_t k, int32_t kp, uint16_t* R, uint16_t* W_S, uint8_t* a_tiles,
                            uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream,
                            int32_t* status) {
@@ -94,6 +100,7 @@ hipError_t launch_rac_prep(bool mx, const uint16_t* x, int64_t M, int64_t N, int
   p.W_S = W_S;
   p.idx = idx;
   p.w_scales = w_scales;
+  p.w_ts = w_ts;
   p.a_tiles = (uint4*)a_tiles;
   p.w_tiles = (uint4*)w_tiles;
   p.M = M;
@@ -132,9 +139,10 @@ hipError_t launch_rac_prep(bool mx, const uint16_t* x, int64_t M, int64_t N, int
 // multiplies the NVFP4 weight, so
 //   Y = s_A s_W sum_K d_A d_W - s_R s_W sum_{t<k} R'[i][t] W'[j][t],
 //   R'[i][t] = c' sb' of Q_A(dX)[i][S_t],  W'[j][t] = c_W sb_W of W[j][S_t],
-// both exact in bf16 (a code times an E4M3 value has at most 6 significant
-// bits), so the bf16 MFMA tail of the GEMM forms the second sum exactly up to
-// fp32 accumulation, and the GEMM applies -s_R s_W.
+// both exact in fp16 (a code times an E4M3 value has at most 6 significant
+// bits, and within fp16's normal range), so the fp16 MFMA tail of the GEMM
+// forms the second sum exactly up to fp32 accumulation, and the GEMM applies
+// -s_R s_W.
 
 namespace {
 
@@ -228,11 +236,11 @@ struct Eq21PrepArgs {
   int32_t nslots;
   float* r_ts;             // s_R (workspace), written by workgroup 0 of that job
   float* r_ts_out;         // optional copy for the caller
-  uint16_t* R;             // bf16 [M][kp]
+  uint16_t* R;             // fp16 [M][kp]
   // weight columns
   const uint8_t* w_codes;
   const uint8_t* w_scales;
-  uint16_t* W_S;           // bf16 [N][kp]
+  uint16_t* W_S;           // fp16 [N][kp]
   const int32_t* idx;
   // scale records
   uint4* a_tiles;
@@ -284,7 +292,8 @@ __global__ __launch_bounds__(256) void eq21_prep_kernel(Eq21PrepArgs p) {
       for (int q = 0; q < 8; ++q) {
         if (j0 + q >= p.N) break;
         const float val = e2m1_value((cb[q] >> ((c & 1) * 4)) & 15u) * e4m3_to_f32(sb[q]);
-        p.W_S[(j0 + q) * p.kp + t] = (uint16_t)(t < kk ? f32_to_bf16_rne(val) : 0u);
+        p.W_S[(j0 + q) * p.kp + t] =
+            t < kk ? __builtin_bit_cast(uint16_t, (_Float16)val) : (uint16_t)0;
       }
     }
     return;
@@ -351,7 +360,7 @@ __global__ __launch_bounds__(256) void eq21_prep_kernel(Eq21PrepArgs p) {
         const float sbv = e4m3_to_f32(sc);
         const uint32_t nib = e2m1_nibble_exact(dc, sbv, sr);
         p.R[(i0 + q) * p.kp + t] =
-            (uint16_t)(t < kk ? f32_to_bf16_rne(e2m1_value(nib) * sbv) : 0u);
+            t < kk ? __builtin_bit_cast(uint16_t, (_Float16)(e2m1_value(nib) * sbv)) : (uint16_t)0;
       }
     }
     return;

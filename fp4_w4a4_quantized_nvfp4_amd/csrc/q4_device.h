@@ -108,6 +108,36 @@ __device__ __forceinline__ uint32_t e2m1_nibble_exact(float x, float s, float st
   return sign | m;
 }
 
+// ------------------------------------------------------------------ tensor scales
+// Y = s_A s_W * sum, without letting the product of the two tensor scales
+// underflow: when s_A s_W is a normal fp32 number one multiply by it (one
+// rounding of the exact product s_A s_W sum), otherwise the mantissas and the
+// exponents apart, fA fW (one rounding) and an exact power-of-two scaling, so
+// that only a result that is itself subnormal loses bits.
+struct OutScale {
+  float mul;   // s_A s_W, or fA fW when split
+  int e;       // eA + eW when split
+  bool split;
+};
+
+__device__ __forceinline__ OutScale out_scale(float sa, float sw) {
+  OutScale o;
+  o.mul = sa * sw;
+  o.e = 0;
+  o.split = !(o.mul >= 0x1p-126f);
+  if (o.split) {
+    int ea, ew;
+    const float fa = frexpf(sa, &ea), fw = frexpf(sw, &ew);
+    o.mul = fa * fw;
+    o.e = ea + ew;
+  }
+  return o;
+}
+
+__device__ __forceinline__ float apply_scale(const OutScale& o, float v) {
+  return o.split ? ldexpf(v * o.mul, o.e) : v * o.mul;
+}
+
 // ------------------------------------------------------------------ wave ops
 __device__ __forceinline__ float wave_xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));

@@ -30,10 +30,14 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t strea
 hipError_t launch_residual_gather(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
                                   const uint8_t* codes, const uint8_t* scales, const float* ts,
                                   const int32_t* idx, int32_t k, uint16_t* R, int64_t ld_r,
-                                  hipStream_t stream, int32_t* status = nullptr);
+                                  hipStream_t stream, int32_t* status = nullptr,
+                                  bool units = false);
+// units (NVFP4): R as the fp16 GEMM operand bf16(r) 2^-e, s_t = f 2^e
 hipError_t launch_wsel_gather(const uint16_t* w_hi_t, int64_t batch, int64_t K, int64_t N,
                               const int32_t* idx, int32_t k, int32_t kp, uint16_t* ws,
-                              hipStream_t stream);
+                              hipStream_t stream, const float* w_ts = nullptr,
+                              const float* a_ts = nullptr);
+// w_ts [batch], a_ts [1] (NVFP4): W_S as the fp16 GEMM operand w / (s_W f)
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t batch, int64_t rows, int64_t cols,
                                  uint16_t* out, hipStream_t stream);
 hipError_t launch_moe_pack_w13(const uint16_t* w13, int32_t E, int32_t F, int32_t H,
@@ -61,6 +65,11 @@ struct GemmArgs {
   // null: the compensation term R W_S^T is added as it is.  Set: it is
   // multiplied by -(r_ts[0] * w_ts[e]) (the residual's own tensor scale and
   // the weight's, subtracted: the FP4-quantized residual form of Eq. 21)
+  // (NVFP4: R and W_S are fp16.  With r_ts null they are in the units of the
+  // W4A4 sum, R = bf16(r) 2^-e_A and W_S = w / (s_W f_A) for s_A = f_A 2^e_A,
+  // and add to the unscaled sum before the single s_A s_W multiply; with r_ts
+  // they are the exact Eq. 21 values c sb.  MXFP4: bf16 R and W_S, added as
+  // they are.)
   const float* r_ts;
   void* Y;                   // store: [rows][ldy] fp32|bf16.  SwiGLU: bf16 [rows][N/2]
   int64_t ldy;
@@ -99,7 +108,8 @@ hipError_t launch_eq21_prep(const uint16_t* x, int64_t M, int64_t N, int32_t K,
                             int32_t* status = nullptr);
 hipError_t launch_rac_prep(bool mx, const uint16_t* x, int64_t M, int64_t N, int32_t K,
                            const uint8_t* a_codes, const uint8_t* a_scales, const float* a_ts,
-                           const uint8_t* w_scales, const uint16_t* w_hi_t, const int32_t* idx,
+                           const uint8_t* w_scales, const float* w_ts, const uint16_t* w_hi_t,
+                           const int32_t* idx,
                            int32_t k, int32_t kp, uint16_t* R, uint16_t* W_S, uint8_t* a_tiles,
                            uint8_t* w_tiles, int64_t a_pad, int64_t w_pad, hipStream_t stream,
                            int32_t* status = nullptr);

@@ -40,6 +40,10 @@ __device__ __forceinline__ bool chan_set_ok(const int32_t* __restrict__ idx, int
 }
 
 // R[i][t] = bf16(RN32(x[i][S_t] - dequant)) for t < k, 0 for k <= t < ld_r.
+// UNITS (NVFP4 GEMM operand): the same bf16 value times 2^-e, s_t = f 2^e
+// (f in [0.5, 1)), as fp16 bits -- exact (an 8-bit mantissa fits fp16's 11)
+// unless the scaled value is an fp16 subnormal; the compensation is then in
+// the units of the W4A4 sum once the weight side carries 1 / (f s_W).
 // One thread per (4 consecutive rows, t), t fastest across lanes: S is
 // ascending and its channels cluster in a few blocks (the outlier blocks), so
 // one load instruction of a wave touches few cache lines, and each row's
@@ -50,7 +54,7 @@ __host__ __device__ inline int64_t residual_gather_items(int64_t rows, int64_t l
   return (rows + 3) / 4 * ld_r;
 }
 
-template <bool MX>
+template <bool MX, bool UNITS = false>
 __device__ __forceinline__ void residual_gather_part(
     const uint16_t* __restrict__ x, int64_t rows, int32_t cols, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ ts,
@@ -58,6 +62,8 @@ __device__ __forceinline__ void residual_gather_part(
     int64_t blk, int64_t nblk) {
   const int64_t total = residual_gather_items(rows, ld_r);
   const float st = MX ? 1.0f : ts[0];
+  int est = 0;
+  if (UNITS && !MX) (void)frexpf(st, &est);
   const int64_t cst = cols / 2, sst = MX ? cols / 32 : cols / 16;
   for (int64_t g = blk * 256 + threadIdx.x; g < total; g += nblk * 256) {
     const int64_t i0 = g / ld_r * 4;
@@ -87,6 +93,8 @@ __device__ __forceinline__ void residual_gather_part(
           s = e4m3_to_f32(sb[q]);
         }
         out = f32_to_bf16_rne(fmaf(-(e2m1_value(nib) * s), st, bf16_to_f32(xv[q])));
+        if (UNITS && !MX)
+          out = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(__uint_as_float(out << 16), -est));
       }
       R[(i0 + q) * ld_r + t] = (uint16_t)out;
     }
@@ -95,12 +103,18 @@ __device__ __forceinline__ void residual_gather_part(
 
 // W_S[b][j][t] = w_hi_t[b][S_t][j] for t < k, 0 for k <= t < kp: a transposing
 // gather through a 64 x 64 LDS tile (the selected rows are contiguous in j).
+// With `w_ts` (NVFP4 GEMM operand, the weights' tensor scales, one per matrix
+// b) and `a_ts` (the activation's tensor scale, s_A = f 2^e): the value
+// w / (s_W[b] f) rounded once more, to fp16 (relative 2^-12), so that the
+// compensation R W_S^T comes in the units of the W4A4 sum.
 // Tile (bx, by) of matrix b covers j in [64 bx, 64 bx + 64), t in [64 by, 64 by + 64).
 __device__ __forceinline__ void wsel_gather_part(const uint16_t* __restrict__ w_hi_t, int64_t K,
                                                  int64_t N, const int32_t* __restrict__ idx,
                                                  int32_t k, int32_t kp, uint16_t* __restrict__ ws,
                                                  int64_t b, int64_t bx, int by,
-                                                 uint16_t (*tile)[66]) {
+                                                 uint16_t (*tile)[66],
+                                                 const float* __restrict__ w_ts = nullptr,
+                                                 const float* __restrict__ a_ts = nullptr) {
   const int64_t j0 = bx * 64;
   const int t0 = by * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -118,6 +132,13 @@ __device__ __forceinline__ void wsel_gather_part(const uint16_t* __restrict__ w_
   uint16_t v[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) v[q] = ok[q] ? src[rowoff[q] + j0 + tx] : (uint16_t)0;
+  if (w_ts) {
+    int ea;
+    const float d = w_ts[b] * frexpf(a_ts[0], &ea);
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      v[q] = __builtin_bit_cast(uint16_t, (_Float16)(bf16_to_f32(v[q]) / d));
+  }
 #pragma unroll
   for (int q = 0; q < 16; ++q) tile[ty + 4 * q][tx] = v[q];
   __syncthreads();

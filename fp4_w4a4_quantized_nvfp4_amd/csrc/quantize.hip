@@ -811,7 +811,7 @@ __global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict
 
 // ====================================================================== gathers
 // residual gather (body in q4_prep.h)
-template <bool MX>
+template <bool MX, bool UNITS>
 __global__ __launch_bounds__(256) void residual_gather_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int32_t cols, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ ts,
@@ -819,8 +819,8 @@ __global__ __launch_bounds__(256) void residual_gather_kernel(
     int32_t* __restrict__ status) {
   const bool ok = chan_set_ok(idx, k, cols);
   if (status && blockIdx.x == 0 && threadIdx.x == 0) status[0] = ok ? 0 : 1;
-  residual_gather_part<MX>(x, rows, cols, codes, scales, ts, idx, ok ? k : 0, R, ld_r, blockIdx.x,
-                           gridDim.x);
+  residual_gather_part<MX, UNITS>(x, rows, cols, codes, scales, ts, idx, ok ? k : 0, R, ld_r,
+                                  blockIdx.x, gridDim.x);
 }
 
 // selected weight columns, one 64 x 64 tile per workgroup (body in q4_prep.h)
@@ -828,11 +828,13 @@ __global__ __launch_bounds__(256) void wsel_gather_kernel(const uint16_t* __rest
                                                           int64_t K, int64_t N,
                                                           const int32_t* __restrict__ idx,
                                                           int32_t k, int32_t kp,
-                                                          uint16_t* __restrict__ ws) {
+                                                          uint16_t* __restrict__ ws,
+                                                          const float* __restrict__ w_ts,
+                                                          const float* __restrict__ a_ts) {
   __shared__ uint16_t tile[64][66];
   const bool ok = chan_set_ok(idx, k, K);
   wsel_gather_part(w_hi_t, K, N, idx, ok ? k : 0, kp, ws, blockIdx.z, blockIdx.x, blockIdx.y,
-                   tile);
+                   tile, w_ts, a_ts);
 }
 
 // out[b][c][r] = in[b][r][c]
@@ -1040,26 +1042,30 @@ hipError_t launch_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, con
 hipError_t launch_residual_gather(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
                                   const uint8_t* codes, const uint8_t* scales, const float* ts,
                                   const int32_t* idx, int32_t k, uint16_t* R, int64_t ld_r,
-                                  hipStream_t stream, int32_t* status) {
+                                  hipStream_t stream, int32_t* status, bool units) {
   const int64_t total = residual_gather_items(rows, ld_r);
   if (total == 0 && !status) return hipSuccess;
   int64_t grid = (total + 255) / 256;
   grid = grid > 65536 ? 65536 : (grid < 1 ? 1 : grid);
   if (mx)
-    hipLaunchKernelGGL(residual_gather_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, x,
-                       rows, (int32_t)cols, codes, scales, ts, idx, k, R, ld_r, status);
+    hipLaunchKernelGGL((residual_gather_kernel<true, false>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, x, rows, (int32_t)cols, codes, scales, ts, idx, k, R, ld_r, status);
+  else if (units)
+    hipLaunchKernelGGL((residual_gather_kernel<false, true>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, x, rows, (int32_t)cols, codes, scales, ts, idx, k, R, ld_r, status);
   else
-    hipLaunchKernelGGL(residual_gather_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       x, rows, (int32_t)cols, codes, scales, ts, idx, k, R, ld_r, status);
+    hipLaunchKernelGGL((residual_gather_kernel<false, false>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, x, rows, (int32_t)cols, codes, scales, ts, idx, k, R, ld_r, status);
   return hipGetLastError();
 }
 
 hipError_t launch_wsel_gather(const uint16_t* w_hi_t, int64_t batch, int64_t K, int64_t N,
                               const int32_t* idx, int32_t k, int32_t kp, uint16_t* ws,
-                              hipStream_t stream) {
+                              hipStream_t stream, const float* w_ts, const float* a_ts) {
   if (batch == 0 || N == 0 || kp == 0) return hipSuccess;
   dim3 grid((unsigned)((N + 63) / 64), (unsigned)((kp + 63) / 64), (unsigned)batch);
-  hipLaunchKernelGGL(wsel_gather_kernel, grid, dim3(256), 0, stream, w_hi_t, K, N, idx, k, kp, ws);
+  hipLaunchKernelGGL(wsel_gather_kernel, grid, dim3(256), 0, stream, w_hi_t, K, N, idx, k, kp, ws,
+                     w_ts, a_ts);
   return hipGetLastError();
 }
 

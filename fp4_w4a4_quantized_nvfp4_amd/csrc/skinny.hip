@@ -182,11 +182,18 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     if (k0 >= K) break;
   }
 
-  const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[e] : 1.0f;
+  // Y = s_A s_W * (sum + compensation) with NVFP4 fp16 compensation operands
+  // in the sum's units; bf16 ones (MXFP4, no tensor scale) are added after
+  // the (unit) scaling.  The product of the tensor scales is applied without
+  // underflow.
+  const OutScale os = g.a_ts ? out_scale(g.a_ts[0], g.w_ts[e]) : OutScale{1.0f, 0, false};
+  const bool units = g.kp > 0 && g.r_res && !MX;
+  if (!units) {
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[ni][q] *= alpha;
+      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
+  }
 
   // residual compensation: bf16 R rows of the tile x bf16 selected W columns
   if (g.kp > 0 && g.r_res) {
@@ -198,15 +205,26 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
       wrow[ni] = g.w_sel + ((int64_t)e * N + (cok[ni] ? col : 0)) * g.kp + 8 * h;
     }
     for (int kt = 0; kt < g.kp; kt += 16) {
-      const bf16x8v af =
-          __builtin_bit_cast(bf16x8v, rok ? *(const uint4*)(rrow + kt) : make_uint4(0, 0, 0, 0));
+      const uint4 av = rok ? *(const uint4*)(rrow + kt) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
-        const bf16x8v bf = __builtin_bit_cast(
-            bf16x8v, cok[ni] ? *(const uint4*)(wrow[ni] + kt) : make_uint4(0, 0, 0, 0));
-        acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[ni], 0, 0, 0);
+        const uint4 bv = cok[ni] ? *(const uint4*)(wrow[ni] + kt) : make_uint4(0, 0, 0, 0);
+        if constexpr (MX)
+          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, av),
+                                                           __builtin_bit_cast(bf16x8v, bv),
+                                                           acc[ni], 0, 0, 0);
+        else
+          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8v, av),
+                                                          __builtin_bit_cast(half8v, bv), acc[ni],
+                                                          0, 0, 0);
       }
     }
+  }
+  if (units) {
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
   }
 
   // accumulator element q of lane l: row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32
@@ -464,11 +482,18 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) cok[ni] = c0 + ni * 32 + l32 < N;
 
-  const float alpha = g.a_ts ? g.a_ts[0] * g.w_ts[e] : 1.0f;
+  // Y = s_A s_W * (sum + compensation) with NVFP4 fp16 compensation operands
+  // in the sum's units; bf16 ones (MXFP4, no tensor scale) are added after
+  // the (unit) scaling.  The product of the tensor scales is applied without
+  // underflow.
+  const OutScale os = g.a_ts ? out_scale(g.a_ts[0], g.w_ts[e]) : OutScale{1.0f, 0, false};
+  const bool units = g.kp > 0 && g.r_res && !MX;
+  if (!units) {
 #pragma unroll
-  for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[ni][q] *= alpha;
+      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
+  }
 
   // residual compensation: bf16 R rows of the tile x bf16 selected W columns
   if (g.kp > 0 && g.r_res) {
@@ -480,15 +505,26 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
       wrow[ni] = g.w_sel + ((int64_t)e * N + (cok[ni] ? col : 0)) * g.kp + 8 * h;
     }
     for (int kt = 0; kt < g.kp; kt += 16) {
-      const bf16x8v af =
-          __builtin_bit_cast(bf16x8v, rok ? *(const uint4*)(rrow + kt) : make_uint4(0, 0, 0, 0));
+      const uint4 av = rok ? *(const uint4*)(rrow + kt) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
-        const bf16x8v bf = __builtin_bit_cast(
-            bf16x8v, cok[ni] ? *(const uint4*)(wrow[ni] + kt) : make_uint4(0, 0, 0, 0));
-        acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[ni], 0, 0, 0);
+        const uint4 bv = cok[ni] ? *(const uint4*)(wrow[ni] + kt) : make_uint4(0, 0, 0, 0);
+        if constexpr (MX)
+          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, av),
+                                                           __builtin_bit_cast(bf16x8v, bv),
+                                                           acc[ni], 0, 0, 0);
+        else
+          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8v, av),
+                                                          __builtin_bit_cast(half8v, bv), acc[ni],
+                                                          0, 0, 0);
       }
     }
+  }
+  if (units) {
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
   }
 
   // accumulator element q of lane l: row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32

@@ -186,8 +186,15 @@ q4_status_t w4a4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_
 /* W4A4 GEMM with Residual Activation Compensation (section 3.3 Eq. 21-22):
  *   Y = W4A4(A, W) + sum_{t<k} R[i][t] W_hi[j][S_t]
  * with R the bf16 residual of x on the channel set S (q4_residual_gather) and
- * W_hi the bf16 weight.  Both extra operands are accumulated into the same
- * fp32 tile as the W4A4 product, after its tensor scaling.
+ * W_hi the bf16 weight.  The compensation is accumulated into the same fp32
+ * tile as the W4A4 product: for NVFP4 as fp16 MFMA steps on R 2^-e_A (exact)
+ * and W_hi / (s_W f_A) (one more rounding, relative 2^-12; s_A = f_A 2^e_A)
+ * into the unscaled sum, then s_A s_W multiplies both; for MXFP4 as bf16
+ * steps.  Range (documented, not checked): |r| / s_A and |W_hi| / s_W below
+ * 2^15 (with tensor scales taken from the operands' own amax they are at
+ * most 448 and 2688).  s_A s_W itself may be as small as the fp32 range
+ * allows: it is applied as mantissa and exponent, so only a result that is
+ * itself subnormal loses bits.
  *   x       bf16 [M][K], the activation that produced A.
  *   w_hi_t  bf16 [K][N]: the transposed bf16 weight (channel-major), so the
  *           selected rows S_t are contiguous.
@@ -220,8 +227,8 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
  * weight (no bf16 weight is needed):
  *   Y = ( dequant(A) - M_S * dequant(Q(dX)) ) W_dequant^T
  *     = s_A s_W sum_K d_A d_W - s_R s_W sum_{t<k} (c sb)_dX[i][S_t] (c sb)_W[j][S_t].
- * Both factors of the second sum are exact in bf16; it runs as extra bf16 MFMA
- * steps into the same fp32 tile.
+ * Both factors of the second sum are exact in fp16; it runs as extra fp16
+ * MFMA steps into the same fp32 tile.
  *   x, A, W, chan_set, k, Y, y_dtype, status as rac_gemm (A and W NVFP4; an
  *           invalid channel set adds no compensation and reports Q4_EINVAL).
  *   resid_tensor_scale_out fp32 [1] (out) or NULL: s_R, written when M, N and
@@ -232,9 +239,10 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
  * computed from the tensor's own amax it is at most 1/6 (or dX is all zero,
  * which is harmless); it falls below 2^-90 only for a tensor whose largest
  * quantization error is below about 2^-90 of its largest element.
- * Workspace (rac_gemm_eq21_workspace_size): at offset 0 the bf16 matrix
- * R' [M][kp] = (c sb) of Q(dX) on S (0 past k), kp = k rounded up to 32, then
- * the weight factor [N][kp], the amax partials, s_R and the scale records. */
+ * Workspace (rac_gemm_eq21_workspace_size): at offset 0 the fp16 matrix
+ * R' [M][kp] = (c sb) of Q(dX) on S (0 past k; exact in fp16), kp = k rounded
+ * up to 32, then the weight factor [N][kp], the amax partials, s_R and the
+ * scale records. */
 size_t rac_gemm_eq21_workspace_size(int64_t M, int64_t N, int64_t K, int32_t k);
 q4_status_t rac_gemm_eq21(int64_t M, int64_t N, int64_t K, const uint16_t *x,
                           const uint8_t *a_codes, const uint8_t *a_scales,

@@ -130,6 +130,28 @@ def test_ragged_shapes(M, N, K, k):
     _check_rac(xb, wb, k, 1)
 
 
+@pytest.mark.parametrize("M,N,K,xs,ws", [(300, 200, 512, 1e-30, 1e-5), (600, 520, 512, 1e-30, 1e-5),
+                                         (300, 200, 512, 1e30, 1e3), (600, 520, 512, 1e30, 1e3),
+                                         (520, 512, 1024, 1e-25, 1e-12)],
+                         ids=["tiny_small", "tiny_large", "huge_small", "huge_large", "tinier_large"])
+def test_extreme_tensor_scales(M, N, K, xs, ws):
+    """Tensor scales whose product s_A s_W is subnormal in fp32 (or large):
+    the outputs are normal numbers and must stay within the tolerance (the
+    product is applied as mantissa and exponent, so it cannot underflow)."""
+    rng = np.random.default_rng(int(M + K))
+    x = rng.standard_t(3, size=(M, K)) * xs
+    x[:, rng.choice(K, 4, replace=False)] *= 30
+    xb = _bits(x.astype(np.float32))
+    wb = _bits((rng.standard_normal((N, K)) * 0.05 * ws).astype(np.float32))
+    Ao = oracle.nvfp4_quantize(xb)
+    Wo = oracle.nvfp4_quantize(wb)
+    alpha = float(np.float32(Ao.tensor_scale)) * float(np.float32(Wo.tensor_scale))
+    say(f"extreme scales: s_A {float(Ao.tensor_scale):.3g} s_W {float(Wo.tensor_scale):.3g} "
+        f"s_A s_W {alpha:.3g}")
+    _check_rac(xb, wb, 16, 0)
+    _check_rac(xb, wb, 0, 0)
+
+
 def test_dense_prefill_workload_full():
     """8192 x 14336 x 4096, k = 128: x quantization bit-exact, scores within the
     summation bound and the selection validated, W codes and scales bit-exact
