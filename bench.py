@@ -106,8 +106,7 @@ def _moe_legs(q4, L, dev, stream, sp, iters=10):
                                          pw.data_ptr(), sp))
                 q4.moe_w4a4_grouped_gemm(tokens, idx, pw, experts, k, out_dtype=q4.OUT_BF16,
                                          workspace=ws, Y=Y)
-            for _ in range(3):
-                layer()
+            _warm(layer, stream)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -132,6 +131,23 @@ def _moe_legs(q4, L, dev, stream, sp, iters=10):
         del w13, w2
         torch.cuda.empty_cache()
     return res
+
+
+def _warm(fn, stream, ms=60.0):
+    """Untimed calls of `fn` until about `ms` of device time has run (three at
+    least): the device's clocks ramp over the first tens of milliseconds of
+    sustained load, and a leg timed inside that ramp reads up to 30 % slow."""
+    import torch
+    for _ in range(3):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    e1.synchronize()
+    for _ in range(min(200, int(ms / max(e0.elapsed_time(e1), 1e-3)))):
+        fn()
 
 
 def _ratio_sweep(q4, L, dev, stream, sp, reps=7):
@@ -337,23 +353,9 @@ def main():
         if events:
             events[2].record(stream)
 
-    _say("dense step: warmup + timed steps")
-    for i in range(a.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t_quant = np.mean([e[0].elapsed_time(e[1]) for e in ev])   # ms
-    t_gemm = np.mean([e[1].elapsed_time(e[2]) for e in ev])
-    ms_step = wall * 1e3 / a.steps
     gemm_flops = 2.0 * M * N * K
     rac_flops = 2.0 * M * N * k
     step_flops = gemm_flops + rac_flops
-    value = step_flops / (ms_step * 1e-3) / 1e12
-    achieved = step_flops / (t_gemm * 1e-3) / 1e12
 
     # ---------------------------------------------------------------- quantizer line
     _say("quantizer workload")
@@ -446,8 +448,7 @@ def main():
                                  None, Wm["codes"].data_ptr(), Wm["scales"].data_ptr(), None,
                                  Wm["w_hi_t"].data_ptr(), im.data_ptr(), k, Y.data_ptr(), 1,
                                  rws.data_ptr(), rws_b, None, sp))
-        for i in range(3):
-            mstep(i)
+        _warm(lambda: mstep(0), stream)
         mev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
         for i in range(5):
             q4._check(L.mxfp4_quantize(x[i % 2].data_ptr(), M, K, cm.data_ptr(), smx.data_ptr(),
@@ -466,37 +467,6 @@ def main():
               "frac_fp4_peak": round(mx_tf / PEAK_FP4_TFLOPS, 4)}
         del Wm
 
-    # ---------------------------------------------------------------- RAC cost
-    # the same call with k = 0 (the W4A4 product alone, same kernel and scale
-    # records), interleaved with the k = 128 call: what the compensation costs
-    wf = None
-    if not a.no_w4a4:
-        _say("W4A4-only leg")
-
-        def wstep(kk):
-            q4._check(L.rac_gemm(0, M, N, K, x[0].data_ptr(), codes.data_ptr(), scales.data_ptr(),
-                                 ts.data_ptr(), W["codes"].data_ptr(), W["scales"].data_ptr(),
-                                 W["tensor_scale"].data_ptr(), W["w_hi_t"].data_ptr(),
-                                 idx.data_ptr() if kk else None, kk, Y.data_ptr(), 1,
-                                 rws.data_ptr(), rws_b, None, sp))
-        tw = {0: [], k: []}
-        for i in range(12):
-            for kk in (0, k):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                wstep(kk)
-                e1.record(stream)
-                e1.synchronize()
-                if i >= 2:
-                    tw[kk].append(e0.elapsed_time(e1))
-        t0w, tkw = float(np.median(tw[0])), float(np.median(tw[k]))
-        wf = {"workload": "dense_8192x14336x4096, rac_gemm with k = 0 (W4A4 product only) "
-                          "alternating with k = 128",
-              "k0_ms": round(t0w, 4), "k0_tflops": round(gemm_flops / (t0w * 1e-3) / 1e12, 2),
-              "k0_frac_fp16_peak": round(gemm_flops / (t0w * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
-              "k128_ms": round(tkw, 4), "rac_overhead_ms": round(tkw - t0w, 4)}
-
     # ---------------------------------------------------------------- Eq. 21 leg
     # the page-literal compensation on the same dense step: the quantization
     # error re-quantized to NVFP4 (own tensor scale, one extra pass over x for
@@ -513,9 +483,7 @@ def main():
                                       W["scales"].data_ptr(), W["tensor_scale"].data_ptr(),
                                       idx.data_ptr(), k, Y.data_ptr(), 1, None, ews.data_ptr(),
                                       ews_b, None, sp))
-        for i in range(3):
-            step(i)
-            estep(i)
+        _warm(lambda: (step(0), estep(0)), stream)
         eev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
         for i in range(5):
             step(i)
@@ -556,6 +524,58 @@ def main():
         cts.append(e0.elapsed_time(e1))
     copy_gbs = 2.0 * (1 << 30) / (float(np.median(cts)) * 1e-3) / 1e9
     del cbuf, cdst
+
+    # ---------------------------------------------------------------- RAC cost
+    # the same call with k = 0 (the W4A4 product alone, same kernel and scale
+    # records), interleaved with the k = 128 call: what the compensation costs
+    wf = None
+    if not a.no_w4a4:
+        _say("W4A4-only leg")
+        step(0)
+
+        def wstep(kk):
+            q4._check(L.rac_gemm(0, M, N, K, x[0].data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                                 ts.data_ptr(), W["codes"].data_ptr(), W["scales"].data_ptr(),
+                                 W["tensor_scale"].data_ptr(), W["w_hi_t"].data_ptr(),
+                                 idx.data_ptr() if kk else None, kk, Y.data_ptr(), 1,
+                                 rws.data_ptr(), rws_b, None, sp))
+        tw = {0: [], k: []}
+        for i in range(12):
+            for kk in (0, k):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                wstep(kk)
+                e1.record(stream)
+                e1.synchronize()
+                if i >= 2:
+                    tw[kk].append(e0.elapsed_time(e1))
+        t0w, tkw = float(np.median(tw[0])), float(np.median(tw[k]))
+        wf = {"workload": "dense_8192x14336x4096, rac_gemm with k = 0 (W4A4 product only) "
+                          "alternating with k = 128",
+              "k0_ms": round(t0w, 4), "k0_tflops": round(gemm_flops / (t0w * 1e-3) / 1e12, 2),
+              "k0_frac_fp16_peak": round(gemm_flops / (t0w * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
+              "k128_ms": round(tkw, 4), "rac_overhead_ms": round(tkw - t0w, 4)}
+
+    # ---------------------------------------------------------------- headline
+    # The dense step is timed last, straight after the W4A4-only leg, so that
+    # its timed steps run at the clocks the device holds under sustained load
+    # (its first ~25 ms of back-to-back steps run up to 30 % slower while the
+    # clocks ramp) and none of them waits on host-side workload generation.
+    _say("dense step: warmup + timed steps")
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_quant = np.mean([e[0].elapsed_time(e[1]) for e in ev])   # ms
+    t_gemm = np.mean([e[1].elapsed_time(e[2]) for e in ev])
+    ms_step = wall * 1e3 / a.steps
+    value = step_flops / (ms_step * 1e-3) / 1e12
+    achieved = step_flops / (t_gemm * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
