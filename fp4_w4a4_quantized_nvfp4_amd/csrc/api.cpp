@@ -62,7 +62,7 @@ int32_t round_up32(int32_t k) { return (k + 31) & ~31; }
 extern "C" {
 
 const char* q4_last_error(void) { return g_err; }
-int32_t q4_version(void) { return 102; }
+int32_t q4_version(void) { return 103; }
 
 // ======================================================================== quantize
 size_t q4_quantize_workspace_size(int64_t rows, int64_t cols, int32_t fmt) {
@@ -593,11 +593,35 @@ q4_status_t q4_moe_pack_w13(const uint16_t* w13, int32_t E, int32_t F, int32_t H
   return hip_status(launch_moe_pack_w13(w13, E, F, H, out, S(stream)), "q4_moe_pack_w13");
 }
 
+size_t q4_scale_records_size(int64_t batch, int64_t rows, int64_t K) {
+  if (batch < 0 || rows < 0 || K <= 0 || K % 128 || rows >= kMaxDim || K >= kMaxDim) return 0;
+  return (size_t)batch * (size_t)(K / 128) * (size_t)tile_rows_pad(rows) * 16;
+}
+
+q4_status_t q4_scale_records(const uint8_t* scales, int64_t batch, int64_t rows, int64_t K,
+                             uint8_t* out, size_t out_bytes, void* stream) {
+  const char* fn = "q4_scale_records";
+  if (batch < 0 || batch >= 65536 || rows < 0 || rows >= kMaxDim || K <= 0 || K >= kMaxDim)
+    return fail(Q4_ESHAPE, "%s: bad shape", fn);
+  if (K % 128) return fail(Q4_ESHAPE, "%s: need K %% 128 == 0 (got %lld)", fn, (long long)K);
+  const size_t need = q4_scale_records_size(batch, rows, K);
+  if (need == 0) return Q4_OK;
+  Q4_REQUIRE_PTR(out);
+  if (out_bytes < need) return fail(Q4_EWORKSPACE, "%s: %zu bytes needed (got %zu)", fn, need, out_bytes);
+  if (rows > 0) Q4_REQUIRE_PTR(scales);
+  return hip_status(launch_scale_tile_batched(scales, batch, rows, (int32_t)K, tile_rows_pad(rows),
+                                              out, S(stream)), fn);
+}
+
 // workspace fields of the grouped expert layer
 namespace {
 struct MoeLayout {
   size_t off[Q4_MOE_WS_FIELDS];
-  size_t inv_perm, tiles, ntiles, tiles_s, ntiles_s, counts, a_rows, w13_sel, w2_sel, qws, total;
+  size_t inv_perm, tiles, ntiles, tiles_s, ntiles_s, counts, a_rows, w13_sel, w2_sel, qws;
+  size_t x_rec, h_rec;   // sorted-row scale records of the two sites (0: none)
+  bool tiled13, tiled2;  // shapes on which the records can be used
+  int64_t rows_pad;
+  size_t total;
 };
 
 MoeLayout moe_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F, int32_t topk,
@@ -640,6 +664,14 @@ MoeLayout moe_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F, in
   L.w2_sel = take((size_t)E * H * (kp ? kp : 1) * 2);
   const size_t qa = quantize_workspace_bytes(T, H), qb = quantize_workspace_bytes(R, F);
   L.qws = take(qa > qb ? qa : qb);
+  // NVFP4 prefill shapes whose grouped GEMMs can read tiled scale records
+  // (256 x 256 tiles: K % 128 == 0, K >= 512, N % 256 == 0)
+  const bool grouped_big = !mx && !moe_skinny(T, E, topk);
+  L.tiled13 = grouped_big && H % 128 == 0 && H >= 512 && (2 * (int64_t)F) % 256 == 0;
+  L.tiled2 = grouped_big && F % 128 == 0 && F >= 512 && H % 256 == 0;
+  L.rows_pad = tile_rows_pad(R);
+  L.x_rec = L.tiled13 ? take((size_t)(H / 128) * L.rows_pad * 16) : 0;
+  L.h_rec = L.tiled2 ? take((size_t)(F / 128) * L.rows_pad * 16) : 0;
   L.total = o;
   return L;
 }
@@ -667,7 +699,8 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
                                   const uint8_t* w13_scales, const float* w13_tensor_scales,
                                   const uint8_t* w2_codes, const uint8_t* w2_scales,
                                   const float* w2_tensor_scales, const uint16_t* w13_hi_t,
-                                  const uint16_t* w2_hi_t, int32_t rac_k, void* Y,
+                                  const uint16_t* w2_hi_t, const uint8_t* w13_scale_records,
+                                  const uint8_t* w2_scale_records, int32_t rac_k, void* Y,
                                   int32_t y_dtype, void* workspace, size_t workspace_bytes,
                                   int32_t* status, void* stream) {
   const char* fn = "moe_w4a4_grouped_gemm";
@@ -692,6 +725,10 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   } else if (w13_tensor_scales || w2_tensor_scales) {
     return fail(Q4_EINVAL, "%s: MXFP4 weights take no tensor scales", fn);
   }
+  if (mx && (w13_scale_records || w2_scale_records))
+    return fail(Q4_EINVAL, "%s: scale records are an NVFP4 layout", fn);
+  if (w13_scale_records) Q4_REQUIRE_PTR(w13_scale_records);
+  if (w2_scale_records) Q4_REQUIRE_PTR(w2_scale_records);
   if (rac_k > 0) {
     Q4_REQUIRE_PTR(w13_hi_t);
     Q4_REQUIRE_PTR(w2_hi_t);
@@ -749,6 +786,10 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   uint16_t* xR = (uint16_t*)P(L.off[6]);
   Q4_TRY(launch_quantize(mx, tokens, T, H, nullptr, xc, xs, xts, (double*)P(L.off[14]), rac_k,
                          rac_k ? xS : nullptr, P(L.qws), s), "moe quantize tokens");
+  const bool rec13 = L.tiled13 && w13_scale_records, rec2 = L.tiled2 && w2_scale_records;
+  if (rec13)
+    Q4_TRY(launch_scale_tile_sorted(xs, a_rows, R, H, offsets, E, L.rows_pad, (uint8_t*)P(L.x_rec),
+                                    s), "moe token scale records");
   if (kp) {
     // NVFP4: fp16 compensation operands in the W4A4 sum's units (R 2^-e_x,
     // W_S / (s_W f_x) per expert)
@@ -782,6 +823,12 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   g.ntiles_dev = ntiles;
   g.a_rows = a_rows;
   g.a_src_rows = T;
+  if (rec13) {
+    g.a_scales_t = (const uint8_t*)P(L.x_rec);
+    g.w_scales_t = w13_scale_records;
+    g.a_rows_pad = L.rows_pad;
+    g.w_rows_pad = tile_rows_pad(2 * (int64_t)F);
+  }
   Q4_TRY(grouped_gemm(g), "moe w13 gemm");
   // ---- activation site 2: h (sorted rows)
   uint8_t* hc = (uint8_t*)P(L.off[8]);
@@ -791,6 +838,9 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   uint16_t* hR = (uint16_t*)P(L.off[12]);
   Q4_TRY(launch_quantize(mx, hbuf, R, F, nullptr, hc, hs, hts, (double*)P(L.off[15]), rac_k,
                          rac_k ? hS : nullptr, P(L.qws), s), "moe quantize h");
+  if (rec2)
+    Q4_TRY(launch_scale_tile_sorted(hs, nullptr, R, F, offsets, E, L.rows_pad, (uint8_t*)P(L.h_rec),
+                                    s), "moe h scale records");
   if (kp) {
     Q4_TRY(launch_residual_gather(mx, hbuf, R, F, hc, hs, hts, hS, rac_k, hR, kp, s, nullptr,
                                   !mx), "moe residual h");
@@ -819,6 +869,12 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   g2.tiles = tiles;
   g2.ntiles_dev = ntiles;
   g2.a_rows = nullptr;
+  if (rec2) {
+    g2.a_scales_t = (const uint8_t*)P(L.h_rec);
+    g2.w_scales_t = w2_scale_records;
+    g2.a_rows_pad = L.rows_pad;
+    g2.w_rows_pad = tile_rows_pad(H);
+  }
   Q4_TRY(grouped_gemm(g2), "moe w2 gemm");
   Q4_TRY(launch_moe_combine((const float*)P(L.off[13]), inv, topk_w, topk_idx, E, T, topk, H, Y,
                             y_dtype == Q4_OUT_BF16, s), "moe combine");

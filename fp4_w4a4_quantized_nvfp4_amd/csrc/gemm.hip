@@ -499,7 +499,6 @@ struct Frag {
 // straight from LDS to the scaled FP4 instruction, no decode (dense only)
 template <bool TILED, bool GROUPED, int EPI, bool RSC = false, bool MX = false>
 __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
-  static_assert(!(TILED && GROUPED), "grouped tiles take raw scales");
   static_assert(GROUPED || EPI == kEpiStore, "SwiGLU is a grouped epilogue");
   static_assert(!MX || (!TILED && !RSC), "MXFP4: raw scales, no scaled compensation");
   // MX scale area: 4 E8M0 bytes per row per chunk
@@ -613,11 +612,15 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
       gs_voff[it] = (uint32_t)a_src(32 * (4 * it + wave) + (lane >> 1)) * sstride + (uint32_t)(lane & 1) * 4u;
   }
   // tiled scale records [chunk][padded row][16 B]: lane l of the wave loads
-  // the record of tile row 64 * wave + l
+  // the record of tile row 64 * wave + l.  Grouped: the A records follow the
+  // sorted rows (each swizzled by its row's offset within its expert, which
+  // is its LDS row, tiles starting at multiples of 256 rows into an expert),
+  // and each expert's W records are a block of their own.
   const __amdgpu_buffer_rsrc_t ast_rs =
       rsrc(g.a_scales_t + ((size_t)m0 << 4), ((int64_t)nk * g.a_rows_pad - m0) << 4);
   const __amdgpu_buffer_rsrc_t bst_rs =
-      rsrc(g.w_scales_t + ((size_t)n0 << 4), ((int64_t)nk * g.w_rows_pad - n0) << 4);
+      rsrc(g.w_scales_t + (((size_t)ex * nk * g.w_rows_pad + n0) << 4),
+           ((int64_t)nk * g.w_rows_pad - n0) << 4);
   const uint32_t t_voff = (uint32_t)(64 * wave + lane) << 4;
 
   // LDS read offsets within a stage of fragment q = 0 for half s2 (piece
@@ -1254,11 +1257,23 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
                          dim3(256), 0, stream, g);
     return hipGetLastError();
   }
+  // Grouped 256 x 256 tiles: with the tiled scale records from K = 512 on,
+  // with raw scales from K = 1024 (below that the fixed cost of a 256 x 256
+  // tile outweighs its better decode reuse; the 256 x 128 kernel does those).
+  // The grid covers every possible tile, rounded up to whole XCD rounds;
+  // workgroups past the tiles that exist return at once.
+  if (grouped && fullk && g.N % big::BN == 0 && g.a_scales_t && g.w_scales_t && g.K >= 512) {
+    const int64_t nb = (max_mtiles * (g.N / big::BN) + 7) / 8 * 8;
+    if (nb == 0) return hipSuccess;
+    if (g.epilogue == kEpiSwiGLU)
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<true, true, kEpiSwiGLU>), dim3((unsigned)nb),
+                         dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<true, true, kEpiStore>), dim3((unsigned)nb),
+                         dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
   if (grouped && fullk && g.N % big::BN == 0 && g.K >= 1024) {
-    // (with fewer than 8 chunks per tile the fixed cost of a 256 x 256 tile
-    // outweighs its better decode reuse; the 256 x 128 kernel does those)
-    // The grid covers every possible tile, rounded up to whole XCD rounds;
-    // workgroups past the tiles that exist return at once.
     const int64_t nb = (max_mtiles * (g.N / big::BN) + 7) / 8 * 8;
     if (nb == 0) return hipSuccess;
     if (g.epilogue == kEpiSwiGLU)
@@ -1292,6 +1307,80 @@ hipError_t launch_scale_tile(const uint8_t* scales, int64_t rows, int32_t K, int
   grid = grid > 8192 ? 8192 : grid;
   hipLaunchKernelGGL(scale_tile_kernel, dim3((unsigned)grid), dim3(256), 0, stream, scales, rows,
                      K, rows_pad, (uint4*)out);
+  return hipGetLastError();
+}
+
+// records of `batch` operands of [rows][K / 16] scales each, one block of
+// [K / 128][rows_pad][16 B] per operand (the expert weights of a grouped GEMM)
+__global__ __launch_bounds__(256) void scale_tile_batched_kernel(const uint8_t* __restrict__ sc,
+                                                                 int64_t rows, int32_t K,
+                                                                 int64_t rows_pad,
+                                                                 uint4* __restrict__ out) {
+  const int64_t b = blockIdx.y;
+  scale_tile_part(sc + b * rows * (K / 16), rows, K, rows_pad, out + b * (K / 128) * rows_pad,
+                  blockIdx.x, gridDim.x);
+}
+
+hipError_t launch_scale_tile_batched(const uint8_t* scales, int64_t batch, int64_t rows, int32_t K,
+                                     int64_t rows_pad, uint8_t* out, hipStream_t stream) {
+  const int64_t total = (int64_t)(K / 128) * rows_pad;
+  if (total == 0 || batch == 0) return hipSuccess;
+  int64_t grid = (total + 255) / 256;
+  grid = grid > 1024 ? 1024 : grid;
+  hipLaunchKernelGGL(scale_tile_batched_kernel, dim3((unsigned)grid, (unsigned)batch), dim3(256), 0,
+                     stream, scales, rows, K, rows_pad, (uint4*)out);
+  return hipGetLastError();
+}
+
+// Records of the R token-sorted rows of a grouped GEMM's A operand: record
+// (c, r) holds the scales of source row a_rows[r] (r itself without a_rows),
+// swizzled for the row's offset within its expert (the expert being the last
+// e with offsets[e] <= r), which is the row's place in its 256-row tile;
+// rows R .. rows_pad - 1 are zero.
+__global__ __launch_bounds__(256) void scale_tile_sorted_kernel(
+    const uint8_t* __restrict__ sc, const int32_t* __restrict__ a_rows, int64_t R, int32_t K,
+    const int32_t* __restrict__ offsets, int32_t E, int64_t rows_pad, uint4* __restrict__ out) {
+  const int64_t total = (int64_t)(K / 128) * rows_pad;
+  const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t c = i / rows_pad, r = i - c * rows_pad;
+    uint2 raw = make_uint2(0, 0);
+    int in_tile = 0;
+    if (r < R) {
+      const int64_t src = a_rows ? (int64_t)a_rows[r] : r;
+      raw = *(const uint2*)(sc + src * (K / 16) + 8 * c);
+      int lo = 0, hi = E;   // offsets[0] <= r < offsets[E]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)offsets[mid] <= r) lo = mid;
+        else hi = mid;
+      }
+      in_tile = (int)((r - offsets[lo]) & 255);
+    }
+    // each E4M3 byte shifted left by 7 is an fp16 of 2^-8 times its value;
+    // the multiply by 256 is exact
+    const uint32_t d0 = __builtin_amdgcn_perm(0u, raw.x, 0x0c010c00u) << 7;
+    const uint32_t d1 = __builtin_amdgcn_perm(0u, raw.x, 0x0c030c02u) << 7;
+    const uint32_t d2 = __builtin_amdgcn_perm(0u, raw.y, 0x0c010c00u) << 7;
+    const uint32_t d3 = __builtin_amdgcn_perm(0u, raw.y, 0x0c030c02u) << 7;
+    const uint4 rec = make_uint4(__builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d0) * k256),
+                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d1) * k256),
+                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d2) * k256),
+                                 __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, d3) * k256));
+    out[i] = swz_sc_rec(rec, in_tile);
+  }
+}
+
+hipError_t launch_scale_tile_sorted(const uint8_t* scales, const int32_t* a_rows, int64_t R,
+                                    int32_t K, const int32_t* offsets, int32_t E, int64_t rows_pad,
+                                    uint8_t* out, hipStream_t stream) {
+  const int64_t total = (int64_t)(K / 128) * rows_pad;
+  if (total == 0) return hipSuccess;
+  int64_t grid = (total + 255) / 256;
+  grid = grid > 4096 ? 4096 : grid;
+  hipLaunchKernelGGL(scale_tile_sorted_kernel, dim3((unsigned)grid), dim3(256), 0, stream, scales,
+                     a_rows, R, K, offsets, E, rows_pad, (uint4*)out);
   return hipGetLastError();
 }
 

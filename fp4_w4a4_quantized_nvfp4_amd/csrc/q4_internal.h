@@ -80,7 +80,9 @@ struct GemmArgs {
   const int32_t* ntiles_dev; // number of valid M tiles (device)
   const int32_t* a_rows;     // A row of each output row (null: identity)
   int64_t a_src_rows;        // rows of the A operand that a_rows indexes (0: M)
-  // optional tiled fp16 scale records (dense NVFP4, K % 128 == 0): see launch_scale_tile
+  // optional tiled fp16 scale records (NVFP4, K % 128 == 0): see launch_scale_tile
+  // (dense), launch_scale_tile_sorted and launch_scale_tile_batched (grouped:
+  // A by sorted row, W one block of nk * w_rows_pad records per expert)
   const uint8_t* a_scales_t;
   const uint8_t* w_scales_t;
   int64_t a_rows_pad;        // rows of the tiled records (a multiple of 256)
@@ -92,6 +94,15 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
 hipError_t launch_scale_tile(const uint8_t* scales, int64_t rows, int32_t K, int64_t rows_pad,
                              uint8_t* out, hipStream_t stream);
 inline int64_t tile_rows_pad(int64_t rows) { return (rows + 255) / 256 * 256; }
+// records of `batch` operands [rows][K / 16]: [batch][K / 128][rows_pad][16 B]
+hipError_t launch_scale_tile_batched(const uint8_t* scales, int64_t batch, int64_t rows, int32_t K,
+                                     int64_t rows_pad, uint8_t* out, hipStream_t stream);
+// records of the R token-sorted rows of a grouped A operand (source row
+// a_rows[r], or r without a_rows; expert ranges `offsets` [E + 1]):
+// [K / 128][rows_pad][16 B], each swizzled for its row's offset in its expert
+hipError_t launch_scale_tile_sorted(const uint8_t* scales, const int32_t* a_rows, int64_t R,
+                                    int32_t K, const int32_t* offsets, int32_t E, int64_t rows_pad,
+                                    uint8_t* out, hipStream_t stream);
 // R and W_S of a dense RAC GEMM (when k > 0 and R, W_S are given) and the
 // scale records of both operands (NVFP4, when a_tiles and w_tiles are given)
 // in one launch

@@ -292,6 +292,20 @@ q4_status_t q4_transpose_bf16(const uint16_t *in, int64_t batch, int64_t rows, i
 q4_status_t q4_moe_pack_w13(const uint16_t *w13, int32_t E, int32_t F, int32_t H,
                             uint16_t *out, void *stream);
 
+/* Scale records of stacked NVFP4 weights (offline): the E4M3 block scales
+ * (one per 16 elements, QUADS section 2.2 "FP4" and the NVFP4 format pages)
+ * of `batch` operands [rows][K/16], widened to fp16 (exact, subnormal scales
+ * included) and laid out as [batch][K/128][rows_pad][16 B], rows_pad = rows
+ * rounded up to 256 (rows past `rows` zero): one record holds the eight
+ * scales of one row over one 128-column chunk, its four dwords in an order
+ * that spreads a tile's LDS reads over the banks.  Derived data only: a
+ * grouped GEMM given the records computes exactly what it computes from the
+ * raw scales.  K % 128 == 0 (Q4_ESHAPE otherwise); out must hold
+ * q4_scale_records_size bytes (Q4_EWORKSPACE); out is caller-owned. */
+size_t q4_scale_records_size(int64_t batch, int64_t rows, int64_t K);
+q4_status_t q4_scale_records(const uint8_t *scales, int64_t batch, int64_t rows, int64_t K,
+                             uint8_t *out, size_t out_bytes, void *stream);
+
 /* Token-sorted grouped W4A4 + RAC SwiGLU expert layer: the compensation of
  * QUADS section 3.3 (Eq. 21-24) at both activation sites of the expert block,
  * the W13 input (the page's profiled site) and the W2 input.
@@ -303,6 +317,12 @@ q4_status_t q4_moe_pack_w13(const uint16_t *w13, int32_t E, int32_t F, int32_t H
  *   w13_hi_t   bf16 [E][H][2F]: per-expert transpose of the packed bf16 W13.
  *   w2_hi_t    bf16 [E][F][H]:  per-expert transpose of the bf16 W2.
  *              Both may be NULL when rac_k == 0.
+ *   w13_scale_records, w2_scale_records: NULL, or (NVFP4 only) the
+ *              q4_scale_records of w13_scales (batch E, rows 2F, K = H) and of
+ *              w2_scales (batch E, rows H, K = F), which must be those scales'
+ *              records (not checked).  Where the shape allows (prefill-sized
+ *              T * topk, H and F multiples of 128 and at least 512) the
+ *              grouped GEMMs then read fp16 scales; results are the same.
  *   rac_k      channels compensated at each of the two activation sites.
  *   Y          [T][H] fp32 or bf16: y_t = sum_s p_ts out_(t,s), slots in order.
  * Steps: sort; quantize tokens (one s_t, one selection over T rows); W13 RAC
@@ -331,7 +351,8 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t *tokens, int64_t T
                                   const uint8_t *w13_scales, const float *w13_tensor_scales,
                                   const uint8_t *w2_codes, const uint8_t *w2_scales,
                                   const float *w2_tensor_scales, const uint16_t *w13_hi_t,
-                                  const uint16_t *w2_hi_t, int32_t rac_k, void *Y,
+                                  const uint16_t *w2_hi_t, const uint8_t *w13_scale_records,
+                                  const uint8_t *w2_scale_records, int32_t rac_k, void *Y,
                                   int32_t y_dtype, void *workspace, size_t workspace_bytes,
                                   int32_t *status, void *stream);
 

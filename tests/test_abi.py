@@ -86,8 +86,17 @@ def test_shape_and_pointer_errors(L):
     assert L.q4_moe_route(fake, 4, 0, 1, fake, fake, None) == 2
     assert L.q4_moe_route(fake, 4, 8, 9, fake, fake, None) == 1
     assert L.moe_w4a4_grouped_gemm(0, fake, 4, 64, fake, fake, 2, 4, 48, fake, fake, fake, fake,
-                                   fake, fake, fake, fake, 0, fake, 1, fake, 1 << 30, None,
-                                   None) == 2
+                                   fake, fake, fake, fake, None, None, 0, fake, 1, fake, 1 << 30,
+                                   None, None) == 2
+    # MoE: scale records are NVFP4 only
+    assert L.moe_w4a4_grouped_gemm(1, fake, 4, 64, fake, fake, 2, 4, 64, fake, fake, None, fake,
+                                   fake, None, fake, fake, fake, None, 0, fake, 1, fake, 1 << 30,
+                                   None, None) == 1
+    assert "NVFP4" in _err(L)
+    # scale records: K % 128, short output
+    assert L.q4_scale_records(fake, 2, 64, 96, fake, 1 << 20, None) == 2
+    assert L.q4_scale_records(fake, 2, 64, 256, fake, 100, None) == 4
+    assert L.q4_scale_records_size(2, 300, 256) == 2 * 2 * 512 * 16
     # sort: topk > 16, misaligned status
     assert L.q4_moe_sort(fake, 4, 32, 17, fake, fake, fake, 1 << 20, None, None) == 1
     assert L.q4_moe_sort(fake, 4, 32, 2, fake, fake, fake, 1 << 20, C.c_void_p(0x100002), None) == 3

@@ -111,7 +111,11 @@ def _check_site(fmt, xb, got, prefix, rac_k):
                                             # grouped tiles (256 x 256 for W13 when
                                             # K >= 1024): partial M tiles, gathered rows
                                             (300, 256, 2, 128, 2, 16),
-                                            (520, 1024, 4, 256, 2, 32)])
+                                            (520, 1024, 4, 256, 2, 32),
+                                            # NVFP4: both grouped GEMMs on 256 x 256
+                                            # tiles reading the tiled scale records
+                                            # (K = 512 at both sites)
+                                            (600, 512, 4, 512, 2, 32)])
 def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
     say(f"moe small fmt={fmt} T={T} H={H} E={E} F={F} topk={topk} k={k}")
     m = q4()
@@ -139,6 +143,60 @@ def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
     say(f"  W2 out rel err {err_o:.2e}")
     assert err_o <= GEMM_TOL
     check_bf16_output(got["Y"], ref["y"], tol=2 * GEMM_TOL)
+
+
+def test_scale_records_layout():
+    """q4_scale_records against the documented layout: record (c, r) of
+    operand b holds the E4M3 scales of row r, columns 128 c .. 128 c + 127, as
+    fp16, dword d stored at d ^ ((r / 8) % 4); rows past `rows` are zero.  The
+    expected fp16 values are the oracle's E4M3 decoding (exact in fp16)."""
+    m = q4()
+    rng = np.random.default_rng(11)
+    b, rows, K = 3, 300, 384
+    sc = rng.integers(0, 127, size=(b, rows, K // 16), dtype=np.uint8)   # every finite E4M3 code
+    rec = host(m.q4_scale_records(dev(sc), K)).reshape(b, K // 128, 512, 4, 4)
+    pad = 512
+    assert rec.shape[2] == pad
+    vals = rec.view(np.uint16).view(np.float16).astype(np.float64)    # [b][c][row][dword][2 halves]
+    vals = vals.reshape(b, K // 128, pad, 4, 2)
+    for r in range(pad):
+        q = (r // 8) % 4
+        d_store = np.arange(4) ^ q                                     # logical dword d is stored at d ^ q
+        logical = vals[:, :, r, d_store, :].reshape(b, K // 128, 8)    # scale 2 d + half
+        if r < rows:
+            want = oracle.formats.E4M3_VALUES[sc[:, r, :].astype(np.int64)].reshape(b, K // 128, 8)
+            assert np.array_equal(logical, want), r
+        else:
+            assert not logical.any(), r
+
+
+def test_scale_records_same_result():
+    """The grouped layer with the weights' scale records equals the layer
+    without them bit for bit where both run the 256 x 256 kernel (K >= 1024 at
+    both sites): the records change where the scales come from, not the
+    arithmetic."""
+    m = q4()
+    rng = np.random.default_rng(12)
+    T, H, E, F, topk, k = 600, 1024, 4, 1024, 2, 32
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[:, rng.choice(H, 3, replace=False)] *= 40
+    logits = dev(rng.standard_normal((T, E)).astype(np.float32))
+    w13 = dev(_bits((rng.standard_normal((E, 2 * F, H)) * 0.05).astype(np.float32)))
+    w2 = dev(_bits((rng.standard_normal((E, H, F)) * 0.05).astype(np.float32)))
+    xd = dev(_bits(x))
+    idx, p = m.q4_moe_route(logits, topk)
+    with_rec = m.prepare_moe_weights(w13, w2)
+    without = m.prepare_moe_weights(w13, w2, scale_records=False)
+    assert "scale_records" in with_rec["w13"] and "scale_records" not in without["w13"]
+    Y1, ws1 = m.moe_w4a4_grouped_gemm(xd, idx, p, with_rec, k, out_dtype=m.OUT_F32)
+    Y0, ws0 = m.moe_w4a4_grouped_gemm(xd, idx, p, without, k, out_dtype=m.OUT_F32)
+    torch.cuda.synchronize()
+    offs, _ = m.moe_workspace_layout(0, T, E, H, F, topk, k)
+    R = T * topk
+    h1 = _ws_field(ws1, offs, 7, R * F * 2, torch.int16)
+    h0 = _ws_field(ws0, offs, 7, R * F * 2, torch.int16)
+    assert np.array_equal(h1, h0)
+    assert np.array_equal(host(Y1).view(np.uint32), host(Y0).view(np.uint32))
 
 
 def _quant(fmt):
