@@ -76,8 +76,8 @@ _SIGS = {
     "moe_workspace_size": (_SZ, [_I32, _I64, _I32, _I32, _I32, _I32, _I32]),
     "moe_workspace_layout": (_I32, [_I32, _I64, _I32, _I32, _I32, _I32, _I32, _P]),
     "moe_w4a4_grouped_gemm": (_I32, [_I32, _P, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P,
-                                     _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _SZ, _P,
-                                     _P]),
+                                     _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _SZ,
+                                     _P, _P]),
 }
 
 
@@ -467,10 +467,12 @@ def moe_workspace_layout(fmt, T, E, H, F, topk, rac_k):
 
 
 def moe_w4a4_grouped_gemm(tokens, topk_idx, topk_w, experts, rac_k, out_dtype=OUT_BF16,
-                          workspace=None, stream=None, Y=None, status=None):
+                          workspace=None, stream=None, Y=None, status=None, h_tensor_scale=None):
     """Token-sorted grouped W4A4+RAC SwiGLU expert layer; returns (Y, workspace).
     ``status`` (optional int32 [1]) receives 0, or 1 for an expert index
-    outside [0, E)."""
+    outside [0, E).  ``h_tensor_scale`` (optional fp32 [1], NVFP4) supplies
+    h's tensor scale; on prefill shapes h is then quantized inside the W13
+    GEMM's epilogue."""
     with _on(stream):
         tokens = _bf16(tokens, "tokens")
         T, H = tokens.shape
@@ -511,7 +513,8 @@ def moe_w4a4_grouped_gemm(tokens, topk_idx, topk_w, experts, rac_k, out_dtype=OU
             _ptr(w2["codes"]), _ptr(w2["scales"]), _ptr(w2["tensor_scale"]),
             _ptr(experts.get("w13_hi_t"), _BF16_TYPES, (E, H, 2 * F), "w13_hi_t") if rac_k else None,
             _ptr(experts.get("w2_hi_t"), _BF16_TYPES, (E, F, H), "w2_hi_t") if rac_k else None,
-            rec13, rec2, rac_k, _ptr(Y), out_dtype, _ptr(workspace, torch.uint8), wsb,
+            rec13, rec2, _ptr(h_tensor_scale, torch.float32, (1,), "h_tensor_scale"),
+            rac_k, _ptr(Y), out_dtype, _ptr(workspace, torch.uint8), wsb,
             _status(status),
             _stream(stream)))
         return Y, workspace

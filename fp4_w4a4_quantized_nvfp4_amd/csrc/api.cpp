@@ -619,6 +619,7 @@ struct MoeLayout {
   size_t off[Q4_MOE_WS_FIELDS];
   size_t inv_perm, tiles, ntiles, tiles_s, ntiles_s, counts, a_rows, w13_sel, w2_sel, qws;
   size_t x_rec, h_rec;   // sorted-row scale records of the two sites (0: none)
+  size_t h_part;         // fp64 [2 * M tiles][F]: h's residual sums (quantizing W13 epilogue)
   bool tiled13, tiled2;  // shapes on which the records can be used
   int64_t rows_pad;
   size_t total;
@@ -672,6 +673,7 @@ MoeLayout moe_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F, in
   L.rows_pad = tile_rows_pad(R);
   L.x_rec = L.tiled13 ? take((size_t)(H / 128) * L.rows_pad * 16) : 0;
   L.h_rec = L.tiled2 ? take((size_t)(F / 128) * L.rows_pad * 16) : 0;
+  L.h_part = grouped_big ? take((size_t)2 * moe_max_tiles(T, E, topk) * F * 8) : 0;
   L.total = o;
   return L;
 }
@@ -700,7 +702,8 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
                                   const uint8_t* w2_codes, const uint8_t* w2_scales,
                                   const float* w2_tensor_scales, const uint16_t* w13_hi_t,
                                   const uint16_t* w2_hi_t, const uint8_t* w13_scale_records,
-                                  const uint8_t* w2_scale_records, int32_t rac_k, void* Y,
+                                  const uint8_t* w2_scale_records, const float* h_tensor_scale,
+                                  int32_t rac_k, void* Y,
                                   int32_t y_dtype, void* workspace, size_t workspace_bytes,
                                   int32_t* status, void* stream) {
   const char* fn = "moe_w4a4_grouped_gemm";
@@ -729,6 +732,10 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
     return fail(Q4_EINVAL, "%s: scale records are an NVFP4 layout", fn);
   if (w13_scale_records) Q4_REQUIRE_PTR(w13_scale_records);
   if (w2_scale_records) Q4_REQUIRE_PTR(w2_scale_records);
+  if (h_tensor_scale) {
+    if (mx) return fail(Q4_EINVAL, "%s: MXFP4 has no tensor scale to supply", fn);
+    Q4_REQUIRE_SCALAR(h_tensor_scale, 4);
+  }
   if (rac_k > 0) {
     Q4_REQUIRE_PTR(w13_hi_t);
     Q4_REQUIRE_PTR(w2_hi_t);
@@ -829,15 +836,35 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
     g.a_rows_pad = L.rows_pad;
     g.w_rows_pad = tile_rows_pad(2 * (int64_t)F);
   }
-  Q4_TRY(grouped_gemm(g), "moe w13 gemm");
   // ---- activation site 2: h (sorted rows)
   uint8_t* hc = (uint8_t*)P(L.off[8]);
   uint8_t* hs = (uint8_t*)P(L.off[9]);
   float* hts = mx ? nullptr : (float*)P(L.off[10]);
   int32_t* hS = (int32_t*)P(L.off[11]);
   uint16_t* hR = (uint16_t*)P(L.off[12]);
-  Q4_TRY(launch_quantize(mx, hbuf, R, F, nullptr, hc, hs, hts, (double*)P(L.off[15]), rac_k,
-                         rac_k ? hS : nullptr, P(L.qws), s), "moe quantize h");
+  double* hscore = (double*)P(L.off[15]);
+  // With a supplied s_h on the 256 x 256 kernel, the W13 epilogue quantizes h
+  // as it stores it (codes, scales, residual sums per half tile): no separate
+  // pass over h.  Otherwise the quantizer runs on h (with the supplied s_h,
+  // when there is one, in place of h's amax).
+  const bool fuse_h = h_tensor_scale && L.h_part && grouped_big_path(g);
+  if (fuse_h) {
+    g.epilogue = kEpiSwiGLUQuant;
+    g.q_codes = hc;
+    g.q_scales = hs;
+    g.q_ts = h_tensor_scale;
+    g.q_partial = (double*)P(L.h_part);
+  }
+  Q4_TRY(grouped_gemm(g), "moe w13 gemm");
+  if (fuse_h) {
+    Q4_TRY(launch_copy_scale(h_tensor_scale, hts, s), "moe h tensor scale");
+    Q4_TRY(launch_score_reduce_dev((const double*)P(L.h_part), ntiles, 2, F, hscore, s),
+           "moe h scores");
+    if (rac_k) Q4_TRY(launch_select(hscore, F, rac_k, hS, s), "moe h selection");
+  } else {
+    Q4_TRY(launch_quantize(mx, hbuf, R, F, h_tensor_scale, hc, hs, hts, hscore, rac_k,
+                           rac_k ? hS : nullptr, P(L.qws), s), "moe quantize h");
+  }
   if (rec2)
     Q4_TRY(launch_scale_tile_sorted(hs, nullptr, R, F, offsets, E, L.rows_pad, (uint8_t*)P(L.h_rec),
                                     s), "moe h scale records");

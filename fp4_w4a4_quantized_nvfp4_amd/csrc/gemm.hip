@@ -19,6 +19,7 @@
 #include <type_traits>
 
 #include "q4_internal.h"
+#include "q4_nvfp4_enc.h"
 #include "q4_prep.h"
 
 namespace q4 {
@@ -500,6 +501,7 @@ struct Frag {
 template <bool TILED, bool GROUPED, int EPI, bool RSC = false, bool MX = false>
 __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   static_assert(GROUPED || EPI == kEpiStore, "SwiGLU is a grouped epilogue");
+  static_assert(EPI != kEpiSwiGLUQuant || !MX, "the quantizing epilogue writes NVFP4");
   static_assert(!MX || (!TILED && !RSC), "MXFP4: raw scales, no scaled compensation");
   // MX scale area: 4 E8M0 bytes per row per chunk
   constexpr int STAGE = big::STAGE<TILED>;
@@ -522,6 +524,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
 
   int64_t m0, n0, m_end;
   int ex = 0;   // expert (grouped)
+  int mt = 0;   // M tile of the table (grouped)
   if constexpr (GROUPED) {
     // tiles of the table ({expert, first row, end row} per M tile), M tile
     // major; each XCD (workgroup index mod 8; the grid is a multiple of 8)
@@ -532,7 +535,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     const int per = (total + 7) >> 3;
     const int l = (int)(blockIdx.x >> 3), t = (int)(blockIdx.x & 7) * per + l;
     if (l >= per || t >= total) return;
-    const int mt = t / nbn;
+    mt = t / nbn;
     const int4 tt = ((const int4*)g.tiles)[mt];
     ex = tt.x;
     m0 = tt.y;
@@ -1047,14 +1050,16 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     };
     // Accumulator element r of lane l is row 8 (r / 4) + 4 (l / 32) + r % 4,
     // column l % 32 of its 32 x 32 tile.
-    if constexpr (EPI == kEpiSwiGLU) {
+    if constexpr (EPI == kEpiSwiGLU || EPI == kEpiSwiGLUQuant) {
       // W13 with gate and up rows interleaved in blocks of 32: MFMA column
       // tile ni = 2p is the gate and 2p + 1 the up of h columns
       // (n0 + 128 wn) / 2 + 32 p + l % 32; h = silu(gate) * up as bf16 into
       // Y [rows][ldy], ldy >= N / 2.  Staged through LDS per pass (a wave's 16
       // rows x 64 h columns) so that every store writes 16 contiguous bytes.
+      constexpr bool QH = EPI == kEpiSwiGLUQuant;
       const int64_t fcols = N / 2, f0 = (n0 + wn * 128) / 2;
-      const bool staged = (fcols % 8) == 0 && (g.ldy % 8) == 0 && (((uintptr_t)g.Y) & 15u) == 0;
+      const bool staged =
+          QH || ((fcols % 8) == 0 && (g.ldy % 8) == 0 && (((uintptr_t)g.Y) & 15u) == 0);
       auto hval = [&](int mi, int p, int r) {
         return silu(sc(acc[mi][2 * p][r])) * (sc(acc[mi][2 * p + 1][r]));
       };
@@ -1062,32 +1067,153 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
         __syncthreads();   // every wave is done with the stages
         constexpr int PS = 144;   // row pitch (bytes): 64 bf16 and 16 bytes of pad
         uint8_t* const ep = stage0 + wave * (16 * PS);
+        // QH: h quantized as it is stored (NVFP4 under the supplied tensor
+        // scale q_ts, the stand-alone quantizer's encoding): the lane that
+        // stores 8 h values of a row encodes them, its neighbour (lane ^ 1)
+        // holding the other half of their 16-block; each lane keeps the fp64
+        // sums of squared residuals of its 8 columns.
+        float qst = 1.0f, inv6st = 1.0f;
+        double st6 = 6.0;
+        int eDp = 0, tie_mode = kTieEven;
+        uint8_t* const tab = stage2;
+        if constexpr (QH) {
+          qst = g.q_ts[0];
+          tie_mode = supplied_tie_mode(qst);
+          int eD;
+          const double Dm = frexp(6.0 * (double)qst, &eD);   // 6 s_t = Dm 2^eD, Dm in [0.5, 1)
+          eDp = eD - 1;
+          inv6st = 1.0f / (6.0f * qst);
+          st6 = 6.0 * (double)qst;
+          if (tid < 128) tab[tid] = (uint8_t)e4m3_mantissa_entry(tid, 2.0 * Dm);
+          __syncthreads();
+        }
+        if constexpr (!QH) {
   #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
+          for (int mi = 0; mi < 4; ++mi) {
   #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int64_t rbase = m0 + wm * 128 + mi * 32 + 16 * half;
+            for (int half = 0; half < 2; ++half) {
+              const int64_t rbase = m0 + wm * 128 + mi * 32 + 16 * half;
   #pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
+              for (int pp = 0; pp < 2; ++pp) {
   #pragma unroll
-              for (int rr = 0; rr < 8; rr += 2) {
-                const int r = 8 * half + rr;
-                const int lr = 8 * (rr >> 2) + 4 * h + (rr & 3);
-                typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                const bf16x2 pr = {(__bf16)hval(mi, pp, r), (__bf16)hval(mi, pp, r + 1)};
-                const uint32_t w = __builtin_bit_cast(uint32_t, pr);
-                uint8_t* const q = ep + lr * PS + (pp * 32 + l32) * 2;
-                *(uint16_t*)q = (uint16_t)w;
-                *(uint16_t*)(q + PS) = (uint16_t)(w >> 16);
+                for (int rr = 0; rr < 8; rr += 2) {
+                  const int r = 8 * half + rr;
+                  const int lr = 8 * (rr >> 2) + 4 * h + (rr & 3);
+                  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                  const bf16x2 pr = {(__bf16)hval(mi, pp, r), (__bf16)hval(mi, pp, r + 1)};
+                  const uint32_t w = __builtin_bit_cast(uint32_t, pr);
+                  uint8_t* const q = ep + lr * PS + (pp * 32 + l32) * 2;
+                  *(uint16_t*)q = (uint16_t)w;
+                  *(uint16_t*)(q + PS) = (uint16_t)(w >> 16);
+                }
+              }
+  #pragma unroll
+              for (int it = 0; it < 2; ++it) {
+                const int cid = it * 64 + lane, lr = cid >> 3, cc = (cid & 7) * 8;
+                const uint4 v = *(const uint4*)(ep + lr * PS + cc * 2);
+                const int64_t row = rbase + lr, col = f0 + cc;
+                if (row < m_end && col < fcols) *(uint4*)((uint16_t*)g.Y + row * g.ldy + col) = v;
               }
             }
+          }
+        } else {
+          // The wave's whole 128 x 64 h block goes to LDS first (its own
+          // region, two waves per stage), then comes back in 16 groups of 8
+          // values per lane, encoded four groups at a time: independent
+          // chains, so that one wave per SIMD still hides the latencies.
+          uint8_t* const epq = (wave < 2 ? stage0 : stage1) + (wave & 1) * (128 * PS);
   #pragma unroll
-            for (int it = 0; it < 2; ++it) {
-              const int cid = it * 64 + lane, lr = cid >> 3, cc = (cid & 7) * 8;
-              const uint4 v = *(const uint4*)(ep + lr * PS + cc * 2);
-              const int64_t row = rbase + lr, col = f0 + cc;
-              if (row < m_end && col < fcols) *(uint4*)((uint16_t*)g.Y + row * g.ldy + col) = v;
+          for (int mi = 0; mi < 4; ++mi) {
+  #pragma unroll
+            for (int half = 0; half < 2; ++half) {
+  #pragma unroll
+              for (int pp = 0; pp < 2; ++pp) {
+  #pragma unroll
+                for (int rr = 0; rr < 8; rr += 2) {
+                  const int r = 8 * half + rr;
+                  const int lr = mi * 32 + 16 * half + 8 * (rr >> 2) + 4 * h + (rr & 3);
+                  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                  const bf16x2 pr = {(__bf16)hval(mi, pp, r), (__bf16)hval(mi, pp, r + 1)};
+                  const uint32_t w = __builtin_bit_cast(uint32_t, pr);
+                  uint8_t* const q = epq + lr * PS + (pp * 32 + l32) * 2;
+                  *(uint16_t*)q = (uint16_t)w;
+                  *(uint16_t*)(q + PS) = (uint16_t)(w >> 16);
+                }
+              }
             }
+          }
+          // QH: h quantized as it is stored (NVFP4 under the supplied tensor
+          // scale q_ts, the stand-alone quantizer's encoding): the lane that
+          // stores 8 h values of a row encodes them, its neighbour (lane ^ 1)
+          // holding the other half of their 16-block; each lane keeps the
+          // fp64 sums of squared residuals of its 8 columns (lane % 8 fixes
+          // them).  Every lane encodes (the block amax and the near-tie
+          // rounds span lanes); only live ones store and count.
+          double qacc[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qacc[i] = 0.0;
+          const int cc = (lane & 7) * 8;
+          const int64_t col = f0 + cc;
+#pragma unroll
+          for (int g4 = 0; g4 < 16; g4 += 4) {
+            uint4 v[4];
+            float xf[4][8], bm[4];
+            int lrow[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              lrow[u] = 16 * ((g4 + u) >> 1) + 8 * ((g4 + u) & 1) + (lane >> 3);
+              v[u] = *(const uint4*)(epq + lrow[u] * PS + cc * 2);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              xf[u][0] = bf16_lo(v[u].x); xf[u][1] = bf16_hi(v[u].x);
+              xf[u][2] = bf16_lo(v[u].y); xf[u][3] = bf16_hi(v[u].y);
+              xf[u][4] = bf16_lo(v[u].z); xf[u][5] = bf16_hi(v[u].z);
+              xf[u][6] = bf16_lo(v[u].w); xf[u][7] = bf16_hi(v[u].w);
+              float m = 0.0f;
+#pragma unroll
+              for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(xf[u][i]));
+              bm[u] = fmaxf(m, dpp_quad_xor1(m));   // 16-block = lane pair
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int64_t row = m0 + wm * 128 + lrow[u];
+              const bool live = row < m_end && col < fcols;
+              uint32_t code, scode;
+              float s;
+              nvfp4_lane_encode<false, 8, true>(&v[u], xf[u], bm[u], qst, eDp, tab, inv6st, st6,
+                                                tie_mode, &code, &scode, &s);
+              if (live) {
+                *(uint4*)((uint16_t*)g.Y + row * g.ldy + col) = v[u];
+                *(uint32_t*)(g.q_codes + row * (fcols / 2) + col / 2) = code;
+                if ((lane & 1) == 0) g.q_scales[row * (fcols / 16) + col / 16] = (uint8_t)scode;
+                const f32x2v c2[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0),
+                                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 1),
+                                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 2),
+                                      __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 3)};
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                  // r = RN32(x - c s s_t): c s is exact, one fused rounding
+                  const double r0 = (double)fmaf(-(c2[b].x * s), qst, xf[u][2 * b]);
+                  const double r1 = (double)fmaf(-(c2[b].y * s), qst, xf[u][2 * b + 1]);
+                  qacc[2 * b] = fma(r0, r0, qacc[2 * b]);
+                  qacc[2 * b + 1] = fma(r1, r1, qacc[2 * b + 1]);
+                }
+              }
+            }
+          }
+          // lanes with the same lane % 8 hold the same 8 columns over
+          // different rows: add them (fixed order), then lanes 0..7 write the
+          // wave's 128-row half-tile sums
+#pragma unroll
+          for (int o = 8; o < 64; o <<= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qacc[i] += __shfl_xor(qacc[i], o, 64);
+          if (lane < 8) {
+            double* const dst = g.q_partial + (int64_t)(2 * mt + wm) * fcols + f0 + lane * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              if (f0 + lane * 8 + i < fcols) dst[i] = qacc[i];
           }
         }
       } else {
@@ -1211,6 +1337,11 @@ hipError_t launch_t(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
 
 }  // namespace
 
+bool grouped_big_path(const GemmArgs& g) {
+  if (g.mx || g.tiles == nullptr || (g.K % BK) != 0 || g.N % big::BN != 0) return false;
+  return (g.a_scales_t && g.w_scales_t) ? g.K >= 512 : g.K >= 1024;
+}
+
 hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
   const bool fullk = (g.K % BK) == 0;
   const bool grouped = g.tiles != nullptr;
@@ -1262,10 +1393,14 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
   // tile outweighs its better decode reuse; the 256 x 128 kernel does those).
   // The grid covers every possible tile, rounded up to whole XCD rounds;
   // workgroups past the tiles that exist return at once.
+  if (g.epilogue == kEpiSwiGLUQuant && !grouped_big_path(g)) return hipErrorInvalidValue;
   if (grouped && fullk && g.N % big::BN == 0 && g.a_scales_t && g.w_scales_t && g.K >= 512) {
     const int64_t nb = (max_mtiles * (g.N / big::BN) + 7) / 8 * 8;
     if (nb == 0) return hipSuccess;
-    if (g.epilogue == kEpiSwiGLU)
+    if (g.epilogue == kEpiSwiGLUQuant)
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<true, true, kEpiSwiGLUQuant>),
+                         dim3((unsigned)nb), dim3(256), 0, stream, g);
+    else if (g.epilogue == kEpiSwiGLU)
       hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<true, true, kEpiSwiGLU>), dim3((unsigned)nb),
                          dim3(256), 0, stream, g);
     else
@@ -1276,7 +1411,10 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
   if (grouped && fullk && g.N % big::BN == 0 && g.K >= 1024) {
     const int64_t nb = (max_mtiles * (g.N / big::BN) + 7) / 8 * 8;
     if (nb == 0) return hipSuccess;
-    if (g.epilogue == kEpiSwiGLU)
+    if (g.epilogue == kEpiSwiGLUQuant)
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<false, true, kEpiSwiGLUQuant>),
+                         dim3((unsigned)nb), dim3(256), 0, stream, g);
+    else if (g.epilogue == kEpiSwiGLU)
       hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<false, true, kEpiSwiGLU>), dim3((unsigned)nb),
                          dim3(256), 0, stream, g);
     else

@@ -25,6 +25,11 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
                            hipStream_t stream);
 hipError_t launch_select(const double* scores, int64_t cols, int32_t topk, int32_t* idx,
                          hipStream_t stream);
+// scores[j] = sum over r < mult * ngroups_dev[0], ascending, of partial[r][j]
+hipError_t launch_score_reduce_dev(const double* partial, const int32_t* ngroups_dev, int32_t mult,
+                                   int64_t cols, double* scores, hipStream_t stream);
+// ts_out[0] = ts_in[0] (1 when ts_in is null)
+hipError_t launch_copy_scale(const float* ts_in, float* ts_out, hipStream_t stream);
 // p[0..n) = v (a kernel, not a memset, so the write may sit in a captured graph)
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 hipError_t launch_residual_gather(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
@@ -44,7 +49,9 @@ hipError_t launch_moe_pack_w13(const uint16_t* w13, int32_t E, int32_t F, int32_
                                uint16_t* out, hipStream_t stream);
 
 // ---------------------------------------------------------------- GEMM
-enum GemmEpilogue : int32_t { kEpiStore = 0, kEpiSwiGLU = 1 };
+// kEpiSwiGLUQuant: the SwiGLU epilogue that also quantizes h to NVFP4 under a
+// supplied tensor scale (grouped 256 x 256 kernel only)
+enum GemmEpilogue : int32_t { kEpiStore = 0, kEpiSwiGLU = 1, kEpiSwiGLUQuant = 2 };
 
 // One W4A4 (+ residual) GEMM, dense or grouped by expert.
 struct GemmArgs {
@@ -87,7 +94,19 @@ struct GemmArgs {
   const uint8_t* w_scales_t;
   int64_t a_rows_pad;        // rows of the tiled records (a multiple of 256)
   int64_t w_rows_pad;
+  // kEpiSwiGLUQuant: h's NVFP4 codes [rows][N/4] and E4M3 scales [rows][N/32]
+  // under the tensor scale q_ts[0], and the fp64 sums of its squared
+  // residuals per h column over each 128-row half of each M tile,
+  // q_partial [2 * M tiles][N/2] (half tile 2 t + i of M tile t)
+  uint8_t* q_codes;
+  uint8_t* q_scales;
+  const float* q_ts;
+  double* q_partial;
 };
+
+// whether a grouped GEMM runs on the 256 x 256 kernel (the one with the
+// quantizing SwiGLU epilogue)
+bool grouped_big_path(const GemmArgs& g);
 
 hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream);
 // scale records [K/128][rows_pad][16 B] of an NVFP4 operand for the dense kernel

@@ -323,6 +323,16 @@ q4_status_t q4_scale_records(const uint8_t *scales, int64_t batch, int64_t rows,
  *              records (not checked).  Where the shape allows (prefill-sized
  *              T * topk, H and F multiples of 128 and at least 512) the
  *              grouped GEMMs then read fp16 scales; results are the same.
+ *   h_tensor_scale: NULL, or (NVFP4 only) device fp32 [1]: h's tensor scale
+ *              supplied by the caller (delayed scaling, e.g. an earlier step's
+ *              s_h) instead of RN32(amax(h) / 2688).  Where the W13 GEMM runs
+ *              on its 256 x 256 tiles (prefill shapes), h is then quantized in
+ *              the W13 epilogue as it is produced (the fused stage of QUADS
+ *              section 3.3 "Efficient implementation"): codes, scales and the
+ *              per-channel residual sums come out of the GEMM, with no
+ *              separate pass over h; elsewhere the quantizer runs on h with
+ *              this scale.  Blocks whose amax exceeds 2688 s_h saturate
+ *              (E4M3 scale 448, codes +-6), as the format defines.
  *   rac_k      channels compensated at each of the two activation sites.
  *   Y          [T][H] fp32 or bf16: y_t = sum_s p_ts out_(t,s), slots in order.
  * Steps: sort; quantize tokens (one s_t, one selection over T rows); W13 RAC
@@ -352,7 +362,8 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t *tokens, int64_t T
                                   const uint8_t *w2_codes, const uint8_t *w2_scales,
                                   const float *w2_tensor_scales, const uint16_t *w13_hi_t,
                                   const uint16_t *w2_hi_t, const uint8_t *w13_scale_records,
-                                  const uint8_t *w2_scale_records, int32_t rac_k, void *Y,
+                                  const uint8_t *w2_scale_records, const float *h_tensor_scale,
+                                  int32_t rac_k, void *Y,
                                   int32_t y_dtype, void *workspace, size_t workspace_bytes,
                                   int32_t *status, void *stream);
 

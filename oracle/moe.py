@@ -71,7 +71,8 @@ def _rows(q: QuantResult, rows: np.ndarray) -> QuantResult:
 
 
 def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
-              wq13=None, wq2=None, fmt: str = "nvfp4", Sx_override=None, Sh_override=None):
+              wq13=None, wq2=None, fmt: str = "nvfp4", Sx_override=None, Sh_override=None,
+              h_tensor_scale=None):
     """Whole expert layer; returns a dict of every intermediate (fp64 unless noted).
 
     x_bits [T, H] bf16 bits; idx/p from ``moe_route``; w13_bits [E, 2F, H] and
@@ -82,7 +83,8 @@ def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
     activation and weight format ("nvfp4" or "mxfp4").  ``Sx_override`` /
     ``Sh_override`` replace the selected channel sets of the two sites (a set
     already validated against this oracle's scores, where several sets are
-    correct at a near-tie).
+    correct at a near-tie).  ``h_tensor_scale`` (NVFP4) quantizes h under that
+    supplied tensor scale instead of RN32(amax(h) / 2688) (delayed scaling).
     """
     quant = nvfp4_quantize if fmt == "nvfp4" else mxfp4_quantize
     T, H = x_bits.shape
@@ -108,7 +110,10 @@ def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
         y13[r0:r1] = rac_gemm(_rows(qx, rows), wq13[e], Rx[rows], w13_bits[e], Sx)
     h = swiglu_bf16(y13[:, :F], y13[:, F:])
     h_used = h if h_override is None else np.asarray(h_override, dtype=np.uint16)
-    qh = quant(h_used)
+    if h_tensor_scale is not None and fmt == "nvfp4":
+        qh = quant(h_used, tensor_scale=float(h_tensor_scale))
+    else:
+        qh = quant(h_used)
     sh = channel_scores(qh.resid)
     Sh = select_topk(sh, rac_k) if Sh_override is None else np.asarray(Sh_override)
     Rh = residual_gather(qh.resid, Sh)

@@ -83,3 +83,45 @@ def check_selection(S_gpu, ref: np.ndarray, k: int, rows: int, gpu_scores=None) 
           f"(k-th score {t!r}): gpu takes {extra}, oracle {miss}", flush=True)
     sys.stdout.flush()
     return S
+
+
+# fp16 rounding of the NVFP4 compensation operands (unit roundoff 2^-11; the
+# fp32 quotient before it adds 2^-23 at most)
+RAC_FP16_REL = 2.0 ** -11 * (1.0 + 2.0 ** -10)
+
+
+def rac_fp16_bound(R: np.ndarray, Wsel: np.ndarray, s_a: float, s_w: float) -> np.ndarray:
+    """Elementwise bound, in output units, of what the NVFP4 GEMM's fp16
+    compensation operands add to its error.  The selected weight columns enter
+    as fp16(w / (s_W f_A)) (s_A = f_A 2^e_A, f_A in [0.5, 1)): relative error
+    RAC_FP16_REL, or 2^-25 absolute in those units below fp16's normal range;
+    the residual enters as bf16(r) 2^-e_A, exact down to 2^-17 and within
+    2^-25 absolute below.  With R [rows][k] and Wsel [cols][k] the residual
+    and weight values on the selected channels:
+        RAC_FP16_REL |R| |Wsel|^T + 2^-25 (s_W |R| 1 + s_A 1 |Wsel|^T)."""
+    R = np.abs(np.asarray(R, dtype=np.float64))
+    W = np.abs(np.asarray(Wsel, dtype=np.float64))
+    if R.shape[1] == 0:
+        return np.zeros((R.shape[0], W.shape[0]))
+    b = RAC_FP16_REL * (R @ W.T)
+    b += 2.0 ** -25 * (s_w * R.sum(axis=1)[:, None] + s_a * W.sum(axis=1)[None, :])
+    return b
+
+
+def check_close(y: np.ndarray, ref: np.ndarray, tol: float, extra=None, bf16_ulp=False) -> float:
+    """|y - ref| <= tol max(|ref|, rms(ref)) (+ extra, elementwise) (+ one bf16
+    ulp of ref when y was rounded to bf16).  Returns the largest relative
+    error against the tol term alone."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 1.0
+    den = np.maximum(np.abs(ref), rms if rms > 0 else 1.0)
+    lim = tol * den
+    if extra is not None:
+        lim = lim + extra
+    if bf16_ulp:
+        lim = lim + np.abs(ref) * 2.0 ** -8
+    bad = np.abs(y - ref) > lim
+    assert not bad.any(), f"outside the bound at {np.argwhere(bad)[:5].tolist()}"
+    return float(np.max(np.abs(y - ref) / den)) if ref.size else 0.0
+

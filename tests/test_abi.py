@@ -86,13 +86,18 @@ def test_shape_and_pointer_errors(L):
     assert L.q4_moe_route(fake, 4, 0, 1, fake, fake, None) == 2
     assert L.q4_moe_route(fake, 4, 8, 9, fake, fake, None) == 1
     assert L.moe_w4a4_grouped_gemm(0, fake, 4, 64, fake, fake, 2, 4, 48, fake, fake, fake, fake,
-                                   fake, fake, fake, fake, None, None, 0, fake, 1, fake, 1 << 30,
-                                   None, None) == 2
+                                   fake, fake, fake, fake, None, None, None, 0, fake, 1, fake,
+                                   1 << 30, None, None) == 2
     # MoE: scale records are NVFP4 only
     assert L.moe_w4a4_grouped_gemm(1, fake, 4, 64, fake, fake, 2, 4, 64, fake, fake, None, fake,
-                                   fake, None, fake, fake, fake, None, 0, fake, 1, fake, 1 << 30,
-                                   None, None) == 1
+                                   fake, None, fake, fake, fake, None, None, 0, fake, 1, fake,
+                                   1 << 30, None, None) == 1
     assert "NVFP4" in _err(L)
+    # MoE: a supplied h tensor scale is NVFP4 only
+    assert L.moe_w4a4_grouped_gemm(1, fake, 4, 64, fake, fake, 2, 4, 64, fake, fake, None, fake,
+                                   fake, None, fake, fake, None, None, fake, 0, fake, 1, fake,
+                                   1 << 30, None, None) == 1
+    assert "tensor scale" in _err(L)
     # scale records: K % 128, short output
     assert L.q4_scale_records(fake, 2, 64, 96, fake, 1 << 20, None) == 2
     assert L.q4_scale_records(fake, 2, 64, 256, fake, 100, None) == 4

@@ -14,7 +14,7 @@ import oracle
 from oracle.quant import QuantResult
 from workloads import WORKLOADS, bf16_bits_from_f32, make_activations, make_logits, make_moe_weights
 from tests.gpu_util import GEMM_TOL, bf16_to_f64, cached, check_bf16_output, dev, gemm_rel_err, host, say
-from tests.parity import check_scores, check_selection
+from tests.parity import check_close, check_scores, check_selection, rac_fp16_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -57,14 +57,18 @@ def test_route_and_sort():
     assert np.array_equal(host(perm), pe) and np.array_equal(host(off), oe)
 
 
-def _run_layer(m, xb, logits, w13, w2, topk, rac_k, fmt=0, out_dtype=1):
+def _run_layer(m, xb, logits, w13, w2, topk, rac_k, fmt=0, out_dtype=1, h_ts=None,
+               experts=None):
     T, H = xb.shape
     E, F2, _ = w13.shape
     F = F2 // 2
     x = dev(xb)
     idx, p = m.q4_moe_route(dev(logits), topk)
-    experts = m.prepare_moe_weights(dev(w13), dev(w2), fmt=fmt)
-    Y, ws = m.moe_w4a4_grouped_gemm(x, idx, p, experts, rac_k, out_dtype=out_dtype)
+    if experts is None:
+        experts = m.prepare_moe_weights(dev(w13), dev(w2), fmt=fmt)
+    hts = None if h_ts is None else dev(np.array([h_ts], dtype=np.float32))
+    Y, ws = m.moe_w4a4_grouped_gemm(x, idx, p, experts, rac_k, out_dtype=out_dtype,
+                                    h_tensor_scale=hts)
     torch.cuda.synchronize()
     offs, _ = m.moe_workspace_layout(fmt, T, E, H, F, topk, rac_k)
     R = T * topk
@@ -89,11 +93,15 @@ def _run_layer(m, xb, logits, w13, w2, topk, rac_k, fmt=0, out_dtype=1):
     return got, experts
 
 
-def _check_site(fmt, xb, got, prefix, rac_k):
+def _check_site(fmt, xb, got, prefix, rac_k, ts=None):
     """One activation site: codes, scales and tensor scale bit-exact, scores
     within the summation bound, the channel set validated; returns the oracle
-    quantization and the (validated) GPU channel set."""
-    q = oracle.nvfp4_quantize(xb) if fmt == 0 else oracle.mxfp4_quantize(xb)
+    quantization and the (validated) GPU channel set.  ``ts``: the supplied
+    tensor scale the site was quantized with (NVFP4)."""
+    if fmt == 0:
+        q = oracle.nvfp4_quantize(xb, tensor_scale=ts)
+    else:
+        q = oracle.mxfp4_quantize(xb)
     assert np.array_equal(got[prefix + "_codes"].reshape(q.codes.shape), q.codes)
     assert np.array_equal(got[prefix + "_scales"].reshape(q.scales.shape), q.scales)
     if fmt == 0:
@@ -143,6 +151,66 @@ def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
     say(f"  W2 out rel err {err_o:.2e}")
     assert err_o <= GEMM_TOL
     check_bf16_output(got["Y"], ref["y"], tol=2 * GEMM_TOL)
+
+
+@pytest.mark.parametrize("T,H,E,F,topk,k", [(600, 512, 4, 512, 2, 32),      # records at both sites
+                                            (520, 1024, 4, 256, 2, 32),     # W2 on 256 x 128 tiles
+                                            (700, 1024, 3, 128, 2, 0)])     # no compensation
+def test_fused_h_quantization(T, H, E, F, topk, k):
+    """A supplied h tensor scale on a prefill-shaped layer: h is quantized in
+    the W13 epilogue.  With s_h equal to the in-call one, h, its codes, scales
+    and selection equal the unfused layer's (scores within the summation
+    bound of each other); with s_h below it (saturated blocks) and above it,
+    codes and scales are bit-exact against the oracle's quantization of the
+    GPU's h under that s_h, scores within the bound, and the W2 product and
+    the layer output against the oracle."""
+    say(f"moe fused h T={T} H={H} E={E} F={F} topk={topk} k={k}")
+    m = q4()
+    rng = np.random.default_rng(T + 7 * H + F)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[:, rng.choice(H, 3, replace=False)] *= 40
+    xb = _bits(x)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    w13 = _bits((rng.standard_normal((E, 2 * F, H)) * 0.05).astype(np.float32))
+    w2 = _bits((rng.standard_normal((E, H, F)) * 0.05).astype(np.float32))
+    experts = m.prepare_moe_weights(dev(w13), dev(w2))
+    base, _ = _run_layer(m, xb, logits, w13, w2, topk, k, experts=experts)
+    s_h = float(base["h_ts"][0])
+    same, _ = _run_layer(m, xb, logits, w13, w2, topk, k, h_ts=s_h, experts=experts)
+    for f in ("h", "h_codes", "h_scales", "h_ts", "x_S"):
+        assert np.array_equal(same[f], base[f]), f
+    check_scores(same["h_scores"], base["h_scores"], T * topk)
+    if k:
+        check_selection(same["h_S"], base["h_scores"], k, T * topk, gpu_scores=same["h_scores"])
+    for mult in (0.37, 3.0):
+        ts = float(np.float32(s_h * mult))
+        got, _ = _run_layer(m, xb, logits, w13, w2, topk, k, h_ts=ts, experts=experts)
+        assert np.array_equal(got["h"], base["h"])
+        _, Sh = _check_site(0, got["h"], got, "h", k, ts=ts)
+        _, Sx = _check_site(0, xb, got, "x", k)
+        ref = oracle.moe_layer(xb, got["idx"], got["p"].astype(np.float64), w13, w2, k,
+                               h_override=got["h"], Sx_override=Sx, Sh_override=Sh,
+                               h_tensor_scale=ts)
+        # a scale below h's amax / 2688 saturates blocks, whose large residuals
+        # make the compensation a large part of the output: its fp16 operands'
+        # rounding (rac_fp16_bound) is then allowed on top of the tolerance
+        bound = np.zeros_like(ref["out"])
+        off = ref["offsets"]
+        for e in range(E):
+            r0, r1 = off[e], off[e + 1]
+            if r1 > r0 and k:
+                Wsel = bf16_to_f64(w2[e])[:, Sh]
+                bound[r0:r1] = rac_fp16_bound(bf16_to_f64(ref["Rh"][r0:r1]), Wsel, ts,
+                                              float(experts["w2"]["tensor_scale"][e]))
+        err_o = check_close(got["out"], ref["out"], GEMM_TOL, extra=bound)
+        say(f"  s_h x {mult}: W2 out rel err {err_o:.2e} "
+            f"(compensation rounding bound up to {float((bound / np.maximum(np.abs(ref['out']), 1e-30)).max()):.1e})")
+        pos = np.empty(T * topk, dtype=np.int64)
+        pos[ref["perm"]] = np.arange(T * topk)
+        yb = np.zeros((T, H))
+        for sl in range(topk):
+            yb += got["p"][:, sl:sl + 1].astype(np.float64) * bound[pos[np.arange(T) * topk + sl]]
+        check_close(bf16_to_f64(got["Y"]), ref["y"], 2 * GEMM_TOL, extra=yb, bf16_ulp=True)
 
 
 def test_scale_records_layout():

@@ -58,3 +58,32 @@ def test_selection_near_tie_accepted_clear_error_rejected():
         check_selection([0, 0], ref, 2, rows=4096)         # duplicate
     with pytest.raises(AssertionError):                    # not the top-k of its own scores
         check_selection([0, 1], ref, 2, rows=4096, gpu_scores=ref)
+
+
+def test_rac_fp16_bound_covers_fp16_operands():
+    """The compensation bound holds for the product formed the GPU's way (the
+    weight divided by s_W f_A and rounded to fp16, the residual times 2^-e_A,
+    then scaled back by s_A s_W), including saturated-block magnitudes and
+    fp16-subnormal weights, and a coarser (bf16) rounding of the weight
+    breaks it."""
+    from tests.parity import RAC_FP16_REL, rac_fp16_bound
+    rng = np.random.default_rng(3)
+    R = (rng.standard_normal((64, 32)) * 50.0).astype(np.float32)
+    R = R.astype(np.float64)
+    W = rng.standard_normal((48, 32)) * 0.02
+    W[:, :4] *= 1e-6                                      # fp16 subnormals in the sum's units
+    W = W.astype(np.float32).astype(np.float64)
+    s_a, s_w = 0.0371, 0.00123
+    f_a, e_a = np.frexp(s_a)
+    exact = R @ W.T
+    Rg = R * 2.0 ** -e_a                                  # exact scaling by a power of two
+    Wg = (W / np.float32(s_w * f_a)).astype(np.float32).astype(np.float16).astype(np.float64)
+    got = (Rg @ Wg.T) * (s_a * s_w)
+    b = rac_fp16_bound(R, W, s_a, s_w)
+    assert (np.abs(got - exact) <= b * (1 + 1e-9) + 1e-300).all()
+    # a bf16 weight (unit roundoff 2^-9) exceeds it somewhere
+    import torch
+    Wb = torch.from_numpy(W / (s_w * f_a)).to(torch.bfloat16).to(torch.float64).numpy()
+    worse = (Rg @ Wb.T) * (s_a * s_w)
+    assert (np.abs(worse - exact) > b).any()
+    assert RAC_FP16_REL > 2.0 ** -11
