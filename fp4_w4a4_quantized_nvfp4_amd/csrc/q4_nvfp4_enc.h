@@ -171,8 +171,10 @@ __device__ __forceinline__ void nvfp4_lane_encode(const uint4* w, const float* x
     s = sc >= 8u ? __uint_as_float((((sc >> 3) + 120u) << 23) | ((sc & 7u) << 20)) : 0.0f;
   }
   const float S = s * st;
-  ok = ok && (S >= 0x1p-60f || S == 0.0f);
-  const float rinv = S > 0.0f ? __builtin_amdgcn_rcpf(S) : 0.0f;
+  // (an all-zero block, m = 0, encodes exactly here whatever its scale: its
+  // codes are the signed zeros x * 0)
+  ok = ok && (S >= 0x1p-60f || S == 0.0f || m == 0.0f);
+  const float rinv = (S > 0.0f && m != 0.0f) ? __builtin_amdgcn_rcpf(S) : 0.0f;
   const float rlo = rinv * (1.0f - 0x1p-20f), rhi = rinv * (1.0f + 0x1p-20f);
   // codes of x * rhi; where the tie mode needs them, also of x * rlo (the
   // two differ only at elements within 2^-20 of a midpoint)

@@ -187,6 +187,22 @@ def test_mxfp4_extremes():
     _compare_nvfp4(_bits(x), 10, mx=True)
 
 
+def test_mxfp4_zero_blocks_wide_layout():
+    """MXFP4 on the 16-channels-per-lane layout with a ragged last strip (768
+    columns: a quarter of the lanes hold no channel) and all-zero 32-blocks,
+    signed zeros and bf16 subnormals in the data: an all-zero block takes the
+    smallest E8M0 scale and signed-zero codes, bit-exact."""
+    rng = np.random.default_rng(22)
+    rows, cols = 65536, 768
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    blk = x.reshape(rows, cols // 32, 32)
+    blk[rng.random((rows, cols // 32)) < 0.05] = 0.0
+    blk[rng.random((rows, cols // 32)) < 0.01] = -0.0
+    tiny = rng.random((rows, cols // 32)) < 0.01
+    blk[tiny] = rng.standard_normal((int(tiny.sum()), 32)).astype(np.float32) * 1e-39
+    _compare_nvfp4(_bits(x), 64, mx=True)
+
+
 def test_deterministic():
     m = q4()
     x = dev(_t3(500, 1024, 31))
