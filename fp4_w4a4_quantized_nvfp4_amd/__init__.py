@@ -71,8 +71,8 @@ _SIGS = {
     "q4_moe_sort": (_I32, [_P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P, _P]),
     "q4_transpose_bf16": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
     "q4_moe_pack_w13": (_I32, [_P, _I32, _I32, _I32, _P, _P]),
-    "q4_scale_records_size": (_SZ, [_I64, _I64, _I64]),
-    "q4_scale_records": (_I32, [_P, _I64, _I64, _I64, _P, _SZ, _P]),
+    "q4_scale_records_size": (_SZ, [_I32, _I64, _I64, _I64]),
+    "q4_scale_records": (_I32, [_I32, _P, _I64, _I64, _I64, _P, _SZ, _P]),
     "moe_workspace_size": (_SZ, [_I32, _I64, _I32, _I32, _I32, _I32, _I32]),
     "moe_workspace_layout": (_I32, [_I32, _I64, _I32, _I32, _I32, _I32, _I32, _P]),
     "moe_w4a4_grouped_gemm": (_I32, [_I32, _P, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P,
@@ -421,38 +421,40 @@ def _quantize_stacked(fmt, w, stream=None):
     return {"fmt": fmt, "codes": codes, "scales": scales, "tensor_scale": ts}
 
 
-def q4_scale_records(scales, K, stream=None):
-    """Tiled fp16 scale records of stacked NVFP4 scales uint8 [batch, rows, K/16]
-    (K % 128 == 0): uint8 [batch, K/128, rows_pad, 16], rows_pad = rows rounded
-    up to 256."""
+def q4_scale_records(scales, K, fmt=NVFP4, stream=None):
+    """Scale records of stacked scales uint8 [batch, rows, K/16] (NVFP4) or
+    [batch, rows, K/32] (MXFP4), K % 128 == 0: uint8 [batch, K/128, rows_pad,
+    16] (fp16 records) or [batch, K/128, rows_pad, 4] (E8M0 bytes), rows_pad =
+    rows rounded up to 256."""
     with _on(stream):
         if scales.dim() != 3:
-            raise ValueError("q4rac: scales must be [batch, rows, K/16]")
+            raise ValueError("q4rac: scales must be [batch, rows, K/16 or K/32]")
         b, rows = scales.shape[0], scales.shape[1]
-        _ptr(scales, torch.uint8, (b, rows, K // 16), "scales")
+        blk, rec = (16, 16) if fmt == NVFP4 else (32, 4)
+        _ptr(scales, torch.uint8, (b, rows, K // blk), "scales")
         L = lib()
-        n = L.q4_scale_records_size(b, rows, K)
+        n = L.q4_scale_records_size(fmt, b, rows, K)
         if n == 0:
             raise Q4Error(f"q4_scale_records: K = {K} is not a positive multiple of 128")
         pad = (rows + 255) // 256 * 256
-        out = _empty((b, K // 128, pad, 16), torch.uint8, scales.device)
-        _check(L.q4_scale_records(_ptr(scales), b, rows, K, _ptr(out), n, _stream(stream)))
+        out = _empty((b, K // 128, pad, rec), torch.uint8, scales.device)
+        _check(L.q4_scale_records(fmt, _ptr(scales), b, rows, K, _ptr(out), n, _stream(stream)))
         return out
 
 
 def prepare_moe_weights(w13, w2, fmt=NVFP4, with_hi=True, stream=None, scale_records=True):
     """Offline expert preparation from logical bf16 w13 [E, 2F, H] and w2 [E, H, F].
-    NVFP4 with H and F multiples of 128: also the weights' tiled fp16 scale
-    records ("scale_records"), which the grouped GEMMs read instead of the raw
-    E4M3 scales (same results)."""
+    With H and F multiples of 128: also the weights' scale records
+    ("scale_records"), which the grouped GEMMs read instead of the raw scales
+    (same results)."""
     w13p = q4_moe_pack_w13(w13, stream)
     out = {"fmt": fmt, "w13": _quantize_stacked(fmt, w13p, stream),
            "w2": _quantize_stacked(fmt, _bf16(w2), stream),
            "E": w13.shape[0], "F": w13.shape[1] // 2, "H": w13.shape[2]}
     H, F = out["H"], out["F"]
-    if scale_records and fmt == NVFP4 and H % 128 == 0 and F % 128 == 0:
-        out["w13"]["scale_records"] = q4_scale_records(out["w13"]["scales"], H, stream)
-        out["w2"]["scale_records"] = q4_scale_records(out["w2"]["scales"], F, stream)
+    if scale_records and H % 128 == 0 and F % 128 == 0:
+        out["w13"]["scale_records"] = q4_scale_records(out["w13"]["scales"], H, fmt, stream)
+        out["w2"]["scale_records"] = q4_scale_records(out["w2"]["scales"], F, fmt, stream)
     if with_hi:
         out["w13_hi_t"] = q4_transpose_bf16(w13p, stream)
         out["w2_hi_t"] = q4_transpose_bf16(_bf16(w2), stream)
@@ -493,12 +495,13 @@ def moe_w4a4_grouped_gemm(tokens, topk_idx, topk_w, experts, rac_k, out_dtype=OU
             _ptr(w13["tensor_scale"], torch.float32, (E,), "w13 tensor_scale")
             _ptr(w2["tensor_scale"], torch.float32, (E,), "w2 tensor_scale")
         rec13 = rec2 = None
+        rsz = 16 if fmt == NVFP4 else 4
         if w13.get("scale_records") is not None:
             rec13 = _ptr(w13["scale_records"], torch.uint8,
-                         (E, H // 128, (2 * F + 255) // 256 * 256, 16), "w13 scale_records")
+                         (E, H // 128, (2 * F + 255) // 256 * 256, rsz), "w13 scale_records")
         if w2.get("scale_records") is not None:
             rec2 = _ptr(w2["scale_records"], torch.uint8,
-                        (E, F // 128, (H + 255) // 256 * 256, 16), "w2 scale_records")
+                        (E, F // 128, (H + 255) // 256 * 256, rsz), "w2 scale_records")
         L = lib()
         wsb = L.moe_workspace_size(fmt, T, E, H, F, topk, rac_k)
         if workspace is None or workspace.numel() < wsb:

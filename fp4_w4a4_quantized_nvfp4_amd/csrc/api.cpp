@@ -593,22 +593,28 @@ q4_status_t q4_moe_pack_w13(const uint16_t* w13, int32_t E, int32_t F, int32_t H
   return hip_status(launch_moe_pack_w13(w13, E, F, H, out, S(stream)), "q4_moe_pack_w13");
 }
 
-size_t q4_scale_records_size(int64_t batch, int64_t rows, int64_t K) {
-  if (batch < 0 || rows < 0 || K <= 0 || K % 128 || rows >= kMaxDim || K >= kMaxDim) return 0;
-  return (size_t)batch * (size_t)(K / 128) * (size_t)tile_rows_pad(rows) * 16;
+size_t q4_scale_records_size(int32_t fmt, int64_t batch, int64_t rows, int64_t K) {
+  if ((fmt != Q4_NVFP4 && fmt != Q4_MXFP4) || batch < 0 || rows < 0 || K <= 0 || K % 128 ||
+      rows >= kMaxDim || K >= kMaxDim)
+    return 0;
+  return (size_t)batch * (size_t)(K / 128) * (size_t)tile_rows_pad(rows) * (fmt == Q4_MXFP4 ? 4 : 16);
 }
 
-q4_status_t q4_scale_records(const uint8_t* scales, int64_t batch, int64_t rows, int64_t K,
-                             uint8_t* out, size_t out_bytes, void* stream) {
+q4_status_t q4_scale_records(int32_t fmt, const uint8_t* scales, int64_t batch, int64_t rows,
+                             int64_t K, uint8_t* out, size_t out_bytes, void* stream) {
   const char* fn = "q4_scale_records";
+  if (fmt != Q4_NVFP4 && fmt != Q4_MXFP4) return fail(Q4_EINVAL, "%s: bad format %d", fn, fmt);
   if (batch < 0 || batch >= 65536 || rows < 0 || rows >= kMaxDim || K <= 0 || K >= kMaxDim)
     return fail(Q4_ESHAPE, "%s: bad shape", fn);
   if (K % 128) return fail(Q4_ESHAPE, "%s: need K %% 128 == 0 (got %lld)", fn, (long long)K);
-  const size_t need = q4_scale_records_size(batch, rows, K);
+  const size_t need = q4_scale_records_size(fmt, batch, rows, K);
   if (need == 0) return Q4_OK;
   Q4_REQUIRE_PTR(out);
   if (out_bytes < need) return fail(Q4_EWORKSPACE, "%s: %zu bytes needed (got %zu)", fn, need, out_bytes);
   if (rows > 0) Q4_REQUIRE_PTR(scales);
+  if (fmt == Q4_MXFP4)
+    return hip_status(launch_mx_scale_records(scales, batch, rows, (int32_t)K, tile_rows_pad(rows),
+                                              out, S(stream)), fn);
   return hip_status(launch_scale_tile_batched(scales, batch, rows, (int32_t)K, tile_rows_pad(rows),
                                               out, S(stream)), fn);
 }
@@ -728,8 +734,6 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   } else if (w13_tensor_scales || w2_tensor_scales) {
     return fail(Q4_EINVAL, "%s: MXFP4 weights take no tensor scales", fn);
   }
-  if (mx && (w13_scale_records || w2_scale_records))
-    return fail(Q4_EINVAL, "%s: scale records are an NVFP4 layout", fn);
   if (w13_scale_records) Q4_REQUIRE_PTR(w13_scale_records);
   if (w2_scale_records) Q4_REQUIRE_PTR(w2_scale_records);
   if (h_tensor_scale) {
@@ -835,6 +839,10 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
     g.w_scales_t = w13_scale_records;
     g.a_rows_pad = L.rows_pad;
     g.w_rows_pad = tile_rows_pad(2 * (int64_t)F);
+  } else if (skinny && w13_scale_records && H % 128 == 0) {
+    // decode-shaped: the skinny kernel streams the weights' fp16 scale records
+    g.w_scales_t = w13_scale_records;
+    g.w_rows_pad = tile_rows_pad(2 * (int64_t)F);
   }
   // ---- activation site 2: h (sorted rows)
   uint8_t* hc = (uint8_t*)P(L.off[8]);
@@ -900,6 +908,9 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
     g2.a_scales_t = (const uint8_t*)P(L.h_rec);
     g2.w_scales_t = w2_scale_records;
     g2.a_rows_pad = L.rows_pad;
+    g2.w_rows_pad = tile_rows_pad(H);
+  } else if (skinny && w2_scale_records && F % 128 == 0) {
+    g2.w_scales_t = w2_scale_records;
     g2.w_rows_pad = tile_rows_pad(H);
   }
   Q4_TRY(grouped_gemm(g2), "moe w2 gemm");

@@ -1470,6 +1470,34 @@ hipError_t launch_scale_tile_batched(const uint8_t* scales, int64_t batch, int64
   return hipGetLastError();
 }
 
+// MXFP4 scale records: the four E8M0 bytes of one row and 128-column chunk,
+// chunk-major, so that a tile's rows of one chunk are contiguous
+__global__ __launch_bounds__(256) void mx_scale_records_kernel(const uint8_t* __restrict__ sc,
+                                                               int64_t rows, int32_t K,
+                                                               int64_t rows_pad,
+                                                               uint32_t* __restrict__ out) {
+  const int64_t b = blockIdx.y;
+  const int64_t total = (int64_t)(K / 128) * rows_pad;
+  const uint8_t* src = sc + b * rows * (K / 32);
+  uint32_t* dst = out + b * total;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t c = i / rows_pad, r = i - c * rows_pad;
+    dst[i] = r < rows ? *(const uint32_t*)(src + r * (K / 32) + 4 * c) : 0u;
+  }
+}
+
+hipError_t launch_mx_scale_records(const uint8_t* scales, int64_t batch, int64_t rows, int32_t K,
+                                   int64_t rows_pad, uint8_t* out, hipStream_t stream) {
+  const int64_t total = (int64_t)(K / 128) * rows_pad;
+  if (total == 0 || batch == 0) return hipSuccess;
+  int64_t grid = (total + 255) / 256;
+  grid = grid > 1024 ? 1024 : grid;
+  hipLaunchKernelGGL(mx_scale_records_kernel, dim3((unsigned)grid, (unsigned)batch), dim3(256), 0,
+                     stream, scales, rows, K, rows_pad, (uint32_t*)out);
+  return hipGetLastError();
+}
+
 // Records of the R token-sorted rows of a grouped GEMM's A operand: record
 // (c, r) holds the scales of source row a_rows[r] (r itself without a_rows),
 // swizzled for the row's offset within its expert (the expert being the last

@@ -116,6 +116,10 @@ inline int64_t tile_rows_pad(int64_t rows) { return (rows + 255) / 256 * 256; }
 // records of `batch` operands [rows][K / 16]: [batch][K / 128][rows_pad][16 B]
 hipError_t launch_scale_tile_batched(const uint8_t* scales, int64_t batch, int64_t rows, int32_t K,
                                      int64_t rows_pad, uint8_t* out, hipStream_t stream);
+// MXFP4 scale records of `batch` operands [rows][K / 32]: [batch][K / 128][rows_pad][4 B],
+// record (c, r) = the E8M0 bytes of blocks 4c .. 4c + 3 of row r (rows past `rows` zero)
+hipError_t launch_mx_scale_records(const uint8_t* scales, int64_t batch, int64_t rows, int32_t K,
+                                   int64_t rows_pad, uint8_t* out, hipStream_t stream);
 // records of the R token-sorted rows of a grouped A operand (source row
 // a_rows[r], or r without a_rows; expert ranges `offsets` [E + 1]):
 // [K / 128][rows_pad][16 B], each swizzled for its row's offset in its expert

@@ -252,21 +252,28 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// The same tiles with the operands staged through LDS: each wave fills its
-// own four-stage LDS ring straight from global memory (global_load_lds, four
-// lanes per 64-byte row chunk, so every load is fully coalesced) three chunks
-// ahead, and reads its MFMA fragments back from LDS.  No barriers: a wave
-// only reads what it loaded itself.  Needs K % 64 == 0 (NVFP4) or
+// The same tiles with the operands staged through LDS, three stages filled
+// straight from global memory (global_load_lds, four lanes per 64-byte row
+// chunk, so every load is fully coalesced) two chunks ahead.  Each wave fills
+// its own weight region of a stage (its 64 W rows); the tile's activation
+// rows are shared: waves 0 and 1 load the 32 code rows, waves 2 and 3 the
+// scales, and one barrier per chunk makes them visible to every wave.  A
+// stage is 20.3 KB, so two workgroups fit in a CU's LDS and two waves share
+// each SIMD, hiding each other's memory waits.  Needs K % 64 == 0 (NVFP4) or
 // K % 128 == 0 (MXFP4: 4-byte scale rows per chunk).
 typedef const void __attribute__((address_space(1)))* sk_gptr_t;
 typedef void __attribute__((address_space(3)))* sk_lptr_t;
 
-constexpr int SW_CODE = 0;        // 64 W rows x 64 B
-constexpr int SA_CODE = 4096;     // 32 A rows x 64 B
-constexpr int SW_SC = 6144;       // W scales: 64 x 8 B (NVFP4) or 64 x 4 B (MXFP4)
-constexpr int SA_SC = 6656;       // A scales: 32 x 8 B (NVFP4) or 32 x 4 B (+ copies)
-constexpr int SREGION = 6912;     // bytes per wave per stage
-constexpr int SSTAGE = 4 * SREGION;
+// Stage layout: per wave, 64 W rows x 64 B of codes, then their scales: raw
+// (64 x 8 B E4M3, or 64 x 4 B E8M0) or, with WREC, the weights' tiled fp16
+// scale records (64 x 16 B); then the shared activation rows (32 x 64 B) and
+// their raw scales (32 x 8 B, or 32 x 4 B and copies).
+constexpr int SW_CODE = 0;
+constexpr int SW_SC = 4096;
+template <bool WREC> constexpr int SWREGION = WREC ? 5120 : 4608;   // bytes per wave per stage
+template <bool WREC> constexpr int SA_CODE = 4 * SWREGION<WREC>;
+template <bool WREC> constexpr int SA_SC = SA_CODE<WREC> + 2048;
+template <bool WREC> constexpr int SSTAGE = SA_SC<WREC> + 256;      // 20736 or 22784 bytes
 
 __device__ __forceinline__ int sk_swz(int row, int piece) {
   return row * 64 + ((piece ^ ((row >> 1) ^ (row >> 2)) & 3) << 4);
@@ -274,13 +281,20 @@ __device__ __forceinline__ int sk_swz(int row, int piece) {
 
 constexpr int sk_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <bool MX, int EPI>
-__global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
-  constexpr int DMA = MX ? 8 : 9;   // global -> LDS loads per wave per chunk
-  __shared__ __attribute__((aligned(16))) uint8_t st0[SSTAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t st1[SSTAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[SSTAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t st3[SSTAGE];
+// WREC (K % 128 == 0): the weight scales come from their records
+// (g.w_scales_t, [E][K / 128][w_rows_pad][record]): NVFP4 the tiled fp16
+// records (16 B, swizzled by row, already widened to fp16), MXFP4 the four
+// E8M0 bytes of the chunk (4 B); a wave's 64 rows of one chunk are one
+// contiguous, coalesced load.
+template <bool MX, int EPI, bool WREC = false>
+__global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs g) {
+  constexpr int DMA = MX ? 6 : (WREC ? 6 : 7);   // global -> LDS loads per wave per chunk
+  constexpr bool FP16REC = WREC && !MX;           // fp16 records in a 1 KB region
+  constexpr int SWR = SWREGION<FP16REC>, SAC = SA_CODE<FP16REC>, SAS = SA_SC<FP16REC>;
+  constexpr int REC_SHIFT = MX ? 2 : 4;           // log2 of the record size
+  __shared__ __attribute__((aligned(16))) uint8_t st0[SSTAGE<FP16REC>];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[SSTAGE<FP16REC>];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[SSTAGE<FP16REC>];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, h = lane >> 5;
@@ -289,54 +303,55 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
   const int nk = (K + CK - 1) / CK;
   const int nbn = (int)((N + SN - 1) / SN);
   const int mt = blockIdx.x / nbn, nt = blockIdx.x % nbn;
-  if (mt >= g.ntiles_dev[0]) return;
+  if (mt >= g.ntiles_dev[0]) return;        // uniform over the workgroup
   const int4 t = ((const int4*)g.tiles)[mt];
   const int e = t.x;
   const int64_t m0 = t.y, m_end = t.z;
+  // (a wave whose columns are all past N still runs: it loads its share of
+  // the activations and takes part in the barriers, and stores nothing)
   const int64_t c0 = (int64_t)nt * SN + wave * 64;
-  if (c0 >= N) return;                      // no barriers: waves are independent
-  const int reg = wave * SREGION;
+  const int reg = wave * SWR;
 
   const int64_t cstride = K / 2, sstride = MX ? K / 32 : K / 16;
   const uint8_t* const wcb = g.w_codes + (int64_t)e * N * cstride;
   const uint8_t* const wsb = g.w_scales + (int64_t)e * N * sstride;
-  // rows past the tile read a valid row again (their results are never stored)
+  // rows past the tile (or past N) read a valid row again (their results are
+  // never stored)
   auto wrow = [&](int r) -> int64_t { return min(c0 + r, N - 1); };
   auto arow_of = [&](int r) -> int64_t {
     const int64_t rr = min(m0 + r, m_end - 1);
     return g.a_rows ? (int64_t)g.a_rows[rr] : rr;
   };
-  // per-lane global offsets of this wave's loads (row and swizzled piece)
-  uint32_t wco[4], aco[2];
-  int wpiece[4], apiece[2];
+  // per-lane global offsets of this wave's weight loads (row and swizzled piece)
+  uint32_t wco[4];
+  int wpiece[4];
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int row = 16 * it + (lane >> 2);
     wpiece[it] = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
     wco[it] = (uint32_t)(wrow(row) * cstride);
   }
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int row = 16 * it + (lane >> 2);
-    apiece[it] = (lane & 3) ^ (((row >> 1) ^ (row >> 2)) & 3);
-    aco[it] = (uint32_t)0;
-  }
-  const uint8_t* abase[2];
-#pragma unroll
-  for (int it = 0; it < 2; ++it) abase[it] = g.a_codes + arow_of(16 * it + (lane >> 2)) * cstride;
-  // scale loads
   const uint8_t* wsrc[2];
-  const uint8_t* asrc;
+  // WREC: this wave's 64 records of chunk 0 (rows c0 .. c0 + 63 exist in the
+  // padded record block even past N)
+  const uint8_t* wrec = nullptr;
+  if constexpr (WREC)
+    wrec = g.w_scales_t + (((int64_t)e * nk * g.w_rows_pad + c0 + lane) << REC_SHIFT);
   if constexpr (MX) {
     wsrc[0] = wsb + wrow(lane) * sstride;
     wsrc[1] = wsrc[0];
-    asrc = g.a_scales + arow_of(lane & 31) * sstride;
   } else {
 #pragma unroll
     for (int it = 0; it < 2; ++it) wsrc[it] = wsb + wrow(32 * it + (lane >> 1)) * sstride + 4 * (lane & 1);
-    asrc = g.a_scales + arow_of(lane >> 1) * sstride + 4 * (lane & 1);
   }
-  (void)aco;
+  // this wave's share of the activation loads: waves 0 and 1 the code rows
+  // 16 w .. 16 w + 15, waves 2 and 3 the scale records (the same bytes)
+  const int arow = 16 * (wave & 1) + (lane >> 2);
+  const int apiece = (lane & 3) ^ (((arow >> 1) ^ (arow >> 2)) & 3);
+  const uint8_t* const acsrc = g.a_codes + arow_of(arow) * cstride;
+  const uint8_t* asrc;
+  if constexpr (MX) asrc = g.a_scales + arow_of(lane & 31) * sstride;
+  else asrc = g.a_scales + arow_of(lane >> 1) * sstride + 4 * (lane & 1);
 
   // chunk c (clamped: past the end, the last chunk again into a stage nobody reads)
   auto issue = [&](int c, uint8_t* const sb) {
@@ -350,17 +365,17 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
       __builtin_amdgcn_global_load_lds((sk_gptr_t)(wcb + wco[it] + k0 / 2 + 16 * pc),
                                        (sk_lptr_t)(base + SW_CODE + it * 1024), 16, 0, 0);
     }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int pc = (k0 + 32 * apiece[it] < K) ? apiece[it] : (apiece[it] & 1);
-      __builtin_amdgcn_global_load_lds((sk_gptr_t)(abase[it] + k0 / 2 + 16 * pc),
-                                       (sk_lptr_t)(base + SA_CODE + it * 1024), 16, 0, 0);
-    }
-    if constexpr (MX) {
+    if constexpr (WREC && MX) {
+      __builtin_amdgcn_global_load_lds(
+          (sk_gptr_t)(wrec + ((int64_t)cc * g.w_rows_pad << REC_SHIFT)), (sk_lptr_t)(base + SW_SC),
+          4, 0, 0);
+    } else if constexpr (WREC) {
+      __builtin_amdgcn_global_load_lds(
+          (sk_gptr_t)(wrec + ((int64_t)cc * g.w_rows_pad << REC_SHIFT)), (sk_lptr_t)(base + SW_SC),
+          16, 0, 0);
+    } else if constexpr (MX) {
       __builtin_amdgcn_global_load_lds((sk_gptr_t)(wsrc[0] + k0 / 32),
                                        (sk_lptr_t)(base + SW_SC), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((sk_gptr_t)(asrc + k0 / 32),
-                                       (sk_lptr_t)(base + SA_SC), 4, 0, 0);
     } else {
       // second dword (blocks 4..7) past K reads the first again
       const int dw = (k0 + 64 < K) ? 1 : 0;
@@ -369,9 +384,19 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
         __builtin_amdgcn_global_load_lds(
             (sk_gptr_t)(wsrc[it] + k0 / 16 - 4 * (lane & 1) + 4 * ((lane & 1) & dw)),
             (sk_lptr_t)(base + SW_SC + it * 256), 4, 0, 0);
+    }
+    if (wave < 2) {
+      const int pc = (k0 + 32 * apiece < K) ? apiece : (apiece & 1);
+      __builtin_amdgcn_global_load_lds((sk_gptr_t)(acsrc + k0 / 2 + 16 * pc),
+                                       (sk_lptr_t)(sb + SAC + (wave & 1) * 1024), 16, 0, 0);
+    } else if constexpr (MX) {
+      __builtin_amdgcn_global_load_lds((sk_gptr_t)(asrc + k0 / 32), (sk_lptr_t)(sb + SAS), 4, 0,
+                                       0);
+    } else {
+      const int dw = (k0 + 64 < K) ? 1 : 0;
       __builtin_amdgcn_global_load_lds(
           (sk_gptr_t)(asrc + k0 / 16 - 4 * (lane & 1) + 4 * ((lane & 1) & dw)),
-          (sk_lptr_t)(base + SA_SC), 4, 0, 0);
+          (sk_lptr_t)(sb + SAS), 4, 0, 0);
     }
   };
 
@@ -381,6 +406,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[ni][q] = 0.0f;
 
+  // (WREC: wb[ni][s] = the fp16 scale pair of blocks 4h + 2s, 4h + 2s + 1 of
+  // W row ni)
+  uint32_t wb[2][2] = {{0u, 0u}, {0u, 0u}};
   auto compute = [&](const SkinnyChunk& c) {
     if constexpr (MX) {
 #pragma unroll
@@ -403,8 +431,16 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const half8v af = decode8_s(word_s(c.a[s], j), e4m3_dup_f16_s(pa, j >= 2));
-          const half8v b0 = decode8_s(word_s(c.b[0][s], j), e4m3_dup_f16_s(pb0, j >= 2));
-          const half8v b1 = decode8_s(word_s(c.b[1][s], j), e4m3_dup_f16_s(pb1, j >= 2));
+          uint32_t d0, d1;
+          if constexpr (FP16REC) {   // fp16 pair: the block's half in both halves
+            d0 = __builtin_amdgcn_perm(wb[0][s], wb[0][s], j >= 2 ? 0x03020302u : 0x01000100u);
+            d1 = __builtin_amdgcn_perm(wb[1][s], wb[1][s], j >= 2 ? 0x03020302u : 0x01000100u);
+          } else {
+            d0 = e4m3_dup_f16_s(pb0, j >= 2);
+            d1 = e4m3_dup_f16_s(pb1, j >= 2);
+          }
+          const half8v b0 = decode8_s(word_s(c.b[0][s], j), d0);
+          const half8v b1 = decode8_s(word_s(c.b[1][s], j), d1);
           acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b0, acc[0], 0, 0, 0);
           acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, b1, acc[1], 0, 0, 0);
         }
@@ -412,28 +448,38 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
     }
   };
 
-  // one chunk from stage sb: fragments, then the loads of chunk c + 3 into
-  // stage nx (read in the previous chunk), then the MFMAs
+  // one chunk from stage sb: its loads (every wave's) have landed after the
+  // wait and the barrier; fragments, then the loads of chunk c + 2 into stage
+  // nx (last read in the previous chunk, which every wave has finished: it
+  // passed the barrier), then the MFMAs
   auto step = [&](int c, const uint8_t* const sb, uint8_t* const nx) {
+    __builtin_amdgcn_s_waitcnt(sk_vmcnt(DMA));
+    __builtin_amdgcn_s_barrier();
     const uint8_t* const base = sb + reg;
     const int k0 = c * CK;
     SkinnyChunk f;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int piece = MX ? 2 * s + h : 2 * h + s;
-      const bool kin = k0 + 32 * piece < K;
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      const uint4 a = *(const uint4*)(base + SA_CODE + sk_swz(l32, piece));
+      const uint4 a = *(const uint4*)(sb + SAC + sk_swz(l32, piece));
       const uint4 b0 = *(const uint4*)(base + SW_CODE + sk_swz(l32, piece));
       const uint4 b1 = *(const uint4*)(base + SW_CODE + sk_swz(32 + l32, piece));
-      f.a[s] = kin ? a : z;
-      f.b[0][s] = kin ? b0 : z;
-      f.b[1][s] = kin ? b1 : z;
+      if constexpr (WREC) {   // K % 128 == 0: every piece is inside K
+        f.a[s] = a;
+        f.b[0][s] = b0;
+        f.b[1][s] = b1;
+      } else {
+        const bool kin = k0 + 32 * piece < K;
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        f.a[s] = kin ? a : z;
+        f.b[0][s] = kin ? b0 : z;
+        f.b[1][s] = kin ? b1 : z;
+      }
     }
     if constexpr (MX) {
       // E8M0 of blocks 2s + h: bytes of the row's 4-byte record; 127 (= 1.0)
       // where the block is past K
-      const uint32_t ra = *(const uint32_t*)(base + SA_SC + l32 * 4);
+      const uint32_t ra = *(const uint32_t*)(sb + SAS + l32 * 4);
       const uint32_t rb0 = *(const uint32_t*)(base + SW_SC + l32 * 4);
       const uint32_t rb1 = *(const uint32_t*)(base + SW_SC + (32 + l32) * 4);
       uint32_t sa = 0, sb0 = 0, sb1 = 0;
@@ -448,36 +494,40 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
       f.sa = sa;
       f.sb[0] = sb0;
       f.sb[1] = sb1;
+    } else if constexpr (FP16REC) {
+      f.sa = *(const uint32_t*)(sb + SAS + l32 * 8 + 4 * h);
+      // record dword d (blocks 2d, 2d + 1) of row r sits at d ^ ((r / 8) % 4);
+      // rows l and 32 + l share that swizzle
+      const int q = (l32 >> 3) & 3;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int slot = (2 * h + s) ^ q;
+        wb[0][s] = *(const uint32_t*)(base + SW_SC + l32 * 16 + slot * 4);
+        wb[1][s] = *(const uint32_t*)(base + SW_SC + (32 + l32) * 16 + slot * 4);
+      }
     } else {
-      f.sa = *(const uint32_t*)(base + SA_SC + l32 * 8 + 4 * h);
+      f.sa = *(const uint32_t*)(sb + SAS + l32 * 8 + 4 * h);
       f.sb[0] = *(const uint32_t*)(base + SW_SC + l32 * 8 + 4 * h);
       f.sb[1] = *(const uint32_t*)(base + SW_SC + (32 + l32) * 8 + 4 * h);
     }
-    issue(c + 3, nx);
+    issue(c + 2, nx);
     compute(f);
   };
   issue(0, st0);
   issue(1, st1);
-  issue(2, st2);
   int kc = 0;
-  for (; kc < nk; kc += 4) {
-    __builtin_amdgcn_s_waitcnt(sk_vmcnt(2 * DMA));
-    step(kc, st0, st3);
+  for (; kc < nk; kc += 3) {
+    step(kc, st0, st2);
     if (kc + 1 >= nk) break;
-    __builtin_amdgcn_s_waitcnt(sk_vmcnt(2 * DMA));
     step(kc + 1, st1, st0);
     if (kc + 2 >= nk) break;
-    __builtin_amdgcn_s_waitcnt(sk_vmcnt(2 * DMA));
     step(kc + 2, st2, st1);
-    if (kc + 3 >= nk) break;
-    __builtin_amdgcn_s_waitcnt(sk_vmcnt(2 * DMA));
-    step(kc + 3, st3, st2);
   }
   __builtin_amdgcn_s_waitcnt(sk_vmcnt(0));
 
   const int64_t r = m0 + l32;
   const bool rok = r < m_end;
-  const int64_t arow = rok ? (g.a_rows ? (int64_t)g.a_rows[r] : r) : 0;
+  const int64_t ar = rok ? (g.a_rows ? (int64_t)g.a_rows[r] : r) : 0;
   bool cok[2];
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) cok[ni] = c0 + ni * 32 + l32 < N;
@@ -495,20 +545,20 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
       for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
   }
 
-  // residual compensation: bf16 R rows of the tile x bf16 selected W columns
+  // residual compensation: R rows of the tile x selected W columns
   if (g.kp > 0 && g.r_res) {
-    const uint16_t* rrow = g.r_res + arow * g.ld_r + 8 * h;
-    const uint16_t* wrow[2];
+    const uint16_t* rrow = g.r_res + ar * g.ld_r + 8 * h;
+    const uint16_t* wrw[2];
 #pragma unroll
     for (int ni = 0; ni < 2; ++ni) {
       const int64_t col = c0 + ni * 32 + l32;
-      wrow[ni] = g.w_sel + ((int64_t)e * N + (cok[ni] ? col : 0)) * g.kp + 8 * h;
+      wrw[ni] = g.w_sel + ((int64_t)e * N + (cok[ni] ? col : 0)) * g.kp + 8 * h;
     }
     for (int kt = 0; kt < g.kp; kt += 16) {
       const uint4 av = rok ? *(const uint4*)(rrow + kt) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int ni = 0; ni < 2; ++ni) {
-        const uint4 bv = cok[ni] ? *(const uint4*)(wrow[ni] + kt) : make_uint4(0, 0, 0, 0);
+        const uint4 bv = cok[ni] ? *(const uint4*)(wrw[ni] + kt) : make_uint4(0, 0, 0, 0);
         if constexpr (MX)
           acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, av),
                                                            __builtin_bit_cast(bf16x8v, bv),
@@ -528,6 +578,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_lds_kernel(GemmArgs g) {
   }
 
   // accumulator element q of lane l: row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32
+  if (c0 >= N) return;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int64_t row = m0 + 8 * (q >> 2) + 4 * h + (q & 3);
@@ -558,6 +609,20 @@ hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t 
   const int64_t nb = max_tiles * nbn;
   if (nb == 0) return hipSuccess;
   const dim3 grid((unsigned)nb), block(256);
+  if (g.w_scales_t && g.K % 128 == 0) {
+    if (g.mx) {
+      if (g.epilogue == kEpiSwiGLU)
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<true, kEpiSwiGLU, true>), grid, block, 0, stream, g);
+      else
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<true, kEpiStore, true>), grid, block, 0, stream, g);
+    } else {
+      if (g.epilogue == kEpiSwiGLU)
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<false, kEpiSwiGLU, true>), grid, block, 0, stream, g);
+      else
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<false, kEpiStore, true>), grid, block, 0, stream, g);
+    }
+    return hipGetLastError();
+  }
   if (g.mx ? g.K % 128 == 0 : g.K % 64 == 0) {
     if (g.mx) {
       if (g.epilogue == kEpiSwiGLU)

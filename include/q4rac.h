@@ -292,19 +292,22 @@ q4_status_t q4_transpose_bf16(const uint16_t *in, int64_t batch, int64_t rows, i
 q4_status_t q4_moe_pack_w13(const uint16_t *w13, int32_t E, int32_t F, int32_t H,
                             uint16_t *out, void *stream);
 
-/* Scale records of stacked NVFP4 weights (offline): the E4M3 block scales
- * (one per 16 elements, QUADS section 2.2 "FP4" and the NVFP4 format pages)
- * of `batch` operands [rows][K/16], widened to fp16 (exact, subnormal scales
- * included) and laid out as [batch][K/128][rows_pad][16 B], rows_pad = rows
- * rounded up to 256 (rows past `rows` zero): one record holds the eight
- * scales of one row over one 128-column chunk, its four dwords in an order
- * that spreads a tile's LDS reads over the banks.  Derived data only: a
- * grouped GEMM given the records computes exactly what it computes from the
- * raw scales.  K % 128 == 0 (Q4_ESHAPE otherwise); out must hold
- * q4_scale_records_size bytes (Q4_EWORKSPACE); out is caller-owned. */
-size_t q4_scale_records_size(int64_t batch, int64_t rows, int64_t K);
-q4_status_t q4_scale_records(const uint8_t *scales, int64_t batch, int64_t rows, int64_t K,
-                             uint8_t *out, size_t out_bytes, void *stream);
+/* Scale records of stacked weights (offline), laid out per 128-column chunk
+ * as [batch][K/128][rows_pad][record], rows_pad = rows rounded up to 256
+ * (rows past `rows` zero), so that a tile's rows of one chunk are contiguous.
+ *   fmt Q4_NVFP4: the E4M3 block scales (one per 16 elements, QUADS section
+ *     2.2 "FP4" and the NVFP4 format pages) of operands [rows][K/16], widened
+ *     to fp16 (exact, subnormal scales included): a 16-byte record holds the
+ *     eight scales of one row and chunk, its four dwords in an order that
+ *     spreads a tile's LDS reads over the banks.
+ *   fmt Q4_MXFP4: the E8M0 scales (one per 32 elements) of operands
+ *     [rows][K/32]: a 4-byte record holds the four of one row and chunk.
+ * Derived data only: a grouped GEMM given the records computes exactly what
+ * it computes from the raw scales.  K % 128 == 0 (Q4_ESHAPE otherwise); out
+ * must hold q4_scale_records_size bytes (Q4_EWORKSPACE); out is caller-owned. */
+size_t q4_scale_records_size(int32_t fmt, int64_t batch, int64_t rows, int64_t K);
+q4_status_t q4_scale_records(int32_t fmt, const uint8_t *scales, int64_t batch, int64_t rows,
+                             int64_t K, uint8_t *out, size_t out_bytes, void *stream);
 
 /* Token-sorted grouped W4A4 + RAC SwiGLU expert layer: the compensation of
  * QUADS section 3.3 (Eq. 21-24) at both activation sites of the expert block,
@@ -317,12 +320,13 @@ q4_status_t q4_scale_records(const uint8_t *scales, int64_t batch, int64_t rows,
  *   w13_hi_t   bf16 [E][H][2F]: per-expert transpose of the packed bf16 W13.
  *   w2_hi_t    bf16 [E][F][H]:  per-expert transpose of the bf16 W2.
  *              Both may be NULL when rac_k == 0.
- *   w13_scale_records, w2_scale_records: NULL, or (NVFP4 only) the
- *              q4_scale_records of w13_scales (batch E, rows 2F, K = H) and of
- *              w2_scales (batch E, rows H, K = F), which must be those scales'
- *              records (not checked).  Where the shape allows (prefill-sized
- *              T * topk, H and F multiples of 128 and at least 512) the
- *              grouped GEMMs then read fp16 scales; results are the same.
+ *   w13_scale_records, w2_scale_records: NULL, or the q4_scale_records (in
+ *              the layer's format) of w13_scales (batch E, rows 2F, K = H) and
+ *              of w2_scales (batch E, rows H, K = F), which must be those
+ *              scales' records (not checked).  Where the shape allows (H and F
+ *              multiples of 128; prefill-sized T * topk also needs them at
+ *              least 512) the grouped GEMMs then read fp16 scales; results
+ *              are the same.
  *   h_tensor_scale: NULL, or (NVFP4 only) device fp32 [1]: h's tensor scale
  *              supplied by the caller (delayed scaling, e.g. an earlier step's
  *              s_h) instead of RN32(amax(h) / 2688).  Where the W13 GEMM runs

@@ -88,20 +88,17 @@ def test_shape_and_pointer_errors(L):
     assert L.moe_w4a4_grouped_gemm(0, fake, 4, 64, fake, fake, 2, 4, 48, fake, fake, fake, fake,
                                    fake, fake, fake, fake, None, None, None, 0, fake, 1, fake,
                                    1 << 30, None, None) == 2
-    # MoE: scale records are NVFP4 only
-    assert L.moe_w4a4_grouped_gemm(1, fake, 4, 64, fake, fake, 2, 4, 64, fake, fake, None, fake,
-                                   fake, None, fake, fake, fake, None, None, 0, fake, 1, fake,
-                                   1 << 30, None, None) == 1
-    assert "NVFP4" in _err(L)
     # MoE: a supplied h tensor scale is NVFP4 only
     assert L.moe_w4a4_grouped_gemm(1, fake, 4, 64, fake, fake, 2, 4, 64, fake, fake, None, fake,
                                    fake, None, fake, fake, None, None, fake, 0, fake, 1, fake,
                                    1 << 30, None, None) == 1
     assert "tensor scale" in _err(L)
-    # scale records: K % 128, short output
-    assert L.q4_scale_records(fake, 2, 64, 96, fake, 1 << 20, None) == 2
-    assert L.q4_scale_records(fake, 2, 64, 256, fake, 100, None) == 4
-    assert L.q4_scale_records_size(2, 300, 256) == 2 * 2 * 512 * 16
+    # scale records: K % 128, short output, format
+    assert L.q4_scale_records(0, fake, 2, 64, 96, fake, 1 << 20, None) == 2
+    assert L.q4_scale_records(0, fake, 2, 64, 256, fake, 100, None) == 4
+    assert L.q4_scale_records(2, fake, 2, 64, 256, fake, 1 << 20, None) == 1
+    assert L.q4_scale_records_size(0, 2, 300, 256) == 2 * 2 * 512 * 16
+    assert L.q4_scale_records_size(1, 2, 300, 256) == 2 * 2 * 512 * 4
     # sort: topk > 16, misaligned status
     assert L.q4_moe_sort(fake, 4, 32, 17, fake, fake, fake, 1 << 20, None, None) == 1
     assert L.q4_moe_sort(fake, 4, 32, 2, fake, fake, fake, 1 << 20, C.c_void_p(0x100002), None) == 3

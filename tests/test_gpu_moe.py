@@ -238,14 +238,32 @@ def test_scale_records_layout():
             assert not logical.any(), r
 
 
-def test_scale_records_same_result():
+def test_mx_scale_records_layout():
+    """MXFP4 records: record (c, r) of operand b is the four E8M0 bytes of row
+    r, blocks 4 c .. 4 c + 3, in order; rows past `rows` are zero."""
+    m = q4()
+    rng = np.random.default_rng(13)
+    b, rows, K = 2, 300, 512
+    sc = rng.integers(0, 256, size=(b, rows, K // 32), dtype=np.uint8)
+    rec = host(m.q4_scale_records(dev(sc), K, fmt=m.MXFP4))
+    assert rec.shape == (b, K // 128, 512, 4)
+    want = sc.reshape(b, rows, K // 128, 4).transpose(0, 2, 1, 3)
+    assert np.array_equal(rec[:, :, :rows], want)
+    assert not rec[:, :, rows:].any()
+
+
+@pytest.mark.parametrize("T,H,E,F,topk,k", [(600, 1024, 4, 1024, 2, 32),   # 256 x 256 tiles
+                                            (64, 1024, 16, 512, 4, 32),     # decode-shaped
+                                            (48, 768, 8, 384, 8, 0)])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_scale_records_same_result(T, H, E, F, topk, k, fmt):
     """The grouped layer with the weights' scale records equals the layer
-    without them bit for bit where both run the 256 x 256 kernel (K >= 1024 at
-    both sites): the records change where the scales come from, not the
+    without them bit for bit where both run the same kernel (the 256 x 256
+    kernel with K >= 1024 at both sites, or the decode-shaped streaming
+    kernel): the records change where the scales come from, not the
     arithmetic."""
     m = q4()
-    rng = np.random.default_rng(12)
-    T, H, E, F, topk, k = 600, 1024, 4, 1024, 2, 32
+    rng = np.random.default_rng(12 + T)
     x = rng.standard_normal((T, H)).astype(np.float32)
     x[:, rng.choice(H, 3, replace=False)] *= 40
     logits = dev(rng.standard_normal((T, E)).astype(np.float32))
@@ -253,13 +271,13 @@ def test_scale_records_same_result():
     w2 = dev(_bits((rng.standard_normal((E, H, F)) * 0.05).astype(np.float32)))
     xd = dev(_bits(x))
     idx, p = m.q4_moe_route(logits, topk)
-    with_rec = m.prepare_moe_weights(w13, w2)
-    without = m.prepare_moe_weights(w13, w2, scale_records=False)
+    with_rec = m.prepare_moe_weights(w13, w2, fmt=fmt)
+    without = m.prepare_moe_weights(w13, w2, fmt=fmt, scale_records=False)
     assert "scale_records" in with_rec["w13"] and "scale_records" not in without["w13"]
     Y1, ws1 = m.moe_w4a4_grouped_gemm(xd, idx, p, with_rec, k, out_dtype=m.OUT_F32)
     Y0, ws0 = m.moe_w4a4_grouped_gemm(xd, idx, p, without, k, out_dtype=m.OUT_F32)
     torch.cuda.synchronize()
-    offs, _ = m.moe_workspace_layout(0, T, E, H, F, topk, k)
+    offs, _ = m.moe_workspace_layout(fmt, T, E, H, F, topk, k)
     R = T * topk
     h1 = _ws_field(ws1, offs, 7, R * F * 2, torch.int16)
     h0 = _ws_field(ws0, offs, 7, R * F * 2, torch.int16)
