@@ -348,11 +348,12 @@ def rac_gemm_eq21(x, A, W, chan_set, out_dtype=OUT_F32, stream=None, Y=None, wor
 
 
 def q4_transpose_bf16(x, stream=None):
-    """[batch,] rows x cols -> [batch,] cols x rows."""
+    """rows x cols -> cols x rows; batch x rows x cols -> cols x batch x rows
+    (channel-major, the matrices interleaved)."""
     x = _bf16(x)
     batch = x.shape[0] if x.dim() == 3 else 1
     rows, cols = x.shape[-2], x.shape[-1]
-    out = _empty(x.shape[:-2] + (cols, rows), x.dtype, x.device)
+    out = _empty((cols, batch, rows) if x.dim() == 3 else (cols, rows), x.dtype, x.device)
     _check(lib().q4_transpose_bf16(_ptr(x), batch, rows, cols, _ptr(out), _stream(stream)))
     return out
 
@@ -514,8 +515,8 @@ def moe_w4a4_grouped_gemm(tokens, topk_idx, topk_w, experts, rac_k, out_dtype=OU
             fmt, _ptr(tokens), T, H, _ptr(topk_idx), _ptr(topk_w), topk, E, F,
             _ptr(w13["codes"]), _ptr(w13["scales"]), _ptr(w13["tensor_scale"]),
             _ptr(w2["codes"]), _ptr(w2["scales"]), _ptr(w2["tensor_scale"]),
-            _ptr(experts.get("w13_hi_t"), _BF16_TYPES, (E, H, 2 * F), "w13_hi_t") if rac_k else None,
-            _ptr(experts.get("w2_hi_t"), _BF16_TYPES, (E, F, H), "w2_hi_t") if rac_k else None,
+            _ptr(experts.get("w13_hi_t"), _BF16_TYPES, (H, E, 2 * F), "w13_hi_t") if rac_k else None,
+            _ptr(experts.get("w2_hi_t"), _BF16_TYPES, (F, E, H), "w2_hi_t") if rac_k else None,
             rec13, rec2, _ptr(h_tensor_scale, torch.float32, (1,), "h_tensor_scale"),
             rac_k, _ptr(Y), out_dtype, _ptr(workspace, torch.uint8), wsb,
             _status(status),

@@ -579,7 +579,8 @@ q4_status_t q4_transpose_bf16(const uint16_t* in, int64_t batch, int64_t rows, i
     Q4_REQUIRE_PTR(in);
     Q4_REQUIRE_PTR(out);
   }
-  return hip_status(launch_transpose_bf16(in, batch, rows, cols, out, S(stream)), "q4_transpose_bf16");
+  return hip_status(launch_transpose_bf16(in, batch, rows, cols, out, S(stream), true),
+                    "q4_transpose_bf16");
 }
 
 q4_status_t q4_moe_pack_w13(const uint16_t* w13, int32_t E, int32_t F, int32_t H, uint16_t* out,

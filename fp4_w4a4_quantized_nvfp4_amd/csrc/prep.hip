@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void rac_prep_kernel(PrepArgs p) {
   const int32_t k = ok ? p.k : 0;
   if (b < p.n_ws) {
     const int64_t by = b / p.ws_gx;
-    wsel_gather_part(p.w_hi_t, p.K, p.N, p.idx, k, p.kp, p.W_S, 0, b - by * p.ws_gx, (int)by,
+    wsel_gather_part(p.w_hi_t, p.K, p.N, 1, p.idx, k, p.kp, p.W_S, 0, b - by * p.ws_gx, (int)by,
                      tile, MX ? nullptr : p.w_ts, p.a_ts);
     return;
   }

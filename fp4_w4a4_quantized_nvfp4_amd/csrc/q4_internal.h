@@ -42,9 +42,11 @@ hipError_t launch_wsel_gather(const uint16_t* w_hi_t, int64_t batch, int64_t K, 
                               const int32_t* idx, int32_t k, int32_t kp, uint16_t* ws,
                               hipStream_t stream, const float* w_ts = nullptr,
                               const float* a_ts = nullptr);
-// w_ts [batch], a_ts [1] (NVFP4): W_S as the fp16 GEMM operand w / (s_W f)
+// w_hi_t channel-major [K][batch][N]; w_ts [batch], a_ts [1] (NVFP4): W_S as
+// the fp16 GEMM operand w / (s_W f)
+// out[b][c][r] = in[b][r][c]; interleave: out[c][b][r] = in[b][r][c]
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t batch, int64_t rows, int64_t cols,
-                                 uint16_t* out, hipStream_t stream);
+                                 uint16_t* out, hipStream_t stream, bool interleave = false);
 hipError_t launch_moe_pack_w13(const uint16_t* w13, int32_t E, int32_t F, int32_t H,
                                uint16_t* out, hipStream_t stream);
 

@@ -101,15 +101,29 @@ __device__ __forceinline__ void residual_gather_part(
   }
 }
 
-// W_S[b][j][t] = w_hi_t[b][S_t][j] for t < k, 0 for k <= t < kp: a transposing
-// gather through a 64 x 64 LDS tile (the selected rows are contiguous in j).
+// 1 / (s_W f_A) for s_A = f_A 2^e_A, f_A in [0.5, 1): the factor that takes a
+// selected weight column to the units of the W4A4 sum
+__device__ __forceinline__ float wsel_scale_inv(float w_ts, float a_ts) {
+  int ea;
+  return 1.0f / (w_ts * frexpf(a_ts, &ea));
+}
+
+// W_S[b][j][t] = W_hi^T of matrix b at (S_t, j) for t < k, 0 for k <= t < kp:
+// a transposing gather through a 64 x 64 LDS tile (the selected rows are
+// contiguous in j).  W_hi^T of `batch` matrices is laid out channel-major,
+// [K][batch][N] (one matrix: [K][N]): the batch's rows of one selected
+// channel are contiguous, so a gather reads 64 contiguous runs rather than
+// 64 rows scattered over every matrix.
 // With `w_ts` (NVFP4 GEMM operand, the weights' tensor scales, one per matrix
 // b) and `a_ts` (the activation's tensor scale, s_A = f 2^e): the value
-// w / (s_W[b] f) rounded once more, to fp16 (relative 2^-12), so that the
-// compensation R W_S^T comes in the units of the W4A4 sum.
+// w / (s_W[b] f), formed as w times the fp32 reciprocal of s_W[b] f (within
+// 2^-23 of the quotient) and rounded to fp16 (relative 2^-11), so that the
+// compensation R W_S^T comes in the units of the W4A4 sum.  (wsel_scale_inv
+// gives that reciprocal; every reader of W_S forms it the same way.)
 // Tile (bx, by) of matrix b covers j in [64 bx, 64 bx + 64), t in [64 by, 64 by + 64).
 __device__ __forceinline__ void wsel_gather_part(const uint16_t* __restrict__ w_hi_t, int64_t K,
-                                                 int64_t N, const int32_t* __restrict__ idx,
+                                                 int64_t N, int64_t batch,
+                                                 const int32_t* __restrict__ idx,
                                                  int32_t k, int32_t kp, uint16_t* __restrict__ ws,
                                                  int64_t b, int64_t bx, int by,
                                                  uint16_t (*tile)[66],
@@ -118,7 +132,7 @@ __device__ __forceinline__ void wsel_gather_part(const uint16_t* __restrict__ w_
   const int64_t j0 = bx * 64;
   const int t0 = by * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const uint16_t* src = w_hi_t + b * K * N;
+  const uint16_t* src = w_hi_t + b * N;
   int64_t rowoff[16];
   bool ok[16];
 #pragma unroll
@@ -126,18 +140,17 @@ __device__ __forceinline__ void wsel_gather_part(const uint16_t* __restrict__ w_
     const int t = t0 + ty + 4 * q;
     int c = t < k ? idx[t] : 0;
     c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
-    rowoff[q] = (int64_t)c * N;
+    rowoff[q] = (int64_t)c * batch * N;
     ok[q] = t < k && j0 + tx < N;
   }
   uint16_t v[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) v[q] = ok[q] ? src[rowoff[q] + j0 + tx] : (uint16_t)0;
   if (w_ts) {
-    int ea;
-    const float d = w_ts[b] * frexpf(a_ts[0], &ea);
+    const float rinv = wsel_scale_inv(w_ts[b], a_ts[0]);
 #pragma unroll
     for (int q = 0; q < 16; ++q)
-      v[q] = __builtin_bit_cast(uint16_t, (_Float16)(bf16_to_f32(v[q]) / d));
+      v[q] = __builtin_bit_cast(uint16_t, (_Float16)(bf16_to_f32(v[q]) * rinv));
   }
 #pragma unroll
   for (int q = 0; q < 16; ++q) tile[ty + 4 * q][tx] = v[q];

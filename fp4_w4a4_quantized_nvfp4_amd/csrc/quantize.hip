@@ -634,20 +634,81 @@ __global__ __launch_bounds__(256) void wsel_gather_kernel(const uint16_t* __rest
                                                           const float* __restrict__ a_ts) {
   __shared__ uint16_t tile[64][66];
   const bool ok = chan_set_ok(idx, k, K);
-  wsel_gather_part(w_hi_t, K, N, idx, ok ? k : 0, kp, ws, blockIdx.z, blockIdx.x, blockIdx.y,
+  wsel_gather_part(w_hi_t, K, N, gridDim.z, idx, ok ? k : 0, kp, ws, blockIdx.z, blockIdx.x, blockIdx.y,
                    tile, w_ts, a_ts);
 }
 
-// out[b][c][r] = in[b][r][c]
+// The same gather in 64 x 256 tiles with 8-byte accesses (N % 4 == 0): each
+// wave reads one selected row's 256 columns per load (lane l: columns
+// 4 l .. 4 l + 3), the tile is transposed through LDS, and each lane writes
+// four consecutive channels of one output row.  Tile (bx, by) of matrix b:
+// j in [256 bx, 256 bx + 256), t in [64 by, 64 by + 64).
+__global__ __launch_bounds__(256) void wsel_gather_wide_kernel(const uint16_t* __restrict__ w_hi_t,
+                                                               int64_t K, int64_t N,
+                                                               const int32_t* __restrict__ idx,
+                                                               int32_t k, int32_t kp,
+                                                               uint16_t* __restrict__ ws,
+                                                               const float* __restrict__ w_ts,
+                                                               const float* __restrict__ a_ts) {
+  constexpr int TP = 264;   // LDS row pitch (u16): 256 columns + 8 of pad
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][TP];
+  const bool ok = chan_set_ok(idx, k, K);
+  const int kk = ok ? k : 0;
+  const int64_t b = blockIdx.z;
+  const int64_t j0 = (int64_t)blockIdx.x * 256;
+  const int t0 = blockIdx.y * 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint16_t* src = w_hi_t + b * N;   // channel-major [K][batch][N]
+  const int64_t cstride = (int64_t)gridDim.z * N;
+  const int64_t jl = j0 + 4 * lane;
+  const bool jok = jl < N;   // N % 4 == 0: the lane's four columns are all in or all out
+  const float rinv = w_ts ? wsel_scale_inv(w_ts[b], a_ts[0]) : 1.0f;
+  uint2 v[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int t = t0 + 4 * q + wave;
+    int c = t < kk ? idx[t] : 0;
+    c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
+    v[q] = (t < kk && jok) ? *(const uint2*)(src + (int64_t)c * cstride + jl) : make_uint2(0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    uint2 w = v[q];
+    if (w_ts) {
+      auto cv = [&](uint32_t x) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(bf16_lo(x) * rinv));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(bf16_hi(x) * rinv));
+        return lo | (hi << 16);
+      };
+      w = make_uint2(cv(w.x), cv(w.y));
+    }
+    *(uint2*)&tile[4 * q + wave][4 * lane] = w;
+  }
+  __syncthreads();
+  uint16_t* dst = ws + b * N * kp;
+  const int tt = 4 * (lane & 15);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int jj = 16 * q + 4 * wave + (lane >> 4);
+    const int64_t j = j0 + jj;
+    const uint32_t a0 = tile[tt][jj], a1 = tile[tt + 1][jj], a2 = tile[tt + 2][jj], a3 = tile[tt + 3][jj];
+    if (j < N && t0 + tt < kp) *(uint2*)(dst + j * kp + t0 + tt) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+  }
+}
+
+// out[b][c][r] = in[b][r][c], or (interleave) out[c][b][r] = in[b][r][c]
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
                                                              int64_t rows, int64_t cols,
-                                                             uint16_t* __restrict__ out) {
+                                                             uint16_t* __restrict__ out,
+                                                             int32_t interleave) {
   __shared__ uint16_t tile[64][66];
   const int64_t b = blockIdx.z;
   const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const uint16_t* src = in + b * rows * cols;
-  uint16_t* dst = out + b * rows * cols;
+  // output row c of matrix b: interleaved rows c * batch + b
+  uint16_t* dst = interleave ? out + b * rows : out + b * rows * cols;
+  const int64_t orow = interleave ? (int64_t)gridDim.z * rows : rows;
   for (int r = ty; r < 64; r += 4) {
     const int64_t rr = r0 + r, cc = c0 + tx;
     tile[r][tx] = (rr < rows && cc < cols) ? src[rr * cols + cc] : (uint16_t)0;
@@ -655,7 +716,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   __syncthreads();
   for (int r = ty; r < 64; r += 4) {
     const int64_t cc = c0 + r, rr = r0 + tx;
-    if (cc < cols && rr < rows) dst[cc * rows + rr] = tile[tx][r];
+    if (cc < cols && rr < rows) dst[cc * orow + rr] = tile[tx][r];
   }
 }
 
@@ -877,6 +938,12 @@ hipError_t launch_wsel_gather(const uint16_t* w_hi_t, int64_t batch, int64_t K, 
                               const int32_t* idx, int32_t k, int32_t kp, uint16_t* ws,
                               hipStream_t stream, const float* w_ts, const float* a_ts) {
   if (batch == 0 || N == 0 || kp == 0) return hipSuccess;
+  if (N % 4 == 0) {
+    dim3 grid((unsigned)((N + 255) / 256), (unsigned)((kp + 63) / 64), (unsigned)batch);
+    hipLaunchKernelGGL(wsel_gather_wide_kernel, grid, dim3(256), 0, stream, w_hi_t, K, N, idx, k,
+                       kp, ws, w_ts, a_ts);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((N + 63) / 64), (unsigned)((kp + 63) / 64), (unsigned)batch);
   hipLaunchKernelGGL(wsel_gather_kernel, grid, dim3(256), 0, stream, w_hi_t, K, N, idx, k, kp, ws,
                      w_ts, a_ts);
@@ -884,10 +951,11 @@ hipError_t launch_wsel_gather(const uint16_t* w_hi_t, int64_t batch, int64_t K, 
 }
 
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t batch, int64_t rows, int64_t cols,
-                                 uint16_t* out, hipStream_t stream) {
+                                 uint16_t* out, hipStream_t stream, bool interleave) {
   if (batch == 0 || rows == 0 || cols == 0) return hipSuccess;
   dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)batch);
-  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, stream, in, rows, cols, out);
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid, dim3(256), 0, stream, in, rows, cols, out,
+                     interleave ? 1 : 0);
   return hipGetLastError();
 }
 

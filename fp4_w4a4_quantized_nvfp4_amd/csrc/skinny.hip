@@ -55,6 +55,56 @@ struct SkinnyChunk {
   uint32_t sa, sb[2];
 };
 
+// The tail of a skinny tile: Y = s_A s_W * (sum + compensation), the NVFP4
+// compensation operands in fp16 in the sum's units, MXFP4's in bf16 added
+// after the (unit) scaling; the product of the tensor scales applied without
+// underflow.  The compensation's R rows are the lane's activation row ar
+// (rok: inside the tile), its weight columns the gathered W_S.
+template <bool MX>
+__device__ __forceinline__ void skinny_tail(const GemmArgs& g, f32x16v (&acc)[2], int e,
+                                            int64_t ar, bool rok, const bool (&cok)[2], int64_t c0,
+                                            int l32, int h) {
+  const int64_t N = g.N;
+  const OutScale os = g.a_ts ? out_scale(g.a_ts[0], g.w_ts[e]) : OutScale{1.0f, 0, false};
+  const bool units = g.kp > 0 && g.r_res && !MX;
+  if (!units) {
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
+  }
+  if (g.kp > 0 && g.r_res) {
+    const uint16_t* rrow = g.r_res + ar * g.ld_r + 8 * h;
+    const uint16_t* wrw[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+      const int64_t col = c0 + ni * 32 + l32;
+      wrw[ni] = g.w_sel + ((int64_t)e * N + (cok[ni] ? col : 0)) * g.kp + 8 * h;
+    }
+    for (int kt = 0; kt < g.kp; kt += 16) {
+      const uint4 av = rok ? *(const uint4*)(rrow + kt) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const uint4 bv = cok[ni] ? *(const uint4*)(wrw[ni] + kt) : make_uint4(0, 0, 0, 0);
+        if constexpr (MX)
+          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, av),
+                                                           __builtin_bit_cast(bf16x8v, bv),
+                                                           acc[ni], 0, 0, 0);
+        else
+          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8v, av),
+                                                          __builtin_bit_cast(half8v, bv), acc[ni],
+                                                          0, 0, 0);
+      }
+    }
+  }
+  if (units) {
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
+  }
+}
+
 template <bool MX, int EPI>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -182,50 +232,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     if (k0 >= K) break;
   }
 
-  // Y = s_A s_W * (sum + compensation) with NVFP4 fp16 compensation operands
-  // in the sum's units; bf16 ones (MXFP4, no tensor scale) are added after
-  // the (unit) scaling.  The product of the tensor scales is applied without
-  // underflow.
-  const OutScale os = g.a_ts ? out_scale(g.a_ts[0], g.w_ts[e]) : OutScale{1.0f, 0, false};
-  const bool units = g.kp > 0 && g.r_res && !MX;
-  if (!units) {
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
-  }
-
-  // residual compensation: bf16 R rows of the tile x bf16 selected W columns
-  if (g.kp > 0 && g.r_res) {
-    const uint16_t* rrow = g.r_res + arow * g.ld_r + 8 * h;
-    const uint16_t* wrow[2];
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int64_t col = c0 + ni * 32 + l32;
-      wrow[ni] = g.w_sel + ((int64_t)e * N + (cok[ni] ? col : 0)) * g.kp + 8 * h;
-    }
-    for (int kt = 0; kt < g.kp; kt += 16) {
-      const uint4 av = rok ? *(const uint4*)(rrow + kt) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const uint4 bv = cok[ni] ? *(const uint4*)(wrow[ni] + kt) : make_uint4(0, 0, 0, 0);
-        if constexpr (MX)
-          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, av),
-                                                           __builtin_bit_cast(bf16x8v, bv),
-                                                           acc[ni], 0, 0, 0);
-        else
-          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8v, av),
-                                                          __builtin_bit_cast(half8v, bv), acc[ni],
-                                                          0, 0, 0);
-      }
-    }
-  }
-  if (units) {
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
-  }
+  skinny_tail<MX>(g, acc, e, arow, rok, cok, c0, l32, h);
 
   // accumulator element q of lane l: row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32
 #pragma unroll
@@ -532,50 +539,7 @@ __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs g) {
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) cok[ni] = c0 + ni * 32 + l32 < N;
 
-  // Y = s_A s_W * (sum + compensation) with NVFP4 fp16 compensation operands
-  // in the sum's units; bf16 ones (MXFP4, no tensor scale) are added after
-  // the (unit) scaling.  The product of the tensor scales is applied without
-  // underflow.
-  const OutScale os = g.a_ts ? out_scale(g.a_ts[0], g.w_ts[e]) : OutScale{1.0f, 0, false};
-  const bool units = g.kp > 0 && g.r_res && !MX;
-  if (!units) {
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
-  }
-
-  // residual compensation: R rows of the tile x selected W columns
-  if (g.kp > 0 && g.r_res) {
-    const uint16_t* rrow = g.r_res + ar * g.ld_r + 8 * h;
-    const uint16_t* wrw[2];
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int64_t col = c0 + ni * 32 + l32;
-      wrw[ni] = g.w_sel + ((int64_t)e * N + (cok[ni] ? col : 0)) * g.kp + 8 * h;
-    }
-    for (int kt = 0; kt < g.kp; kt += 16) {
-      const uint4 av = rok ? *(const uint4*)(rrow + kt) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const uint4 bv = cok[ni] ? *(const uint4*)(wrw[ni] + kt) : make_uint4(0, 0, 0, 0);
-        if constexpr (MX)
-          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, av),
-                                                           __builtin_bit_cast(bf16x8v, bv),
-                                                           acc[ni], 0, 0, 0);
-        else
-          acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8v, av),
-                                                          __builtin_bit_cast(half8v, bv), acc[ni],
-                                                          0, 0, 0);
-      }
-    }
-  }
-  if (units) {
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
-  }
+  skinny_tail<MX>(g, acc, e, ar, rok, cok, c0, l32, h);
 
   // accumulator element q of lane l: row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32
   if (c0 >= N) return;

@@ -188,9 +188,12 @@ q4_status_t w4a4_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint8_
  * with R the bf16 residual of x on the channel set S (q4_residual_gather) and
  * W_hi the bf16 weight.  The compensation is accumulated into the same fp32
  * tile as the W4A4 product: for NVFP4 as fp16 MFMA steps on R 2^-e_A (exact)
- * and W_hi / (s_W f_A) (one more rounding, relative 2^-12; s_A = f_A 2^e_A)
- * into the unscaled sum, then s_A s_W multiplies both; for MXFP4 as bf16
- * steps.  Range (documented, not checked): |r| / s_A and |W_hi| / s_W below
+ * and W_hi / (s_W f_A) (W_hi times the fp32 reciprocal of s_W f_A, rounded
+ * to fp16: relative error at most 2^-11 + 2^-21; s_A = f_A 2^e_A) into the
+ * unscaled sum, then s_A s_W multiplies both; for MXFP4 as bf16 steps.  The
+ * compensation term therefore carries that relative rounding, which matters
+ * only where it is large against the output (blocks saturated under a
+ * supplied tensor scale).  Range (documented, not checked): |r| / s_A and |W_hi| / s_W below
  * 2^15 (with tensor scales taken from the operands' own amax they are at
  * most 448 and 2688).  s_A s_W itself may be as small as the fp32 range
  * allows: it is applied as mantissa and exponent, so only a result that is
@@ -280,8 +283,11 @@ q4_status_t q4_moe_sort(const int32_t *topk_idx, int64_t T, int32_t E, int32_t t
                         size_t workspace_bytes, int32_t *status, void *stream);
 
 /* Weight preparation (offline).
- * q4_transpose_bf16: out[c][r] = in[r][c] for a [rows][cols] bf16 matrix,
- *   repeated over `batch` stacked matrices.  Used to build W_hi^T.
+ * q4_transpose_bf16: out[c][b][r] = in[b][r][c] for `batch` stacked
+ *   [rows][cols] bf16 matrices (one matrix: out[c][r] = in[r][c]), so the
+ *   output is channel-major with the matrices interleaved, [cols][batch][rows].
+ *   Used to build W_hi^T: the batch's rows of one channel are contiguous, and
+ *   a gather of the selected channels reads a few contiguous runs.
  * q4_moe_pack_w13: the logical W13 of each expert, [2F][H] with gate rows
  *   0..F-1 and up rows F..2F-1, is re-ordered into groups of 32 rows
  *   [gate 32g..32g+31, up 32g..32g+31] for g = 0..F/32-1 (F % 32 == 0); the
@@ -317,8 +323,9 @@ q4_status_t q4_scale_records(int32_t fmt, const uint8_t *scales, int64_t batch, 
  *   w13_*      stacked packed W13 of all experts: rows E*2F (q4_moe_pack_w13
  *              order), cols H; w13_tensor_scales fp32 [E] (NVFP4) or NULL.
  *   w2_*       stacked W2: rows E*H, cols F; w2_tensor_scales fp32 [E] or NULL.
- *   w13_hi_t   bf16 [E][H][2F]: per-expert transpose of the packed bf16 W13.
- *   w2_hi_t    bf16 [E][F][H]:  per-expert transpose of the bf16 W2.
+ *   w13_hi_t   bf16 [H][E][2F]: q4_transpose_bf16 of the packed bf16 W13
+ *              (the experts' transposes, channel-major and interleaved).
+ *   w2_hi_t    bf16 [F][E][H]:  q4_transpose_bf16 of the bf16 W2.
  *              Both may be NULL when rac_k == 0.
  *   w13_scale_records, w2_scale_records: NULL, or the q4_scale_records (in
  *              the layer's format) of w13_scales (batch E, rows 2F, K = H) and

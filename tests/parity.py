@@ -86,7 +86,7 @@ def check_selection(S_gpu, ref: np.ndarray, k: int, rows: int, gpu_scores=None) 
 
 
 # fp16 rounding of the NVFP4 compensation operands (unit roundoff 2^-11; the
-# fp32 quotient before it adds 2^-23 at most)
+# fp32 product with the reciprocal of s_W f_A before it adds 2^-23 at most)
 RAC_FP16_REL = 2.0 ** -11 * (1.0 + 2.0 ** -10)
 
 

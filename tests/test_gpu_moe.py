@@ -238,6 +238,18 @@ def test_scale_records_layout():
             assert not logical.any(), r
 
 
+def test_transpose_interleaved_layout():
+    """q4_transpose_bf16 of stacked matrices: out[c][b][r] = in[b][r][c]
+    (channel-major, matrices interleaved); one matrix: the plain transpose."""
+    m = q4()
+    rng = np.random.default_rng(14)
+    x = rng.integers(0, 1 << 16, size=(3, 70, 130), dtype=np.uint16)
+    got = host(m.q4_transpose_bf16(dev(x)))
+    assert got.shape == (130, 3, 70) and np.array_equal(got, x.transpose(2, 0, 1))
+    got1 = host(m.q4_transpose_bf16(dev(x[1])))
+    assert np.array_equal(got1, x[1].T)
+
+
 def test_mx_scale_records_layout():
     """MXFP4 records: record (c, r) of operand b is the four E8M0 bytes of row
     r, blocks 4 c .. 4 c + 3, in order; rows past `rows` are zero."""

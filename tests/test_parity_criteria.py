@@ -77,7 +77,8 @@ def test_rac_fp16_bound_covers_fp16_operands():
     f_a, e_a = np.frexp(s_a)
     exact = R @ W.T
     Rg = R * 2.0 ** -e_a                                  # exact scaling by a power of two
-    Wg = (W / np.float32(s_w * f_a)).astype(np.float32).astype(np.float16).astype(np.float64)
+    rinv = np.float32(1.0) / np.float32(np.float32(s_w) * np.float32(f_a))
+    Wg = (W.astype(np.float32) * rinv).astype(np.float32).astype(np.float16).astype(np.float64)
     got = (Rg @ Wg.T) * (s_a * s_w)
     b = rac_fp16_bound(R, W, s_a, s_w)
     assert (np.abs(got - exact) <= b * (1 + 1e-9) + 1e-300).all()
