@@ -158,12 +158,12 @@ def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
                                             (700, 1024, 3, 128, 2, 0)])     # no compensation
 def test_fused_h_quantization(T, H, E, F, topk, k):
     """A supplied h tensor scale on a prefill-shaped layer: h is quantized in
-    the W13 epilogue.  With s_h equal to the in-call one, h, its codes, scales
-    and selection equal the unfused layer's (scores within the summation
-    bound of each other); with s_h below it (saturated blocks) and above it,
-    codes and scales are bit-exact against the oracle's quantization of the
-    GPU's h under that s_h, scores within the bound, and the W2 product and
-    the layer output against the oracle."""
+    the W13 epilogue.  With s_h equal to the in-call one, below it (saturated
+    blocks) and above it: h agrees with the unfused layer's (which orders the
+    sums of experts' last rows differently) within the GEMM tolerance, codes
+    and scales are bit-exact against the oracle's quantization of the GPU's h
+    under that s_h, scores within the bound, the selection valid, and the W2
+    product and the layer output agree with the oracle."""
     say(f"moe fused h T={T} H={H} E={E} F={F} topk={topk} k={k}")
     m = q4()
     rng = np.random.default_rng(T + 7 * H + F)
@@ -176,16 +176,12 @@ def test_fused_h_quantization(T, H, E, F, topk, k):
     experts = m.prepare_moe_weights(dev(w13), dev(w2))
     base, _ = _run_layer(m, xb, logits, w13, w2, topk, k, experts=experts)
     s_h = float(base["h_ts"][0])
-    same, _ = _run_layer(m, xb, logits, w13, w2, topk, k, h_ts=s_h, experts=experts)
-    for f in ("h", "h_codes", "h_scales", "h_ts", "x_S"):
-        assert np.array_equal(same[f], base[f]), f
-    check_scores(same["h_scores"], base["h_scores"], T * topk)
-    if k:
-        check_selection(same["h_S"], base["h_scores"], k, T * topk, gpu_scores=same["h_scores"])
-    for mult in (0.37, 3.0):
+    for mult in (1.0, 0.37, 3.0):
         ts = float(np.float32(s_h * mult))
         got, _ = _run_layer(m, xb, logits, w13, w2, topk, k, h_ts=ts, experts=experts)
-        assert np.array_equal(got["h"], base["h"])
+        assert np.array_equal(got["x_S"], base["x_S"])
+        assert got["h_ts"][0] == np.float32(ts)
+        check_bf16_output(got["h"], bf16_to_f64(base["h"]), tol=2 * GEMM_TOL)
         _, Sh = _check_site(0, got["h"], got, "h", k, ts=ts)
         _, Sx = _check_site(0, xb, got, "x", k)
         ref = oracle.moe_layer(xb, got["idx"], got["p"].astype(np.float64), w13, w2, k,
