@@ -34,12 +34,11 @@ PEAK_FP4_TFLOPS = 10100.0          # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 
 # HBM bytes per launch of the dense GEMM kernel from rocprofv3 --pmc FETCH_SIZE /
-# WRITE_SIZE (KiB per dispatch) scaled by the factors a plain 1 GiB copy gives
-# (fetch x 2.00, write x 1.00); valid only for the kernel source it was taken on
-# (recorded here for a source whose NVFP4 instantiations assemble to the same
-# instructions as the one the counters were taken on)
-TRAFFIC = {"gemm_src_sha256": "0595cd58d7ae3513a81a9c685ad0694f870698dda855420a486988df3f3f25c3",
-           "fetch_kib": 242328.6, "fetch_scale": 2.0, "write_kib": 265216.0, "write_scale": 1.0}
+# WRITE_SIZE (KiB per dispatch, taken on the kernel source with this sha256)
+# scaled by the factors a plain 1 GiB copy gives (fetch x 2.00, write x 1.00);
+# any change to that source makes the record stale, and the line reports null
+TRAFFIC = {"gemm_src_sha256": "61a445ba82f030809d5564e445bd255071ee53bcb37f56243cb9d1a445687bc1",
+           "fetch_kib": 240888.7, "fetch_scale": 2.0, "write_kib": 234752.0, "write_scale": 1.0}
 
 
 def _args():
