@@ -802,14 +802,19 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   if (rec13)
     Q4_TRY(launch_scale_tile_sorted(xs, a_rows, R, H, offsets, E, L.rows_pad, (uint8_t*)P(L.x_rec),
                                     s), "moe token scale records");
+  // Decode-shaped layers read the selected weight columns straight from
+  // W_hi^T inside the streaming GEMM (bf16, with the plain bf16 residual);
+  // otherwise they are gathered first.  NVFP4 gathered operands are fp16 in
+  // the W4A4 sum's units (R 2^-e_x, W_S / (s_W f_x) per expert).
+  const bool direct13 = skinny && kp && skinny_direct_ok(mx, H, 2 * (int64_t)F);
+  const bool direct2 = skinny && kp && skinny_direct_ok(mx, F, H);
   if (kp) {
-    // NVFP4: fp16 compensation operands in the W4A4 sum's units (R 2^-e_x,
-    // W_S / (s_W f_x) per expert)
     Q4_TRY(launch_residual_gather(mx, tokens, T, H, xc, xs, xts, xS, rac_k, xR, kp, s, nullptr,
-                                  !mx), "moe residual tokens");
-    Q4_TRY(launch_wsel_gather(w13_hi_t, E, H, 2 * (int64_t)F, xS, rac_k, kp,
-                              (uint16_t*)P(L.w13_sel), s, mx ? nullptr : w13_tensor_scales, xts),
-           "moe w13 gather");
+                                  !mx && !direct13), "moe residual tokens");
+    if (!direct13)
+      Q4_TRY(launch_wsel_gather(w13_hi_t, E, H, 2 * (int64_t)F, xS, rac_k, kp,
+                                (uint16_t*)P(L.w13_sel), s, mx ? nullptr : w13_tensor_scales, xts),
+             "moe w13 gather");
   }
   uint16_t* hbuf = (uint16_t*)P(L.off[7]);
   GemmArgs g{};
@@ -825,8 +830,14 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   g.w_ts = w13_tensor_scales;
   g.r_res = kp ? xR : nullptr;
   g.ld_r = kp;
-  g.w_sel = kp ? (const uint16_t*)P(L.w13_sel) : nullptr;
+  g.w_sel = kp && !direct13 ? (const uint16_t*)P(L.w13_sel) : nullptr;
   g.kp = kp;
+  if (direct13) {
+    g.w_hi_t = w13_hi_t;
+    g.w_hi_batch = E;
+    g.sel = xS;
+    g.sel_k = rac_k;
+  }
   g.Y = hbuf;
   g.ldy = F;
   g.y_bf16 = 1;
@@ -879,9 +890,10 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
                                     s), "moe h scale records");
   if (kp) {
     Q4_TRY(launch_residual_gather(mx, hbuf, R, F, hc, hs, hts, hS, rac_k, hR, kp, s, nullptr,
-                                  !mx), "moe residual h");
-    Q4_TRY(launch_wsel_gather(w2_hi_t, E, F, H, hS, rac_k, kp, (uint16_t*)P(L.w2_sel), s,
-                              mx ? nullptr : w2_tensor_scales, hts), "moe w2 gather");
+                                  !mx && !direct2), "moe residual h");
+    if (!direct2)
+      Q4_TRY(launch_wsel_gather(w2_hi_t, E, F, H, hS, rac_k, kp, (uint16_t*)P(L.w2_sel), s,
+                                mx ? nullptr : w2_tensor_scales, hts), "moe w2 gather");
   }
   GemmArgs g2{};
   g2.M = R;
@@ -896,8 +908,14 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   g2.w_ts = w2_tensor_scales;
   g2.r_res = kp ? hR : nullptr;
   g2.ld_r = kp;
-  g2.w_sel = kp ? (const uint16_t*)P(L.w2_sel) : nullptr;
+  g2.w_sel = kp && !direct2 ? (const uint16_t*)P(L.w2_sel) : nullptr;
   g2.kp = kp;
+  if (direct2) {
+    g2.w_hi_t = w2_hi_t;
+    g2.w_hi_batch = E;
+    g2.sel = hS;
+    g2.sel_k = rac_k;
+  }
   g2.Y = P(L.off[13]);
   g2.ldy = H;
   g2.y_bf16 = 0;

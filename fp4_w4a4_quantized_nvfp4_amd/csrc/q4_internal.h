@@ -104,6 +104,15 @@ struct GemmArgs {
   uint8_t* q_scales;
   const float* q_ts;
   double* q_partial;
+  // direct compensation (streaming kernel, skinny_direct_ok): the selected
+  // weight columns are read in the GEMM from W_hi^T, channel-major
+  // interleaved [K][w_hi_batch][N] bf16, at the channels sel[0 .. kp) (sel_k
+  // of them valid), instead of a gathered w_sel; r_res is then the plain
+  // bf16 residual and both go to bf16 MFMAs after the s_A s_W scaling
+  const uint16_t* w_hi_t;
+  int64_t w_hi_batch;
+  const int32_t* sel;
+  int32_t sel_k;
 };
 
 // whether a grouped GEMM runs on the 256 x 256 kernel (the one with the
@@ -170,5 +179,8 @@ hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const f
 // grouped GEMM over tiles of at most kSkinnyBM rows (few rows per expert)
 constexpr int kSkinnyBM = 32;
 hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t stream);
+// whether launch_skinny_gemm runs a kernel that can read the compensation
+// columns directly (GemmArgs::w_hi_t)
+bool skinny_direct_ok(bool mx, int64_t K, int64_t N);
 
 }  // namespace q4

@@ -288,6 +288,74 @@ __device__ __forceinline__ int sk_swz(int row, int piece) {
 
 constexpr int sk_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Direct compensation (g.w_hi_t): Y = s_A s_W sum + R W_S^T with the plain
+// bf16 residual R and the selected weight columns read here from W_hi^T
+// ([K][batch][N] bf16, channel-major interleaved: the 64 columns a wave
+// owns are 128 contiguous bytes of each selected channel's row), so no
+// gathered W_S is written and read back.  64 channels a pass: each wave
+// brings its rows into its own LDS region (`region`, 8 blocks of 8 rows x
+// 128 B, block pitch 1088 B so that the two lane halves, which read blocks
+// i and i + 1, hit disjoint banks) with eight global -> LDS loads, then reads
+// each lane's eight consecutive channels of one column (the bf16 MFMA's B
+// operand) out of it.  Padding channels (t >= sel_k) load a valid row; R is
+// zero there.  Needs N % 8 == 0.
+constexpr int SKD_BLOCK = 1088;
+template <bool MX>
+__device__ __forceinline__ void skinny_tail_direct(const GemmArgs& g, f32x16v (&acc)[2], int e,
+                                                   int64_t ar, bool rok, int64_t c0, int lane,
+                                                   uint8_t* region) {
+  const int l32 = lane & 31, h = lane >> 5;
+  const int64_t N = g.N;
+  if constexpr (!MX) {
+    const OutScale os = g.a_ts ? out_scale(g.a_ts[0], g.w_ts[e]) : OutScale{1.0f, 0, false};
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[ni][q] = apply_scale(os, acc[ni][q]);
+  }
+  const uint16_t* rrow = g.r_res + ar * g.ld_r + 8 * h;
+  // this lane's 16-byte piece of each row: columns c0 + 8 p .. + 7, p = lane % 8
+  // (pieces past N read the last piece of the row again; never stored)
+  const int64_t col = min(c0 + 8 * (lane & 7), N - 8);
+  const int64_t rstride = g.w_hi_batch * N;
+  const uint16_t* const wbase = g.w_hi_t + (int64_t)e * N + col;
+  const int Kc = g.K;
+  for (int t0 = 0; t0 < g.kp; t0 += 64) {
+    const int nb = min(8, (g.kp - t0) >> 3);   // blocks of 8 channels this pass (4 or 8)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < nb) {
+        const int t = t0 + 8 * i + (lane >> 3);
+        int c = g.sel[min(t, g.sel_k - 1)];
+        c = c < 0 ? 0 : (c >= Kc ? Kc - 1 : c);
+        __builtin_amdgcn_global_load_lds((sk_gptr_t)(wbase + (int64_t)c * rstride),
+                                         (sk_lptr_t)(region + i * SKD_BLOCK), 16, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(sk_vmcnt(0));
+    for (int kt = 0; kt < nb * 8; kt += 16) {
+      const uint4 av = rok ? *(const uint4*)(rrow + t0 + kt) : make_uint4(0, 0, 0, 0);
+      // lane half h takes channels kt + 8 h .. + 7: block kt / 8 + h, rows 0..7
+      const uint8_t* const blk = region + (kt / 8 + h) * SKD_BLOCK;
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) {
+        const uint16_t* const p = (const uint16_t*)(blk + (ni * 32 + l32) * 2);
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = (uint32_t)p[(2 * q) * 64] | ((uint32_t)p[(2 * q + 1) * 64] << 16);
+        const uint4 bv = make_uint4(w[0], w[1], w[2], w[3]);
+        acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8v, av),
+                                                         __builtin_bit_cast(bf16x8v, bv), acc[ni],
+                                                         0, 0, 0);
+      }
+    }
+  }
+}
+
+bool skinny_lds_path(const GemmArgs& g) { return g.mx ? g.K % 128 == 0 : g.K % 64 == 0; }
+static_assert(2 * 8 * SKD_BLOCK <= 20736, "direct compensation regions exceed a stage");
+
 // WREC (K % 128 == 0): the weight scales come from their records
 // (g.w_scales_t, [E][K / 128][w_rows_pad][record]): NVFP4 the tiled fp16
 // records (16 B, swizzled by row, already widened to fp16), MXFP4 the four
@@ -539,7 +607,16 @@ __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs g) {
 #pragma unroll
   for (int ni = 0; ni < 2; ++ni) cok[ni] = c0 + ni * 32 + l32 < N;
 
-  skinny_tail<MX>(g, acc, e, ar, rok, cok, c0, l32, h);
+  if (g.w_hi_t && g.kp > 0 && g.r_res) {
+    // the stages are free once every wave's loads into them (the clamped
+    // ones of the last two steps included) have landed: waves 0 and 1 take
+    // stage 0 for their compensation rows, waves 2 and 3 stage 1
+    __syncthreads();
+    uint8_t* const region = (wave < 2 ? st0 : st1) + (wave & 1) * (8 * SKD_BLOCK);
+    skinny_tail_direct<MX>(g, acc, e, ar, rok, c0, lane, region);
+  } else {
+    skinny_tail<MX>(g, acc, e, ar, rok, cok, c0, l32, h);
+  }
 
   // accumulator element q of lane l: row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32
   if (c0 >= N) return;
@@ -568,7 +645,14 @@ __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs g) {
 
 }  // namespace
 
+bool skinny_direct_ok(bool mx, int64_t K, int64_t N) {
+  return (mx ? K % 128 == 0 : K % 64 == 0) && N % 8 == 0;
+}
+
 hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t stream) {
+  // direct compensation only on the LDS kernels (checked by the caller with
+  // skinny_direct_ok; refused here rather than read out of bounds)
+  if (g.w_hi_t && g.kp > 0 && !skinny_direct_ok(g.mx, g.K, g.N)) return hipErrorInvalidValue;
   const int64_t nbn = (g.N + SN - 1) / SN;
   const int64_t nb = max_tiles * nbn;
   if (nb == 0) return hipSuccess;
@@ -587,7 +671,7 @@ hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t 
     }
     return hipGetLastError();
   }
-  if (g.mx ? g.K % 128 == 0 : g.K % 64 == 0) {
+  if (skinny_lds_path(g)) {
     if (g.mx) {
       if (g.epilogue == kEpiSwiGLU)
         hipLaunchKernelGGL((gemm_skinny_lds_kernel<true, kEpiSwiGLU>), grid, block, 0, stream, g);

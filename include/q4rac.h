@@ -358,11 +358,16 @@ size_t moe_workspace_size(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t 
 /* (host) offsets[0..Q4_MOE_WS_FIELDS-1] in bytes from the workspace base:
  *   0 perm int32 [T*topk]      1 offsets int32 [E+1]      2 x codes
  *   3 x scales                 4 x tensor scale fp32      5 x channel set int32 [rac_k]
- *   6 x residual R bf16 [T][kp] 7 h bf16 [T*topk][F]       8 h codes
+ *   6 x residual R [T][kp]     7 h bf16 [T*topk][F]       8 h codes
  *   9 h scales                10 h tensor scale fp32     11 h channel set
- *  12 h residual R bf16 [T*topk][kp]                     13 out fp32 [T*topk][H]
+ *  12 h residual R [T*topk][kp]                          13 out fp32 [T*topk][H]
  *  14 x channel scores fp64 [H]                          15 h channel scores fp64 [F]
- * kp = rac_k rounded up to a multiple of 32. */
+ * kp = rac_k rounded up to a multiple of 32.  R holds bf16(r) on the selected
+ * channels (zero past rac_k), except for an NVFP4 GEMM that takes its
+ * selected weight columns from a gathered copy (layers with more than 64
+ * routed rows per expert on average, or K % 64 != 0): there it holds the fp16
+ * operand bf16(r) 2^-e, s_t = f 2^e with f in [0.5, 1).  Decode-shaped layers
+ * read the selected columns of W_hi^T inside the GEMM. */
 #define Q4_MOE_WS_FIELDS 16
 q4_status_t moe_workspace_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F,
                                  int32_t topk, int32_t rac_k, size_t *offsets);

@@ -123,7 +123,16 @@ def _check_site(fmt, xb, got, prefix, rac_k, ts=None):
                                             # NVFP4: both grouped GEMMs on 256 x 256
                                             # tiles reading the tiled scale records
                                             # (K = 512 at both sites)
-                                            (600, 512, 4, 512, 2, 32)])
+                                            (600, 512, 4, 512, 2, 32),
+                                            # decode-shaped (streaming kernel) with the
+                                            # compensation columns read from W_hi^T:
+                                            # kp = 128 in two passes with padding
+                                            # channels, kp = 96 as 64 + 32, column
+                                            # counts not a multiple of 256; W2 with
+                                            # K % 64 != 0 (NVFP4) or K % 128 != 0
+                                            # (MXFP4) falls back to the gathered W_S
+                                            (48, 512, 8, 160, 2, 100),
+                                            (40, 256, 8, 192, 2, 70)])
 def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
     say(f"moe small fmt={fmt} T={T} H={H} E={E} F={F} topk={topk} k={k}")
     m = q4()
