@@ -233,6 +233,111 @@ __global__ __launch_bounds__(1024) void moe_scatter_kernel(const int32_t* __rest
   }
 }
 
+// The whole sort in one workgroup for few routed rows (decode-shaped layers,
+// n <= kSortSmallBlocks * 1024): expert counts, offsets and tile tables, then
+// the stable scatter block by block in flat order (ranks from wave ballots and
+// per-wave counts, a running base per expert).  Same outputs as the three
+// kernels above, one launch instead of three.
+constexpr int kSortSmallBlocks = 8;
+__global__ __launch_bounds__(1024) void moe_sort_small_kernel(
+    const int32_t* __restrict__ idx, int64_t n, int32_t E, int32_t topk,
+    int32_t* __restrict__ perm, int32_t* __restrict__ offsets, int32_t* __restrict__ inv_perm,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ ntiles, int32_t* __restrict__ a_rows,
+    int32_t bm2, int32_t* __restrict__ tiles2, int32_t* __restrict__ ntiles2,
+    int32_t* __restrict__ status) {
+  __shared__ int wcnt[16][1024];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1025];
+  __shared__ int s_tile[1025];
+  __shared__ int s_tile2[1025];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nb = (int)((n + 1023) / 1024);
+  for (int e = threadIdx.x; e < E; e += 1024) s_cnt[e] = 0;
+  for (int q = threadIdx.x; q < 16 * E; q += 1024) wcnt[q / E][q % E] = 0;
+  __syncthreads();
+  // counts (each thread keeps its rows' experts for the scatter)
+  int ex[kSortSmallBlocks];
+  int bad_any = 0;
+#pragma unroll
+  for (int b = 0; b < kSortSmallBlocks; ++b) {
+    const int64_t i = (int64_t)b * 1024 + threadIdx.x;
+    const bool valid = b < nb && i < n;
+    bool bad;
+    ex[b] = routed_expert(idx, i, valid, E, bad);
+    bad_any |= bad;
+    uint64_t pending = __ballot(valid);
+    while (pending) {
+      const int leader = __ffsll((unsigned long long)pending) - 1;
+      const int d0 = __shfl(ex[b], leader, 64);
+      const uint64_t same = __ballot(valid && ex[b] == d0) & pending;
+      if (lane == leader) atomicAdd(&s_cnt[d0], __popcll(same));
+      pending &= ~same;
+    }
+  }
+  bad_any = __syncthreads_or(bad_any);
+  if (threadIdx.x == 0) {
+    if (status) status[0] = bad_any ? 1 : 0;
+    int o = 0, tcount = 0, tcount2 = 0;
+    for (int e = 0; e < E; ++e) {
+      s_off[e] = o;
+      s_tile[e] = tcount;
+      s_tile2[e] = tcount2;
+      o += s_cnt[e];
+      tcount += (s_cnt[e] + kGemmBM - 1) / kGemmBM;
+      if (tiles2) tcount2 += (s_cnt[e] + bm2 - 1) / bm2;
+    }
+    s_off[E] = o;
+    s_tile[E] = tcount;
+    s_tile2[E] = tcount2;
+    ntiles[0] = tcount;
+    if (tiles2) ntiles2[0] = tcount2;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += 1024) offsets[e] = s_off[e];
+  write_tiles(s_off, s_tile, E, kGemmBM, tiles);
+  if (tiles2) write_tiles(s_off, s_tile2, E, bm2, tiles2);
+  // s_cnt becomes the running base of each expert
+  for (int e = threadIdx.x; e < E; e += 1024) s_cnt[e] = s_off[e];
+  __syncthreads();
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int b = 0; b < kSortSmallBlocks; ++b) {
+    if (b >= nb) break;                        // uniform
+    const int64_t i = (int64_t)b * 1024 + threadIdx.x;
+    const bool valid = i < n;
+    const int e = ex[b];
+    int rank = 0;
+    uint64_t pending = __ballot(valid);
+    while (pending) {
+      const int leader = __ffsll((unsigned long long)pending) - 1;
+      const int d0 = __shfl(e, leader, 64);
+      const uint64_t same = __ballot(valid && e == d0) & pending;
+      if (valid && e == d0) rank = __popcll(same & below);
+      if (lane == leader) wcnt[wv][d0] = __popcll(same);
+      pending &= ~same;
+    }
+    __syncthreads();
+    if (valid) {
+      for (int w = 0; w < wv; ++w) rank += wcnt[w][e];
+      const int pos = s_cnt[e] + rank;
+      perm[pos] = (int32_t)i;
+      inv_perm[i] = pos;
+      if (a_rows) a_rows[pos] = (int32_t)(i / topk);
+    }
+    __syncthreads();
+    // advance the bases past this block and clear the wave counts
+    for (int e2 = threadIdx.x; e2 < E; e2 += 1024) {
+      int add = 0;
+      for (int w = 0; w < 16; ++w) {
+        add += wcnt[w][e2];
+        wcnt[w][e2] = 0;
+      }
+      s_cnt[e2] += add;
+    }
+    __syncthreads();
+  }
+}
+
 // y[t][h] = sum over slots s = 0..topk-1 of w[t][s] * out[inv_perm[t*topk+s]][h]
 // (fp32, slot order fixed; a slot with an invalid expert index contributes
 // nothing).  One workgroup per (token, 1024 columns).
@@ -294,6 +399,12 @@ hipError_t launch_moe_sort(const int32_t* idx, int64_t T, int32_t E, int32_t top
                            int32_t* tiles2, int32_t* ntiles2, int32_t* status) {
   const int64_t n = T * topk;
   const int64_t nb = (n + 1023) / 1024;
+  if (nb <= kSortSmallBlocks && E <= 1024) {
+    hipLaunchKernelGGL(moe_sort_small_kernel, dim3(1), dim3(1024), 0, stream, idx, n, E, topk,
+                       perm, offsets, inv_perm, tiles, ntiles, a_rows, bm2, tiles2, ntiles2,
+                       status);
+    return hipGetLastError();
+  }
   int32_t* flags = counts + align256((size_t)(nb > 0 ? nb : 1) * E * 4) / 4;
   if (nb > 0)
     hipLaunchKernelGGL(moe_block_hist_kernel, dim3((unsigned)nb), dim3(1024), 0, stream, idx, n,

@@ -106,15 +106,16 @@ __device__ float nvfp4_tensor_scale_dev(const QuantKArgs& a, uint32_t* red, int*
   return st;
 }
 
-// One workgroup = 8 waves = one 256-row group of one strip of 64 * CPL
-// channels; wave w owns the 32-row tile w of the group, lane l owns channels
-// strip * 64 * CPL + CPL * l .. + CPL - 1 (CPL = 8 or 16 channels per lane).
+// One workgroup = 8 waves = one group of 8 TR rows of one strip of 64 * CPL
+// channels; wave w owns the TR-row tile w of the group, lane l owns channels
+// strip * 64 * CPL + CPL * l .. + CPL - 1 (CPL = 8 or 16 channels per lane;
+// TR = 32, or 8 for small tensors, so that they still spread over the CUs).
 // Every lane sums its squared residuals over its tile's rows in order; the
 // eight tile sums are then added in tile order through LDS, giving one fp64
 // partial per (group, channel).  Codes and scales: nvfp4_lane_encode (near
 // ties are frequent: s_t is a rounded simple rational, so many x / (s s_t)
 // fall within 2^-24 of a midpoint).
-template <bool MX, int CPL>
+template <bool MX, int CPL, int TR = kScoreTileRows>
 __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
   constexpr int NW = CPL / 8;              // code words (8 nibbles) per lane per row
   constexpr int U = 64 / CPL;              // rows in flight per lane
@@ -153,8 +154,8 @@ __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = 0.0;
 
-  const int64_t r0 = group * (kScoreTileRows * kScoreGroupTiles) + wave * kScoreTileRows;
-  const int nr = (int)max((int64_t)0, min((int64_t)kScoreTileRows, a.rows - r0));
+  const int64_t r0 = group * (TR * kScoreGroupTiles) + wave * TR;
+  const int nr = (int)max((int64_t)0, min((int64_t)TR, a.rows - r0));
   const int64_t cstride = cols / 2, sstride = MX ? cols / 32 : cols / 16;
 
   // x, codes and scales of this wave's tile through buffer resources based at
@@ -739,14 +740,22 @@ __global__ void tensor_scale_kernel(const float* ts_in, float* ts_out) {
   if (threadIdx.x == 0) ts_out[0] = ts_in ? ts_in[0] : 1.0f;
 }
 
-static int64_t score_groups(int64_t rows) {
-  const int64_t g = kScoreTileRows * kScoreGroupTiles;
+// rows per score tile: 32 (256-row groups), or 8 for a tensor whose 256-row
+// groups would make fewer than 128 workgroups, each walking its rows one
+// after another (decode-sized activations: 256 x 4096 would be 8 workgroups)
+static int quant_tile_rows(int64_t rows, int64_t cols) {
+  const int64_t units = (rows + 255) / 256 * ((cols + 511) / 512);
+  return units < 128 ? 8 : kScoreTileRows;
+}
+
+static int64_t score_groups(int64_t rows, int64_t cols) {
+  const int64_t g = (int64_t)quant_tile_rows(rows, cols) * kScoreGroupTiles;
   return (rows + g - 1) / g;
 }
 
 size_t quantize_workspace_bytes(int64_t rows, int64_t cols) {
-  return align256(kAmaxBlocks * 4) + align256((size_t)score_groups(rows) * (size_t)cols * 8) +
-         align256((size_t)cols * 8);
+  return align256(kAmaxBlocks * 4) +
+         align256((size_t)score_groups(rows, cols) * (size_t)cols * 8) + align256((size_t)cols * 8);
 }
 
 hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
@@ -755,7 +764,8 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
                            hipStream_t stream) {
   uint8_t* base = (uint8_t*)ws;
   uint32_t* amax = (uint32_t*)base;
-  const int64_t ngroups = score_groups(rows);
+  const int64_t ngroups = score_groups(rows, cols);
+  const bool small = quant_tile_rows(rows, cols) != kScoreTileRows;
   const size_t amax_bytes = align256(kAmaxBlocks * 4);
   double* partial = (double*)(base + amax_bytes);
   double* scores = chan_score ? chan_score
@@ -779,7 +789,7 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
   a.cols = (int32_t)cols;
   // 16 channels per lane halves the per-block work; 8 per lane when that
   // would leave fewer than 256 workgroups (one per CU)
-  const bool wide = ngroups * ((cols + 1023) / 1024) >= 256;
+  const bool wide = !small && ngroups * ((cols + 1023) / 1024) >= 256;
   a.nstrips = (int32_t)(wide ? (cols + 1023) / 1024 : (cols + 511) / 512);
   a.ngroups = ngroups;
   a.ts_in = ts_in;
@@ -793,7 +803,11 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
   const int64_t units = ngroups * a.nstrips;
   if (units > 0) {
     const unsigned grid = (unsigned)units;
-    if (mx && wide)
+    if (small && mx)
+      hipLaunchKernelGGL((quantize_kernel<true, 8, 8>), dim3(grid), dim3(512), 0, stream, a);
+    else if (small)
+      hipLaunchKernelGGL((quantize_kernel<false, 8, 8>), dim3(grid), dim3(512), 0, stream, a);
+    else if (mx && wide)
       hipLaunchKernelGGL((quantize_kernel<true, 16>), dim3(grid), dim3(512), 0, stream, a);
     else if (mx)
       hipLaunchKernelGGL((quantize_kernel<true, 8>), dim3(grid), dim3(512), 0, stream, a);

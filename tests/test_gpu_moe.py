@@ -42,18 +42,21 @@ def _ws_field(ws, offs, i, nbytes, dtype):
     return host(ws[offs[i]:offs[i] + nbytes].view(dtype))
 
 
-def test_route_and_sort():
+# routed rows 2400 and 8192 (the one-workgroup sort, up to 8 blocks of 1024
+# rows) and 8800 (the block-histogram sort, a ragged last block)
+@pytest.mark.parametrize("T,E", [(300, 128), (1024, 128), (1100, 128), (300, 40)])
+def test_route_and_sort(T, E):
     m = q4()
-    rng = np.random.default_rng(5)
-    logits = rng.standard_normal((300, 128)).astype(np.float32)
-    logits[7, 10] = logits[7, 99] = logits[7].max() + 1.0           # tie at the top
+    rng = np.random.default_rng(5 + T + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[7, 10] = logits[7, 39] = logits[7].max() + 1.0           # tie at the top
     idx, w = m.q4_moe_route(dev(logits), 8)
     idx, w = host(idx), host(w)
     oi, op = oracle.moe_route(logits, 8)
     assert np.array_equal(idx, oi)
     np.testing.assert_allclose(w, op, rtol=2e-6, atol=1e-7)
-    perm, off = m.q4_moe_sort(dev(idx), 128)
-    pe, oe = oracle.moe_sort(idx, 128)
+    perm, off = m.q4_moe_sort(dev(idx), E)
+    pe, oe = oracle.moe_sort(idx, E)
     assert np.array_equal(host(perm), pe) and np.array_equal(host(off), oe)
 
 
