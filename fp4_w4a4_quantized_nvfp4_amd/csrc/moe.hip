@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
 // The token sort is a stable counting sort over blocks of 1024 routed rows:
 // per-block expert histograms, per-expert bases (one thread per expert walks
 // the blocks in order), then a scatter in which each row's rank inside its
-// block comes from wave ballots and per-wave counts.
+// block comes from its rank inside its wave (wave_rank) and per-wave counts.
 
 // An expert index outside [0, E) is invalid: it is counted as expert 0 (so
 // every index the sort writes stays in bounds), its slot gets weight 0 in the
@@ -93,6 +93,38 @@ __device__ __forceinline__ int routed_expert(const int32_t* __restrict__ idx, in
   return bad ? 0 : e;
 }
 
+// Rank of this lane's expert among the wave's lanes below it with the same
+// expert, and (last) whether no lane above it has that expert: the wave's 64
+// experts go to its LDS row `ids` and every lane compares against all of them
+// (sixteen 16-byte broadcast reads), so the cost does not grow with the number
+// of distinct experts in the wave.  Invalid lanes take part with key -1, which
+// no expert equals, and get last = false.
+__device__ __forceinline__ int wave_rank(int e, bool valid, int* ids, bool& last) {
+  const int lane = threadIdx.x & 63;
+  const int key = valid ? e : -1;
+  ids[lane] = key;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  int below = 0, above = 0;
+#pragma unroll
+  for (int j4 = 0; j4 < 16; ++j4) {
+    const int4 v = ((const int4*)ids)[j4];
+    const int k[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = 4 * j4 + c;
+      const int eq = k[c] == key ? 1 : 0;
+      below += j < lane ? eq : 0;
+      above += j > lane ? eq : 0;
+    }
+  }
+  // the row is reused by the next call: every lane has read it first
+  __builtin_amdgcn_wave_barrier();
+  last = valid && above == 0;
+  return below;
+}
+
 // bt[b][e] = rows of block b routed to expert e; flags[b] = block b holds an
 // invalid expert index
 __global__ __launch_bounds__(1024) void moe_block_hist_kernel(const int32_t* __restrict__ idx,
@@ -100,7 +132,8 @@ __global__ __launch_bounds__(1024) void moe_block_hist_kernel(const int32_t* __r
                                                               int32_t* __restrict__ bt,
                                                               int32_t* __restrict__ flags) {
   __shared__ int hist[1024];
-  const int lane = threadIdx.x & 63;
+  __shared__ int ids[16][64];
+  const int wv = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < E; e += 1024) hist[e] = 0;
   __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
@@ -109,16 +142,56 @@ __global__ __launch_bounds__(1024) void moe_block_hist_kernel(const int32_t* __r
   const int e = routed_expert(idx, i, valid, E, bad);
   const int any_bad = __syncthreads_or(bad);
   if (threadIdx.x == 0) flags[blockIdx.x] = any_bad;
-  uint64_t pending = __ballot(valid);
-  while (pending) {
-    const int leader = __ffsll((unsigned long long)pending) - 1;
-    const int d0 = __shfl(e, leader, 64);
-    const uint64_t same = __ballot(valid && e == d0) & pending;
-    if (lane == leader) atomicAdd(&hist[d0], __popcll(same));
-    pending &= ~same;
-  }
+  bool last;
+  const int rank = wave_rank(e, valid, ids[wv], last);
+  if (last) atomicAdd(&hist[e], rank + 1);
   __syncthreads();
   for (int q = threadIdx.x; q < E; q += 1024) bt[(int64_t)blockIdx.x * E + q] = hist[q];
+}
+
+// Per-expert offsets and tile starts as exclusive prefix sums over e < E of
+// the counts s_cnt[e], ceil(s_cnt[e] / kGemmBM) and (bm2 > 0) ceil(s_cnt[e] /
+// bm2), totals at index E; also writes ntiles[0] and ntiles2[0].  Needs a
+// 1024-thread workgroup and E <= 1024; wave shuffles, then the waves' totals
+// through LDS (no serial walk over the experts).
+__device__ __forceinline__ void expert_scan(const int* s_cnt, int32_t E, int bm2, int* s_off,
+                                            int* s_tile, int* s_tile2, int (*wsum)[3],
+                                            int32_t* __restrict__ ntiles,
+                                            int32_t* __restrict__ ntiles2) {
+  const int e = threadIdx.x, lane = e & 63, wv = e >> 6;
+  const int c = e < E ? s_cnt[e] : 0;
+  const int v[3] = {c, (c + kGemmBM - 1) / kGemmBM, bm2 > 0 ? (c + bm2 - 1) / bm2 : 0};
+  int inc[3] = {v[0], v[1], v[2]};
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int u = __shfl_up(inc[q], o, 64);
+      if (lane >= o) inc[q] += u;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) wsum[wv][q] = inc[q];
+  }
+  __syncthreads();
+  int base[3] = {0, 0, 0};
+  for (int w = 0; w < wv; ++w) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) base[q] += wsum[w][q];
+  }
+  int* const out[3] = {s_off, s_tile, s_tile2};
+  if (e < E) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) out[q][e] = base[q] + inc[q] - v[q];
+  }
+  if (e == E - 1) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) out[q][E] = base[q] + inc[q];
+    ntiles[0] = base[1] + inc[1];
+    if (ntiles2) ntiles2[0] = base[2] + inc[2];
+  }
+  __syncthreads();
 }
 
 // tile entries {e, begin, end, 0}, at most bm rows each, for every expert
@@ -152,6 +225,7 @@ __global__ __launch_bounds__(1024) void moe_offsets_kernel(int32_t* __restrict__
   __shared__ int s_off[1025];
   __shared__ int s_tile[1025];
   __shared__ int s_tile2[1025];
+  __shared__ int wsum[16][3];
   int bad = 0;
   for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) bad |= flags[b];
   bad = __syncthreads_or(bad);
@@ -173,23 +247,8 @@ __global__ __launch_bounds__(1024) void moe_offsets_kernel(int32_t* __restrict__
     s_cnt[e] = c;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int o = 0, tcount = 0, tcount2 = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = o;
-      s_tile[e] = tcount;
-      s_tile2[e] = tcount2;
-      o += s_cnt[e];
-      tcount += (s_cnt[e] + kGemmBM - 1) / kGemmBM;
-      if (tiles2) tcount2 += (s_cnt[e] + bm2 - 1) / bm2;
-    }
-    s_off[E] = o;
-    s_tile[E] = tcount;
-    s_tile2[E] = tcount2;
-    ntiles[0] = tcount;
-    if (tiles2) ntiles2[0] = tcount2;
-  }
-  __syncthreads();
+  expert_scan(s_cnt, E, tiles2 ? bm2 : 0, s_off, s_tile, s_tile2, wsum, ntiles,
+              tiles2 ? ntiles2 : nullptr);
   for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = s_off[e];
   write_tiles(s_off, s_tile, E, kGemmBM, tiles);
   if (tiles2) write_tiles(s_off, s_tile2, E, bm2, tiles2);
@@ -205,24 +264,17 @@ __global__ __launch_bounds__(1024) void moe_scatter_kernel(const int32_t* __rest
                                                            int32_t topk,
                                                            int32_t* __restrict__ a_rows) {
   __shared__ int wcnt[16][1024];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ int ids[16][64];
+  const int wv = threadIdx.x >> 6;
   for (int q = threadIdx.x; q < 16 * E; q += 1024) wcnt[q / E][q % E] = 0;
   __syncthreads();
   const int64_t i = (int64_t)blockIdx.x * 1024 + threadIdx.x;
   const bool valid = i < n;
   bool bad;
   const int e = routed_expert(idx, i, valid, E, bad);
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  int rank = 0;
-  uint64_t pending = __ballot(valid);
-  while (pending) {
-    const int leader = __ffsll((unsigned long long)pending) - 1;
-    const int d0 = __shfl(e, leader, 64);
-    const uint64_t same = __ballot(valid && e == d0) & pending;
-    if (valid && e == d0) rank = __popcll(same & below);
-    if (lane == leader) wcnt[wv][d0] = __popcll(same);
-    pending &= ~same;
-  }
+  bool last;
+  int rank = wave_rank(e, valid, ids[wv], last);
+  if (last) wcnt[wv][e] = rank + 1;
   __syncthreads();
   if (valid) {
     for (int w = 0; w < wv; ++w) rank += wcnt[w][e];
@@ -235,8 +287,8 @@ __global__ __launch_bounds__(1024) void moe_scatter_kernel(const int32_t* __rest
 
 // The whole sort in one workgroup for few routed rows (decode-shaped layers,
 // n <= kSortSmallBlocks * 1024): expert counts, offsets and tile tables, then
-// the stable scatter block by block in flat order (ranks from wave ballots and
-// per-wave counts, a running base per expert).  Same outputs as the three
+// the stable scatter block by block in flat order (in-wave ranks and per-wave
+// counts, a running base per expert).  Same outputs as the three
 // kernels above, one launch instead of three.
 constexpr int kSortSmallBlocks = 8;
 __global__ __launch_bounds__(1024) void moe_sort_small_kernel(
@@ -250,13 +302,17 @@ __global__ __launch_bounds__(1024) void moe_sort_small_kernel(
   __shared__ int s_off[1025];
   __shared__ int s_tile[1025];
   __shared__ int s_tile2[1025];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  __shared__ int wsum[16][3];
+  __shared__ int ids[16][64];
+  const int wv = threadIdx.x >> 6;
   const int nb = (int)((n + 1023) / 1024);
   for (int e = threadIdx.x; e < E; e += 1024) s_cnt[e] = 0;
   for (int q = threadIdx.x; q < 16 * E; q += 1024) wcnt[q / E][q % E] = 0;
   __syncthreads();
-  // counts (each thread keeps its rows' experts for the scatter)
-  int ex[kSortSmallBlocks];
+  // counts; each thread keeps its rows' experts, in-wave ranks and
+  // last-of-expert flags for the scatter
+  int ex[kSortSmallBlocks], rk[kSortSmallBlocks];
+  bool lst[kSortSmallBlocks];
   int bad_any = 0;
 #pragma unroll
   for (int b = 0; b < kSortSmallBlocks; ++b) {
@@ -265,57 +321,28 @@ __global__ __launch_bounds__(1024) void moe_sort_small_kernel(
     bool bad;
     ex[b] = routed_expert(idx, i, valid, E, bad);
     bad_any |= bad;
-    uint64_t pending = __ballot(valid);
-    while (pending) {
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int d0 = __shfl(ex[b], leader, 64);
-      const uint64_t same = __ballot(valid && ex[b] == d0) & pending;
-      if (lane == leader) atomicAdd(&s_cnt[d0], __popcll(same));
-      pending &= ~same;
-    }
+    rk[b] = b < nb ? wave_rank(ex[b], valid, ids[wv], lst[b]) : 0;
+    if (b >= nb) lst[b] = false;
+    if (lst[b]) atomicAdd(&s_cnt[ex[b]], rk[b] + 1);
   }
   bad_any = __syncthreads_or(bad_any);
-  if (threadIdx.x == 0) {
-    if (status) status[0] = bad_any ? 1 : 0;
-    int o = 0, tcount = 0, tcount2 = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = o;
-      s_tile[e] = tcount;
-      s_tile2[e] = tcount2;
-      o += s_cnt[e];
-      tcount += (s_cnt[e] + kGemmBM - 1) / kGemmBM;
-      if (tiles2) tcount2 += (s_cnt[e] + bm2 - 1) / bm2;
-    }
-    s_off[E] = o;
-    s_tile[E] = tcount;
-    s_tile2[E] = tcount2;
-    ntiles[0] = tcount;
-    if (tiles2) ntiles2[0] = tcount2;
-  }
-  __syncthreads();
+  if (threadIdx.x == 0 && status) status[0] = bad_any ? 1 : 0;
+  expert_scan(s_cnt, E, tiles2 ? bm2 : 0, s_off, s_tile, s_tile2, wsum, ntiles,
+              tiles2 ? ntiles2 : nullptr);
   for (int e = threadIdx.x; e <= E; e += 1024) offsets[e] = s_off[e];
   write_tiles(s_off, s_tile, E, kGemmBM, tiles);
   if (tiles2) write_tiles(s_off, s_tile2, E, bm2, tiles2);
   // s_cnt becomes the running base of each expert
   for (int e = threadIdx.x; e < E; e += 1024) s_cnt[e] = s_off[e];
   __syncthreads();
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int b = 0; b < kSortSmallBlocks; ++b) {
     if (b >= nb) break;                        // uniform
     const int64_t i = (int64_t)b * 1024 + threadIdx.x;
     const bool valid = i < n;
     const int e = ex[b];
-    int rank = 0;
-    uint64_t pending = __ballot(valid);
-    while (pending) {
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int d0 = __shfl(e, leader, 64);
-      const uint64_t same = __ballot(valid && e == d0) & pending;
-      if (valid && e == d0) rank = __popcll(same & below);
-      if (lane == leader) wcnt[wv][d0] = __popcll(same);
-      pending &= ~same;
-    }
+    int rank = rk[b];
+    if (lst[b]) wcnt[wv][e] = rank + 1;
     __syncthreads();
     if (valid) {
       for (int w = 0; w < wv; ++w) rank += wcnt[w][e];
