@@ -154,10 +154,11 @@ def _moe_legs(q4, L, dev, stream, sp, iters=10):
     return res
 
 
-def _warm(fn, stream, ms=60.0):
+def _warm(fn, stream, ms=60.0, max_calls=200):
     """Untimed calls of `fn` until about `ms` of device time has run (three at
-    least): the device's clocks ramp over the first tens of milliseconds of
-    sustained load, and a leg timed inside that ramp reads up to 30 % slow."""
+    least, `max_calls` at most): the device's clocks ramp over the first tens
+    of milliseconds of sustained load, and a leg timed inside that ramp reads
+    up to 30 % slow."""
     import torch
     for _ in range(3):
         fn()
@@ -167,7 +168,7 @@ def _warm(fn, stream, ms=60.0):
     fn()
     e1.record(stream)
     e1.synchronize()
-    for _ in range(min(200, int(ms / max(e0.elapsed_time(e1), 1e-3)))):
+    for _ in range(min(max_calls, int(ms / max(e0.elapsed_time(e1), 1e-3)))):
         fn()
 
 
@@ -401,8 +402,12 @@ def main():
                                    iq.data_ptr(), wsq.data_ptr(), wsq_b, sp))
 
     def time_q(supplied):
-        for i in range(5):
-            qstep(i, supplied)
+        cnt = [0]
+
+        def one():
+            qstep(cnt[0], supplied)
+            cnt[0] += 1
+        _warm(one, stream, max_calls=1000)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
