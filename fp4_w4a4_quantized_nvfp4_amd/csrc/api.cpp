@@ -54,6 +54,10 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 hipStream_t S(void* s) { return (hipStream_t)s; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+// channels of a quantized tensor / the GEMM reduction length: the kernels
+// address a tile's rows with 32-bit offsets (a 40-row window of x, a 256-row
+// tile of codes)
+constexpr int64_t kMaxCols = (int64_t)1 << 24;
 
 int32_t round_up32(int32_t k) { return (k + 31) & ~31; }
 
@@ -77,9 +81,10 @@ static q4_status_t quantize_common(bool mx, const uint16_t* x, int64_t rows, int
                                    int32_t* chan_idx, void* ws, size_t ws_bytes, void* stream,
                                    const char* fn) {
   const int blk = mx ? 32 : 16;
-  if (rows < 0 || cols <= 0 || cols % blk != 0 || rows >= kMaxDim || cols >= kMaxDim)
-    return fail(Q4_ESHAPE, "%s: need rows >= 0 and cols > 0 with cols %% %d == 0 (got %lld x %lld)",
-                fn, blk, (long long)rows, (long long)cols);
+  if (rows < 0 || cols <= 0 || cols % blk != 0 || rows >= kMaxDim || cols > kMaxCols)
+    return fail(Q4_ESHAPE,
+                "%s: need rows >= 0 and 0 < cols <= 2^24 with cols %% %d == 0 (got %lld x %lld)", fn,
+                blk, (long long)rows, (long long)cols);
   if (topk < 0 || topk > cols || topk > Q4_MAX_TOPK)
     return fail(Q4_EINVAL, "%s: topk %d outside [0, min(cols, %d)]", fn, topk, Q4_MAX_TOPK);
   if (rows > 0) {
@@ -160,9 +165,10 @@ q4_status_t nvfp4_quantize_noalloc(const uint16_t* x, int64_t rows, int64_t cols
                                    float* tensor_scale_out, double* chan_score, int32_t topk,
                                    int32_t* chan_idx, void* stream) {
   const char* fn = "nvfp4_quantize_noalloc";
-  if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows >= kMaxDim || cols >= kMaxDim)
-    return fail(Q4_ESHAPE, "%s: need rows >= 0 and cols > 0 with cols %% 16 == 0 (got %lld x %lld)",
-                fn, (long long)rows, (long long)cols);
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows >= kMaxDim || cols > kMaxCols)
+    return fail(Q4_ESHAPE,
+                "%s: need rows >= 0 and 0 < cols <= 2^24 with cols %% 16 == 0 (got %lld x %lld)", fn,
+                (long long)rows, (long long)cols);
   const size_t need = quantize_workspace_bytes(rows, cols);
   if (need > kNoAllocScratchBytes)
     return fail(Q4_EWORKSPACE,
@@ -196,8 +202,8 @@ q4_status_t nvfp4_qdq(const uint16_t* x, int64_t rows, int64_t cols, const float
                       void* y, int32_t y_dtype, float* tensor_scale_out, void* workspace,
                       size_t workspace_bytes, void* stream) {
   const char* fn = "nvfp4_qdq";
-  if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows >= kMaxDim || cols >= kMaxDim)
-    return fail(Q4_ESHAPE, "%s: need rows >= 0 and cols > 0 with cols %% 16 == 0", fn);
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows >= kMaxDim || cols > kMaxCols)
+    return fail(Q4_ESHAPE, "%s: need rows >= 0 and 0 < cols <= 2^24 with cols %% 16 == 0", fn);
   if (y_dtype != Q4_OUT_F32 && y_dtype != Q4_OUT_BF16) return fail(Q4_EINVAL, "%s: bad y_dtype", fn);
   if (rows > 0) {
     Q4_REQUIRE_PTR(y);
@@ -287,9 +293,10 @@ static q4_status_t check_gemm(const char* fn, int32_t fmt, int64_t M, int64_t N,
                               const uint8_t* w_codes, const uint8_t* w_scales, const float* w_ts,
                               void* Y, int32_t y_dtype) {
   if (fmt != Q4_NVFP4 && fmt != Q4_MXFP4) return fail(Q4_EINVAL, "%s: bad format %d", fn, fmt);
-  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
-    return fail(Q4_ESHAPE, "%s: need M, N >= 0 and K > 0 with K %% 32 == 0 (got %lld, %lld, %lld)",
-                fn, (long long)M, (long long)N, (long long)K);
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0 || M >= kMaxDim || N >= kMaxDim || K > kMaxCols)
+    return fail(Q4_ESHAPE,
+                "%s: need M, N >= 0 and 0 < K <= 2^24 with K %% 32 == 0 (got %lld, %lld, %lld)", fn,
+                (long long)M, (long long)N, (long long)K);
   if (y_dtype != Q4_OUT_F32 && y_dtype != Q4_OUT_BF16) return fail(Q4_EINVAL, "%s: bad y_dtype", fn);
   if (M > 0 && N > 0) {
     Q4_REQUIRE_PTR(a_codes);
@@ -391,8 +398,8 @@ q4_status_t rac_gemm(int32_t fmt, int64_t M, int64_t N, int64_t K, const uint16_
   // the workspace has room for them
   uint8_t* ta = nullptr;
   uint8_t* tw = nullptr;
-  if (!mx && K % 128 == 0 && M >= 512 && N >= 512 && workspace &&
-      ((uintptr_t)workspace & 15u) == 0 &&
+  if (!mx && K % 128 == 0 && M >= 512 && N >= 512 && records_fit(M, K) && records_fit(N, K) &&
+      workspace && ((uintptr_t)workspace & 15u) == 0 &&
       workspace_bytes >= rac_bytes + scale_tiles_bytes(M, N, K)) {
     ta = (uint8_t*)workspace + rac_bytes;
     tw = ta + align256((size_t)tile_rows_pad(M) * (size_t)(K / 128) * 16);
@@ -491,7 +498,7 @@ q4_status_t rac_gemm_eq21(int64_t M, int64_t N, int64_t K, const uint16_t* x,
   float* r_ts = (float*)((uint8_t*)slots + align256((size_t)kEq21MaxSlots * 4));
   uint8_t* ta = nullptr;
   uint8_t* tw = nullptr;
-  if (K % 128 == 0 && M >= 512 && N >= 512) {
+  if (K % 128 == 0 && M >= 512 && N >= 512 && records_fit(M, K) && records_fit(N, K)) {
     ta = (uint8_t*)r_ts + 256;
     tw = ta + align256((size_t)tile_rows_pad(M) * (size_t)(K / 128) * 16);
     g.a_scales_t = ta;
@@ -675,8 +682,10 @@ MoeLayout moe_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F, in
   // NVFP4 prefill shapes whose grouped GEMMs can read tiled scale records
   // (256 x 256 tiles: K % 128 == 0, K >= 512, N % 256 == 0)
   const bool grouped_big = !mx && !moe_skinny(T, E, topk);
-  L.tiled13 = grouped_big && H % 128 == 0 && H >= 512 && (2 * (int64_t)F) % 256 == 0;
-  L.tiled2 = grouped_big && F % 128 == 0 && F >= 512 && H % 256 == 0;
+  L.tiled13 = grouped_big && H % 128 == 0 && H >= 512 && (2 * (int64_t)F) % 256 == 0 &&
+              records_fit(R, H) && records_fit(2 * (int64_t)F, H);
+  L.tiled2 = grouped_big && F % 128 == 0 && F >= 512 && H % 256 == 0 && records_fit(R, F) &&
+             records_fit(H, F);
   L.rows_pad = tile_rows_pad(R);
   L.x_rec = L.tiled13 ? take((size_t)(H / 128) * L.rows_pad * 16) : 0;
   L.h_rec = L.tiled2 ? take((size_t)(F / 128) * L.rows_pad * 16) : 0;
@@ -719,8 +728,8 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   if (T < 0 || T * 16 >= kMaxDim) return fail(Q4_ESHAPE, "%s: bad T", fn);
   if (E < 1 || E > 1024) return fail(Q4_ESHAPE, "%s: need 1 <= E <= 1024", fn);
   if (topk < 1 || topk > E || topk > 16) return fail(Q4_EINVAL, "%s: need 1 <= topk <= min(E, 16)", fn);
-  if (H <= 0 || H % 32 || F <= 0 || F % 32)
-    return fail(Q4_ESHAPE, "%s: need H %% 32 == 0 and F %% 32 == 0 (got H %d, F %d)", fn, H, F);
+  if (H <= 0 || H % 32 || F <= 0 || F % 32 || H > kMaxCols || F > kMaxCols)
+    return fail(Q4_ESHAPE, "%s: need 0 < H, F <= 2^24, multiples of 32 (got H %d, F %d)", fn, H, F);
   if ((int64_t)E * 2 * F >= kMaxDim || (int64_t)E * H >= kMaxDim) return fail(Q4_ESHAPE, "%s: too many weight rows", fn);
   if (rac_k < 0 || rac_k > F || rac_k > H || rac_k > Q4_MAX_TOPK)
     return fail(Q4_EINVAL, "%s: rac_k %d outside [0, min(H, F, %d)]", fn, rac_k, Q4_MAX_TOPK);

@@ -16,6 +16,7 @@
 //
 // Tiles: 256 x 128 per workgroup of four waves (2 x 2), 128 x 64 per wave
 // (4 x 2 MFMA 32x32 tiles), K chunks of 128 double-buffered in LDS.
+#include <algorithm>
 #include <type_traits>
 
 #include "q4_internal.h"
@@ -1337,8 +1338,17 @@ hipError_t launch_t(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
 
 }  // namespace
 
+// Grouped 256 x 256 tiles address A (codes, scales) and R rows absolutely,
+// from the start of the operand, with 32-bit offsets: at most 4 GiB of them
+static bool grouped_offsets_fit(const GemmArgs& g) {
+  const int64_t rows = g.a_src_rows > 0 ? g.a_src_rows : g.M;
+  const int64_t row_bytes = std::max<int64_t>(g.K / 2, g.r_res ? 2 * (int64_t)g.ld_r : 0);
+  return rows * row_bytes <= (int64_t)0xffffffffLL;
+}
+
 bool grouped_big_path(const GemmArgs& g) {
   if (g.mx || g.tiles == nullptr || (g.K % BK) != 0 || g.N % big::BN != 0) return false;
+  if (!grouped_offsets_fit(g)) return false;
   return (g.a_scales_t && g.w_scales_t) ? g.K >= 512 : g.K >= 1024;
 }
 
@@ -1348,7 +1358,7 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
   // MXFP4 grouped: the 256 x 256 tiles win from K = 512 on (no decode, so a
   // tile's fixed cost is smaller than on the NVFP4 path, which keeps its
   // 256 x 128 tiles below K = 1024)
-  if (g.mx && grouped && fullk && g.N % big::BN == 0 && g.K >= 512) {
+  if (g.mx && grouped && fullk && g.N % big::BN == 0 && g.K >= 512 && grouped_offsets_fit(g)) {
     const int64_t nb = (max_mtiles * (g.N / big::BN) + 7) / 8 * 8;
     if (nb == 0) return hipSuccess;
     if (g.epilogue == kEpiSwiGLU)
@@ -1394,7 +1404,8 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
   // The grid covers every possible tile, rounded up to whole XCD rounds;
   // workgroups past the tiles that exist return at once.
   if (g.epilogue == kEpiSwiGLUQuant && !grouped_big_path(g)) return hipErrorInvalidValue;
-  if (grouped && fullk && g.N % big::BN == 0 && g.a_scales_t && g.w_scales_t && g.K >= 512) {
+  if (grouped && fullk && g.N % big::BN == 0 && g.a_scales_t && g.w_scales_t && g.K >= 512 &&
+      grouped_offsets_fit(g)) {
     const int64_t nb = (max_mtiles * (g.N / big::BN) + 7) / 8 * 8;
     if (nb == 0) return hipSuccess;
     if (g.epilogue == kEpiSwiGLUQuant)
@@ -1408,7 +1419,7 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
                          dim3(256), 0, stream, g);
     return hipGetLastError();
   }
-  if (grouped && fullk && g.N % big::BN == 0 && g.K >= 1024) {
+  if (grouped && fullk && g.N % big::BN == 0 && g.K >= 1024 && grouped_offsets_fit(g)) {
     const int64_t nb = (max_mtiles * (g.N / big::BN) + 7) / 8 * 8;
     if (nb == 0) return hipSuccess;
     if (g.epilogue == kEpiSwiGLUQuant)

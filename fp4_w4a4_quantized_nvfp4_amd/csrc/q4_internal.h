@@ -124,6 +124,12 @@ hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t s
 hipError_t launch_scale_tile(const uint8_t* scales, int64_t rows, int32_t K, int64_t rows_pad,
                              uint8_t* out, hipStream_t stream);
 inline int64_t tile_rows_pad(int64_t rows) { return (rows + 255) / 256 * 256; }
+// The 256 x 256 kernel addresses its operands through buffer resources with
+// 32-bit offsets: tiled scale records of an operand of `rows` rows fit when
+// all K / 128 chunks of them (16 bytes per padded row) span at most 4 GiB
+inline bool records_fit(int64_t rows, int64_t K) {
+  return tile_rows_pad(rows) * (K / 128) * 16 <= (int64_t)0xffffffffLL;
+}
 // records of `batch` operands [rows][K / 16]: [batch][K / 128][rows_pad][16 B]
 hipError_t launch_scale_tile_batched(const uint8_t* scales, int64_t batch, int64_t rows, int32_t K,
                                      int64_t rows_pad, uint8_t* out, hipStream_t stream);

@@ -353,7 +353,11 @@ __device__ __forceinline__ void skinny_tail_direct(const GemmArgs& g, f32x16v (&
   }
 }
 
-bool skinny_lds_path(const GemmArgs& g) { return g.mx ? g.K % 128 == 0 : g.K % 64 == 0; }
+// (the LDS kernels keep each weight row's offset from the expert's first row
+// in 32 bits)
+bool skinny_lds_path(const GemmArgs& g) {
+  return (g.mx ? g.K % 128 == 0 : g.K % 64 == 0) && g.N * (int64_t)(g.K / 2) <= 0xffffffffLL;
+}
 static_assert(2 * 8 * SKD_BLOCK <= 20736, "direct compensation regions exceed a stage");
 
 // WREC (K % 128 == 0): the weight scales come from their records
@@ -646,7 +650,7 @@ __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs g) {
 }  // namespace
 
 bool skinny_direct_ok(bool mx, int64_t K, int64_t N) {
-  return (mx ? K % 128 == 0 : K % 64 == 0) && N % 8 == 0;
+  return (mx ? K % 128 == 0 : K % 64 == 0) && N * (K / 2) <= 0xffffffffLL && N % 8 == 0;
 }
 
 hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t stream) {
@@ -657,7 +661,7 @@ hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t 
   const int64_t nb = max_tiles * nbn;
   if (nb == 0) return hipSuccess;
   const dim3 grid((unsigned)nb), block(256);
-  if (g.w_scales_t && g.K % 128 == 0) {
+  if (g.w_scales_t && g.K % 128 == 0 && skinny_lds_path(g)) {
     if (g.mx) {
       if (g.epilogue == kEpiSwiGLU)
         hipLaunchKernelGGL((gemm_skinny_lds_kernel<true, kEpiSwiGLU, true>), grid, block, 0, stream, g);

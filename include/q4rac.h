@@ -14,6 +14,15 @@
  * synchronisation.  Calls are stateless and thread-safe when they use distinct
  * workspaces and outputs.
  *
+ * Sizes: rows, M, N and T * topk below 2^31; channels of a quantized tensor and
+ * the GEMM reduction length K (MoE: H and F) at most 2^24 (larger ones are
+ * refused with Q4_ESHAPE).  Within those limits every shape runs; the fastest
+ * kernels address a tile's operands with 32-bit offsets and are used only
+ * where those fit (tiled scale records of at most 4 GiB per operand, a
+ * gathered MoE activation operand of at most 4 GiB, an expert weight matrix
+ * of at most 4 GiB of codes), other shapes run on kernels with 64-bit
+ * addressing and give the same results.
+ *
  * Alignment: tensor scales, logits, routing weights and index arrays need 4-byte
  * alignment, channel scores 8-byte; every other device pointer (activations,
  * codes, scales, outputs, workspaces) must be 16-byte aligned.  Inputs must be

@@ -47,6 +47,18 @@ def test_shape_and_pointer_errors(L):
     assert "cols % 16" in _err(L)
     # topk beyond cols
     assert L.nvfp4_quantize(fake, 4, 32, None, fake, fake, fake, None, 33, fake, fake, 1 << 30, None) == 1
+    # channels beyond 2^24 (quantizers, weight QDQ), K beyond 2^24 (GEMMs, MoE H and F)
+    big = (1 << 24) + 32
+    assert L.nvfp4_quantize(fake, 4, big, None, fake, fake, fake, None, 0, None, fake, 1 << 40, None) == 2
+    assert "2^24" in _err(L)
+    assert L.nvfp4_quantize(fake, 4, 1 << 24, None, fake, fake, fake, None, 0, None, fake, 8, None) == 4
+    assert L.mxfp4_quantize(fake, 4, big, fake, fake, None, 0, None, fake, 1 << 40, None) == 2
+    assert L.nvfp4_quantize_noalloc(fake, 4, big, None, fake, fake, fake, None, 0, None, None) == 2
+    assert L.nvfp4_qdq(fake, 4, big, None, fake, 0, fake, fake, 1 << 40, None) == 2
+    assert L.w4a4_gemm(0, 8, 8, big, fake, fake, fake, fake, fake, fake, fake, 0, None) == 2
+    assert L.moe_w4a4_grouped_gemm(0, fake, 4, big, fake, fake, 2, 4, 64, fake, fake, fake, fake,
+                                   fake, fake, fake, fake, None, None, None, 0, fake, 1, fake,
+                                   1 << 40, None, None) == 2
     # misaligned input
     assert L.nvfp4_quantize(odd, 4, 32, None, fake, fake, fake, None, 0, None, fake, 1 << 30, None) == 3
     # workspace too small

@@ -135,7 +135,14 @@ def _check_site(fmt, xb, got, prefix, rac_k, ts=None):
                                             # K % 64 != 0 (NVFP4) or K % 128 != 0
                                             # (MXFP4) falls back to the gathered W_S
                                             (48, 512, 8, 160, 2, 100),
-                                            (40, 256, 8, 192, 2, 70)])
+                                            (40, 256, 8, 192, 2, 70),
+                                            # degenerate routing: one expert (every
+                                            # token's single slot) on the streaming
+                                            # and on the 256 x 256 kernels; every
+                                            # expert in every token's top-k
+                                            (37, 256, 1, 128, 1, 16),
+                                            (600, 512, 1, 512, 1, 32),
+                                            (50, 256, 4, 128, 4, 16)])
 def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
     say(f"moe small fmt={fmt} T={T} H={H} E={E} F={F} topk={topk} k={k}")
     m = q4()
@@ -163,6 +170,24 @@ def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
     say(f"  W2 out rel err {err_o:.2e}")
     assert err_o <= GEMM_TOL
     check_bf16_output(got["Y"], ref["y"], tol=2 * GEMM_TOL)
+
+
+@pytest.mark.parametrize("fmt", [0, 1], ids=["nvfp4", "mxfp4"])
+def test_empty_token_batch(fmt):
+    """T = 0: the layer runs, writes nothing and reports no error."""
+    m = q4()
+    E, H, F, topk, k = 4, 256, 128, 2, 16
+    rng = np.random.default_rng(9)
+    w13 = _bits((rng.standard_normal((E, 2 * F, H)) * 0.05).astype(np.float32))
+    w2 = _bits((rng.standard_normal((E, H, F)) * 0.05).astype(np.float32))
+    experts = m.prepare_moe_weights(dev(w13), dev(w2), fmt=fmt)
+    x = torch.empty((0, H), dtype=torch.int16, device="cuda")
+    idx = torch.empty((0, topk), dtype=torch.int32, device="cuda")
+    p = torch.empty((0, topk), dtype=torch.float32, device="cuda")
+    st = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    Y, _ = m.moe_w4a4_grouped_gemm(x, idx, p, experts, k, out_dtype=m.OUT_BF16, status=st)
+    torch.cuda.synchronize()
+    assert tuple(Y.shape) == (0, H) and int(host(st)[0]) == 0
 
 
 @pytest.mark.parametrize("T,H,E,F,topk,k", [(600, 512, 4, 512, 2, 32),      # records at both sites
