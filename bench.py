@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 # WRITE_SIZE (KiB per dispatch, taken on the kernel source with this sha256)
 # scaled by the factors a plain 1 GiB copy gives (fetch x 2.00, write x 1.00);
 # any change to that source makes the record stale, and the line reports null
-TRAFFIC = {"gemm_src_sha256": "61a445ba82f030809d5564e445bd255071ee53bcb37f56243cb9d1a445687bc1",
-           "fetch_kib": 240888.7, "fetch_scale": 2.0, "write_kib": 234752.0, "write_scale": 1.0}
+TRAFFIC = {"gemm_src_sha256": "c2bccc2a2829fdfa64ad139e46fb01b79d9ab5774c3cce9acad62e0c4b9488b1",
+           "fetch_kib": 240862.0, "fetch_scale": 2.0, "write_kib": 234752.0, "write_scale": 1.0}
 
 
 def _args():
