@@ -424,21 +424,21 @@ def _quantize_stacked(fmt, w, stream=None):
 
 def q4_scale_records(scales, K, fmt=NVFP4, stream=None):
     """Scale records of stacked scales uint8 [batch, rows, K/16] (NVFP4) or
-    [batch, rows, K/32] (MXFP4), K % 128 == 0: uint8 [batch, K/128, rows_pad,
-    16] (fp16 records) or [batch, K/128, rows_pad, 4] (E8M0 bytes), rows_pad =
-    rows rounded up to 256."""
+    [batch, rows, K/32] (MXFP4), K % 128 == 0, as one flat uint8 buffer:
+    NVFP4 [batch, K/128, rows_pad, 16] fp16 records followed by [batch, K/128,
+    rows_pad, 8] raw E4M3 records; MXFP4 [batch, K/128, rows_pad, 4] E8M0
+    bytes; rows_pad = rows rounded up to 256."""
     with _on(stream):
         if scales.dim() != 3:
             raise ValueError("q4rac: scales must be [batch, rows, K/16 or K/32]")
         b, rows = scales.shape[0], scales.shape[1]
-        blk, rec = (16, 16) if fmt == NVFP4 else (32, 4)
+        blk = 16 if fmt == NVFP4 else 32
         _ptr(scales, torch.uint8, (b, rows, K // blk), "scales")
         L = lib()
         n = L.q4_scale_records_size(fmt, b, rows, K)
         if n == 0:
             raise Q4Error(f"q4_scale_records: K = {K} is not a positive multiple of 128")
-        pad = (rows + 255) // 256 * 256
-        out = _empty((b, K // 128, pad, rec), torch.uint8, scales.device)
+        out = _empty((n,), torch.uint8, scales.device)
         _check(L.q4_scale_records(fmt, _ptr(scales), b, rows, K, _ptr(out), n, _stream(stream)))
         return out
 
@@ -496,14 +496,13 @@ def moe_w4a4_grouped_gemm(tokens, topk_idx, topk_w, experts, rac_k, out_dtype=OU
             _ptr(w13["tensor_scale"], torch.float32, (E,), "w13 tensor_scale")
             _ptr(w2["tensor_scale"], torch.float32, (E,), "w2 tensor_scale")
         rec13 = rec2 = None
-        rsz = 16 if fmt == NVFP4 else 4
+        L = lib()
         if w13.get("scale_records") is not None:
             rec13 = _ptr(w13["scale_records"], torch.uint8,
-                         (E, H // 128, (2 * F + 255) // 256 * 256, rsz), "w13 scale_records")
+                         (L.q4_scale_records_size(fmt, E, 2 * F, H),), "w13 scale_records")
         if w2.get("scale_records") is not None:
             rec2 = _ptr(w2["scale_records"], torch.uint8,
-                        (E, F // 128, (H + 255) // 256 * 256, rsz), "w2 scale_records")
-        L = lib()
+                        (L.q4_scale_records_size(fmt, E, H, F),), "w2 scale_records")
         wsb = L.moe_workspace_size(fmt, T, E, H, F, topk, rac_k)
         if workspace is None or workspace.numel() < wsb:
             workspace = _empty((max(wsb, 1),), torch.uint8, tokens.device)

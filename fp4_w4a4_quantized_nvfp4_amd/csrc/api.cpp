@@ -66,7 +66,7 @@ int32_t round_up32(int32_t k) { return (k + 31) & ~31; }
 extern "C" {
 
 const char* q4_last_error(void) { return g_err; }
-int32_t q4_version(void) { return 103; }
+int32_t q4_version(void) { return 104; }
 
 // ======================================================================== quantize
 size_t q4_quantize_workspace_size(int64_t rows, int64_t cols, int32_t fmt) {
@@ -605,7 +605,13 @@ size_t q4_scale_records_size(int32_t fmt, int64_t batch, int64_t rows, int64_t K
   if ((fmt != Q4_NVFP4 && fmt != Q4_MXFP4) || batch < 0 || rows < 0 || K <= 0 || K % 128 ||
       rows >= kMaxDim || K >= kMaxDim)
     return 0;
-  return (size_t)batch * (size_t)(K / 128) * (size_t)tile_rows_pad(rows) * (fmt == Q4_MXFP4 ? 4 : 16);
+  // NVFP4: the fp16 records (16 B) followed by the raw E4M3 records (8 B)
+  return (size_t)batch * (size_t)(K / 128) * (size_t)tile_rows_pad(rows) * (fmt == Q4_MXFP4 ? 4 : 24);
+}
+
+// bytes of the fp16 part of an NVFP4 record buffer (the E4M3 part follows)
+static size_t fp16_records_bytes(int64_t batch, int64_t rows, int64_t K) {
+  return (size_t)batch * (size_t)(K / 128) * (size_t)tile_rows_pad(rows) * 16;
 }
 
 q4_status_t q4_scale_records(int32_t fmt, const uint8_t* scales, int64_t batch, int64_t rows,
@@ -623,8 +629,12 @@ q4_status_t q4_scale_records(int32_t fmt, const uint8_t* scales, int64_t batch, 
   if (fmt == Q4_MXFP4)
     return hip_status(launch_mx_scale_records(scales, batch, rows, (int32_t)K, tile_rows_pad(rows),
                                               out, S(stream)), fn);
-  return hip_status(launch_scale_tile_batched(scales, batch, rows, (int32_t)K, tile_rows_pad(rows),
-                                              out, S(stream)), fn);
+  hipError_t e = launch_scale_tile_batched(scales, batch, rows, (int32_t)K, tile_rows_pad(rows), out,
+                                           S(stream));
+  if (e == hipSuccess)
+    e = launch_e4m3_scale_records(scales, batch, rows, (int32_t)K, tile_rows_pad(rows),
+                                  out + fp16_records_bytes(batch, rows, K), S(stream));
+  return hip_status(e, fn);
 }
 
 // workspace fields of the grouped expert layer
@@ -861,9 +871,13 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
     g.a_rows_pad = L.rows_pad;
     g.w_rows_pad = tile_rows_pad(2 * (int64_t)F);
   } else if (skinny && w13_scale_records && H % 128 == 0) {
-    // decode-shaped: the skinny kernel streams the weights' fp16 scale records
-    g.w_scales_t = w13_scale_records;
+    // decode-shaped: the streaming kernel reads the weights' scale records,
+    // NVFP4 the raw E4M3 part (half the bytes of the fp16 records)
     g.w_rows_pad = tile_rows_pad(2 * (int64_t)F);
+    if (mx)
+      g.w_scales_t = w13_scale_records;
+    else
+      g.w_rec8 = w13_scale_records + fp16_records_bytes(E, 2 * (int64_t)F, H);
   }
   // ---- activation site 2: h (sorted rows)
   uint8_t* hc = (uint8_t*)P(L.off[8]);
@@ -938,8 +952,11 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
     g2.a_rows_pad = L.rows_pad;
     g2.w_rows_pad = tile_rows_pad(H);
   } else if (skinny && w2_scale_records && F % 128 == 0) {
-    g2.w_scales_t = w2_scale_records;
     g2.w_rows_pad = tile_rows_pad(H);
+    if (mx)
+      g2.w_scales_t = w2_scale_records;
+    else
+      g2.w_rec8 = w2_scale_records + fp16_records_bytes(E, H, F);
   }
   Q4_TRY(grouped_gemm(g2), "moe w2 gemm");
   Q4_TRY(launch_moe_combine((const float*)P(L.off[13]), inv, topk_w, topk_idx, E, T, topk, H, Y,

@@ -113,6 +113,10 @@ struct GemmArgs {
   int64_t w_hi_batch;
   const int32_t* sel;
   int32_t sel_k;
+  // optional raw E4M3 scale records of the weights for the streaming kernel
+  // (NVFP4, K % 128 == 0): [E][K/128][w_rows_pad][8 B], record (c, r) the
+  // scale bytes of row r's blocks 8 c .. 8 c + 7 (launch_e4m3_scale_records)
+  const uint8_t* w_rec8;
 };
 
 // whether a grouped GEMM runs on the 256 x 256 kernel (the one with the
@@ -185,6 +189,10 @@ hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const f
 // grouped GEMM over tiles of at most kSkinnyBM rows (few rows per expert)
 constexpr int kSkinnyBM = 32;
 hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t stream);
+// raw E4M3 scale records of `batch` NVFP4 operands [rows][K / 16]:
+// [batch][K / 128][rows_pad][8 B] (rows past `rows` zero)
+hipError_t launch_e4m3_scale_records(const uint8_t* scales, int64_t batch, int64_t rows, int32_t K,
+                                     int64_t rows_pad, uint8_t* out, hipStream_t stream);
 // whether launch_skinny_gemm runs a kernel that can read the compensation
 // columns directly (GemmArgs::w_hi_t)
 bool skinny_direct_ok(bool mx, int64_t K, int64_t N);

@@ -16,6 +16,8 @@
 // with their E8M0 block scales.  Lane (row l % 32, half h) supplies, for
 // K-step (s2, j), word j of the 16-byte piece 2 h + s2 of its row's 64-byte
 // chunk, the same K order for both operands.
+#include <algorithm>
+
 #include "q4_internal.h"
 
 namespace q4 {
@@ -360,17 +362,20 @@ bool skinny_lds_path(const GemmArgs& g) {
 }
 static_assert(2 * 8 * SKD_BLOCK <= 20736, "direct compensation regions exceed a stage");
 
-// WREC (K % 128 == 0): the weight scales come from their records
-// (g.w_scales_t, [E][K / 128][w_rows_pad][record]): NVFP4 the tiled fp16
+// WREC (K % 128 == 0): the weight scales come from records, [E][K / 128]
+// [w_rows_pad][record], so that a wave's 64 rows of one chunk are one
+// contiguous, coalesced piece.  WREC 1 (g.w_scales_t): NVFP4 the tiled fp16
 // records (16 B, swizzled by row, already widened to fp16), MXFP4 the four
-// E8M0 bytes of the chunk (4 B); a wave's 64 rows of one chunk are one
-// contiguous, coalesced load.
-template <bool MX, int EPI, bool WREC = false>
+// E8M0 bytes of the chunk (4 B).  WREC 2 (g.w_rec8, NVFP4): the raw E4M3
+// bytes of the chunk (8 B; half the bytes of the fp16 records, widened in
+// the decode like raw scales).
+template <bool MX, int EPI, int WREC = 0>
 __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs g) {
-  constexpr int DMA = MX ? 6 : (WREC ? 6 : 7);   // global -> LDS loads per wave per chunk
-  constexpr bool FP16REC = WREC && !MX;           // fp16 records in a 1 KB region
+  static_assert(WREC != 2 || !MX, "E4M3 records are NVFP4");
+  constexpr int DMA = MX ? 6 : (WREC == 1 ? 6 : 7);   // global -> LDS loads per wave per chunk
+  constexpr bool FP16REC = WREC == 1 && !MX;           // fp16 records in a 1 KB region
   constexpr int SWR = SWREGION<FP16REC>, SAC = SA_CODE<FP16REC>, SAS = SA_SC<FP16REC>;
-  constexpr int REC_SHIFT = MX ? 2 : 4;           // log2 of the record size
+  constexpr int REC_SHIFT = MX ? 2 : (WREC == 2 ? 3 : 4);   // log2 of the record size
   __shared__ __attribute__((aligned(16))) uint8_t st0[SSTAGE<FP16REC>];
   __shared__ __attribute__((aligned(16))) uint8_t st1[SSTAGE<FP16REC>];
   __shared__ __attribute__((aligned(16))) uint8_t st2[SSTAGE<FP16REC>];
@@ -414,8 +419,10 @@ __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs g) {
   // WREC: this wave's 64 records of chunk 0 (rows c0 .. c0 + 63 exist in the
   // padded record block even past N)
   const uint8_t* wrec = nullptr;
-  if constexpr (WREC)
+  if constexpr (WREC == 1)
     wrec = g.w_scales_t + (((int64_t)e * nk * g.w_rows_pad + c0 + lane) << REC_SHIFT);
+  else if constexpr (WREC == 2)   // lane l loads dword l % 2 of row c0 + l / 2 (rows 0..31)
+    wrec = g.w_rec8 + (((int64_t)e * nk * g.w_rows_pad + c0) << REC_SHIFT) + 4 * lane;
   if constexpr (MX) {
     wsrc[0] = wsb + wrow(lane) * sstride;
     wsrc[1] = wsrc[0];
@@ -444,10 +451,18 @@ __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs g) {
       __builtin_amdgcn_global_load_lds((sk_gptr_t)(wcb + wco[it] + k0 / 2 + 16 * pc),
                                        (sk_lptr_t)(base + SW_CODE + it * 1024), 16, 0, 0);
     }
-    if constexpr (WREC && MX) {
+    if constexpr (WREC == 1 && MX) {
       __builtin_amdgcn_global_load_lds(
           (sk_gptr_t)(wrec + ((int64_t)cc * g.w_rows_pad << REC_SHIFT)), (sk_lptr_t)(base + SW_SC),
           4, 0, 0);
+    } else if constexpr (WREC == 2) {
+      // rows 0..31, then rows 32..63: 256 contiguous bytes each, the raw
+      // scales' LDS layout (8 bytes per row)
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+        __builtin_amdgcn_global_load_lds(
+            (sk_gptr_t)(wrec + ((int64_t)cc * g.w_rows_pad << REC_SHIFT) + 256 * it),
+            (sk_lptr_t)(base + SW_SC + it * 256), 4, 0, 0);
     } else if constexpr (WREC) {
       __builtin_amdgcn_global_load_lds(
           (sk_gptr_t)(wrec + ((int64_t)cc * g.w_rows_pad << REC_SHIFT)), (sk_lptr_t)(base + SW_SC),
@@ -647,7 +662,33 @@ __global__ __launch_bounds__(256, 2) void gemm_skinny_lds_kernel(GemmArgs g) {
   }
 }
 
+// raw E4M3 scale records: out[b][c][r] = the 8 scale bytes of row r's
+// blocks 8 c .. 8 c + 7 (zero past `rows`); one 8-byte record per thread
+__global__ __launch_bounds__(256) void e4m3_scale_records_kernel(const uint8_t* __restrict__ sc,
+                                                                 int64_t batch, int64_t rows,
+                                                                 int32_t K, int64_t rows_pad,
+                                                                 uint2* __restrict__ out) {
+  const int64_t nk = K / 128, per = nk * rows_pad;
+  const int64_t total = batch * per;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * 256) {
+    const int64_t b = i / per, rem = i - b * per;
+    const int64_t c = rem / rows_pad, r = rem - c * rows_pad;
+    out[i] = r < rows ? *(const uint2*)(sc + (b * rows + r) * (K / 16) + 8 * c) : make_uint2(0, 0);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_e4m3_scale_records(const uint8_t* scales, int64_t batch, int64_t rows, int32_t K,
+                                     int64_t rows_pad, uint8_t* out, hipStream_t stream) {
+  const int64_t total = batch * (K / 128) * rows_pad;
+  if (total == 0) return hipSuccess;
+  const int64_t nb = std::min<int64_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(e4m3_scale_records_kernel, dim3((unsigned)nb), dim3(256), 0, stream, scales,
+                     batch, rows, K, rows_pad, (uint2*)out);
+  return hipGetLastError();
+}
 
 bool skinny_direct_ok(bool mx, int64_t K, int64_t N) {
   return (mx ? K % 128 == 0 : K % 64 == 0) && N * (K / 2) <= 0xffffffffLL && N % 8 == 0;
@@ -661,17 +702,24 @@ hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t 
   const int64_t nb = max_tiles * nbn;
   if (nb == 0) return hipSuccess;
   const dim3 grid((unsigned)nb), block(256);
+  if (!g.mx && g.w_rec8 && g.K % 128 == 0 && skinny_lds_path(g)) {
+    if (g.epilogue == kEpiSwiGLU)
+      hipLaunchKernelGGL((gemm_skinny_lds_kernel<false, kEpiSwiGLU, 2>), grid, block, 0, stream, g);
+    else
+      hipLaunchKernelGGL((gemm_skinny_lds_kernel<false, kEpiStore, 2>), grid, block, 0, stream, g);
+    return hipGetLastError();
+  }
   if (g.w_scales_t && g.K % 128 == 0 && skinny_lds_path(g)) {
     if (g.mx) {
       if (g.epilogue == kEpiSwiGLU)
-        hipLaunchKernelGGL((gemm_skinny_lds_kernel<true, kEpiSwiGLU, true>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<true, kEpiSwiGLU, 1>), grid, block, 0, stream, g);
       else
-        hipLaunchKernelGGL((gemm_skinny_lds_kernel<true, kEpiStore, true>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<true, kEpiStore, 1>), grid, block, 0, stream, g);
     } else {
       if (g.epilogue == kEpiSwiGLU)
-        hipLaunchKernelGGL((gemm_skinny_lds_kernel<false, kEpiSwiGLU, true>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<false, kEpiSwiGLU, 1>), grid, block, 0, stream, g);
       else
-        hipLaunchKernelGGL((gemm_skinny_lds_kernel<false, kEpiStore, true>), grid, block, 0, stream, g);
+        hipLaunchKernelGGL((gemm_skinny_lds_kernel<false, kEpiStore, 1>), grid, block, 0, stream, g);
     }
     return hipGetLastError();
   }

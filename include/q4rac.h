@@ -311,10 +311,14 @@ q4_status_t q4_moe_pack_w13(const uint16_t *w13, int32_t E, int32_t F, int32_t H
  * as [batch][K/128][rows_pad][record], rows_pad = rows rounded up to 256
  * (rows past `rows` zero), so that a tile's rows of one chunk are contiguous.
  *   fmt Q4_NVFP4: the E4M3 block scales (one per 16 elements, QUADS section
- *     2.2 "FP4" and the NVFP4 format pages) of operands [rows][K/16], widened
- *     to fp16 (exact, subnormal scales included): a 16-byte record holds the
- *     eight scales of one row and chunk, its four dwords in an order that
- *     spreads a tile's LDS reads over the banks.
+ *     2.2 "FP4" and the NVFP4 format pages) of operands [rows][K/16], twice:
+ *     first widened to fp16 (exact, subnormal scales included), a 16-byte
+ *     record holding the eight scales of one row and chunk with its four
+ *     dwords in an order that spreads a tile's LDS reads over the banks (read
+ *     by the 256 x 256 grouped GEMM); then as raw bytes, an 8-byte record
+ *     holding the same eight scales in block order (read by the grouped GEMM
+ *     of decode-shaped layers, which streams the weights: half the bytes).
+ *     Size batch * (K/128) * rows_pad * 24.
  *   fmt Q4_MXFP4: the E8M0 scales (one per 32 elements) of operands
  *     [rows][K/32]: a 4-byte record holds the four of one row and chunk.
  * Derived data only: a grouped GEMM given the records computes exactly what
@@ -341,8 +345,8 @@ q4_status_t q4_scale_records(int32_t fmt, const uint8_t *scales, int64_t batch, 
  *              of w2_scales (batch E, rows H, K = F), which must be those
  *              scales' records (not checked).  Where the shape allows (H and F
  *              multiples of 128; prefill-sized T * topk also needs them at
- *              least 512) the grouped GEMMs then read fp16 scales; results
- *              are the same.
+ *              least 512) the grouped GEMMs then read the records instead of
+ *              the raw scales; results are the same.
  *   h_tensor_scale: NULL, or (NVFP4 only) device fp32 [1]: h's tensor scale
  *              supplied by the caller (delayed scaling, e.g. an earlier step's
  *              s_h) instead of RN32(amax(h) / 2688).  Where the W13 GEMM runs

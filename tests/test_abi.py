@@ -109,7 +109,7 @@ def test_shape_and_pointer_errors(L):
     assert L.q4_scale_records(0, fake, 2, 64, 96, fake, 1 << 20, None) == 2
     assert L.q4_scale_records(0, fake, 2, 64, 256, fake, 100, None) == 4
     assert L.q4_scale_records(2, fake, 2, 64, 256, fake, 1 << 20, None) == 1
-    assert L.q4_scale_records_size(0, 2, 300, 256) == 2 * 2 * 512 * 16
+    assert L.q4_scale_records_size(0, 2, 300, 256) == 2 * 2 * 512 * (16 + 8)
     assert L.q4_scale_records_size(1, 2, 300, 256) == 2 * 2 * 512 * 4
     # sort: topk > 16, misaligned status
     assert L.q4_moe_sort(fake, 4, 32, 17, fake, fake, fake, 1 << 20, None, None) == 1

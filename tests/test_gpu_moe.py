@@ -247,16 +247,24 @@ def test_fused_h_quantization(T, H, E, F, topk, k):
 
 
 def test_scale_records_layout():
-    """q4_scale_records against the documented layout: record (c, r) of
-    operand b holds the E4M3 scales of row r, columns 128 c .. 128 c + 127, as
-    fp16, dword d stored at d ^ ((r / 8) % 4); rows past `rows` are zero.  The
-    expected fp16 values are the oracle's E4M3 decoding (exact in fp16)."""
+    """q4_scale_records against the documented layout.  First part: record
+    (c, r) of operand b holds the E4M3 scales of row r, columns 128 c ..
+    128 c + 127, as fp16, dword d stored at d ^ ((r / 8) % 4); the expected
+    fp16 values are the oracle's E4M3 decoding (exact in fp16).  Second part:
+    the same scales' raw bytes, 8 per record, in block order.  Rows past
+    `rows` are zero in both."""
     m = q4()
     rng = np.random.default_rng(11)
     b, rows, K = 3, 300, 384
     sc = rng.integers(0, 127, size=(b, rows, K // 16), dtype=np.uint8)   # every finite E4M3 code
-    rec = host(m.q4_scale_records(dev(sc), K)).reshape(b, K // 128, 512, 4, 4)
+    flat = host(m.q4_scale_records(dev(sc), K))
     pad = 512
+    n16 = b * (K // 128) * pad * 16
+    assert flat.size == n16 + b * (K // 128) * pad * 8
+    raw = flat[n16:].reshape(b, K // 128, pad, 8)
+    assert np.array_equal(raw[:, :, :rows], sc.reshape(b, rows, K // 128, 8).transpose(0, 2, 1, 3))
+    assert not raw[:, :, rows:].any()
+    rec = flat[:n16].reshape(b, K // 128, pad, 4, 4)
     assert rec.shape[2] == pad
     vals = rec.view(np.uint16).view(np.float16).astype(np.float64)    # [b][c][row][dword][2 halves]
     vals = vals.reshape(b, K // 128, pad, 4, 2)
@@ -290,15 +298,17 @@ def test_mx_scale_records_layout():
     rng = np.random.default_rng(13)
     b, rows, K = 2, 300, 512
     sc = rng.integers(0, 256, size=(b, rows, K // 32), dtype=np.uint8)
-    rec = host(m.q4_scale_records(dev(sc), K, fmt=m.MXFP4))
-    assert rec.shape == (b, K // 128, 512, 4)
+    rec = host(m.q4_scale_records(dev(sc), K, fmt=m.MXFP4)).reshape(b, K // 128, 512, 4)
     want = sc.reshape(b, rows, K // 128, 4).transpose(0, 2, 1, 3)
     assert np.array_equal(rec[:, :, :rows], want)
     assert not rec[:, :, rows:].any()
 
 
 @pytest.mark.parametrize("T,H,E,F,topk,k", [(600, 1024, 4, 1024, 2, 32),   # 256 x 256 tiles
-                                            (64, 1024, 16, 512, 4, 32),     # decode-shaped
+                                            # decode-shaped: the streaming kernel with
+                                            # the raw E4M3 records (NVFP4) against
+                                            # the raw scales
+                                            (64, 1024, 16, 512, 4, 32),
                                             (48, 768, 8, 384, 8, 0)])
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_scale_records_same_result(T, H, E, F, topk, k, fmt):
