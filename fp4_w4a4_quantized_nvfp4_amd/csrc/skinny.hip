@@ -324,6 +324,9 @@ __device__ __forceinline__ void skinny_tail_direct(const GemmArgs& g, f32x16v (&
   const int Kc = g.K;
   for (int t0 = 0; t0 < g.kp; t0 += 64) {
     const int nb = min(8, (g.kp - t0) >> 3);   // blocks of 8 channels this pass (4 or 8)
+    // the previous pass's LDS reads are complete before its rows are replaced
+    // (s_waitcnt lgkmcnt(0), the other counters left alone)
+    if (t0 > 0) __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i < nb) {
