@@ -539,6 +539,9 @@ static int64_t moe_max_tiles(int64_t T, int32_t E, int32_t topk) {
 static int64_t moe_max_tiles_skinny(int64_t T, int32_t E, int32_t topk) {
   return (T * topk + kSkinnyBM - 1) / kSkinnyBM + E;
 }
+static int64_t moe_max_tiles_wide(int64_t T, int32_t E, int32_t topk) {
+  return (T * topk + kWideBM - 1) / kWideBM + E;
+}
 // few rows per expert (decode-shaped): the grouped GEMMs stream the weights
 // with 32-row tiles instead of 256-row tiles
 static bool moe_skinny(int64_t T, int32_t E, int32_t topk) { return T * topk <= 64 * (int64_t)E; }
@@ -794,18 +797,33 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
     e = (call);                            \
     if (e != hipSuccess) return hip_status(e, what); \
   } while (0)
-  // the sort also writes each sorted row's token and, for decode-shaped
-  // layers, the 32-row tile table of the skinny kernel
+  // NVFP4 prefill shapes read the weights' tiled scale records when given.
+  // With them, GEMMs whose N is a multiple of 512 run on 128 x 512 tiles
+  // (half the empty rows of 256-row tiles at a few hundred rows per expert);
+  // the W13 GEMM that quantizes h in its epilogue keeps the 256-row tiles.
+  const bool rec13 = L.tiled13 && w13_scale_records, rec2 = L.tiled2 && w2_scale_records;
+  const bool wide13 = rec13 && !h_tensor_scale && grouped_wide_ok(H, 2 * (int64_t)F);
+  const bool wide2 = rec2 && grouped_wide_ok(F, H);
+  // the sort also writes each sorted row's token and a second tile table:
+  // 32-row tiles of the skinny kernel (decode-shaped layers) or 128-row
+  // tiles of the 128 x 512 kernel
   const bool skinny = moe_skinny(T, E, topk);
+  const bool table2 = skinny || wide13 || wide2;
   Q4_TRY(launch_moe_sort(topk_idx, T, E, topk, perm, offsets, inv, tiles, ntiles,
-                         (int32_t*)P(L.counts), s, a_rows, skinny ? kSkinnyBM : 0,
-                         skinny ? (int32_t*)P(L.tiles_s) : nullptr,
-                         skinny ? (int32_t*)P(L.ntiles_s) : nullptr, status), "moe sort");
+                         (int32_t*)P(L.counts), s, a_rows,
+                         skinny ? kSkinnyBM : (table2 ? kWideBM : 0),
+                         table2 ? (int32_t*)P(L.tiles_s) : nullptr,
+                         table2 ? (int32_t*)P(L.ntiles_s) : nullptr, status), "moe sort");
   auto grouped_gemm = [&](GemmArgs& gg) {
     if (skinny) {
       gg.tiles = (const int32_t*)P(L.tiles_s);
       gg.ntiles_dev = (const int32_t*)P(L.ntiles_s);
       return launch_skinny_gemm(gg, moe_max_tiles_skinny(T, E, topk), s);
+    }
+    if (gg.wide) {
+      gg.tiles = (const int32_t*)P(L.tiles_s);
+      gg.ntiles_dev = (const int32_t*)P(L.ntiles_s);
+      return launch_w4a4_gemm(gg, moe_max_tiles_wide(T, E, topk), s);
     }
     return launch_w4a4_gemm(gg, moe_max_tiles(T, E, topk), s);
   };
@@ -817,7 +835,6 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   uint16_t* xR = (uint16_t*)P(L.off[6]);
   Q4_TRY(launch_quantize(mx, tokens, T, H, nullptr, xc, xs, xts, (double*)P(L.off[14]), rac_k,
                          rac_k ? xS : nullptr, P(L.qws), s), "moe quantize tokens");
-  const bool rec13 = L.tiled13 && w13_scale_records, rec2 = L.tiled2 && w2_scale_records;
   if (rec13)
     Q4_TRY(launch_scale_tile_sorted(xs, a_rows, R, H, offsets, E, L.rows_pad, (uint8_t*)P(L.x_rec),
                                     s), "moe token scale records");
@@ -870,6 +887,7 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
     g.w_scales_t = w13_scale_records;
     g.a_rows_pad = L.rows_pad;
     g.w_rows_pad = tile_rows_pad(2 * (int64_t)F);
+    g.wide = wide13;
   } else if (skinny && w13_scale_records && H % 128 == 0) {
     // decode-shaped: the streaming kernel reads the weights' scale records,
     // NVFP4 the raw E4M3 part (half the bytes of the fp16 records)
@@ -951,6 +969,7 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
     g2.w_scales_t = w2_scale_records;
     g2.a_rows_pad = L.rows_pad;
     g2.w_rows_pad = tile_rows_pad(H);
+    g2.wide = wide2;
   } else if (skinny && w2_scale_records && F % 128 == 0) {
     g2.w_rows_pad = tile_rows_pad(H);
     if (mx)

@@ -499,15 +499,28 @@ struct Frag {
 // instantiation so the plain kernels keep their register allocation
 // MX: MXFP4 operands (E8M0 scale per 32 elements, no tensor scale) fed
 // straight from LDS to the scaled FP4 instruction, no decode (dense only)
-template <bool TILED, bool GROUPED, int EPI, bool RSC = false, bool MX = false>
+// WIDE: grouped 128 x 512 tiles (NVFP4, tiled records, store or SwiGLU
+// epilogue) for experts whose row counts leave mostly empty 256-row tiles:
+// every wave still owns a 128 x 128 block (all 128 rows, its own quarter of
+// the columns), so the per-wave work and LDS reads are those of 256 x 256
+template <bool TILED, bool GROUPED, int EPI, bool RSC = false, bool MX = false, bool WIDE = false>
 __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   static_assert(GROUPED || EPI == kEpiStore, "SwiGLU is a grouped epilogue");
   static_assert(EPI != kEpiSwiGLUQuant || !MX, "the quantizing epilogue writes NVFP4");
   static_assert(!MX || (!TILED && !RSC), "MXFP4: raw scales, no scaled compensation");
-  // MX scale area: 4 E8M0 bytes per row per chunk
-  constexpr int STAGE = big::STAGE<TILED>;
-  constexpr int B_SC_OFF = MX ? A_SC_OFF + BM * 4 : big::B_SC_OFF<TILED>;
-  constexpr int DMA_PER_CHUNK = MX ? 10 : big::DMA_PER_CHUNK<TILED>;
+  static_assert(!WIDE || (TILED && GROUPED && !RSC && !MX && EPI != kEpiSwiGLUQuant),
+                "128 x 512 tiles: grouped NVFP4 with scale records, store or SwiGLU epilogue");
+  constexpr int TBM = WIDE ? 128 : BM, TBN = WIDE ? 512 : BN;
+  // stage layout: A codes, B codes, A scales, B scales (MX: 4 E8M0 bytes per
+  // row per chunk)
+  constexpr int B_CODE_OFF = TBM * CB;
+  constexpr int A_SC_OFF = (TBM + TBN) * CB;
+  constexpr int B_SC_OFF = MX ? A_SC_OFF + BM * 4 : A_SC_OFF + TBM * SC_ROW<TILED>;
+  constexpr int STAGE = WIDE ? B_SC_OFF + TBN * 16 : big::STAGE<TILED>;
+  // WIDE: 2 + 8 code loads, one A record load (waves 2 and 3 repeat the
+  // records of waves 0 and 1, byte for byte) and two B record loads
+  constexpr int DMA_PER_CHUNK = MX ? 10 : (WIDE ? 13 : big::DMA_PER_CHUNK<TILED>);
+  static_assert(3 * STAGE <= 160 * 1024, "three stages fit the LDS");
   // one LDS object per stage, addressed with compile-time stage indices, so
   // the compiler can tell that reads of one stage do not wait for the
   // global -> LDS loads still filling another
@@ -518,6 +531,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
+  // the wave's 128 x 128 block: tile rows arow .. + 127, columns bcol .. + 127
+  const int arow = WIDE ? 0 : wm * 128, bcol = WIDE ? wave * 128 : wn * 128;
   const int l32 = lane & 31, h = lane >> 5;
   const int K = g.K;
   const int64_t N = g.N;
@@ -531,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     // major; each XCD (workgroup index mod 8; the grid is a multiple of 8)
     // takes a contiguous range of the tiles that exist, so it works through
     // whole experts and their weights stay in its L2
-    const int nbn = (int)((N + BN - 1) / BN);
+    const int nbn = (int)((N + TBN - 1) / TBN);
     const int total = g.ntiles_dev[0] * nbn;
     const int per = (total + 7) >> 3;
     const int l = (int)(blockIdx.x >> 3), t = (int)(blockIdx.x & 7) * per + l;
@@ -541,7 +556,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     ex = tt.x;
     m0 = tt.y;
     m_end = tt.z;
-    n0 = (int64_t)(t - mt * nbn) * BN;
+    n0 = (int64_t)(t - mt * nbn) * TBN;
   } else {
     const int nbm = (int)((g.M + BM - 1) / BM), nbn = (int)((N + BN - 1) / BN);
     const int nb = nbm * nbn;
@@ -595,10 +610,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   const int c_row = 16 * wave + (lane >> 2);
   const uint32_t c_piece = (uint32_t)(((lane & 3) ^ (((c_row >> 1) ^ (c_row >> 2)) & 3)) * 16);
   const uint32_t c_voff = (uint32_t)c_row * cstride + c_piece;
-  uint32_t ga_voff[4] = {0, 0, 0, 0};   // grouped: A code offset of load `it`
+  uint32_t ga_voff[4] = {0, 0, 0, 0};   // grouped: A code offset of load `it` (< TBM / 64)
   if constexpr (GROUPED) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int it = 0; it < TBM / 64; ++it)
       ga_voff[it] = (uint32_t)a_src(16 * (4 * it + wave) + (lane >> 2)) * cstride + c_piece;
   }
   // raw scale loads: instruction `it` of this wave fills 256 bytes of LDS
@@ -626,6 +641,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
       rsrc(g.w_scales_t + (((size_t)ex * nk * g.w_rows_pad + n0) << 4),
            ((int64_t)nk * g.w_rows_pad - n0) << 4);
   const uint32_t t_voff = (uint32_t)(64 * wave + lane) << 4;
+  const int ta_row = WIDE ? 64 * (wave & 1) : 64 * wave;   // first A record row of the wave
+  const uint32_t ta_voff = (uint32_t)(ta_row + lane) << 4;
 
   // LDS read offsets within a stage of fragment q = 0 for half s2 (piece
   // p = 2 h + s2 holds scale blocks 2p and 2p + 1).  Both swizzles depend on
@@ -634,7 +651,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   // goes into the instruction's immediate offset.
   uint32_t ca_off[2], cb_off[2], sa_off[2], sb_off[2];
   {
-    const int ra = wm * 128 + l32, rb = wn * 128 + l32;
+    const int ra = arow + l32, rb = bcol + l32;
     ca_off[0] = (uint32_t)swz(ra, 2 * h);
     cb_off[0] = (uint32_t)(B_CODE_OFF + swz(rb, 2 * h));
     ca_off[1] = ca_off[0] ^ 16u;
@@ -658,13 +675,16 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     const uint32_t kb = (uint32_t)kc * (BK / 2);
     uint8_t* const dst = sbase + wave * 1024;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < TBN / 64; ++it) {
       const uint32_t so = kb + (uint32_t)(64 * it) * cstride;
-      if constexpr (GROUPED)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lptr_t)(dst + it * 4096), 16, ga_voff[it], kb,
-                                                 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lptr_t)(dst + it * 4096), 16, c_voff, so, 0, 0);
+      if (it < TBM / 64) {
+        if constexpr (GROUPED)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lptr_t)(dst + it * 4096), 16,
+                                                   ga_voff[it < TBM / 64 ? it : 0], kb, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rs, (lptr_t)(dst + it * 4096), 16, c_voff, so, 0,
+                                                   0);
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rs, (lptr_t)(dst + B_CODE_OFF + it * 4096), 16,
                                                c_voff, so, 0, 0);
     }
@@ -682,10 +702,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rs, (lptr_t)(sbase + B_SC_OFF + wave * 256), 4,
                                                mxs_voff, ks, 0, 0);
     } else if constexpr (TILED) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ast_rs, (lptr_t)(sbase + A_SC_OFF + wave * 1024), 16,
-                                               t_voff, (uint32_t)(kc * g.a_rows_pad) << 4, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(bst_rs, (lptr_t)(sbase + B_SC_OFF + wave * 1024), 16,
-                                               t_voff, (uint32_t)(kc * g.w_rows_pad) << 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ast_rs, (lptr_t)(sbase + A_SC_OFF + ta_row * 16), 16,
+                                               ta_voff, (uint32_t)(kc * g.a_rows_pad) << 4, 0, 0);
+#pragma unroll
+      for (int it = 0; it < TBN / 256; ++it)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            bst_rs, (lptr_t)(sbase + B_SC_OFF + wave * 1024 + it * 4096), 16, t_voff,
+            ((uint32_t)(kc * g.w_rows_pad) << 4) + (uint32_t)it * 4096u, 0, 0);
     } else {
       const uint32_t ks = (uint32_t)kc * (BK / 16);
       uint8_t* const sdst = sbase + wave * 256;
@@ -725,24 +748,27 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   // same row / piece layout as the code loads, with the operands' own strides
   const uint32_t r_voff = (uint32_t)c_row * r_stride + c_piece;
   const uint32_t w_voff = (uint32_t)c_row * w_stride + c_piece;
-  uint32_t gr_voff[4] = {0, 0, 0, 0};   // grouped: R offset of load `it`
+  uint32_t gr_voff[4] = {0, 0, 0, 0};   // grouped: R offset of load `it` (< TBM / 64)
   if constexpr (GROUPED) {
     if (nrac > 0) {
 #pragma unroll
-      for (int it = 0; it < 4; ++it)
+      for (int it = 0; it < TBM / 64; ++it)
         gr_voff[it] = (uint32_t)a_src(16 * (4 * it + wave) + (lane >> 2)) * r_stride + c_piece;
     }
   }
   auto issue_rac = [&](int j, uint8_t* const sbase) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      if constexpr (GROUPED)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_rs, (lptr_t)(sbase + wave * 1024 + it * 4096), 16,
-                                                 gr_voff[it], 64u * (uint32_t)j, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_rs, (lptr_t)(sbase + wave * 1024 + it * 4096), 16,
-                                                 r_voff, 64u * (uint32_t)j + (uint32_t)(64 * it) * r_stride,
-                                                 0, 0);
+    for (int it = 0; it < TBN / 64; ++it) {
+      if (it < TBM / 64) {
+        if constexpr (GROUPED)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_rs, (lptr_t)(sbase + wave * 1024 + it * 4096), 16,
+                                                   gr_voff[it < TBM / 64 ? it : 0], 64u * (uint32_t)j,
+                                                   0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              r_rs, (lptr_t)(sbase + wave * 1024 + it * 4096), 16, r_voff,
+              64u * (uint32_t)j + (uint32_t)(64 * it) * r_stride, 0, 0);
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           w_rs, (lptr_t)(sbase + B_CODE_OFF + wave * 1024 + it * 4096), 16, w_voff,
           64u * (uint32_t)j + (uint32_t)(64 * it) * w_stride, 0, 0);
@@ -859,8 +885,8 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
   // Piece 2 s2 + h of a row: half s2 = 1 is half 0 with offset bit 5 flipped.
   if (nrac > 0) {
     uint32_t ra_off[2], rb_off[2];
-    ra_off[0] = (uint32_t)swz(wm * 128 + l32, h);
-    rb_off[0] = (uint32_t)(B_CODE_OFF + swz(wn * 128 + l32, h));
+    ra_off[0] = (uint32_t)swz(arow + l32, h);
+    rb_off[0] = (uint32_t)(B_CODE_OFF + swz(bcol + l32, h));
     ra_off[1] = ra_off[0] ^ 32u;
     rb_off[1] = rb_off[0] ^ 32u;
     uint4 A0[4], B0[4], A1[4], B1[4];
@@ -952,7 +978,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     // then 32 scaled FP4 MFMAs.
     __shared__ __attribute__((aligned(16))) uint8_t stage3[STAGE];
     issue_chunk(min(3, nk - 1), stage3);
-    const int ra = wm * 128 + l32, rb = wn * 128 + l32;
+    const int ra = arow + l32, rb = bcol + l32;
     uint32_t xa[2], xb[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -1058,7 +1084,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
       // Y [rows][ldy], ldy >= N / 2.  Staged through LDS per pass (a wave's 16
       // rows x 64 h columns) so that every store writes 16 contiguous bytes.
       constexpr bool QH = EPI == kEpiSwiGLUQuant;
-      const int64_t fcols = N / 2, f0 = (n0 + wn * 128) / 2;
+      const int64_t fcols = N / 2, f0 = (n0 + bcol) / 2;
       const bool staged =
           QH || ((fcols % 8) == 0 && (g.ldy % 8) == 0 && (((uintptr_t)g.Y) & 15u) == 0);
       auto hval = [&](int mi, int p, int r) {
@@ -1093,7 +1119,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
           for (int mi = 0; mi < 4; ++mi) {
   #pragma unroll
             for (int half = 0; half < 2; ++half) {
-              const int64_t rbase = m0 + wm * 128 + mi * 32 + 16 * half;
+              const int64_t rbase = m0 + arow + mi * 32 + 16 * half;
   #pragma unroll
               for (int pp = 0; pp < 2; ++pp) {
   #pragma unroll
@@ -1178,7 +1204,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              const int64_t row = m0 + wm * 128 + lrow[u];
+              const int64_t row = m0 + arow + lrow[u];
               const bool live = row < m_end && col < fcols;
               uint32_t code, scode;
               float s;
@@ -1222,7 +1248,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
         for (int mi = 0; mi < 4; ++mi) {
   #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int64_t row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int64_t row = m0 + arow + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
             if (row >= m_end) continue;
   #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
@@ -1249,7 +1275,7 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
       for (int mi = 0; mi < 4; ++mi) {
   #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int64_t rbase = m0 + wm * 128 + mi * 32 + 16 * half;
+          const int64_t rbase = m0 + arow + mi * 32 + 16 * half;
           if (g.y_bf16) {
   #pragma unroll
             for (int ni = 0; ni < 4; ++ni) {
@@ -1270,8 +1296,10 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
             for (int it = 0; it < 4; ++it) {
               const int cid = it * 64 + lane, lr = cid >> 4, cc = (cid & 15) * 8;
               const uint4 v = *(const uint4*)(ep + lr * PB + cc * 2);
-              const int64_t row = rbase + lr, col = n0 + wn * 128 + cc;
-              if (row < m_end && col < N) *(uint4*)((uint16_t*)g.Y + row * g.ldy + col) = v;
+              const int64_t row = rbase + lr, col = n0 + bcol + cc;
+              if (row < m_end && col < N)   // nontemporal, as the fp32 rows below
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, v),
+                                            (u32x4v*)((uint16_t*)g.Y + row * g.ldy + col));
             }
           } else {
   #pragma unroll
@@ -1287,8 +1315,13 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
             for (int it = 0; it < 8; ++it) {
               const int cid = it * 64 + lane, lr = cid >> 5, cc = (cid & 31) * 4;
               const uint4 v = *(const uint4*)(ep + lr * PF + cc * 4);
-              const int64_t row = rbase + lr, col = n0 + wn * 128 + cc;
-              if (row < m_end && col < N) *(uint4*)((float*)g.Y + row * g.ldy + col) = v;
+              const int64_t row = rbase + lr, col = n0 + bcol + cc;
+              // nontemporal: an output of this size is read back by another
+              // kernel, once, long after; keeping it out of the caches frees
+              // the write path for the next tiles' loads
+              if (row < m_end && col < N)
+                __builtin_nontemporal_store(__builtin_bit_cast(u32x4v, v),
+                                            (u32x4v*)((float*)g.Y + row * g.ldy + col));
             }
           }
         }
@@ -1299,11 +1332,11 @@ __global__ __launch_bounds__(256, 1) void gemm_nvfp4_big_kernel(GemmArgs g) {
     for (int mi = 0; mi < 4; ++mi) {
   #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t row = m0 + arow + mi * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row >= m_end) continue;
   #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-          const int64_t col = n0 + wn * 128 + ni * 32 + l32;
+          const int64_t col = n0 + bcol + ni * 32 + l32;
           if (col >= N) continue;
           const float v = sc(acc[mi][ni][r]);
           if (g.y_bf16)
@@ -1346,6 +1379,8 @@ static bool grouped_offsets_fit(const GemmArgs& g) {
   return rows * row_bytes <= (int64_t)0xffffffffLL;
 }
 
+bool grouped_wide_ok(int64_t K, int64_t N) { return K % BK == 0 && K >= 512 && N % 512 == 0; }
+
 bool grouped_big_path(const GemmArgs& g) {
   if (g.mx || g.tiles == nullptr || (g.K % BK) != 0 || g.N % big::BN != 0) return false;
   if (!grouped_offsets_fit(g)) return false;
@@ -1355,6 +1390,21 @@ bool grouped_big_path(const GemmArgs& g) {
 hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream) {
   const bool fullk = (g.K % BK) == 0;
   const bool grouped = g.tiles != nullptr;
+  // 128 x 512 tiles: the caller's table lists kWideBM-row M tiles
+  if (g.wide) {
+    if (!grouped || !g.a_scales_t || !g.w_scales_t || !grouped_wide_ok(g.K, g.N) ||
+        g.epilogue == kEpiSwiGLUQuant || g.mx || !grouped_offsets_fit(g))
+      return hipErrorInvalidValue;
+    const int64_t nb = (max_mtiles * (g.N / 512) + 7) / 8 * 8;
+    if (nb == 0) return hipSuccess;
+    if (g.epilogue == kEpiSwiGLU)
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<true, true, kEpiSwiGLU, false, false, true>),
+                         dim3((unsigned)nb), dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((big::gemm_nvfp4_big_kernel<true, true, kEpiStore, false, false, true>),
+                         dim3((unsigned)nb), dim3(256), 0, stream, g);
+    return hipGetLastError();
+  }
   // MXFP4 grouped: the 256 x 256 tiles win from K = 512 on (no decode, so a
   // tile's fixed cost is smaller than on the NVFP4 path, which keeps its
   // 256 x 128 tiles below K = 1024)

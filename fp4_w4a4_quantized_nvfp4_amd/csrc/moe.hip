@@ -383,7 +383,8 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
     const int32_t ex = idx[t * topk + s];
     const float p = (ex >= 0 && ex < E) ? w[t * topk + s] : 0.0f;
     const int64_t r = inv_perm[t * topk + s];
-    const float4 v = *(const float4*)(out + r * H + h0);
+    // each W2 row is read once: nontemporal
+    const f32x4v v = __builtin_nontemporal_load((const f32x4v*)(out + r * H + h0));
     a0 = fmaf(p, v.x, a0);
     a1 = fmaf(p, v.y, a1);
     a2 = fmaf(p, v.z, a2);

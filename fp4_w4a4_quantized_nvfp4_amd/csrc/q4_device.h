@@ -14,9 +14,11 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef float f32x16v __attribute__((ext_vector_type(16)));
 typedef int i32x8v __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 constexpr int kScoreTileRows = 32;   // rows summed in order into one tile sum
 constexpr int kScoreGroupTiles = 8;  // tile sums added in order into one group sum

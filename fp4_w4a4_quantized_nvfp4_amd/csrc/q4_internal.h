@@ -117,11 +117,17 @@ struct GemmArgs {
   // (NVFP4, K % 128 == 0): [E][K/128][w_rows_pad][8 B], record (c, r) the
   // scale bytes of row r's blocks 8 c .. 8 c + 7 (launch_e4m3_scale_records)
   const uint8_t* w_rec8;
+  // grouped, with tiled records: 128 x 512 tiles, `tiles` then listing M
+  // tiles of kWideBM rows (grouped_wide_ok)
+  int32_t wide;
 };
 
 // whether a grouped GEMM runs on the 256 x 256 kernel (the one with the
 // quantizing SwiGLU epilogue)
 bool grouped_big_path(const GemmArgs& g);
+// whether a grouped NVFP4 GEMM with tiled scale records (K % 128 == 0,
+// K >= 512) and N columns can run on 128 x 512 tiles
+bool grouped_wide_ok(int64_t K, int64_t N);
 
 hipError_t launch_w4a4_gemm(const GemmArgs& g, int64_t max_mtiles, hipStream_t stream);
 // scale records [K/128][rows_pad][16 B] of an NVFP4 operand for the dense kernel
@@ -188,6 +194,8 @@ hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const f
                               int32_t H, void* Y, int32_t y_bf16, hipStream_t stream);
 // grouped GEMM over tiles of at most kSkinnyBM rows (few rows per expert)
 constexpr int kSkinnyBM = 32;
+// M tile rows of the grouped 128 x 512 tiles (GemmArgs::wide)
+constexpr int kWideBM = 128;
 hipError_t launch_skinny_gemm(const GemmArgs& g, int64_t max_tiles, hipStream_t stream);
 // raw E4M3 scale records of `batch` NVFP4 operands [rows][K / 16]:
 // [batch][K / 128][rows_pad][8 B] (rows past `rows` zero)

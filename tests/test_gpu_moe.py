@@ -123,9 +123,10 @@ def _check_site(fmt, xb, got, prefix, rac_k, ts=None):
                                             # K >= 1024): partial M tiles, gathered rows
                                             (300, 256, 2, 128, 2, 16),
                                             (520, 1024, 4, 256, 2, 32),
-                                            # NVFP4: both grouped GEMMs on 256 x 256
+                                            # NVFP4: both grouped GEMMs on 128 x 512
                                             # tiles reading the tiled scale records
-                                            # (K = 512 at both sites)
+                                            # (K = 512 at both sites, ragged 128-row
+                                            # tiles)
                                             (600, 512, 4, 512, 2, 32),
                                             # decode-shaped (streaming kernel) with the
                                             # compensation columns read from W_hi^T:
@@ -138,7 +139,7 @@ def _check_site(fmt, xb, got, prefix, rac_k, ts=None):
                                             (40, 256, 8, 192, 2, 70),
                                             # degenerate routing: one expert (every
                                             # token's single slot) on the streaming
-                                            # and on the 256 x 256 kernels; every
+                                            # and on the 128 x 512 kernels; every
                                             # expert in every token's top-k
                                             (37, 256, 1, 128, 1, 16),
                                             (600, 512, 1, 512, 1, 32),
@@ -304,7 +305,9 @@ def test_mx_scale_records_layout():
     assert not rec[:, :, rows:].any()
 
 
-@pytest.mark.parametrize("T,H,E,F,topk,k", [(600, 1024, 4, 1024, 2, 32),   # 256 x 256 tiles
+@pytest.mark.parametrize("T,H,E,F,topk,k", [(600, 1024, 4, 1024, 2, 32),   # NVFP4: 128 x 512
+                                            # tiles with the records, 256 x 256
+                                            # without; MXFP4: 256 x 256 both
                                             # decode-shaped: the streaming kernel with
                                             # the raw E4M3 records (NVFP4) against
                                             # the raw scales
@@ -313,10 +316,11 @@ def test_mx_scale_records_layout():
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_scale_records_same_result(T, H, E, F, topk, k, fmt):
     """The grouped layer with the weights' scale records equals the layer
-    without them bit for bit where both run the same kernel (the 256 x 256
-    kernel with K >= 1024 at both sites, or the decode-shaped streaming
-    kernel): the records change where the scales come from, not the
-    arithmetic."""
+    without them bit for bit: the records change where the scales come from,
+    not the arithmetic.  At K >= 1024 the prefill-shaped NVFP4 layer runs
+    128 x 512 tiles with the records and 256 x 256 tiles without, and each
+    output element still sums the same products in the same order; the
+    decode-shaped layer runs the streaming kernel either way."""
     m = q4()
     rng = np.random.default_rng(12 + T)
     x = rng.standard_normal((T, H)).astype(np.float32)
