@@ -78,6 +78,9 @@ _SIGS = {
     "moe_w4a4_grouped_gemm": (_I32, [_I32, _P, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P,
                                      _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P, _SZ,
                                      _P, _P]),
+    "moe_w4a4_grouped_gemm_ex": (_I32, [_I32, _P, _I64, _I32, _P, _P, _I32, _I32, _I32, _P, _P,
+                                        _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _I32, _P,
+                                        _SZ, _P, C.c_uint32, _P]),
 }
 
 
@@ -469,13 +472,19 @@ def moe_workspace_layout(fmt, T, E, H, F, topk, rac_k):
     return list(offs), L.moe_workspace_size(fmt, T, E, H, F, topk, rac_k)
 
 
+MOE_FUSE_H_QUANT = 1
+
+
 def moe_w4a4_grouped_gemm(tokens, topk_idx, topk_w, experts, rac_k, out_dtype=OUT_BF16,
-                          workspace=None, stream=None, Y=None, status=None, h_tensor_scale=None):
+                          workspace=None, stream=None, Y=None, status=None, h_tensor_scale=None,
+                          fuse_h=False):
     """Token-sorted grouped W4A4+RAC SwiGLU expert layer; returns (Y, workspace).
     ``status`` (optional int32 [1]) receives 0, or 1 for an expert index
     outside [0, E).  ``h_tensor_scale`` (optional fp32 [1], NVFP4) supplies
-    h's tensor scale; on prefill shapes h is then quantized inside the W13
-    GEMM's epilogue."""
+    h's tensor scale, so h's quantization needs no amax pass.  ``fuse_h``
+    (with ``h_tensor_scale``): on prefill shapes, quantize h inside the W13
+    GEMM's epilogue instead of in a separate pass (moe_w4a4_grouped_gemm_ex,
+    Q4_MOE_FUSE_H_QUANT)."""
     with _on(stream):
         tokens = _bf16(tokens, "tokens")
         T, H = tokens.shape
@@ -510,7 +519,7 @@ def moe_w4a4_grouped_gemm(tokens, topk_idx, topk_w, experts, rac_k, out_dtype=OU
             Y = _empty((T, H), torch.float32 if out_dtype == OUT_F32 else torch.bfloat16,
                        tokens.device)
         _out_check(Y, T, H, out_dtype)
-        _check(L.moe_w4a4_grouped_gemm(
+        _check(L.moe_w4a4_grouped_gemm_ex(
             fmt, _ptr(tokens), T, H, _ptr(topk_idx), _ptr(topk_w), topk, E, F,
             _ptr(w13["codes"]), _ptr(w13["scales"]), _ptr(w13["tensor_scale"]),
             _ptr(w2["codes"]), _ptr(w2["scales"]), _ptr(w2["tensor_scale"]),
@@ -518,6 +527,6 @@ def moe_w4a4_grouped_gemm(tokens, topk_idx, topk_w, experts, rac_k, out_dtype=OU
             _ptr(experts.get("w2_hi_t"), _BF16_TYPES, (F, E, H), "w2_hi_t") if rac_k else None,
             rec13, rec2, _ptr(h_tensor_scale, torch.float32, (1,), "h_tensor_scale"),
             rac_k, _ptr(Y), out_dtype, _ptr(workspace, torch.uint8), wsb,
-            _status(status),
+            _status(status), MOE_FUSE_H_QUANT if fuse_h else 0,
             _stream(stream)))
         return Y, workspace

@@ -66,7 +66,7 @@ int32_t round_up32(int32_t k) { return (k + 31) & ~31; }
 extern "C" {
 
 const char* q4_last_error(void) { return g_err; }
-int32_t q4_version(void) { return 104; }
+int32_t q4_version(void) { return 105; }
 
 // ======================================================================== quantize
 size_t q4_quantize_workspace_size(int64_t rows, int64_t cols, int32_t fmt) {
@@ -724,18 +724,22 @@ q4_status_t moe_workspace_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, i
   return Q4_OK;
 }
 
-q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T, int32_t H,
-                                  const int32_t* topk_idx, const float* topk_w, int32_t topk,
-                                  int32_t E, int32_t F, const uint8_t* w13_codes,
-                                  const uint8_t* w13_scales, const float* w13_tensor_scales,
-                                  const uint8_t* w2_codes, const uint8_t* w2_scales,
-                                  const float* w2_tensor_scales, const uint16_t* w13_hi_t,
-                                  const uint16_t* w2_hi_t, const uint8_t* w13_scale_records,
-                                  const uint8_t* w2_scale_records, const float* h_tensor_scale,
-                                  int32_t rac_k, void* Y,
-                                  int32_t y_dtype, void* workspace, size_t workspace_bytes,
-                                  int32_t* status, void* stream) {
+q4_status_t moe_w4a4_grouped_gemm_ex(int32_t fmt, const uint16_t* tokens, int64_t T, int32_t H,
+                                     const int32_t* topk_idx, const float* topk_w, int32_t topk,
+                                     int32_t E, int32_t F, const uint8_t* w13_codes,
+                                     const uint8_t* w13_scales, const float* w13_tensor_scales,
+                                     const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                     const float* w2_tensor_scales, const uint16_t* w13_hi_t,
+                                     const uint16_t* w2_hi_t, const uint8_t* w13_scale_records,
+                                     const uint8_t* w2_scale_records, const float* h_tensor_scale,
+                                     int32_t rac_k, void* Y,
+                                     int32_t y_dtype, void* workspace, size_t workspace_bytes,
+                                     int32_t* status, uint32_t flags, void* stream) {
   const char* fn = "moe_w4a4_grouped_gemm";
+  if (flags & ~(uint32_t)Q4_MOE_FUSE_H_QUANT) return fail(Q4_EINVAL, "%s: unknown flags 0x%x", fn, flags);
+  const bool fuse_req = (flags & Q4_MOE_FUSE_H_QUANT) != 0;
+  if (fuse_req && !h_tensor_scale)
+    return fail(Q4_EINVAL, "%s: Q4_MOE_FUSE_H_QUANT needs h_tensor_scale", fn);
   if (fmt != Q4_NVFP4 && fmt != Q4_MXFP4) return fail(Q4_EINVAL, "%s: bad format %d", fn, fmt);
   const bool mx = fmt == Q4_MXFP4;
   if (T < 0 || T * 16 >= kMaxDim) return fail(Q4_ESHAPE, "%s: bad T", fn);
@@ -800,9 +804,9 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   // NVFP4 prefill shapes read the weights' tiled scale records when given.
   // With them, GEMMs whose N is a multiple of 512 run on 128 x 512 tiles
   // (half the empty rows of 256-row tiles at a few hundred rows per expert);
-  // the W13 GEMM that quantizes h in its epilogue keeps the 256-row tiles.
+  // a W13 GEMM asked to quantize h in its epilogue keeps the 256-row tiles.
   const bool rec13 = L.tiled13 && w13_scale_records, rec2 = L.tiled2 && w2_scale_records;
-  const bool wide13 = rec13 && !h_tensor_scale && grouped_wide_ok(H, 2 * (int64_t)F);
+  const bool wide13 = rec13 && !fuse_req && grouped_wide_ok(H, 2 * (int64_t)F);
   const bool wide2 = rec2 && grouped_wide_ok(F, H);
   // the sort also writes each sorted row's token and a second tile table:
   // 32-row tiles of the skinny kernel (decode-shaped layers) or 128-row
@@ -904,11 +908,12 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
   int32_t* hS = (int32_t*)P(L.off[11]);
   uint16_t* hR = (uint16_t*)P(L.off[12]);
   double* hscore = (double*)P(L.off[15]);
-  // With a supplied s_h on the 256 x 256 kernel, the W13 epilogue quantizes h
-  // as it stores it (codes, scales, residual sums per half tile): no separate
-  // pass over h.  Otherwise the quantizer runs on h (with the supplied s_h,
-  // when there is one, in place of h's amax).
-  const bool fuse_h = h_tensor_scale && L.h_part && grouped_big_path(g);
+  // Asked for (Q4_MOE_FUSE_H_QUANT, with a supplied s_h) and on the 256 x 256
+  // kernel, the W13 epilogue quantizes h as it stores it (codes, scales,
+  // residual sums per half tile): no separate pass over h.  Otherwise the
+  // quantizer runs on h (with the supplied s_h, when there is one, in place of
+  // h's amax).
+  const bool fuse_h = fuse_req && L.h_part && grouped_big_path(g);
   if (fuse_h) {
     g.epilogue = kEpiSwiGLUQuant;
     g.q_codes = hc;
@@ -982,6 +987,24 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T
                             y_dtype == Q4_OUT_BF16, s), "moe combine");
 #undef Q4_TRY
   return Q4_OK;
+}
+
+q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t* tokens, int64_t T, int32_t H,
+                                  const int32_t* topk_idx, const float* topk_w, int32_t topk,
+                                  int32_t E, int32_t F, const uint8_t* w13_codes,
+                                  const uint8_t* w13_scales, const float* w13_tensor_scales,
+                                  const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                  const float* w2_tensor_scales, const uint16_t* w13_hi_t,
+                                  const uint16_t* w2_hi_t, const uint8_t* w13_scale_records,
+                                  const uint8_t* w2_scale_records, const float* h_tensor_scale,
+                                  int32_t rac_k, void* Y,
+                                  int32_t y_dtype, void* workspace, size_t workspace_bytes,
+                                  int32_t* status, void* stream) {
+  return moe_w4a4_grouped_gemm_ex(fmt, tokens, T, H, topk_idx, topk_w, topk, E, F, w13_codes,
+                                  w13_scales, w13_tensor_scales, w2_codes, w2_scales,
+                                  w2_tensor_scales, w13_hi_t, w2_hi_t, w13_scale_records,
+                                  w2_scale_records, h_tensor_scale, rac_k, Y, y_dtype, workspace,
+                                  workspace_bytes, status, 0u, stream);
 }
 
 }  // extern "C"

@@ -349,14 +349,11 @@ q4_status_t q4_scale_records(int32_t fmt, const uint8_t *scales, int64_t batch, 
  *              the raw scales; results are the same.
  *   h_tensor_scale: NULL, or (NVFP4 only) device fp32 [1]: h's tensor scale
  *              supplied by the caller (delayed scaling, e.g. an earlier step's
- *              s_h) instead of RN32(amax(h) / 2688).  Where the W13 GEMM runs
- *              on its 256 x 256 tiles (prefill shapes), h is then quantized in
- *              the W13 epilogue as it is produced (the fused stage of QUADS
- *              section 3.3 "Efficient implementation"): codes, scales and the
- *              per-channel residual sums come out of the GEMM, with no
- *              separate pass over h; elsewhere the quantizer runs on h with
- *              this scale.  Blocks whose amax exceeds 2688 s_h saturate
- *              (E4M3 scale 448, codes +-6), as the format defines.
+ *              s_h) instead of RN32(amax(h) / 2688): the quantizer runs on h
+ *              with this scale and no amax pass.  Blocks whose amax exceeds
+ *              2688 s_h saturate (E4M3 scale 448, codes +-6), as the format
+ *              defines.  moe_w4a4_grouped_gemm_ex can instead quantize h inside
+ *              the W13 GEMM (Q4_MOE_FUSE_H_QUANT).
  *   rac_k      channels compensated at each of the two activation sites.
  *   Y          [T][H] fp32 or bf16: y_t = sum_s p_ts out_(t,s), slots in order.
  * Steps: sort; quantize tokens (one s_t, one selection over T rows); W13 RAC
@@ -395,6 +392,33 @@ q4_status_t moe_w4a4_grouped_gemm(int32_t fmt, const uint16_t *tokens, int64_t T
                                   int32_t rac_k, void *Y,
                                   int32_t y_dtype, void *workspace, size_t workspace_bytes,
                                   int32_t *status, void *stream);
+/* moe_w4a4_grouped_gemm with option flags (the plain call is flags = 0):
+ *   Q4_MOE_FUSE_H_QUANT  with h_tensor_scale (else Q4_EINVAL): where the W13
+ *       GEMM can run on 256 x 256 tiles (prefill shapes: NVFP4, H % 128 == 0,
+ *       2F % 256 == 0, H >= 1024, or H >= 512 with the weights' scale
+ *       records), h is quantized in the W13 epilogue as it is produced: the
+ *       fused stage of QUADS section 3.3 "Efficient implementation".  Codes,
+ *       scales and the per-channel residual sums come out of the GEMM, with
+ *       no separate pass over h.  Elsewhere the flag changes nothing.
+ *       Results are those of the unfused call with the same h_tensor_scale,
+ *       except that W13 then runs on 256 x 256 tiles rather than 128 x 512:
+ *       h can differ from the unfused call's in the order of the sums of an
+ *       expert's last rows, within the GEMM tolerance.  The epilogue's
+ *       encoding runs beside no MFMA work, so the fused call can be slower
+ *       than the unfused one.
+ * Unknown flag bits: Q4_EINVAL. */
+#define Q4_MOE_FUSE_H_QUANT 1u
+q4_status_t moe_w4a4_grouped_gemm_ex(int32_t fmt, const uint16_t *tokens, int64_t T, int32_t H,
+                                     const int32_t *topk_idx, const float *topk_w, int32_t topk,
+                                     int32_t E, int32_t F, const uint8_t *w13_codes,
+                                     const uint8_t *w13_scales, const float *w13_tensor_scales,
+                                     const uint8_t *w2_codes, const uint8_t *w2_scales,
+                                     const float *w2_tensor_scales, const uint16_t *w13_hi_t,
+                                     const uint16_t *w2_hi_t, const uint8_t *w13_scale_records,
+                                     const uint8_t *w2_scale_records, const float *h_tensor_scale,
+                                     int32_t rac_k, void *Y,
+                                     int32_t y_dtype, void *workspace, size_t workspace_bytes,
+                                     int32_t *status, uint32_t flags, void *stream);
 
 #ifdef __cplusplus
 }

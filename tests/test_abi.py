@@ -105,6 +105,15 @@ def test_shape_and_pointer_errors(L):
                                    fake, None, fake, fake, None, None, fake, 0, fake, 1, fake,
                                    1 << 30, None, None) == 1
     assert "tensor scale" in _err(L)
+    # MoE option flags: unknown bits; h fused into the W13 epilogue needs a supplied s_h
+    assert L.moe_w4a4_grouped_gemm_ex(0, fake, 4, 64, fake, fake, 2, 4, 64, fake, fake, fake, fake,
+                                      fake, fake, fake, fake, None, None, fake, 0, fake, 1, fake,
+                                      1 << 30, None, 2, None) == 1
+    assert "flags" in _err(L)
+    assert L.moe_w4a4_grouped_gemm_ex(0, fake, 4, 64, fake, fake, 2, 4, 64, fake, fake, fake, fake,
+                                      fake, fake, fake, fake, None, None, None, 0, fake, 1, fake,
+                                      1 << 30, None, 1, None) == 1
+    assert "h_tensor_scale" in _err(L)
     # scale records: K % 128, short output, format
     assert L.q4_scale_records(0, fake, 2, 64, 96, fake, 1 << 20, None) == 2
     assert L.q4_scale_records(0, fake, 2, 64, 256, fake, 100, None) == 4

@@ -61,7 +61,7 @@ def test_route_and_sort(T, E):
 
 
 def _run_layer(m, xb, logits, w13, w2, topk, rac_k, fmt=0, out_dtype=1, h_ts=None,
-               experts=None):
+               experts=None, fuse_h=False):
     T, H = xb.shape
     E, F2, _ = w13.shape
     F = F2 // 2
@@ -71,7 +71,7 @@ def _run_layer(m, xb, logits, w13, w2, topk, rac_k, fmt=0, out_dtype=1, h_ts=Non
         experts = m.prepare_moe_weights(dev(w13), dev(w2), fmt=fmt)
     hts = None if h_ts is None else dev(np.array([h_ts], dtype=np.float32))
     Y, ws = m.moe_w4a4_grouped_gemm(x, idx, p, experts, rac_k, out_dtype=out_dtype,
-                                    h_tensor_scale=hts)
+                                    h_tensor_scale=hts, fuse_h=fuse_h)
     torch.cuda.synchronize()
     offs, _ = m.moe_workspace_layout(fmt, T, E, H, F, topk, rac_k)
     R = T * topk
@@ -191,18 +191,22 @@ def test_empty_token_batch(fmt):
     assert tuple(Y.shape) == (0, H) and int(host(st)[0]) == 0
 
 
+@pytest.mark.parametrize("fuse", [True, False], ids=["fused", "separate"])
 @pytest.mark.parametrize("T,H,E,F,topk,k", [(600, 512, 4, 512, 2, 32),      # records at both sites
                                             (520, 1024, 4, 256, 2, 32),     # W2 on 256 x 128 tiles
                                             (700, 1024, 3, 128, 2, 0)])     # no compensation
-def test_fused_h_quantization(T, H, E, F, topk, k):
-    """A supplied h tensor scale on a prefill-shaped layer: h is quantized in
-    the W13 epilogue.  With s_h equal to the in-call one, below it (saturated
-    blocks) and above it: h agrees with the unfused layer's (which orders the
-    sums of experts' last rows differently) within the GEMM tolerance, codes
-    and scales are bit-exact against the oracle's quantization of the GPU's h
-    under that s_h, scores within the bound, the selection valid, and the W2
-    product and the layer output agree with the oracle."""
-    say(f"moe fused h T={T} H={H} E={E} F={F} topk={topk} k={k}")
+def test_fused_h_quantization(T, H, E, F, topk, k, fuse):
+    """A supplied h tensor scale on a prefill-shaped layer, h quantized in
+    the W13 epilogue (fused, on 256 x 256 tiles) or by the quantizer without
+    an amax pass (separate).  With s_h equal to the in-call one, below it
+    (saturated blocks) and above it: h agrees with the in-call layer's (whose
+    tiles may order the sums of experts' last rows differently) within the
+    GEMM tolerance, codes and scales are bit-exact against the oracle's
+    quantization of the GPU's h under that s_h, scores within the bound, the
+    selection valid, and the W2 product and the layer output agree with the
+    oracle."""
+    say(f"moe supplied s_h ({'fused' if fuse else 'separate'}) T={T} H={H} E={E} F={F} "
+        f"topk={topk} k={k}")
     m = q4()
     rng = np.random.default_rng(T + 7 * H + F)
     x = rng.standard_normal((T, H)).astype(np.float32)
@@ -216,7 +220,8 @@ def test_fused_h_quantization(T, H, E, F, topk, k):
     s_h = float(base["h_ts"][0])
     for mult in (1.0, 0.37, 3.0):
         ts = float(np.float32(s_h * mult))
-        got, _ = _run_layer(m, xb, logits, w13, w2, topk, k, h_ts=ts, experts=experts)
+        got, _ = _run_layer(m, xb, logits, w13, w2, topk, k, h_ts=ts, experts=experts,
+                            fuse_h=fuse)
         assert np.array_equal(got["x_S"], base["x_S"])
         assert got["h_ts"][0] == np.float32(ts)
         check_bf16_output(got["h"], bf16_to_f64(base["h"]), tol=2 * GEMM_TOL)
