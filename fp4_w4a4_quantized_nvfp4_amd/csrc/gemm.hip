@@ -1567,6 +1567,10 @@ hipError_t launch_mx_scale_records(const uint8_t* scales, int64_t batch, int64_t
 __global__ __launch_bounds__(256) void scale_tile_sorted_kernel(
     const uint8_t* __restrict__ sc, const int32_t* __restrict__ a_rows, int64_t R, int32_t K,
     const int32_t* __restrict__ offsets, int32_t E, int64_t rows_pad, uint4* __restrict__ out) {
+  // the experts' first rows, searched in LDS (E <= 1024)
+  __shared__ int32_t s_off[1025];
+  for (int e = threadIdx.x; e <= E; e += 256) s_off[e] = offsets[e];
+  __syncthreads();
   const int64_t total = (int64_t)(K / 128) * rows_pad;
   const half2v k256 = {(_Float16)256.0f, (_Float16)256.0f};
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total;
@@ -1580,10 +1584,10 @@ __global__ __launch_bounds__(256) void scale_tile_sorted_kernel(
       int lo = 0, hi = E;   // offsets[0] <= r < offsets[E]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if ((int64_t)offsets[mid] <= r) lo = mid;
+        if ((int64_t)s_off[mid] <= r) lo = mid;
         else hi = mid;
       }
-      in_tile = (int)((r - offsets[lo]) & 255);
+      in_tile = (int)((r - s_off[lo]) & 255);
     }
     // each E4M3 byte shifted left by 7 is an fp16 of 2^-8 times its value;
     // the multiply by 256 is exact
