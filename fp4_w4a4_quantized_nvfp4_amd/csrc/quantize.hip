@@ -639,11 +639,14 @@ __global__ __launch_bounds__(256) void wsel_gather_kernel(const uint16_t* __rest
                    tile, w_ts, a_ts);
 }
 
-// The same gather in 64 x 256 tiles with 8-byte accesses (N % 4 == 0): each
+// The same gather in CH x 256 tiles with 8-byte accesses (N % 4 == 0): each
 // wave reads one selected row's 256 columns per load (lane l: columns
 // 4 l .. 4 l + 3), the tile is transposed through LDS, and each lane writes
 // four consecutive channels of one output row.  Tile (bx, by) of matrix b:
-// j in [256 bx, 256 bx + 256), t in [64 by, 64 by + 64).
+// j in [256 bx, 256 bx + 256), t in [CH by, CH by + CH).  The loads go out
+// before the channel-set check (every channel is clamped into [0, K)); an
+// invalid set then zeroes what they read.
+template <int CH>
 __global__ __launch_bounds__(256) void wsel_gather_wide_kernel(const uint16_t* __restrict__ w_hi_t,
                                                                int64_t K, int64_t N,
                                                                const int32_t* __restrict__ idx,
@@ -651,30 +654,31 @@ __global__ __launch_bounds__(256) void wsel_gather_wide_kernel(const uint16_t* _
                                                                uint16_t* __restrict__ ws,
                                                                const float* __restrict__ w_ts,
                                                                const float* __restrict__ a_ts) {
-  constexpr int TP = 264;   // LDS row pitch (u16): 256 columns + 8 of pad
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][TP];
-  const bool ok = chan_set_ok(idx, k, K);
-  const int kk = ok ? k : 0;
+  constexpr int TP = 264;           // LDS row pitch (u16): 256 columns + 8 of pad
+  constexpr int LPR = CH / 4;       // lanes per output row (four channels each)
+  constexpr int RPI = 64 / LPR;     // output rows per wave and store
+  __shared__ __attribute__((aligned(16))) uint16_t tile[CH][TP];
   const int64_t b = blockIdx.z;
   const int64_t j0 = (int64_t)blockIdx.x * 256;
-  const int t0 = blockIdx.y * 64;
+  const int t0 = blockIdx.y * CH;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint16_t* src = w_hi_t + b * N;   // channel-major [K][batch][N]
   const int64_t cstride = (int64_t)gridDim.z * N;
   const int64_t jl = j0 + 4 * lane;
   const bool jok = jl < N;   // N % 4 == 0: the lane's four columns are all in or all out
-  const float rinv = w_ts ? wsel_scale_inv(w_ts[b], a_ts[0]) : 1.0f;
-  uint2 v[16];
+  uint2 v[CH / 4];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < CH / 4; ++q) {
     const int t = t0 + 4 * q + wave;
-    int c = t < kk ? idx[t] : 0;
+    int c = t < k ? idx[t] : 0;
     c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
-    v[q] = (t < kk && jok) ? *(const uint2*)(src + (int64_t)c * cstride + jl) : make_uint2(0, 0);
+    v[q] = (t < k && jok) ? *(const uint2*)(src + (int64_t)c * cstride + jl) : make_uint2(0, 0);
   }
+  const bool ok = chan_set_ok(idx, k, K);
+  const float rinv = w_ts ? wsel_scale_inv(w_ts[b], a_ts[0]) : 1.0f;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    uint2 w = v[q];
+  for (int q = 0; q < CH / 4; ++q) {
+    uint2 w = ok ? v[q] : make_uint2(0, 0);
     if (w_ts) {
       auto cv = [&](uint32_t x) {
         const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(bf16_lo(x) * rinv));
@@ -687,10 +691,10 @@ __global__ __launch_bounds__(256) void wsel_gather_wide_kernel(const uint16_t* _
   }
   __syncthreads();
   uint16_t* dst = ws + b * N * kp;
-  const int tt = 4 * (lane & 15);
+  const int tt = 4 * (lane % LPR);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int jj = 16 * q + 4 * wave + (lane >> 4);
+  for (int q = 0; q < 256 / (4 * RPI); ++q) {
+    const int jj = 4 * RPI * q + RPI * wave + lane / LPR;
     const int64_t j = j0 + jj;
     const uint32_t a0 = tile[tt][jj], a1 = tile[tt + 1][jj], a2 = tile[tt + 2][jj], a3 = tile[tt + 3][jj];
     if (j < N && t0 + tt < kp) *(uint2*)(dst + j * kp + t0 + tt) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
@@ -954,9 +958,10 @@ hipError_t launch_wsel_gather(const uint16_t* w_hi_t, int64_t batch, int64_t K, 
                               hipStream_t stream, const float* w_ts, const float* a_ts) {
   if (batch == 0 || N == 0 || kp == 0) return hipSuccess;
   if (N % 4 == 0) {
-    dim3 grid((unsigned)((N + 255) / 256), (unsigned)((kp + 63) / 64), (unsigned)batch);
-    hipLaunchKernelGGL(wsel_gather_wide_kernel, grid, dim3(256), 0, stream, w_hi_t, K, N, idx, k,
-                       kp, ws, w_ts, a_ts);
+    constexpr int CH = 32;   // channels per workgroup
+    dim3 grid((unsigned)((N + 255) / 256), (unsigned)((kp + CH - 1) / CH), (unsigned)batch);
+    hipLaunchKernelGGL(wsel_gather_wide_kernel<CH>, grid, dim3(256), 0, stream, w_hi_t, K, N, idx,
+                       k, kp, ws, w_ts, a_ts);
     return hipGetLastError();
   }
   dim3 grid((unsigned)((N + 63) / 64), (unsigned)((kp + 63) / 64), (unsigned)batch);
