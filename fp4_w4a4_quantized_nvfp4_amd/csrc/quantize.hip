@@ -293,29 +293,82 @@ __global__ __launch_bounds__(512, 4) void quantize_kernel(QuantKArgs a) {
 }
 
 // ====================================================================== scores
-// score_j = sum over groups ascending of the group partial sums (fp64).  One
-// wave per 64 channels, so that the loads spread over as many CUs as possible
-// (ngroups_dev: the group count is mult * ngroups_dev[0], read on the device)
-__global__ __launch_bounds__(64) void score_reduce_kernel(const double* __restrict__ partial,
-                                                          int64_t ngroups, int32_t cols,
-                                                          double* __restrict__ scores,
-                                                          const int32_t* __restrict__ ngroups_dev,
-                                                          int32_t mult) {
-  const int j = blockIdx.x * 64 + threadIdx.x;
-  if (j >= cols) return;
+// score_j = sum of the group partial sums (fp64), in a fixed order: W waves
+// per 64 channels, wave w summing groups [w G / W, (w + 1) G / W) in
+// ascending order, then the W sums added in wave order.  Many groups (a
+// tensor of many rows) spread over W waves; few keep W = 1, which spreads
+// the loads over as many CUs as possible.  (ngroups_dev: the group count is
+// mult * ngroups_dev[0], read on the device.)
+template <int W>
+__global__ __launch_bounds__(64 * W) void score_reduce_kernel(const double* __restrict__ partial,
+                                                              int64_t ngroups, int32_t cols,
+                                                              double* __restrict__ scores,
+                                                              const int32_t* __restrict__ ngroups_dev,
+                                                              int32_t mult) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane;
+  const bool live = j < cols;
   if (ngroups_dev) ngroups = (int64_t)ngroups_dev[0] * mult;
+  const int64_t g0 = ngroups * w / W, g1 = ngroups * (w + 1) / W;
   double s = 0.0;
-  int64_t t = 0;
-  // up to 64 loads in flight; slots past the last group read as +0.0, which
-  // leaves the (non-negative) running sum unchanged
-  for (; t < ngroups; t += 64) {
-    double p[64];
+  // up to B loads in flight (8 or 16 waves per workgroup, two or four per
+  // SIMD: a smaller batch); slots past the range read as +0.0, which leaves
+  // the (non-negative) running sum unchanged
+  constexpr int B = W >= 8 ? 16 : 64;
+  for (int64_t t = g0; t < g1; t += B) {
+    double p[B];
 #pragma unroll
-    for (int u = 0; u < 64; ++u) p[u] = t + u < ngroups ? partial[(t + u) * cols + j] : 0.0;
+    for (int u = 0; u < B; ++u) p[u] = (live && t + u < g1) ? partial[(t + u) * cols + j] : 0.0;
 #pragma unroll
-    for (int u = 0; u < 64; ++u) s += p[u];
+    for (int u = 0; u < B; ++u) s += p[u];
   }
-  scores[j] = s;
+  if constexpr (W == 1) {
+    if (live) scores[j] = s;
+  } else {
+    __shared__ double red[W][64];
+    red[w][lane] = s;
+    __syncthreads();
+    if (w == 0 && live) {
+      double tot = 0.0;
+#pragma unroll
+      for (int i = 0; i < W; ++i) tot += red[i][lane];
+      scores[j] = tot;
+    }
+  }
+}
+
+// waves per 64 channels for a reduction over ngroups groups: about 16
+// groups per wave, at most 16 waves
+static int score_waves(int64_t ngroups) {
+  int w = 1;
+  while (w < 16 && ngroups >= 32 * (int64_t)w) w *= 2;
+  return w;
+}
+
+static void launch_score_reduce_host(const double* partial, int64_t ngroups, int64_t cols,
+                                     double* scores, hipStream_t stream) {
+  const dim3 grid((unsigned)((cols + 63) / 64));
+  switch (score_waves(ngroups)) {
+    case 16:
+      hipLaunchKernelGGL(score_reduce_kernel<16>, grid, dim3(1024), 0, stream, partial, ngroups,
+                         (int32_t)cols, scores, nullptr, 0);
+      break;
+    case 8:
+      hipLaunchKernelGGL(score_reduce_kernel<8>, grid, dim3(512), 0, stream, partial, ngroups,
+                         (int32_t)cols, scores, nullptr, 0);
+      break;
+    case 4:
+      hipLaunchKernelGGL(score_reduce_kernel<4>, grid, dim3(256), 0, stream, partial, ngroups,
+                         (int32_t)cols, scores, nullptr, 0);
+      break;
+    case 2:
+      hipLaunchKernelGGL(score_reduce_kernel<2>, grid, dim3(128), 0, stream, partial, ngroups,
+                         (int32_t)cols, scores, nullptr, 0);
+      break;
+    default:
+      hipLaunchKernelGGL(score_reduce_kernel<1>, grid, dim3(64), 0, stream, partial, ngroups,
+                         (int32_t)cols, scores, nullptr, 0);
+  }
 }
 
 // ====================================================================== top-k
@@ -824,8 +877,7 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
     // no rows: still report s_t (1, or the supplied value)
     hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(64), 0, stream, ts_in, ts_out);
   }
-  hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(64), 0,
-                     stream, (const double*)partial, ngroups, (int32_t)cols, scores, nullptr, 0);
+  launch_score_reduce_host((const double*)partial, ngroups, cols, scores, stream);
   if (topk > 0) return launch_select(scores, cols, topk, chan_idx, stream);
   return hipGetLastError();
 }
@@ -833,7 +885,7 @@ hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t col
 hipError_t launch_score_reduce_dev(const double* partial, const int32_t* ngroups_dev, int32_t mult,
                                    int64_t cols, double* scores, hipStream_t stream) {
   if (cols <= 0) return hipSuccess;
-  hipLaunchKernelGGL(score_reduce_kernel, dim3((unsigned)((cols + 63) / 64)), dim3(64), 0, stream,
+  hipLaunchKernelGGL(score_reduce_kernel<1>, dim3((unsigned)((cols + 63) / 64)), dim3(64), 0, stream,
                      partial, (int64_t)0, (int32_t)cols, scores, ngroups_dev, mult);
   return hipGetLastError();
 }
