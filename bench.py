@@ -37,8 +37,8 @@ PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
 # WRITE_SIZE (KiB per dispatch, taken on the kernel source with this sha256)
 # scaled by the factors a plain 1 GiB copy gives (fetch x 2.00, write x 1.00);
 # any change to that source makes the record stale, and the line reports null
-TRAFFIC = {"gemm_src_sha256": "3958b2212e744a2c53a4d6d9fb64b9bf4289fa1d949ae4ce30ae5a8ad63515b5",
-           "fetch_kib": 240320.3, "fetch_scale": 2.0, "write_kib": 234753.9, "write_scale": 1.0}
+TRAFFIC = {"gemm_src_sha256": "8d786d3323691165200a95601965da269ed6d7240413414e1b5efa42afaba412",
+           "fetch_kib": 240497.4, "fetch_scale": 2.0, "write_kib": 234752.9, "write_scale": 1.0}
 
 
 def _args():
