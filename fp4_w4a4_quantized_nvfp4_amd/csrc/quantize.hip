@@ -360,6 +360,450 @@ static void launch_score_reduce_host(const double* partial, int64_t ngroups, int
   }
 }
 
+// ====================================================================== top-k
+// One workgroup of 1024 threads.  Radix select over the fp64 bit patterns
+// (non-negative doubles order as unsigned integers), eight 8-bit digits from
+// the top: a wave-aggregated histogram, then one wave finds the digit that
+// holds the k-th largest key.  The emit pass takes every key above it and the
+// lowest-index copies of it, in ascending channel order.
+__device__ __forceinline__ int block_excl_scan_bits(bool flag, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint64_t b = __ballot(flag);
+  int in_wave = __popcll(b & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+  if (lane == 0) wsum[w] = __popcll(b);
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    int v = wsum[i];
+    before += (i < w) ? v : 0;
+    tot += v;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + in_wave;
+}
+
+__global__ __launch_bounds__(1024) void topk_kernel(const double* __restrict__ scores, int32_t cols,
+                                                    int32_t k, int32_t* __restrict__ out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_kleft;
+  __shared__ int wsum[16];
+  const uint64_t* keys = (const uint64_t*)scores;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint64_t prefix = 0, mask = 0;
+  int kleft = k;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int j0 = 0; j0 < cols; j0 += 1024) {
+      const int j = j0 + tid;
+      const uint64_t key = j < cols ? keys[j] : 0ull;
+      const bool valid = j < cols && (key & mask) == prefix;
+      const uint32_t digit = (uint32_t)(key >> shift) & 255u;
+      uint64_t pending = __ballot(valid);
+      while (pending) {
+        const int leader = __ffsll((unsigned long long)pending) - 1;
+        const uint32_t d0 = (uint32_t)__shfl((int)digit, leader, 64);
+        const uint64_t same = __ballot(valid && digit == d0) & pending;
+        if (lane == leader) atomicAdd(&hist[d0], (uint32_t)__popcll(same));
+        pending &= ~same;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns digits 255-4l .. 252-4l (descending)
+      uint32_t c[4];
+      uint32_t sum = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[q] = hist[255 - 4 * lane - q];
+        sum += c[q];
+      }
+      uint32_t incl = sum;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_up((int)incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      uint32_t cum = incl - sum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (cum < (uint32_t)kleft && cum + c[q] >= (uint32_t)kleft) {
+          s_prefix = prefix | ((uint64_t)(255 - 4 * lane - q) << shift);
+          s_kleft = kleft - (int)cum;
+        }
+        cum += c[q];
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    kleft = s_kleft;
+    mask |= 0xffull << shift;
+  }
+  const uint64_t T = prefix;   // the k-th largest key; kleft of its copies are taken
+  int base_eq = 0, base_sel = 0;
+  for (int c0 = 0; c0 < cols; c0 += 1024) {
+    const int j = c0 + tid;
+    const uint64_t key = j < cols ? keys[j] : 0ull;
+    const bool eq = j < cols && key == T;
+    const bool gt = j < cols && key > T;
+    int tot_eq, tot_sel;
+    const int eq_rank = base_eq + block_excl_scan_bits(eq, wsum, &tot_eq);
+    const bool sel = gt || (eq && eq_rank < kleft);
+    const int pos = base_sel + block_excl_scan_bits(sel, wsum, &tot_sel);
+    if (sel) out[pos] = j;
+    base_eq += tot_eq;
+    base_sel += tot_sel;
+  }
+}
+
+// Register-resident variant for cols <= 1024 * KPT: thread t holds the keys
+// of channels t*KPT .. t*KPT + KPT - 1 (loaded once), the radix passes stop as
+// soon as the bin that holds the k-th largest key is taken whole, and the
+// emit pass needs two block scans (ties by channel index, then positions).
+__device__ __forceinline__ int block_excl_scan_int(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int s = wsum[i];
+    before += (i < w) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
+// Register-resident top-k (cols <= 1024 * KPT), one workgroup of 1024
+// threads holding KPT keys each (fp64 bit patterns: non-negative doubles
+// order as unsigned integers).  Radix select with 11-bit digits from the
+// first bit where two keys differ (two histogram buffers, so one pass costs
+// two barriers).  Once the bin holding the k-th key has at most 64 keys and
+// is not taken whole, those are ranked directly (key descending, channel
+// ascending).  The emit pass takes every key above the boundary and the
+// chosen keys on it, in ascending channel order.
+template <int KPT>
+__global__ __launch_bounds__(1024) void topk_reg_kernel(const double* __restrict__ scores,
+                                                        int32_t cols, int32_t k,
+                                                        int32_t* __restrict__ out) {
+  constexpr int DB = 11, NB = 1 << DB;   // digit bits, bins
+  constexpr int BPL = NB / 64;           // bins per lane in the boundary search
+  constexpr int kCand = 64;
+  __shared__ uint32_t hist[2][NB];
+  __shared__ uint64_t s_prefix;
+  __shared__ uint64_t s_or[16];
+  __shared__ int s_kleft, s_done, s_cnt, s_nc;
+  __shared__ int wsum[16];
+  __shared__ uint64_t c_key[kCand];
+  __shared__ int c_idx[kCand];
+  __shared__ int c_rank[kCand];
+  const uint64_t* keys = (const uint64_t*)scores;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j0 = tid * KPT;
+  uint64_t kv[KPT];
+#pragma unroll
+  for (int q = 0; q < KPT; ++q) kv[q] = j0 + q < cols ? keys[j0 + q] : 0ull;
+  const uint64_t ref = keys[0];
+  for (int i = tid; i < NB; i += 1024) hist[0][i] = 0;
+  if (tid == 0) s_nc = 0;
+  if (tid < kCand) c_rank[tid] = 0;
+  // Bits that every key shares need no pass: the radix passes start at the
+  // highest bit where two keys differ (OR of key ^ key 0 over all keys).
+  uint64_t dx = 0;
+#pragma unroll
+  for (int q = 0; q < KPT; ++q)
+    if (j0 + q < cols) dx |= kv[q] ^ ref;
+  for (int o = 32; o >= 1; o >>= 1) dx |= (uint64_t)__shfl_xor((long long)dx, o, 64);
+  if (lane == 0) s_or[wave] = dx;
+  __syncthreads();
+  uint64_t dall = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) dall |= s_or[w];
+  const int lead = dall ? __clzll((long long)dall) : 64;   // bits all keys share
+  uint64_t mask = lead == 0 ? 0ull : (lead == 64 ? ~0ull : ~0ull << (64 - lead));
+  uint64_t prefix = ref & mask;
+  int kleft = k;
+  bool done = false;
+  int cnt = 0x7fffffff;
+  // DB-bit digits from the first differing bit down; the last pass may
+  // overlap bits already fixed by the prefix (equal on every key it counts)
+  int pb = 0;
+  for (int shift = 64 - lead - DB; lead < 64; shift -= DB, pb ^= 1) {
+    const int sh = shift < 0 ? 0 : shift;
+    uint32_t* h = hist[pb];
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const bool valid = j0 + q < cols && (kv[q] & mask) == prefix;
+      if (valid) atomicAdd(&h[(uint32_t)(kv[q] >> sh) & (NB - 1)], 1u);
+    }
+    for (int i = tid; i < NB; i += 1024) hist[pb ^ 1][i] = 0;   // for the next pass
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns digits NB-1-BPL*l .. NB-BPL-BPL*l (descending); its sum is
+      // read in a lane-rotated order (bank-conflict free), then the one lane
+      // range holding the k-th key is scanned bin by bin across the wave
+      uint32_t sum = 0;
+#pragma unroll
+      for (int q = 0; q < BPL; ++q) sum += h[NB - 1 - BPL * lane - ((q + lane) & (BPL - 1))];
+      uint32_t incl = sum;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_up((int)incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      const uint32_t before = incl - sum;
+      const uint64_t hit = __ballot(before < (uint32_t)kleft && incl >= (uint32_t)kleft);
+      const int L = hit ? (int)__builtin_ctzll(hit) : 63;   // exactly one lane holds it
+      const uint32_t base = (uint32_t)__shfl((int)before, L, 64);
+      const int dig = NB - 1 - BPL * L - lane;                  // lanes < BPL: descending digits
+      const uint32_t cb = lane < BPL ? h[dig] : 0u;
+      uint32_t inc2 = cb;
+      for (int o = 1; o < BPL; o <<= 1) {
+        const uint32_t v = (uint32_t)__shfl_up((int)inc2, o, 64);
+        if (lane >= o) inc2 += v;
+      }
+      const uint32_t cum = base + inc2 - cb;
+      if (lane < BPL && cum < (uint32_t)kleft && cum + cb >= (uint32_t)kleft) {
+        s_prefix = prefix | ((uint64_t)dig << sh);
+        s_kleft = kleft - (int)cum;
+        s_done = (cum + cb == (uint32_t)kleft) ? 1 : 0;   // the whole bin is taken
+        s_cnt = (int)cb;
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    kleft = s_kleft;
+    mask |= (uint64_t)(NB - 1) << sh;
+    done = s_done != 0;
+    cnt = s_cnt;
+    if (done || sh == 0 || cnt <= kCand) break;
+  }
+  // the boundary bin: taken whole (done), ranked (at most kCand keys), or
+  // keys all equal (every bit decided), taken by channel order
+  const bool ranked = !done && cnt <= kCand && lead < 64;
+  int slot[KPT];
+  int eq_rank = 0;
+  if (ranked) {
+    // candidate slots: a ballot per key position, one atomic per wave
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const bool c = j0 + q < cols && (kv[q] & mask) == prefix;
+      const uint64_t b = __ballot(c);
+      int base = 0;
+      if (b != 0ull) {
+        if (lane == 0) base = atomicAdd(&s_nc, (int)__popcll(b));
+        base = __shfl(base, 0, 64);
+      }
+      slot[q] = -1;
+      if (c) {
+        const int sl = base + (int)__popcll(b & ((1ull << lane) - 1ull));
+        c_key[sl] = kv[q];
+        c_idx[sl] = j0 + q;
+        slot[q] = sl;
+      }
+    }
+    __syncthreads();
+    // rank of candidate l = number of candidates before it (key descending,
+    // channel ascending); the sixteen waves each compare against every
+    // sixteenth candidate and add their counts
+    if (lane < cnt) {
+      const uint64_t key = c_key[lane];
+      const int id = c_idx[lane];
+      int r = 0;
+      for (int i = wave; i < cnt; i += 16) {
+        const uint64_t k2 = c_key[i];
+        r += (k2 > key || (k2 == key && c_idx[i] < id)) ? 1 : 0;
+      }
+      if (r) atomicAdd(&c_rank[lane], r);
+    }
+    __syncthreads();
+  } else if (!done) {
+    int neq = 0;
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) neq += (j0 + q < cols && (kv[q] & mask) == prefix) ? 1 : 0;
+    int etot;
+    eq_rank = block_excl_scan_int(neq, wsum, &etot);
+  }
+  bool sel[KPT];
+  int nsel = 0;
+#pragma unroll
+  for (int q = 0; q < KPT; ++q) {
+    const bool valid = j0 + q < cols;
+    const uint64_t mk = kv[q] & mask;
+    const bool eq = valid && mk == prefix;
+    bool take_eq = done;
+    if (ranked) take_eq = eq && c_rank[slot[q]] < kleft;
+    else if (!done) take_eq = eq_rank < kleft;
+    sel[q] = valid && (mk > prefix || (eq && take_eq));
+    eq_rank += eq ? 1 : 0;
+    nsel += sel[q] ? 1 : 0;
+  }
+  int tot;
+  int pos = block_excl_scan_int(nsel, wsum, &tot);
+#pragma unroll
+  for (int q = 0; q < KPT; ++q)
+    if (sel[q]) out[pos++] = j0 + q;
+}
+
+// ====================================================================== gathers
+// residual gather (body in q4_prep.h)
+template <bool MX, bool UNITS>
+__global__ __launch_bounds__(256) void residual_gather_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int32_t cols, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ ts,
+    const int32_t* __restrict__ idx, int32_t k, uint16_t* __restrict__ R, int64_t ld_r,
+    int32_t* __restrict__ status) {
+  const bool ok = chan_set_ok(idx, k, cols);
+  if (status && blockIdx.x == 0 && threadIdx.x == 0) status[0] = ok ? 0 : 1;
+  residual_gather_part<MX, UNITS>(x, rows, cols, codes, scales, ts, idx, ok ? k : 0, R, ld_r,
+                                  blockIdx.x, gridDim.x);
+}
+
+// selected weight columns, one 64 x 64 tile per workgroup (body in q4_prep.h)
+__global__ __launch_bounds__(256) void wsel_gather_kernel(const uint16_t* __restrict__ w_hi_t,
+                                                          int64_t K, int64_t N,
+                                                          const int32_t* __restrict__ idx,
+                                                          int32_t k, int32_t kp,
+                                                          uint16_t* __restrict__ ws,
+                                                          const float* __restrict__ w_ts,
+                                                          const float* __restrict__ a_ts) {
+  __shared__ uint16_t tile[64][66];
+  const bool ok = chan_set_ok(idx, k, K);
+  wsel_gather_part(w_hi_t, K, N, gridDim.z, idx, ok ? k : 0, kp, ws, blockIdx.z, blockIdx.x, blockIdx.y,
+                   tile, w_ts, a_ts);
+}
+
+// The same gather in CH x 256 tiles with 8-byte accesses (N % 4 == 0): each
+// wave reads one selected row's 256 columns per load (lane l: columns
+// 4 l .. 4 l + 3), the tile is transposed through LDS, and each lane writes
+// four consecutive channels of one output row.  Tile (bx, by) of matrix b:
+// j in [256 bx, 256 bx + 256), t in [CH by, CH by + CH).  The loads go out
+// before the channel-set check (every channel is clamped into [0, K)); an
+// invalid set then zeroes what they read.
+template <int CH>
+__global__ __launch_bounds__(256) void wsel_gather_wide_kernel(const uint16_t* __restrict__ w_hi_t,
+                                                               int64_t K, int64_t N,
+                                                               const int32_t* __restrict__ idx,
+                                                               int32_t k, int32_t kp,
+                                                               uint16_t* __restrict__ ws,
+                                                               const float* __restrict__ w_ts,
+                                                               const float* __restrict__ a_ts) {
+  constexpr int TP = 264;           // LDS row pitch (u16): 256 columns + 8 of pad
+  constexpr int LPR = CH / 4;       // lanes per output row (four channels each)
+  constexpr int RPI = 64 / LPR;     // output rows per wave and store
+  __shared__ __attribute__((aligned(16))) uint16_t tile[CH][TP];
+  const int64_t b = blockIdx.z;
+  const int64_t j0 = (int64_t)blockIdx.x * 256;
+  const int t0 = blockIdx.y * CH;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint16_t* src = w_hi_t + b * N;   // channel-major [K][batch][N]
+  const int64_t cstride = (int64_t)gridDim.z * N;
+  const int64_t jl = j0 + 4 * lane;
+  const bool jok = jl < N;   // N % 4 == 0: the lane's four columns are all in or all out
+  uint2 v[CH / 4];
+#pragma unroll
+  for (int q = 0; q < CH / 4; ++q) {
+    const int t = t0 + 4 * q + wave;
+    int c = t < k ? idx[t] : 0;
+    c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
+    v[q] = (t < k && jok) ? *(const uint2*)(src + (int64_t)c * cstride + jl) : make_uint2(0, 0);
+  }
+  const bool ok = chan_set_ok(idx, k, K);
+  const float rinv = w_ts ? wsel_scale_inv(w_ts[b], a_ts[0]) : 1.0f;
+#pragma unroll
+  for (int q = 0; q < CH / 4; ++q) {
+    uint2 w = ok ? v[q] : make_uint2(0, 0);
+    if (w_ts) {
+      auto cv = [&](uint32_t x) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)(bf16_lo(x) * rinv));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)(bf16_hi(x) * rinv));
+        return lo | (hi << 16);
+      };
+      w = make_uint2(cv(w.x), cv(w.y));
+    }
+    *(uint2*)&tile[4 * q + wave][4 * lane] = w;
+  }
+  __syncthreads();
+  uint16_t* dst = ws + b * N * kp;
+  const int tt = 4 * (lane % LPR);
+#pragma unroll
+  for (int q = 0; q < 256 / (4 * RPI); ++q) {
+    const int jj = 4 * RPI * q + RPI * wave + lane / LPR;
+    const int64_t j = j0 + jj;
+    const uint32_t a0 = tile[tt][jj], a1 = tile[tt + 1][jj], a2 = tile[tt + 2][jj], a3 = tile[tt + 3][jj];
+    if (j < N && t0 + tt < kp) *(uint2*)(dst + j * kp + t0 + tt) = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+  }
+}
+
+// out[b][c][r] = in[b][r][c], or (interleave) out[c][b][r] = in[b][r][c]
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
+                                                             int64_t rows, int64_t cols,
+                                                             uint16_t* __restrict__ out,
+                                                             int32_t interleave) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t b = blockIdx.z;
+  const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const uint16_t* src = in + b * rows * cols;
+  // output row c of matrix b: interleaved rows c * batch + b
+  uint16_t* dst = interleave ? out + b * rows : out + b * rows * cols;
+  const int64_t orow = interleave ? (int64_t)gridDim.z * rows : rows;
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t rr = r0 + r, cc = c0 + tx;
+    tile[r][tx] = (rr < rows && cc < cols) ? src[rr * cols + cc] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t cc = c0 + r, rr = r0 + tx;
+    if (cc < cols && rr < rows) dst[cc * orow + rr] = tile[tx][r];
+  }
+}
+
+// packed row p of expert e <- logical row: group g = p / 64, q = p % 64;
+// q < 32 -> gate row 32g + q, else up row F + 32g + (q - 32)
+__global__ __launch_bounds__(256) void moe_pack_w13_kernel(const uint16_t* __restrict__ w13,
+                                                           int32_t F, int32_t H,
+                                                           uint16_t* __restrict__ out) {
+  const int64_t e = blockIdx.z;
+  const int p = blockIdx.y;
+  const int g = p >> 6, q = p & 63;
+  const int src_row = q < 32 ? 32 * g + q : F + 32 * g + (q - 32);
+  const uint16_t* s = w13 + (e * 2 * F + src_row) * (int64_t)H;
+  uint16_t* d = out + (e * 2 * F + p) * (int64_t)H;
+  for (int h = blockIdx.x * 256 + threadIdx.x; h < H; h += gridDim.x * 256) d[h] = s[h];
+}
+
+// ====================================================================== launchers
+__global__ void tensor_scale_kernel(const float* ts_in, float* ts_out) {
+  if (threadIdx.x == 0) ts_out[0] = ts_in ? ts_in[0] : 1.0f;
+}
+
+// rows per score tile: 32 (256-row groups), or 8 for a tensor whose 256-row
+// groups would make fewer than 128 workgroups, each walking its rows one
+// after another (decode-sized activations: 256 x 4096 would be 8 workgroups)
+static int quant_tile_rows(int64_t rows, int64_t cols) {
+  const int64_t units = (rows + 255) / 256 * ((cols + 511) / 512);
+  return units < 128 ? 8 : kScoreTileRows;
+}
+
+static int64_t score_groups(int64_t rows, int64_t cols) {
+  const int64_t g = (int64_t)quant_tile_rows(rows, cols) * kScoreGroupTiles;
+  return (rows + g - 1) / g;
+}
+
+size_t quantize_workspace_bytes(int64_t rows, int64_t cols) {
+  return align256(kAmaxBlocks * 4) +
+         align256((size_t)score_groups(rows, cols) * (size_t)cols * 8) + align256((size_t)cols * 8);
+}
+
 hipError_t launch_quantize(bool mx, const uint16_t* x, int64_t rows, int64_t cols,
                            const float* ts_in, uint8_t* codes, uint8_t* scales, float* ts_out,
                            double* chan_score, int32_t topk, int32_t* chan_idx, void* ws,
