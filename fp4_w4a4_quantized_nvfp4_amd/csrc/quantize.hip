@@ -789,9 +789,11 @@ __global__ void tensor_scale_kernel(const float* ts_in, float* ts_out) {
 // rows per score tile: 32 (256-row groups), or 8 for a tensor whose 256-row
 // groups would make fewer than 128 workgroups, each walking its rows one
 // after another (decode-sized activations: 256 x 4096 would be 8 workgroups)
+// 8-row score tiles (four times the workgroups) while the 32-row tiles would
+// give fewer workgroups than the chip has compute units
 static int quant_tile_rows(int64_t rows, int64_t cols) {
   const int64_t units = (rows + 255) / 256 * ((cols + 511) / 512);
-  return units < 128 ? 8 : kScoreTileRows;
+  return units < 256 ? 8 : kScoreTileRows;
 }
 
 static int64_t score_groups(int64_t rows, int64_t cols) {
