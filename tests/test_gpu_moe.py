@@ -128,6 +128,11 @@ def _check_site(fmt, xb, got, prefix, rac_k, ts=None):
                                             # (K = 512 at both sites, ragged 128-row
                                             # tiles)
                                             (600, 512, 4, 512, 2, 32),
+                                            # records with N not a multiple of 512:
+                                            # W13 (N = 768) on 256 x 256 tiles; W2
+                                            # (N = 768, K = 512) on 256 x 256 tiles
+                                            (600, 512, 4, 384, 2, 32),
+                                            (600, 768, 4, 512, 2, 32),
                                             # decode-shaped (streaming kernel) with the
                                             # compensation columns read from W_hi^T:
                                             # kp = 128 in two passes with padding
