@@ -678,7 +678,7 @@ MoeLayout moe_layout(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t F, in
   L.off[10] = take(4);
   L.off[11] = take((size_t)(rac_k > 0 ? rac_k : 1) * 4);
   L.off[12] = take((size_t)R * (kp ? kp : 1) * 2);
-  L.off[13] = take((size_t)R * H * 4);         // out fp32
+  L.off[13] = take((size_t)R * H * 4);         // out, Y's type (room for fp32)
   L.off[14] = take((size_t)H * 8);             // x scores
   L.off[15] = take((size_t)F * 8);             // h scores
   L.inv_perm = take((size_t)R * 4);
@@ -964,7 +964,7 @@ q4_status_t moe_w4a4_grouped_gemm_ex(int32_t fmt, const uint16_t* tokens, int64_
   }
   g2.Y = P(L.off[13]);
   g2.ldy = H;
-  g2.y_bf16 = 0;
+  g2.y_bf16 = y_dtype == Q4_OUT_BF16;   // expert outputs in the layer's output type
   g2.epilogue = kEpiStore;
   g2.tiles = tiles;
   g2.ntiles_dev = ntiles;
@@ -983,7 +983,7 @@ q4_status_t moe_w4a4_grouped_gemm_ex(int32_t fmt, const uint16_t* tokens, int64_
       g2.w_rec8 = w2_scale_records + fp16_records_bytes(E, H, F);
   }
   Q4_TRY(grouped_gemm(g2), "moe w2 gemm");
-  Q4_TRY(launch_moe_combine((const float*)P(L.off[13]), inv, topk_w, topk_idx, E, T, topk, H, Y,
+  Q4_TRY(launch_moe_combine(P(L.off[13]), g2.y_bf16, inv, topk_w, topk_idx, E, T, topk, H, Y,
                             y_dtype == Q4_OUT_BF16, s), "moe combine");
 #undef Q4_TRY
   return Q4_OK;

@@ -366,37 +366,56 @@ __global__ __launch_bounds__(1024) void moe_sort_small_kernel(
 }
 
 // y[t][h] = sum over slots s = 0..topk-1 of w[t][s] * out[inv_perm[t*topk+s]][h]
-// (fp32, slot order fixed; a slot with an invalid expert index contributes
-// nothing).  One workgroup per (token, 1024 columns).
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ out,
+// (fp32 sums, slot order fixed; a slot with an invalid expert index
+// contributes nothing).  The W2 rows `out` are fp32 (IN_BF16 false) or bf16:
+// the expert outputs are rounded to the layer's output type before they are
+// combined.  A lane takes C columns (one 16-byte load per slot), a workgroup
+// 256 C columns of one token.
+template <bool IN_BF16>
+__global__ __launch_bounds__(256) void moe_combine_kernel(const void* __restrict__ out,
                                                           const int32_t* __restrict__ inv_perm,
                                                           const float* __restrict__ w,
                                                           const int32_t* __restrict__ idx,
                                                           int32_t E, int64_t T, int32_t topk,
                                                           int32_t H, void* Y, int32_t y_bf16) {
-  const int nch = (H + 1023) / 1024;
+  constexpr int C = IN_BF16 ? 8 : 4;
+  const int nch = (H + 256 * C - 1) / (256 * C);
   const int64_t t = blockIdx.x / nch;
-  const int h0 = (int)(blockIdx.x % nch) * 1024 + threadIdx.x * 4;
-  if (t >= T || h0 >= H) return;
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  const int h0 = (int)(blockIdx.x % nch) * (256 * C) + threadIdx.x * C;
+  if (t >= T || h0 >= H) return;   // H % C == 0: a lane's columns are all in or all out
+  float a[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) a[i] = 0.0f;
   for (int s = 0; s < topk; ++s) {
     const int32_t ex = idx[t * topk + s];
     const float p = (ex >= 0 && ex < E) ? w[t * topk + s] : 0.0f;
     const int64_t r = inv_perm[t * topk + s];
     // each W2 row is read once: nontemporal
-    const f32x4v v = __builtin_nontemporal_load((const f32x4v*)(out + r * H + h0));
-    a0 = fmaf(p, v.x, a0);
-    a1 = fmaf(p, v.y, a1);
-    a2 = fmaf(p, v.z, a2);
-    a3 = fmaf(p, v.w, a3);
+    const u32x4v v = __builtin_nontemporal_load(
+        (const u32x4v*)((const uint8_t*)out + (r * H + h0) * (IN_BF16 ? 2 : 4)));
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      float x;
+      if constexpr (IN_BF16)
+        x = __builtin_bit_cast(float, (i & 1) ? (v[i / 2] & 0xffff0000u) : (v[i / 2] << 16));
+      else
+        x = __builtin_bit_cast(float, v[i]);
+      a[i] = fmaf(p, x, a[i]);
+    }
   }
   if (y_bf16) {
-    uint2 o;
-    o.x = f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
-    o.y = f32_to_bf16_rne(a2) | (f32_to_bf16_rne(a3) << 16);
-    *(uint2*)((uint16_t*)Y + t * H + h0) = o;
+    uint32_t o[C / 2];
+#pragma unroll
+    for (int i = 0; i < C / 2; ++i)
+      o[i] = f32_to_bf16_rne(a[2 * i]) | (f32_to_bf16_rne(a[2 * i + 1]) << 16);
+    if constexpr (C == 8)
+      *(uint4*)((uint16_t*)Y + t * H + h0) = make_uint4(o[0], o[1], o[2], o[3]);
+    else
+      *(uint2*)((uint16_t*)Y + t * H + h0) = make_uint2(o[0], o[1]);
   } else {
-    *(float4*)((float*)Y + t * H + h0) = make_float4(a0, a1, a2, a3);
+#pragma unroll
+    for (int i = 0; i < C; i += 4)
+      *(float4*)((float*)Y + t * H + h0 + i) = make_float4(a[i], a[i + 1], a[i + 2], a[i + 3]);
   }
 }
 
@@ -446,13 +465,19 @@ hipError_t launch_moe_sort(const int32_t* idx, int64_t T, int32_t E, int32_t top
   return hipGetLastError();
 }
 
-hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const float* topk_w,
-                              const int32_t* topk_idx, int32_t E, int64_t T, int32_t topk,
-                              int32_t H, void* Y, int32_t y_bf16, hipStream_t stream) {
+hipError_t launch_moe_combine(const void* out, int32_t out_bf16, const int32_t* inv_perm,
+                              const float* topk_w, const int32_t* topk_idx, int32_t E, int64_t T,
+                              int32_t topk, int32_t H, void* Y, int32_t y_bf16,
+                              hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const int64_t nch = (H + 1023) / 1024;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)(T * nch)), dim3(256), 0, stream, out,
-                     inv_perm, topk_w, topk_idx, E, T, topk, H, Y, y_bf16);
+  if (H % (out_bf16 ? 8 : 4)) return hipErrorInvalidValue;
+  const int64_t cols = 256 * (out_bf16 ? 8 : 4), nch = (H + cols - 1) / cols;
+  if (out_bf16)
+    hipLaunchKernelGGL(moe_combine_kernel<true>, dim3((unsigned)(T * nch)), dim3(256), 0, stream,
+                       out, inv_perm, topk_w, topk_idx, E, T, topk, H, Y, y_bf16);
+  else
+    hipLaunchKernelGGL(moe_combine_kernel<false>, dim3((unsigned)(T * nch)), dim3(256), 0, stream,
+                       out, inv_perm, topk_w, topk_idx, E, T, topk, H, Y, y_bf16);
   return hipGetLastError();
 }
 

@@ -189,9 +189,11 @@ hipError_t launch_moe_sort(const int32_t* idx, int64_t T, int32_t E, int32_t top
                            int32_t* ntiles, int32_t* counts, hipStream_t stream,
                            int32_t* a_rows = nullptr, int32_t bm2 = 0, int32_t* tiles2 = nullptr,
                            int32_t* ntiles2 = nullptr, int32_t* status = nullptr);
-hipError_t launch_moe_combine(const float* out, const int32_t* inv_perm, const float* topk_w,
-                              const int32_t* topk_idx, int32_t E, int64_t T, int32_t topk,
-                              int32_t H, void* Y, int32_t y_bf16, hipStream_t stream);
+// out: the W2 rows, fp32 or (out_bf16) bf16; H % 8 == 0 for bf16 rows
+hipError_t launch_moe_combine(const void* out, int32_t out_bf16, const int32_t* inv_perm,
+                              const float* topk_w, const int32_t* topk_idx, int32_t E, int64_t T,
+                              int32_t topk, int32_t H, void* Y, int32_t y_bf16,
+                              hipStream_t stream);
 // grouped GEMM over tiles of at most kSkinnyBM rows (few rows per expert)
 constexpr int kSkinnyBM = 32;
 // M tile rows of the grouped 128 x 512 tiles (GemmArgs::wide)

@@ -355,7 +355,9 @@ q4_status_t q4_scale_records(int32_t fmt, const uint8_t *scales, int64_t batch, 
  *              defines.  moe_w4a4_grouped_gemm_ex can instead quantize h inside
  *              the W13 GEMM (Q4_MOE_FUSE_H_QUANT).
  *   rac_k      channels compensated at each of the two activation sites.
- *   Y          [T][H] fp32 or bf16: y_t = sum_s p_ts out_(t,s), slots in order.
+ *   Y          [T][H] fp32 or bf16: y_t = sum_s p_ts out_(t,s), slots in order,
+ *              summed in fp32.  The expert rows out_(t,s) are kept in Y's type:
+ *              with a bf16 Y each is rounded to bf16 (nearest even) first.
  * Steps: sort; quantize tokens (one s_t, one selection over T rows); W13 RAC
  * GEMM over sorted rows with the SwiGLU epilogue h = bf16(silu(g) * u); quantize
  * h over all T*topk sorted rows (one s_t, one selection); W2 RAC GEMM; combine.
@@ -370,7 +372,7 @@ size_t moe_workspace_size(int32_t fmt, int64_t T, int32_t E, int32_t H, int32_t 
  *   3 x scales                 4 x tensor scale fp32      5 x channel set int32 [rac_k]
  *   6 x residual R [T][kp]     7 h bf16 [T*topk][F]       8 h codes
  *   9 h scales                10 h tensor scale fp32     11 h channel set
- *  12 h residual R [T*topk][kp]                          13 out fp32 [T*topk][H]
+ *  12 h residual R [T*topk][kp]     13 out [T*topk][H], Y's type (fp32 or bf16)
  *  14 x channel scores fp64 [H]                          15 h channel scores fp64 [F]
  * kp = rac_k rounded up to a multiple of 32.  R holds bf16(r) on the selected
  * channels (zero past rac_k), except for an NVFP4 GEMM that takes its

@@ -17,6 +17,10 @@ plain reading used here is the standard SwiGLU expert layer:
   activation tensor (one tensor scale, one channel selection);
 * W2 projection with residual compensation, and y_t = sum over slots
   (slot 0 first) of p * out.
+* With a bf16 layer output (``out_bf16``) the expert rows enter that sum as
+  bf16 values (out rounded once, to nearest even), the form in which an
+  expert-parallel layer hands them back for combining; with an fp32 output
+  they enter unrounded.
 """
 from __future__ import annotations
 
@@ -72,7 +76,7 @@ def _rows(q: QuantResult, rows: np.ndarray) -> QuantResult:
 
 def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
               wq13=None, wq2=None, fmt: str = "nvfp4", Sx_override=None, Sh_override=None,
-              h_tensor_scale=None):
+              h_tensor_scale=None, out_bf16: bool = False):
     """Whole expert layer; returns a dict of every intermediate (fp64 unless noted).
 
     x_bits [T, H] bf16 bits; idx/p from ``moe_route``; w13_bits [E, 2F, H] and
@@ -85,6 +89,8 @@ def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
     already validated against this oracle's scores, where several sets are
     correct at a near-tie).  ``h_tensor_scale`` (NVFP4) quantizes h under that
     supplied tensor scale instead of RN32(amax(h) / 2688) (delayed scaling).
+    ``out_bf16`` rounds each W2 row to bf16 before the combine ("out" stays
+    the exact product, "out_used" is what the combine sums).
     """
     quant = nvfp4_quantize if fmt == "nvfp4" else mxfp4_quantize
     T, H = x_bits.shape
@@ -124,13 +130,15 @@ def moe_layer(x_bits, idx, p, w13_bits, w2_bits, rac_k: int, h_override=None,
             continue
         rows = np.arange(r0, r1)
         out[r0:r1] = rac_gemm(_rows(qh, rows), wq2[e], Rh[rows], w2_bits[e], Sh)
+    out_used = bf16_bits_to_f64(f64_to_bf16_bits(out)) if out_bf16 else out
     pos = np.empty(T * k, dtype=np.int64)
     pos[perm] = np.arange(T * k)
     y = np.zeros((T, H), dtype=np.float64)
     for s in range(k):
-        y += p[:, s:s + 1] * out[pos[np.arange(T) * k + s]]
+        y += p[:, s:s + 1] * out_used[pos[np.arange(T) * k + s]]
     return dict(perm=perm, offsets=offsets, qx=qx, scores_x=sx, Sx=Sx, Rx=Rx, y13=y13, h=h,
-                qh=qh, scores_h=sh, Sh=Sh, Rh=Rh, out=out, y=y, wq13=wq13, wq2=wq2)
+                qh=qh, scores_h=sh, Sh=Sh, Rh=Rh, out=out, out_used=out_used, y=y, wq13=wq13,
+                wq2=wq2)
 
 
 def dense_swiglu_reference(x_bits, w13_bits, w2_bits):

@@ -515,6 +515,30 @@ def test_moe_route_and_sort_brute_force():
         assert np.all(idx.reshape(-1)[seg] == e) and np.all(np.diff(seg) > 0)
 
 
+def test_moe_bf16_expert_rows():
+    # one slot of weight 1: the layer output is the expert row itself, so with
+    # bf16 expert rows it is out rounded once to nearest bf16 (ties to even);
+    # everything before the combine is unchanged
+    rng = np.random.default_rng(10)
+    T, H, F = 16, 64, 32
+    x = _bits(rng.standard_normal((T, H)).astype(np.float32))
+    w13 = _bits((rng.standard_normal((1, 2 * F, H)) * 0.1).astype(np.float32))
+    w2 = _bits((rng.standard_normal((1, H, F)) * 0.1).astype(np.float32))
+    idx = np.zeros((T, 1), dtype=np.int32)
+    ex = oracle.moe_layer(x, idx, np.ones((T, 1)), w13, w2, rac_k=8)
+    rb = oracle.moe_layer(x, idx, np.ones((T, 1)), w13, w2, rac_k=8, out_bf16=True)
+    np.testing.assert_array_equal(rb["out"], ex["out"])
+    np.testing.assert_array_equal(ex["y"], ex["out"])
+    # every value is a bf16 value, the nearest one to the exact row
+    u = rb["y"].astype(np.float32).view(np.uint32)
+    assert np.all(u & 0xFFFF == 0) and np.all(rb["y"].astype(np.float32) == rb["y"])
+    up = (u + (1 << 16)).view(np.float32).astype(np.float64)
+    dn = (u - (1 << 16)).view(np.float32).astype(np.float64)
+    d = np.abs(rb["y"] - ex["out"])
+    assert np.all(d <= np.abs(up - ex["out"])) and np.all(d <= np.abs(dn - ex["out"]))
+    assert np.any(d > 0)
+
+
 def test_moe_identical_experts_collapse_to_one():
     # with every expert identical, sum_s p_s out_s == out (weights sum to 1)
     rng = np.random.default_rng(9)
