@@ -123,13 +123,16 @@ def _moe_legs(q4, L, dev, stream, sp, iters=10):
                 offs, _ = q4.moe_workspace_layout(fmt, T, E, H, F, topk, k)
                 s_h = ws[offs[10]:offs[10] + 4].view(torch.float32).clone()
 
-                def timed(fuse):
+                Y32 = torch.empty((T, H), dtype=torch.float32, device=dev)
+
+                def timed(fuse, h_scale=s_h, f32=False):
                     def layer_s():
                         q4._check(L.q4_moe_route(logits.data_ptr(), T, E, topk, idx.data_ptr(),
                                                  pw.data_ptr(), sp))
                         q4.moe_w4a4_grouped_gemm(tokens, idx, pw, experts, k,
-                                                 out_dtype=q4.OUT_BF16, workspace=ws, Y=Y,
-                                                 h_tensor_scale=s_h, fuse_h=fuse)
+                                                 out_dtype=q4.OUT_F32 if f32 else q4.OUT_BF16,
+                                                 workspace=ws, Y=Y32 if f32 else Y,
+                                                 h_tensor_scale=h_scale, fuse_h=fuse)
                     _warm(layer_s, stream)
                     e0.record(stream)
                     for _ in range(iters):
@@ -139,6 +142,9 @@ def _moe_legs(q4, L, dev, stream, sp, iters=10):
                     return e0.elapsed_time(e1) / iters
                 supplied_ms = timed(False)
                 fused_ms = timed(True)
+                # fp32 output: fp32 expert rows, the combine without their rounding
+                f32_ms = timed(False, h_scale=None, f32=True)
+                del Y32
             w_bytes = sum(t.numel() * t.element_size() for t in
                           (experts["w13"]["codes"], experts["w13"]["scales"],
                            experts["w2"]["codes"], experts["w2"]["scales"]))
@@ -151,6 +157,7 @@ def _moe_legs(q4, L, dev, stream, sp, iters=10):
             if supplied_ms is not None:
                 leg["supplied_h_scale_ms"] = round(supplied_ms, 4)
                 leg["fused_h_epilogue_ms"] = round(fused_ms, 4)
+                leg["f32_out_ms"] = round(f32_ms, 4)
             res.setdefault(name, {})[leg["fmt"]] = leg
             del experts, ws
         res[name]["shape"] = {"T": T, "H": H, "E": E, "F": F, "topk": topk, "rac_k": k,
