@@ -390,17 +390,23 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const void* __restrict
     const int32_t ex = idx[t * topk + s];
     const float p = (ex >= 0 && ex < E) ? w[t * topk + s] : 0.0f;
     const int64_t r = inv_perm[t * topk + s];
-    // each W2 row is read once: nontemporal
-    const u32x4v v = __builtin_nontemporal_load(
-        (const u32x4v*)((const uint8_t*)out + (r * H + h0) * (IN_BF16 ? 2 : 4)));
+    // each W2 row is read once: nontemporal (16 bytes; the elements are
+    // taken by name, not by a subscript of the loaded vector)
+    if constexpr (IN_BF16) {
+      const uint4 v = __builtin_bit_cast(
+          uint4, __builtin_nontemporal_load((const u32x4v*)((const uint16_t*)out + r * H + h0)));
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      float x;
-      if constexpr (IN_BF16)
-        x = __builtin_bit_cast(float, (i & 1) ? (v[i / 2] & 0xffff0000u) : (v[i / 2] << 16));
-      else
-        x = __builtin_bit_cast(float, v[i]);
-      a[i] = fmaf(p, x, a[i]);
+      for (int i = 0; i < 4; ++i) {
+        a[2 * i] = fmaf(p, __builtin_bit_cast(float, w[i] << 16), a[2 * i]);
+        a[2 * i + 1] = fmaf(p, __builtin_bit_cast(float, w[i] & 0xffff0000u), a[2 * i + 1]);
+      }
+    } else {
+      const f32x4v v = __builtin_nontemporal_load((const f32x4v*)((const float*)out + r * H + h0));
+      a[0] = fmaf(p, v.x, a[0]);
+      a[1] = fmaf(p, v.y, a[1]);
+      a[2] = fmaf(p, v.z, a[2]);
+      a[3] = fmaf(p, v.w, a[3]);
     }
   }
   if (y_bf16) {

@@ -198,6 +198,35 @@ def test_small_layer_stagewise(fmt, T, H, E, F, topk, k):
 
 
 @pytest.mark.parametrize("fmt", [0, 1], ids=["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("T,H,E,F,topk,k", [(600, 512, 4, 512, 2, 32),   # 128 x 512 tiles (NVFP4)
+                                            (40, 256, 8, 192, 2, 70)])   # streaming kernel
+def test_small_layer_f32_output(fmt, T, H, E, F, topk, k):
+    """An fp32 layer output keeps the W2 rows in fp32: they are within the
+    GEMM tolerance of the oracle's exact rows with no rounding allowance, and
+    the output is the oracle's unrounded combine within twice that."""
+    say(f"moe f32 out fmt={fmt} T={T} H={H} E={E} F={F} topk={topk} k={k}")
+    m = q4()
+    rng = np.random.default_rng(3 * T + H + E)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    x[:, rng.choice(H, 3, replace=False)] *= 40
+    xb = _bits(x)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    w13 = _bits((rng.standard_normal((E, 2 * F, H)) * 0.05).astype(np.float32))
+    w2 = _bits((rng.standard_normal((E, H, F)) * 0.05).astype(np.float32))
+    got, _ = _run_layer(m, xb, logits, w13, w2, topk, k, fmt, out_dtype=0)
+    assert got["out"].dtype == np.float32 and got["Y"].dtype == np.float32
+    _, Sx = _check_site(fmt, xb, got, "x", k)
+    _, Sh = _check_site(fmt, got["h"], got, "h", k)
+    ref = oracle.moe_layer(xb, got["idx"], got["p"].astype(np.float64), w13, w2, k,
+                           h_override=got["h"], fmt="nvfp4" if fmt == 0 else "mxfp4",
+                           Sx_override=Sx, Sh_override=Sh)
+    err_o = gemm_rel_err(got["out"], ref["out"])
+    say(f"  W2 out rel err {err_o:.2e}")
+    assert err_o <= GEMM_TOL
+    check_close(got["Y"], ref["y"], 2 * GEMM_TOL)
+
+
+@pytest.mark.parametrize("fmt", [0, 1], ids=["nvfp4", "mxfp4"])
 def test_empty_token_batch(fmt):
     """T = 0: the layer runs, writes nothing and reports no error."""
     m = q4()
