@@ -8,6 +8,21 @@
 namespace q4 {
 
 // ====================================================================== route
+// 64-bit value of lane (lane's DPP source under CTRL), every lane active
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t k) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xf,
+                                                            0xf, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xf, 0xf,
+                                                            false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t k, int l) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), l);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // one wave per token: repeated arg-max over the logits (ties -> smaller
 // expert), then softmax over the selected logits.  MAXPER logits per lane
 // (E <= 64 MAXPER).
@@ -33,31 +48,37 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
   bool taken[MAXPER];
 #pragma unroll
   for (int q = 0; q < MAXPER; ++q) taken[q] = !(q < per && q * 64 + lane < E);
+  // Each candidate is one 64-bit key: the logit's bits in an order-keeping
+  // form above the complement of the expert index, so the largest key is the
+  // largest logit and, among equal logits, the smaller expert (-0 counts as
+  // +0, as the float comparison has it).  A taken (or
+  // absent) candidate is key 0, below every logit, -inf included.
+  auto key_of = [](float x, int ex) {
+    const uint32_t u = __float_as_uint(x + 0.0f);   // -0 -> +0: equal logits, equal keys
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)~ex;
+  };
   float sel[16];
   int sel_e[16];
   for (int s = 0; s < topk; ++s) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    uint64_t kb = 0;
 #pragma unroll
-    for (int q = 0; q < MAXPER; ++q) {
-      const int ex = q * 64 + lane;
-      if (!taken[q] && (v[q] > bv || (v[q] == bv && ex < be))) {
-        bv = v[q];
-        be = ex;
-      }
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    for (int q = 0; q < MAXPER; ++q)
+      if (!taken[q]) kb = max(kb, key_of(v[q], q * 64 + lane));
+    // wave maximum: within rows of 16 lanes by DPP (lane pairs, quads,
+    // half rows, rows), then over the four rows' lanes 0, 16, 32, 48
+    kb = max(kb, dpp_u64<0xB1>(kb));    // quad_perm [1, 0, 3, 2]
+    kb = max(kb, dpp_u64<0x4E>(kb));    // quad_perm [2, 3, 0, 1]
+    kb = max(kb, dpp_u64<0x141>(kb));   // row_half_mirror
+    kb = max(kb, dpp_u64<0x140>(kb));   // row_mirror
+    kb = max(max(readlane_u64(kb, 0), readlane_u64(kb, 16)),
+             max(readlane_u64(kb, 32), readlane_u64(kb, 48)));
+    const int be = (int)~(uint32_t)kb;
+    const uint32_t o = (uint32_t)(kb >> 32);
 #pragma unroll
     for (int q = 0; q < MAXPER; ++q)
       if (q * 64 + lane == be) taken[q] = true;
-    sel[s] = bv;
+    sel[s] = __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
     sel_e[s] = be;
   }
   if (lane == 0) {
