@@ -51,8 +51,8 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
   // Each candidate is one 64-bit key: the logit's bits in an order-keeping
   // form above the complement of the expert index, so the largest key is the
   // largest logit and, among equal logits, the smaller expert (-0 counts as
-  // +0, as the float comparison has it).  A taken (or
-  // absent) candidate is key 0, below every logit, -inf included.
+  // +0, as the float comparison has it).  A taken (or absent) candidate is
+  // key 0, below every logit, -inf included.
   auto key_of = [](float x, int ex) {
     const uint32_t u = __float_as_uint(x + 0.0f);   // -0 -> +0: equal logits, equal keys
     const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -416,11 +416,11 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const void* __restrict
     if constexpr (IN_BF16) {
       const uint4 v = __builtin_bit_cast(
           uint4, __builtin_nontemporal_load((const u32x4v*)((const uint16_t*)out + r * H + h0)));
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t pair[4] = {v.x, v.y, v.z, v.w};   // two bf16 columns each
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[2 * i] = fmaf(p, __builtin_bit_cast(float, w[i] << 16), a[2 * i]);
-        a[2 * i + 1] = fmaf(p, __builtin_bit_cast(float, w[i] & 0xffff0000u), a[2 * i + 1]);
+        a[2 * i] = fmaf(p, __builtin_bit_cast(float, pair[i] << 16), a[2 * i]);
+        a[2 * i + 1] = fmaf(p, __builtin_bit_cast(float, pair[i] & 0xffff0000u), a[2 * i + 1]);
       }
     } else {
       const f32x4v v = __builtin_nontemporal_load((const f32x4v*)((const float*)out + r * H + h0));
